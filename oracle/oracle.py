@@ -1,0 +1,259 @@
+"""Python front of the fp64 CPU oracle (oracle/e3_oracle.c), via ctypes.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this module.  It shares
+no code with the HIP library (``clebsch_gordan_tensor_amd``): irreps are
+passed here as plain lists of ``(l, parity)`` and every array is float64.
+
+What each function computes, and the passage it follows, is stated in the C
+file next to the function it wraps.  Where a result has a plain definition
+(the convolution and tensor product of the e3j paper, E.1 Eq.10-13 and
+Eq.16), the oracle is that definition written out as loops.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libe3oracle.so")
+_MAX_IRREPS = 16
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from oracle.build import build_oracle  # builds only when nothing is built
+        build_oracle()
+    lib = C.CDLL(_LIB_PATH)
+    dp = C.POINTER(C.c_double)
+    ip = C.POINTER(C.c_int)
+    lp = C.POINTER(C.c_int64)
+    lib.oracle_cg_complex.restype = C.c_double
+    lib.oracle_cg_complex.argtypes = [C.c_int] * 6
+    lib.oracle_cg_real.restype = C.c_int
+    lib.oracle_cg_real.argtypes = [C.c_int, C.c_int, C.c_int, dp]
+    lib.oracle_umat.restype = None
+    lib.oracle_umat.argtypes = [C.c_int, dp, dp]
+    lib.oracle_sh_batch.restype = C.c_int
+    lib.oracle_sh_batch.argtypes = [C.c_int, C.c_int64, dp, dp]
+    lib.oracle_num_threads.restype = C.c_int
+    lib.oracle_num_paths.restype = C.c_int
+    lib.oracle_num_paths.argtypes = [C.c_void_p]
+    lib.oracle_path_info.restype = C.c_int
+    lib.oracle_path_info.argtypes = [C.c_void_p, C.c_int, ip, ip, ip]
+    lib.oracle_conv_forward.restype = C.c_int
+    lib.oracle_conv_forward.argtypes = [C.c_void_p, C.c_int, C.c_int64, ip, ip, dp, dp, dp, dp,
+                                        C.c_int, ip, dp]
+    lib.oracle_tp_forward.restype = C.c_int
+    lib.oracle_tp_forward.argtypes = [C.c_void_p, C.c_int64, dp, dp, dp, C.c_int, lp, dp]
+    lib.oracle_conv_backward_dx.restype = C.c_int
+    lib.oracle_conv_backward_dx.argtypes = [C.c_void_p, C.c_int, C.c_int64, ip, ip, dp, dp, dp,
+                                            dp, C.c_int, ip, dp]
+    lib.oracle_conv_backward_edge.restype = C.c_int
+    lib.oracle_conv_backward_edge.argtypes = [C.c_void_p, C.c_int, C.c_int64, ip, ip, dp, dp,
+                                              dp, dp, dp, C.c_int, lp, dp, dp]
+    _lib = lib
+    return lib
+
+
+class _CDesc(C.Structure):
+    _fields_ = [("nx", C.c_int), ("ny", C.c_int), ("no", C.c_int),
+                ("xl", C.c_int * _MAX_IRREPS), ("xp", C.c_int * _MAX_IRREPS),
+                ("yl", C.c_int * _MAX_IRREPS), ("yp", C.c_int * _MAX_IRREPS),
+                ("ol", C.c_int * _MAX_IRREPS), ("op", C.c_int * _MAX_IRREPS),
+                ("C", C.c_int)]
+
+
+def parse_irreps(s: str):
+    """'128x0e+128x1o' -> (mul, [(0, 1), (1, -1)]); every mul must agree."""
+    out, muls = [], set()
+    for term in s.replace(" ", "").split("+"):
+        if "x" in term:
+            mul, ir = term.split("x")
+            muls.add(int(mul))
+        else:
+            ir = term
+            muls.add(1)
+        l, p = int(ir[:-1]), {"e": 1, "o": -1}[ir[-1]]
+        out.append((l, p))
+    if len(muls) != 1:
+        raise ValueError("channel-wise irreps need one multiplicity: " + s)
+    return muls.pop(), out
+
+
+class Desc:
+    """Irreps of x, y and the output, as lists of (l, parity), and C channels."""
+
+    def __init__(self, x, y, out, channels):
+        self.x, self.y, self.out, self.C = list(x), list(y), list(out), int(channels)
+        c = _CDesc()
+        c.nx, c.ny, c.no, c.C = len(self.x), len(self.y), len(self.out), self.C
+        for arr_l, arr_p, ir in ((c.xl, c.xp, self.x), (c.yl, c.yp, self.y),
+                                 (c.ol, c.op, self.out)):
+            if len(ir) > _MAX_IRREPS:
+                raise ValueError("too many irreps")
+            for i, (l, p) in enumerate(ir):
+                arr_l[i], arr_p[i] = l, p
+        self._c = c
+
+    @property
+    def dx(self):
+        return sum(2 * l + 1 for l, _ in self.x)
+
+    @property
+    def dy(self):
+        return sum(2 * l + 1 for l, _ in self.y)
+
+    @property
+    def dout(self):
+        return sum(2 * l + 1 for l, _ in self.out)
+
+    def ptr(self):
+        return C.byref(self._c)
+
+
+def _dp(a):
+    return a.ctypes.data_as(C.POINTER(C.c_double))
+
+
+def _ip(a):
+    return a.ctypes.data_as(C.POINTER(C.c_int))
+
+
+def _lp(a):
+    return a.ctypes.data_as(C.POINTER(C.c_int64))
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def cg_complex(l1, m1, l2, m2, L, M) -> float:
+    return _load().oracle_cg_complex(l1, m1, l2, m2, L, M)
+
+
+def cg_real(l1, l2, L) -> np.ndarray:
+    out = np.zeros((2 * L + 1) * (2 * l1 + 1) * (2 * l2 + 1))
+    if _load().oracle_cg_real(l1, l2, L, _dp(out)) != 0:
+        raise ValueError("uncoupled triple")
+    return out.reshape(2 * L + 1, 2 * l1 + 1, 2 * l2 + 1)
+
+
+def umat(l) -> np.ndarray:
+    n = 2 * l + 1
+    re, im = np.zeros(n * n), np.zeros(n * n)
+    _load().oracle_umat(l, _dp(re), _dp(im))
+    return (re + 1j * im).reshape(n, n)
+
+
+def sh(lmax: int, vecs) -> np.ndarray:
+    v = _f64(vecs).reshape(-1, 3)
+    out = np.zeros((v.shape[0], (lmax + 1) ** 2))
+    if _load().oracle_sh_batch(lmax, v.shape[0], _dp(v), _dp(out)) != 0:
+        raise ValueError("lmax out of range")
+    return out
+
+
+def num_paths(d: Desc) -> int:
+    return _load().oracle_num_paths(d.ptr())
+
+
+def paths(d: Desc):
+    lib = _load()
+    res = []
+    for i in range(num_paths(d)):
+        a, b, c = C.c_int(), C.c_int(), C.c_int()
+        lib.oracle_path_info(d.ptr(), i, C.byref(a), C.byref(b), C.byref(c))
+        res.append((a.value, b.value, c.value))
+    return res
+
+
+def _y_args(evec, Y):
+    if (evec is None) == (Y is None):
+        raise ValueError("give exactly one of evec, Y")
+    ev = _f64(evec) if evec is not None else None
+    yy = _f64(Y) if Y is not None else None
+    return ev, yy
+
+
+def conv_forward(d: Desc, rowptr, sender, x, w, evec=None, Y=None, rows=None):
+    """m[rows] (all receivers by default), shape [len(rows)][dout][C]."""
+    rowptr, sender = _i32(rowptr), _i32(sender)
+    n_nodes = rowptr.shape[0] - 1
+    rows = np.arange(n_nodes, dtype=np.int32) if rows is None else _i32(rows)
+    ev, yy = _y_args(evec, Y)
+    x, w = _f64(x), _f64(w)
+    m = np.zeros((rows.shape[0], d.dout, d.C))
+    r = _load().oracle_conv_forward(d.ptr(), n_nodes, sender.shape[0], _ip(rowptr), _ip(sender),
+                                    _dp(ev) if ev is not None else None,
+                                    _dp(yy) if yy is not None else None, _dp(x), _dp(w),
+                                    rows.shape[0], _ip(rows), _dp(m))
+    if r != 0:
+        raise ValueError("oracle_conv_forward rejected its arguments")
+    return m
+
+
+def tp_forward(d: Desc, x, y, w, rows=None):
+    """z[rows] (all rows by default), shape [len(rows)][dout][C]."""
+    x, y, w = _f64(x), _f64(y), _f64(w)
+    n = x.shape[0]
+    rows = np.arange(n, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    z = np.zeros((rows.shape[0], d.dout, d.C))
+    r = _load().oracle_tp_forward(d.ptr(), n, _dp(x), _dp(y), _dp(w), rows.shape[0], _lp(rows),
+                                  _dp(z))
+    if r != 0:
+        raise ValueError("oracle_tp_forward rejected its arguments")
+    return z
+
+
+def conv_backward_dx(d: Desc, rowptr, sender, w, dm, evec=None, Y=None, rows=None):
+    """dx[rows] (all senders by default), shape [len(rows)][dx][C]."""
+    rowptr, sender = _i32(rowptr), _i32(sender)
+    n_nodes = rowptr.shape[0] - 1
+    rows = np.arange(n_nodes, dtype=np.int32) if rows is None else _i32(rows)
+    ev, yy = _y_args(evec, Y)
+    w, dm = _f64(w), _f64(dm)
+    dx = np.zeros((rows.shape[0], d.dx, d.C))
+    r = _load().oracle_conv_backward_dx(d.ptr(), n_nodes, sender.shape[0], _ip(rowptr),
+                                        _ip(sender), _dp(ev) if ev is not None else None,
+                                        _dp(yy) if yy is not None else None, _dp(w), _dp(dm),
+                                        rows.shape[0], _ip(rows), _dp(dx))
+    if r != 0:
+        raise ValueError("oracle_conv_backward_dx rejected its arguments")
+    return dx
+
+
+def conv_backward_edge(d: Desc, rowptr, sender, x, w, dm, evec=None, Y=None, edges=None):
+    """(dw[edges] [len][P][C], dY[edges] [len][dy]); all edges by default."""
+    rowptr, sender = _i32(rowptr), _i32(sender)
+    n_nodes = rowptr.shape[0] - 1
+    n_edges = sender.shape[0]
+    edges = (np.arange(n_edges, dtype=np.int64) if edges is None
+             else np.ascontiguousarray(edges, np.int64))
+    ev, yy = _y_args(evec, Y)
+    x, w, dm = _f64(x), _f64(w), _f64(dm)
+    P = num_paths(d)
+    dw = np.zeros((edges.shape[0], P, d.C))
+    dY = np.zeros((edges.shape[0], d.dy))
+    r = _load().oracle_conv_backward_edge(d.ptr(), n_nodes, n_edges, _ip(rowptr), _ip(sender),
+                                          _dp(ev) if ev is not None else None,
+                                          _dp(yy) if yy is not None else None, _dp(x), _dp(w),
+                                          _dp(dm), edges.shape[0], _lp(edges), _dp(dw), _dp(dY))
+    if r != 0:
+        raise ValueError("oracle_conv_backward_edge rejected its arguments")
+    return dw, dY

@@ -1,0 +1,392 @@
+"""Pins for the oracle's convolution, tensor product and their VJPs (CPU only).
+
+The oracle writes out the e3j paper's E.1 Eq.10-13 (forward) and Eq.16
+(backward) as loops.  These tests check it against independent routes to the
+same numbers: a vectorised dense contraction with numpy scatter-add, the
+special cases that reduce to a sparse matrix-vector product (scipy.sparse) and
+to a tensor-field-network filter, linearity, rotation and inversion
+equivariance, the tensor product as a convolution on the identity graph, the
+adjoint (VJP) identity, Euler's identity for a trilinear map and central
+finite differences.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.sparse as sps
+
+from clebsch_gordan_tensor_amd import synth as S
+from oracle import oracle as O
+
+
+def desc_of(x, y, out, C):
+    return O.Desc(x, y, out, C)
+
+
+def offsets(irreps):
+    o, r = 0, []
+    for l, _ in irreps:
+        r.append(o)
+        o += 2 * l + 1
+    return r
+
+
+def paths_of(x, y, out):
+    res = []
+    for ix, (lx, px) in enumerate(x):
+        for iy, (ly, py) in enumerate(y):
+            for io, (lo, po) in enumerate(out):
+                if abs(lx - ly) <= lo <= lx + ly and px * py == po:
+                    res.append((ix, iy, io))
+    return res
+
+
+def dense_conv(x_ir, y_ir, o_ir, graph, x, w, Y):
+    """Vectorised reference: messages for all edges with dense CG blocks,
+    then np.add.at into receivers (padding edges masked out)."""
+    N, E = graph.n_nodes, graph.n_edges
+    C = x.shape[2]
+    xo, yo, oo = offsets(x_ir), offsets(y_ir), offsets(o_ir)
+    m = np.zeros((N, sum(2 * l + 1 for l, _ in o_ir), C))
+    snd = graph.sender.astype(np.int64)
+    ok = snd >= 0
+    xs = x[np.where(ok, snd, 0)]
+    for p, (ix, iy, io) in enumerate(paths_of(x_ir, y_ir, o_ir)):
+        l1, l2, L = x_ir[ix][0], y_ir[iy][0], o_ir[io][0]
+        T = O.cg_real(l1, l2, L)
+        xa = xs[:, xo[ix]:xo[ix] + 2 * l1 + 1, :]
+        ye = Y[:, yo[iy]:yo[iy] + 2 * l2 + 1]
+        msg = np.einsum("Mij,eiq,ej->eMq", T, xa, ye) * w[:, p, None, :]
+        msg[~ok] = 0
+        np.add.at(m[:, oo[io]:oo[io] + 2 * L + 1, :], graph.receiver, msg)
+    return m
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return S.make_conv("tiny")
+
+
+def with_padding(graph, n_pad_per_node=2, seed=9):
+    """Insert padding edges (sender = -1, garbage vectors) into every segment."""
+    rng = np.random.default_rng(seed)
+    snd, rcv, ev = [], [], []
+    for b in range(graph.n_nodes):
+        lo, hi = graph.rowptr[b], graph.rowptr[b + 1]
+        snd += list(graph.sender[lo:hi]) + [-1] * n_pad_per_node
+        rcv += [b] * (hi - lo + n_pad_per_node)
+        ev += list(graph.evec[lo:hi]) + list(rng.standard_normal((n_pad_per_node, 3)))
+    counts = np.bincount(np.array(rcv), minlength=graph.n_nodes)
+    rowptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return S.Graph(pos=graph.pos, rowptr=rowptr, sender=np.array(snd, np.int32),
+                   receiver=np.array(rcv, np.int32), evec=np.array(ev, np.float32))
+
+
+def test_tiny_edge_count():
+    # 64 nodes in a 6 A cube, 3 A cutoff, seed 0: the generator's count
+    g = S.make_conv("tiny").graph
+    assert g.n_edges == 1024
+    assert np.all(np.diff(g.rowptr) >= 0) and g.rowptr[-1] == g.n_edges
+
+
+def test_forward_matches_dense_reference(tiny):
+    p = tiny
+    d = desc_of(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    Y = O.sh(1, p.graph.evec)
+    m = O.conv_forward(d, p.graph.rowptr, p.graph.sender, p.x, p.w, evec=p.graph.evec)
+    ref = dense_conv(p.x_irreps, p.y_irreps, p.out_irreps, p.graph, p.x.astype(float),
+                     p.w.astype(float), Y)
+    np.testing.assert_allclose(m, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_forward_lmax3_matches_dense_reference():
+    rng = np.random.default_rng(3)
+    g = S.random_graph(40, 8.0, 4.0, seed=3)
+    x_ir = [(0, 1), (1, -1), (2, 1), (3, -1), (1, 1)]
+    y_ir = S.sh_irreps(3)
+    o_ir = [(0, 1), (1, -1), (2, 1), (3, -1), (1, 1), (2, -1), (0, -1)]
+    C = 3
+    P = len(paths_of(x_ir, y_ir, o_ir))
+    x = rng.standard_normal((g.n_nodes, S.dim(x_ir), C))
+    w = rng.standard_normal((g.n_edges, P, C))
+    d = desc_of(x_ir, y_ir, o_ir, C)
+    assert O.num_paths(d) == P and O.paths(d) == paths_of(x_ir, y_ir, o_ir)
+    m = O.conv_forward(d, g.rowptr, g.sender, x, w, evec=g.evec)
+    ref = dense_conv(x_ir, y_ir, o_ir, g, x, w, O.sh(3, g.evec))
+    np.testing.assert_allclose(m, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_scalar_path_is_a_weighted_spmv():
+    # (0e x 0e -> 0e), C channels: m_b = sum_e w_e x_sender  (CSR mat-vec)
+    rng = np.random.default_rng(1)
+    g = S.random_graph(200, 10.0, 3.0, seed=1)
+    C = 5
+    x = rng.standard_normal((g.n_nodes, 1, C))
+    w = rng.standard_normal((g.n_edges, 1, C))
+    d = desc_of([(0, 1)], [(0, 1)], [(0, 1)], C)
+    m = O.conv_forward(d, g.rowptr, g.sender, x, w, evec=g.evec)
+    for q in range(C):
+        A = sps.csr_matrix((w[:, 0, q], g.sender, g.rowptr), shape=(g.n_nodes, g.n_nodes))
+        np.testing.assert_allclose(m[:, 0, q], A @ x[:, 0, q], rtol=1e-12, atol=1e-12)
+
+
+def test_scalar_features_give_a_filter_of_harmonics():
+    # x scalar: m_b^(L) = sum_a w_{ab,L} x_a Y_L(r_ab)   (paths (0, L, L) are identities)
+    rng = np.random.default_rng(2)
+    g = S.random_graph(60, 8.0, 4.0, seed=2)
+    C = 4
+    o_ir = S.sh_irreps(3)
+    x = rng.standard_normal((g.n_nodes, 1, C))
+    w = rng.standard_normal((g.n_edges, 4, C))
+    d = desc_of([(0, 1)], S.sh_irreps(3), o_ir, C)
+    m = O.conv_forward(d, g.rowptr, g.sender, x, w, evec=g.evec)
+    Y = O.sh(3, g.evec)
+    ref = np.zeros_like(m)
+    for e in range(g.n_edges):
+        a, b = g.sender[e], g.receiver[e]
+        for L in range(4):
+            sl = slice(L * L, (L + 1) * (L + 1))
+            ref[b, sl, :] += w[e, L] * x[a, 0] * Y[e, sl, None]
+    np.testing.assert_allclose(m, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_given_harmonics_equal_vector_mode(tiny):
+    p = tiny
+    d = desc_of(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    Y = O.sh(1, p.graph.evec)
+    a = O.conv_forward(d, p.graph.rowptr, p.graph.sender, p.x, p.w, evec=p.graph.evec)
+    b = O.conv_forward(d, p.graph.rowptr, p.graph.sender, p.x, p.w, Y=Y)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-15)
+
+
+def test_trilinearity(tiny):
+    p = tiny
+    rng = np.random.default_rng(4)
+    d = desc_of(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    g = p.graph
+    Y = O.sh(1, g.evec)
+    f = lambda x, w, Y: O.conv_forward(d, g.rowptr, g.sender, x, w, Y=Y)
+    x1, x2 = rng.standard_normal((2,) + p.x.shape)
+    w1, w2 = rng.standard_normal((2,) + p.w.shape)
+    Y1, Y2 = rng.standard_normal((2,) + Y.shape)
+    a, b = 0.7, -1.3
+    np.testing.assert_allclose(f(a * x1 + b * x2, w1, Y1), a * f(x1, w1, Y1) + b * f(x2, w1, Y1), atol=1e-12)
+    np.testing.assert_allclose(f(x1, a * w1 + b * w2, Y1), a * f(x1, w1, Y1) + b * f(x1, w2, Y1), atol=1e-12)
+    np.testing.assert_allclose(f(x1, w1, a * Y1 + b * Y2), a * f(x1, w1, Y1) + b * f(x1, w1, Y2), atol=1e-12)
+
+
+def test_padding_edges_are_no_ops(tiny):
+    p = tiny
+    rng = np.random.default_rng(5)
+    gp = with_padding(p.graph)
+    real = gp.sender >= 0
+    wp = rng.standard_normal((gp.n_edges,) + p.w.shape[1:]) * 100
+    wp[real] = p.w
+    d = desc_of(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    m0 = O.conv_forward(d, p.graph.rowptr, p.graph.sender, p.x, p.w, evec=p.graph.evec)
+    m1 = O.conv_forward(d, gp.rowptr, gp.sender, p.x, wp, evec=gp.evec)
+    np.testing.assert_allclose(m1, m0, rtol=1e-13, atol=1e-13)
+    dm = rng.standard_normal(m0.shape)
+    dx0 = O.conv_backward_dx(d, p.graph.rowptr, p.graph.sender, p.w, dm, evec=p.graph.evec)
+    dx1 = O.conv_backward_dx(d, gp.rowptr, gp.sender, wp, dm, evec=gp.evec)
+    np.testing.assert_allclose(dx1, dx0, rtol=1e-13, atol=1e-13)
+    dw, dY = O.conv_backward_edge(d, gp.rowptr, gp.sender, p.x, wp, dm, evec=gp.evec)
+    assert np.all(dw[~real] == 0) and np.all(dY[~real] == 0)
+    dw0, dY0 = O.conv_backward_edge(d, p.graph.rowptr, p.graph.sender, p.x, p.w, dm,
+                                    evec=p.graph.evec)
+    np.testing.assert_allclose(dw[real], dw0, atol=1e-13)
+    np.testing.assert_allclose(dY[real], dY0, atol=1e-13)
+
+
+def test_isolated_and_hub_receivers():
+    # node 0 receives nothing, node 1 receives from everybody (a hub)
+    rng = np.random.default_rng(6)
+    n, C = 30, 2
+    snd = np.array([a for a in range(n) if a != 1], np.int32)
+    rowptr = np.zeros(n + 1, np.int32)
+    rowptr[2:] = len(snd)
+    ev = rng.standard_normal((len(snd), 3))
+    x_ir, y_ir, o_ir = [(0, 1), (1, -1)], S.sh_irreps(2), [(0, 1), (1, -1), (2, 1)]
+    d = desc_of(x_ir, y_ir, o_ir, C)
+    x = rng.standard_normal((n, 4, C))
+    w = rng.standard_normal((len(snd), O.num_paths(d), C))
+    m = O.conv_forward(d, rowptr, snd, x, w, evec=ev)
+    assert np.all(m[0] == 0) and np.all(m[2:] == 0) and np.abs(m[1]).max() > 0
+    g = S.Graph(pos=None, rowptr=rowptr, sender=snd, receiver=np.full(len(snd), 1, np.int32),
+                evec=ev.astype(np.float32))
+    ref = dense_conv(x_ir, y_ir, o_ir, g, x, w, O.sh(2, ev))
+    np.testing.assert_allclose(m, ref, atol=1e-12)
+
+
+def _rot(rng):
+    q, r = np.linalg.qr(rng.standard_normal((3, 3)))
+    q = q @ np.diag(np.sign(np.diag(r)))
+    if np.linalg.det(q) < 0:
+        q[:, 0] = -q[:, 0]
+    return q
+
+
+def _dmat(l, R, rng):
+    P = rng.standard_normal((4 * (2 * l + 1) + 8, 3))
+    A = O.sh(3, P)[:, l * l:(l + 1) ** 2]
+    B = O.sh(3, P @ R.T)[:, l * l:(l + 1) ** 2]
+    return np.linalg.lstsq(A, B, rcond=None)[0].T
+
+
+def _block_rotate(irreps, R, rng, feat):
+    out = np.empty_like(feat)
+    o = 0
+    for l, _ in irreps:
+        D = _dmat(l, R, rng)
+        out[:, o:o + 2 * l + 1] = np.einsum("ij,njq->niq", D, feat[:, o:o + 2 * l + 1])
+        o += 2 * l + 1
+    return out
+
+
+def test_rotation_equivariance():
+    rng = np.random.default_rng(7)
+    g = S.random_graph(50, 7.0, 3.5, seed=7)
+    x_ir = [(0, 1), (1, -1), (2, 1), (3, -1)]
+    y_ir, o_ir = S.sh_irreps(3), [(0, 1), (1, -1), (2, 1), (3, -1)]
+    C = 3
+    d = desc_of(x_ir, y_ir, o_ir, C)
+    x = rng.standard_normal((g.n_nodes, 16, C))
+    w = rng.standard_normal((g.n_edges, O.num_paths(d), C))
+    R = _rot(rng)
+    m = O.conv_forward(d, g.rowptr, g.sender, x, w, evec=g.evec.astype(float))
+    mr = O.conv_forward(d, g.rowptr, g.sender, _block_rotate(x_ir, R, rng, x), w,
+                        evec=g.evec.astype(float) @ R.T)
+    np.testing.assert_allclose(mr, _block_rotate(o_ir, R, rng, m), atol=1e-11)
+
+
+def test_inversion_parity():
+    # pos -> -pos flips r; x^(l,p) -> p x; then m^(L,p) -> p m
+    rng = np.random.default_rng(8)
+    g = S.random_graph(50, 7.0, 3.5, seed=8)
+    x_ir = [(0, 1), (1, -1), (1, 1), (2, 1)]
+    o_ir = [(0, 1), (0, -1), (1, -1), (1, 1), (2, 1), (3, -1)]
+    C = 2
+    d = desc_of(x_ir, S.sh_irreps(3), o_ir, C)
+    x = rng.standard_normal((g.n_nodes, S.dim(x_ir), C))
+    w = rng.standard_normal((g.n_edges, O.num_paths(d), C))
+    sx = np.concatenate([[p] * (2 * l + 1) for l, p in x_ir])[None, :, None]
+    so = np.concatenate([[p] * (2 * l + 1) for l, p in o_ir])[None, :, None]
+    m = O.conv_forward(d, g.rowptr, g.sender, x, w, evec=g.evec)
+    mi = O.conv_forward(d, g.rowptr, g.sender, sx * x, w, evec=-g.evec)
+    np.testing.assert_allclose(mi, so * m, atol=1e-12)
+
+
+def test_tensor_product_is_conv_on_identity_graph():
+    rng = np.random.default_rng(9)
+    B, C = 37, 4
+    x_ir, y_ir = [(0, 1), (1, -1), (2, 1)], S.sh_irreps(3)
+    o_ir = [(0, 1), (1, -1), (2, 1), (3, -1)]
+    d = desc_of(x_ir, y_ir, o_ir, C)
+    assert O.num_paths(d) == 17
+    x = rng.standard_normal((B, 9, C))
+    y = rng.standard_normal((B, 16))
+    w = rng.standard_normal((B, 17, C))
+    z = O.tp_forward(d, x, y, w)
+    ident = np.arange(B, dtype=np.int32)
+    m = O.conv_forward(d, np.arange(B + 1, dtype=np.int32), ident, x, w, Y=y)
+    np.testing.assert_allclose(z, m, rtol=1e-13, atol=1e-13)
+    zs = O.tp_forward(d, x, y, w, rows=[5, 0, 36])
+    np.testing.assert_allclose(zs, z[[5, 0, 36]], rtol=0, atol=0)
+
+
+def _bwd_all(d, g, x, w, dm, Y):
+    dx = O.conv_backward_dx(d, g.rowptr, g.sender, w, dm, Y=Y)
+    dw, dY = O.conv_backward_edge(d, g.rowptr, g.sender, x, w, dm, Y=Y)
+    return dx, dw, dY
+
+
+@pytest.fixture(scope="module")
+def bwd_case():
+    rng = np.random.default_rng(10)
+    g = S.random_graph(45, 7.0, 3.5, seed=10)
+    x_ir = [(0, 1), (1, -1), (2, 1)]
+    y_ir = S.sh_irreps(3)
+    o_ir = [(0, 1), (1, -1), (2, 1), (3, -1)]
+    C = 3
+    d = desc_of(x_ir, y_ir, o_ir, C)
+    x = rng.standard_normal((g.n_nodes, 9, C))
+    w = rng.standard_normal((g.n_edges, O.num_paths(d), C))
+    Y = O.sh(3, g.evec)
+    dm = rng.standard_normal((g.n_nodes, 16, C))
+    return d, g, x, w, Y, dm, rng
+
+
+def test_vjp_adjoint_identity(bwd_case):
+    # m is linear in each input, so <dx, t> = <dm, m(t, w, Y)> for any t, etc.
+    d, g, x, w, Y, dm, rng = bwd_case
+    f = lambda x, w, Y: O.conv_forward(d, g.rowptr, g.sender, x, w, Y=Y)
+    dx, dw, dY = _bwd_all(d, g, x, w, dm, Y)
+    tx, tw, tY = rng.standard_normal(x.shape), rng.standard_normal(w.shape), rng.standard_normal(Y.shape)
+    assert np.vdot(dx, tx) == pytest.approx(np.vdot(dm, f(tx, w, Y)), rel=1e-12)
+    assert np.vdot(dw, tw) == pytest.approx(np.vdot(dm, f(x, tw, Y)), rel=1e-12)
+    assert np.vdot(dY, tY) == pytest.approx(np.vdot(dm, f(x, w, tY)), rel=1e-12)
+
+
+def test_euler_identity(bwd_case):
+    # for a trilinear map, <dm, m> = <dx, x> = <dw, w> = <dY, Y>
+    d, g, x, w, Y, dm, _ = bwd_case
+    m = O.conv_forward(d, g.rowptr, g.sender, x, w, Y=Y)
+    dx, dw, dY = _bwd_all(d, g, x, w, dm, Y)
+    ref = np.vdot(dm, m)
+    for v in (np.vdot(dx, x), np.vdot(dw, w), np.vdot(dY, Y)):
+        assert v == pytest.approx(ref, rel=1e-12)
+
+
+def test_central_finite_differences(bwd_case):
+    d, g, x, w, Y, dm, rng = bwd_case
+    loss = lambda x, w, Y: np.vdot(dm, O.conv_forward(d, g.rowptr, g.sender, x, w, Y=Y))
+    dx, dw, dY = _bwd_all(d, g, x, w, dm, Y)
+    h = 1e-4
+    for arr, grad, k in ((x, dx, 0), (w, dw, 1), (Y, dY, 2)):
+        for _ in range(4):
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += h
+            am[idx] -= h
+            args_p = [x, w, Y]
+            args_m = [x, w, Y]
+            args_p[k], args_m[k] = ap, am
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert fd == pytest.approx(grad[idx], rel=1e-7, abs=1e-9)
+
+
+def test_vector_mode_backward_equals_given_mode(bwd_case):
+    d, g, x, w, Y, dm, _ = bwd_case
+    dx0, dw0, dY0 = _bwd_all(d, g, x, w, dm, Y)
+    dx1 = O.conv_backward_dx(d, g.rowptr, g.sender, w, dm, evec=g.evec)
+    dw1, dY1 = O.conv_backward_edge(d, g.rowptr, g.sender, x, w, dm, evec=g.evec)
+    np.testing.assert_allclose(dx1, dx0, atol=1e-13)
+    np.testing.assert_allclose(dw1, dw0, atol=1e-13)
+    np.testing.assert_allclose(dY1, dY0, atol=1e-13)
+
+
+def test_sampled_rows_equal_full(bwd_case):
+    d, g, x, w, Y, dm, _ = bwd_case
+    rows = np.array([7, 0, 44, 7, 13], np.int32)
+    m = O.conv_forward(d, g.rowptr, g.sender, x, w, Y=Y)
+    np.testing.assert_array_equal(O.conv_forward(d, g.rowptr, g.sender, x, w, Y=Y, rows=rows),
+                                  m[rows])
+    dx, dw, dY = _bwd_all(d, g, x, w, dm, Y)
+    np.testing.assert_allclose(O.conv_backward_dx(d, g.rowptr, g.sender, w, dm, Y=Y, rows=rows),
+                               dx[rows], rtol=0, atol=1e-14)
+    e = np.array([3, g.n_edges - 1, 0], np.int64)
+    dws, dYs = O.conv_backward_edge(d, g.rowptr, g.sender, x, w, dm, Y=Y, edges=e)
+    np.testing.assert_array_equal(dws, dw[e])
+    np.testing.assert_array_equal(dYs, dY[e])
+
+
+def test_rejects_bad_arguments():
+    d = desc_of([(0, 1)], [(1, 1)], [(1, 1)], 1)  # y irrep 1e is not a harmonic parity
+    g = S.random_graph(5, 3.0, 2.0, seed=0)
+    with pytest.raises(ValueError):
+        O.conv_forward(d, g.rowptr, g.sender, np.zeros((5, 1, 1)),
+                       np.zeros((g.n_edges, 1, 1)), evec=g.evec)
+    d2 = desc_of([(0, 1)], [(0, 1)], [(0, 1)], 1)
+    with pytest.raises(ValueError):
+        O.conv_forward(d2, g.rowptr, g.sender, np.zeros((5, 1, 1)),
+                       np.zeros((g.n_edges, 1, 1)), evec=g.evec, rows=[7])
