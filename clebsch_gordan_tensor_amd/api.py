@@ -1,0 +1,280 @@
+"""Thin Python binding of libe3hip.so (include/e3hip.h), via ctypes.
+
+Argument marshalling only: every step of the convolution runs in the HIP
+kernels of the library.  Tensors are torch tensors on the GPU (torch is used
+for device memory and streams); the calls are asynchronous on the current
+torch stream.  The library must have been built (``__graft_entry__.build()``
+or ``python -m clebsch_gordan_tensor_amd.build``); a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+from . import synth
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libe3hip.so")
+_lib = None
+
+E3_F32, E3_BF16 = 0, 1
+E3_Y_GIVEN = 1
+
+
+class E3Error(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"e3hip status {status}: {msg}")
+        self.status = status
+
+
+class _Irrep(C.Structure):
+    _fields_ = [("mul", C.c_int32), ("l", C.c_int32), ("parity", C.c_int32)]
+
+
+class _Irreps(C.Structure):
+    _fields_ = [("n", C.c_int32), ("v", C.POINTER(_Irrep))]
+
+
+class _Desc(C.Structure):
+    _fields_ = [("x", _Irreps), ("y", _Irreps), ("out", _Irreps), ("flags", C.c_int32)]
+
+
+EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
+           "e3_spherical_harmonics", "e3_tp_forward", "e3_conv_forward",
+           "e3_conv_workspace_size", "e3_conv_prepare_transpose", "e3_conv_backward",
+           "e3_last_error"]
+
+
+def lib():
+    """Open libe3hip.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = C.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    dp = C.POINTER(_Desc)
+    L.e3_num_paths.argtypes = [dp, C.POINTER(i32)]
+    L.e3_path_info.argtypes = [dp, i32, C.POINTER(i32), C.POINTER(i32), C.POINTER(i32)]
+    L.e3_supported.argtypes = [dp, C.c_int]
+    L.e3_supported.restype = i32
+    L.e3_cg_block.argtypes = [i32, i32, i32, C.POINTER(C.c_double)]
+    L.e3_spherical_harmonics.argtypes = [i32, i64, vp, vp, vp]
+    L.e3_tp_forward.argtypes = [dp, i64, vp, vp, vp, vp, C.c_int, vp]
+    L.e3_conv_forward.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, C.c_int, vp]
+    L.e3_conv_workspace_size.argtypes = [i32, i32, C.POINTER(sz)]
+    L.e3_conv_prepare_transpose.argtypes = [i32, i32, vp, vp, vp, sz, vp]
+    L.e3_conv_backward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp,
+                                   C.c_int, vp]
+    L.e3_last_error.restype = C.c_char_p
+    for name in EXPORTS:
+        if name != "e3_last_error" and name != "e3_supported":
+            getattr(L, name).restype = C.c_int
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != 0:
+        raise E3Error(status, lib().e3_last_error().decode())
+
+
+@dataclass
+class Desc:
+    """Irreps of x, y (multiplicity 1) and the output, as lists of (l, parity),
+    with C channels on x and the output."""
+    x: list
+    y: list
+    out: list
+    channels: int
+    flags: int = 0
+
+    @classmethod
+    def from_strings(cls, x: str, y: str, out: str, flags: int = 0):
+        C_, xi = synth.parse_irreps(x)
+        _, yi = synth.parse_irreps(y)
+        C2, oi = synth.parse_irreps(out)
+        if C2 != C_:
+            raise ValueError("x and out need the same multiplicity")
+        return cls(xi, yi, oi, C_, flags)
+
+    def with_flags(self, flags):
+        return Desc(self.x, self.y, self.out, self.channels, flags)
+
+    @property
+    def dx(self):
+        return synth.dim(self.x)
+
+    @property
+    def dy(self):
+        return synth.dim(self.y)
+
+    @property
+    def dout(self):
+        return synth.dim(self.out)
+
+    def c(self):
+        """ctypes struct (kept alive together with its arrays)."""
+        def arr(ir, mul):
+            a = (_Irrep * max(1, len(ir)))()
+            for i, (l, p) in enumerate(ir):
+                a[i] = _Irrep(mul, l, p)
+            return a
+        ax, ay, ao = arr(self.x, self.channels), arr(self.y, 1), arr(self.out, self.channels)
+        d = _Desc(_Irreps(len(self.x), ax), _Irreps(len(self.y), ay),
+                  _Irreps(len(self.out), ao), self.flags)
+        d._keep = (ax, ay, ao)
+        return d
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return E3_F32
+    if t.dtype == torch.bfloat16:
+        return E3_BF16
+    raise TypeError(f"unsupported storage dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, shape=None, dtype=None):
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def num_paths(desc: Desc) -> int:
+    n = C.c_int32()
+    _check(lib().e3_num_paths(C.byref(desc.c()), C.byref(n)))
+    return n.value
+
+
+def path_info(desc: Desc, i: int):
+    a, b, c = C.c_int32(), C.c_int32(), C.c_int32()
+    _check(lib().e3_path_info(C.byref(desc.c()), i, C.byref(a), C.byref(b), C.byref(c)))
+    return a.value, b.value, c.value
+
+
+def supported(desc: Desc, dtype_code: int = E3_F32) -> bool:
+    return bool(lib().e3_supported(C.byref(desc.c()), dtype_code))
+
+
+def cg_block(l1: int, l2: int, L: int):
+    import numpy as np
+    out = np.zeros((2 * L + 1) * (2 * l1 + 1) * (2 * l2 + 1))
+    _check(lib().e3_cg_block(l1, l2, L, out.ctypes.data_as(C.POINTER(C.c_double))))
+    return out.reshape(2 * L + 1, 2 * l1 + 1, 2 * l2 + 1)
+
+
+def spherical_harmonics(lmax: int, vec, out=None, stream=None):
+    import torch
+    _need(vec, "vec", dtype=torch.float32)
+    n = vec.shape[0]
+    if out is None:
+        out = torch.empty((n, (lmax + 1) ** 2), device=vec.device, dtype=torch.float32)
+    _need(out, "out", shape=(n, (lmax + 1) ** 2), dtype=torch.float32)
+    _check(lib().e3_spherical_harmonics(lmax, n, _ptr(vec), _ptr(out), _stream(stream)))
+    return out
+
+
+def tp_forward(desc: Desc, x, y, w, out=None, stream=None):
+    import torch
+    B = x.shape[0]
+    P = num_paths(desc)
+    _need(x, "x", shape=(B, desc.dx, desc.channels))
+    _need(y, "y", shape=(B, desc.dy), dtype=torch.float32)
+    _need(w, "w", shape=(B, P, desc.channels), dtype=x.dtype)
+    if out is None:
+        out = torch.empty((B, desc.dout, desc.channels), device=x.device, dtype=x.dtype)
+    _need(out, "out", shape=(B, desc.dout, desc.channels), dtype=x.dtype)
+    _check(lib().e3_tp_forward(C.byref(desc.c()), B, _ptr(x), _ptr(y), _ptr(w), _ptr(out),
+                               _dtype_code(x), _stream(stream)))
+    return out
+
+
+def conv_forward(desc: Desc, rowptr, sender, edge_vec_or_Y, x, w, out=None, stream=None):
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    P = num_paths(desc)
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    ycols = desc.dy if desc.flags & E3_Y_GIVEN else 3
+    _need(edge_vec_or_Y, "edge_vec_or_Y", shape=(E, ycols), dtype=torch.float32)
+    _need(x, "x", shape=(N, desc.dx, desc.channels))
+    _need(w, "w", shape=(E, P, desc.channels), dtype=x.dtype)
+    if out is None:
+        out = torch.empty((N, desc.dout, desc.channels), device=x.device, dtype=x.dtype)
+    _need(out, "out", shape=(N, desc.dout, desc.channels), dtype=x.dtype)
+    _check(lib().e3_conv_forward(C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender),
+                                 _ptr(edge_vec_or_Y), _ptr(x), _ptr(w), _ptr(out),
+                                 _dtype_code(x), _stream(stream)))
+    return out
+
+
+def workspace_size(n_nodes: int, n_edges: int) -> int:
+    b = C.c_size_t()
+    _check(lib().e3_conv_workspace_size(n_nodes, n_edges, C.byref(b)))
+    return b.value
+
+
+def conv_prepare_transpose(rowptr, sender, workspace=None, stream=None):
+    """Build the sender-ordered edge index; returns the workspace (uint8 tensor)."""
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    nb = workspace_size(N, E)
+    if workspace is None:
+        workspace = torch.empty(nb, device=rowptr.device, dtype=torch.uint8)
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    _check(lib().e3_conv_prepare_transpose(N, E, _ptr(rowptr), _ptr(sender), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(stream)))
+    return workspace
+
+
+def conv_backward(desc: Desc, rowptr, sender, workspace, edge_vec_or_Y, x, w, dm,
+                  dx=None, dw=None, dY=None, stream=None):
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    P = num_paths(desc)
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    ycols = desc.dy if desc.flags & E3_Y_GIVEN else 3
+    _need(edge_vec_or_Y, "edge_vec_or_Y", shape=(E, ycols), dtype=torch.float32)
+    _need(x, "x", shape=(N, desc.dx, desc.channels))
+    _need(w, "w", shape=(E, P, desc.channels), dtype=x.dtype)
+    _need(dm, "dm", shape=(N, desc.dout, desc.channels), dtype=x.dtype)
+    dev, dt = x.device, x.dtype
+    if dx is None:
+        dx = torch.empty((N, desc.dx, desc.channels), device=dev, dtype=dt)
+    if dw is None:
+        dw = torch.empty((E, P, desc.channels), device=dev, dtype=dt)
+    if dY is None:
+        dY = torch.empty((E, desc.dy), device=dev, dtype=torch.float32)
+    _need(dx, "dx", shape=(N, desc.dx, desc.channels), dtype=dt)
+    _need(dw, "dw", shape=(E, P, desc.channels), dtype=dt)
+    _need(dY, "dY", shape=(E, desc.dy), dtype=torch.float32)
+    _check(lib().e3_conv_backward(C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _ptr(edge_vec_or_Y), _ptr(x), _ptr(w), _ptr(dm), _ptr(dx),
+                                  _ptr(dw), _ptr(dY), _dtype_code(x), _stream(stream)))
+    return dx, dw, dY

@@ -1,0 +1,284 @@
+// C-ABI entry points (include/e3hip.h): argument checks, signature dispatch
+// and kernel launches.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "e3hip.h"
+#include "host/cg_ladder.h"
+#include "kernels/registry.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+e3_status fail(e3_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+e3_status ok() {
+  g_last_error.clear();
+  return E3_OK;
+}
+
+struct Parsed {
+  int C = 0;
+  std::vector<e3k::IrSpec> x, y, o;
+  int P = 0, dx = 0, dy = 0, dout = 0;
+  std::vector<int> pix, piy, pio;
+};
+
+e3_status parse_list(const e3_irreps& in, const char* what, std::vector<e3k::IrSpec>& out,
+                     std::vector<int>& muls) {
+  if (in.n < 0 || (in.n > 0 && in.v == nullptr))
+    return fail(E3_ERR_IRREPS, std::string(what) + ": bad irreps list");
+  out.clear();
+  for (int i = 0; i < in.n; ++i) {
+    const e3_irrep& r = in.v[i];
+    if (r.l < 0 || r.l > 64 || (r.parity != 1 && r.parity != -1) || r.mul <= 0)
+      return fail(E3_ERR_IRREPS, std::string(what) + ": block " + std::to_string(i) +
+                                     " needs mul > 0, l >= 0, parity +1 or -1");
+    out.push_back({r.l, r.parity});
+    muls.push_back(r.mul);
+  }
+  return E3_OK;
+}
+
+e3_status parse(const e3_desc* d, Parsed& p) {
+  if (!d) return fail(E3_ERR_INVALID_ARG, "desc is null");
+  std::vector<int> mx, my, mo;
+  e3_status s;
+  if ((s = parse_list(d->x, "x", p.x, mx)) != E3_OK) return s;
+  if ((s = parse_list(d->y, "y", p.y, my)) != E3_OK) return s;
+  if ((s = parse_list(d->out, "out", p.o, mo)) != E3_OK) return s;
+  if (p.x.empty() || p.y.empty() || p.o.empty())
+    return fail(E3_ERR_IRREPS, "x, y and out need at least one block each");
+  p.C = mx[0];
+  for (int m : mx)
+    if (m != p.C) return fail(E3_ERR_IRREPS, "x blocks need one multiplicity (channel-wise)");
+  for (int m : mo)
+    if (m != p.C) return fail(E3_ERR_IRREPS, "out blocks need the multiplicity of x");
+  for (int m : my)
+    if (m != 1) return fail(E3_ERR_IRREPS, "y blocks need multiplicity 1");
+  p.dx = p.dy = p.dout = 0;
+  for (auto& r : p.x) p.dx += 2 * r.l + 1;
+  for (auto& r : p.y) p.dy += 2 * r.l + 1;
+  for (auto& r : p.o) p.dout += 2 * r.l + 1;
+  p.pix.clear();
+  p.piy.clear();
+  p.pio.clear();
+  for (size_t i = 0; i < p.x.size(); ++i)
+    for (size_t j = 0; j < p.y.size(); ++j)
+      for (size_t k = 0; k < p.o.size(); ++k) {
+        const int l1 = p.x[i].l, l2 = p.y[j].l, L = p.o[k].l;
+        const int lo = l1 > l2 ? l1 - l2 : l2 - l1;
+        if (lo <= L && L <= l1 + l2 && p.x[i].p * p.y[j].p == p.o[k].p) {
+          p.pix.push_back(int(i));
+          p.piy.push_back(int(j));
+          p.pio.push_back(int(k));
+        }
+      }
+  p.P = int(p.pix.size());
+  return E3_OK;
+}
+
+const e3k::KernelSet* const kSets[] = {&e3k::kSetL1, &e3k::kSetL1to3, &e3k::kSetL2to3,
+                                       &e3k::kSetL3to3};
+
+bool same(const std::vector<e3k::IrSpec>& a, const e3k::IrSpec* b, int nb) {
+  if (int(a.size()) != nb) return false;
+  for (int i = 0; i < nb; ++i)
+    if (a[i].l != b[i].l || a[i].p != b[i].p) return false;
+  return true;
+}
+
+const e3k::KernelSet* find_set(const Parsed& p) {
+  for (const e3k::KernelSet* k : kSets)
+    if (same(p.x, k->x, k->nx) && same(p.y, k->y, k->ny) && same(p.o, k->o, k->no)) return k;
+  return nullptr;
+}
+
+// Lanes per edge group: G = C / cpl must be a power of two in [1, 64].
+int group_lanes(int C, int cpl) {
+  if (C <= 0 || C % cpl) return -1;
+  const int G = C / cpl;
+  if (G > 64 || (G & (G - 1))) return -1;
+  return G;
+}
+
+e3_status select(const Parsed& p, e3_dtype dt, const e3k::KernelSet*& ks, int& G) {
+  if (dt != E3_F32 && dt != E3_BF16) return fail(E3_ERR_INVALID_ARG, "unknown dtype");
+  ks = find_set(p);
+  if (!ks)
+    return fail(E3_ERR_UNSUPPORTED,
+                "no kernel for this irreps signature (supported: x in {0e+1o, 0e+1o+2e, "
+                "0e+1o+2e+3o}, y = harmonics 0e+1o[+2e+3o], out = 0e+1o[+2e+3o])");
+  G = group_lanes(p.C, ks->cpl);
+  if (G < 0)
+    return fail(E3_ERR_UNSUPPORTED, "channel count must be 4 * 2^k with 4 <= C <= 256, got " +
+                                        std::to_string(p.C));
+  return E3_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+e3_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(E3_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+e3_status e3_num_paths(const e3_desc* desc, int32_t* n_paths) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if (!n_paths) return fail(E3_ERR_INVALID_ARG, "n_paths is null");
+  *n_paths = p.P;
+  return ok();
+}
+
+e3_status e3_path_info(const e3_desc* desc, int32_t i, int32_t* ix, int32_t* iy, int32_t* iout) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if (!ix || !iy || !iout) return fail(E3_ERR_INVALID_ARG, "null output pointer");
+  if (i < 0 || i >= p.P) return fail(E3_ERR_INVALID_ARG, "path index out of range");
+  *ix = p.pix[i];
+  *iy = p.piy[i];
+  *iout = p.pio[i];
+  return ok();
+}
+
+int32_t e3_supported(const e3_desc* desc, e3_dtype dtype) {
+  Parsed p;
+  if (parse(desc, p) != E3_OK) return 0;
+  const e3k::KernelSet* ks;
+  int G;
+  return select(p, dtype, ks, G) == E3_OK ? 1 : 0;
+}
+
+e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out) {
+  if (!out) return fail(E3_ERR_INVALID_ARG, "out is null");
+  if (l1 < 0 || l2 < 0 || L < 0 || l1 > 3 || l2 > 3 || L > 3)
+    return fail(E3_ERR_INVALID_ARG, "degrees must be in 0..3");
+  std::vector<double> T;
+  if (!e3::cg_real_block(l1, l2, L, T)) return fail(E3_ERR_INVALID_ARG, "triple does not couple");
+  for (size_t k = 0; k < T.size(); ++k) out[k] = T[k];
+  return ok();
+}
+
+e3_status e3_spherical_harmonics(int32_t lmax, int64_t n, const float* vec, float* Y,
+                                 void* stream) {
+  if (lmax < 0 || lmax > 3) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..3");
+  if (n < 0) return fail(E3_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return ok();
+  if (!vec || !Y) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  return hip_status(e3k::launch_harmonics(lmax, n, vec, Y, hipStream_t(stream)), "harmonics");
+}
+
+e3_status e3_tp_forward(const e3_desc* desc, int64_t n_rows, const void* x, const float* y,
+                        const void* w, void* z, e3_dtype dtype, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  const e3k::KernelSet* ks;
+  int G;
+  if ((s = select(p, dtype, ks, G)) != E3_OK) return s;
+  if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows == 0) return ok();
+  if (!x || !y || !w || !z) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(z))
+    return fail(E3_ERR_ALIGNMENT, "x, w and z must be 16-byte aligned");
+  e3k::TpArgs a{n_rows, p.C, G, x, y, w, z};
+  return hip_status(ks->tp[dtype](a, hipStream_t(stream)), "tp_forward");
+}
+
+e3_status e3_conv_forward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                          const int32_t* rowptr, const int32_t* sender,
+                          const float* edge_vec_or_Y, const void* x, const void* w, void* m,
+                          e3_dtype dtype, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  const e3k::KernelSet* ks;
+  int G;
+  if ((s = select(p, dtype, ks, G)) != E3_OK) return s;
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes == 0) return ok();
+  if (!rowptr || !m || !x) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (n_edges > 0 && (!sender || !edge_vec_or_Y || !w))
+    return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(x) || !aligned16(m) || (n_edges > 0 && !aligned16(w)))
+    return fail(E3_ERR_ALIGNMENT, "x, w and m must be 16-byte aligned");
+  const bool yg = (desc->flags & E3_Y_GIVEN) != 0;
+  e3k::FwdArgs a{n_nodes, n_edges, p.C, G, rowptr, sender, edge_vec_or_Y, x, w, m};
+  return hip_status(ks->fwd[dtype][yg](a, hipStream_t(stream)), "conv_forward");
+}
+
+e3_status e3_conv_workspace_size(int32_t n_nodes, int32_t n_edges, size_t* bytes) {
+  if (!bytes) return fail(E3_ERR_INVALID_ARG, "bytes is null");
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  *bytes = size_t(e3k::transpose_layout(n_nodes, n_edges).total_words) * sizeof(int32_t);
+  return ok();
+}
+
+e3_status e3_conv_prepare_transpose(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                                    const int32_t* sender, void* workspace, size_t ws_bytes,
+                                    void* stream) {
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  size_t need = 0;
+  e3_conv_workspace_size(n_nodes, n_edges, &need);
+  if (!workspace || ws_bytes < need)
+    return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  if (!aligned16(workspace)) return fail(E3_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  if (n_nodes > 0 && !rowptr) return fail(E3_ERR_INVALID_ARG, "rowptr is null");
+  if (n_edges > 0 && !sender) return fail(E3_ERR_INVALID_ARG, "sender is null");
+  return hip_status(e3k::launch_prepare_transpose(n_nodes, n_edges, rowptr, sender,
+                                                  static_cast<int*>(workspace), hipStream_t(stream)),
+                    "prepare_transpose");
+}
+
+e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                           const int32_t* rowptr, const int32_t* sender, const void* workspace,
+                           size_t ws_bytes, const float* edge_vec_or_Y, const void* x,
+                           const void* w, const void* dm, void* dx, void* dw, float* dY,
+                           e3_dtype dtype, void* stream) {
+  (void)rowptr;
+  (void)sender;
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  const e3k::KernelSet* ks;
+  int G;
+  if ((s = select(p, dtype, ks, G)) != E3_OK) return s;
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes == 0) return ok();
+  size_t need = 0;
+  e3_conv_workspace_size(n_nodes, n_edges, &need);
+  if (!workspace || ws_bytes < need)
+    return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  if (!x || !dx || !dm) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (n_edges > 0 && (!edge_vec_or_Y || !w || !dw || !dY))
+    return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(x) || !aligned16(dm) || !aligned16(dx) ||
+      (n_edges > 0 && (!aligned16(w) || !aligned16(dw))))
+    return fail(E3_ERR_ALIGNMENT, "x, w, dm, dx and dw must be 16-byte aligned");
+  const e3k::TransposeLayout L = e3k::transpose_layout(n_nodes, n_edges);
+  const int* ws = static_cast<const int*>(workspace);
+  const bool yg = (desc->flags & E3_Y_GIVEN) != 0;
+  e3k::BwdArgs a{n_nodes, p.C, G, ws + L.colptr, ws + L.perm, ws + L.recv, ws + L.npad,
+                 ws + L.padlist, n_edges, edge_vec_or_Y, x, w, dm, dx, dw, dY};
+  return hip_status(ks->bwd[dtype][yg](a, hipStream_t(stream)), "conv_backward");
+}
+
+const char* e3_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,449 @@
+// Device-side building blocks shared by the gfx950 kernels: compile-time
+// path tables, unrolled per-path contractions, channel-vector loads/stores,
+// the harmonics of an edge vector, and wavefront shuffles.
+//
+// Layouts (all row-major, channels innermost -- the "trailing channels"
+// layout of the e3j paper, E.2.1):
+//   node features   x[n][dx][C],  messages m[n][dout][C]
+//   edge weights    w[e][P][C]    (P paths in canonical order)
+//   harmonics       Y[e][dy]      (shared by all channels)
+// A lane owns CPL consecutive channels; G = C / CPL lanes form an edge group
+// and a 64-lane wavefront holds 64 / G groups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "../generated/cg_table.inc"
+
+namespace e3k {
+
+// ------------------------------------------------------------ signatures
+
+struct Ir {
+  int l, p;
+};
+
+struct PathC {
+  int l1, l2, L;   // degrees of the x, y and output irreps
+  int xo, yo, oo;  // component offsets of those irreps
+  int roff, rcnt;  // records of the real CG block in kRec
+};
+
+template <int N>
+struct PathList {
+  PathC p[N > 0 ? N : 1];
+};
+
+constexpr bool couples(Ir a, Ir b, Ir c) {
+  const int lo = a.l > b.l ? a.l - b.l : b.l - a.l;
+  return lo <= c.l && c.l <= a.l + b.l && a.p * b.p == c.p;
+}
+
+template <class S>
+constexpr int count_paths() {
+  int n = 0;
+  for (int i = 0; i < S::NX; ++i)
+    for (int j = 0; j < S::NY; ++j)
+      for (int k = 0; k < S::NO; ++k) n += couples(S::X[i], S::Y[j], S::O[k]) ? 1 : 0;
+  return n;
+}
+
+template <int N>
+constexpr int dim_of(const Ir (&v)[N]) {
+  int d = 0;
+  for (int i = 0; i < N; ++i) d += 2 * v[i].l + 1;
+  return d;
+}
+
+template <class S>
+constexpr PathList<count_paths<S>()> make_paths() {
+  PathList<count_paths<S>()> r{};
+  int n = 0, xo = 0;
+  for (int i = 0; i < S::NX; ++i) {
+    int yo = 0;
+    for (int j = 0; j < S::NY; ++j) {
+      int oo = 0;
+      for (int k = 0; k < S::NO; ++k) {
+        if (couples(S::X[i], S::Y[j], S::O[k])) {
+          const int l1 = S::X[i].l, l2 = S::Y[j].l, L = S::O[k].l;
+          r.p[n++] = PathC{l1, l2, L, xo, yo, oo, kRecOff[l1][l2][L], kRecCnt[l1][l2][L]};
+        }
+        oo += 2 * S::O[k].l + 1;
+      }
+      yo += 2 * S::Y[j].l + 1;
+    }
+    xo += 2 * S::X[i].l + 1;
+  }
+  return r;
+}
+
+template <class S>
+constexpr bool degrees_supported() {
+  for (int i = 0; i < S::NX; ++i)
+    if (S::X[i].l > kTabLmax) return false;
+  for (int i = 0; i < S::NY; ++i)
+    if (S::Y[i].l > kTabLmax) return false;
+  for (int i = 0; i < S::NO; ++i)
+    if (S::O[i].l > kTabLmax) return false;
+  return true;
+}
+
+template <class S>
+struct Plan {
+  static_assert(degrees_supported<S>(), "irreps above the generated table's degree");
+  static constexpr int DX = dim_of(S::X);
+  static constexpr int DY = dim_of(S::Y);
+  static constexpr int DO = dim_of(S::O);
+  static constexpr int NP = count_paths<S>();
+  static constexpr PathList<NP> paths = make_paths<S>();
+};
+
+// Records of one path are sorted by (M, m1, m2); a "group" is a run of
+// records with the same (M, m1), whose y-coefficients sum to one scalar.
+constexpr bool same_pair(int i, int j) { return kRec[i].M == kRec[j].M && kRec[i].m1 == kRec[j].m1; }
+constexpr bool group_first(int roff, int r) { return r == 0 || !same_pair(roff + r - 1, roff + r); }
+constexpr bool group_last(int roff, int rcnt, int r) {
+  return r == rcnt - 1 || !same_pair(roff + r, roff + r + 1);
+}
+
+// ------------------------------------------------------------- static for
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+template <int B, int E, class F>
+__device__ __forceinline__ void sfor(F&& f) {
+  if constexpr (B < E) {
+    f(ic<B>{});
+    sfor<B + 1, E>(f);
+  }
+}
+
+// -------------------------------------------------------- storage types
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Load CPL consecutive channels starting at p (p aligned to CPL elements).
+template <class T, int CPL>
+__device__ __forceinline__ void load_ch(const T* __restrict__ p, float (&v)[CPL]) {
+  if constexpr (std::is_same_v<T, float>) {
+    static_assert(CPL == 4 || CPL == 2 || CPL == 1, "fp32 channel vector");
+    if constexpr (CPL == 4) {
+      const float4 t = *reinterpret_cast<const float4*>(p);
+      v[0] = t.x;
+      v[1] = t.y;
+      v[2] = t.z;
+      v[3] = t.w;
+    } else if constexpr (CPL == 2) {
+      const float2 t = *reinterpret_cast<const float2*>(p);
+      v[0] = t.x;
+      v[1] = t.y;
+    } else {
+      v[0] = *p;
+    }
+  } else {
+    static_assert(CPL == 4 || CPL == 8, "bf16 channel vector");
+    if constexpr (CPL == 4) {
+      const uint2 t = *reinterpret_cast<const uint2*>(p);
+      v[0] = bf16_to_f32(t.x & 0xFFFFu);
+      v[1] = bf16_to_f32(t.x >> 16);
+      v[2] = bf16_to_f32(t.y & 0xFFFFu);
+      v[3] = bf16_to_f32(t.y >> 16);
+    } else {
+      const uint4 t = *reinterpret_cast<const uint4*>(p);
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+      }
+    }
+  }
+}
+
+template <class T, int CPL>
+__device__ __forceinline__ void store_ch(T* __restrict__ p, const float (&v)[CPL]) {
+  if constexpr (std::is_same_v<T, float>) {
+    if constexpr (CPL == 4) {
+      *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if constexpr (CPL == 2) {
+      *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    } else {
+      *p = v[0];
+    }
+  } else {
+    if constexpr (CPL == 4) {
+      uint2 t;
+      t.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+      t.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      *reinterpret_cast<uint2*>(p) = t;
+    } else {
+      uint4 t;
+      t.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+      t.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      t.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
+      t.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+      *reinterpret_cast<uint4*>(p) = t;
+    }
+  }
+}
+
+// ------------------------------------------------------------- harmonics
+
+// Component-normalised real harmonics of degree l (m = -l..l) of r/|r|,
+// written into out[0..2l].  A zero vector gives 0 for l >= 1.
+template <int L>
+__device__ __forceinline__ void harmonics_l(float x, float y, float z, float* out) {
+  if constexpr (L == 0) {
+    out[0] = 1.0f;
+  } else if constexpr (L == 1) {
+    const float k = 1.7320508075688772f;  // sqrt(3)
+    out[0] = k * y;
+    out[1] = k * z;
+    out[2] = k * x;
+  } else if constexpr (L == 2) {
+    const float k15 = 3.872983346207417f;        // sqrt(15)
+    const float k5h = 1.118033988749895f;        // sqrt(5)/2
+    const float xx = x * x, yy = y * y, zz = z * z;
+    out[0] = k15 * x * y;
+    out[1] = k15 * y * z;
+    out[2] = k5h * (2.0f * zz - xx - yy);
+    out[3] = k15 * x * z;
+    out[4] = 0.5f * k15 * (xx - yy);
+  } else {
+    static_assert(L == 3, "degree above 3");
+    const float a = 2.091650066335189f;   // sqrt(35/8)
+    const float b = 10.246950765959598f;  // sqrt(105)
+    const float c = 1.620185174601965f;   // sqrt(21/8)
+    const float d = 1.3228756555322954f;  // sqrt(7)/2
+    const float xx = x * x, yy = y * y, zz = z * z;
+    const float t = 4.0f * zz - xx - yy;
+    out[0] = a * (3.0f * xx - yy) * y;
+    out[1] = b * x * y * z;
+    out[2] = c * y * t;
+    out[3] = d * z * (2.0f * zz - 3.0f * xx - 3.0f * yy);
+    out[4] = c * x * t;
+    out[5] = 0.5f * b * (xx - yy) * z;
+    out[6] = a * (xx - 3.0f * yy) * x;
+  }
+}
+
+// r / |r| for any finite r: scaled by its largest component first, so that
+// the squared norm lies in [1, 3] (no underflow or overflow); 0 stays 0.
+__device__ __forceinline__ void unit_vector(float& x, float& y, float& z) {
+  const float s = fmaxf(fabsf(x), fmaxf(fabsf(y), fabsf(z)));
+  if (s > 0.0f) {
+    const float is = 1.0f / s;
+    x *= is;
+    y *= is;
+    z *= is;
+    const float inv = rsqrtf(x * x + y * y + z * z);
+    x *= inv;
+    y *= inv;
+    z *= inv;
+  }
+}
+
+template <class S>
+constexpr int y_offset(int j) {
+  int o = 0;
+  for (int i = 0; i < j; ++i) o += 2 * S::Y[i].l + 1;
+  return o;
+}
+
+// y operand of one edge for signature S: harmonics of the edge vector, one
+// bank per y irrep, or a given row Y[e][dy] when YG.
+template <class S, bool YG>
+__device__ __forceinline__ void edge_y(const float* __restrict__ src, int64_t e,
+                                       float (&Y)[Plan<S>::DY]) {
+  constexpr int DY = Plan<S>::DY;
+  if constexpr (YG) {
+    const float* p = src + e * DY;
+#pragma unroll
+    for (int i = 0; i < DY; ++i) Y[i] = p[i];
+  } else {
+    const float* p = src + e * 3;
+    float x = p[0], y = p[1], z = p[2];
+    unit_vector(x, y, z);
+    sfor<0, S::NY>([&](auto j) {
+      constexpr int l = S::Y[j].l;
+      constexpr int off = y_offset<S>(j);
+      float h[2 * l + 1];
+      harmonics_l<l>(x, y, z, h);
+#pragma unroll
+      for (int m = 0; m < 2 * l + 1; ++m) Y[off + m] = h[m];
+    });
+  }
+}
+
+// ------------------------------------------------------------ shuffles
+
+__device__ __forceinline__ float xor_shuffle(float v, int s) { return __shfl_xor(v, s, 64); }
+
+// Sum over the 64/G edge groups of a wavefront (butterfly, fixed order):
+// afterwards every group holds the total.
+template <int N, int CPL>
+__device__ __forceinline__ void reduce_groups(float (&a)[N][CPL], int G) {
+  for (int s = G; s < 64; s <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) a[i][k] += xor_shuffle(a[i][k], s);
+  }
+}
+
+// Sum over the G lanes of one edge group (butterfly, fixed order).
+template <int N>
+__device__ __forceinline__ void reduce_lanes(float (&a)[N], int G) {
+  for (int s = 1; s < G; s <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] += xor_shuffle(a[i], s);
+  }
+}
+
+// ------------------------------------------------- per-edge contractions
+
+// Forward message of one edge added into acc (e3j E.1 Eq.13, with the edge
+// scalar of each path factored out of its CG sum as in E.4):
+//   acc[oo+M][k] += w[P][k] * sum_{m1,m2} c_P(M,m1,m2) Y[yo+m2] x[xo+m1][k]
+// Per path the cheaper order is used: contract then weight (2L+1 products
+// per channel) or weight x first (2l1+1 products per channel).
+template <class S, int CPL>
+__device__ __forceinline__ void edge_forward(const float (&Y)[Plan<S>::DY],
+                                             const float (&xv)[Plan<S>::DX][CPL],
+                                             const float (&wv)[Plan<S>::NP][CPL],
+                                             float (&acc)[Plan<S>::DO][CPL]) {
+  using PL = Plan<S>;
+  sfor<0, PL::NP>([&](auto pi) {
+    constexpr PathC P = PL::paths.p[pi];
+    constexpr int n1 = 2 * P.l1 + 1, nL = 2 * P.L + 1;
+    if constexpr (n1 < nL) {
+      float u[n1][CPL];
+#pragma unroll
+      for (int a = 0; a < n1; ++a)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) u[a][k] = wv[pi][k] * xv[P.xo + a][k];
+      float A = 0.0f;
+      sfor<0, P.rcnt>([&](auto r) {
+        constexpr int i = P.roff + r;
+        constexpr CgRec R = kRec[i];
+        if constexpr (group_first(P.roff, r))
+          A = R.c * Y[P.yo + R.m2];
+        else
+          A = fmaf(R.c, Y[P.yo + R.m2], A);
+        if constexpr (group_last(P.roff, P.rcnt, r)) {
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) acc[P.oo + R.M][k] = fmaf(A, u[R.m1][k], acc[P.oo + R.M][k]);
+        }
+      });
+    } else {
+      float z[nL][CPL];
+#pragma unroll
+      for (int M = 0; M < nL; ++M)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) z[M][k] = 0.0f;
+      float A = 0.0f;
+      sfor<0, P.rcnt>([&](auto r) {
+        constexpr int i = P.roff + r;
+        constexpr CgRec R = kRec[i];
+        if constexpr (group_first(P.roff, r))
+          A = R.c * Y[P.yo + R.m2];
+        else
+          A = fmaf(R.c, Y[P.yo + R.m2], A);
+        if constexpr (group_last(P.roff, P.rcnt, r)) {
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) z[R.M][k] = fmaf(A, xv[P.xo + R.m1][k], z[R.M][k]);
+        }
+      });
+#pragma unroll
+      for (int M = 0; M < nL; ++M)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) acc[P.oo + M][k] = fmaf(wv[pi][k], z[M][k], acc[P.oo + M][k]);
+    }
+  });
+}
+
+// Backward of one edge (e3j E.1 Eq.16 with one scalar per path; the scalar
+// separates from the CG sum as in E.4):
+//   B_P[m1][k]  = sum_{M,m2} c Y[yo+m2] dm[oo+M][k]
+//   dx[xo+m1][k] += w[P][k] B_P[m1][k]
+//   dw[P][k]      = sum_m1 x[xo+m1][k] B_P[m1][k]
+//   dYl[yo+m2]   += sum_{M,m1} c sum_{k in lane} w[P][k] x[xo+m1][k] dm[oo+M][k]
+// dYl holds this lane's partial sums over its own channels.
+template <class S, int CPL>
+__device__ __forceinline__ void edge_backward(const float (&Y)[Plan<S>::DY],
+                                              const float (&xv)[Plan<S>::DX][CPL],
+                                              const float (&wv)[Plan<S>::NP][CPL],
+                                              const float (&dmv)[Plan<S>::DO][CPL],
+                                              float (&dxa)[Plan<S>::DX][CPL],
+                                              float (&dwv)[Plan<S>::NP][CPL],
+                                              float (&dYl)[Plan<S>::DY]) {
+  using PL = Plan<S>;
+  // this edge's dx contribution, summed over paths before it joins the
+  // running per-sender sum (one rounding into the large sum per edge)
+  float t[PL::DX][CPL];
+#pragma unroll
+  for (int i = 0; i < PL::DX; ++i)
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) t[i][k] = 0.0f;
+  sfor<0, PL::NP>([&](auto pi) {
+    constexpr PathC P = PL::paths.p[pi];
+    constexpr int n1 = 2 * P.l1 + 1;
+    float B[n1][CPL], xw[n1][CPL];
+#pragma unroll
+    for (int a = 0; a < n1; ++a)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        B[a][k] = 0.0f;
+        xw[a][k] = wv[pi][k] * xv[P.xo + a][k];
+      }
+    float A = 0.0f, T = 0.0f;
+    sfor<0, P.rcnt>([&](auto r) {
+      constexpr int i = P.roff + r;
+      constexpr CgRec R = kRec[i];
+      constexpr bool first = group_first(P.roff, r);
+      constexpr bool last = group_last(P.roff, P.rcnt, r);
+      if constexpr (first) {
+        A = R.c * Y[P.yo + R.m2];
+        T = xw[R.m1][0] * dmv[P.oo + R.M][0];
+#pragma unroll
+        for (int k = 1; k < CPL; ++k) T = fmaf(xw[R.m1][k], dmv[P.oo + R.M][k], T);
+      } else {
+        A = fmaf(R.c, Y[P.yo + R.m2], A);
+      }
+      dYl[P.yo + R.m2] = fmaf(R.c, T, dYl[P.yo + R.m2]);
+      if constexpr (last) {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) B[R.m1][k] = fmaf(A, dmv[P.oo + R.M][k], B[R.m1][k]);
+      }
+    });
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      float s = 0.0f;
+#pragma unroll
+      for (int a = 0; a < n1; ++a) {
+        t[P.xo + a][k] = fmaf(wv[pi][k], B[a][k], t[P.xo + a][k]);
+        s = fmaf(xv[P.xo + a][k], B[a][k], s);
+      }
+      dwv[pi][k] = s;
+    }
+  });
+#pragma unroll
+  for (int i = 0; i < PL::DX; ++i)
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) dxa[i][k] += t[i][k];
+}
+
+}  // namespace e3k

@@ -1,0 +1,253 @@
+// gfx950 kernels of the fused equivariant convolution and the batched
+// channel-wise tensor product, templated on the irreps signature S, the
+// storage type T (float or bf16) and CPL, the channels held per lane.
+//
+// Work mapping: one 64-lane wavefront per receiver (forward) or per sender
+// (backward).  The wavefront is split into 64/G edge groups of G = C/CPL
+// lanes; group g walks edges g, g + 64/G, ... of the segment, each lane
+// keeping CPL channels of the accumulator in registers.  Segments close with
+// a fixed butterfly over the groups, so results are bitwise reproducible
+// and no float atomics are used (e3j E.3: receiver-stationary aggregation;
+// E.4: segmented reduction keyed on receivers, and on senders for dx).
+#pragma once
+
+#include "common.h"
+#include "registry.h"
+
+namespace e3k {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = 64 * kWavesPerBlock;
+
+// ------------------------------------------------------------- forward
+// m[b] = sum over the CSR segment of b of the weighted CG messages
+// (e3j A.3 Eq.7, E.1 Eq.12-13).  Padding edges (sender < 0) are skipped.
+template <class S, class T, int CPL, bool YG>
+__global__ void __launch_bounds__(kBlock)
+    k_conv_fwd(int n_nodes, int n_edges, int C, int G, const int* __restrict__ rowptr,
+               const int* __restrict__ sender, const float* __restrict__ ysrc,
+               const T* __restrict__ x, const T* __restrict__ w, T* __restrict__ m) {
+  using PL = Plan<S>;
+  const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (b >= n_nodes) return;  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const int NG = 64 / G;
+  const int g = lane / G, c0 = (lane - g * G) * CPL;
+
+  float acc[PL::DO][CPL];
+#pragma unroll
+  for (int i = 0; i < PL::DO; ++i)
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) acc[i][k] = 0.0f;
+
+  // a malformed rowptr cannot move the walk outside [0, n_edges)
+  const int beg = max(rowptr[b], 0), end = min(rowptr[b + 1], n_edges);
+  for (int e = beg + g; e < end; e += NG) {
+    const int a = sender[e];
+    if (a < 0 || a >= n_nodes) continue;  // padding edge
+    float Y[PL::DY];
+    edge_y<S, YG>(ysrc, e, Y);
+    float xv[PL::DX][CPL];
+    const T* xa = x + int64_t(a) * PL::DX * C + c0;
+#pragma unroll
+    for (int i = 0; i < PL::DX; ++i) load_ch<T, CPL>(xa + int64_t(i) * C, xv[i]);
+    float wv[PL::NP][CPL];
+    const T* we = w + int64_t(e) * PL::NP * C + c0;
+#pragma unroll
+    for (int p = 0; p < PL::NP; ++p) load_ch<T, CPL>(we + int64_t(p) * C, wv[p]);
+    edge_forward<S, CPL>(Y, xv, wv, acc);
+  }
+
+  reduce_groups<PL::DO, CPL>(acc, G);
+  T* mb = m + int64_t(b) * PL::DO * C + c0;
+#pragma unroll
+  for (int i = 0; i < PL::DO; ++i)
+    if (i % NG == g) store_ch<T, CPL>(mb + int64_t(i) * C, acc[i]);
+}
+
+// ------------------------------------------------------------ backward
+// Sender-ordered walk over the transposed index (colptr, perm, recv):
+// dx[a] accumulates in registers over a's out-edges; dw[e] and dY[e] are
+// edge-local and written once (e3j E.1 Eq.16; the sender-keyed reduction of
+// E.4 replaces the atomics of E.3).
+template <class S, class T, int CPL, bool YG>
+__global__ void __launch_bounds__(kBlock)
+    k_conv_bwd(int n_nodes, int n_edges, int C, int G, const int* __restrict__ colptr,
+               const int* __restrict__ perm, const int* __restrict__ recv,
+               const float* __restrict__ ysrc, const T* __restrict__ x,
+               const T* __restrict__ w, const T* __restrict__ dm, T* __restrict__ dx,
+               T* __restrict__ dw, float* __restrict__ dY) {
+  using PL = Plan<S>;
+  const int a = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (a >= n_nodes) return;  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const int NG = 64 / G;
+  const int g = lane / G, cl = lane - g * G, c0 = cl * CPL;
+
+  float xv[PL::DX][CPL], dxa[PL::DX][CPL];
+  const T* xa = x + int64_t(a) * PL::DX * C + c0;
+#pragma unroll
+  for (int i = 0; i < PL::DX; ++i) {
+    load_ch<T, CPL>(xa + int64_t(i) * C, xv[i]);
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) dxa[i][k] = 0.0f;
+  }
+
+  // clamped so that a workspace built for another graph stays in bounds
+  const int beg = max(colptr[a], 0), end = min(colptr[a + 1], n_edges);
+  for (int j = beg + g; j < end; j += NG) {
+    const int e = perm[j];
+    const int b = recv[j];
+    if (e < 0 || e >= n_edges || b < 0 || b >= n_nodes) continue;  // only for malformed CSR
+    float Y[PL::DY];
+    edge_y<S, YG>(ysrc, e, Y);
+    float wv[PL::NP][CPL], dmv[PL::DO][CPL];
+    const T* we = w + int64_t(e) * PL::NP * C + c0;
+#pragma unroll
+    for (int p = 0; p < PL::NP; ++p) load_ch<T, CPL>(we + int64_t(p) * C, wv[p]);
+    const T* dmb = dm + int64_t(b) * PL::DO * C + c0;
+#pragma unroll
+    for (int i = 0; i < PL::DO; ++i) load_ch<T, CPL>(dmb + int64_t(i) * C, dmv[i]);
+
+    float dwv[PL::NP][CPL];
+    float dYl[PL::DY];
+#pragma unroll
+    for (int i = 0; i < PL::DY; ++i) dYl[i] = 0.0f;
+    edge_backward<S, CPL>(Y, xv, wv, dmv, dxa, dwv, dYl);
+
+    T* dwe = dw + int64_t(e) * PL::NP * C + c0;
+#pragma unroll
+    for (int p = 0; p < PL::NP; ++p) store_ch<T, CPL>(dwe + int64_t(p) * C, dwv[p]);
+    reduce_lanes<PL::DY>(dYl, G);
+    float* dYe = dY + int64_t(e) * PL::DY;
+#pragma unroll
+    for (int i = 0; i < PL::DY; ++i)
+      if (i % G == cl) dYe[i] = dYl[i];
+  }
+
+  reduce_groups<PL::DX, CPL>(dxa, G);
+  T* dxo = dx + int64_t(a) * PL::DX * C + c0;
+#pragma unroll
+  for (int i = 0; i < PL::DX; ++i)
+    if (i % NG == g) store_ch<T, CPL>(dxo + int64_t(i) * C, dxa[i]);
+}
+
+// Padding edges take no part in the transposed walk; their edge cotangents
+// are zero.  npad and padlist come from the prepare step.
+template <class T>
+__global__ void __launch_bounds__(256)
+    k_zero_padding_edges(const int* __restrict__ npad, const int* __restrict__ padlist,
+                         int n_edges, int row, int dy, T* __restrict__ dw,
+                         float* __restrict__ dY) {
+  const int n = min(*npad, n_edges);
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int64_t e = padlist[i];
+    if (e < 0 || e >= n_edges) continue;
+    for (int k = threadIdx.x; k < row; k += blockDim.x) dw[e * row + k] = T{};
+    for (int k = threadIdx.x; k < dy; k += blockDim.x) dY[e * dy + k] = 0.0f;
+  }
+}
+
+// --------------------------------------------------- batched tensor product
+// z[r] = sum_P w[r][P] (x[r] (x)_CG y[r])_P for independent rows (e3j E.1
+// Eq.10-11); each edge group handles one row.
+template <class S, class T, int CPL>
+__global__ void __launch_bounds__(kBlock)
+    k_tp_fwd(int64_t n_rows, int C, int G, const T* __restrict__ x, const float* __restrict__ y,
+             const T* __restrict__ w, T* __restrict__ z) {
+  using PL = Plan<S>;
+  const int lane = threadIdx.x & 63;
+  const int NG = 64 / G;
+  const int g = lane / G, c0 = (lane - g * G) * CPL;
+  const int64_t row =
+      (int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6)) * NG + g;
+  if (row >= n_rows) return;  // group-uniform; no shuffles follow
+
+  float Y[PL::DY];
+  edge_y<S, true>(y, row, Y);
+  float xv[PL::DX][CPL];
+  const T* xr = x + row * PL::DX * C + c0;
+#pragma unroll
+  for (int i = 0; i < PL::DX; ++i) load_ch<T, CPL>(xr + int64_t(i) * C, xv[i]);
+  float wv[PL::NP][CPL];
+  const T* wr = w + row * PL::NP * C + c0;
+#pragma unroll
+  for (int p = 0; p < PL::NP; ++p) load_ch<T, CPL>(wr + int64_t(p) * C, wv[p]);
+  float acc[PL::DO][CPL];
+#pragma unroll
+  for (int i = 0; i < PL::DO; ++i)
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) acc[i][k] = 0.0f;
+  edge_forward<S, CPL>(Y, xv, wv, acc);
+  T* zr = z + row * PL::DO * C + c0;
+#pragma unroll
+  for (int i = 0; i < PL::DO; ++i) store_ch<T, CPL>(zr + int64_t(i) * C, acc[i]);
+}
+
+// ------------------------------------------------------------ launchers
+
+inline unsigned blocks_for(int64_t waves) {
+  return unsigned((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+}
+
+template <class S, class T, int CPL, bool YG>
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
+  if (a.n_nodes <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_conv_fwd<S, T, CPL, YG>), dim3(blocks_for(a.n_nodes)), dim3(kBlock), 0, s,
+                     a.n_nodes, a.n_edges, a.C, a.G, a.rowptr, a.sender, a.ysrc,
+                     static_cast<const T*>(a.x), static_cast<const T*>(a.w),
+                     static_cast<T*>(a.m));
+  return hipGetLastError();
+}
+
+template <class S, class T, int CPL, bool YG>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
+  if (a.n_nodes <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_conv_bwd<S, T, CPL, YG>), dim3(blocks_for(a.n_nodes)), dim3(kBlock), 0, s,
+                     a.n_nodes, int(a.n_edges), a.C, a.G, a.colptr, a.perm, a.recv, a.ysrc,
+                     static_cast<const T*>(a.x), static_cast<const T*>(a.w),
+                     static_cast<const T*>(a.dm), static_cast<T*>(a.dx), static_cast<T*>(a.dw),
+                     a.dY);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.n_edges <= 0) return err;
+  hipLaunchKernelGGL((k_zero_padding_edges<T>), dim3(256), dim3(256), 0, s, a.npad, a.padlist,
+                     int(a.n_edges), Plan<S>::NP * a.C, Plan<S>::DY, static_cast<T*>(a.dw), a.dY);
+  return hipGetLastError();
+}
+
+template <class S, class T, int CPL>
+hipError_t launch_tp(const TpArgs& a, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  const int64_t groups_per_wave = 64 / a.G;
+  const int64_t waves = (a.n_rows + groups_per_wave - 1) / groups_per_wave;
+  hipLaunchKernelGGL((k_tp_fwd<S, T, CPL>), dim3(blocks_for(waves)), dim3(kBlock), 0, s, a.n_rows,
+                     a.C, a.G, static_cast<const T*>(a.x), a.y, static_cast<const T*>(a.w),
+                     static_cast<T*>(a.z));
+  return hipGetLastError();
+}
+
+template <class S, int CPL>
+KernelSet make_set(const char* name) {
+  KernelSet k{};
+  k.name = name;
+  k.nx = S::NX;
+  k.ny = S::NY;
+  k.no = S::NO;
+  for (int i = 0; i < S::NX; ++i) k.x[i] = IrSpec{S::X[i].l, S::X[i].p};
+  for (int i = 0; i < S::NY; ++i) k.y[i] = IrSpec{S::Y[i].l, S::Y[i].p};
+  for (int i = 0; i < S::NO; ++i) k.o[i] = IrSpec{S::O[i].l, S::O[i].p};
+  k.cpl = CPL;
+  k.fwd[0][0] = &launch_fwd<S, float, CPL, false>;
+  k.fwd[0][1] = &launch_fwd<S, float, CPL, true>;
+  k.fwd[1][0] = &launch_fwd<S, bf16_t, CPL, false>;
+  k.fwd[1][1] = &launch_fwd<S, bf16_t, CPL, true>;
+  k.bwd[0][0] = &launch_bwd<S, float, CPL, false>;
+  k.bwd[0][1] = &launch_bwd<S, float, CPL, true>;
+  k.bwd[1][0] = &launch_bwd<S, bf16_t, CPL, false>;
+  k.bwd[1][1] = &launch_bwd<S, bf16_t, CPL, true>;
+  k.tp[0] = &launch_tp<S, float, CPL>;
+  k.tp[1] = &launch_tp<S, bf16_t, CPL>;
+  return k;
+}
+
+}  // namespace e3k

@@ -1,0 +1,81 @@
+// Host-visible table of the specialised kernels: one KernelSet per irreps
+// signature, holding launchers for every storage type and y mode.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace e3k {
+
+struct FwdArgs {
+  int n_nodes, n_edges, C, G;
+  const int* rowptr;
+  const int* sender;
+  const float* ysrc;  // edge vectors [E][3] or harmonics [E][dy]
+  const void* x;
+  const void* w;
+  void* m;
+};
+
+struct BwdArgs {
+  int n_nodes, C, G;
+  const int* colptr;
+  const int* perm;
+  const int* recv;
+  const int* npad;
+  const int* padlist;
+  int64_t n_edges;
+  const float* ysrc;
+  const void* x;
+  const void* w;
+  const void* dm;
+  void* dx;
+  void* dw;
+  float* dY;
+};
+
+struct TpArgs {
+  int64_t n_rows;
+  int C, G;
+  const void* x;
+  const float* y;
+  const void* w;
+  void* z;
+};
+
+using FwdFn = hipError_t (*)(const FwdArgs&, hipStream_t);
+using BwdFn = hipError_t (*)(const BwdArgs&, hipStream_t);
+using TpFn = hipError_t (*)(const TpArgs&, hipStream_t);
+
+struct IrSpec {
+  int l, p;
+};
+
+struct KernelSet {
+  const char* name;
+  int nx, ny, no;
+  IrSpec x[4], y[4], o[4];
+  int cpl;            // channels per lane
+  FwdFn fwd[2][2];    // [dtype: 0 f32, 1 bf16][y given]
+  BwdFn bwd[2][2];
+  TpFn tp[2];
+};
+
+extern const KernelSet kSetL1;
+extern const KernelSet kSetL1to3;
+extern const KernelSet kSetL2to3;
+extern const KernelSet kSetL3to3;
+
+// Prepare-transpose and harmonics launchers (prep.hip).
+hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr, const int* sender,
+                                    int* ws, hipStream_t s);
+hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hipStream_t s);
+
+// Workspace layout of the transposed edge index (int32 words).
+struct TransposeLayout {
+  int64_t npad, colptr, cursor, tmp_e, tmp_b, perm, recv, padlist, bsum, total_words;
+};
+TransposeLayout transpose_layout(int64_t n_nodes, int64_t n_edges);
+
+}  // namespace e3k

@@ -1,0 +1,42 @@
+// Irreps signatures (x, y, output) with specialised, fully unrolled kernels.
+// Every x and output irrep carries the same multiplicity C (channel-wise
+// product); y is the harmonic bank (multiplicity 1).  Parities: e = +1, o = -1.
+#pragma once
+
+#include "common.h"
+
+namespace e3k {
+
+// 0e+1o (x) Y_0..1 -> 0e+1o
+struct SigL1 {
+  static constexpr int NX = 2, NY = 2, NO = 2;
+  static constexpr Ir X[NX] = {{0, 1}, {1, -1}};
+  static constexpr Ir Y[NY] = {{0, 1}, {1, -1}};
+  static constexpr Ir O[NO] = {{0, 1}, {1, -1}};
+};
+
+// 0e+1o (x) Y_0..3 -> 0e+1o+2e+3o   (MACE-like interaction, 10 paths)
+struct SigL1to3 {
+  static constexpr int NX = 2, NY = 4, NO = 4;
+  static constexpr Ir X[NX] = {{0, 1}, {1, -1}};
+  static constexpr Ir Y[NY] = {{0, 1}, {1, -1}, {2, 1}, {3, -1}};
+  static constexpr Ir O[NO] = {{0, 1}, {1, -1}, {2, 1}, {3, -1}};
+};
+
+// 0e+1o+2e (x) Y_0..3 -> 0e+1o+2e+3o   (17 paths)
+struct SigL2to3 {
+  static constexpr int NX = 3, NY = 4, NO = 4;
+  static constexpr Ir X[NX] = {{0, 1}, {1, -1}, {2, 1}};
+  static constexpr Ir Y[NY] = {{0, 1}, {1, -1}, {2, 1}, {3, -1}};
+  static constexpr Ir O[NO] = {{0, 1}, {1, -1}, {2, 1}, {3, -1}};
+};
+
+// 0e+1o+2e+3o (x) Y_0..3 -> 0e+1o+2e+3o   (23 paths)
+struct SigL3to3 {
+  static constexpr int NX = 4, NY = 4, NO = 4;
+  static constexpr Ir X[NX] = {{0, 1}, {1, -1}, {2, 1}, {3, -1}};
+  static constexpr Ir Y[NY] = {{0, 1}, {1, -1}, {2, 1}, {3, -1}};
+  static constexpr Ir O[NO] = {{0, 1}, {1, -1}, {2, 1}, {3, -1}};
+};
+
+}  // namespace e3k

@@ -175,6 +175,29 @@ def radius_graph(pos: np.ndarray, cutoff: float) -> Graph:
                  receiver=rcv.astype(np.int32), evec=evec)
 
 
+def subgraph(g: Graph, ids):
+    """Edges ids of g (kept in receiver order) as a CSR over all g's nodes:
+    (rowptr, sender, evec, sorted ids).  Used to hand a sample of a large
+    graph to a checker."""
+    ids = np.sort(np.asarray(ids, dtype=np.int64))
+    counts = np.bincount(g.receiver[ids], minlength=g.n_nodes)
+    rowptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return rowptr, g.sender[ids], g.evec[ids], ids
+
+
+def edges_of_receivers(g: Graph, recv):
+    """Sub-graph with the in-edges of the given receivers."""
+    recv = np.unique(np.asarray(recv))
+    ids = (np.concatenate([np.arange(g.rowptr[b], g.rowptr[b + 1]) for b in recv])
+           if len(recv) else np.zeros(0, np.int64))
+    return subgraph(g, ids)
+
+
+def edges_of_senders(g: Graph, snd):
+    """Sub-graph with the out-edges of the given senders."""
+    return subgraph(g, np.nonzero(np.isin(g.sender, np.asarray(snd)))[0])
+
+
 def random_graph(n_nodes: int, box: float, cutoff: float, seed: int,
                  permute_labels: bool = False) -> Graph:
     """Uniform positions in [0, box)^3 from PCG64(seed); optional random

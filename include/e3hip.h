@@ -1,0 +1,161 @@
+/*
+ * e3hip.h -- C ABI of the MI355X (gfx950) fused equivariant convolution.
+ *
+ * The library computes, on one AMD GPU, the hot path of E(3)-equivariant
+ * message passing described in "e3j: An Efficient and Open-Source Backend for
+ * Euclidean Equivariant Operations on GPU and TPU" (arXiv html version):
+ *
+ *   harmonics of edge vectors            (A.3 Eq.4, G.1)
+ *   channel-wise Clebsch-Gordan product  (A.3 Eq.6, E.1 Eq.10)
+ *   per-edge, per-path scalar weighting  (E.1 Eq.11)
+ *   receiver segment sum                 (A.3 Eq.7, E.1 Eq.12-13)
+ *   its vector-Jacobian product          (E.1 Eq.16)
+ *
+ * Conventions
+ *   - An irreps list is a sequence of (l, parity) blocks; a block of degree l
+ *     has 2l+1 components ordered m = -l..l.  Every x and output block has the
+ *     same multiplicity C (channel-wise product); y has multiplicity 1.
+ *   - Harmonics are real and component-normalised: sum_m Y_lm(r)^2 = 2l+1,
+ *     with Y_1 = sqrt(3) (y, z, x) / |r|.
+ *   - Coupling coefficients: Condon-Shortley CG moved to the real harmonic
+ *     basis (a real block for l1+l2+L even, the imaginary part for odd).
+ *   - Paths: for every x block, then every y block, then every output block,
+ *     keep (x, y, out) when |l_x - l_y| <= l_out <= l_x + l_y and
+ *     p_x p_y = p_out (parity rule, B.1).  Each path has its own weight per
+ *     edge and channel; paths landing on the same output block are summed
+ *     after weighting ("collapsed" output, one copy of each output block).
+ *   - Layouts (row-major, channels innermost):
+ *       x, dx      [rows][dx][C]       (dx = sum over x blocks of 2l+1)
+ *       w, dw      [rows][P][C]        (P paths in the order above)
+ *       m, dm, z   [rows][dout][C]
+ *       y, Y, dY   [rows][dy]          (float32 always)
+ *       edge_vec   [E][3]              (float32, r_e = pos[receiver] - pos[sender])
+ *   - Graph: CSR by receiver.  rowptr[N+1] (rowptr[0] = 0, non-decreasing,
+ *     rowptr[N] = E); sender[E]; edges of receiver b are
+ *     rowptr[b] .. rowptr[b+1]-1.  A sender outside [0, N) marks a padding
+ *     edge (the e3j paper, 3.1.2): it contributes nothing and its dw and dY
+ *     are zero.
+ *
+ * Memory and streams
+ *   - Every array argument is a DEVICE pointer unless stated otherwise; the
+ *     caller owns all of them.  x, w, m, dm, dx, dw must be 16-byte aligned.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise the host.  No call allocates device
+ *     memory; the backward pass takes its index from a caller-owned workspace.
+ *   - Outputs are fully overwritten; inputs are never modified.
+ *   - Results are bitwise reproducible for the same inputs and device (no
+ *     floating-point atomics).
+ *
+ * Errors
+ *   - Every entry point returns an e3_status; E3_OK is 0.  On failure
+ *     nothing is launched and e3_last_error() describes the problem.
+ *     HIP launch errors come back as E3_ERR_HIP.
+ *   - Supported signatures (irreps triples) are reported by e3_supported().
+ */
+#ifndef E3HIP_H
+#define E3HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  E3_OK = 0,
+  E3_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad lmax */
+  E3_ERR_IRREPS = -2,      /* malformed irreps (l < 0, parity not +-1, mixed multiplicities) */
+  E3_ERR_UNSUPPORTED = -3, /* signature or channel count without a kernel */
+  E3_ERR_ALIGNMENT = -4,   /* feature pointer not 16-byte aligned */
+  E3_ERR_WORKSPACE = -6,   /* workspace missing or too small */
+  E3_ERR_HIP = -7          /* the HIP runtime reported an error */
+} e3_status;
+
+typedef enum { E3_F32 = 0, E3_BF16 = 1 } e3_dtype; /* storage; arithmetic is fp32 */
+
+typedef struct {
+  int32_t mul;    /* multiplicity (channels); 1 for y */
+  int32_t l;      /* degree */
+  int32_t parity; /* +1 even, -1 odd */
+} e3_irrep;
+
+typedef struct {
+  int32_t n;          /* number of blocks */
+  const e3_irrep* v;  /* HOST pointer to n blocks */
+} e3_irreps;
+
+enum {
+  E3_Y_GIVEN = 1 /* conv: edge_vec_or_Y holds harmonics Y[E][dy], not vectors */
+};
+
+typedef struct {
+  e3_irreps x, y, out;
+  int32_t flags;
+} e3_desc;
+
+/* Number of paths P of a descriptor (host only, no GPU work). */
+e3_status e3_num_paths(const e3_desc* desc, int32_t* n_paths);
+
+/* Indices into x, y, out of path i (host only). */
+e3_status e3_path_info(const e3_desc* desc, int32_t i, int32_t* ix, int32_t* iy, int32_t* iout);
+
+/* 1 if the descriptor, storage type and channel count have a kernel. */
+int32_t e3_supported(const e3_desc* desc, e3_dtype dtype);
+
+/* Real coupling block T[M][m1][m2] of (l1, l2, L), l <= 3, written to the
+ * HOST array out[(2L+1)(2l1+1)(2l2+1)] (the table the kernels are built
+ * from; e3j G.2 construction). */
+e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out);
+
+/* Harmonics Y[n][(lmax+1)^2] of vec[n][3] (e3j A.3 Eq.4), lmax <= 3. */
+e3_status e3_spherical_harmonics(int32_t lmax, int64_t n, const float* vec, float* Y,
+                                 void* stream);
+
+/* Batched channel-wise tensor product (e3j E.1 Eq.10-11) over n_rows
+ * independent rows:  z[r] = sum_P w[r][P] (x[r] (x) y[r])_P.
+ * x [n][dx][C], y [n][dy] float32, w [n][P][C], z [n][dout][C]. */
+e3_status e3_tp_forward(const e3_desc* desc, int64_t n_rows, const void* x, const float* y,
+                        const void* w, void* z, e3_dtype dtype, void* stream);
+
+/* Fused convolution forward (e3j A.3 Eq.7, E.1 Eq.12-13):
+ *   m[b] = sum_{e in row b} sum_P w[e][P] (x[sender[e]] (x) Y(r_e))_P.
+ * edge_vec_or_Y: edge vectors [E][3], or Y [E][dy] with E3_Y_GIVEN.
+ * Receivers without edges get m = 0. */
+e3_status e3_conv_forward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                          const int32_t* rowptr, const int32_t* sender,
+                          const float* edge_vec_or_Y, const void* x, const void* w, void* m,
+                          e3_dtype dtype, void* stream);
+
+/* Size in bytes of the workspace that holds the sender-ordered edge index. */
+e3_status e3_conv_workspace_size(int32_t n_nodes, int32_t n_edges, size_t* bytes);
+
+/* Build the sender-ordered (transposed) edge index of a graph into the
+ * workspace: a counting sort by sender, stable in edge id (the sender-keyed
+ * traversal of the e3j backward, E.4).  Once per graph; the backward pass
+ * reads it.  ws_bytes must be >= e3_conv_workspace_size(). */
+e3_status e3_conv_prepare_transpose(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                                    const int32_t* sender, void* workspace, size_t ws_bytes,
+                                    void* stream);
+
+/* Fused convolution backward (e3j E.1 Eq.16 with one scalar per path):
+ *   dx[a]  = sum_{e: sender(e)=a} sum_P w[e][P] (Y(r_e) (x)^T dm[recv(e)])_P
+ *   dw[e][P] = sum_M (x[sender] (x) Y(r_e))_P[M] dm[recv(e)][M]
+ *   dY[e]  = sum_channels sum_P w[e][P] (x[sender] (x)^T dm[recv(e)])_P
+ * dm is the cotangent of m.  workspace: from e3_conv_prepare_transpose on the
+ * same graph.  dY is float32 [E][dy]; with E3_Y_GIVEN it is the cotangent of
+ * the given Y, otherwise of the harmonics of the edge vectors. */
+e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                           const int32_t* rowptr, const int32_t* sender, const void* workspace,
+                           size_t ws_bytes, const float* edge_vec_or_Y, const void* x,
+                           const void* w, const void* dm, void* dx, void* dw, float* dY,
+                           e3_dtype dtype, void* stream);
+
+/* Text of the last error on this thread ("" if none). */
+const char* e3_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* E3HIP_H */

@@ -1,0 +1,132 @@
+"""CPU checks of the C-ABI library: it loads without a GPU, exports every
+symbol that include/e3hip.h declares, enumerates paths like the oracle, its
+host CG table (ladder construction) equals the oracle's Racah table, and its
+argument checks return the documented status codes before any GPU work."""
+import ctypes as C
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+from clebsch_gordan_tensor_amd import api
+from clebsch_gordan_tensor_amd import synth as S
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return api.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "e3hip.h")).read()
+    names = set(re.findall(r"^\s*(?:e3_status|int32_t|const char\*)\s+(e3_\w+)\s*\(", hdr, re.M))
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(api.EXPORTS) == names
+
+
+SIGNATURES = [
+    ("8x0e+8x1o", 1, "8x0e+8x1o"),
+    ("128x0e+128x1o", 3, "128x0e+128x1o+128x2e+128x3o"),
+    ("128x0e+128x1o+128x2e", 3, "128x0e+128x1o+128x2e+128x3o"),
+    ("64x0e+64x1o+64x2e+64x3o", 3, "64x0e+64x1o+64x2e+64x3o"),
+    ("4x1e+4x0o+4x2o", 2, "4x0e+4x1o+4x1e+4x2e+4x3o"),
+]
+
+
+@pytest.mark.parametrize("xs,lmax,os_", SIGNATURES)
+def test_paths_match_oracle(lib, xs, lmax, os_):
+    C_, xi = S.parse_irreps(xs)
+    _, oi = S.parse_irreps(os_)
+    yi = S.sh_irreps(lmax)
+    d = api.Desc(xi, yi, oi, C_)
+    od = O.Desc(xi, yi, oi, C_)
+    assert api.num_paths(d) == O.num_paths(od) == S.num_paths(xi, yi, oi)
+    assert [api.path_info(d, i) for i in range(api.num_paths(d))] == O.paths(od)
+
+
+def test_expected_path_counts():
+    counts = {"tiny": 4, "water3k": 10, "mace64k": 10, "ho20k": 23}
+    for name, n in counts.items():
+        cfg = S.CONV_CONFIGS[name]
+        C_, xi = S.parse_irreps(cfg["x"])
+        _, oi = S.parse_irreps(cfg["out"])
+        assert S.num_paths(xi, S.sh_irreps(cfg["lmax"]), oi) == n
+    C_, xi = S.parse_irreps(S.TP_CONFIG["x"])
+    _, oi = S.parse_irreps(S.TP_CONFIG["out"])
+    assert S.num_paths(xi, S.sh_irreps(3), oi) == 17
+
+
+def test_host_cg_table_equals_oracle(lib):
+    # two independent constructions: ladder operators (library) and Racah (oracle)
+    for l1, l2 in itertools.product(range(4), repeat=2):
+        for L in range(abs(l1 - l2), min(l1 + l2, 3) + 1):
+            np.testing.assert_allclose(api.cg_block(l1, l2, L), O.cg_real(l1, l2, L),
+                                       atol=1e-12, err_msg=str((l1, l2, L)))
+
+
+def test_supported_signatures(lib):
+    for xs, lmax, os_ in SIGNATURES[:4]:
+        d = api.Desc.from_strings(xs, "+".join(f"{l}{'e' if l % 2 == 0 else 'o'}"
+                                               for l in range(lmax + 1)), os_)
+        assert api.supported(d, api.E3_F32) and api.supported(d, api.E3_BF16)
+    d = api.Desc.from_strings(*SIGNATURES[4][::2][:1], "0e+1o+2e", SIGNATURES[4][2])
+    assert not api.supported(d)
+    # channel counts: 4 * 2^k up to 256
+    for C_, ok in ((4, True), (8, True), (96, False), (256, True), (512, False), (6, False)):
+        d = api.Desc([(0, 1), (1, -1)], [(0, 1), (1, -1)], [(0, 1), (1, -1)], C_)
+        assert api.supported(d) == ok, C_
+
+
+def _desc_c(d):
+    return C.byref(d.c())
+
+
+def test_error_codes(lib):
+    good = api.Desc([(0, 1), (1, -1)], [(0, 1), (1, -1)], [(0, 1), (1, -1)], 8)
+    n = C.c_int32()
+    assert lib.e3_num_paths(None, C.byref(n)) == -1
+    bad_l = api.Desc([(-1, 1)], [(0, 1)], [(0, 1)], 8)
+    assert lib.e3_num_paths(_desc_c(bad_l), C.byref(n)) == -2
+    bad_p = api.Desc([(0, 0)], [(0, 1)], [(0, 1)], 8)
+    assert lib.e3_num_paths(_desc_c(bad_p), C.byref(n)) == -2
+    # mixed multiplicities
+    dc = good.c()
+    dc.out.v[1].mul = 4
+    assert lib.e3_num_paths(C.byref(dc), C.byref(n)) == -2
+    assert lib.e3_path_info(_desc_c(good), 99, C.byref(n), C.byref(n), C.byref(n)) == -1
+    # unsupported signature: rejected before any launch
+    uns = api.Desc([(0, 1), (2, -1)], [(0, 1)], [(0, 1)], 8)
+    assert lib.e3_conv_forward(_desc_c(uns), 4, 4, None, None, None, None, None, None, 0, None) == -3
+    # negative sizes, null pointers, misalignment, empty problems
+    assert lib.e3_conv_forward(_desc_c(good), -1, 0, None, None, None, None, None, None, 0, None) == -1
+    assert lib.e3_conv_forward(_desc_c(good), 0, 0, None, None, None, None, None, None, 0, None) == 0
+    assert lib.e3_conv_forward(_desc_c(good), 4, 4, None, None, None, None, None, None, 0, None) == -1
+    fake = C.c_void_p(0x10000)
+    odd = C.c_void_p(0x10004)
+    assert lib.e3_conv_forward(_desc_c(good), 4, 4, fake, fake, fake, odd, fake, fake, 0,
+                               None) == -4
+    assert lib.e3_conv_forward(_desc_c(good), 4, 4, fake, fake, fake, fake, fake, fake, 7,
+                               None) == -1  # unknown dtype
+    assert lib.e3_tp_forward(_desc_c(good), 0, None, None, None, None, 0, None) == 0
+    assert lib.e3_tp_forward(_desc_c(good), -2, None, None, None, None, 0, None) == -1
+    assert lib.e3_spherical_harmonics(4, 10, fake, fake, None) == -1
+    assert lib.e3_spherical_harmonics(2, 0, None, None, None) == 0
+    sz = C.c_size_t()
+    assert lib.e3_conv_workspace_size(10, 100, C.byref(sz)) == 0
+    need = sz.value
+    assert need >= 4 * (5 * 100 + 2 * 11)
+    assert lib.e3_conv_prepare_transpose(10, 100, fake, fake, fake, need - 1, None) == -6
+    assert lib.e3_conv_prepare_transpose(10, 100, fake, fake, None, need, None) == -6
+    assert lib.e3_conv_backward(_desc_c(good), 10, 100, fake, fake, fake, need - 4, fake, fake,
+                                fake, fake, fake, fake, fake, 0, None) == -6
+    assert "workspace" in lib.e3_last_error().decode()
+    out = np.zeros(10)
+    assert lib.e3_cg_block(1, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
+    assert lib.e3_cg_block(4, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1

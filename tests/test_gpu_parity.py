@@ -1,0 +1,351 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerance (per output tensor): max|gpu - oracle| / RMS(oracle) <= 1e-5 for
+fp32 storage and <= 2e-2 for bf16 storage with fp32 accumulation.  Small
+cases compare every element; the full-size workloads (the launch
+configuration the benchmark times) compare sampled rows that the oracle
+computes one by one.  For bf16 the oracle reads the bf16-rounded inputs.
+"""
+import numpy as np
+import pytest
+
+from clebsch_gordan_tensor_amd import synth as S
+from oracle import oracle as O
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, dev, edges_of_receivers,
+                            edges_of_senders, host, subgraph)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    from clebsch_gordan_tensor_amd import api
+    api.lib()  # raises if the library was not built
+    return api
+
+
+def desc_pair(xi, yi, oi, C, flags=0):
+    from clebsch_gordan_tensor_amd import api
+    return api.Desc(xi, yi, oi, C, flags), O.Desc(xi, yi, oi, C)
+
+
+def run_conv(gpu, d, g, x, w, dm, dtype="f32", Y=None):
+    """Forward + prepare + backward on the GPU; returns host arrays."""
+    rowptr, sender = dev(g.rowptr), dev(g.sender)
+    ysrc = dev(Y.astype(np.float32)) if Y is not None else dev(g.evec)
+    xd, wd, dmd = dev(x, dtype), dev(w, dtype), dev(dm, dtype)
+    m = gpu.conv_forward(d, rowptr, sender, ysrc, xd, wd)
+    ws = gpu.conv_prepare_transpose(rowptr, sender)
+    dx, dw, dY = gpu.conv_backward(d, rowptr, sender, ws, ysrc, xd, wd, dmd)
+    torch.cuda.synchronize()
+    return host(m), host(dx), host(dw), host(dY)
+
+
+def oracle_all(od, g, x, w, dm, Y=None):
+    kw = dict(Y=Y) if Y is not None else dict(evec=g.evec)
+    m = O.conv_forward(od, g.rowptr, g.sender, x, w, **kw)
+    dx = O.conv_backward_dx(od, g.rowptr, g.sender, w, dm, **kw)
+    dw, dY = O.conv_backward_edge(od, g.rowptr, g.sender, x, w, dm, **kw)
+    return m, dx, dw, dY
+
+
+def check_all(got, ref, tol, name):
+    # in bf16 mode m, dx and dw are stored in bf16 (dY is always fp32)
+    bf = tol == TOL_BF16
+    for k, a, b in zip(("m", "dx", "dw", "dY"), got, ref):
+        assert_close(a, b, tol, f"{name}:{k}", bf16_out=bf and k != "dY")
+
+
+# ------------------------------------------------------------------ harmonics
+
+def test_harmonics_kernel(gpu):
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal((1000, 3)).astype(np.float32)
+    v[0] = 0.0
+    v[1] = [0, 0, 1e-20]     # |r|^2 below the fp32 normal range
+    v[2] = [3e19, -2e19, 1e19]  # |r|^2 above the fp32 range
+    for lmax in range(4):
+        Y = host(gpu.spherical_harmonics(lmax, dev(v)))
+        ref = O.sh(lmax, v.astype(np.float64))
+        assert np.abs(Y - ref).max() < 5e-6
+
+
+# ------------------------------------------------------------ tiny, full check
+
+def test_tiny_config_full(gpu):
+    p = S.make_conv("tiny")
+    d, od = desc_pair(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    got = run_conv(gpu, d, p.graph, p.x, p.w, p.dm)
+    ref = oracle_all(od, p.graph, p.x, p.w, p.dm)
+    check_all(got, ref, TOL_F32, "tiny")
+
+
+def _random_problem(xi, yi, oi, C, n, box, rc, seed, pad=0, dtype="f32"):
+    rng = np.random.default_rng(seed)
+    g = S.random_graph(n, box, rc, seed)
+    if pad:
+        from tests.test_oracle_conv import with_padding
+        g = with_padding(g, pad, seed)
+    P = S.num_paths(xi, yi, oi)
+    x = rng.standard_normal((n, S.dim(xi), C)).astype(np.float32)
+    w = rng.standard_normal((g.n_edges, P, C)).astype(np.float32)
+    dm = rng.standard_normal((n, S.dim(oi), C)).astype(np.float32)
+    if dtype == "bf16":
+        x, w, dm = S.round_bf16(x), S.round_bf16(w), S.round_bf16(dm)
+    return g, x, w, dm
+
+
+SIGS = {
+    "L1": ("0e+1o", 1, "0e+1o"),
+    "L1to3": ("0e+1o", 3, "0e+1o+2e+3o"),
+    "L2to3": ("0e+1o+2e", 3, "0e+1o+2e+3o"),
+    "L3to3": ("0e+1o+2e+3o", 3, "0e+1o+2e+3o"),
+}
+
+
+def _irreps(s):
+    return S.parse_irreps(s)[1]
+
+
+@pytest.mark.parametrize("sig", list(SIGS))
+@pytest.mark.parametrize("C", [4, 8, 32, 128])
+def test_signatures_and_channel_counts(gpu, sig, C):
+    xs, lmax, os_ = SIGS[sig]
+    xi, yi, oi = _irreps(xs), S.sh_irreps(lmax), _irreps(os_)
+    g, x, w, dm = _random_problem(xi, yi, oi, C, 70, 8.0, 3.8, seed=C + len(sig))
+    d, od = desc_pair(xi, yi, oi, C)
+    got = run_conv(gpu, d, g, x, w, dm)
+    ref = oracle_all(od, g, x, w, dm)
+    check_all(got, ref, TOL_F32, f"{sig}/C{C}")
+
+
+@pytest.mark.parametrize("sig", list(SIGS))
+def test_bf16_storage(gpu, sig):
+    xs, lmax, os_ = SIGS[sig]
+    xi, yi, oi = _irreps(xs), S.sh_irreps(lmax), _irreps(os_)
+    C = 64
+    g, x, w, dm = _random_problem(xi, yi, oi, C, 60, 8.0, 3.8, seed=5, dtype="bf16")
+    d, od = desc_pair(xi, yi, oi, C)
+    got = run_conv(gpu, d, g, x, w, dm, dtype="bf16")
+    ref = oracle_all(od, g, x, w, dm)
+    check_all(got, ref, TOL_BF16, f"{sig}/bf16")
+
+
+def test_channel_count_256(gpu):
+    xi, yi, oi = _irreps("0e+1o"), S.sh_irreps(3), _irreps("0e+1o+2e+3o")
+    g, x, w, dm = _random_problem(xi, yi, oi, 256, 40, 7.0, 3.5, seed=11)
+    d, od = desc_pair(xi, yi, oi, 256)
+    check_all(run_conv(gpu, d, g, x, w, dm), oracle_all(od, g, x, w, dm), TOL_F32, "C256")
+
+
+def test_padding_edges_and_empty_receivers(gpu):
+    xi, yi, oi = _irreps("0e+1o"), S.sh_irreps(3), _irreps("0e+1o+2e+3o")
+    g, x, w, dm = _random_problem(xi, yi, oi, 16, 80, 12.0, 3.0, seed=2, pad=3)
+    assert (np.diff(g.rowptr) == 3).any()  # some receivers have only padding
+    d, od = desc_pair(xi, yi, oi, 16)
+    got = run_conv(gpu, d, g, x, w, dm)
+    ref = oracle_all(od, g, x, w, dm)
+    check_all(got, ref, TOL_F32, "padding")
+    pad = g.sender < 0
+    assert np.all(got[2][pad] == 0) and np.all(got[3][pad] == 0)
+
+
+def test_hub_receiver_and_isolated_nodes(gpu):
+    rng = np.random.default_rng(3)
+    n, C = 3000, 32
+    snd = np.array([a for a in range(n) if a != 1], np.int32)  # node 1 receives from all
+    rowptr = np.zeros(n + 1, np.int32)
+    rowptr[2:] = len(snd)
+    ev = rng.standard_normal((len(snd), 3)).astype(np.float32)
+    g = S.Graph(pos=None, rowptr=rowptr, sender=snd, receiver=np.full(len(snd), 1, np.int32),
+                evec=ev)
+    xi, yi, oi = _irreps("0e+1o"), S.sh_irreps(3), _irreps("0e+1o+2e+3o")
+    x = rng.standard_normal((n, 4, C)).astype(np.float32)
+    w = rng.standard_normal((len(snd), 10, C)).astype(np.float32)
+    dm = rng.standard_normal((n, 16, C)).astype(np.float32)
+    d, od = desc_pair(xi, yi, oi, C)
+    got = run_conv(gpu, d, g, x, w, dm)
+    ref = oracle_all(od, g, x, w, dm)
+    # only node 1 receives: compare it against its own RMS
+    assert_close(got[0][1], ref[0][1], TOL_F32, "hub:m")
+    assert np.all(got[0][0] == 0) and np.all(got[0][2:] == 0)
+    check_all((got[0][1:2],) + tuple(got[1:]), (ref[0][1:2],) + tuple(ref[1:]), TOL_F32, "hub")
+
+
+def test_empty_graph(gpu):
+    n, C = 5, 8
+    xi, yi, oi = _irreps("0e+1o"), S.sh_irreps(1), _irreps("0e+1o")
+    g = S.Graph(pos=None, rowptr=np.zeros(n + 1, np.int32), sender=np.zeros(0, np.int32),
+                receiver=np.zeros(0, np.int32), evec=np.zeros((0, 3), np.float32))
+    d, _ = desc_pair(xi, yi, oi, C)
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((n, 4, C)).astype(np.float32)
+    m, dx, dw, dY = run_conv(gpu, d, g, x, np.zeros((0, 4, C), np.float32),
+                             rng.standard_normal((n, 4, C)).astype(np.float32))
+    assert np.all(m == 0) and np.all(dx == 0) and dw.size == 0 and dY.size == 0
+
+
+def test_given_harmonics_mode(gpu):
+    from clebsch_gordan_tensor_amd import api
+    xi, yi, oi = _irreps("0e+1o+2e"), S.sh_irreps(3), _irreps("0e+1o+2e+3o")
+    g, x, w, dm = _random_problem(xi, yi, oi, 16, 60, 8.0, 3.8, seed=6)
+    rng = np.random.default_rng(6)
+    Y = rng.standard_normal((g.n_edges, 16))  # any y works in this mode
+    d = api.Desc(xi, yi, oi, 16, api.E3_Y_GIVEN)
+    od = O.Desc(xi, yi, oi, 16)
+    got = run_conv(gpu, d, g, x, w, dm, Y=Y)
+    ref = oracle_all(od, g, x, w, dm, Y=Y.astype(np.float32).astype(np.float64))
+    check_all(got, ref, TOL_F32, "Y given")
+
+
+def test_determinism_bitwise(gpu):
+    p = S.make_conv("water3k")
+    d, _ = desc_pair(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    a = run_conv(gpu, d, p.graph, p.x, p.w, p.dm)
+    b = run_conv(gpu, d, p.graph, p.x, p.w, p.dm)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32))
+
+
+def test_transpose_index(gpu):
+    from clebsch_gordan_tensor_amd import api
+    g = S.random_graph(500, 12.0, 3.5, seed=8)
+    from tests.test_oracle_conv import with_padding
+    g = with_padding(g, 1, 8)
+    ws = api.conv_prepare_transpose(dev(g.rowptr), dev(g.sender))
+    torch.cuda.synchronize()
+    words = ws.view(torch.int32).cpu().numpy()
+    # layout: npad at 0, colptr at 64, the rest follows (see transpose_layout)
+    up = lambda v: (v + 63) // 64 * 64
+    N, E = g.n_nodes, g.n_edges
+    colptr = words[64:64 + N + 1]
+    o = 64 + 2 * up(N + 1)
+    perm = words[o + 2 * up(E): o + 2 * up(E) + E]
+    recv = words[o + 3 * up(E): o + 3 * up(E) + E]
+    real = np.nonzero(g.sender >= 0)[0]
+    order = real[np.lexsort((real, g.sender[real]))]  # by sender, stable in edge id
+    assert words[0] == (g.sender < 0).sum()
+    assert colptr[-1] == len(real)
+    assert np.array_equal(perm[:len(real)], order)
+    assert np.array_equal(recv[:len(real)], g.receiver[order])
+    assert np.array_equal(colptr, np.concatenate([[0], np.cumsum(np.bincount(g.sender[real], minlength=N))]))
+
+
+# ---------------------------------------------------- tensor product (rows)
+
+def _tp_check(gpu, rows, sample=None):
+    p = S.make_tp(rows=rows)
+    from clebsch_gordan_tensor_amd import api
+    d = api.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    od = O.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    yd = gpu.spherical_harmonics(3, dev(p.u))
+    z = gpu.tp_forward(d, dev(p.x), yd, dev(p.w))
+    torch.cuda.synchronize()
+    idx = np.arange(rows) if sample is None else sample
+    y_or = O.sh(3, p.u[idx].astype(np.float64))
+    ref = O.tp_forward(od, p.x[idx], y_or, p.w[idx])
+    assert_close(host(z)[idx], ref, TOL_F32, f"tp{rows}")
+
+
+def test_tp_ragged(gpu):
+    _tp_check(gpu, 4099)
+
+
+def test_tp_full_size_sampled(gpu):
+    rng = np.random.default_rng(0)
+    _tp_check(gpu, S.TP_CONFIG["rows"], sample=np.sort(rng.choice(S.TP_CONFIG["rows"], 2000, replace=False)))
+
+
+def test_tp_equals_conv_on_identity_graph(gpu):
+    from clebsch_gordan_tensor_amd import api
+    xi, yi, oi = _irreps("0e+1o+2e"), S.sh_irreps(3), _irreps("0e+1o+2e+3o")
+    rng = np.random.default_rng(9)
+    B, C = 777, 128
+    x = rng.standard_normal((B, 9, C)).astype(np.float32)
+    y = rng.standard_normal((B, 16)).astype(np.float32)
+    w = rng.standard_normal((B, 17, C)).astype(np.float32)
+    d = api.Desc(xi, yi, oi, C, api.E3_Y_GIVEN)
+    ident = dev(np.arange(B, dtype=np.int32))
+    z = gpu.tp_forward(d, dev(x), dev(y), dev(w))
+    m = gpu.conv_forward(d, dev(np.arange(B + 1, dtype=np.int32)), ident, dev(y), dev(x), dev(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(z), host(m))
+
+
+# ----------------------------------------------- full-size workloads, sampled
+
+def _sampled_conv_check(gpu, p, tol, n_nodes_sample=192, n_edges_sample=384):
+    g = p.graph
+    dtype = p.dtype
+    d, od = desc_pair(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    m, dx, dw, dY = run_conv(gpu, d, g, p.x, p.w, p.dm, dtype=dtype)
+    rng = np.random.default_rng(123)
+    nodes = np.sort(rng.choice(g.n_nodes, n_nodes_sample, replace=False))
+    edges = np.sort(rng.choice(g.n_edges, n_edges_sample, replace=False))
+    x64 = p.x.astype(np.float64)
+    # forward: in-edges of the sampled receivers
+    rp, sn, ev, ids = edges_of_receivers(g, nodes)
+    ref_m = O.conv_forward(od, rp, sn, x64, p.w[ids], evec=ev, rows=nodes)
+    bf = p.dtype == "bf16"
+    assert_close(m[nodes], ref_m, tol, f"{p.name}:m", bf16_out=bf)
+    # backward, node cotangent: out-edges of the sampled senders
+    rp, sn, ev, ids = edges_of_senders(g, nodes)
+    ref_dx = O.conv_backward_dx(od, rp, sn, p.w[ids], p.dm, evec=ev, rows=nodes)
+    assert_close(dx[nodes], ref_dx, tol, f"{p.name}:dx", bf16_out=bf)
+    # backward, edge cotangents
+    rp, sn, ev, ids = subgraph(g, edges)
+    ref_dw, ref_dY = O.conv_backward_edge(od, rp, sn, x64, p.w[ids], p.dm, evec=ev)
+    assert_close(dw[edges], ref_dw, tol, f"{p.name}:dw", bf16_out=bf)
+    assert_close(dY[edges], ref_dY, tol, f"{p.name}:dY")
+
+
+def test_water3k_full(gpu):
+    p = S.make_conv("water3k")
+    d, od = desc_pair(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    got = run_conv(gpu, d, p.graph, p.x, p.w, p.dm)
+    ref = oracle_all(od, p.graph, p.x, p.w, p.dm)
+    check_all(got, ref, TOL_F32, "water3k")
+
+
+def test_mace64k_sampled(gpu):
+    _sampled_conv_check(gpu, S.make_conv("mace64k"), TOL_F32)
+
+
+def test_ho20k_bf16_sampled(gpu):
+    _sampled_conv_check(gpu, S.make_conv("ho20k"), TOL_BF16)
+
+
+# ------------------------------------------------------------ equivariance
+
+def test_gpu_rotation_equivariance(gpu):
+    """m(R r, D x) = D m(r, x) for the GPU outputs, to 1e-5 of the RMS."""
+    from tests.test_oracle_conv import _block_rotate, _rot
+    xi, yi, oi = _irreps("0e+1o"), S.sh_irreps(3), _irreps("0e+1o+2e+3o")
+    g, x, w, dm = _random_problem(xi, yi, oi, 32, 200, 12.0, 4.0, seed=12)
+    rng = np.random.default_rng(12)
+    R = _rot(rng)
+    d, _ = desc_pair(xi, yi, oi, 32)
+    m = run_conv(gpu, d, g, x, w, dm)[0]
+    xr = _block_rotate(xi, R, np.random.default_rng(1), x.astype(np.float64)).astype(np.float32)
+    gr = S.Graph(pos=None, rowptr=g.rowptr, sender=g.sender, receiver=g.receiver,
+                 evec=(g.evec.astype(np.float64) @ R.T).astype(np.float32))
+    mr = run_conv(gpu, d, gr, xr, w, dm)[0]
+    ref = _block_rotate(oi, R, np.random.default_rng(2), m.astype(np.float64))
+    assert_close(mr, ref, TOL_F32, "equivariance")
+
+
+# ------------------------------------------------------------------ errors
+
+def test_unsupported_signature_is_rejected(gpu):
+    from clebsch_gordan_tensor_amd import api
+    d = api.Desc(_irreps("0e+2o"), S.sh_irreps(1), _irreps("0e"), 8)
+    assert not api.supported(d)
+    x = dev(np.zeros((3, 6, 8), np.float32))
+    with pytest.raises(api.E3Error) as ei:
+        api.conv_forward(d, dev(np.zeros(4, np.int32)), dev(np.zeros(0, np.int32)),
+                         dev(np.zeros((0, 3), np.float32)), x, dev(np.zeros((0, 1, 8), np.float32)))
+    assert ei.value.status == -3
