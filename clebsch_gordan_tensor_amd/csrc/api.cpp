@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
@@ -102,7 +103,8 @@ const e3k::KernelSet* find_set(const Parsed& p) {
   return nullptr;
 }
 
-// Lanes per edge group: G = C / cpl must be a power of two in [1, 64].
+// Lanes per edge group for cpl channels per lane: G = C / cpl must be a
+// power of two in [1, 64].
 int group_lanes(int C, int cpl) {
   if (C <= 0 || C % cpl) return -1;
   const int G = C / cpl;
@@ -110,18 +112,44 @@ int group_lanes(int C, int cpl) {
   return G;
 }
 
-e3_status select(const Parsed& p, e3_dtype dt, const e3k::KernelSet*& ks, int& G) {
+enum class Kind { fwd, bwd, tp };
+
+// Channels per lane: the backward keeps two per lane (one edge per
+// wavefront at C = 128, half the registers of four), the forward and the
+// tensor product four (two edges or rows per wavefront).  Overridable with
+// E3HIP_FWD_CPL / E3HIP_BWD_CPL (2 or 4) for tuning.
+int preferred_cpl(Kind k) {
+  static const int fwd = [] {
+    const char* e = std::getenv("E3HIP_FWD_CPL");
+    return (e && std::atoi(e) == 2) ? 2 : 4;
+  }();
+  static const int bwd = [] {
+    const char* e = std::getenv("E3HIP_BWD_CPL");
+    return (e && std::atoi(e) == 4) ? 4 : 2;
+  }();
+  return k == Kind::fwd ? fwd : k == Kind::bwd ? bwd : 4;
+}
+
+e3_status select(const Parsed& p, e3_dtype dt, Kind kind, const e3k::KernelSet*& ks, int& G,
+                 int& cpl_idx) {
   if (dt != E3_F32 && dt != E3_BF16) return fail(E3_ERR_INVALID_ARG, "unknown dtype");
   ks = find_set(p);
   if (!ks)
     return fail(E3_ERR_UNSUPPORTED,
                 "no kernel for this irreps signature (supported: x in {0e+1o, 0e+1o+2e, "
                 "0e+1o+2e+3o}, y = harmonics 0e+1o[+2e+3o], out = 0e+1o[+2e+3o])");
-  G = group_lanes(p.C, ks->cpl);
-  if (G < 0)
-    return fail(E3_ERR_UNSUPPORTED, "channel count must be 4 * 2^k with 4 <= C <= 256, got " +
-                                        std::to_string(p.C));
-  return E3_OK;
+  const int pref = preferred_cpl(kind);
+  const int alt = kind == Kind::tp ? 4 : (pref == 2 ? 4 : 2);
+  for (int cpl : {pref, alt}) {
+    G = group_lanes(p.C, cpl);
+    if (G > 0) {
+      cpl_idx = cpl == 2 ? 0 : 1;
+      return E3_OK;
+    }
+  }
+  return fail(E3_ERR_UNSUPPORTED,
+              "channel count must be a power of two, 2 <= C <= 256 (4 <= C for the tensor "
+              "product), got " + std::to_string(p.C));
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -161,8 +189,11 @@ int32_t e3_supported(const e3_desc* desc, e3_dtype dtype) {
   Parsed p;
   if (parse(desc, p) != E3_OK) return 0;
   const e3k::KernelSet* ks;
-  int G;
-  return select(p, dtype, ks, G) == E3_OK ? 1 : 0;
+  int G, ci;
+  return (select(p, dtype, Kind::fwd, ks, G, ci) == E3_OK &&
+          select(p, dtype, Kind::bwd, ks, G, ci) == E3_OK)
+             ? 1
+             : 0;
 }
 
 e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out) {
@@ -190,8 +221,8 @@ e3_status e3_tp_forward(const e3_desc* desc, int64_t n_rows, const void* x, cons
   e3_status s = parse(desc, p);
   if (s != E3_OK) return s;
   const e3k::KernelSet* ks;
-  int G;
-  if ((s = select(p, dtype, ks, G)) != E3_OK) return s;
+  int G, ci;
+  if ((s = select(p, dtype, Kind::tp, ks, G, ci)) != E3_OK) return s;
   if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
   if (n_rows == 0) return ok();
   if (!x || !y || !w || !z) return fail(E3_ERR_INVALID_ARG, "null pointer");
@@ -209,8 +240,8 @@ e3_status e3_conv_forward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
   e3_status s = parse(desc, p);
   if (s != E3_OK) return s;
   const e3k::KernelSet* ks;
-  int G;
-  if ((s = select(p, dtype, ks, G)) != E3_OK) return s;
+  int G, ci;
+  if ((s = select(p, dtype, Kind::fwd, ks, G, ci)) != E3_OK) return s;
   if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
   if (n_nodes == 0) return ok();
   if (!rowptr || !m || !x) return fail(E3_ERR_INVALID_ARG, "null pointer");
@@ -220,7 +251,7 @@ e3_status e3_conv_forward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
     return fail(E3_ERR_ALIGNMENT, "x, w and m must be 16-byte aligned");
   const bool yg = (desc->flags & E3_Y_GIVEN) != 0;
   e3k::FwdArgs a{n_nodes, n_edges, p.C, G, rowptr, sender, edge_vec_or_Y, x, w, m};
-  return hip_status(ks->fwd[dtype][yg](a, hipStream_t(stream)), "conv_forward");
+  return hip_status(ks->fwd[dtype][yg][ci](a, hipStream_t(stream)), "conv_forward");
 }
 
 e3_status e3_conv_workspace_size(int32_t n_nodes, int32_t n_edges, size_t* bytes) {
@@ -257,8 +288,8 @@ e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges
   e3_status s = parse(desc, p);
   if (s != E3_OK) return s;
   const e3k::KernelSet* ks;
-  int G;
-  if ((s = select(p, dtype, ks, G)) != E3_OK) return s;
+  int G, ci;
+  if ((s = select(p, dtype, Kind::bwd, ks, G, ci)) != E3_OK) return s;
   if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
   if (n_nodes == 0) return ok();
   size_t need = 0;
@@ -276,7 +307,7 @@ e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges
   const bool yg = (desc->flags & E3_Y_GIVEN) != 0;
   e3k::BwdArgs a{n_nodes, p.C, G, ws + L.colptr, ws + L.perm, ws + L.recv, ws + L.npad,
                  ws + L.padlist, n_edges, edge_vec_or_Y, x, w, dm, dx, dw, dY};
-  return hip_status(ks->bwd[dtype][yg](a, hipStream_t(stream)), "conv_backward");
+  return hip_status(ks->bwd[dtype][yg][ci](a, hipStream_t(stream)), "conv_backward");
 }
 
 const char* e3_last_error(void) { return g_last_error.c_str(); }

@@ -109,6 +109,12 @@ constexpr bool group_last(int roff, int rcnt, int r) {
   return r == rcnt - 1 || !same_pair(roff + r, roff + r + 1);
 }
 
+constexpr int pow2_ceil_c(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
 // ------------------------------------------------------------- static for
 
 template <int I>
@@ -135,6 +141,40 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Streaming variants for data touched once (edge weights in, edge and node
+// outputs out): non-temporal hints keep them from evicting the gathered
+// node rows from the caches.
+typedef float vf4 __attribute__((ext_vector_type(4)));
+typedef float vf2 __attribute__((ext_vector_type(2)));
+typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
+
+template <class T, int CPL>
+__device__ __forceinline__ void load_ch_stream(const T* __restrict__ p, float (&v)[CPL]) {
+  if constexpr (std::is_same_v<T, float> && CPL == 4) {
+    const vf4 t = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
+    v[0] = t.x;
+    v[1] = t.y;
+    v[2] = t.z;
+    v[3] = t.w;
+  } else if constexpr (std::is_same_v<T, float> && CPL == 2) {
+    const vf2 t = __builtin_nontemporal_load(reinterpret_cast<const vf2*>(p));
+    v[0] = t.x;
+    v[1] = t.y;
+  } else if constexpr (!std::is_same_v<T, float> && CPL == 4) {
+    const vu2 t = __builtin_nontemporal_load(reinterpret_cast<const vu2*>(p));
+    v[0] = bf16_to_f32(t.x & 0xFFFFu);
+    v[1] = bf16_to_f32(t.x >> 16);
+    v[2] = bf16_to_f32(t.y & 0xFFFFu);
+    v[3] = bf16_to_f32(t.y >> 16);
+  } else if constexpr (!std::is_same_v<T, float> && CPL == 2) {
+    const uint32_t t = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    v[0] = bf16_to_f32(t & 0xFFFFu);
+    v[1] = bf16_to_f32(t >> 16);
+  } else {
+    load_ch<T, CPL>(p, v);
+  }
+}
+
 // Load CPL consecutive channels starting at p (p aligned to CPL elements).
 template <class T, int CPL>
 __device__ __forceinline__ void load_ch(const T* __restrict__ p, float (&v)[CPL]) {
@@ -154,8 +194,12 @@ __device__ __forceinline__ void load_ch(const T* __restrict__ p, float (&v)[CPL]
       v[0] = *p;
     }
   } else {
-    static_assert(CPL == 4 || CPL == 8, "bf16 channel vector");
-    if constexpr (CPL == 4) {
+    static_assert(CPL == 2 || CPL == 4 || CPL == 8, "bf16 channel vector");
+    if constexpr (CPL == 2) {
+      const uint32_t t = *reinterpret_cast<const uint32_t*>(p);
+      v[0] = bf16_to_f32(t & 0xFFFFu);
+      v[1] = bf16_to_f32(t >> 16);
+    } else if constexpr (CPL == 4) {
       const uint2 t = *reinterpret_cast<const uint2*>(p);
       v[0] = bf16_to_f32(t.x & 0xFFFFu);
       v[1] = bf16_to_f32(t.x >> 16);
@@ -184,7 +228,9 @@ __device__ __forceinline__ void store_ch(T* __restrict__ p, const float (&v)[CPL
       *p = v[0];
     }
   } else {
-    if constexpr (CPL == 4) {
+    if constexpr (CPL == 2) {
+      *reinterpret_cast<uint32_t*>(p) = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+    } else if constexpr (CPL == 4) {
       uint2 t;
       t.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
       t.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
@@ -197,6 +243,26 @@ __device__ __forceinline__ void store_ch(T* __restrict__ p, const float (&v)[CPL
       t.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
       *reinterpret_cast<uint4*>(p) = t;
     }
+  }
+}
+
+template <class T, int CPL>
+__device__ __forceinline__ void store_ch_stream(T* __restrict__ p, const float (&v)[CPL]) {
+  if constexpr (std::is_same_v<T, float> && CPL == 4) {
+    const vf4 t = {v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(t, reinterpret_cast<vf4*>(p));
+  } else if constexpr (std::is_same_v<T, float> && CPL == 2) {
+    const vf2 t = {v[0], v[1]};
+    __builtin_nontemporal_store(t, reinterpret_cast<vf2*>(p));
+  } else if constexpr (!std::is_same_v<T, float> && CPL == 4) {
+    const vu2 t = {f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                   f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+    __builtin_nontemporal_store(t, reinterpret_cast<vu2*>(p));
+  } else if constexpr (!std::is_same_v<T, float> && CPL == 2) {
+    __builtin_nontemporal_store(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                reinterpret_cast<uint32_t*>(p));
+  } else {
+    store_ch<T, CPL>(p, v);
   }
 }
 
@@ -290,27 +356,181 @@ __device__ __forceinline__ void edge_y(const float* __restrict__ src, int64_t e,
 
 // ------------------------------------------------------------ shuffles
 
-__device__ __forceinline__ float xor_shuffle(float v, int s) { return __shfl_xor(v, s, 64); }
+// v from lane (lane ^ S): ds_swizzle in xor mode inside 32-lane halves,
+// bpermute across the halves.
+template <int S>
+__device__ __forceinline__ float shfl_xor_c(float v) {
+  if constexpr (S < 32)
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (S << 10) | 0x1F));
+  else
+    return __shfl_xor(v, 32, 64);
+}
+
+// Same with a wave-uniform runtime stride s in {1, 2, ..., 32}.
+__device__ __forceinline__ float shfl_xor_rt(float v, int s) {
+  switch (s) {
+    case 1: return shfl_xor_c<1>(v);
+    case 2: return shfl_xor_c<2>(v);
+    case 4: return shfl_xor_c<4>(v);
+    case 8: return shfl_xor_c<8>(v);
+    case 16: return shfl_xor_c<16>(v);
+    default: return shfl_xor_c<32>(v);
+  }
+}
+
+// VALU cross-lane moves of gfx950 (lane layouts as documented for the ISA):
+//  swap32(a, b): a's lanes 32..63 trade places with b's lanes 0..31;
+//  swap16(a, b): a's odd 16-lane rows trade places with b's even rows;
+//  dpp<CTRL>(v): v read through a DPP lane permutation (row_mirror 0x140,
+//  row_half_mirror 0x141, quad_perm [3,2,1,0] 0x1B, quad_perm [1,0,3,2] 0xB1).
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of N values over all 64 lanes of a wavefront, scattered: on return
+// v[0] of every lane with (lane & 3) == 0 holds the complete sum of value
+// index `first` (the return value), for first < N.  Pairings: lane halves
+// (swap32), 16-lane rows (swap16), then row mirror, half-row mirror and
+// quad mirror; each halving step keeps one half of the live values, and once
+// a single value is left the remaining pairings add it up.  Fixed order, so
+// bitwise reproducible; no LDS traffic.
+template <int N>
+__device__ __forceinline__ int wave_reduce_scatter(float (&v)[pow2_ceil_c(N)], int lane) {
+  constexpr int NP = pow2_ceil_c(N);
+  static_assert(NP <= 16, "at most 16 values");
+  int first = 0;
+  sfor<0, 6>([&](auto j) {
+    constexpr int L = NP >> j;  // live values before step j
+    constexpr int H = L / 2;
+    if constexpr (j == 0 || j == 1) {
+      const bool upper = j == 0 ? lane >= 32 : (lane & 16) != 0;
+      if constexpr (L >= 2) {
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+          if constexpr (j == 0) swap32(v[i], v[i + H]); else swap16(v[i], v[i + H]);
+          v[i] = v[i] + v[i + H];
+        }
+        first += upper ? H : 0;
+      } else {
+        float t = v[0];
+        if constexpr (j == 0) swap32(v[0], t); else swap16(v[0], t);
+        v[0] = v[0] + t;
+      }
+    } else {
+      constexpr int CTRL = j == 2 ? 0x140 : j == 3 ? 0x141 : j == 4 ? 0x1B : 0xB1;
+      constexpr int BIT = j == 2 ? 8 : j == 3 ? 4 : j == 4 ? 2 : 1;
+      if constexpr (L >= 2) {
+        const bool upper = (lane & BIT) != 0;
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+          const float lo = v[i] + dpp<CTRL>(v[i]);
+          const float hi = v[i + H] + dpp<CTRL>(v[i + H]);
+          v[i] = upper ? hi : lo;
+        }
+        first += upper ? H : 0;
+      } else {
+        v[0] = v[0] + dpp<CTRL>(v[0]);
+      }
+    }
+  });
+  return first;
+}
+
+// Two edge groups of 32 lanes: sum acc over the two halves, scattered: the
+// lower half ends with the totals of rows [0, N/2), the upper half with
+// rows [N/2, N), both in acc[0 .. N/2).
+template <int N, int CPL>
+__device__ __forceinline__ void halves_reduce_scatter(float (&a)[N][CPL]) {
+  static_assert(N % 2 == 0, "even row count");
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i)
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      swap32(a[i][k], a[i + N / 2][k]);
+      a[i][k] = a[i][k] + a[i + N / 2][k];
+    }
+}
 
 // Sum over the 64/G edge groups of a wavefront (butterfly, fixed order):
 // afterwards every group holds the total.
 template <int N, int CPL>
 __device__ __forceinline__ void reduce_groups(float (&a)[N][CPL], int G) {
-  for (int s = G; s < 64; s <<= 1) {
+  sfor<0, 6>([&](auto k) {
+    constexpr int S = 1 << k;
+    if (S >= G) {
 #pragma unroll
-    for (int i = 0; i < N; ++i)
+      for (int i = 0; i < N; ++i)
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) a[i][k] += xor_shuffle(a[i][k], s);
-  }
+        for (int c = 0; c < CPL; ++c) a[i][c] += shfl_xor_c<S>(a[i][c]);
+    }
+  });
 }
 
-// Sum over the G lanes of one edge group (butterfly, fixed order).
+constexpr int pow2_ceil(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// Sum of N per-lane values over the G lanes of an edge group (G a power of
+// two <= 64, groups aligned to G lanes), as a reduce-scatter: at each
+// stride, from G/2 down, a lane pair splits the live values, each keeps one
+// half and adds its partner's copy of that half; once one value is left,
+// the remaining strides are plain butterfly adds.  On return the lane holds
+// the complete sums of values first .. first+count-1 in v[0 .. count), and
+// lanes that share `first` hold identical sums.  Fixed order: bitwise
+// reproducible.
 template <int N>
-__device__ __forceinline__ void reduce_lanes(float (&a)[N], int G) {
-  for (int s = 1; s < G; s <<= 1) {
+struct Scatter {
+  static constexpr int NP = pow2_ceil(N);
+  float v[NP];
+  int first;  // index of v[0]
+  int count;  // complete values held
+};
+
+template <int N>
+__device__ __forceinline__ void reduce_scatter(const float (&a)[N], int G, int lane,
+                                               Scatter<N>& r) {
+  constexpr int NP = Scatter<N>::NP;
 #pragma unroll
-    for (int i = 0; i < N; ++i) a[i] += xor_shuffle(a[i], s);
-  }
+  for (int i = 0; i < NP; ++i) r.v[i] = i < N ? a[i] : 0.0f;
+  int first = 0, live = NP;
+  sfor<0, 6>([&](auto j) {
+    constexpr int L = NP >> j;  // live values if every earlier step halved
+    const int s = G >> (j + 1);
+    if (s >= 1) {
+      if constexpr (L >= 2) {
+        const bool upper = (lane & s) != 0;
+#pragma unroll
+        for (int i = 0; i < L / 2; ++i) {
+          const float keep = upper ? r.v[i + L / 2] : r.v[i];
+          const float send = upper ? r.v[i] : r.v[i + L / 2];
+          r.v[i] = keep + shfl_xor_rt(send, s);
+        }
+        first += upper ? L / 2 : 0;
+        live = L / 2;
+      } else {
+        r.v[0] += shfl_xor_rt(r.v[0], s);
+      }
+    }
+  });
+  r.first = first;
+  r.count = live;
 }
 
 // ------------------------------------------------- per-edge contractions
@@ -381,14 +601,15 @@ __device__ __forceinline__ void edge_forward(const float (&Y)[Plan<S>::DY],
 //   dx[xo+m1][k] += w[P][k] B_P[m1][k]
 //   dw[P][k]      = sum_m1 x[xo+m1][k] B_P[m1][k]
 //   dYl[yo+m2]   += sum_{M,m1} c sum_{k in lane} w[P][k] x[xo+m1][k] dm[oo+M][k]
-// dYl holds this lane's partial sums over its own channels.
-template <class S, int CPL>
+// dYl holds this lane's partial sums over its own channels; dw[P] is stored
+// to dwe + P*C as soon as the path is done.
+template <class S, int CPL, class TS>
 __device__ __forceinline__ void edge_backward(const float (&Y)[Plan<S>::DY],
                                               const float (&xv)[Plan<S>::DX][CPL],
                                               const float (&wv)[Plan<S>::NP][CPL],
                                               const float (&dmv)[Plan<S>::DO][CPL],
                                               float (&dxa)[Plan<S>::DX][CPL],
-                                              float (&dwv)[Plan<S>::NP][CPL],
+                                              TS* __restrict__ dwe, int C,
                                               float (&dYl)[Plan<S>::DY]) {
   using PL = Plan<S>;
   // this edge's dx contribution, summed over paths before it joins the
@@ -429,6 +650,7 @@ __device__ __forceinline__ void edge_backward(const float (&Y)[Plan<S>::DY],
         for (int k = 0; k < CPL; ++k) B[R.m1][k] = fmaf(A, dmv[P.oo + R.M][k], B[R.m1][k]);
       }
     });
+    float dwp[CPL];
 #pragma unroll
     for (int k = 0; k < CPL; ++k) {
       float s = 0.0f;
@@ -437,8 +659,9 @@ __device__ __forceinline__ void edge_backward(const float (&Y)[Plan<S>::DY],
         t[P.xo + a][k] = fmaf(wv[pi][k], B[a][k], t[P.xo + a][k]);
         s = fmaf(xv[P.xo + a][k], B[a][k], s);
       }
-      dwv[pi][k] = s;
+      dwp[k] = s;
     }
+    store_ch_stream<TS, CPL>(dwe + int64_t(pi) * C, dwp);
   });
 #pragma unroll
   for (int i = 0; i < PL::DX; ++i)

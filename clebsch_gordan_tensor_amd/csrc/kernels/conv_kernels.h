@@ -54,15 +54,23 @@ __global__ void __launch_bounds__(kBlock)
     float wv[PL::NP][CPL];
     const T* we = w + int64_t(e) * PL::NP * C + c0;
 #pragma unroll
-    for (int p = 0; p < PL::NP; ++p) load_ch<T, CPL>(we + int64_t(p) * C, wv[p]);
+    for (int p = 0; p < PL::NP; ++p) load_ch_stream<T, CPL>(we + int64_t(p) * C, wv[p]);
     edge_forward<S, CPL>(Y, xv, wv, acc);
   }
 
-  reduce_groups<PL::DO, CPL>(acc, G);
   T* mb = m + int64_t(b) * PL::DO * C + c0;
+  if (G == 32 && PL::DO % 2 == 0) {  // two groups: halves trade their halves
+    halves_reduce_scatter<PL::DO, CPL>(acc);
+    const int off = g * (PL::DO / 2);
 #pragma unroll
-  for (int i = 0; i < PL::DO; ++i)
-    if (i % NG == g) store_ch<T, CPL>(mb + int64_t(i) * C, acc[i]);
+    for (int i = 0; i < PL::DO / 2; ++i)
+      store_ch_stream<T, CPL>(mb + int64_t(off + i) * C, acc[i]);
+  } else {
+    reduce_groups<PL::DO, CPL>(acc, G);
+#pragma unroll
+    for (int i = 0; i < PL::DO; ++i)
+      if (i % NG == g) store_ch<T, CPL>(mb + int64_t(i) * C, acc[i]);
+  }
 }
 
 // ------------------------------------------------------------ backward
@@ -104,25 +112,38 @@ __global__ void __launch_bounds__(kBlock)
     float wv[PL::NP][CPL], dmv[PL::DO][CPL];
     const T* we = w + int64_t(e) * PL::NP * C + c0;
 #pragma unroll
-    for (int p = 0; p < PL::NP; ++p) load_ch<T, CPL>(we + int64_t(p) * C, wv[p]);
+    for (int p = 0; p < PL::NP; ++p) load_ch_stream<T, CPL>(we + int64_t(p) * C, wv[p]);
     const T* dmb = dm + int64_t(b) * PL::DO * C + c0;
 #pragma unroll
     for (int i = 0; i < PL::DO; ++i) load_ch<T, CPL>(dmb + int64_t(i) * C, dmv[i]);
 
-    float dwv[PL::NP][CPL];
     float dYl[PL::DY];
 #pragma unroll
     for (int i = 0; i < PL::DY; ++i) dYl[i] = 0.0f;
-    edge_backward<S, CPL>(Y, xv, wv, dmv, dxa, dwv, dYl);
-
-    T* dwe = dw + int64_t(e) * PL::NP * C + c0;
-#pragma unroll
-    for (int p = 0; p < PL::NP; ++p) store_ch<T, CPL>(dwe + int64_t(p) * C, dwv[p]);
-    reduce_lanes<PL::DY>(dYl, G);
+    edge_backward<S, CPL>(Y, xv, wv, dmv, dxa, dw + int64_t(e) * PL::NP * C + c0, C, dYl);
+    // dY[e] = sum over the group's channels: reduce-scatter, then the
+    // lanes that own distinct values store them
     float* dYe = dY + int64_t(e) * PL::DY;
+    if (G == 64) {  // one edge per wavefront: VALU-only cross-lane moves
+      constexpr int NPY = pow2_ceil_c(PL::DY);
+      float v[NPY];
 #pragma unroll
-    for (int i = 0; i < PL::DY; ++i)
-      if (i % G == cl) dYe[i] = dYl[i];
+      for (int i = 0; i < NPY; ++i) v[i] = i < PL::DY ? dYl[i] : 0.0f;
+      const int first = wave_reduce_scatter<PL::DY>(v, lane);
+      if ((lane & 3) == 0 && first < PL::DY) dYe[first] = v[0];
+    } else {
+      Scatter<PL::DY> sc;
+      reduce_scatter<PL::DY>(dYl, G, lane, sc);
+      constexpr int NPY = Scatter<PL::DY>::NP;
+      const int dup = (G > NPY ? G / NPY : 1) - 1;  // lanes holding copies
+      if ((cl & dup) == 0) {
+#pragma unroll
+        for (int i = 0; i < NPY; ++i) {
+          const int idx = sc.first + i;
+          if (i < sc.count && idx < PL::DY) dYe[idx] = sc.v[i];
+        }
+      }
+    }
   }
 
   reduce_groups<PL::DX, CPL>(dxa, G);
@@ -186,6 +207,14 @@ __global__ void __launch_bounds__(kBlock)
 
 // ------------------------------------------------------------ launchers
 
+template <int B, int E, class F>
+void sfor_host(F&& f) {
+  if constexpr (B < E) {
+    f(ic<B>{});
+    sfor_host<B + 1, E>(f);
+  }
+}
+
 inline unsigned blocks_for(int64_t waves) {
   return unsigned((waves + kWavesPerBlock - 1) / kWavesPerBlock);
 }
@@ -226,7 +255,7 @@ hipError_t launch_tp(const TpArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class S, int CPL>
+template <class S>
 KernelSet make_set(const char* name) {
   KernelSet k{};
   k.name = name;
@@ -236,17 +265,19 @@ KernelSet make_set(const char* name) {
   for (int i = 0; i < S::NX; ++i) k.x[i] = IrSpec{S::X[i].l, S::X[i].p};
   for (int i = 0; i < S::NY; ++i) k.y[i] = IrSpec{S::Y[i].l, S::Y[i].p};
   for (int i = 0; i < S::NO; ++i) k.o[i] = IrSpec{S::O[i].l, S::O[i].p};
-  k.cpl = CPL;
-  k.fwd[0][0] = &launch_fwd<S, float, CPL, false>;
-  k.fwd[0][1] = &launch_fwd<S, float, CPL, true>;
-  k.fwd[1][0] = &launch_fwd<S, bf16_t, CPL, false>;
-  k.fwd[1][1] = &launch_fwd<S, bf16_t, CPL, true>;
-  k.bwd[0][0] = &launch_bwd<S, float, CPL, false>;
-  k.bwd[0][1] = &launch_bwd<S, float, CPL, true>;
-  k.bwd[1][0] = &launch_bwd<S, bf16_t, CPL, false>;
-  k.bwd[1][1] = &launch_bwd<S, bf16_t, CPL, true>;
-  k.tp[0] = &launch_tp<S, float, CPL>;
-  k.tp[1] = &launch_tp<S, bf16_t, CPL>;
+  sfor_host<0, 2>([&](auto c) {
+    constexpr int CPL = c == 0 ? 2 : 4;
+    k.fwd[0][0][c] = &launch_fwd<S, float, CPL, false>;
+    k.fwd[0][1][c] = &launch_fwd<S, float, CPL, true>;
+    k.fwd[1][0][c] = &launch_fwd<S, bf16_t, CPL, false>;
+    k.fwd[1][1][c] = &launch_fwd<S, bf16_t, CPL, true>;
+    k.bwd[0][0][c] = &launch_bwd<S, float, CPL, false>;
+    k.bwd[0][1][c] = &launch_bwd<S, float, CPL, true>;
+    k.bwd[1][0][c] = &launch_bwd<S, bf16_t, CPL, false>;
+    k.bwd[1][1][c] = &launch_bwd<S, bf16_t, CPL, true>;
+  });
+  k.tp[0] = &launch_tp<S, float, 4>;
+  k.tp[1] = &launch_tp<S, bf16_t, 4>;
   return k;
 }
 

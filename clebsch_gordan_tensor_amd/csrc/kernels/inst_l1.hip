@@ -3,5 +3,5 @@
 #include "signatures.h"
 
 namespace e3k {
-const KernelSet kSetL1 = make_set<SigL1, 4>("L1");
+const KernelSet kSetL1 = make_set<SigL1>("L1");
 }  // namespace e3k

@@ -3,5 +3,5 @@
 #include "signatures.h"
 
 namespace e3k {
-const KernelSet kSetL1to3 = make_set<SigL1to3, 4>("L1to3");
+const KernelSet kSetL1to3 = make_set<SigL1to3>("L1to3");
 }  // namespace e3k

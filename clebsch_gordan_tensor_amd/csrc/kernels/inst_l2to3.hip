@@ -3,5 +3,5 @@
 #include "signatures.h"
 
 namespace e3k {
-const KernelSet kSetL2to3 = make_set<SigL2to3, 4>("L2to3");
+const KernelSet kSetL2to3 = make_set<SigL2to3>("L2to3");
 }  // namespace e3k

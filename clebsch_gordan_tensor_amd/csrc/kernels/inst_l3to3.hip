@@ -3,5 +3,5 @@
 #include "signatures.h"
 
 namespace e3k {
-const KernelSet kSetL3to3 = make_set<SigL3to3, 4>("L3to3");
+const KernelSet kSetL3to3 = make_set<SigL3to3>("L3to3");
 }  // namespace e3k

@@ -56,10 +56,10 @@ struct KernelSet {
   const char* name;
   int nx, ny, no;
   IrSpec x[4], y[4], o[4];
-  int cpl;            // channels per lane
-  FwdFn fwd[2][2];    // [dtype: 0 f32, 1 bf16][y given]
-  BwdFn bwd[2][2];
-  TpFn tp[2];
+  // [dtype: 0 f32, 1 bf16][y given][channels per lane: 0 -> 2, 1 -> 4]
+  FwdFn fwd[2][2][2];
+  BwdFn bwd[2][2][2];
+  TpFn tp[2];  // 4 channels per lane
 };
 
 extern const KernelSet kSetL1;

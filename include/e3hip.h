@@ -100,7 +100,11 @@ e3_status e3_num_paths(const e3_desc* desc, int32_t* n_paths);
 /* Indices into x, y, out of path i (host only). */
 e3_status e3_path_info(const e3_desc* desc, int32_t i, int32_t* ix, int32_t* iy, int32_t* iout);
 
-/* 1 if the descriptor, storage type and channel count have a kernel. */
+/* 1 if the descriptor, storage type and channel count have convolution
+ * kernels: the irreps triple must be one of the specialised signatures
+ * (x 0e+1o, 0e+1o+2e or 0e+1o+2e+3o; y the harmonic bank 0e+1o or
+ * 0e+1o+2e+3o; out 0e+1o or 0e+1o+2e+3o) and C a power of two with
+ * 2 <= C <= 256 (4 <= C for e3_tp_forward). */
 int32_t e3_supported(const e3_desc* desc, e3_dtype dtype);
 
 /* Real coupling block T[M][m1][m2] of (l1, l2, L), l <= 3, written to the
