@@ -62,7 +62,7 @@ def lib():
     L.e3_cg_block.argtypes = [i32, i32, i32, C.POINTER(C.c_double)]
     L.e3_spherical_harmonics.argtypes = [i32, i64, vp, vp, vp]
     L.e3_tp_forward.argtypes = [dp, i64, vp, vp, vp, vp, C.c_int, vp]
-    L.e3_conv_forward.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, C.c_int, vp]
+    L.e3_conv_forward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, C.c_int, vp]
     L.e3_conv_workspace_size.argtypes = [i32, i32, C.POINTER(sz)]
     L.e3_conv_prepare_transpose.argtypes = [i32, i32, vp, vp, vp, sz, vp]
     L.e3_conv_backward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp,
@@ -211,7 +211,10 @@ def tp_forward(desc: Desc, x, y, w, out=None, stream=None):
     return out
 
 
-def conv_forward(desc: Desc, rowptr, sender, edge_vec_or_Y, x, w, out=None, stream=None):
+def conv_forward(desc: Desc, rowptr, sender, edge_vec_or_Y, x, w, out=None, workspace=None,
+                 stream=None):
+    """m = conv(x, Y(edge_vec), w).  workspace (optional) is the prepared
+    per-graph index; with it receivers are visited in its locality order."""
     import torch
     N, E = rowptr.shape[0] - 1, sender.shape[0]
     P = num_paths(desc)
@@ -224,9 +227,10 @@ def conv_forward(desc: Desc, rowptr, sender, edge_vec_or_Y, x, w, out=None, stre
     if out is None:
         out = torch.empty((N, desc.dout, desc.channels), device=x.device, dtype=x.dtype)
     _need(out, "out", shape=(N, desc.dout, desc.channels), dtype=x.dtype)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().e3_conv_forward(C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender),
-                                 _ptr(edge_vec_or_Y), _ptr(x), _ptr(w), _ptr(out),
-                                 _dtype_code(x), _stream(stream)))
+                                 _ptr(workspace), wsb, _ptr(edge_vec_or_Y), _ptr(x), _ptr(w),
+                                 _ptr(out), _dtype_code(x), _stream(stream)))
     return out
 
 

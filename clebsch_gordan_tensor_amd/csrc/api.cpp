@@ -233,9 +233,9 @@ e3_status e3_tp_forward(const e3_desc* desc, int64_t n_rows, const void* x, cons
 }
 
 e3_status e3_conv_forward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
-                          const int32_t* rowptr, const int32_t* sender,
-                          const float* edge_vec_or_Y, const void* x, const void* w, void* m,
-                          e3_dtype dtype, void* stream) {
+                          const int32_t* rowptr, const int32_t* sender, const void* workspace,
+                          size_t ws_bytes, const float* edge_vec_or_Y, const void* x,
+                          const void* w, void* m, e3_dtype dtype, void* stream) {
   Parsed p;
   e3_status s = parse(desc, p);
   if (s != E3_OK) return s;
@@ -249,8 +249,16 @@ e3_status e3_conv_forward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
     return fail(E3_ERR_INVALID_ARG, "null pointer");
   if (!aligned16(x) || !aligned16(m) || (n_edges > 0 && !aligned16(w)))
     return fail(E3_ERR_ALIGNMENT, "x, w and m must be 16-byte aligned");
+  const int* order = nullptr;
+  if (workspace) {
+    size_t need = 0;
+    e3_conv_workspace_size(n_nodes, n_edges, &need);
+    if (ws_bytes < need)
+      return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+    order = static_cast<const int*>(workspace) + e3k::transpose_layout(n_nodes, n_edges).order;
+  }
   const bool yg = (desc->flags & E3_Y_GIVEN) != 0;
-  e3k::FwdArgs a{n_nodes, n_edges, p.C, G, rowptr, sender, edge_vec_or_Y, x, w, m};
+  e3k::FwdArgs a{n_nodes, n_edges, p.C, G, order, rowptr, sender, edge_vec_or_Y, x, w, m};
   return hip_status(ks->fwd[dtype][yg][ci](a, hipStream_t(stream)), "conv_forward");
 }
 
@@ -305,7 +313,7 @@ e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges
   const e3k::TransposeLayout L = e3k::transpose_layout(n_nodes, n_edges);
   const int* ws = static_cast<const int*>(workspace);
   const bool yg = (desc->flags & E3_Y_GIVEN) != 0;
-  e3k::BwdArgs a{n_nodes, p.C, G, ws + L.colptr, ws + L.perm, ws + L.recv, ws + L.npad,
+  e3k::BwdArgs a{n_nodes, p.C, G, ws + L.order, ws + L.colptr, ws + L.perm, ws + L.recv, ws + L.npad,
                  ws + L.padlist, n_edges, edge_vec_or_Y, x, w, dm, dx, dw, dY};
   return hip_status(ks->bwd[dtype][yg][ci](a, hipStream_t(stream)), "conv_backward");
 }

@@ -329,6 +329,29 @@ constexpr int y_offset(int j) {
   return o;
 }
 
+// Harmonics of every y irrep of S from one (unnormalised) edge vector.
+template <class S>
+__device__ __forceinline__ void edge_y_from_vec(float x, float y, float z,
+                                                float (&Y)[Plan<S>::DY]) {
+  unit_vector(x, y, z);
+  sfor<0, S::NY>([&](auto j) {
+    constexpr int l = S::Y[j].l;
+    constexpr int off = y_offset<S>(j);
+    float h[2 * l + 1];
+    harmonics_l<l>(x, y, z, h);
+#pragma unroll
+    for (int m = 0; m < 2 * l + 1; ++m) Y[off + m] = h[m];
+  });
+}
+
+// Orders this wavefront's LDS accesses around a staging step: the compiler
+// may not move LDS reads or writes across it, and the LDS queue drains.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
 // y operand of one edge for signature S: harmonics of the edge vector, one
 // bank per y irrep, or a given row Y[e][dy] when YG.
 template <class S, bool YG>

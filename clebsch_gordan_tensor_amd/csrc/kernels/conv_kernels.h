@@ -18,21 +18,36 @@ namespace e3k {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = 64 * kWavesPerBlock;
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
+
+// Node handled by this wavefront.  Workgroups are dispatched round-robin
+// over the XCDs (workgroup i on XCD i % 8); each XCD is given a contiguous
+// share of the traversal order, so the nodes that run together on one XCD
+// are neighbours and share gathered rows in that XCD's L2.  The grid is a
+// multiple of 8 workgroups; -1 for the waves past the end.
+__device__ __forceinline__ int node_of_wave(int n_nodes, const int* __restrict__ order) {
+  const int per_xcd = gridDim.x / kXcds;
+  const int blk = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int w = blk * kWavesPerBlock + (threadIdx.x >> 6);
+  if (w >= n_nodes) return -1;
+  return order ? order[w] : w;
+}
 
 // ------------------------------------------------------------- forward
 // m[b] = sum over the CSR segment of b of the weighted CG messages
 // (e3j A.3 Eq.7, E.1 Eq.12-13).  Padding edges (sender < 0) are skipped.
 template <class S, class T, int CPL, bool YG>
 __global__ void __launch_bounds__(kBlock)
-    k_conv_fwd(int n_nodes, int n_edges, int C, int G, const int* __restrict__ rowptr,
+    k_conv_fwd(int n_nodes, int n_edges, int C, int G, const int* __restrict__ order,
+               const int* __restrict__ rowptr,
                const int* __restrict__ sender, const float* __restrict__ ysrc,
                const T* __restrict__ x, const T* __restrict__ w, T* __restrict__ m) {
   using PL = Plan<S>;
-  const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (b >= n_nodes) return;  // wave-uniform
+  const int b = node_of_wave(n_nodes, order);
+  if (b < 0 || b >= n_nodes) return;  // wave-uniform
   const int lane = threadIdx.x & 63;
   const int NG = 64 / G;
-  const int g = lane / G, c0 = (lane - g * G) * CPL;
+  const int g = lane / G, ch0 = (lane - g * G) * CPL;
 
   float acc[PL::DO][CPL];
 #pragma unroll
@@ -40,25 +55,70 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
     for (int k = 0; k < CPL; ++k) acc[i][k] = 0.0f;
 
+  // The segment is walked in chunks of 64 edges whose senders (and edge
+  // vectors) are first staged in LDS with one coalesced load per lane, so
+  // every edge then costs a single round trip to memory (x and w together).
+  __shared__ int s_snd[kWavesPerBlock][64];
+  __shared__ float s_vec[kWavesPerBlock][YG ? 1 : 64 * 3];
+  int* snd = s_snd[threadIdx.x >> 6];
+  float* vec = s_vec[threadIdx.x >> 6];
   // a malformed rowptr cannot move the walk outside [0, n_edges)
   const int beg = max(rowptr[b], 0), end = min(rowptr[b + 1], n_edges);
-  for (int e = beg + g; e < end; e += NG) {
-    const int a = sender[e];
-    if (a < 0 || a >= n_nodes) continue;  // padding edge
-    float Y[PL::DY];
-    edge_y<S, YG>(ysrc, e, Y);
-    float xv[PL::DX][CPL];
-    const T* xa = x + int64_t(a) * PL::DX * C + c0;
+  for (int c0 = beg; c0 < end; c0 += 64) {
+    const int cn = min(64, end - c0);
+    wave_lds_fence();  // every lane is done with the previous chunk
+    if (lane < cn) {
+      snd[lane] = sender[c0 + lane];
+      if constexpr (!YG) {
+        const float* r = ysrc + int64_t(c0 + lane) * 3;
+        vec[3 * lane] = r[0];
+        vec[3 * lane + 1] = r[1];
+        vec[3 * lane + 2] = r[2];
+      }
+    }
+    wave_lds_fence();
+    // software pipeline: the loads of the group's next edge are in flight
+    // while the current edge is contracted
+    auto valid = [&](int j) { return j < cn && snd[j] >= 0 && snd[j] < n_nodes; };
+    auto issue = [&](int j, float (&xv)[PL::DX][CPL], float (&wv)[PL::NP][CPL]) {
+      const T* xa = x + int64_t(snd[j]) * PL::DX * C + ch0;
 #pragma unroll
-    for (int i = 0; i < PL::DX; ++i) load_ch<T, CPL>(xa + int64_t(i) * C, xv[i]);
-    float wv[PL::NP][CPL];
-    const T* we = w + int64_t(e) * PL::NP * C + c0;
+      for (int i = 0; i < PL::DX; ++i) load_ch<T, CPL>(xa + int64_t(i) * C, xv[i]);
+      const T* we = w + int64_t(c0 + j) * PL::NP * C + ch0;
 #pragma unroll
-    for (int p = 0; p < PL::NP; ++p) load_ch_stream<T, CPL>(we + int64_t(p) * C, wv[p]);
-    edge_forward<S, CPL>(Y, xv, wv, acc);
+      for (int p = 0; p < PL::NP; ++p) load_ch_stream<T, CPL>(we + int64_t(p) * C, wv[p]);
+    };
+    float xc[PL::DX][CPL], wc[PL::NP][CPL];
+    int j = g;
+    bool vc = valid(j);
+    if (vc) issue(j, xc, wc);
+    while (j < cn) {
+      const int jn = j + NG;
+      const bool vn = valid(jn);
+      float xn[PL::DX][CPL], wn[PL::NP][CPL];
+      if (vn) issue(jn, xn, wn);
+      if (vc) {
+        float Y[PL::DY];
+        if constexpr (YG)
+          edge_y<S, true>(ysrc, c0 + j, Y);
+        else
+          edge_y_from_vec<S>(vec[3 * j], vec[3 * j + 1], vec[3 * j + 2], Y);
+        edge_forward<S, CPL>(Y, xc, wc, acc);
+      }
+#pragma unroll
+      for (int i = 0; i < PL::DX; ++i)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) xc[i][k] = xn[i][k];
+#pragma unroll
+      for (int i = 0; i < PL::NP; ++i)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) wc[i][k] = wn[i][k];
+      j = jn;
+      vc = vn;
+    }
   }
 
-  T* mb = m + int64_t(b) * PL::DO * C + c0;
+  T* mb = m + int64_t(b) * PL::DO * C + ch0;
   if (G == 32 && PL::DO % 2 == 0) {  // two groups: halves trade their halves
     halves_reduce_scatter<PL::DO, CPL>(acc);
     const int off = g * (PL::DO / 2);
@@ -80,20 +140,21 @@ __global__ void __launch_bounds__(kBlock)
 // E.4 replaces the atomics of E.3).
 template <class S, class T, int CPL, bool YG>
 __global__ void __launch_bounds__(kBlock)
-    k_conv_bwd(int n_nodes, int n_edges, int C, int G, const int* __restrict__ colptr,
+    k_conv_bwd(int n_nodes, int n_edges, int C, int G, const int* __restrict__ order,
+               const int* __restrict__ colptr,
                const int* __restrict__ perm, const int* __restrict__ recv,
                const float* __restrict__ ysrc, const T* __restrict__ x,
                const T* __restrict__ w, const T* __restrict__ dm, T* __restrict__ dx,
                T* __restrict__ dw, float* __restrict__ dY) {
   using PL = Plan<S>;
-  const int a = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (a >= n_nodes) return;  // wave-uniform
+  const int a = node_of_wave(n_nodes, order);
+  if (a < 0 || a >= n_nodes) return;  // wave-uniform
   const int lane = threadIdx.x & 63;
   const int NG = 64 / G;
-  const int g = lane / G, cl = lane - g * G, c0 = cl * CPL;
+  const int g = lane / G, cl = lane - g * G, ch0 = cl * CPL;
 
   float xv[PL::DX][CPL], dxa[PL::DX][CPL];
-  const T* xa = x + int64_t(a) * PL::DX * C + c0;
+  const T* xa = x + int64_t(a) * PL::DX * C + ch0;
 #pragma unroll
   for (int i = 0; i < PL::DX; ++i) {
     load_ch<T, CPL>(xa + int64_t(i) * C, xv[i]);
@@ -101,26 +162,54 @@ __global__ void __launch_bounds__(kBlock)
     for (int k = 0; k < CPL; ++k) dxa[i][k] = 0.0f;
   }
 
+  // Out-edges in chunks of 64: edge ids, receivers and edge vectors are
+  // staged in LDS (one load per lane), then each edge costs one round trip.
+  __shared__ int s_e[kWavesPerBlock][64];
+  __shared__ int s_b[kWavesPerBlock][64];
+  __shared__ float s_vec[kWavesPerBlock][YG ? 1 : 64 * 3];
+  int* se = s_e[threadIdx.x >> 6];
+  int* sb = s_b[threadIdx.x >> 6];
+  float* vec = s_vec[threadIdx.x >> 6];
   // clamped so that a workspace built for another graph stays in bounds
   const int beg = max(colptr[a], 0), end = min(colptr[a + 1], n_edges);
-  for (int j = beg + g; j < end; j += NG) {
-    const int e = perm[j];
-    const int b = recv[j];
-    if (e < 0 || e >= n_edges || b < 0 || b >= n_nodes) continue;  // only for malformed CSR
+  for (int c0 = beg; c0 < end; c0 += 64) {
+    const int cn = min(64, end - c0);
+    wave_lds_fence();
+    if (lane < cn) {
+      int e = perm[c0 + lane];
+      const int b = recv[c0 + lane];
+      if (e < 0 || e >= n_edges || b < 0 || b >= n_nodes) e = -1;  // only for malformed CSR
+      se[lane] = e;
+      sb[lane] = b;
+      if constexpr (!YG) {
+        const float* r = ysrc + int64_t(e < 0 ? 0 : e) * 3;
+        vec[3 * lane] = r[0];
+        vec[3 * lane + 1] = r[1];
+        vec[3 * lane + 2] = r[2];
+      }
+    }
+    wave_lds_fence();
+  for (int jj = g; jj < cn; jj += NG) {
+    const int e = se[jj];
+    const int b = sb[jj];
+    if (e < 0) continue;
     float Y[PL::DY];
-    edge_y<S, YG>(ysrc, e, Y);
+    if constexpr (YG)
+      edge_y<S, true>(ysrc, e, Y);
+    else
+      edge_y_from_vec<S>(vec[3 * jj], vec[3 * jj + 1], vec[3 * jj + 2], Y);
     float wv[PL::NP][CPL], dmv[PL::DO][CPL];
-    const T* we = w + int64_t(e) * PL::NP * C + c0;
+    const T* we = w + int64_t(e) * PL::NP * C + ch0;
 #pragma unroll
     for (int p = 0; p < PL::NP; ++p) load_ch_stream<T, CPL>(we + int64_t(p) * C, wv[p]);
-    const T* dmb = dm + int64_t(b) * PL::DO * C + c0;
+    const T* dmb = dm + int64_t(b) * PL::DO * C + ch0;
 #pragma unroll
     for (int i = 0; i < PL::DO; ++i) load_ch<T, CPL>(dmb + int64_t(i) * C, dmv[i]);
 
     float dYl[PL::DY];
 #pragma unroll
     for (int i = 0; i < PL::DY; ++i) dYl[i] = 0.0f;
-    edge_backward<S, CPL>(Y, xv, wv, dmv, dxa, dw + int64_t(e) * PL::NP * C + c0, C, dYl);
+    edge_backward<S, CPL>(Y, xv, wv, dmv, dxa, dw + int64_t(e) * PL::NP * C + ch0, C, dYl);
     // dY[e] = sum over the group's channels: reduce-scatter, then the
     // lanes that own distinct values store them
     float* dYe = dY + int64_t(e) * PL::DY;
@@ -145,9 +234,10 @@ __global__ void __launch_bounds__(kBlock)
       }
     }
   }
+  }
 
   reduce_groups<PL::DX, CPL>(dxa, G);
-  T* dxo = dx + int64_t(a) * PL::DX * C + c0;
+  T* dxo = dx + int64_t(a) * PL::DX * C + ch0;
 #pragma unroll
   for (int i = 0; i < PL::DX; ++i)
     if (i % NG == g) store_ch<T, CPL>(dxo + int64_t(i) * C, dxa[i]);
@@ -219,11 +309,17 @@ inline unsigned blocks_for(int64_t waves) {
   return unsigned((waves + kWavesPerBlock - 1) / kWavesPerBlock);
 }
 
+// One wavefront per node, rounded up to a whole number of XCD shares.
+inline unsigned node_blocks(int64_t n_nodes) {
+  const int64_t b = (n_nodes + kWavesPerBlock - 1) / kWavesPerBlock;
+  return unsigned((b + kXcds - 1) / kXcds * kXcds);
+}
+
 template <class S, class T, int CPL, bool YG>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   if (a.n_nodes <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_conv_fwd<S, T, CPL, YG>), dim3(blocks_for(a.n_nodes)), dim3(kBlock), 0, s,
-                     a.n_nodes, a.n_edges, a.C, a.G, a.rowptr, a.sender, a.ysrc,
+  hipLaunchKernelGGL((k_conv_fwd<S, T, CPL, YG>), dim3(node_blocks(a.n_nodes)), dim3(kBlock), 0, s,
+                     a.n_nodes, a.n_edges, a.C, a.G, a.order, a.rowptr, a.sender, a.ysrc,
                      static_cast<const T*>(a.x), static_cast<const T*>(a.w),
                      static_cast<T*>(a.m));
   return hipGetLastError();
@@ -232,8 +328,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
 template <class S, class T, int CPL, bool YG>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   if (a.n_nodes <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_conv_bwd<S, T, CPL, YG>), dim3(blocks_for(a.n_nodes)), dim3(kBlock), 0, s,
-                     a.n_nodes, int(a.n_edges), a.C, a.G, a.colptr, a.perm, a.recv, a.ysrc,
+  hipLaunchKernelGGL((k_conv_bwd<S, T, CPL, YG>), dim3(node_blocks(a.n_nodes)), dim3(kBlock), 0, s,
+                     a.n_nodes, int(a.n_edges), a.C, a.G, a.order, a.colptr, a.perm, a.recv, a.ysrc,
                      static_cast<const T*>(a.x), static_cast<const T*>(a.w),
                      static_cast<const T*>(a.dm), static_cast<T*>(a.dx), static_cast<T*>(a.dw),
                      a.dY);

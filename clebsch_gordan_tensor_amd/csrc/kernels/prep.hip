@@ -10,6 +10,7 @@
 // every bucket is fixed by a rank sort, so the index is deterministic.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "common.h"
@@ -41,8 +42,9 @@ __global__ void __launch_bounds__(256)
 // Exclusive scan, pass 1: each block scans one tile in LDS, writes the
 // tile-local exclusive prefix and the tile total.
 __global__ void __launch_bounds__(kScanBlock)
-    k_scan_tiles(const int* __restrict__ in, int64_t n, int* __restrict__ out,
-                 int* __restrict__ tile_sum) {
+    k_scan_tiles(const int* in, int64_t n, int* out, int* __restrict__ tile_sum) {
+  // in and out may be the same array: a thread reads its own items before
+  // it writes them and never touches another thread's items
   __shared__ int s[kScanBlock];
   const int64_t base = int64_t(blockIdx.x) * kScanTile + int64_t(threadIdx.x) * kScanItems;
   int v[kScanItems], t = 0;
@@ -145,6 +147,65 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Breadth-first traversal over in-edges, one level per launch: every
+// wavefront takes a node of the current level [lb, le) of `order` and claims
+// its unvisited senders; claims are counted with one atomic per wavefront and
+// appended to `order`.  The order inside a level depends on timing; it only
+// decides which wavefront handles which node later, never a result.
+__global__ void __launch_bounds__(256)
+    k_bfs_expand(int n_nodes, int n_edges, const int* __restrict__ rowptr,
+                 const int* __restrict__ sender, int* __restrict__ order,
+                 int* __restrict__ visited, int* __restrict__ tail, int lb, int le) {
+  const int lane = threadIdx.x & 63;
+  for (int f = lb + blockIdx.x * 4 + (threadIdx.x >> 6); f < le; f += gridDim.x * 4) {
+    const int u = order[f];
+    const int beg = max(rowptr[u], 0), end = min(rowptr[u + 1], n_edges);
+    for (int e0 = beg; e0 < end; e0 += 64) {  // wave-uniform bounds
+      const int e = e0 + lane;
+      int a = -1;
+      if (e < end) {
+        a = sender[e];
+        if (a < 0 || a >= n_nodes) a = -1;
+      }
+      const bool claim = a >= 0 && atomicExch(visited + a, 1) == 0;
+      const uint64_t mask = __ballot(claim);
+      if (mask) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(tail, __popcll(mask));
+        base = __shfl(base, 0, 64);
+        if (claim) order[base + __popcll(mask & ((uint64_t(1) << lane) - 1))] = a;
+      }
+    }
+  }
+}
+
+__global__ void k_bfs_seed(int* __restrict__ order, int* __restrict__ visited,
+                           int* __restrict__ tail, int s) {
+  order[0] = s;
+  visited[s] = 1;
+  *tail = 1;
+}
+
+// flag[i] = 1 for nodes the traversal did not reach (flag[n] = 0).
+__global__ void __launch_bounds__(256)
+    k_unvisited_flags(int n_nodes, const int* __restrict__ visited, int* __restrict__ flag) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i <= n_nodes;
+       i += int64_t(gridDim.x) * blockDim.x)
+    flag[i] = (i < n_nodes && !visited[i]) ? 1 : 0;
+}
+
+// Unreached nodes go after the traversal, in index order.
+__global__ void __launch_bounds__(256)
+    k_append_unvisited(int n_nodes, const int* __restrict__ visited, const int* __restrict__ pos,
+                       int start, int* __restrict__ order) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n_nodes;
+       i += int64_t(gridDim.x) * blockDim.x)
+    if (!visited[i]) {
+      const int k = start + pos[i];
+      if (k < n_nodes) order[k] = int(i);
+    }
+}
+
 template <int LMAX>
 __global__ void __launch_bounds__(256)
     k_harmonics(int64_t n, const float* __restrict__ vec, float* __restrict__ Y) {
@@ -189,10 +250,54 @@ TransposeLayout transpose_layout(int64_t n_nodes, int64_t n_edges) {
   o += up(n_edges);
   L.padlist = o;
   o += up(n_edges);
+  L.order = o;
+  o += up(n_nodes);
+  L.flag = o;
+  o += up(n_nodes + 1);
   L.bsum = o;
   o += up((n_nodes + 1 + kScanTile - 1) / kScanTile + 1);
   L.total_words = o;
   return L;
+}
+
+// Traversal order of the nodes for the convolution kernels (ws + L.order):
+// breadth-first from node 0 over in-edges, then every unreached node in
+// index order.  Neighbouring nodes end up close in the order, so the
+// wavefronts that run together gather overlapping node rows.  One host
+// synchronisation per level (the level bounds come back to the host).
+hipError_t build_locality_order(int n_nodes, int n_edges, const int* rowptr, const int* sender,
+                                int* ws, const TransposeLayout& L, hipStream_t s) {
+  int* order = ws + L.order;
+  int* visited = ws + L.cursor;  // free once the buckets are ranked
+  int* tail = ws + L.npad + 1;
+  const int64_t n1 = int64_t(n_nodes) + 1;
+  hipLaunchKernelGGL(k_fill, dim3(grid_for(n1, 256)), dim3(256), 0, s, visited, n1, 0);
+  hipLaunchKernelGGL(k_bfs_seed, dim3(1), dim3(1), 0, s, order, visited, tail, 0);
+  int lb = 0, le = 1, h_tail = 1;
+  while (lb < le) {
+    const unsigned g = unsigned(std::min<int64_t>((int64_t(le - lb) + 3) / 4, 1 << 16));
+    hipLaunchKernelGGL(k_bfs_expand, dim3(g), dim3(256), 0, s, n_nodes, n_edges, rowptr, sender,
+                       order, visited, tail, lb, le);
+    hipError_t err = hipMemcpyAsync(&h_tail, tail, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err != hipSuccess) return err;
+    if (h_tail < le || h_tail > n_nodes) return hipErrorUnknown;  // cannot happen
+    lb = le;
+    le = h_tail;
+  }
+  if (h_tail < n_nodes) {
+    int* flag = ws + L.flag;
+    hipLaunchKernelGGL(k_unvisited_flags, dim3(grid_for(n1, 256)), dim3(256), 0, s, n_nodes, visited,
+                       flag);
+    const unsigned tiles = unsigned((n1 + kScanTile - 1) / kScanTile);
+    hipLaunchKernelGGL(k_scan_tiles, dim3(tiles), dim3(kScanBlock), 0, s, flag, n1, flag,
+                       ws + L.bsum);
+    hipLaunchKernelGGL(k_scan_tile_sums, dim3(1), dim3(kScanBlock), 0, s, ws + L.bsum, int(tiles));
+    hipLaunchKernelGGL(k_scan_add, dim3(tiles), dim3(kScanBlock), 0, s, flag, n1, ws + L.bsum);
+    hipLaunchKernelGGL(k_append_unvisited, dim3(grid_for(n_nodes, 256)), dim3(256), 0, s, n_nodes,
+                       visited, flag, h_tail, order);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr, const int* sender,
@@ -224,7 +329,9 @@ hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr,
     hipLaunchKernelGGL(k_rank_buckets, dim3(wb), dim3(256), 0, s, n_nodes, colptr, ws + L.tmp_e,
                        ws + L.tmp_b, ws + L.perm, ws + L.recv);
   }
-  return hipGetLastError();
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || n_nodes == 0) return err;
+  return build_locality_order(n_nodes, n_edges, rowptr, sender, ws, L, s);
 }
 
 hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hipStream_t s) {

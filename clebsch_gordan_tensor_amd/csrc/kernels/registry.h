@@ -10,6 +10,7 @@ namespace e3k {
 
 struct FwdArgs {
   int n_nodes, n_edges, C, G;
+  const int* order;  // traversal order of the receivers, or null for 0..N-1
   const int* rowptr;
   const int* sender;
   const float* ysrc;  // edge vectors [E][3] or harmonics [E][dy]
@@ -20,6 +21,7 @@ struct FwdArgs {
 
 struct BwdArgs {
   int n_nodes, C, G;
+  const int* order;  // traversal order of the senders
   const int* colptr;
   const int* perm;
   const int* recv;
@@ -74,7 +76,7 @@ hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hip
 
 // Workspace layout of the transposed edge index (int32 words).
 struct TransposeLayout {
-  int64_t npad, colptr, cursor, tmp_e, tmp_b, perm, recv, padlist, bsum, total_words;
+  int64_t npad, colptr, cursor, tmp_e, tmp_b, perm, recv, padlist, order, flag, bsum, total_words;
 };
 TransposeLayout transpose_layout(int64_t n_nodes, int64_t n_edges);
 

@@ -125,19 +125,26 @@ e3_status e3_tp_forward(const e3_desc* desc, int64_t n_rows, const void* x, cons
 /* Fused convolution forward (e3j A.3 Eq.7, E.1 Eq.12-13):
  *   m[b] = sum_{e in row b} sum_P w[e][P] (x[sender[e]] (x) Y(r_e))_P.
  * edge_vec_or_Y: edge vectors [E][3], or Y [E][dy] with E3_Y_GIVEN.
+ * workspace: optional (NULL allowed); when given it must come from
+ * e3_conv_prepare_transpose on the same graph, and receivers are then
+ * visited in its locality order (same results, better cache reuse).
  * Receivers without edges get m = 0. */
 e3_status e3_conv_forward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
-                          const int32_t* rowptr, const int32_t* sender,
-                          const float* edge_vec_or_Y, const void* x, const void* w, void* m,
-                          e3_dtype dtype, void* stream);
+                          const int32_t* rowptr, const int32_t* sender, const void* workspace,
+                          size_t ws_bytes, const float* edge_vec_or_Y, const void* x,
+                          const void* w, void* m, e3_dtype dtype, void* stream);
 
 /* Size in bytes of the workspace that holds the sender-ordered edge index. */
 e3_status e3_conv_workspace_size(int32_t n_nodes, int32_t n_edges, size_t* bytes);
 
-/* Build the sender-ordered (transposed) edge index of a graph into the
- * workspace: a counting sort by sender, stable in edge id (the sender-keyed
- * traversal of the e3j backward, E.4).  Once per graph; the backward pass
- * reads it.  ws_bytes must be >= e3_conv_workspace_size(). */
+/* Build the per-graph index into the workspace:
+ *  - the sender-ordered (transposed) edge list, a counting sort by sender
+ *    stable in edge id (the sender-keyed traversal of the e3j backward, E.4),
+ *    which the backward pass reads;
+ *  - a locality order of the nodes (breadth-first over in-edges, then the
+ *    unreached nodes in index order) in which both passes visit nodes.
+ * Once per graph.  ws_bytes must be >= e3_conv_workspace_size().  This call
+ * synchronises `stream` with the host once per breadth-first level. */
 e3_status e3_conv_prepare_transpose(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
                                     const int32_t* sender, void* workspace, size_t ws_bytes,
                                     void* stream);

@@ -103,16 +103,20 @@ def test_error_codes(lib):
     assert lib.e3_path_info(_desc_c(good), 99, C.byref(n), C.byref(n), C.byref(n)) == -1
     # unsupported signature: rejected before any launch
     uns = api.Desc([(0, 1), (2, -1)], [(0, 1)], [(0, 1)], 8)
-    assert lib.e3_conv_forward(_desc_c(uns), 4, 4, None, None, None, None, None, None, 0, None) == -3
+    assert lib.e3_conv_forward(_desc_c(uns), 4, 4, None, None, None, 0, None, None, None, None, 0,
+                               None) == -3
     # negative sizes, null pointers, misalignment, empty problems
-    assert lib.e3_conv_forward(_desc_c(good), -1, 0, None, None, None, None, None, None, 0, None) == -1
-    assert lib.e3_conv_forward(_desc_c(good), 0, 0, None, None, None, None, None, None, 0, None) == 0
-    assert lib.e3_conv_forward(_desc_c(good), 4, 4, None, None, None, None, None, None, 0, None) == -1
+    assert lib.e3_conv_forward(_desc_c(good), -1, 0, None, None, None, 0, None, None, None, None, 0,
+                               None) == -1
+    assert lib.e3_conv_forward(_desc_c(good), 0, 0, None, None, None, 0, None, None, None, None, 0,
+                               None) == 0
+    assert lib.e3_conv_forward(_desc_c(good), 4, 4, None, None, None, 0, None, None, None, None, 0,
+                               None) == -1
     fake = C.c_void_p(0x10000)
     odd = C.c_void_p(0x10004)
-    assert lib.e3_conv_forward(_desc_c(good), 4, 4, fake, fake, fake, odd, fake, fake, 0,
+    assert lib.e3_conv_forward(_desc_c(good), 4, 4, fake, fake, None, 0, fake, odd, fake, fake, 0,
                                None) == -4
-    assert lib.e3_conv_forward(_desc_c(good), 4, 4, fake, fake, fake, fake, fake, fake, 7,
+    assert lib.e3_conv_forward(_desc_c(good), 4, 4, fake, fake, None, 0, fake, fake, fake, fake, 7,
                                None) == -1  # unknown dtype
     assert lib.e3_tp_forward(_desc_c(good), 0, None, None, None, None, 0, None) == 0
     assert lib.e3_tp_forward(_desc_c(good), -2, None, None, None, None, 0, None) == -1
@@ -127,6 +131,9 @@ def test_error_codes(lib):
     assert lib.e3_conv_backward(_desc_c(good), 10, 100, fake, fake, fake, need - 4, fake, fake,
                                 fake, fake, fake, fake, fake, 0, None) == -6
     assert "workspace" in lib.e3_last_error().decode()
+    # forward: a workspace is optional, but a given one must be large enough
+    assert lib.e3_conv_forward(_desc_c(good), 10, 100, fake, fake, fake, need - 4, fake, fake, fake,
+                               fake, 0, None) == -6
     out = np.zeros(10)
     assert lib.e3_cg_block(1, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
     assert lib.e3_cg_block(4, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1

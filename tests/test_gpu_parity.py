@@ -38,10 +38,14 @@ def run_conv(gpu, d, g, x, w, dm, dtype="f32", Y=None):
     rowptr, sender = dev(g.rowptr), dev(g.sender)
     ysrc = dev(Y.astype(np.float32)) if Y is not None else dev(g.evec)
     xd, wd, dmd = dev(x, dtype), dev(w, dtype), dev(dm, dtype)
-    m = gpu.conv_forward(d, rowptr, sender, ysrc, xd, wd)
     ws = gpu.conv_prepare_transpose(rowptr, sender)
+    m = gpu.conv_forward(d, rowptr, sender, ysrc, xd, wd, workspace=ws)
     dx, dw, dY = gpu.conv_backward(d, rowptr, sender, ws, ysrc, xd, wd, dmd)
+    # the plain receiver order gives bitwise the same forward result
+    m0 = gpu.conv_forward(d, rowptr, sender, ysrc, xd, wd)
     torch.cuda.synchronize()
+    assert torch.equal(m.view(torch.int16) if m.dtype == torch.bfloat16 else m.view(torch.int32),
+                       m0.view(torch.int16) if m0.dtype == torch.bfloat16 else m0.view(torch.int32))
     return host(m), host(dx), host(dw), host(dY)
 
 
@@ -233,6 +237,10 @@ def test_transpose_index(gpu):
     assert np.array_equal(perm[:len(real)], order)
     assert np.array_equal(recv[:len(real)], g.receiver[order])
     assert np.array_equal(colptr, np.concatenate([[0], np.cumsum(np.bincount(g.sender[real], minlength=N))]))
+    # the locality order is a permutation of the nodes
+    o2 = o + 5 * up(E)
+    order = words[o2:o2 + N]
+    assert np.array_equal(np.sort(order), np.arange(N))
 
 
 # ---------------------------------------------------- tensor product (rows)
