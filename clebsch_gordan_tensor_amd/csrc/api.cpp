@@ -114,20 +114,41 @@ int group_lanes(int C, int cpl) {
 
 enum class Kind { fwd, bwd, tp };
 
-// Channels per lane: the backward keeps two per lane (one edge per
-// wavefront at C = 128, half the registers of four), the forward and the
-// tensor product four (two edges or rows per wavefront).  Overridable with
-// E3HIP_FWD_CPL / E3HIP_BWD_CPL (2 or 4) for tuning.
-int preferred_cpl(Kind k) {
-  static const int fwd = [] {
+// Per-lane register estimate (fp32 words) of a kernel holding cpl channels
+// per lane: feature, weight and accumulator vectors scale with cpl, the
+// harmonics and the per-edge coefficient temporaries do not.
+int register_estimate(const e3k::KernelSet& k, Kind kind, int cpl) {
+  if (kind == Kind::bwd) return (3 * k.dx + k.np + k.dout) * cpl + 2 * k.dy + 48;
+  return (k.dx + k.np + k.dout) * cpl + k.dy + 40;
+}
+
+// Channels per lane: the largest of 4, 2, 1 whose register estimate keeps
+// several wavefronts per SIMD (forward 176, backward 176 words), with
+// G = C / cpl lanes per edge group a power of two <= 64.  The tensor
+// product uses 4.  E3HIP_FWD_CPL / E3HIP_BWD_CPL (1, 2 or 4) force a choice
+// when it is valid, for tuning.
+int choose_cpl(const e3k::KernelSet& k, Kind kind, int C) {
+  if (kind == Kind::tp) return group_lanes(C, 4) > 0 ? 4 : -1;
+  static const int force_fwd = [] {
     const char* e = std::getenv("E3HIP_FWD_CPL");
-    return (e && std::atoi(e) == 2) ? 2 : 4;
+    return e ? std::atoi(e) : 0;
   }();
-  static const int bwd = [] {
+  static const int force_bwd = [] {
     const char* e = std::getenv("E3HIP_BWD_CPL");
-    return (e && std::atoi(e) == 4) ? 4 : 2;
+    return e ? std::atoi(e) : 0;
   }();
-  return k == Kind::fwd ? fwd : k == Kind::bwd ? bwd : 4;
+  const int force = kind == Kind::fwd ? force_fwd : force_bwd;
+  if ((force == 1 || force == 2 || force == 4) && group_lanes(C, force) > 0) return force;
+  // the backward of the small signatures is best at two channels per lane
+  // (one edge per wavefront at C = 128): prefer 2 there over 4
+  const int first = kind == Kind::bwd ? 2 : 4;
+  for (int cpl : {first, first == 4 ? 2 : 1, 1}) {
+    if (group_lanes(C, cpl) <= 0) continue;
+    if (register_estimate(k, kind, cpl) <= 176) return cpl;
+  }
+  for (int cpl : {1, 2, 4})
+    if (group_lanes(C, cpl) > 0) return cpl;
+  return -1;
 }
 
 e3_status select(const Parsed& p, e3_dtype dt, Kind kind, const e3k::KernelSet*& ks, int& G,
@@ -138,17 +159,14 @@ e3_status select(const Parsed& p, e3_dtype dt, Kind kind, const e3k::KernelSet*&
     return fail(E3_ERR_UNSUPPORTED,
                 "no kernel for this irreps signature (supported: x in {0e+1o, 0e+1o+2e, "
                 "0e+1o+2e+3o}, y = harmonics 0e+1o[+2e+3o], out = 0e+1o[+2e+3o])");
-  const int pref = preferred_cpl(kind);
-  const int alt = kind == Kind::tp ? 4 : (pref == 2 ? 4 : 2);
-  for (int cpl : {pref, alt}) {
+  const int cpl = choose_cpl(*ks, kind, p.C);
+  if (cpl > 0) {
     G = group_lanes(p.C, cpl);
-    if (G > 0) {
-      cpl_idx = cpl == 2 ? 0 : 1;
-      return E3_OK;
-    }
+    cpl_idx = cpl == 1 ? 0 : cpl == 2 ? 1 : 2;
+    return E3_OK;
   }
   return fail(E3_ERR_UNSUPPORTED,
-              "channel count must be a power of two, 2 <= C <= 256 (4 <= C for the tensor "
+              "channel count must be a power of two, 1 <= C <= 256 (4 <= C for the tensor "
               "product), got " + std::to_string(p.C));
 }
 

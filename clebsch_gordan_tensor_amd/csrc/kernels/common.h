@@ -141,40 +141,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Streaming variants for data touched once (edge weights in, edge and node
-// outputs out): non-temporal hints keep them from evicting the gathered
-// node rows from the caches.
-typedef float vf4 __attribute__((ext_vector_type(4)));
-typedef float vf2 __attribute__((ext_vector_type(2)));
-typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
-
-template <class T, int CPL>
-__device__ __forceinline__ void load_ch_stream(const T* __restrict__ p, float (&v)[CPL]) {
-  if constexpr (std::is_same_v<T, float> && CPL == 4) {
-    const vf4 t = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
-    v[0] = t.x;
-    v[1] = t.y;
-    v[2] = t.z;
-    v[3] = t.w;
-  } else if constexpr (std::is_same_v<T, float> && CPL == 2) {
-    const vf2 t = __builtin_nontemporal_load(reinterpret_cast<const vf2*>(p));
-    v[0] = t.x;
-    v[1] = t.y;
-  } else if constexpr (!std::is_same_v<T, float> && CPL == 4) {
-    const vu2 t = __builtin_nontemporal_load(reinterpret_cast<const vu2*>(p));
-    v[0] = bf16_to_f32(t.x & 0xFFFFu);
-    v[1] = bf16_to_f32(t.x >> 16);
-    v[2] = bf16_to_f32(t.y & 0xFFFFu);
-    v[3] = bf16_to_f32(t.y >> 16);
-  } else if constexpr (!std::is_same_v<T, float> && CPL == 2) {
-    const uint32_t t = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-    v[0] = bf16_to_f32(t & 0xFFFFu);
-    v[1] = bf16_to_f32(t >> 16);
-  } else {
-    load_ch<T, CPL>(p, v);
-  }
-}
-
 // Load CPL consecutive channels starting at p (p aligned to CPL elements).
 template <class T, int CPL>
 __device__ __forceinline__ void load_ch(const T* __restrict__ p, float (&v)[CPL]) {
@@ -194,8 +160,10 @@ __device__ __forceinline__ void load_ch(const T* __restrict__ p, float (&v)[CPL]
       v[0] = *p;
     }
   } else {
-    static_assert(CPL == 2 || CPL == 4 || CPL == 8, "bf16 channel vector");
-    if constexpr (CPL == 2) {
+    static_assert(CPL == 1 || CPL == 2 || CPL == 4 || CPL == 8, "bf16 channel vector");
+    if constexpr (CPL == 1) {
+      v[0] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+    } else if constexpr (CPL == 2) {
       const uint32_t t = *reinterpret_cast<const uint32_t*>(p);
       v[0] = bf16_to_f32(t & 0xFFFFu);
       v[1] = bf16_to_f32(t >> 16);
@@ -228,7 +196,9 @@ __device__ __forceinline__ void store_ch(T* __restrict__ p, const float (&v)[CPL
       *p = v[0];
     }
   } else {
-    if constexpr (CPL == 2) {
+    if constexpr (CPL == 1) {
+      *reinterpret_cast<uint16_t*>(p) = uint16_t(f32_to_bf16_rne(v[0]));
+    } else if constexpr (CPL == 2) {
       *reinterpret_cast<uint32_t*>(p) = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
     } else if constexpr (CPL == 4) {
       uint2 t;
@@ -243,6 +213,40 @@ __device__ __forceinline__ void store_ch(T* __restrict__ p, const float (&v)[CPL
       t.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
       *reinterpret_cast<uint4*>(p) = t;
     }
+  }
+}
+
+// Streaming variants for data touched once (edge weights in, edge and node
+// outputs out): non-temporal hints keep them from evicting the gathered
+// node rows from the caches.
+typedef float vf4 __attribute__((ext_vector_type(4)));
+typedef float vf2 __attribute__((ext_vector_type(2)));
+typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
+
+template <class T, int CPL>
+__device__ __forceinline__ void load_ch_stream(const T* __restrict__ p, float (&v)[CPL]) {
+  if constexpr (std::is_same_v<T, float> && CPL == 4) {
+    const vf4 t = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
+    v[0] = t.x;
+    v[1] = t.y;
+    v[2] = t.z;
+    v[3] = t.w;
+  } else if constexpr (std::is_same_v<T, float> && CPL == 2) {
+    const vf2 t = __builtin_nontemporal_load(reinterpret_cast<const vf2*>(p));
+    v[0] = t.x;
+    v[1] = t.y;
+  } else if constexpr (!std::is_same_v<T, float> && CPL == 4) {
+    const vu2 t = __builtin_nontemporal_load(reinterpret_cast<const vu2*>(p));
+    v[0] = bf16_to_f32(t.x & 0xFFFFu);
+    v[1] = bf16_to_f32(t.x >> 16);
+    v[2] = bf16_to_f32(t.y & 0xFFFFu);
+    v[3] = bf16_to_f32(t.y >> 16);
+  } else if constexpr (!std::is_same_v<T, float> && CPL == 2) {
+    const uint32_t t = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    v[0] = bf16_to_f32(t & 0xFFFFu);
+    v[1] = bf16_to_f32(t >> 16);
+  } else {
+    load_ch<T, CPL>(p, v);
   }
 }
 

@@ -20,6 +20,11 @@ constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = 64 * kWavesPerBlock;
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 
+// The forward keeps the next edge's x and w in flight (a second register
+// buffer) only when that buffer is small.
+template <class S, int CPL>
+constexpr bool kFwdPrefetch = (Plan<S>::DX + Plan<S>::NP) * CPL <= 64;
+
 // Node handled by this wavefront.  Workgroups are dispatched round-robin
 // over the XCDs (workgroup i on XCD i % 8); each XCD is given a contiguous
 // share of the traversal order, so the nodes that run together on one XCD
@@ -91,6 +96,19 @@ __global__ void __launch_bounds__(kBlock)
     float xc[PL::DX][CPL], wc[PL::NP][CPL];
     int j = g;
     bool vc = valid(j);
+    if constexpr (!kFwdPrefetch<S, CPL>) {
+      for (; j < cn; j += NG) {
+        if (!valid(j)) continue;
+        issue(j, xc, wc);
+        float Y[PL::DY];
+        if constexpr (YG)
+          edge_y<S, true>(ysrc, c0 + j, Y);
+        else
+          edge_y_from_vec<S>(vec[3 * j], vec[3 * j + 1], vec[3 * j + 2], Y);
+        edge_forward<S, CPL>(Y, xc, wc, acc);
+      }
+      continue;
+    }
     if (vc) issue(j, xc, wc);
     while (j < cn) {
       const int jn = j + NG;
@@ -361,8 +379,12 @@ KernelSet make_set(const char* name) {
   for (int i = 0; i < S::NX; ++i) k.x[i] = IrSpec{S::X[i].l, S::X[i].p};
   for (int i = 0; i < S::NY; ++i) k.y[i] = IrSpec{S::Y[i].l, S::Y[i].p};
   for (int i = 0; i < S::NO; ++i) k.o[i] = IrSpec{S::O[i].l, S::O[i].p};
-  sfor_host<0, 2>([&](auto c) {
-    constexpr int CPL = c == 0 ? 2 : 4;
+  k.dx = Plan<S>::DX;
+  k.dy = Plan<S>::DY;
+  k.dout = Plan<S>::DO;
+  k.np = Plan<S>::NP;
+  sfor_host<0, 3>([&](auto c) {
+    constexpr int CPL = 1 << c;
     k.fwd[0][0][c] = &launch_fwd<S, float, CPL, false>;
     k.fwd[0][1][c] = &launch_fwd<S, float, CPL, true>;
     k.fwd[1][0][c] = &launch_fwd<S, bf16_t, CPL, false>;

@@ -58,9 +58,10 @@ struct KernelSet {
   const char* name;
   int nx, ny, no;
   IrSpec x[4], y[4], o[4];
-  // [dtype: 0 f32, 1 bf16][y given][channels per lane: 0 -> 2, 1 -> 4]
-  FwdFn fwd[2][2][2];
-  BwdFn bwd[2][2][2];
+  int dx, dy, dout, np;  // component and path counts of the signature
+  // [dtype: 0 f32, 1 bf16][y given][channels per lane: 0 -> 1, 1 -> 2, 2 -> 4]
+  FwdFn fwd[2][2][3];
+  BwdFn bwd[2][2][3];
   TpFn tp[2];  // 4 channels per lane
 };
 
