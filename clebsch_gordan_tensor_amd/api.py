@@ -64,7 +64,7 @@ def lib():
     L.e3_tp_forward.argtypes = [dp, i64, vp, vp, vp, vp, C.c_int, vp]
     L.e3_conv_forward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, C.c_int, vp]
     L.e3_conv_workspace_size.argtypes = [i32, i32, C.POINTER(sz)]
-    L.e3_conv_prepare_transpose.argtypes = [i32, i32, vp, vp, vp, sz, vp]
+    L.e3_conv_prepare_transpose.argtypes = [i32, i32, vp, vp, vp, vp, sz, vp]
     L.e3_conv_backward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp,
                                    C.c_int, vp]
     L.e3_last_error.restype = C.c_char_p
@@ -240,8 +240,10 @@ def workspace_size(n_nodes: int, n_edges: int) -> int:
     return b.value
 
 
-def conv_prepare_transpose(rowptr, sender, workspace=None, stream=None):
-    """Build the sender-ordered edge index; returns the workspace (uint8 tensor)."""
+def conv_prepare_transpose(rowptr, sender, workspace=None, edge_vec=None, stream=None):
+    """Build the per-graph index (sender-ordered edge list and node locality
+    order); returns the workspace (uint8 tensor).  edge_vec (optional, [E][3]
+    float32) lets the order follow rebuilt positions."""
     import torch
     N, E = rowptr.shape[0] - 1, sender.shape[0]
     nb = workspace_size(N, E)
@@ -249,7 +251,10 @@ def conv_prepare_transpose(rowptr, sender, workspace=None, stream=None):
         workspace = torch.empty(nb, device=rowptr.device, dtype=torch.uint8)
     _need(rowptr, "rowptr", dtype=torch.int32)
     _need(sender, "sender", dtype=torch.int32)
-    _check(lib().e3_conv_prepare_transpose(N, E, _ptr(rowptr), _ptr(sender), _ptr(workspace),
+    if edge_vec is not None:
+        _need(edge_vec, "edge_vec", shape=(E, 3), dtype=torch.float32)
+    _check(lib().e3_conv_prepare_transpose(N, E, _ptr(rowptr), _ptr(sender), _ptr(edge_vec),
+                                           _ptr(workspace),
                                            workspace.numel() * workspace.element_size(),
                                            _stream(stream)))
     return workspace

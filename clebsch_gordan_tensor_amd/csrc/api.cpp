@@ -288,8 +288,8 @@ e3_status e3_conv_workspace_size(int32_t n_nodes, int32_t n_edges, size_t* bytes
 }
 
 e3_status e3_conv_prepare_transpose(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
-                                    const int32_t* sender, void* workspace, size_t ws_bytes,
-                                    void* stream) {
+                                    const int32_t* sender, const float* edge_vec, void* workspace,
+                                    size_t ws_bytes, void* stream) {
   if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
   size_t need = 0;
   e3_conv_workspace_size(n_nodes, n_edges, &need);
@@ -299,6 +299,7 @@ e3_status e3_conv_prepare_transpose(int32_t n_nodes, int32_t n_edges, const int3
   if (n_nodes > 0 && !rowptr) return fail(E3_ERR_INVALID_ARG, "rowptr is null");
   if (n_edges > 0 && !sender) return fail(E3_ERR_INVALID_ARG, "sender is null");
   return hip_status(e3k::launch_prepare_transpose(n_nodes, n_edges, rowptr, sender,
+                                                  n_edges > 0 ? edge_vec : nullptr,
                                                   static_cast<int*>(workspace), hipStream_t(stream)),
                     "prepare_transpose");
 }

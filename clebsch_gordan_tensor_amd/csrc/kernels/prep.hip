@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 
 #include "common.h"
@@ -23,6 +24,7 @@ namespace {
 constexpr int kScanBlock = 256;
 constexpr int kScanItems = 4;
 constexpr int kScanTile = kScanBlock * kScanItems;
+constexpr int kMortonBitsHost = 18;  // Morton cells: 6 bits per axis, 262,144 cells
 
 __global__ void __launch_bounds__(256) k_fill(int* __restrict__ p, int64_t n, int v) {
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
@@ -152,9 +154,13 @@ __global__ void __launch_bounds__(256)
 // its unvisited senders; claims are counted with one atomic per wavefront and
 // appended to `order`.  The order inside a level depends on timing; it only
 // decides which wavefront handles which node later, never a result.
+// When edge vectors are given, a claimed sender also gets a position
+// relative to the root along the traversal tree: pos[a] = pos[u] - r_e
+// (r_e = pos[receiver] - pos[sender]).
 __global__ void __launch_bounds__(256)
     k_bfs_expand(int n_nodes, int n_edges, const int* __restrict__ rowptr,
-                 const int* __restrict__ sender, int* __restrict__ order,
+                 const int* __restrict__ sender, const float* __restrict__ evec,
+                 float* __restrict__ pos, int* __restrict__ order,
                  int* __restrict__ visited, int* __restrict__ tail, int lb, int le) {
   const int lane = threadIdx.x & 63;
   for (int f = lb + blockIdx.x * 4 + (threadIdx.x >> 6); f < le; f += gridDim.x * 4) {
@@ -173,17 +179,106 @@ __global__ void __launch_bounds__(256)
         int base = 0;
         if (lane == 0) base = atomicAdd(tail, __popcll(mask));
         base = __shfl(base, 0, 64);
-        if (claim) order[base + __popcll(mask & ((uint64_t(1) << lane) - 1))] = a;
+        if (claim) {
+          order[base + __popcll(mask & ((uint64_t(1) << lane) - 1))] = a;
+          if (evec) {
+            pos[3 * a] = pos[3 * u] - evec[3 * int64_t(e)];
+            pos[3 * a + 1] = pos[3 * u + 1] - evec[3 * int64_t(e) + 1];
+            pos[3 * a + 2] = pos[3 * u + 2] - evec[3 * int64_t(e) + 2];
+          }
+        }
       }
     }
   }
 }
 
 __global__ void k_bfs_seed(int* __restrict__ order, int* __restrict__ visited,
-                           int* __restrict__ tail, int s) {
+                           int* __restrict__ tail, float* __restrict__ pos, int s) {
   order[0] = s;
   visited[s] = 1;
   *tail = 1;
+  if (pos) pos[3 * s] = pos[3 * s + 1] = pos[3 * s + 2] = 0.0f;
+}
+
+// Order-preserving int key of a float (for atomic min/max).
+__device__ __forceinline__ int fkey(float f) {
+  const int i = __float_as_int(f);
+  return i >= 0 ? i : i ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float kfloat(int k) {
+  return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF);
+}
+
+// Bounding box of the reconstructed positions of order[0 .. n).
+__global__ void __launch_bounds__(256)
+    k_bbox(int n, const int* __restrict__ order, const float* __restrict__ pos,
+           int* __restrict__ box /* min xyz, max xyz as fkey */) {
+  int lo[3] = {INT_MAX, INT_MAX, INT_MAX}, hi[3] = {INT_MIN, INT_MIN, INT_MIN};
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const int v = order[i];
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      const int k = fkey(pos[3 * v + d]);
+      lo[d] = min(lo[d], k);
+      hi[d] = max(hi[d], k);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+    atomicMin(box + d, lo[d]);
+    atomicMax(box + 3 + d, hi[d]);
+  }
+}
+
+// Spread the low 6 bits of v to every third bit.
+__device__ __forceinline__ int spread6(int v) {
+  int r = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) r |= ((v >> b) & 1) << (3 * b);
+  return r;
+}
+
+// Morton code of the cell of each reached node; counts per cell.
+__global__ void __launch_bounds__(256)
+    k_morton_keys(int n, const int* __restrict__ order, const float* __restrict__ pos,
+                  const int* __restrict__ box, int* __restrict__ key, int* __restrict__ hist) {
+  float lo[3], inv[3];
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+    lo[d] = kfloat(box[d]);
+    const float ext = kfloat(box[3 + d]) - lo[d];
+    inv[d] = ext > 0.0f ? 63.999f / ext : 0.0f;
+  }
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const int v = order[i];
+    int c = 0;
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      const int q = min(63, max(0, int((pos[3 * v + d] - lo[d]) * inv[d])));
+      c |= spread6(q) << d;
+    }
+    key[i] = c;
+    atomicAdd(hist + c, 1);
+  }
+}
+
+// Scatter order[0 .. n) into cell order (cells by Morton code; inside a
+// cell the order depends on timing, which only affects scheduling).
+__global__ void __launch_bounds__(256)
+    k_morton_scatter(int n, const int* __restrict__ order, const int* __restrict__ key,
+                     const int* __restrict__ start, int* __restrict__ cursor,
+                     int* __restrict__ out) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const int c = key[i];
+    const int k = start[c] + atomicAdd(cursor + c, 1);
+    if (k < n) out[k] = order[i];
+  }
+}
+
+__global__ void __launch_bounds__(256)
+    k_copy_i32(const int* __restrict__ src, int* __restrict__ dst, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    dst[i] = src[i];
 }
 
 // flag[i] = 1 for nodes the traversal did not reach (flag[n] = 0).
@@ -254,36 +349,82 @@ TransposeLayout transpose_layout(int64_t n_nodes, int64_t n_edges) {
   o += up(n_nodes);
   L.flag = o;
   o += up(n_nodes + 1);
+  L.pos = o;
+  o += up(3 * n_nodes);
+  L.key = o;
+  o += up(n_nodes);
+  L.order2 = o;
+  o += up(n_nodes);
+  L.box = o;
+  o += 64;
+  L.cell = o;
+  o += up((int64_t(1) << kMortonBitsHost) + 1);
+  L.cell_cursor = o;
+  o += up(int64_t(1) << kMortonBitsHost);
   L.bsum = o;
-  o += up((n_nodes + 1 + kScanTile - 1) / kScanTile + 1);
+  // tile sums of the largest scan (the cell counts or the node counts)
+  o += up((std::max<int64_t>(n_nodes + 1, (int64_t(1) << kMortonBitsHost) + 1) + kScanTile - 1) /
+              kScanTile +
+          1);
   L.total_words = o;
   return L;
 }
 
 // Traversal order of the nodes for the convolution kernels (ws + L.order):
-// breadth-first from node 0 over in-edges, then every unreached node in
-// index order.  Neighbouring nodes end up close in the order, so the
+// breadth-first from node 0 over in-edges; with edge vectors, the reached
+// nodes are then re-sorted by the Morton cell of their position rebuilt
+// along the traversal tree; every unreached node follows in index order.  Neighbouring nodes end up close in the order, so the
 // wavefronts that run together gather overlapping node rows.  One host
 // synchronisation per level (the level bounds come back to the host).
 hipError_t build_locality_order(int n_nodes, int n_edges, const int* rowptr, const int* sender,
-                                int* ws, const TransposeLayout& L, hipStream_t s) {
+                                const float* evec, int* ws, const TransposeLayout& L,
+                                hipStream_t s) {
   int* order = ws + L.order;
   int* visited = ws + L.cursor;  // free once the buckets are ranked
   int* tail = ws + L.npad + 1;
+  float* pos = evec ? reinterpret_cast<float*>(ws + L.pos) : nullptr;
   const int64_t n1 = int64_t(n_nodes) + 1;
   hipLaunchKernelGGL(k_fill, dim3(grid_for(n1, 256)), dim3(256), 0, s, visited, n1, 0);
-  hipLaunchKernelGGL(k_bfs_seed, dim3(1), dim3(1), 0, s, order, visited, tail, 0);
+  hipLaunchKernelGGL(k_bfs_seed, dim3(1), dim3(1), 0, s, order, visited, tail, pos, 0);
   int lb = 0, le = 1, h_tail = 1;
   while (lb < le) {
     const unsigned g = unsigned(std::min<int64_t>((int64_t(le - lb) + 3) / 4, 1 << 16));
     hipLaunchKernelGGL(k_bfs_expand, dim3(g), dim3(256), 0, s, n_nodes, n_edges, rowptr, sender,
-                       order, visited, tail, lb, le);
+                       evec, pos, order, visited, tail, lb, le);
     hipError_t err = hipMemcpyAsync(&h_tail, tail, sizeof(int), hipMemcpyDeviceToHost, s);
     if (err == hipSuccess) err = hipStreamSynchronize(s);
     if (err != hipSuccess) return err;
     if (h_tail < le || h_tail > n_nodes) return hipErrorUnknown;  // cannot happen
     lb = le;
     le = h_tail;
+  }
+  const int reached = h_tail;
+  if (pos && reached > 1) {
+    // spatially compact order of the reached nodes: Morton cells of the
+    // reconstructed positions, counting-sorted
+    int* box = ws + L.box;
+    int* key = ws + L.key;
+    int* cell = ws + L.cell;
+    int* cur = ws + L.cell_cursor;
+    const int64_t ncell = int64_t(1) << kMortonBitsHost;
+    hipLaunchKernelGGL(k_fill, dim3(1), dim3(64), 0, s, box, int64_t(3), INT_MAX);
+    hipLaunchKernelGGL(k_fill, dim3(1), dim3(64), 0, s, box + 3, int64_t(3), INT_MIN);
+    hipLaunchKernelGGL(k_fill, dim3(grid_for(ncell + 1, 256)), dim3(256), 0, s, cell, ncell + 1, 0);
+    hipLaunchKernelGGL(k_fill, dim3(grid_for(ncell, 256)), dim3(256), 0, s, cur, ncell, 0);
+    hipLaunchKernelGGL(k_bbox, dim3(grid_for(reached, 256)), dim3(256), 0, s, reached, order, pos,
+                       box);
+    hipLaunchKernelGGL(k_morton_keys, dim3(grid_for(reached, 256)), dim3(256), 0, s, reached, order,
+                       pos, box, key, cell);
+    const unsigned tiles = unsigned((ncell + 1 + kScanTile - 1) / kScanTile);
+    hipLaunchKernelGGL(k_scan_tiles, dim3(tiles), dim3(kScanBlock), 0, s, cell, ncell + 1, cell,
+                       ws + L.bsum);
+    hipLaunchKernelGGL(k_scan_tile_sums, dim3(1), dim3(kScanBlock), 0, s, ws + L.bsum, int(tiles));
+    hipLaunchKernelGGL(k_scan_add, dim3(tiles), dim3(kScanBlock), 0, s, cell, ncell + 1,
+                       ws + L.bsum);
+    hipLaunchKernelGGL(k_morton_scatter, dim3(grid_for(reached, 256)), dim3(256), 0, s, reached,
+                       order, key, cell, cur, ws + L.order2);
+    hipLaunchKernelGGL(k_copy_i32, dim3(grid_for(reached, 256)), dim3(256), 0, s, ws + L.order2,
+                       order, reached);
   }
   if (h_tail < n_nodes) {
     int* flag = ws + L.flag;
@@ -301,7 +442,7 @@ hipError_t build_locality_order(int n_nodes, int n_edges, const int* rowptr, con
 }
 
 hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr, const int* sender,
-                                    int* ws, hipStream_t s) {
+                                    const float* evec, int* ws, hipStream_t s) {
   const TransposeLayout L = transpose_layout(n_nodes, n_edges);
   int* npad = ws + L.npad;
   int* colptr = ws + L.colptr;
@@ -331,7 +472,7 @@ hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr,
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || n_nodes == 0) return err;
-  return build_locality_order(n_nodes, n_edges, rowptr, sender, ws, L, s);
+  return build_locality_order(n_nodes, n_edges, rowptr, sender, evec, ws, L, s);
 }
 
 hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hipStream_t s) {

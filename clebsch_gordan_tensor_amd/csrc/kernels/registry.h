@@ -72,12 +72,13 @@ extern const KernelSet kSetL3to3;
 
 // Prepare-transpose and harmonics launchers (prep.hip).
 hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr, const int* sender,
-                                    int* ws, hipStream_t s);
+                                    const float* evec, int* ws, hipStream_t s);
 hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hipStream_t s);
 
 // Workspace layout of the transposed edge index (int32 words).
 struct TransposeLayout {
-  int64_t npad, colptr, cursor, tmp_e, tmp_b, perm, recv, padlist, order, flag, bsum, total_words;
+  int64_t npad, colptr, cursor, tmp_e, tmp_b, perm, recv, padlist, order, flag, pos, key, order2,
+      box, cell, cell_cursor, bsum, total_words;
 };
 TransposeLayout transpose_layout(int64_t n_nodes, int64_t n_edges);
 

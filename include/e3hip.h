@@ -141,13 +141,18 @@ e3_status e3_conv_workspace_size(int32_t n_nodes, int32_t n_edges, size_t* bytes
  *  - the sender-ordered (transposed) edge list, a counting sort by sender
  *    stable in edge id (the sender-keyed traversal of the e3j backward, E.4),
  *    which the backward pass reads;
- *  - a locality order of the nodes (breadth-first over in-edges, then the
- *    unreached nodes in index order) in which both passes visit nodes.
- * Once per graph.  ws_bytes must be >= e3_conv_workspace_size().  This call
- * synchronises `stream` with the host once per breadth-first level. */
+ *  - a locality order of the nodes in which both passes visit them:
+ *    breadth-first over in-edges from node 0; when edge_vec [E][3] (device,
+ *    r = pos[receiver] - pos[sender]) is given, the reached nodes are then
+ *    sorted by the Morton cell of their position rebuilt along the traversal
+ *    tree; unreached nodes follow in index order.  edge_vec may be NULL.
+ * The order only changes which wavefront handles which node: results are
+ * the same with any order.  Once per graph.  ws_bytes must be >=
+ * e3_conv_workspace_size().  This call synchronises `stream` with the host
+ * once per breadth-first level. */
 e3_status e3_conv_prepare_transpose(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
-                                    const int32_t* sender, void* workspace, size_t ws_bytes,
-                                    void* stream);
+                                    const int32_t* sender, const float* edge_vec, void* workspace,
+                                    size_t ws_bytes, void* stream);
 
 /* Fused convolution backward (e3j E.1 Eq.16 with one scalar per path):
  *   dx[a]  = sum_{e: sender(e)=a} sum_P w[e][P] (Y(r_e) (x)^T dm[recv(e)])_P

@@ -126,8 +126,8 @@ def test_error_codes(lib):
     assert lib.e3_conv_workspace_size(10, 100, C.byref(sz)) == 0
     need = sz.value
     assert need >= 4 * (5 * 100 + 2 * 11)
-    assert lib.e3_conv_prepare_transpose(10, 100, fake, fake, fake, need - 1, None) == -6
-    assert lib.e3_conv_prepare_transpose(10, 100, fake, fake, None, need, None) == -6
+    assert lib.e3_conv_prepare_transpose(10, 100, fake, fake, None, fake, need - 1, None) == -6
+    assert lib.e3_conv_prepare_transpose(10, 100, fake, fake, None, None, need, None) == -6
     assert lib.e3_conv_backward(_desc_c(good), 10, 100, fake, fake, fake, need - 4, fake, fake,
                                 fake, fake, fake, fake, fake, 0, None) == -6
     assert "workspace" in lib.e3_last_error().decode()

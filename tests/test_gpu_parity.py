@@ -38,7 +38,7 @@ def run_conv(gpu, d, g, x, w, dm, dtype="f32", Y=None):
     rowptr, sender = dev(g.rowptr), dev(g.sender)
     ysrc = dev(Y.astype(np.float32)) if Y is not None else dev(g.evec)
     xd, wd, dmd = dev(x, dtype), dev(w, dtype), dev(dm, dtype)
-    ws = gpu.conv_prepare_transpose(rowptr, sender)
+    ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=None if Y is not None else ysrc)
     m = gpu.conv_forward(d, rowptr, sender, ysrc, xd, wd, workspace=ws)
     dx, dw, dY = gpu.conv_backward(d, rowptr, sender, ws, ysrc, xd, wd, dmd)
     # the plain receiver order gives bitwise the same forward result
@@ -237,10 +237,18 @@ def test_transpose_index(gpu):
     assert np.array_equal(perm[:len(real)], order)
     assert np.array_equal(recv[:len(real)], g.receiver[order])
     assert np.array_equal(colptr, np.concatenate([[0], np.cumsum(np.bincount(g.sender[real], minlength=N))]))
-    # the locality order is a permutation of the nodes
+    # the locality order is a permutation of the nodes, with and without the
+    # positions rebuilt from edge vectors
     o2 = o + 5 * up(E)
     order = words[o2:o2 + N]
     assert np.array_equal(np.sort(order), np.arange(N))
+    ws2 = api.conv_prepare_transpose(dev(g.rowptr), dev(g.sender), edge_vec=dev(g.evec))
+    torch.cuda.synchronize()
+    w2 = ws2.view(torch.int32).cpu().numpy()
+    assert np.array_equal(np.sort(w2[o2:o2 + N]), np.arange(N))
+    assert np.array_equal(w2[64:64 + N + 1], colptr)
+    nr = len(real)  # the tail of perm past the real edges is not written
+    assert np.array_equal(w2[o + 2 * up(E): o + 2 * up(E) + nr], perm[:nr])
 
 
 # ---------------------------------------------------- tensor product (rows)
