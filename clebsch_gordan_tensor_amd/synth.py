@@ -240,6 +240,7 @@ class TPProblem:
     x: np.ndarray    # [B, dx, C]
     u: np.ndarray    # [B, 3] random unit vectors (y = harmonics of u)
     w: np.ndarray    # [B, P, C]
+    dz: np.ndarray = None  # [B, dout, C] upstream gradient of z
     dtype: str = "f32"
 
 
@@ -309,7 +310,7 @@ def make_conv(name: str, seed: int = 0, with_dm: bool = True) -> ConvProblem:
                        x=x, w=w, dm=dm, dtype=cfg["dtype"], extra=dict(cfg, box=box))
 
 
-def make_tp(seed: int = 0, rows: int | None = None) -> TPProblem:
+def make_tp(seed: int = 0, rows: int | None = None, with_dz: bool = False) -> TPProblem:
     cfg = TP_CONFIG
     B = cfg["rows"] if rows is None else rows
     C, xi = parse_irreps(cfg["x"])
@@ -320,5 +321,6 @@ def make_tp(seed: int = 0, rows: int | None = None) -> TPProblem:
     u /= np.linalg.norm(u, axis=1, keepdims=True)
     x = normal((B, dim(xi), C), seed, TAG_X)
     w = normal((B, P, C), seed, TAG_W)
+    dz = normal((B, dim(oi), C), seed, TAG_DM) if with_dz else None
     return TPProblem(name="tp", x_irreps=xi, y_irreps=yi, out_irreps=oi, channels=C, x=x,
-                     u=u.astype(np.float32), w=w, dtype="f32")
+                     u=u.astype(np.float32), w=w, dz=dz, dtype="f32")

@@ -589,3 +589,151 @@ int oracle_sh_batch(int lmax, int64_t n, const double *r, double *out) {
   for (int64_t i = 0; i < n; ++i) oracle_sh(lmax, r + 3 * i, out + i * d);
   return 0;
 }
+
+/* Batched TP backward, the VJP of oracle_tp_forward ([e3j] E.1 Eq.14-15:
+ * each cotangent is the tensor product with the coefficient records
+ * permuted, here with the per-path scalars of Eq.11):
+ *   dx[r][xoff+m1][q] = sum_P w[r][P][q] sum_{M,m2} T_P[M][m1][m2] y[r][yoff+m2] dz[r][ooff+M][q]
+ *   dw[r][P][q]       = sum_M (sum_{m1,m2} T_P[M][m1][m2] x[r][xoff+m1][q] y[r][yoff+m2]) dz[r][ooff+M][q]
+ *   dy[r][yoff+m2]    = sum_q sum_P w[r][P][q] sum_{M,m1} T_P[M][m1][m2] x[r][xoff+m1][q] dz[r][ooff+M][q]
+ * for rows[0..nrows-1]; dx [nrows][dx][C], dw [nrows][P][C], dy [nrows][dy]. */
+int oracle_tp_backward(const oracle_desc *d, int64_t n_rows, const double *x, const double *y,
+                       const double *w, const double *dz, int nrows, const int64_t *rows,
+                       double *dxo, double *dwo, double *dyo) {
+  oplan *pl = malloc(sizeof(oplan));
+  if (plan_build(d, pl) != 0) {
+    plan_free(pl);
+    free(pl);
+    return -1;
+  }
+  const int C = d->C, P = pl->np, dx = pl->dx, dy = pl->dy, dout = pl->dout;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int i = 0; i < nrows; ++i) {
+    double *dxr = dxo + (int64_t)i * dx * C, *dwr = dwo + (int64_t)i * P * C;
+    double *dyr = dyo + (int64_t)i * dy;
+    memset(dxr, 0, sizeof(double) * dx * C);
+    memset(dwr, 0, sizeof(double) * P * C);
+    memset(dyr, 0, sizeof(double) * dy);
+    int64_t r = rows[i];
+    if (r < 0 || r >= n_rows) {
+      bad = 1;
+      continue;
+    }
+    const double *xr = x + r * dx * C, *yr = y + r * dy, *wr = w + r * P * C;
+    const double *dzr = dz + r * dout * C;
+    for (int pi = 0; pi < P; ++pi) {
+      const opath *p = &pl->p[pi];
+      int n1 = 2 * p->l1 + 1, n2 = 2 * p->l2 + 1, nL = 2 * p->L + 1;
+      for (int M = 0; M < nL; ++M)
+        for (int m1 = 0; m1 < n1; ++m1)
+          for (int m2 = 0; m2 < n2; ++m2) {
+            double c = p->T[(M * n1 + m1) * n2 + m2];
+            if (c == 0.0) continue;
+            for (int q = 0; q < C; ++q) {
+              double g = dzr[(p->ooff + M) * C + q];
+              double xv = xr[(p->xoff + m1) * C + q], yv = yr[p->yoff + m2];
+              dxr[(p->xoff + m1) * C + q] += wr[pi * C + q] * c * yv * g;
+              dwr[pi * C + q] += c * xv * yv * g;
+              dyr[p->yoff + m2] += wr[pi * C + q] * c * xv * g;
+            }
+          }
+    }
+  }
+  plan_free(pl);
+  free(pl);
+  return bad ? -1 : 0;
+}
+
+/* Gradient of the harmonics with respect to the (unnormalised) vector:
+ * out[k] = sum_m dY[m] dY_lm/dr_k for l = 0..lmax, i.e. J^T dY with
+ * J = dY/dr.  Written from the closed forms of oracle_sh_l: with
+ * u = r/|r| the harmonics are polynomials P(u), and
+ * dP/dr = (I - u u^T) grad_u P / |r|.  A zero vector gives 0. */
+int oracle_sh_grad(int lmax, const double r[3], const double *dY, double out[3]) {
+  if (lmax < 0 || lmax > ORACLE_MAX_L) return -1;
+  out[0] = out[1] = out[2] = 0.0;
+  double n = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+  if (n == 0.0) return 0;
+  double x = r[0] / n, y = r[1] / n, z = r[2] / n;
+  double g[3] = {0, 0, 0}; /* sum_m dY[m] grad_u P_lm(u) */
+  int o = 0;
+  for (int l = 0; l <= lmax; ++l) {
+    const double *w = dY + o;
+    /* partial derivatives of each component polynomial, (d/dx, d/dy, d/dz) */
+    double d[7][3];
+    int nm = 2 * l + 1;
+    switch (l) {
+      case 0:
+        d[0][0] = d[0][1] = d[0][2] = 0.0;
+        break;
+      case 1: {
+        double s3 = sqrt(3.0);
+        double t[3][3] = {{0, s3, 0}, {0, 0, s3}, {s3, 0, 0}}; /* y, z, x */
+        memcpy(d, t, sizeof(t));
+        break;
+      }
+      case 2: {
+        double s15 = sqrt(15.0), s5 = sqrt(5.0);
+        double t[5][3] = {{s15 * y, s15 * x, 0},
+                          {0, s15 * z, s15 * y},
+                          {-s5 * x, -s5 * y, 2 * s5 * z},
+                          {s15 * z, 0, s15 * x},
+                          {s15 * x, -s15 * y, 0}};
+        memcpy(d, t, sizeof(t));
+        break;
+      }
+      case 3: {
+        double a = sqrt(35.0 / 8.0), b = sqrt(105.0), c = sqrt(21.0 / 8.0), e = sqrt(7.0);
+        double q = 4 * z * z - x * x - y * y;
+        double t[7][3] = {
+            {a * 6 * x * y, a * (3 * x * x - 3 * y * y), 0},
+            {b * y * z, b * x * z, b * x * y},
+            {c * y * (-2 * x), c * (q - 2 * y * y), c * y * 8 * z},
+            {0.5 * e * z * (-6 * x), 0.5 * e * z * (-6 * y), 0.5 * e * (6 * z * z - 3 * x * x - 3 * y * y)},
+            {c * (q - 2 * x * x), c * x * (-2 * y), c * x * 8 * z},
+            {0.5 * b * 2 * x * z, -0.5 * b * 2 * y * z, 0.5 * b * (x * x - y * y)},
+            {a * (3 * x * x - 3 * y * y), a * (-6 * x * y), 0}};
+        memcpy(d, t, sizeof(t));
+        break;
+      }
+    }
+    for (int m = 0; m < nm; ++m)
+      for (int k = 0; k < 3; ++k) g[k] += w[m] * d[m][k];
+    o += nm;
+  }
+  /* project out the radial part and scale by 1/|r| */
+  double u[3] = {x, y, z};
+  double ug = u[0] * g[0] + u[1] * g[1] + u[2] * g[2];
+  for (int k = 0; k < 3; ++k) out[k] = (g[k] - u[k] * ug) / n;
+  return 0;
+}
+
+int oracle_sh_grad_batch(int lmax, int64_t n, const double *r, const double *dY, double *out) {
+  if (lmax < 0 || lmax > ORACLE_MAX_L) return -1;
+  const int d = (lmax + 1) * (lmax + 1);
+  for (int64_t i = 0; i < n; ++i) oracle_sh_grad(lmax, r + 3 * i, dY + i * d, out + 3 * i);
+  return 0;
+}
+
+/* Position gradient from edge-vector gradients.  With r_e = pos[recv(e)] -
+ * pos[sender(e)], a scalar E that depends on the positions only through the
+ * r_e has dE/dpos[b] = sum_{e: recv(e)=b} g_e - sum_{e: sender(e)=b} g_e,
+ * g_e = dE/dr_e; the force is F_b = -dE/dpos[b] (conservative forces, the
+ * third page, 2.2 Eq.3).  Padding edges (sender outside [0,N)) are skipped.
+ * dpos [N][3]. */
+int oracle_edge_grad_to_nodes(int n_nodes, int64_t n_edges, const int *rowptr, const int *sender,
+                              const double *g, double *dpos) {
+  if (n_nodes < 0 || n_edges < 0 || rowptr[0] != 0 || rowptr[n_nodes] != n_edges) return -1;
+  memset(dpos, 0, sizeof(double) * 3 * (size_t)n_nodes);
+  for (int b = 0; b < n_nodes; ++b)
+    for (int e = rowptr[b]; e < rowptr[b + 1]; ++e) {
+      int a = sender[e];
+      if (a < 0 || a >= n_nodes) continue;
+      for (int k = 0; k < 3; ++k) {
+        dpos[3 * b + k] += g[3 * e + k];
+        dpos[3 * a + k] -= g[3 * e + k];
+      }
+    }
+  return 0;
+}

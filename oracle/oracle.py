@@ -59,6 +59,13 @@ def _load():
     lib.oracle_conv_backward_edge.restype = C.c_int
     lib.oracle_conv_backward_edge.argtypes = [C.c_void_p, C.c_int, C.c_int64, ip, ip, dp, dp,
                                               dp, dp, dp, C.c_int, lp, dp, dp]
+    lib.oracle_tp_backward.restype = C.c_int
+    lib.oracle_tp_backward.argtypes = [C.c_void_p, C.c_int64, dp, dp, dp, dp, C.c_int, lp, dp,
+                                       dp, dp]
+    lib.oracle_sh_grad_batch.restype = C.c_int
+    lib.oracle_sh_grad_batch.argtypes = [C.c_int, C.c_int64, dp, dp, dp]
+    lib.oracle_edge_grad_to_nodes.restype = C.c_int
+    lib.oracle_edge_grad_to_nodes.argtypes = [C.c_int, C.c_int64, ip, ip, dp, dp]
     _lib = lib
     return lib
 
@@ -257,3 +264,42 @@ def conv_backward_edge(d: Desc, rowptr, sender, x, w, dm, evec=None, Y=None, edg
     if r != 0:
         raise ValueError("oracle_conv_backward_edge rejected its arguments")
     return dw, dY
+
+
+def tp_backward(d: Desc, x, y, w, dz, rows=None):
+    """(dx, dw, dy) of the batched TP for the cotangent dz, at rows (all by
+    default): shapes [len][dx][C], [len][P][C], [len][dy]."""
+    x, y, w, dz = _f64(x), _f64(y), _f64(w), _f64(dz)
+    n = x.shape[0]
+    rows = np.arange(n, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    P = num_paths(d)
+    dx = np.zeros((rows.shape[0], d.dx, d.C))
+    dw = np.zeros((rows.shape[0], P, d.C))
+    dy = np.zeros((rows.shape[0], d.dy))
+    r = _load().oracle_tp_backward(d.ptr(), n, _dp(x), _dp(y), _dp(w), _dp(dz), rows.shape[0],
+                                   _lp(rows), _dp(dx), _dp(dw), _dp(dy))
+    if r != 0:
+        raise ValueError("oracle_tp_backward rejected its arguments")
+    return dx, dw, dy
+
+
+def sh_grad(lmax: int, vecs, dY) -> np.ndarray:
+    """Vector gradient J^T dY of the harmonics of vecs [n][3], dY [n][(lmax+1)^2]."""
+    v = _f64(vecs).reshape(-1, 3)
+    g = _f64(dY).reshape(v.shape[0], (lmax + 1) ** 2)
+    out = np.zeros((v.shape[0], 3))
+    if _load().oracle_sh_grad_batch(lmax, v.shape[0], _dp(v), _dp(g), _dp(out)) != 0:
+        raise ValueError("lmax out of range")
+    return out
+
+
+def edge_grad_to_nodes(rowptr, sender, g) -> np.ndarray:
+    """dpos [N][3] from edge-vector gradients g [E][3] (r_e = pos[recv] - pos[sender])."""
+    rowptr, sender = _i32(rowptr), _i32(sender)
+    g = _f64(g).reshape(sender.shape[0], 3)
+    n = rowptr.shape[0] - 1
+    out = np.zeros((n, 3))
+    if _load().oracle_edge_grad_to_nodes(n, sender.shape[0], _ip(rowptr), _ip(sender), _dp(g),
+                                         _dp(out)) != 0:
+        raise ValueError("oracle_edge_grad_to_nodes rejected its arguments")
+    return out
