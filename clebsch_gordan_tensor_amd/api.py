@@ -40,8 +40,9 @@ class _Desc(C.Structure):
 
 
 EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
-           "e3_spherical_harmonics", "e3_tp_forward", "e3_conv_forward",
-           "e3_conv_workspace_size", "e3_conv_prepare_transpose", "e3_conv_backward",
+           "e3_spherical_harmonics", "e3_spherical_harmonics_backward", "e3_tp_forward",
+           "e3_tp_backward", "e3_conv_forward", "e3_conv_workspace_size",
+           "e3_conv_prepare_transpose", "e3_conv_backward", "e3_edge_grad_to_nodes",
            "e3_last_error"]
 
 
@@ -61,7 +62,10 @@ def lib():
     L.e3_supported.restype = i32
     L.e3_cg_block.argtypes = [i32, i32, i32, C.POINTER(C.c_double)]
     L.e3_spherical_harmonics.argtypes = [i32, i64, vp, vp, vp]
+    L.e3_spherical_harmonics_backward.argtypes = [i32, i64, vp, vp, vp, vp]
     L.e3_tp_forward.argtypes = [dp, i64, vp, vp, vp, vp, C.c_int, vp]
+    L.e3_tp_backward.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, C.c_int, vp]
+    L.e3_edge_grad_to_nodes.argtypes = [i32, i32, vp, vp, vp, sz, vp, vp, vp]
     L.e3_conv_forward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, C.c_int, vp]
     L.e3_conv_workspace_size.argtypes = [i32, i32, C.POINTER(sz)]
     L.e3_conv_prepare_transpose.argtypes = [i32, i32, vp, vp, vp, vp, sz, vp]
@@ -196,6 +200,45 @@ def spherical_harmonics(lmax: int, vec, out=None, stream=None):
     return out
 
 
+def spherical_harmonics_backward(lmax: int, vec, dY, out=None, stream=None):
+    """dvec [n][3] = J^T dY, J the Jacobian of the harmonics of vec [n][3]."""
+    import torch
+    _need(vec, "vec", dtype=torch.float32)
+    n = vec.shape[0]
+    _need(vec, "vec", shape=(n, 3))
+    _need(dY, "dY", shape=(n, (lmax + 1) ** 2), dtype=torch.float32)
+    if out is None:
+        out = torch.empty((n, 3), device=vec.device, dtype=torch.float32)
+    _need(out, "out", shape=(n, 3), dtype=torch.float32)
+    _check(lib().e3_spherical_harmonics_backward(lmax, n, _ptr(vec), _ptr(dY), _ptr(out),
+                                                 _stream(stream)))
+    return out
+
+
+def tp_backward(desc: Desc, x, y, w, dz, dx=None, dw=None, dy=None, stream=None):
+    """(dx, dw, dy) of z = tp_forward(x, y, w) for the cotangent dz."""
+    import torch
+    B = x.shape[0]
+    P = num_paths(desc)
+    _need(x, "x", shape=(B, desc.dx, desc.channels))
+    _need(y, "y", shape=(B, desc.dy), dtype=torch.float32)
+    _need(w, "w", shape=(B, P, desc.channels), dtype=x.dtype)
+    _need(dz, "dz", shape=(B, desc.dout, desc.channels), dtype=x.dtype)
+    dev, dt = x.device, x.dtype
+    if dx is None:
+        dx = torch.empty((B, desc.dx, desc.channels), device=dev, dtype=dt)
+    if dw is None:
+        dw = torch.empty((B, P, desc.channels), device=dev, dtype=dt)
+    if dy is None:
+        dy = torch.empty((B, desc.dy), device=dev, dtype=torch.float32)
+    _need(dx, "dx", shape=(B, desc.dx, desc.channels), dtype=dt)
+    _need(dw, "dw", shape=(B, P, desc.channels), dtype=dt)
+    _need(dy, "dy", shape=(B, desc.dy), dtype=torch.float32)
+    _check(lib().e3_tp_backward(C.byref(desc.c()), B, _ptr(x), _ptr(y), _ptr(w), _ptr(dz),
+                                _ptr(dx), _ptr(dw), _ptr(dy), _dtype_code(x), _stream(stream)))
+    return dx, dw, dy
+
+
 def tp_forward(desc: Desc, x, y, w, out=None, stream=None):
     import torch
     B = x.shape[0]
@@ -287,3 +330,21 @@ def conv_backward(desc: Desc, rowptr, sender, workspace, edge_vec_or_Y, x, w, dm
                                   _ptr(edge_vec_or_Y), _ptr(x), _ptr(w), _ptr(dm), _ptr(dx),
                                   _ptr(dw), _ptr(dY), _dtype_code(x), _stream(stream)))
     return dx, dw, dY
+
+
+def edge_grad_to_nodes(rowptr, sender, workspace, edge_grad, out=None, stream=None):
+    """node_grad [N][3]: sum of edge_grad over each node's in-edges minus the
+    sum over its out-edges (r_e = pos[recv] - pos[sender]); forces are its
+    negative.  workspace: from conv_prepare_transpose on the same graph."""
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    _need(edge_grad, "edge_grad", shape=(E, 3), dtype=torch.float32)
+    if out is None:
+        out = torch.empty((N, 3), device=rowptr.device, dtype=torch.float32)
+    _need(out, "out", shape=(N, 3), dtype=torch.float32)
+    _check(lib().e3_edge_grad_to_nodes(N, E, _ptr(rowptr), _ptr(sender), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _ptr(edge_grad), _ptr(out), _stream(stream)))
+    return out

@@ -112,20 +112,21 @@ int group_lanes(int C, int cpl) {
   return G;
 }
 
-enum class Kind { fwd, bwd, tp };
+enum class Kind { fwd, bwd, tp, tpb };
 
 // Per-lane register estimate (fp32 words) of a kernel holding cpl channels
 // per lane: feature, weight and accumulator vectors scale with cpl, the
 // harmonics and the per-edge coefficient temporaries do not.
 int register_estimate(const e3k::KernelSet& k, Kind kind, int cpl) {
   if (kind == Kind::bwd) return (3 * k.dx + k.np + k.dout) * cpl + 2 * k.dy + 48;
+  if (kind == Kind::tpb) return (2 * k.dx + k.np + k.dout) * cpl + 2 * k.dy + 48;
   return (k.dx + k.np + k.dout) * cpl + k.dy + 40;
 }
 
 // Channels per lane: the largest of 4, 2, 1 whose register estimate keeps
-// several wavefronts per SIMD (forward 176, backward 176 words), with
-// G = C / cpl lanes per edge group a power of two <= 64.  The tensor
-// product uses 4.  E3HIP_FWD_CPL / E3HIP_BWD_CPL (1, 2 or 4) force a choice
+// several wavefronts per SIMD (176 words), with G = C / cpl lanes per edge
+// group a power of two <= 64; the backward passes try 2 first.  The tensor
+// product forward uses 4.  E3HIP_FWD_CPL / E3HIP_BWD_CPL (1, 2 or 4) force a choice
 // when it is valid, for tuning.
 int choose_cpl(const e3k::KernelSet& k, Kind kind, int C) {
   if (kind == Kind::tp) return group_lanes(C, 4) > 0 ? 4 : -1;
@@ -141,7 +142,7 @@ int choose_cpl(const e3k::KernelSet& k, Kind kind, int C) {
   if ((force == 1 || force == 2 || force == 4) && group_lanes(C, force) > 0) return force;
   // the backward of the small signatures is best at two channels per lane
   // (one edge per wavefront at C = 128): prefer 2 there over 4
-  const int first = kind == Kind::bwd ? 2 : 4;
+  const int first = kind == Kind::fwd ? 4 : 2;
   for (int cpl : {first, first == 4 ? 2 : 1, 1}) {
     if (group_lanes(C, cpl) <= 0) continue;
     if (register_estimate(k, kind, cpl) <= 176) return cpl;
@@ -248,6 +249,51 @@ e3_status e3_tp_forward(const e3_desc* desc, int64_t n_rows, const void* x, cons
     return fail(E3_ERR_ALIGNMENT, "x, w and z must be 16-byte aligned");
   e3k::TpArgs a{n_rows, p.C, G, x, y, w, z};
   return hip_status(ks->tp[dtype](a, hipStream_t(stream)), "tp_forward");
+}
+
+e3_status e3_tp_backward(const e3_desc* desc, int64_t n_rows, const void* x, const float* y,
+                         const void* w, const void* dz, void* dx, void* dw, float* dy,
+                         e3_dtype dtype, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  const e3k::KernelSet* ks;
+  int G, ci;
+  if ((s = select(p, dtype, Kind::tpb, ks, G, ci)) != E3_OK) return s;
+  if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows == 0) return ok();
+  if (!x || !y || !w || !dz || !dx || !dw || !dy) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(dz) || !aligned16(dx) || !aligned16(dw))
+    return fail(E3_ERR_ALIGNMENT, "x, w, dz, dx and dw must be 16-byte aligned");
+  e3k::TpBwdArgs a{n_rows, p.C, G, x, y, w, dz, dx, dw, dy};
+  return hip_status(ks->tpb[dtype][ci](a, hipStream_t(stream)), "tp_backward");
+}
+
+e3_status e3_spherical_harmonics_backward(int32_t lmax, int64_t n, const float* vec,
+                                          const float* dY, float* dvec, void* stream) {
+  if (lmax < 0 || lmax > 3) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..3");
+  if (n < 0) return fail(E3_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return ok();
+  if (!vec || !dY || !dvec) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  return hip_status(e3k::launch_harmonics_grad(lmax, n, vec, dY, dvec, hipStream_t(stream)),
+                    "harmonics_backward");
+}
+
+e3_status e3_edge_grad_to_nodes(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                                const int32_t* sender, const void* workspace, size_t ws_bytes,
+                                const float* edge_grad, float* node_grad, void* stream) {
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes == 0) return ok();
+  size_t need = 0;
+  e3_conv_workspace_size(n_nodes, n_edges, &need);
+  if (!workspace || ws_bytes < need)
+    return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  if (!rowptr || !node_grad || (n_edges > 0 && (!sender || !edge_grad)))
+    return fail(E3_ERR_INVALID_ARG, "null pointer");
+  return hip_status(e3k::launch_edge_grad_to_nodes(n_nodes, n_edges, rowptr, sender,
+                                                   static_cast<const int*>(workspace), edge_grad,
+                                                   node_grad, hipStream_t(stream)),
+                    "edge_grad_to_nodes");
 }
 
 e3_status e3_conv_forward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,

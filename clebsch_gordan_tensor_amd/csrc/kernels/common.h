@@ -272,12 +272,34 @@ __device__ __forceinline__ void store_ch_stream(T* __restrict__ p, const float (
 
 // ------------------------------------------------------------- harmonics
 
-// Component-normalised real harmonics of degree l (m = -l..l) of r/|r|,
-// written into out[0..2l].  A zero vector gives 0 for l >= 1.
-template <int L>
-__device__ __forceinline__ void harmonics_l(float x, float y, float z, float* out) {
+// Value and gradient along the three axes, for differentiating the
+// harmonic polynomials below by forward-mode arithmetic.
+struct Dual3 {
+  float v, d0, d1, d2;
+  __device__ Dual3(float c = 0.0f) : v(c), d0(0.0f), d1(0.0f), d2(0.0f) {}
+  __device__ Dual3(float c, float a, float b, float e) : v(c), d0(a), d1(b), d2(e) {}
+};
+__device__ __forceinline__ Dual3 operator+(Dual3 a, Dual3 b) {
+  return {a.v + b.v, a.d0 + b.d0, a.d1 + b.d1, a.d2 + b.d2};
+}
+__device__ __forceinline__ Dual3 operator-(Dual3 a, Dual3 b) {
+  return {a.v - b.v, a.d0 - b.d0, a.d1 - b.d1, a.d2 - b.d2};
+}
+__device__ __forceinline__ Dual3 operator*(Dual3 a, Dual3 b) {
+  return {a.v * b.v, fmaf(a.d0, b.v, a.v * b.d0), fmaf(a.d1, b.v, a.v * b.d1),
+          fmaf(a.d2, b.v, a.v * b.d2)};
+}
+__device__ __forceinline__ Dual3 operator*(float c, Dual3 a) {
+  return {c * a.v, c * a.d0, c * a.d1, c * a.d2};
+}
+
+// Component-normalised real harmonics of degree l (m = -l..l) of the unit
+// vector (x, y, z), written into out[0..2l]; Sc is float, or Dual3 to get
+// the partial derivatives of each polynomial as well.
+template <int L, class Sc>
+__device__ __forceinline__ void harmonics_l(Sc x, Sc y, Sc z, Sc* out) {
   if constexpr (L == 0) {
-    out[0] = 1.0f;
+    out[0] = Sc(1.0f);
   } else if constexpr (L == 1) {
     const float k = 1.7320508075688772f;  // sqrt(3)
     out[0] = k * y;
@@ -286,7 +308,7 @@ __device__ __forceinline__ void harmonics_l(float x, float y, float z, float* ou
   } else if constexpr (L == 2) {
     const float k15 = 3.872983346207417f;        // sqrt(15)
     const float k5h = 1.118033988749895f;        // sqrt(5)/2
-    const float xx = x * x, yy = y * y, zz = z * z;
+    const Sc xx = x * x, yy = y * y, zz = z * z;
     out[0] = k15 * x * y;
     out[1] = k15 * y * z;
     out[2] = k5h * (2.0f * zz - xx - yy);
@@ -298,8 +320,8 @@ __device__ __forceinline__ void harmonics_l(float x, float y, float z, float* ou
     const float b = 10.246950765959598f;  // sqrt(105)
     const float c = 1.620185174601965f;   // sqrt(21/8)
     const float d = 1.3228756555322954f;  // sqrt(7)/2
-    const float xx = x * x, yy = y * y, zz = z * z;
-    const float t = 4.0f * zz - xx - yy;
+    const Sc xx = x * x, yy = y * y, zz = z * z;
+    const Sc t = 4.0f * zz - xx - yy;
     out[0] = a * (3.0f * xx - yy) * y;
     out[1] = b * x * y * z;
     out[2] = c * y * t;

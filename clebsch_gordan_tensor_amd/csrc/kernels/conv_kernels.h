@@ -152,6 +152,37 @@ __global__ void __launch_bounds__(kBlock)
 }
 
 // ------------------------------------------------------------ backward
+
+// dst[0..N) = sum of v[0..N) over the G lanes of this lane's edge group (cl
+// is the lane's index in the group): a reduce-scatter, after which the
+// lanes that own distinct sums store them.  Lanes of other groups are never
+// read, so groups past the end of the work may have returned already; with
+// G = 64 the whole wavefront must be present.
+template <int N>
+__device__ __forceinline__ void store_group_sum(const float (&v)[N], int G, int lane, int cl,
+                                                float* __restrict__ dst) {
+  if (G == 64) {  // VALU-only cross-lane moves
+    constexpr int NP = pow2_ceil_c(N);
+    float t[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) t[i] = i < N ? v[i] : 0.0f;
+    const int first = wave_reduce_scatter<N>(t, lane);
+    if ((lane & 3) == 0 && first < N) dst[first] = t[0];
+  } else {
+    Scatter<N> sc;
+    reduce_scatter<N>(v, G, lane, sc);
+    constexpr int NP = Scatter<N>::NP;
+    const int dup = (G > NP ? G / NP : 1) - 1;  // lanes holding copies
+    if ((cl & dup) == 0) {
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int idx = sc.first + i;
+        if (i < sc.count && idx < N) dst[idx] = sc.v[i];
+      }
+    }
+  }
+}
+
 // Sender-ordered walk over the transposed index (colptr, perm, recv):
 // dx[a] accumulates in registers over a's out-edges; dw[e] and dY[e] are
 // edge-local and written once (e3j E.1 Eq.16; the sender-keyed reduction of
@@ -228,29 +259,8 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
     for (int i = 0; i < PL::DY; ++i) dYl[i] = 0.0f;
     edge_backward<S, CPL>(Y, xv, wv, dmv, dxa, dw + int64_t(e) * PL::NP * C + ch0, C, dYl);
-    // dY[e] = sum over the group's channels: reduce-scatter, then the
-    // lanes that own distinct values store them
-    float* dYe = dY + int64_t(e) * PL::DY;
-    if (G == 64) {  // one edge per wavefront: VALU-only cross-lane moves
-      constexpr int NPY = pow2_ceil_c(PL::DY);
-      float v[NPY];
-#pragma unroll
-      for (int i = 0; i < NPY; ++i) v[i] = i < PL::DY ? dYl[i] : 0.0f;
-      const int first = wave_reduce_scatter<PL::DY>(v, lane);
-      if ((lane & 3) == 0 && first < PL::DY) dYe[first] = v[0];
-    } else {
-      Scatter<PL::DY> sc;
-      reduce_scatter<PL::DY>(dYl, G, lane, sc);
-      constexpr int NPY = Scatter<PL::DY>::NP;
-      const int dup = (G > NPY ? G / NPY : 1) - 1;  // lanes holding copies
-      if ((cl & dup) == 0) {
-#pragma unroll
-        for (int i = 0; i < NPY; ++i) {
-          const int idx = sc.first + i;
-          if (i < sc.count && idx < PL::DY) dYe[idx] = sc.v[i];
-        }
-      }
-    }
+    // dY[e] = sum over the group's channels
+    store_group_sum<PL::DY>(dYl, G, lane, cl, dY + int64_t(e) * PL::DY);
   }
   }
 
@@ -313,6 +323,51 @@ __global__ void __launch_bounds__(kBlock)
   for (int i = 0; i < PL::DO; ++i) store_ch<T, CPL>(zr + int64_t(i) * C, acc[i]);
 }
 
+// Batched tensor-product backward (e3j E.1 Eq.14-16, one scalar per path):
+// for the cotangent dz of z,
+//   dx[r] = sum_P w[r][P] (y[r] (x)^T dz[r])_P,  dw[r][P] = <(x[r] (x) y[r])_P, dz[r]>,
+//   dy[r] = sum over channels of sum_P w[r][P] (x[r] (x)^T dz[r])_P,
+// in one pass over the row; each edge group handles one row.
+template <class S, class T, int CPL>
+__global__ void __launch_bounds__(kBlock)
+    k_tp_bwd(int64_t n_rows, int C, int G, const T* __restrict__ x, const float* __restrict__ y,
+             const T* __restrict__ w, const T* __restrict__ dz, T* __restrict__ dx,
+             T* __restrict__ dw, float* __restrict__ dy) {
+  using PL = Plan<S>;
+  const int lane = threadIdx.x & 63;
+  const int NG = 64 / G;
+  const int g = lane / G, cl = lane - g * G, c0 = cl * CPL;
+  const int64_t row =
+      (int64_t(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6)) * NG + g;
+  if (row >= n_rows) return;  // group-uniform (wave-uniform when G = 64)
+
+  float Y[PL::DY];
+  edge_y<S, true>(y, row, Y);
+  float xv[PL::DX][CPL], wv[PL::NP][CPL], dzv[PL::DO][CPL];
+  const T* xr = x + row * PL::DX * C + c0;
+#pragma unroll
+  for (int i = 0; i < PL::DX; ++i) load_ch_stream<T, CPL>(xr + int64_t(i) * C, xv[i]);
+  const T* wr = w + row * PL::NP * C + c0;
+#pragma unroll
+  for (int p = 0; p < PL::NP; ++p) load_ch_stream<T, CPL>(wr + int64_t(p) * C, wv[p]);
+  const T* dzr = dz + row * PL::DO * C + c0;
+#pragma unroll
+  for (int i = 0; i < PL::DO; ++i) load_ch_stream<T, CPL>(dzr + int64_t(i) * C, dzv[i]);
+
+  float dxr[PL::DX][CPL], dYl[PL::DY];
+#pragma unroll
+  for (int i = 0; i < PL::DX; ++i)
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) dxr[i][k] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PL::DY; ++i) dYl[i] = 0.0f;
+  edge_backward<S, CPL>(Y, xv, wv, dzv, dxr, dw + row * PL::NP * C + c0, C, dYl);
+  T* dxo = dx + row * PL::DX * C + c0;
+#pragma unroll
+  for (int i = 0; i < PL::DX; ++i) store_ch_stream<T, CPL>(dxo + int64_t(i) * C, dxr[i]);
+  store_group_sum<PL::DY>(dYl, G, lane, cl, dy + row * PL::DY);
+}
+
 // ------------------------------------------------------------ launchers
 
 template <int B, int E, class F>
@@ -369,6 +424,18 @@ hipError_t launch_tp(const TpArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <class S, class T, int CPL>
+hipError_t launch_tp_bwd(const TpBwdArgs& a, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  const int64_t groups_per_wave = 64 / a.G;
+  const int64_t waves = (a.n_rows + groups_per_wave - 1) / groups_per_wave;
+  hipLaunchKernelGGL((k_tp_bwd<S, T, CPL>), dim3(blocks_for(waves)), dim3(kBlock), 0, s,
+                     a.n_rows, a.C, a.G, static_cast<const T*>(a.x), a.y,
+                     static_cast<const T*>(a.w), static_cast<const T*>(a.dz),
+                     static_cast<T*>(a.dx), static_cast<T*>(a.dw), a.dy);
+  return hipGetLastError();
+}
+
 template <class S>
 KernelSet make_set(const char* name) {
   KernelSet k{};
@@ -393,6 +460,8 @@ KernelSet make_set(const char* name) {
     k.bwd[0][1][c] = &launch_bwd<S, float, CPL, true>;
     k.bwd[1][0][c] = &launch_bwd<S, bf16_t, CPL, false>;
     k.bwd[1][1][c] = &launch_bwd<S, bf16_t, CPL, true>;
+    k.tpb[0][c] = &launch_tp_bwd<S, float, CPL>;
+    k.tpb[1][c] = &launch_tp_bwd<S, bf16_t, CPL>;
   });
   k.tp[0] = &launch_tp<S, float, 4>;
   k.tp[1] = &launch_tp<S, bf16_t, 4>;

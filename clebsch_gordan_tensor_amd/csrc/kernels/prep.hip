@@ -316,6 +316,100 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Gradient of the harmonics with respect to the unnormalised vector:
+// dvec[i] = sum_k dY[i][k] dY_k/dr.  The polynomials of the unit vector u
+// are differentiated by forward-mode arithmetic (Dual3), and the chain rule
+// through u = r/|r| projects out the radial part: dY/dr = (I - u u^T) dY/du
+// / |r|.  A zero vector gets 0.
+template <int LMAX>
+__global__ void __launch_bounds__(256)
+    k_harmonics_grad(int64_t n, const float* __restrict__ vec, const float* __restrict__ dY,
+                     float* __restrict__ dvec) {
+  constexpr int D = (LMAX + 1) * (LMAX + 1);
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    float x = vec[3 * i], y = vec[3 * i + 1], z = vec[3 * i + 2];
+    float g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
+    // |r| through the same largest-component scaling as unit_vector
+    const float s = fmaxf(fabsf(x), fmaxf(fabsf(y), fabsf(z)));
+    if (s > 0.0f) {
+      const float is = 1.0f / s;
+      x *= is;
+      y *= is;
+      z *= is;
+      const float inv = rsqrtf(x * x + y * y + z * z);
+      x *= inv;
+      y *= inv;
+      z *= inv;
+      const float inv_norm = inv * is;
+      Dual3 h[D];
+      sfor<0, LMAX + 1>([&](auto l) {
+        harmonics_l<l>(Dual3(x, 1.0f, 0.0f, 0.0f), Dual3(y, 0.0f, 1.0f, 0.0f),
+                       Dual3(z, 0.0f, 0.0f, 1.0f), h + l * l);
+      });
+      const float* gy = dY + i * D;
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
+        const float c = gy[k];
+        g0 = fmaf(c, h[k].d0, g0);
+        g1 = fmaf(c, h[k].d1, g1);
+        g2 = fmaf(c, h[k].d2, g2);
+      }
+      const float ug = x * g0 + y * g1 + z * g2;
+      g0 = (g0 - x * ug) * inv_norm;
+      g1 = (g1 - y * ug) * inv_norm;
+      g2 = (g2 - z * ug) * inv_norm;
+    }
+    dvec[3 * i] = g0;
+    dvec[3 * i + 1] = g1;
+    dvec[3 * i + 2] = g2;
+  }
+}
+
+// Position gradient from edge-vector gradients g[E][3], with r_e =
+// pos[recv] - pos[sender]: dpos[b] = sum of g over b's in-edges (its CSR
+// row) minus the sum over its out-edges (its column of the transposed
+// index).  One wavefront per node; lanes take edges in a fixed stride and
+// close with a fixed butterfly, so the result is reproducible.  Padding
+// edges (sender outside [0, N)) are skipped.
+__global__ void __launch_bounds__(256)
+    k_edge_grad_to_nodes(int n_nodes, int n_edges, const int* __restrict__ rowptr,
+                         const int* __restrict__ sender, const int* __restrict__ colptr,
+                         const int* __restrict__ perm, const float* __restrict__ g,
+                         float* __restrict__ dpos) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= n_nodes) return;  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+  const int beg = max(rowptr[b], 0), end = min(rowptr[b + 1], n_edges);
+  for (int e = beg + lane; e < end; e += 64) {
+    const int a = sender[e];
+    if (a < 0 || a >= n_nodes) continue;
+    s0 += g[3 * int64_t(e)];
+    s1 += g[3 * int64_t(e) + 1];
+    s2 += g[3 * int64_t(e) + 2];
+  }
+  const int cb = max(colptr[b], 0), ce = min(colptr[b + 1], n_edges);
+  for (int j = cb + lane; j < ce; j += 64) {
+    const int e = perm[j];
+    if (e < 0 || e >= n_edges) continue;
+    s0 -= g[3 * int64_t(e)];
+    s1 -= g[3 * int64_t(e) + 1];
+    s2 -= g[3 * int64_t(e) + 2];
+  }
+  sfor<0, 6>([&](auto k) {
+    constexpr int m = 32 >> k;
+    s0 += shfl_xor_c<m>(s0);
+    s1 += shfl_xor_c<m>(s1);
+    s2 += shfl_xor_c<m>(s2);
+  });
+  if (lane == 0) {
+    dpos[3 * int64_t(b)] = s0;
+    dpos[3 * int64_t(b) + 1] = s1;
+    dpos[3 * int64_t(b) + 2] = s2;
+  }
+}
+
 unsigned grid_for(int64_t n, int per_block) {
   int64_t g = (n + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -485,6 +579,30 @@ hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hip
     case 3: hipLaunchKernelGGL(k_harmonics<3>, g, b, 0, s, n, vec, Y); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
+                                 float* dvec, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const dim3 g(grid_for(n, 256)), b(256);
+  switch (lmax) {
+    case 0: hipLaunchKernelGGL(k_harmonics_grad<0>, g, b, 0, s, n, vec, dY, dvec); break;
+    case 1: hipLaunchKernelGGL(k_harmonics_grad<1>, g, b, 0, s, n, vec, dY, dvec); break;
+    case 2: hipLaunchKernelGGL(k_harmonics_grad<2>, g, b, 0, s, n, vec, dY, dvec); break;
+    case 3: hipLaunchKernelGGL(k_harmonics_grad<3>, g, b, 0, s, n, vec, dY, dvec); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr,
+                                     const int* sender, const int* ws, const float* g,
+                                     float* dpos, hipStream_t s) {
+  if (n_nodes <= 0) return hipSuccess;
+  const TransposeLayout L = transpose_layout(n_nodes, n_edges);
+  hipLaunchKernelGGL(k_edge_grad_to_nodes, dim3(unsigned((int64_t(n_nodes) + 3) / 4)), dim3(256),
+                     0, s, n_nodes, n_edges, rowptr, sender, ws + L.colptr, ws + L.perm, g, dpos);
   return hipGetLastError();
 }
 

@@ -46,9 +46,22 @@ struct TpArgs {
   void* z;
 };
 
+struct TpBwdArgs {
+  int64_t n_rows;
+  int C, G;
+  const void* x;
+  const float* y;
+  const void* w;
+  const void* dz;
+  void* dx;
+  void* dw;
+  float* dy;
+};
+
 using FwdFn = hipError_t (*)(const FwdArgs&, hipStream_t);
 using BwdFn = hipError_t (*)(const BwdArgs&, hipStream_t);
 using TpFn = hipError_t (*)(const TpArgs&, hipStream_t);
+using TpBwdFn = hipError_t (*)(const TpBwdArgs&, hipStream_t);
 
 struct IrSpec {
   int l, p;
@@ -62,7 +75,8 @@ struct KernelSet {
   // [dtype: 0 f32, 1 bf16][y given][channels per lane: 0 -> 1, 1 -> 2, 2 -> 4]
   FwdFn fwd[2][2][3];
   BwdFn bwd[2][2][3];
-  TpFn tp[2];  // 4 channels per lane
+  TpFn tp[2];          // 4 channels per lane
+  TpBwdFn tpb[2][3];   // [dtype][channels per lane]
 };
 
 extern const KernelSet kSetL1;
@@ -74,6 +88,11 @@ extern const KernelSet kSetL3to3;
 hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr, const int* sender,
                                     const float* evec, int* ws, hipStream_t s);
 hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hipStream_t s);
+hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
+                                 float* dvec, hipStream_t s);
+hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr,
+                                     const int* sender, const int* ws, const float* g,
+                                     float* dpos, hipStream_t s);
 
 // Workspace layout of the transposed edge index (int32 words).
 struct TransposeLayout {

@@ -11,6 +11,11 @@
  *   receiver segment sum                 (A.3 Eq.7, E.1 Eq.12-13)
  *   its vector-Jacobian product          (E.1 Eq.16)
  *
+ * and the chain from the harmonic cotangent to per-atom position gradients
+ * (conservative forces F = -dE/dpos, "Ab Initio Accuracy Beyond the Cutoff:
+ * Distributed Message-Passing Equivariant Attention at Tens-of-Millions-of-
+ * Atom Scale", cited as Tessera, 2.2 Eq.3).
+ *
  * Conventions
  *   - An irreps list is a sequence of (l, parity) blocks; a block of degree l
  *     has 2l+1 components ordered m = -l..l.  Every x and output block has the
@@ -121,6 +126,40 @@ e3_status e3_spherical_harmonics(int32_t lmax, int64_t n, const float* vec, floa
  * x [n][dx][C], y [n][dy] float32, w [n][P][C], z [n][dout][C]. */
 e3_status e3_tp_forward(const e3_desc* desc, int64_t n_rows, const void* x, const float* y,
                         const void* w, void* z, e3_dtype dtype, void* stream);
+
+/* Batched tensor-product backward (e3j E.1 Eq.14-16, with one scalar per
+ * path as in Eq.11): for the cotangent dz [n][dout][C] of z,
+ *   dx[r] = sum_P w[r][P] (y[r] (x)^T dz[r])_P            [n][dx][C]
+ *   dw[r][P] = sum_M (x[r] (x) y[r])_P[M] dz[r][M]        [n][P][C]
+ *   dy[r] = sum_channels sum_P w[r][P] (x[r] (x)^T dz[r])_P  [n][dy] float32
+ * One pass per row; dx, dw, dy are overwritten.  x, w, dz, dx, dw must be
+ * 16-byte aligned.  The signatures and channel counts of e3_supported. */
+e3_status e3_tp_backward(const e3_desc* desc, int64_t n_rows, const void* x, const float* y,
+                         const void* w, const void* dz, void* dx, void* dw, float* dy,
+                         e3_dtype dtype, void* stream);
+
+/* Gradient of the harmonics with respect to the vectors (chain rule from
+ * the harmonic cotangent to the edge vector, toward conservative forces,
+ * Tessera 2.2 Eq.3):
+ *   dvec[i][k] = sum_j dY[i][j] dY_j(vec[i]) / dvec[i][k],
+ * dY [n][(lmax+1)^2], vec and dvec [n][3], float32, lmax <= 3.  Since the
+ * harmonics depend on the direction only, dvec is orthogonal to vec; a zero
+ * vector gets 0.  Feed it the dY of e3_conv_backward. */
+e3_status e3_spherical_harmonics_backward(int32_t lmax, int64_t n, const float* vec,
+                                          const float* dY, float* dvec, void* stream);
+
+/* Per-node gradient from per-edge vector gradients, for r_e = pos[receiver]
+ * - pos[sender]:
+ *   node_grad[b] = sum_{e: receiver(e) = b} edge_grad[e]
+ *                - sum_{e: sender(e) = b} edge_grad[e],
+ * edge_grad [E][3], node_grad [N][3] float32 (the force on b is
+ * -node_grad[b]; Tessera 2.2 Eq.3).
+ * rowptr / sender as for the convolution; workspace from
+ * e3_conv_prepare_transpose on the same graph.  Padding edges are skipped.
+ * Deterministic (no atomics). */
+e3_status e3_edge_grad_to_nodes(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                                const int32_t* sender, const void* workspace, size_t ws_bytes,
+                                const float* edge_grad, float* node_grad, void* stream);
 
 /* Fused convolution forward (e3j A.3 Eq.7, E.1 Eq.12-13):
  *   m[b] = sum_{e in row b} sum_P w[e][P] (x[sender[e]] (x) Y(r_e))_P.

@@ -19,6 +19,10 @@
  *     - E.1 Eq.16  VJP of the convolution (dx, dy, ds)
  *     - B.1        parity selection rule p1 p2 = p3
  *     - G.1 Eq.19-21 spin / ladder structure of the harmonics
+ *   [Tessera] "Ab Initio Accuracy Beyond the Cutoff: Distributed
+ *          Message-Passing Equivariant Attention at Tens-of-Millions-of-Atom
+ *          Scale" (html version).
+ *     - 2.2 Eq.3   forces as the negative analytic gradient of the energy
  *   Textbook material used where the pages stay silent (normalisation and
  *   phase are left open there, G.1 and G.2): Racah's closed form for the
  *   complex CG coefficients with the Condon-Shortley phase, and the standard
@@ -719,8 +723,8 @@ int oracle_sh_grad_batch(int lmax, int64_t n, const double *r, const double *dY,
 /* Position gradient from edge-vector gradients.  With r_e = pos[recv(e)] -
  * pos[sender(e)], a scalar E that depends on the positions only through the
  * r_e has dE/dpos[b] = sum_{e: recv(e)=b} g_e - sum_{e: sender(e)=b} g_e,
- * g_e = dE/dr_e; the force is F_b = -dE/dpos[b] (conservative forces, the
- * third page, 2.2 Eq.3).  Padding edges (sender outside [0,N)) are skipped.
+ * g_e = dE/dr_e; the force is F_b = -dE/dpos[b] ([Tessera] 2.2 Eq.3).
+ * Padding edges (sender outside [0,N)) are skipped.
  * dpos [N][3]. */
 int oracle_edge_grad_to_nodes(int n_nodes, int64_t n_edges, const int *rowptr, const int *sender,
                               const double *g, double *dpos) {

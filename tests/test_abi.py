@@ -134,6 +134,25 @@ def test_error_codes(lib):
     # forward: a workspace is optional, but a given one must be large enough
     assert lib.e3_conv_forward(_desc_c(good), 10, 100, fake, fake, fake, need - 4, fake, fake, fake,
                                fake, 0, None) == -6
+    # tensor-product backward, harmonics gradient, edge-to-node reduction
+    assert lib.e3_tp_backward(_desc_c(good), 0, None, None, None, None, None, None, None, 0,
+                              None) == 0
+    assert lib.e3_tp_backward(_desc_c(good), -1, None, None, None, None, None, None, None, 0,
+                              None) == -1
+    assert lib.e3_tp_backward(_desc_c(good), 5, fake, fake, fake, fake, fake, None, fake, 0,
+                              None) == -1
+    assert lib.e3_tp_backward(_desc_c(good), 5, fake, fake, fake, odd, fake, fake, fake, 0,
+                              None) == -4
+    assert lib.e3_tp_backward(_desc_c(uns), 5, fake, fake, fake, fake, fake, fake, fake, 0,
+                              None) == -3
+    assert lib.e3_spherical_harmonics_backward(4, 10, fake, fake, fake, None) == -1
+    assert lib.e3_spherical_harmonics_backward(3, -1, fake, fake, fake, None) == -1
+    assert lib.e3_spherical_harmonics_backward(3, 10, fake, None, fake, None) == -1
+    assert lib.e3_spherical_harmonics_backward(3, 0, None, None, None, None) == 0
+    assert lib.e3_edge_grad_to_nodes(0, 0, None, None, None, 0, None, None, None) == 0
+    assert lib.e3_edge_grad_to_nodes(-1, 0, None, None, None, 0, None, None, None) == -1
+    assert lib.e3_edge_grad_to_nodes(10, 100, fake, fake, fake, need - 1, fake, fake, None) == -6
+    assert lib.e3_edge_grad_to_nodes(10, 100, fake, None, fake, need, fake, fake, None) == -1
     out = np.zeros(10)
     assert lib.e3_cg_block(1, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
     assert lib.e3_cg_block(4, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1

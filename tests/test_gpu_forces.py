@@ -1,0 +1,288 @@
+"""GPU parity of the gradient chain past the convolution VJP, through the C
+ABI, against the fp64 oracle: the batched tensor-product backward, the
+gradient of the harmonics with respect to the edge vectors, the reduction
+of edge-vector gradients to per-atom position gradients, and the whole
+chain from a node cotangent to forces.
+
+Tolerance as for the convolution: max|gpu - oracle| / RMS(oracle) <= 1e-5
+per output tensor (fp32 storage), 2e-2 ahead of the output's own rounding
+for bf16 storage.
+"""
+import numpy as np
+import pytest
+
+from clebsch_gordan_tensor_amd import synth as S
+from oracle import oracle as O
+from tests.gpu_util import TOL_BF16, TOL_F32, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    from clebsch_gordan_tensor_amd import api
+    api.lib()
+    return api
+
+
+def _irreps(s):
+    return S.parse_irreps(s)[1]
+
+
+# ------------------------------------------------------ harmonics gradient
+
+@pytest.mark.parametrize("lmax", [0, 1, 2, 3])
+def test_harmonics_backward(gpu, lmax):
+    rng = np.random.default_rng(40 + lmax)
+    n = 5000
+    v = (rng.standard_normal((n, 3)) * rng.uniform(0.8, 5.0, (n, 1))).astype(np.float32)
+    dY = rng.standard_normal((n, (lmax + 1) ** 2)).astype(np.float32)
+    got = host(gpu.spherical_harmonics_backward(lmax, dev(v), dev(dY)))
+    ref = O.sh_grad(lmax, v.astype(np.float64), dY.astype(np.float64))
+    if lmax == 0:
+        assert np.all(got == 0.0)
+    else:
+        assert_close(got, ref, TOL_F32, f"harmonics_backward l<={lmax}")
+
+
+def test_harmonics_backward_extreme_vectors(gpu):
+    # the gradient scales as 1/|r|: compare each row against its own scale
+    rng = np.random.default_rng(44)
+    v = rng.standard_normal((64, 3)).astype(np.float32)
+    v[0] = 0.0
+    v[1] = [0, 0, 1e-20]
+    v[2] = [3e19, -2e19, 1e19]
+    v[3] = [1e-30, 2e-30, -1e-30]
+    v[4] = [0, 5.0, 0]
+    dY = rng.standard_normal((64, 16)).astype(np.float32)
+    got = host(gpu.spherical_harmonics_backward(3, dev(v), dev(dY)))
+    ref = O.sh_grad(3, v.astype(np.float64), dY.astype(np.float64))
+    assert np.all(got[0] == 0.0)
+    scale = np.linalg.norm(dY, axis=1) / np.maximum(np.linalg.norm(v.astype(np.float64), axis=1),
+                                                    1e-300)
+    err = np.abs(got[1:] - ref[1:]).max(axis=1) / scale[1:]
+    assert err.max() < 1e-5, err.max()
+    # the gradient is tangent to the sphere
+    g64, v64 = got[1:].astype(np.float64), v[1:].astype(np.float64)
+    dots = np.abs(np.sum(g64 * v64, axis=1))
+    assert np.all(dots <= 1e-5 * np.linalg.norm(g64, axis=1) * np.linalg.norm(v64, axis=1))
+
+
+# ---------------------------------------------------- tensor-product backward
+
+def _tp_bwd_case(B, C, seed, xs="0e+1o+2e", os_="0e+1o+2e+3o"):
+    rng = np.random.default_rng(seed)
+    xi, yi, oi = _irreps(xs), S.sh_irreps(3), _irreps(os_)
+    x = rng.standard_normal((B, S.dim(xi), C)).astype(np.float32)
+    y = O.sh(3, rng.standard_normal((B, 3))).astype(np.float32)
+    P = S.num_paths(xi, yi, oi)
+    w = rng.standard_normal((B, P, C)).astype(np.float32)
+    dz = rng.standard_normal((B, S.dim(oi), C)).astype(np.float32)
+    return xi, yi, oi, x, y, w, dz
+
+
+def _tp_bwd_run(gpu, xi, yi, oi, C, x, y, w, dz, dtype="f32"):
+    from clebsch_gordan_tensor_amd import api
+    d = api.Desc(xi, yi, oi, C)
+    dx, dw, dy = gpu.tp_backward(d, dev(x, dtype), dev(y), dev(w, dtype), dev(dz, dtype))
+    torch.cuda.synchronize()
+    return host(dx), host(dw), host(dy)
+
+
+@pytest.mark.parametrize("C", [4, 8, 32, 128, 256])
+def test_tp_backward_channel_counts(gpu, C):
+    B = 301 if C >= 128 else 1037  # ragged against every group size
+    xi, yi, oi, x, y, w, dz = _tp_bwd_case(B, C, 50 + C)
+    got = _tp_bwd_run(gpu, xi, yi, oi, C, x, y, w, dz)
+    ref = O.tp_backward(O.Desc(xi, yi, oi, C), x, y, w, dz)
+    for k, a, b in zip(("dx", "dw", "dy"), got, ref):
+        assert_close(a, b, TOL_F32, f"tp_backward C={C}:{k}")
+
+
+@pytest.mark.parametrize("sig", [("0e+1o", "0e+1o+2e+3o"), ("0e+1o+2e+3o", "0e+1o+2e+3o")])
+def test_tp_backward_other_signatures(gpu, sig):
+    C = 64
+    xi, yi, oi, x, y, w, dz = _tp_bwd_case(517, C, 60, *sig)
+    got = _tp_bwd_run(gpu, xi, yi, oi, C, x, y, w, dz)
+    ref = O.tp_backward(O.Desc(xi, yi, oi, C), x, y, w, dz)
+    for k, a, b in zip(("dx", "dw", "dy"), got, ref):
+        assert_close(a, b, TOL_F32, f"tp_backward {sig}:{k}")
+
+
+def test_tp_backward_bf16(gpu):
+    C = 128
+    xi, yi, oi, x, y, w, dz = _tp_bwd_case(700, C, 61)
+    x, w, dz = S.round_bf16(x), S.round_bf16(w), S.round_bf16(dz)
+    got = _tp_bwd_run(gpu, xi, yi, oi, C, x, y, w, dz, dtype="bf16")
+    ref = O.tp_backward(O.Desc(xi, yi, oi, C), x, y, w, dz)
+    for k, a, b in zip(("dx", "dw", "dy"), got, ref):
+        assert_close(a, b, TOL_BF16, f"tp_backward bf16:{k}", bf16_out=k != "dy")
+
+
+def test_tp_backward_full_size_sampled(gpu):
+    p = S.make_tp(with_dz=True)
+    from clebsch_gordan_tensor_amd import api
+    d = api.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    yd = gpu.spherical_harmonics(3, dev(p.u))
+    dx, dw, dy = gpu.tp_backward(d, dev(p.x), yd, dev(p.w), dev(p.dz))
+    torch.cuda.synchronize()
+    B = p.x.shape[0]
+    idx = np.sort(np.random.default_rng(0).choice(B, 1500, replace=False))
+    y_or = O.sh(3, p.u[idx].astype(np.float64))
+    ref = O.tp_backward(O.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels), p.x[idx], y_or,
+                        p.w[idx], p.dz[idx])
+    for k, a, b in zip(("dx", "dw", "dy"), (dx, dw, dy), ref):
+        assert_close(host(a[torch.from_numpy(idx).cuda()]), b, TOL_F32, f"tp_backward full:{k}")
+
+
+def test_tp_backward_equals_conv_backward_on_identity_graph(gpu):
+    # the identity graph (edge i: row i -> row i) turns the convolution
+    # backward into the tensor-product backward; two different kernels
+    from clebsch_gordan_tensor_amd import api
+    C = 128
+    xi, yi, oi, x, y, w, dz = _tp_bwd_case(333, C, 62)
+    d = api.Desc(xi, yi, oi, C, api.E3_Y_GIVEN)
+    B = x.shape[0]
+    rowptr, ident = dev(np.arange(B + 1, dtype=np.int32)), dev(np.arange(B, dtype=np.int32))
+    ws = gpu.conv_prepare_transpose(rowptr, ident)
+    cdx, cdw, cdy = gpu.conv_backward(d, rowptr, ident, ws, dev(y), dev(x), dev(w), dev(dz))
+    tdx, tdw, tdy = gpu.tp_backward(d, dev(x), dev(y), dev(w), dev(dz))
+    torch.cuda.synchronize()
+    for k, a, b in zip(("dx", "dw", "dy"), (tdx, tdw, tdy), (cdx, cdw, cdy)):
+        assert_close(host(a), host(b), TOL_F32, f"tp vs conv backward:{k}")
+
+
+def test_tp_backward_empty(gpu):
+    from clebsch_gordan_tensor_amd import api
+    C = 128
+    xi, yi, oi, x, y, w, dz = _tp_bwd_case(0, C, 63)
+    d = api.Desc(xi, yi, oi, C)
+    e = lambda shape: torch.empty(shape, device="cuda", dtype=torch.float32)
+    dx, dw, dy = gpu.tp_backward(d, e((0, 9, C)), e((0, 16)), e((0, 17, C)), e((0, 16, C)))
+    torch.cuda.synchronize()
+    assert dx.shape[0] == 0 and dw.shape[0] == 0 and dy.shape[0] == 0
+
+
+# ------------------------------------------------ edge gradients to atoms
+
+def test_edge_grad_to_nodes_with_padding(gpu):
+    from tests.test_oracle_conv import with_padding
+    g = with_padding(S.random_graph(300, 9.0, 3.0, seed=70), n_pad_per_node=2, seed=71)
+    rng = np.random.default_rng(72)
+    eg = rng.standard_normal((g.n_edges, 3)).astype(np.float32)
+    rowptr, sender = dev(g.rowptr), dev(g.sender)
+    ws = gpu.conv_prepare_transpose(rowptr, sender)
+    got = gpu.edge_grad_to_nodes(rowptr, sender, ws, dev(eg))
+    again = gpu.edge_grad_to_nodes(rowptr, sender, ws, dev(eg))
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), again.view(torch.int32))
+    ref = O.edge_grad_to_nodes(g.rowptr, g.sender, eg.astype(np.float64))
+    assert_close(host(got), ref, TOL_F32, "edge_grad_to_nodes")
+
+
+def test_edge_grad_to_nodes_isolated_and_hub(gpu):
+    # node 0 has every other node as in-neighbour (a hub of 2000 in-edges),
+    # node 1 has no edges at all
+    n = 2001
+    snd = np.concatenate([np.arange(2, n), [0]]).astype(np.int32)
+    rowptr = np.zeros(n + 1, np.int32)
+    rowptr[1:] = n - 2  # all hub edges in row 0 ...
+    rowptr[3:] = n - 1  # ... and one edge 0 -> 2 in row 2
+    rng = np.random.default_rng(73)
+    eg = rng.standard_normal((n - 1, 3)).astype(np.float32)
+    rp, sd = dev(rowptr), dev(snd)
+    ws = gpu.conv_prepare_transpose(rp, sd)
+    got = host(gpu.edge_grad_to_nodes(rp, sd, ws, dev(eg)))
+    ref = O.edge_grad_to_nodes(rowptr, snd, eg.astype(np.float64))
+    assert np.all(got[1] == 0.0)
+    assert_close(got, ref, TOL_F32, "edge_grad_to_nodes hub")
+
+
+# --------------------------------------------------- the chain to forces
+#
+# Gate for the position gradients.  dvec_e = J_e^T dY_e with J_e = dY/dr,
+# whose entries grow as 1/|r_e|; iid positions put some pairs ~25x closer
+# than the median pair (water3k: 0.155 A against 3.9 A), so dvec is heavy-
+# tailed (max/RMS ~ 130) and even rounding the exact dvec to float32 gives
+# max|err|/RMS = 5e-6.  The gate is therefore taken per edge against the
+# propagated scale  s_e = K_e (RMS(dY) + max_m |dY_e[m]|),  K_e = max_c
+# sum_m |J_e[m][c]|: an error of 1e-5 of RMS(dY) in dY (its own gate) plus
+# float32 rounding relative to the edge's own terms moves dvec_e by at most
+# 1e-5 s_e.  A per-coordinate scale would not do: the Jacobian column along
+# r_e vanishes (harmonics depend on the direction only).  A per-atom sum is
+# bounded by the sum of its edges' scales.
+
+def _edge_scale(ev, dY):
+    """s_e = K_e (RMS(dY) + max_m |dY_e[m]|), K_e = max_c sum_m |dY_m/dr_c|."""
+    A = np.zeros((ev.shape[0], 3))
+    for m in range(16):
+        u = np.zeros((ev.shape[0], 16))
+        u[:, m] = 1.0
+        A += np.abs(O.sh_grad(3, ev, u))
+    K = A.max(axis=1)
+    return K * (np.sqrt(np.mean(dY ** 2)) + np.abs(dY).max(axis=1))
+
+
+@pytest.fixture(scope="module")
+def water3k_chain():
+    p = S.make_conv("water3k")
+    g = p.graph
+    od = O.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    _, rdY = O.conv_backward_edge(od, g.rowptr, g.sender, p.x, p.w, p.dm, evec=g.evec)
+    ev64 = g.evec.astype(np.float64)
+    scale_e = _edge_scale(ev64, rdY)
+    recv = np.repeat(np.arange(g.n_nodes), np.diff(g.rowptr))
+    scale_n = np.zeros(g.n_nodes)
+    np.add.at(scale_n, recv, scale_e)
+    np.add.at(scale_n, g.sender, scale_e)
+    return p, rdY, ev64, scale_e[:, None], scale_n[:, None]
+
+
+def _ratio(got, ref, scale, what):
+    e = float((np.abs(got.astype(np.float64) - ref) / scale).max())
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    assert e <= TOL_F32, f"{what}: max |err| / propagated scale = {e:.3e}"
+    return e
+
+
+def test_force_kernels_water3k_from_oracle_cotangent(gpu, water3k_chain):
+    # the two new kernels alone at full water3k size: the oracle's dY (as
+    # float32) goes in
+    p, rdY, ev64, scale_e, scale_n = water3k_chain
+    g = p.graph
+    dY32 = rdY.astype(np.float32)
+    rdvec = O.sh_grad(3, ev64, dY32.astype(np.float64))
+    rdpos = O.edge_grad_to_nodes(g.rowptr, g.sender, rdvec)
+    rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+    ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=ev)
+    dvec = gpu.spherical_harmonics_backward(3, ev, dev(dY32))
+    dpos = gpu.edge_grad_to_nodes(rowptr, sender, ws, dvec)
+    torch.cuda.synchronize()
+    _ratio(host(dvec), rdvec, scale_e, "water3k:dvec (oracle dY)")
+    _ratio(host(dpos), rdpos, scale_n, "water3k:dpos (oracle dY)")
+
+
+def test_force_chain_water3k(gpu, water3k_chain):
+    # dE/dpos for E = <dm, m>: conv backward (dY) -> harmonics gradient ->
+    # edge-to-atom reduction, all on the GPU, against the oracle's chain
+    p, rdY, ev64, scale_e, scale_n = water3k_chain
+    g = p.graph
+    from clebsch_gordan_tensor_amd import api
+    d = api.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+    ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=ev)
+    _, _, dY = gpu.conv_backward(d, rowptr, sender, ws, ev, dev(p.x), dev(p.w), dev(p.dm))
+    dvec = gpu.spherical_harmonics_backward(3, ev, dY)
+    dpos = gpu.edge_grad_to_nodes(rowptr, sender, ws, dvec)
+    torch.cuda.synchronize()
+    rdvec = O.sh_grad(3, ev64, rdY)
+    rdpos = O.edge_grad_to_nodes(g.rowptr, g.sender, rdvec)
+    _ratio(host(dvec), rdvec, scale_e, "water3k:dvec")
+    _ratio(host(dpos), rdpos, scale_n, "water3k:dpos")
+    # translation invariance: the forces sum to zero
+    tot = host(dpos).astype(np.float64).sum(axis=0)
+    assert np.abs(tot).max() <= 1e-4 * np.sqrt(np.mean(rdpos ** 2)) * g.n_nodes ** 0.5

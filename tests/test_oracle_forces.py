@@ -1,8 +1,9 @@
 """Pins of the oracle's gradient chain beyond the convolution VJP: the batched
 tensor-product backward, the gradient of the harmonics with respect to the
 edge vector, and the reduction of edge-vector gradients to per-atom
-position gradients (forces are their negatives: the third page,
-"Conservative Forces", 2.2 Eq.3).
+position gradients (forces are their negatives: "Ab Initio Accuracy Beyond
+the Cutoff: Distributed Message-Passing Equivariant Attention at
+Tens-of-Millions-of-Atom Scale", 2.2 Eq.3).
 
 Every pin is independent of the code it checks: central finite differences
 of the forward functions in fp64, the Euler identity of a trilinear map,
