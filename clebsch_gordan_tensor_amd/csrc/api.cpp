@@ -125,11 +125,11 @@ int register_estimate(const e3k::KernelSet& k, Kind kind, int cpl) {
 
 // Channels per lane: the largest of 4, 2, 1 whose register estimate keeps
 // several wavefronts per SIMD (176 words), with G = C / cpl lanes per edge
-// group a power of two <= 64; the backward passes try 2 first.  The tensor
-// product forward uses 4.  E3HIP_FWD_CPL / E3HIP_BWD_CPL (1, 2 or 4) force a choice
-// when it is valid, for tuning.
+// group a power of two <= 64; the backward passes try 2 first.  When no
+// choice fits the estimate, the smallest valid one.  E3HIP_FWD_CPL,
+// E3HIP_BWD_CPL and E3HIP_TP_CPL (1, 2 or 4) force a choice when it is
+// valid, for tuning.
 int choose_cpl(const e3k::KernelSet& k, Kind kind, int C) {
-  if (kind == Kind::tp) return group_lanes(C, 4) > 0 ? 4 : -1;
   static const int force_fwd = [] {
     const char* e = std::getenv("E3HIP_FWD_CPL");
     return e ? std::atoi(e) : 0;
@@ -138,11 +138,15 @@ int choose_cpl(const e3k::KernelSet& k, Kind kind, int C) {
     const char* e = std::getenv("E3HIP_BWD_CPL");
     return e ? std::atoi(e) : 0;
   }();
-  const int force = kind == Kind::fwd ? force_fwd : force_bwd;
+  static const int force_tp = [] {
+    const char* e = std::getenv("E3HIP_TP_CPL");
+    return e ? std::atoi(e) : 0;
+  }();
+  const int force = kind == Kind::fwd ? force_fwd : kind == Kind::tp ? force_tp : force_bwd;
   if ((force == 1 || force == 2 || force == 4) && group_lanes(C, force) > 0) return force;
   // the backward of the small signatures is best at two channels per lane
   // (one edge per wavefront at C = 128): prefer 2 there over 4
-  const int first = kind == Kind::fwd ? 4 : 2;
+  const int first = kind == Kind::fwd || kind == Kind::tp ? 4 : 2;
   for (int cpl : {first, first == 4 ? 2 : 1, 1}) {
     if (group_lanes(C, cpl) <= 0) continue;
     if (register_estimate(k, kind, cpl) <= 176) return cpl;
@@ -167,8 +171,8 @@ e3_status select(const Parsed& p, e3_dtype dt, Kind kind, const e3k::KernelSet*&
     return E3_OK;
   }
   return fail(E3_ERR_UNSUPPORTED,
-              "channel count must be a power of two, 1 <= C <= 256 (4 <= C for the tensor "
-              "product), got " + std::to_string(p.C));
+              "channel count must be a power of two, 1 <= C <= 256, got " +
+                  std::to_string(p.C));
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -248,7 +252,7 @@ e3_status e3_tp_forward(const e3_desc* desc, int64_t n_rows, const void* x, cons
   if (!aligned16(x) || !aligned16(w) || !aligned16(z))
     return fail(E3_ERR_ALIGNMENT, "x, w and z must be 16-byte aligned");
   e3k::TpArgs a{n_rows, p.C, G, x, y, w, z};
-  return hip_status(ks->tp[dtype](a, hipStream_t(stream)), "tp_forward");
+  return hip_status(ks->tp[dtype][ci](a, hipStream_t(stream)), "tp_forward");
 }
 
 e3_status e3_tp_backward(const e3_desc* desc, int64_t n_rows, const void* x, const float* y,

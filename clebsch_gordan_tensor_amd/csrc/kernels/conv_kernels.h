@@ -304,14 +304,15 @@ __global__ void __launch_bounds__(kBlock)
 
   float Y[PL::DY];
   edge_y<S, true>(y, row, Y);
+  // every operand is read once and z written once: streaming accesses
   float xv[PL::DX][CPL];
   const T* xr = x + row * PL::DX * C + c0;
 #pragma unroll
-  for (int i = 0; i < PL::DX; ++i) load_ch<T, CPL>(xr + int64_t(i) * C, xv[i]);
+  for (int i = 0; i < PL::DX; ++i) load_ch_stream<T, CPL>(xr + int64_t(i) * C, xv[i]);
   float wv[PL::NP][CPL];
   const T* wr = w + row * PL::NP * C + c0;
 #pragma unroll
-  for (int p = 0; p < PL::NP; ++p) load_ch<T, CPL>(wr + int64_t(p) * C, wv[p]);
+  for (int p = 0; p < PL::NP; ++p) load_ch_stream<T, CPL>(wr + int64_t(p) * C, wv[p]);
   float acc[PL::DO][CPL];
 #pragma unroll
   for (int i = 0; i < PL::DO; ++i)
@@ -320,7 +321,7 @@ __global__ void __launch_bounds__(kBlock)
   edge_forward<S, CPL>(Y, xv, wv, acc);
   T* zr = z + row * PL::DO * C + c0;
 #pragma unroll
-  for (int i = 0; i < PL::DO; ++i) store_ch<T, CPL>(zr + int64_t(i) * C, acc[i]);
+  for (int i = 0; i < PL::DO; ++i) store_ch_stream<T, CPL>(zr + int64_t(i) * C, acc[i]);
 }
 
 // Batched tensor-product backward (e3j E.1 Eq.14-16, one scalar per path):
@@ -463,8 +464,11 @@ KernelSet make_set(const char* name) {
     k.tpb[0][c] = &launch_tp_bwd<S, float, CPL>;
     k.tpb[1][c] = &launch_tp_bwd<S, bf16_t, CPL>;
   });
-  k.tp[0] = &launch_tp<S, float, 4>;
-  k.tp[1] = &launch_tp<S, bf16_t, 4>;
+  sfor_host<0, 3>([&](auto c) {
+    constexpr int CPL = 1 << c;
+    k.tp[0][c] = &launch_tp<S, float, CPL>;
+    k.tp[1][c] = &launch_tp<S, bf16_t, CPL>;
+  });
   return k;
 }
 

@@ -75,8 +75,8 @@ struct KernelSet {
   // [dtype: 0 f32, 1 bf16][y given][channels per lane: 0 -> 1, 1 -> 2, 2 -> 4]
   FwdFn fwd[2][2][3];
   BwdFn bwd[2][2][3];
-  TpFn tp[2];          // 4 channels per lane
-  TpBwdFn tpb[2][3];   // [dtype][channels per lane]
+  TpFn tp[2][3];       // [dtype][channels per lane]
+  TpBwdFn tpb[2][3];
 };
 
 extern const KernelSet kSetL1;

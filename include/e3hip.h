@@ -109,7 +109,7 @@ e3_status e3_path_info(const e3_desc* desc, int32_t i, int32_t* ix, int32_t* iy,
  * kernels: the irreps triple must be one of the specialised signatures
  * (x 0e+1o, 0e+1o+2e or 0e+1o+2e+3o; y the harmonic bank 0e+1o or
  * 0e+1o+2e+3o; out 0e+1o or 0e+1o+2e+3o) and C a power of two with
- * 2 <= C <= 256 (4 <= C for e3_tp_forward). */
+ * 1 <= C <= 256.  The tensor-product calls accept the same. */
 int32_t e3_supported(const e3_desc* desc, e3_dtype dtype);
 
 /* Real coupling block T[M][m1][m2] of (l1, l2, L), l <= 3, written to the
