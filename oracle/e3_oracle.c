@@ -741,3 +741,55 @@ int oracle_edge_grad_to_nodes(int n_nodes, int64_t n_edges, const int *rowptr, c
     }
   return 0;
 }
+
+/* Equivariant channel mixing within each irrep ([e3j] A.3 Eq.5).  The
+ * equivariant choice of the mixing tensor is W^{km}_{k'm'} = W^{k}_{k'}
+ * delta_{mm'} for every pair of blocks of equal (l, parity) (a map between
+ * blocks of different type cannot commute with all rotations and the
+ * inversion); so
+ *   y[r][o, m][k] = sum over input blocks i with (l_i, p_i) = (l_o, p_o) of
+ *                   sum_{k'} x[r][i, m][k'] W_io[k'][k],
+ * with x [rows][dx][Cin], y [rows][dy][Cout], and W holding, for every such
+ * (i, o) pair in i-major then o order, a row-major Cin x Cout matrix.
+ * Output blocks without a matching input block are zero.  Returns the
+ * number of weight matrices (>= 0), or -1 on bad arguments; when y is NULL
+ * only the count is computed. */
+int oracle_linear(int nin, const int *in_l, const int *in_p, int cin, int nout, const int *out_l,
+                  const int *out_p, int cout, int64_t n_rows, const double *x, const double *W,
+                  double *y) {
+  if (nin < 0 || nout < 0 || cin < 1 || cout < 1 || n_rows < 0) return -1;
+  int din = 0, dout = 0, inoff[ORACLE_MAX_IRREPS], outoff[ORACLE_MAX_IRREPS];
+  if (nin > ORACLE_MAX_IRREPS || nout > ORACLE_MAX_IRREPS) return -1;
+  for (int i = 0; i < nin; ++i) {
+    inoff[i] = din;
+    din += 2 * in_l[i] + 1;
+  }
+  for (int o = 0; o < nout; ++o) {
+    outoff[o] = dout;
+    dout += 2 * out_l[o] + 1;
+  }
+  /* pair index of (i, o), -1 when the types differ */
+  int pair[ORACLE_MAX_IRREPS][ORACLE_MAX_IRREPS], np = 0;
+  for (int i = 0; i < nin; ++i)
+    for (int o = 0; o < nout; ++o)
+      pair[i][o] = (in_l[i] == out_l[o] && in_p[i] == out_p[o]) ? np++ : -1;
+  if (!y) return np;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    double *yr = y + r * dout * cout;
+    const double *xr = x + r * din * cin;
+    memset(yr, 0, sizeof(double) * dout * cout);
+    for (int o = 0; o < nout; ++o)
+      for (int i = 0; i < nin; ++i) {
+        if (pair[i][o] < 0) continue;
+        const double *Wio = W + (int64_t)pair[i][o] * cin * cout;
+        for (int m = 0; m < 2 * out_l[o] + 1; ++m)
+          for (int k = 0; k < cout; ++k) {
+            double s = 0.0;
+            for (int kp = 0; kp < cin; ++kp) s += xr[(inoff[i] + m) * cin + kp] * Wio[kp * cout + k];
+            yr[(outoff[o] + m) * cout + k] += s;
+          }
+      }
+  }
+  return np;
+}

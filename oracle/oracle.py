@@ -66,6 +66,9 @@ def _load():
     lib.oracle_sh_grad_batch.argtypes = [C.c_int, C.c_int64, dp, dp, dp]
     lib.oracle_edge_grad_to_nodes.restype = C.c_int
     lib.oracle_edge_grad_to_nodes.argtypes = [C.c_int, C.c_int64, ip, ip, dp, dp]
+    lib.oracle_linear.restype = C.c_int
+    lib.oracle_linear.argtypes = [C.c_int, ip, ip, C.c_int, C.c_int, ip, ip, C.c_int, C.c_int64,
+                                  dp, dp, dp]
     _lib = lib
     return lib
 
@@ -303,3 +306,37 @@ def edge_grad_to_nodes(rowptr, sender, g) -> np.ndarray:
                                          _dp(out)) != 0:
         raise ValueError("oracle_edge_grad_to_nodes rejected its arguments")
     return out
+
+
+def _lp_arrays(irreps):
+    ls = np.ascontiguousarray([l for l, _ in irreps], dtype=np.int32)
+    ps = np.ascontiguousarray([p for _, p in irreps], dtype=np.int32)
+    return ls, ps
+
+
+def linear_num_weights(in_irreps, out_irreps) -> int:
+    """Number of Cin x Cout weight matrices of the channel mixing."""
+    il, ip_ = _lp_arrays(in_irreps)
+    ol, op_ = _lp_arrays(out_irreps)
+    n = _load().oracle_linear(len(il), _ip(il), _ip(ip_), 1, len(ol), _ip(ol), _ip(op_), 1, 0,
+                              None, None, None)
+    if n < 0:
+        raise ValueError("oracle_linear rejected the irreps")
+    return n
+
+
+def linear(in_irreps, out_irreps, x, W):
+    """y [rows][dout][Cout] of the per-irrep channel mixing; x [rows][din][Cin],
+    W [n_pairs][Cin][Cout]."""
+    x, W = _f64(x), _f64(W)
+    il, ip_ = _lp_arrays(in_irreps)
+    ol, op_ = _lp_arrays(out_irreps)
+    rows, din, cin = x.shape
+    cout = W.shape[-1]
+    dout = sum(2 * l + 1 for l, _ in out_irreps)
+    y = np.zeros((rows, dout, cout))
+    n = _load().oracle_linear(len(il), _ip(il), _ip(ip_), cin, len(ol), _ip(ol), _ip(op_), cout,
+                              rows, _dp(x), _dp(W), _dp(y))
+    if n < 0:
+        raise ValueError("oracle_linear rejected its arguments")
+    return y
