@@ -43,7 +43,7 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_spherical_harmonics", "e3_spherical_harmonics_backward", "e3_tp_forward",
            "e3_tp_backward", "e3_conv_forward", "e3_conv_workspace_size",
            "e3_conv_prepare_transpose", "e3_conv_backward", "e3_edge_grad_to_nodes",
-           "e3_last_error"]
+           "e3_linear_num_weights", "e3_linear", "e3_last_error"]
 
 
 def lib():
@@ -66,6 +66,9 @@ def lib():
     L.e3_tp_forward.argtypes = [dp, i64, vp, vp, vp, vp, C.c_int, vp]
     L.e3_tp_backward.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, C.c_int, vp]
     L.e3_edge_grad_to_nodes.argtypes = [i32, i32, vp, vp, vp, sz, vp, vp, vp]
+    ip = C.POINTER(_Irreps)
+    L.e3_linear_num_weights.argtypes = [ip, ip, C.POINTER(i32)]
+    L.e3_linear.argtypes = [ip, ip, i64, vp, vp, vp, C.c_int, vp]
     L.e3_conv_forward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, C.c_int, vp]
     L.e3_conv_workspace_size.argtypes = [i32, i32, C.POINTER(sz)]
     L.e3_conv_prepare_transpose.argtypes = [i32, i32, vp, vp, vp, vp, sz, vp]
@@ -347,4 +350,45 @@ def edge_grad_to_nodes(rowptr, sender, workspace, edge_grad, out=None, stream=No
     _check(lib().e3_edge_grad_to_nodes(N, E, _ptr(rowptr), _ptr(sender), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(),
                                        _ptr(edge_grad), _ptr(out), _stream(stream)))
+    return out
+
+
+def _irreps_struct(irreps, mul):
+    a = (_Irrep * max(1, len(irreps)))()
+    for i, (l, p) in enumerate(irreps):
+        a[i] = _Irrep(mul, l, p)
+    st = _Irreps(len(irreps), a)
+    st._keep = a
+    return st
+
+
+def linear_num_weights(in_irreps, out_irreps) -> int:
+    """Number of [Cin][Cout] weight matrices of the per-irrep channel mixing."""
+    n = C.c_int32()
+    a, b = _irreps_struct(in_irreps, 8), _irreps_struct(out_irreps, 32)
+    _check(lib().e3_linear_num_weights(C.byref(a), C.byref(b), C.byref(n)))
+    return n.value
+
+
+def linear(in_irreps, out_irreps, x, W, out=None, stream=None):
+    """y [rows][dout][Cout] = per-irrep channel mixing of x [rows][din][Cin]
+    with W [n_pairs][Cin][Cout] (float32); in/out irreps as lists of (l, parity)."""
+    import torch
+    rows, din, cin = x.shape
+    n_pairs, cin_w, cout = W.shape
+    if cin_w != cin:
+        raise ValueError("W and x disagree on Cin")
+    if din != synth.dim(in_irreps):
+        raise ValueError("x does not match the input irreps")
+    _need(x, "x")
+    _need(W, "W", dtype=torch.float32)
+    dout = synth.dim(out_irreps)
+    if out is None:
+        out = torch.empty((rows, dout, cout), device=x.device, dtype=x.dtype)
+    _need(out, "out", shape=(rows, dout, cout), dtype=x.dtype)
+    a, b = _irreps_struct(in_irreps, cin), _irreps_struct(out_irreps, cout)
+    if n_pairs != linear_num_weights(in_irreps, out_irreps):
+        raise ValueError("W has the wrong number of matrices")
+    _check(lib().e3_linear(C.byref(a), C.byref(b), rows, _ptr(x), _ptr(W), _ptr(out),
+                           _dtype_code(x), _stream(stream)))
     return out

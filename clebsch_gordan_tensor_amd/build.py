@@ -26,6 +26,7 @@ HIP_SOURCES = [
     "kernels/inst_l2to3.hip",
     "kernels/inst_l3to3.hip",
     "kernels/prep.hip",
+    "kernels/linear.hip",
     "api.cpp",
     "host/cg_ladder.cpp",
 ]

@@ -387,6 +387,93 @@ e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges
   return hip_status(ks->bwd[dtype][yg][ci](a, hipStream_t(stream)), "conv_backward");
 }
 
+namespace {
+
+// Block lists of a channel mixing: every block of a list has one
+// multiplicity (the channel count of that side).
+e3_status parse_linear(const e3_irreps* in, const e3_irreps* out, std::vector<e3k::IrSpec>& li,
+                       std::vector<e3k::IrSpec>& lo, int& cin, int& cout) {
+  if (!in || !out) return fail(E3_ERR_INVALID_ARG, "irreps pointer is null");
+  std::vector<int> mi, mo;
+  e3_status s;
+  if ((s = parse_list(*in, "in", li, mi)) != E3_OK) return s;
+  if ((s = parse_list(*out, "out", lo, mo)) != E3_OK) return s;
+  if (li.empty() || lo.empty()) return fail(E3_ERR_IRREPS, "in and out need at least one block");
+  cin = mi[0];
+  cout = mo[0];
+  for (int m : mi)
+    if (m != cin) return fail(E3_ERR_IRREPS, "in blocks need one multiplicity");
+  for (int m : mo)
+    if (m != cout) return fail(E3_ERR_IRREPS, "out blocks need one multiplicity");
+  return E3_OK;
+}
+
+}  // namespace
+
+e3_status e3_linear_num_weights(const e3_irreps* in, const e3_irreps* out, int32_t* n_pairs) {
+  std::vector<e3k::IrSpec> li, lo;
+  int cin, cout;
+  e3_status s = parse_linear(in, out, li, lo, cin, cout);
+  if (s != E3_OK) return s;
+  if (!n_pairs) return fail(E3_ERR_INVALID_ARG, "n_pairs is null");
+  int n = 0;
+  for (auto& a : li)
+    for (auto& b : lo) n += (a.l == b.l && a.p == b.p);
+  *n_pairs = n;
+  return ok();
+}
+
+e3_status e3_linear(const e3_irreps* in, const e3_irreps* out, int64_t n_rows, const void* x,
+                    const float* W, void* y, e3_dtype dtype, void* stream) {
+  std::vector<e3k::IrSpec> li, lo;
+  int cin, cout;
+  e3_status s = parse_linear(in, out, li, lo, cin, cout);
+  if (s != E3_OK) return s;
+  if (dtype != E3_F32 && dtype != E3_BF16) return fail(E3_ERR_INVALID_ARG, "unknown dtype");
+  if (cin % 8 != 0 || cin > 256 || cout % 32 != 0 || cout > 1024)
+    return fail(E3_ERR_UNSUPPORTED, "channel mixing needs Cin a multiple of 8 up to 256 and "
+                                    "Cout a multiple of 32 up to 1024");
+  if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows == 0) return ok();
+  if (!x || !W || !y) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(W))
+    return fail(E3_ERR_ALIGNMENT, "x, W and y must be 16-byte aligned");
+  int din = 0, dout = 0;
+  for (auto& a : li) din += 2 * a.l + 1;
+  for (auto& b : lo) dout += 2 * b.l + 1;
+  // pair index of (i, o): input-block major, then output block
+  std::vector<int> pair(li.size() * lo.size(), -1);
+  int np = 0;
+  for (size_t i = 0; i < li.size(); ++i)
+    for (size_t o = 0; o < lo.size(); ++o)
+      if (li[i].l == lo[o].l && li[i].p == lo[o].p) pair[i * lo.size() + o] = np++;
+  int out_off = 0;
+  for (size_t o = 0; o < lo.size(); ++o) {
+    const int deg = 2 * lo[o].l + 1;
+    int in_off = 0, used = 0;
+    for (size_t i = 0; i < li.size(); ++i) {
+      const int pi = pair[i * lo.size() + o];
+      if (pi >= 0) {
+        e3k::LinearBlockArgs a{n_rows, din, dout, cin, cout, in_off, out_off, deg,
+                               x, W + int64_t(pi) * cin * cout, y, used > 0, 0};
+        if ((s = hip_status(e3k::launch_linear(a, dtype == E3_BF16, hipStream_t(stream)),
+                            "linear")) != E3_OK)
+          return s;
+        ++used;
+      }
+      in_off += 2 * li[i].l + 1;
+    }
+    if (used == 0) {
+      e3k::LinearBlockArgs a{n_rows, din, dout, cin, cout, 0, out_off, deg, x, W, y, 0, 1};
+      if ((s = hip_status(e3k::launch_linear(a, dtype == E3_BF16, hipStream_t(stream)),
+                          "linear")) != E3_OK)
+        return s;
+    }
+    out_off += deg;
+  }
+  return ok();
+}
+
 const char* e3_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

@@ -1,0 +1,237 @@
+// Equivariant channel mixing within each irrep (e3j A.3 Eq.5): for a pair of
+// blocks of equal degree and parity,
+//   y[r][out_off + m][col] (+)= sum_k x[r][in_off + m][k] W[k][col],
+// a GEMM whose rows are the (r, m) components of the block.  Dense and
+// contraction-shaped, so it runs on the fp32 matrix cores: each wavefront
+// computes 32-row tiles with v_mfma_f32_32x32x2_f32 against a slab of W
+// held in LDS; workgroups are persistent over the row tiles so the slab is
+// loaded once per workgroup.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.h"
+#include "registry.h"
+
+namespace e3k {
+namespace {
+
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+constexpr int kLinBlock = 256;   // 4 wavefronts
+constexpr int kLinPad = 8;       // LDS row padding of the W slab (floats)
+
+// LDS of one workgroup: a cin x (up to 128) slab of W, rows padded.
+constexpr size_t linear_lds_bytes(int cin) { return size_t(cin) * (128 + kLinPad) * sizeof(float); }
+
+// One 32-row x cw-column output tile per wavefront and iteration; the MFMA
+// operand layouts (32x32x2, fp32): A[i][s] from lane s*32 + i, B[s][j] from
+// lane s*32 + j, and D[i][j] in register r of lane j + 32*((i/4) % 2) for
+// i = 8*(r/4) + 4*(lane/32) + r%4.  The two k slots s of one MFMA take
+// k = kb + 4s + t for t = 0..3 over four MFMAs, so each lane reads four
+// consecutive k of its row with one vector load.
+//
+// NK > 0 fixes cin = 8 NK: a lane then holds its row's whole A operand in
+// registers and loads the next tile's while the matrix cores work on this
+// one; NK = 0 streams A in steps of 8 k for any cin.
+template <class T, int NCT, int NK>
+__global__ void __launch_bounds__(kLinBlock)
+    k_linear(int64_t n_rows, int din, int dout, int cin, int cout, int in_off, int out_off,
+             int deg, int col0, const T* __restrict__ x, const float* __restrict__ W,
+             T* __restrict__ y, int accumulate) {
+  // W slab [cin][CW] with the columns of one lane adjacent: column
+  // ct*32 + j sits at j*NCT + ct, so a lane reads its NCT B operands of
+  // one k with one vector LDS load
+  extern __shared__ float s_w[];  // [cin][NCT*32 + kLinPad]
+  constexpr int CW = NCT * 32;
+  constexpr int LD = CW + kLinPad;
+  typedef float f4v __attribute__((ext_vector_type(4)));
+#pragma unroll 8
+  for (int idx = threadIdx.x; idx < cin * (CW / 4); idx += kLinBlock) {
+    const int k = idx / (CW / 4), c = 4 * (idx - k * (CW / 4));
+    const f4v v = *reinterpret_cast<const f4v*>(W + int64_t(k) * cout + col0 + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_w[k * LD + ((c + e) % 32) * NCT + (c + e) / 32] = v[e];
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 31, s = lane >> 5;
+  const int64_t n_comp = n_rows * deg;  // rows of this GEMM
+  const int64_t n_tiles = (n_comp + 31) / 32;
+  const int64_t waves = int64_t(gridDim.x) * (kLinBlock / 64);
+  // this lane's A row of tile t (a zero row past the end)
+  auto a_row = [&](int64_t t, bool& valid) {
+    const int64_t q = t * 32 + i;
+    valid = q < n_comp;
+    const int64_t qq = valid ? q : 0;
+    const int64_t r = qq / deg;
+    const int m = int(qq - r * deg);
+    return x + (r * din + in_off + m) * int64_t(cin) + 4 * s;
+  };
+  constexpr int NB = NK > 0 ? NK : 1;
+  float abuf[NB][4];
+  auto fetch = [&](int64_t t, float (&a)[NB][4]) {
+    bool v;
+    const T* xr = a_row(t, v);
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) {
+      load_ch<T, 4>(xr + 8 * kb, a[kb]);
+      if (!v) a[kb][0] = a[kb][1] = a[kb][2] = a[kb][3] = 0.0f;
+    }
+  };
+  int64_t t = int64_t(blockIdx.x) * (kLinBlock / 64) + (threadIdx.x >> 6);
+  if (NK > 0 && t < n_tiles) fetch(t, abuf);
+  for (; t < n_tiles; t += waves) {
+    f16v acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f16v{};
+    // B operands of k = kb + 4s + u, u = 0..3
+    auto load_b = [&](int kb, float (&b)[4][NCT]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* p = s_w + (kb + 4 * s + u) * LD + i * NCT;
+        if constexpr (NCT == 4) {
+          const f4v v = *reinterpret_cast<const f4v*>(p);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) b[u][ct] = v[ct];
+        } else {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) b[u][ct] = p[ct];
+        }
+      }
+    };
+    auto mfma8 = [&](const float (&a)[4], const float (&b)[4][NCT]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          acc[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u], b[u][ct], acc[ct], 0, 0, 0);
+    };
+    if constexpr (NK > 0) {
+      float anext[NB][4];
+      if (t + waves < n_tiles) fetch(t + waves, anext);
+      // B of the next 8 k is read from LDS while this 8 k is multiplied;
+      // the scheduling fence keeps the compiler from hoisting more B reads
+      // (which would cost registers and occupancy)
+      float bc[4][NCT], bn[4][NCT];
+      load_b(0, bc);
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb) {
+        if (kb + 1 < NK) load_b(8 * (kb + 1), bn);
+        mfma8(abuf[kb], bc);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) bc[u][ct] = bn[u][ct];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) abuf[kb][u] = anext[kb][u];
+    } else {
+      bool v;
+      const T* xr = a_row(t, v);
+      for (int kb = 0; kb < cin; kb += 8) {
+        float a[4], b[4][NCT];
+        load_ch<T, 4>(xr + kb, a);
+        if (!v) a[0] = a[1] = a[2] = a[3] = 0.0f;
+        load_b(kb, b);
+        mfma8(a, b);
+      }
+    }
+    // D[i][j]: column j = lane % 32 of each 32-column tile
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int row = 8 * (rr / 4) + 4 * s + (rr % 4);
+      const int64_t qo = t * 32 + row;
+      if (qo >= n_comp) continue;
+      const int64_t ro = qo / deg;
+      const int mo = int(qo - ro * deg);
+      T* yr = y + (ro * dout + out_off + mo) * int64_t(cout) + col0 + i;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        float v[1] = {acc[ct][rr]};
+        if (accumulate) {
+          float o[1];
+          load_ch<T, 1>(yr + ct * 32, o);
+          v[0] += o[0];
+        }
+        store_ch<T, 1>(yr + ct * 32, v);
+      }
+    }
+  }
+}
+
+// Zero fill of one output block (no matching input block).
+template <class T>
+__global__ void __launch_bounds__(256)
+    k_linear_zero(int64_t n_rows, int dout, int cout, int out_off, int deg, T* __restrict__ y) {
+  const int64_t per_row = int64_t(deg) * cout;
+  const int64_t n = n_rows * per_row;
+  for (int64_t idx = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; idx < n;
+       idx += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t r = idx / per_row;
+    const int64_t rem = idx - r * per_row;
+    y[(r * dout + out_off) * int64_t(cout) + rem] = T{};
+  }
+}
+
+template <class T, int NCT, int NK>
+hipError_t launch_one(const LinearBlockArgs& a, int col0, hipStream_t s) {
+  const size_t lds = size_t(a.cin) * (NCT * 32 + kLinPad) * sizeof(float);
+  // the W slab may exceed the default 64 KB of dynamic LDS
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_linear<T, NCT, NK>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(linear_lds_bytes(256)));
+  if (attr != hipSuccess) return attr;
+  const int64_t tiles = (a.n_rows * a.deg + 31) / 32;
+  // persistent: at most 2 workgroups per CU, 256 CUs
+  int64_t blocks = (tiles + 3) / 4;
+  if (blocks > 512) blocks = 512;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((k_linear<T, NCT, NK>), dim3(unsigned(blocks)), dim3(kLinBlock), lds, s,
+                     a.n_rows, a.din, a.dout, a.cin, a.cout, a.in_off, a.out_off, a.deg, col0,
+                     static_cast<const T*>(a.x), a.W, static_cast<T*>(a.y), a.accumulate);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_linear_t(const LinearBlockArgs& a, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  if (a.zero) {
+    const int64_t n = a.n_rows * a.deg * a.cout;
+    int64_t g = (n + 255) / 256;
+    if (g > (1 << 20)) g = 1 << 20;
+    hipLaunchKernelGGL((k_linear_zero<T>), dim3(unsigned(g)), dim3(256), 0, s, a.n_rows, a.dout,
+                       a.cout, a.out_off, a.deg, static_cast<T*>(a.y));
+    return hipGetLastError();
+  }
+  // column slabs of up to 128 channels
+  for (int col0 = 0; col0 < a.cout; col0 += 128) {
+    const int cw = a.cout - col0 < 128 ? a.cout - col0 : 128;
+    hipError_t e;
+    if (cw == 128 && a.cin == 128)
+      e = launch_one<T, 4, 16>(a, col0, s);
+    else if (cw == 128 && a.cin == 64)
+      e = launch_one<T, 4, 8>(a, col0, s);
+    else
+      switch (cw / 32) {
+        case 1: e = launch_one<T, 1, 0>(a, col0, s); break;
+        case 2: e = launch_one<T, 2, 0>(a, col0, s); break;
+        case 3: e = launch_one<T, 3, 0>(a, col0, s); break;
+        default: e = launch_one<T, 4, 0>(a, col0, s); break;
+      }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_linear(const LinearBlockArgs& a, int bf16, hipStream_t s) {
+  return bf16 ? launch_linear_t<bf16_t>(a, s) : launch_linear_t<float>(a, s);
+}
+
+}  // namespace e3k

@@ -94,6 +94,20 @@ hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr
                                      const int* sender, const int* ws, const float* g,
                                      float* dpos, hipStream_t s);
 
+// One block pair of the per-irrep channel mixing (linear.hip): rows of x
+// block [in_off, in_off + deg) times W [cin][cout] into y block
+// [out_off, out_off + deg); `accumulate` adds to y, `zero` only clears the
+// output block.
+struct LinearBlockArgs {
+  int64_t n_rows;
+  int din, dout, cin, cout, in_off, out_off, deg;
+  const void* x;
+  const float* W;
+  void* y;
+  int accumulate, zero;
+};
+hipError_t launch_linear(const LinearBlockArgs& a, int bf16, hipStream_t s);
+
 // Workspace layout of the transposed edge index (int32 words).
 struct TransposeLayout {
   int64_t npad, colptr, cursor, tmp_e, tmp_b, perm, recv, padlist, order, flag, pos, key, order2,

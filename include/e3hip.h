@@ -206,6 +206,25 @@ e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges
                            const void* w, const void* dm, void* dx, void* dw, float* dY,
                            e3_dtype dtype, void* stream);
 
+/* Number of weight matrices of the channel mixing from `in` to `out`: one
+ * per (input block, output block) pair of equal degree and parity (host). */
+e3_status e3_linear_num_weights(const e3_irreps* in, const e3_irreps* out, int32_t* n_pairs);
+
+/* Equivariant channel mixing within each irrep (e3j A.3 Eq.5, with the
+ * rotation- and inversion-commuting choice of the mixing tensor,
+ * W^{km}_{k'm'} = W^k_{k'} delta_{mm'} between blocks of equal (l, parity)):
+ *   y[r][o, m][k] = sum over input blocks i with (l_i, p_i) = (l_o, p_o) of
+ *                   sum_{k'} x[r][i, m][k'] W_io[k'][k].
+ * Every `in` block has multiplicity Cin (a multiple of 8, <= 256), every
+ * `out` block Cout (a multiple of 32, <= 1024).  x [n_rows][din][Cin] and
+ * y [n_rows][dout][Cout] in the storage type, W float32, all three 16-byte
+ * aligned; W holds the e3_linear_num_weights matrices [Cin][Cout]
+ * row-major, ordered by input block, then output block.  Output blocks
+ * without a matching input block are zero.  Runs on the fp32 matrix cores; fp32 accumulation for both
+ * storage types.  y must not overlap x. */
+e3_status e3_linear(const e3_irreps* in, const e3_irreps* out, int64_t n_rows, const void* x,
+                    const float* W, void* y, e3_dtype dtype, void* stream);
+
 /* Text of the last error on this thread ("" if none). */
 const char* e3_last_error(void);
 

@@ -153,6 +153,23 @@ def test_error_codes(lib):
     assert lib.e3_edge_grad_to_nodes(-1, 0, None, None, None, 0, None, None, None) == -1
     assert lib.e3_edge_grad_to_nodes(10, 100, fake, fake, fake, need - 1, fake, fake, None) == -6
     assert lib.e3_edge_grad_to_nodes(10, 100, fake, None, fake, need, fake, fake, None) == -1
+    # channel mixing: counts, channel constraints, pointers, alignment
+    ir = api._irreps_struct([(0, 1), (1, -1), (1, 1)], 16)
+    ir_out = api._irreps_struct([(1, -1), (0, 1), (2, 1)], 32)
+    assert lib.e3_linear_num_weights(C.byref(ir), C.byref(ir_out), C.byref(n)) == 0
+    assert n.value == 2
+    assert lib.e3_linear(C.byref(ir), C.byref(ir_out), 0, None, None, None, 0, None) == 0
+    assert lib.e3_linear(C.byref(ir), C.byref(ir_out), 5, None, fake, fake, 0, None) == -1
+    assert lib.e3_linear(C.byref(ir), C.byref(ir_out), 5, odd, fake, fake, 0, None) == -4
+    assert lib.e3_linear(C.byref(ir), C.byref(ir_out), 5, fake, odd, fake, 0, None) == -4
+    bad_c = api._irreps_struct([(0, 1)], 12)
+    assert lib.e3_linear(C.byref(bad_c), C.byref(ir_out), 5, fake, fake, fake, 0, None) == -3
+    bad_c = api._irreps_struct([(0, 1)], 16)
+    bad_o = api._irreps_struct([(0, 1)], 48)
+    assert lib.e3_linear(C.byref(bad_c), C.byref(bad_o), 5, fake, fake, fake, 0, None) == -3
+    mixed = api._irreps_struct([(0, 1), (1, -1)], 16)
+    mixed.v[1].mul = 8
+    assert lib.e3_linear(C.byref(mixed), C.byref(ir_out), 5, fake, fake, fake, 0, None) == -2
     out = np.zeros(10)
     assert lib.e3_cg_block(1, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
     assert lib.e3_cg_block(4, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
