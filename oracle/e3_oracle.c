@@ -793,3 +793,62 @@ int oracle_linear(int nin, const int *in_l, const int *in_p, int cin, int nout, 
   }
   return np;
 }
+
+/* VJP of oracle_linear for the cotangent dy [rows][dout][Cout]:
+ *   dx[r][i, m][k'] = sum over output blocks o of the type of i of
+ *                     sum_k dy[r][o, m][k] W_io[k'][k]
+ *   dW_io[k'][k]    = sum_r sum_m x[r][i, m][k'] dy[r][o, m][k]
+ * (dx [rows][din][Cin], dW like W).  Returns the pair count or -1. */
+int oracle_linear_backward(int nin, const int *in_l, const int *in_p, int cin, int nout,
+                           const int *out_l, const int *out_p, int cout, int64_t n_rows,
+                           const double *x, const double *W, const double *dy, double *dx,
+                           double *dW) {
+  if (nin < 0 || nout < 0 || cin < 1 || cout < 1 || n_rows < 0) return -1;
+  if (nin > ORACLE_MAX_IRREPS || nout > ORACLE_MAX_IRREPS) return -1;
+  int din = 0, dout = 0, inoff[ORACLE_MAX_IRREPS], outoff[ORACLE_MAX_IRREPS];
+  for (int i = 0; i < nin; ++i) {
+    inoff[i] = din;
+    din += 2 * in_l[i] + 1;
+  }
+  for (int o = 0; o < nout; ++o) {
+    outoff[o] = dout;
+    dout += 2 * out_l[o] + 1;
+  }
+  int pair[ORACLE_MAX_IRREPS][ORACLE_MAX_IRREPS], np = 0;
+  for (int i = 0; i < nin; ++i)
+    for (int o = 0; o < nout; ++o)
+      pair[i][o] = (in_l[i] == out_l[o] && in_p[i] == out_p[o]) ? np++ : -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    double *dxr = dx + r * din * cin;
+    const double *dyr = dy + r * dout * cout;
+    memset(dxr, 0, sizeof(double) * din * cin);
+    for (int i = 0; i < nin; ++i)
+      for (int o = 0; o < nout; ++o) {
+        if (pair[i][o] < 0) continue;
+        const double *Wio = W + (int64_t)pair[i][o] * cin * cout;
+        for (int m = 0; m < 2 * in_l[i] + 1; ++m)
+          for (int kp = 0; kp < cin; ++kp) {
+            double s = 0.0;
+            for (int k = 0; k < cout; ++k) s += dyr[(outoff[o] + m) * cout + k] * Wio[kp * cout + k];
+            dxr[(inoff[i] + m) * cin + kp] += s;
+          }
+      }
+  }
+  /* dW: one pair and one weight entry per task, rows summed in order */
+  for (int i = 0; i < nin; ++i)
+    for (int o = 0; o < nout; ++o) {
+      if (pair[i][o] < 0) continue;
+      double *dWio = dW + (int64_t)pair[i][o] * cin * cout;
+#pragma omp parallel for schedule(static)
+      for (int kp = 0; kp < cin; ++kp)
+        for (int k = 0; k < cout; ++k) {
+          double s = 0.0;
+          for (int64_t r = 0; r < n_rows; ++r)
+            for (int m = 0; m < 2 * in_l[i] + 1; ++m)
+              s += x[(r * din + inoff[i] + m) * cin + kp] * dy[(r * dout + outoff[o] + m) * cout + k];
+          dWio[kp * cout + k] = s;
+        }
+    }
+  return np;
+}

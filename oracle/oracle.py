@@ -69,6 +69,9 @@ def _load():
     lib.oracle_linear.restype = C.c_int
     lib.oracle_linear.argtypes = [C.c_int, ip, ip, C.c_int, C.c_int, ip, ip, C.c_int, C.c_int64,
                                   dp, dp, dp]
+    lib.oracle_linear_backward.restype = C.c_int
+    lib.oracle_linear_backward.argtypes = [C.c_int, ip, ip, C.c_int, C.c_int, ip, ip, C.c_int,
+                                           C.c_int64, dp, dp, dp, dp, dp]
     _lib = lib
     return lib
 
@@ -340,3 +343,20 @@ def linear(in_irreps, out_irreps, x, W):
     if n < 0:
         raise ValueError("oracle_linear rejected its arguments")
     return y
+
+
+def linear_backward(in_irreps, out_irreps, x, W, dy):
+    """(dx [rows][din][Cin], dW [n_pairs][Cin][Cout]) of the channel mixing."""
+    x, W, dy = _f64(x), _f64(W), _f64(dy)
+    il, ip_ = _lp_arrays(in_irreps)
+    ol, op_ = _lp_arrays(out_irreps)
+    rows, din, cin = x.shape
+    cout = W.shape[-1]
+    dx = np.zeros_like(x)
+    dW = np.zeros_like(W)
+    n = _load().oracle_linear_backward(len(il), _ip(il), _ip(ip_), cin, len(ol), _ip(ol),
+                                       _ip(op_), cout, rows, _dp(x), _dp(W), _dp(dy), _dp(dx),
+                                       _dp(dW))
+    if n < 0:
+        raise ValueError("oracle_linear_backward rejected its arguments")
+    return dx, dW

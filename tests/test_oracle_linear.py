@@ -89,3 +89,60 @@ def test_linear_rotation_equivariance():
 def test_linear_rejects_bad_arguments():
     with pytest.raises(ValueError):
         O.linear([(0, 1)], [(0, 1)], np.zeros((2, 1, 0)), np.zeros((1, 0, 1)))
+
+
+def test_linear_backward_adjoint_and_finite_differences():
+    # y is bilinear in (x, W): <dy, y> = <dx, x> = <dW, W>; and each
+    # gradient entry equals a central difference of <dy, y>
+    ins = [(0, 1), (1, -1), (0, 1), (2, 1)]
+    outs = [(1, -1), (0, 1), (2, 1), (3, -1)]
+    rng = np.random.default_rng(84)
+    x = rng.standard_normal((6, _dim(ins), 3))
+    W = rng.standard_normal((O.linear_num_weights(ins, outs), 3, 4))
+    dy = rng.standard_normal((6, _dim(outs), 4))
+    dx, dW = O.linear_backward(ins, outs, x, W, dy)
+    ref = np.vdot(dy, O.linear(ins, outs, x, W))
+    assert np.vdot(dx, x) == pytest.approx(ref, rel=1e-12)
+    assert np.vdot(dW, W) == pytest.approx(ref, rel=1e-12)
+    # the 3o output block has no source: its cotangent reaches nothing
+    assert np.all(dx[:, :, :] == O.linear_backward(ins, outs, x, W, _zero_block(dy, outs, 3))[0])
+    h = 1e-5
+    loss = lambda x, W: np.vdot(dy, O.linear(ins, outs, x, W))
+    for arr, grad, k in ((x, dx, 0), (W, dW, 1)):
+        for _ in range(5):
+            idx = tuple(rng.integers(0, s) for s in arr.shape)
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += h
+            am[idx] -= h
+            args_p, args_m = [x, W], [x, W]
+            args_p[k], args_m[k] = ap, am
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert fd == pytest.approx(grad[idx], rel=1e-7, abs=1e-9)
+
+
+def test_linear_backward_matches_einsum():
+    ins, outs = [(0, 1), (1, -1), (1, -1)], [(1, -1), (0, 1)]
+    rng = np.random.default_rng(85)
+    x = rng.standard_normal((9, 7, 4))
+    W = rng.standard_normal((O.linear_num_weights(ins, outs), 4, 5))
+    dy = rng.standard_normal((9, 4, 5))
+    dx, dW = O.linear_backward(ins, outs, x, W, dy)
+    io, oo = _offsets(ins), _offsets(outs)
+    rdx, rdW = np.zeros_like(x), np.zeros_like(W)
+    for n, (i, o) in enumerate(_pairs(ins, outs)):
+        d = 2 * ins[i][0] + 1
+        rdx[:, io[i]:io[i] + d] += np.einsum("rmc,kc->rmk", dy[:, oo[o]:oo[o] + d], W[n])
+        rdW[n] = np.einsum("rmk,rmc->kc", x[:, io[i]:io[i] + d], dy[:, oo[o]:oo[o] + d])
+    np.testing.assert_allclose(dx, rdx, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dW, rdW, rtol=1e-12, atol=1e-12)
+
+
+def _dim(irreps):
+    return sum(2 * l + 1 for l, _ in irreps)
+
+
+def _zero_block(dy, outs, o):
+    z = dy.copy()
+    off = _offsets(outs)[o]
+    z[:, off:off + 2 * outs[o][0] + 1] = 0.0
+    return z
