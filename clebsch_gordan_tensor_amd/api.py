@@ -43,7 +43,8 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_spherical_harmonics", "e3_spherical_harmonics_backward", "e3_tp_forward",
            "e3_tp_backward", "e3_conv_forward", "e3_conv_workspace_size",
            "e3_conv_prepare_transpose", "e3_conv_backward", "e3_edge_grad_to_nodes",
-           "e3_linear_num_weights", "e3_linear", "e3_last_error"]
+           "e3_linear_num_weights", "e3_linear", "e3_linear_workspace_size",
+           "e3_linear_backward", "e3_last_error"]
 
 
 def lib():
@@ -69,6 +70,8 @@ def lib():
     ip = C.POINTER(_Irreps)
     L.e3_linear_num_weights.argtypes = [ip, ip, C.POINTER(i32)]
     L.e3_linear.argtypes = [ip, ip, i64, vp, vp, vp, C.c_int, vp]
+    L.e3_linear_workspace_size.argtypes = [ip, ip, C.POINTER(sz)]
+    L.e3_linear_backward.argtypes = [ip, ip, i64, vp, vp, vp, vp, vp, vp, sz, C.c_int, vp]
     L.e3_conv_forward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, C.c_int, vp]
     L.e3_conv_workspace_size.argtypes = [i32, i32, C.POINTER(sz)]
     L.e3_conv_prepare_transpose.argtypes = [i32, i32, vp, vp, vp, vp, sz, vp]
@@ -392,3 +395,30 @@ def linear(in_irreps, out_irreps, x, W, out=None, stream=None):
     _check(lib().e3_linear(C.byref(a), C.byref(b), rows, _ptr(x), _ptr(W), _ptr(out),
                            _dtype_code(x), _stream(stream)))
     return out
+
+
+def linear_backward(in_irreps, out_irreps, x, W, dy, dx=None, dW=None, workspace=None,
+                    stream=None):
+    """(dx, dW) of linear() for the cotangent dy."""
+    import torch
+    rows, din, cin = x.shape
+    n_pairs, _, cout = W.shape
+    _need(x, "x")
+    _need(W, "W", dtype=torch.float32)
+    _need(dy, "dy", shape=(rows, synth.dim(out_irreps), cout), dtype=x.dtype)
+    a, b = _irreps_struct(in_irreps, cin), _irreps_struct(out_irreps, cout)
+    nb = C.c_size_t()
+    _check(lib().e3_linear_workspace_size(C.byref(a), C.byref(b), C.byref(nb)))
+    if workspace is None:
+        workspace = torch.empty(nb.value, device=x.device, dtype=torch.uint8)
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dW is None:
+        dW = torch.empty_like(W)
+    _need(dx, "dx", shape=tuple(x.shape), dtype=x.dtype)
+    _need(dW, "dW", shape=tuple(W.shape), dtype=torch.float32)
+    _check(lib().e3_linear_backward(C.byref(a), C.byref(b), rows, _ptr(x), _ptr(W), _ptr(dy),
+                                    _ptr(dx), _ptr(dW), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _dtype_code(x), _stream(stream)))
+    return dx, dW

@@ -455,7 +455,7 @@ e3_status e3_linear(const e3_irreps* in, const e3_irreps* out, int64_t n_rows, c
       const int pi = pair[i * lo.size() + o];
       if (pi >= 0) {
         e3k::LinearBlockArgs a{n_rows, din, dout, cin, cout, in_off, out_off, deg,
-                               x, W + int64_t(pi) * cin * cout, y, used > 0, 0};
+                               x, W + int64_t(pi) * cin * cout, y, used > 0, 0, 0};
         if ((s = hip_status(e3k::launch_linear(a, dtype == E3_BF16, hipStream_t(stream)),
                             "linear")) != E3_OK)
           return s;
@@ -464,13 +464,91 @@ e3_status e3_linear(const e3_irreps* in, const e3_irreps* out, int64_t n_rows, c
       in_off += 2 * li[i].l + 1;
     }
     if (used == 0) {
-      e3k::LinearBlockArgs a{n_rows, din, dout, cin, cout, 0, out_off, deg, x, W, y, 0, 1};
+      e3k::LinearBlockArgs a{n_rows, din, dout, cin, cout, 0, out_off, deg, x, W, y, 0, 1, 0};
       if ((s = hip_status(e3k::launch_linear(a, dtype == E3_BF16, hipStream_t(stream)),
                           "linear")) != E3_OK)
         return s;
     }
     out_off += deg;
   }
+  return ok();
+}
+
+e3_status e3_linear_workspace_size(const e3_irreps* in, const e3_irreps* out, size_t* bytes) {
+  std::vector<e3k::IrSpec> li, lo;
+  int cin, cout;
+  e3_status s = parse_linear(in, out, li, lo, cin, cout);
+  if (s != E3_OK) return s;
+  if (!bytes) return fail(E3_ERR_INVALID_ARG, "bytes is null");
+  *bytes = size_t(e3k::kLinDwChunks) * cin * cout * sizeof(float);
+  return ok();
+}
+
+e3_status e3_linear_backward(const e3_irreps* in, const e3_irreps* out, int64_t n_rows,
+                             const void* x, const float* W, const void* dy, void* dx, float* dW,
+                             void* workspace, size_t ws_bytes, e3_dtype dtype, void* stream) {
+  std::vector<e3k::IrSpec> li, lo;
+  int cin, cout;
+  e3_status s = parse_linear(in, out, li, lo, cin, cout);
+  if (s != E3_OK) return s;
+  if (dtype != E3_F32 && dtype != E3_BF16) return fail(E3_ERR_INVALID_ARG, "unknown dtype");
+  if (cin % 32 != 0 || cin > 128 || cout % 32 != 0 || cout > 256)
+    return fail(E3_ERR_UNSUPPORTED, "channel-mixing backward needs Cin a multiple of 32 up to "
+                                    "128 and Cout a multiple of 32 up to 256");
+  if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
+  size_t need = 0;
+  e3_linear_workspace_size(in, out, &need);
+  if (!workspace || ws_bytes < need)
+    return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  if (!dW || (n_rows > 0 && (!x || !W || !dy || !dx)))
+    return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(workspace) || !aligned16(dW) ||
+      (n_rows > 0 && (!aligned16(x) || !aligned16(W) || !aligned16(dy) || !aligned16(dx))))
+    return fail(E3_ERR_ALIGNMENT, "x, W, dy, dx, dW and the workspace must be 16-byte aligned");
+  int din = 0, dout = 0;
+  std::vector<int> ioff, ooff;
+  for (auto& a : li) {
+    ioff.push_back(din);
+    din += 2 * a.l + 1;
+  }
+  for (auto& b : lo) {
+    ooff.push_back(dout);
+    dout += 2 * b.l + 1;
+  }
+  std::vector<int> pair(li.size() * lo.size(), -1);
+  int np = 0;
+  for (size_t i = 0; i < li.size(); ++i)
+    for (size_t o = 0; o < lo.size(); ++o)
+      if (li[i].l == lo[o].l && li[i].p == lo[o].p) pair[i * lo.size() + o] = np++;
+  const hipStream_t st = hipStream_t(stream);
+  const int bf = dtype == E3_BF16;
+  // dx: per input block, dy of each matching output block times W^T
+  if (n_rows > 0)
+    for (size_t i = 0; i < li.size(); ++i) {
+      const int deg = 2 * li[i].l + 1;
+      int used = 0;
+      for (size_t o = 0; o < lo.size(); ++o) {
+        const int pi = pair[i * lo.size() + o];
+        if (pi < 0) continue;
+        e3k::LinearBlockArgs a{n_rows, dout, din, cout, cin, ooff[o], ioff[i], deg,
+                               dy, W + int64_t(pi) * cin * cout, dx, used > 0, 0, 1};
+        if ((s = hip_status(e3k::launch_linear(a, bf, st), "linear_backward")) != E3_OK) return s;
+        ++used;
+      }
+      if (used == 0) {
+        e3k::LinearBlockArgs a{n_rows, dout, din, cout, cin, 0, ioff[i], deg, dy, W, dx, 0, 1, 0};
+        if ((s = hip_status(e3k::launch_linear(a, bf, st), "linear_backward")) != E3_OK) return s;
+      }
+    }
+  // dW per pair, through the workspace's partial sums
+  for (size_t i = 0; i < li.size(); ++i)
+    for (size_t o = 0; o < lo.size(); ++o) {
+      const int pi = pair[i * lo.size() + o];
+      if (pi < 0) continue;
+      e3k::LinearDwArgs a{n_rows, din, dout, cin, cout, ioff[i], ooff[o], 2 * li[i].l + 1,
+                          x, dy, static_cast<float*>(workspace), dW + int64_t(pi) * cin * cout, 0};
+      if ((s = hip_status(e3k::launch_linear_dw(a, bf, st), "linear_backward")) != E3_OK) return s;
+    }
   return ok();
 }
 

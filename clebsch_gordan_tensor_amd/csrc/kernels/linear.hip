@@ -37,21 +37,33 @@ constexpr size_t linear_lds_bytes(int cin) { return size_t(cin) * (128 + kLinPad
 template <class T, int NCT, int NK>
 __global__ void __launch_bounds__(kLinBlock)
     k_linear(int64_t n_rows, int din, int dout, int cin, int cout, int in_off, int out_off,
-             int deg, int col0, const T* __restrict__ x, const float* __restrict__ W,
-             T* __restrict__ y, int accumulate) {
+             int deg, int col0, const T* __restrict__ x, const float* __restrict__ W, int w_ld,
+             int w_trans, T* __restrict__ y, int accumulate) {
   // W slab [cin][CW] with the columns of one lane adjacent: column
   // ct*32 + j sits at j*NCT + ct, so a lane reads its NCT B operands of
   // one k with one vector LDS load
   extern __shared__ float s_w[];  // [cin][NCT*32 + kLinPad]
   constexpr int CW = NCT * 32;
   constexpr int LD = CW + kLinPad;
+  // Logical W[k][c] is W[k * w_ld + c] in memory, or W[c * w_ld + k] when
+  // w_trans (the backward's W^T); either way read in 16-byte pieces.
   typedef float f4v __attribute__((ext_vector_type(4)));
+  if (!w_trans) {
 #pragma unroll 8
-  for (int idx = threadIdx.x; idx < cin * (CW / 4); idx += kLinBlock) {
-    const int k = idx / (CW / 4), c = 4 * (idx - k * (CW / 4));
-    const f4v v = *reinterpret_cast<const f4v*>(W + int64_t(k) * cout + col0 + c);
+    for (int idx = threadIdx.x; idx < cin * (CW / 4); idx += kLinBlock) {
+      const int k = idx / (CW / 4), c = 4 * (idx - k * (CW / 4));
+      const f4v v = *reinterpret_cast<const f4v*>(W + int64_t(k) * w_ld + col0 + c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_w[k * LD + ((c + e) % 32) * NCT + (c + e) / 32] = v[e];
+      for (int e = 0; e < 4; ++e) s_w[k * LD + ((c + e) % 32) * NCT + (c + e) / 32] = v[e];
+    }
+  } else {
+#pragma unroll 8
+    for (int idx = threadIdx.x; idx < CW * (cin / 4); idx += kLinBlock) {
+      const int c = idx / (cin / 4), k = 4 * (idx - c * (cin / 4));
+      const f4v v = *reinterpret_cast<const f4v*>(W + int64_t(col0 + c) * w_ld + k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_w[(k + e) * LD + (c % 32) * NCT + c / 32] = v[e];
+    }
   }
   __syncthreads();
 
@@ -193,7 +205,8 @@ hipError_t launch_one(const LinearBlockArgs& a, int col0, hipStream_t s) {
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL((k_linear<T, NCT, NK>), dim3(unsigned(blocks)), dim3(kLinBlock), lds, s,
                      a.n_rows, a.din, a.dout, a.cin, a.cout, a.in_off, a.out_off, a.deg, col0,
-                     static_cast<const T*>(a.x), a.W, static_cast<T*>(a.y), a.accumulate);
+                     static_cast<const T*>(a.x), a.W, a.w_trans ? a.cin : a.cout, a.w_trans,
+                     static_cast<T*>(a.y), a.accumulate);
   return hipGetLastError();
 }
 
@@ -228,10 +241,134 @@ hipError_t launch_linear_t(const LinearBlockArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
+// ------------------------------------------------------- weight gradient
+// Partial dW over one chunk of the block's rows q = (r, m):
+//   part[chunk][a][b] = sum_{q in chunk} x[q][a] dy[q][b],
+// on the fp32 matrix cores with K = rows: wavefront w owns the 32 input
+// channels [32w, 32w + 32) and all NTB 32-column tiles of the output
+// channels; A[i][s] = x[q0 + s][32w + i], B[s][j] = dy[q0 + s][32 tb + j].
+// Eight rows are loaded ahead of the eight being multiplied.
+template <class T, int NTB>
+__global__ void __launch_bounds__(kLinBlock)
+    k_linear_dw(int64_t n_rows, int din, int dout, int cin, int cout, int in_off, int out_off,
+                int deg, int64_t chunk, const T* __restrict__ x, const T* __restrict__ dy,
+                float* __restrict__ part) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int i = lane & 31, s = lane >> 5;
+  if (32 * w >= cin) return;  // wave-uniform; no block-wide barrier follows
+  const int64_t n_comp = n_rows * deg;
+  const int64_t q_beg = int64_t(blockIdx.x) * chunk;
+  const int64_t q_end = q_beg + chunk < n_comp ? q_beg + chunk : n_comp;
+
+  f16v acc[NTB];
+#pragma unroll
+  for (int t = 0; t < NTB; ++t) acc[t] = f16v{};
+  // operands of rows q0 + 2u + s, u = 0..3
+  auto fetch = [&](int64_t q0, float (&a)[4], float (&b)[4][NTB]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t q = q0 + 2 * u + s;
+      const bool v = q < q_end;
+      const int64_t qq = v ? q : q_beg;
+      const int64_t r = qq / deg;
+      const int m = int(qq - r * deg);
+      float t1[1];
+      load_ch<T, 1>(x + (r * din + in_off + m) * int64_t(cin) + 32 * w + i, t1);
+      a[u] = v ? t1[0] : 0.0f;
+      const T* dyr = dy + (r * dout + out_off + m) * int64_t(cout) + i;
+#pragma unroll
+      for (int t = 0; t < NTB; ++t) {
+        load_ch<T, 1>(dyr + 32 * t, t1);
+        b[u][t] = v ? t1[0] : 0.0f;
+      }
+    }
+  };
+  float ac[4], bc[4][NTB];
+  if (q_beg < q_end) fetch(q_beg, ac, bc);
+  for (int64_t q0 = q_beg; q0 < q_end; q0 += 8) {
+    float an[4], bn[4][NTB];
+    if (q0 + 8 < q_end) fetch(q0 + 8, an, bn);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < NTB; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(ac[u], bc[u][t], acc[t], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ac[u] = an[u];
+#pragma unroll
+      for (int t = 0; t < NTB; ++t) bc[u][t] = bn[u][t];
+    }
+  }
+  // D[i][j] -> part[chunk][32w + i'][32t + j]
+  float* pc = part + int64_t(blockIdx.x) * cin * cout;
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int row = 8 * (rr / 4) + 4 * s + (rr % 4);
+#pragma unroll
+    for (int t = 0; t < NTB; ++t) pc[int64_t(32 * w + row) * cout + 32 * t + i] = acc[t][rr];
+  }
+}
+
+// dW[e] (+)= sum over chunks c = 0..n-1 of part[c][e], in that order.
+__global__ void __launch_bounds__(256)
+    k_linear_dw_reduce(int n_chunks, int64_t n_elem, const float* __restrict__ part,
+                       float* __restrict__ dW, int accumulate) {
+  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < n_elem;
+       e += int64_t(gridDim.x) * blockDim.x) {
+    float sum = accumulate ? dW[e] : 0.0f;
+    for (int c = 0; c < n_chunks; ++c) sum += part[int64_t(c) * n_elem + e];
+    dW[e] = sum;
+  }
+}
+
+template <class T, int NTB>
+hipError_t launch_dw_t(const LinearDwArgs& a, int n_chunks, int64_t chunk, hipStream_t s) {
+  hipLaunchKernelGGL((k_linear_dw<T, NTB>), dim3(unsigned(n_chunks)), dim3(kLinBlock), 0, s,
+                     a.n_rows, a.din, a.dout, a.cin, a.cout, a.in_off, a.out_off, a.deg, chunk,
+                     static_cast<const T*>(a.x), static_cast<const T*>(a.dy), a.part);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_dw(const LinearDwArgs& a, hipStream_t s) {
+  const int64_t n_comp = a.n_rows * a.deg;
+  const int64_t n_elem = int64_t(a.cin) * a.cout;
+  if (n_comp <= 0) {
+    hipLaunchKernelGGL(k_linear_dw_reduce, dim3(unsigned((n_elem + 255) / 256)), dim3(256), 0, s,
+                       0, n_elem, a.part, a.dW, a.accumulate);
+    return hipGetLastError();
+  }
+  // chunks of a multiple of 8 rows, at most kLinDwChunks of them
+  int64_t chunk = (n_comp + kLinDwChunks - 1) / kLinDwChunks;
+  chunk = (chunk + 7) / 8 * 8;
+  const int n_chunks = int((n_comp + chunk - 1) / chunk);
+  hipError_t e;
+  switch (a.cout / 32) {
+    case 1: e = launch_dw_t<T, 1>(a, n_chunks, chunk, s); break;
+    case 2: e = launch_dw_t<T, 2>(a, n_chunks, chunk, s); break;
+    case 3: e = launch_dw_t<T, 3>(a, n_chunks, chunk, s); break;
+    case 4: e = launch_dw_t<T, 4>(a, n_chunks, chunk, s); break;
+    case 5: e = launch_dw_t<T, 5>(a, n_chunks, chunk, s); break;
+    case 6: e = launch_dw_t<T, 6>(a, n_chunks, chunk, s); break;
+    case 7: e = launch_dw_t<T, 7>(a, n_chunks, chunk, s); break;
+    default: e = launch_dw_t<T, 8>(a, n_chunks, chunk, s); break;
+  }
+  if (e != hipSuccess) return e;
+  int64_t g = (n_elem + 255) / 256;
+  hipLaunchKernelGGL(k_linear_dw_reduce, dim3(unsigned(g)), dim3(256), 0, s, n_chunks, n_elem,
+                     a.part, a.dW, a.accumulate);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_linear(const LinearBlockArgs& a, int bf16, hipStream_t s) {
   return bf16 ? launch_linear_t<bf16_t>(a, s) : launch_linear_t<float>(a, s);
+}
+
+hipError_t launch_linear_dw(const LinearDwArgs& a, int bf16, hipStream_t s) {
+  return bf16 ? launch_dw<bf16_t>(a, s) : launch_dw<float>(a, s);
 }
 
 }  // namespace e3k

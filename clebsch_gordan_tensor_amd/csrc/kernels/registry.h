@@ -98,15 +98,32 @@ hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr
 // block [in_off, in_off + deg) times W [cin][cout] into y block
 // [out_off, out_off + deg); `accumulate` adds to y, `zero` only clears the
 // output block.
+// With w_trans, W is read as the transpose of a [cout][cin] matrix (the
+// backward's dy W^T).
 struct LinearBlockArgs {
   int64_t n_rows;
   int din, dout, cin, cout, in_off, out_off, deg;
   const void* x;
   const float* W;
   void* y;
-  int accumulate, zero;
+  int accumulate, zero, w_trans;
 };
 hipError_t launch_linear(const LinearBlockArgs& a, int bf16, hipStream_t s);
+
+// Weight gradient of one block pair: dW [cin][cout] (+)= sum over the
+// block's rows of x^T dy, through per-chunk partial sums in `part`
+// (kLinDwChunks * cin * cout floats) added in chunk order.
+constexpr int kLinDwChunks = 1024;
+struct LinearDwArgs {
+  int64_t n_rows;
+  int din, dout, cin, cout, in_off, out_off, deg;
+  const void* x;
+  const void* dy;
+  float* part;
+  float* dW;
+  int accumulate;
+};
+hipError_t launch_linear_dw(const LinearDwArgs& a, int bf16, hipStream_t s);
 
 // Workspace layout of the transposed edge index (int32 words).
 struct TransposeLayout {

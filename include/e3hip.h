@@ -225,6 +225,22 @@ e3_status e3_linear_num_weights(const e3_irreps* in, const e3_irreps* out, int32
 e3_status e3_linear(const e3_irreps* in, const e3_irreps* out, int64_t n_rows, const void* x,
                     const float* W, void* y, e3_dtype dtype, void* stream);
 
+/* Bytes of the workspace of e3_linear_backward (partial weight-gradient
+ * sums; host only). */
+e3_status e3_linear_workspace_size(const e3_irreps* in, const e3_irreps* out, size_t* bytes);
+
+/* Backward of e3_linear for the cotangent dy [n_rows][dout][Cout]:
+ *   dx[r][i, m][k'] = sum over output blocks o of the type of i of
+ *                     sum_k dy[r][o, m][k] W_io[k'][k]          [n_rows][din][Cin]
+ *   dW_io[k'][k]    = sum_r sum_m x[r][i, m][k'] dy[r][o, m][k]  float32, like W
+ * dW is summed through fixed per-chunk partials in the caller's workspace
+ * (e3_linear_workspace_size bytes), so the result is reproducible.
+ * Needs Cin a multiple of 32 up to 128 and Cout a multiple of 32 up to 256;
+ * every pointer 16-byte aligned.  n_rows = 0 gives dW = 0. */
+e3_status e3_linear_backward(const e3_irreps* in, const e3_irreps* out, int64_t n_rows,
+                             const void* x, const float* W, const void* dy, void* dx, float* dW,
+                             void* workspace, size_t ws_bytes, e3_dtype dtype, void* stream);
+
 /* Text of the last error on this thread ("" if none). */
 const char* e3_last_error(void);
 

@@ -85,3 +85,75 @@ def test_linear_deterministic_and_empty(gpu):
     e = gpu.linear(ins, outs, torch.empty((0, 4, 64), device="cuda"), dev(W))
     torch.cuda.synchronize()
     assert e.shape == (0, 4, 64)
+
+
+# ----------------------------------------------------------------- backward
+
+def _bwd_case(ins, outs, rows, cin, cout, seed):
+    x, W = _case(ins, outs, rows, cin, cout, seed)
+    dy = np.random.default_rng(seed + 1).standard_normal(
+        (rows, S.dim(outs), cout)).astype(np.float32)
+    return x, W, dy
+
+
+@pytest.mark.parametrize("xs,os_,rows,cin,cout", [
+    ("0e+1o+2e+3o", "0e+1o+2e+3o", 3001, 128, 128),
+    ("0e+1o", "0e+1o+2e+3o", 1111, 128, 128),     # output blocks without a source
+    ("0e+0e+1o+2e", "0e+1o", 777, 64, 32),        # an input block without a target
+    ("1o+0e", "0e+1o+1o", 555, 32, 256),          # two targets of one input block
+])
+def test_linear_backward_matches_oracle(gpu, xs, os_, rows, cin, cout):
+    ins, outs = _ir(xs), _ir(os_)
+    x, W, dy = _bwd_case(ins, outs, rows, cin, cout, 110 + rows)
+    dx, dW = gpu.linear_backward(ins, outs, dev(x), dev(W), dev(dy))
+    rdx, rdW = O.linear_backward(ins, outs, x, W, dy)
+    assert_close(host(dx), rdx, TOL_F32, f"linear dx {xs}->{os_}")
+    assert_close(host(dW), rdW, TOL_F32, f"linear dW {xs}->{os_}")
+
+
+def test_linear_backward_bf16(gpu):
+    ins = outs = _ir("0e+1o+2e+3o")
+    x, W, dy = _bwd_case(ins, outs, 1500, 128, 128, 120)
+    x, dy = S.round_bf16(x), S.round_bf16(dy)
+    dx, dW = gpu.linear_backward(ins, outs, dev(x, "bf16"), dev(W), dev(dy, "bf16"))
+    rdx, rdW = O.linear_backward(ins, outs, x, W, dy)
+    assert_close(host(dx), rdx, TOL_BF16, "linear dx bf16", bf16_out=True)
+    assert_close(host(dW), rdW, TOL_F32, "linear dW bf16 inputs")  # dW is float32
+
+
+def test_linear_backward_full_size(gpu):
+    # 64k rows: dx on sampled rows against the oracle; dW through the
+    # bilinear identity <dW, W> = <dx, x> = <dy, y> (y from the forward)
+    ins = outs = _ir("0e+1o+2e+3o")
+    x, W, dy = _bwd_case(ins, outs, 64000, 128, 128, 121)
+    xd, Wd, dyd = dev(x), dev(W), dev(dy)
+    dx, dW = gpu.linear_backward(ins, outs, xd, Wd, dyd)
+    y = gpu.linear(ins, outs, xd, Wd)
+    torch.cuda.synchronize()
+    idx = np.sort(np.random.default_rng(2).choice(64000, 1000, replace=False))
+    rdx, _ = O.linear_backward(ins, outs, x[idx], W, dy[idx])
+    assert_close(host(dx[torch.from_numpy(idx).cuda()]), rdx, TOL_F32, "linear dx 64k")
+    f64 = lambda t: host(t).astype(np.float64)
+    ref = np.vdot(dy.astype(np.float64), f64(y))
+    for v in (np.vdot(f64(dW), W.astype(np.float64)), np.vdot(f64(dx), x.astype(np.float64))):
+        assert abs(v - ref) <= 1e-5 * abs(ref)
+
+
+def test_linear_backward_no_rows_gives_zero_dW(gpu):
+    ins = outs = _ir("0e+1o")
+    W = dev(np.ones((2, 32, 32), np.float32))
+    dW = torch.full((2, 32, 32), 7.0, device="cuda")
+    gpu.linear_backward(ins, outs, torch.empty((0, 4, 32), device="cuda"), W,
+                        torch.empty((0, 4, 32), device="cuda"), dW=dW)
+    torch.cuda.synchronize()
+    assert torch.all(dW == 0)
+
+
+def test_linear_backward_deterministic(gpu):
+    ins = outs = _ir("0e+1o+2e")
+    x, W, dy = _bwd_case(ins, outs, 5000, 64, 64, 122)
+    a = gpu.linear_backward(ins, outs, dev(x), dev(W), dev(dy))
+    b = gpu.linear_backward(ins, outs, dev(x), dev(W), dev(dy))
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
