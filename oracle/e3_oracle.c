@@ -64,6 +64,10 @@ typedef struct {
   int yl[ORACLE_MAX_IRREPS], yp[ORACLE_MAX_IRREPS];
   int ol[ORACLE_MAX_IRREPS], op[ORACLE_MAX_IRREPS];
   int C; /* channels (multiplicity of every x and output irrep) */
+  /* 0: paths landing on the same output irrep are summed (collapsed);
+   * 1: every path keeps its own output block, in path order (e3j's
+   *    default, one output block per path: A.3, E.1) */
+  int per_path;
 } oracle_desc;
 
 int oracle_num_threads(void) {
@@ -284,6 +288,13 @@ static int plan_build(const oracle_desc *d, oplan *pl) {
         p->T = malloc(sizeof(double) * (2 * L + 1) * (2 * l1 + 1) * (2 * l2 + 1));
         if (oracle_cg_real(l1, l2, L, p->T) != 0) return -1;
       }
+  if (d->per_path) { /* one output block per path, in path order */
+    pl->dout = 0;
+    for (int i = 0; i < pl->np; ++i) {
+      pl->p[i].ooff = pl->dout;
+      pl->dout += 2 * pl->p[i].L + 1;
+    }
+  }
   return 0;
 }
 

@@ -81,7 +81,7 @@ class _CDesc(C.Structure):
                 ("xl", C.c_int * _MAX_IRREPS), ("xp", C.c_int * _MAX_IRREPS),
                 ("yl", C.c_int * _MAX_IRREPS), ("yp", C.c_int * _MAX_IRREPS),
                 ("ol", C.c_int * _MAX_IRREPS), ("op", C.c_int * _MAX_IRREPS),
-                ("C", C.c_int)]
+                ("C", C.c_int), ("per_path", C.c_int)]
 
 
 def parse_irreps(s: str):
@@ -102,12 +102,16 @@ def parse_irreps(s: str):
 
 
 class Desc:
-    """Irreps of x, y and the output, as lists of (l, parity), and C channels."""
+    """Irreps of x, y and the output, as lists of (l, parity), and C channels;
+    per_path: one output block per path (path order) instead of one per
+    output irrep."""
 
-    def __init__(self, x, y, out, channels):
+    def __init__(self, x, y, out, channels, per_path=False):
         self.x, self.y, self.out, self.C = list(x), list(y), list(out), int(channels)
+        self.per_path = bool(per_path)
         c = _CDesc()
         c.nx, c.ny, c.no, c.C = len(self.x), len(self.y), len(self.out), self.C
+        c.per_path = int(self.per_path)
         for arr_l, arr_p, ir in ((c.xl, c.xp, self.x), (c.yl, c.yp, self.y),
                                  (c.ol, c.op, self.out)):
             if len(ir) > _MAX_IRREPS:
@@ -126,6 +130,8 @@ class Desc:
 
     @property
     def dout(self):
+        if self.per_path:
+            return sum(2 * self.out[o][0] + 1 for _, _, o in paths(self))
         return sum(2 * l + 1 for l, _ in self.out)
 
     def ptr(self):

@@ -390,3 +390,70 @@ def test_rejects_bad_arguments():
     with pytest.raises(ValueError):
         O.conv_forward(d2, g.rowptr, g.sender, np.zeros((5, 1, 1)),
                        np.zeros((g.n_edges, 1, 1)), evec=g.evec, rows=[7])
+
+
+# ------------------------------------------------ one output block per path
+
+def _per_path_case():
+    rng = np.random.default_rng(60)
+    g = S.random_graph(40, 6.0, 3.0, seed=60)
+    x_ir, o_ir = [(0, 1), (1, -1), (2, 1)], [(0, 1), (1, -1), (2, 1), (3, -1)]
+    C = 3
+    d = desc_of(x_ir, S.sh_irreps(3), o_ir, C)
+    dp = O.Desc(x_ir, S.sh_irreps(3), o_ir, C, per_path=True)
+    x = rng.standard_normal((g.n_nodes, 9, C))
+    w = rng.standard_normal((g.n_edges, O.num_paths(d), C))
+    return rng, g, d, dp, x, w, o_ir
+
+
+def test_per_path_blocks_sum_to_collapsed():
+    rng, g, d, dp, x, w, o_ir = _per_path_case()
+    m = O.conv_forward(d, g.rowptr, g.sender, x, w, evec=g.evec)
+    mp = O.conv_forward(dp, g.rowptr, g.sender, x, w, evec=g.evec)
+    paths = O.paths(d)
+    assert mp.shape[1] == sum(2 * o_ir[o][0] + 1 for _, _, o in paths)
+    off_o = np.cumsum([0] + [2 * l + 1 for l, _ in o_ir])
+    acc = np.zeros_like(m)
+    off = 0
+    for (_, _, o) in paths:
+        n = 2 * o_ir[o][0] + 1
+        acc[:, off_o[o]:off_o[o] + n] += mp[:, off:off + n]
+        off += n
+    np.testing.assert_allclose(acc, m, rtol=1e-12, atol=1e-12)
+
+
+def test_per_path_block_is_the_single_path_convolution():
+    # block P equals the collapsed convolution with every other path's
+    # weight set to zero, read at P's output irrep
+    rng, g, d, dp, x, w, o_ir = _per_path_case()
+    mp = O.conv_forward(dp, g.rowptr, g.sender, x, w, evec=g.evec)
+    off_o = np.cumsum([0] + [2 * l + 1 for l, _ in o_ir])
+    off = 0
+    for pi, (_, _, o) in enumerate(O.paths(d)):
+        n = 2 * o_ir[o][0] + 1
+        w1 = np.zeros_like(w)
+        w1[:, pi] = w[:, pi]
+        m1 = O.conv_forward(d, g.rowptr, g.sender, x, w1, evec=g.evec)
+        np.testing.assert_allclose(mp[:, off:off + n], m1[:, off_o[o]:off_o[o] + n],
+                                   rtol=1e-12, atol=1e-12)
+        off += n
+
+
+def test_per_path_backward_euler_and_finite_differences():
+    rng, g, d, dp, x, w, o_ir = _per_path_case()
+    Y = O.sh(3, g.evec)
+    dm = rng.standard_normal((g.n_nodes, dp.dout, dp.C))
+    m = O.conv_forward(dp, g.rowptr, g.sender, x, w, Y=Y)
+    dx = O.conv_backward_dx(dp, g.rowptr, g.sender, w, dm, Y=Y)
+    dw, dY = O.conv_backward_edge(dp, g.rowptr, g.sender, x, w, dm, Y=Y)
+    ref = np.vdot(dm, m)
+    for v in (np.vdot(dx, x), np.vdot(dw, w), np.vdot(dY, Y)):
+        assert v == pytest.approx(ref, rel=1e-12)
+    loss = lambda w: np.vdot(dm, O.conv_forward(dp, g.rowptr, g.sender, x, w, Y=Y))
+    h = 1e-4
+    for _ in range(4):
+        idx = tuple(rng.integers(0, s) for s in w.shape)
+        wp, wm = w.copy(), w.copy()
+        wp[idx] += h
+        wm[idx] -= h
+        assert (loss(wp) - loss(wm)) / (2 * h) == pytest.approx(dw[idx], rel=1e-7, abs=1e-9)
