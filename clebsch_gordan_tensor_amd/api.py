@@ -19,6 +19,7 @@ _lib = None
 
 E3_F32, E3_BF16 = 0, 1
 E3_Y_GIVEN = 1
+E3_OUT_PER_PATH = 2
 
 
 class E3Error(RuntimeError):
@@ -122,6 +123,9 @@ class Desc:
 
     @property
     def dout(self):
+        if self.flags & E3_OUT_PER_PATH:  # one output block per path
+            return sum(2 * self.out[o][0] + 1
+                       for _, _, o in synth.path_list(self.x, self.y, self.out))
         return synth.dim(self.out)
 
     def c(self):

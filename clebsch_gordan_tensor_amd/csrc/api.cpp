@@ -28,6 +28,7 @@ e3_status ok() {
 
 struct Parsed {
   int C = 0;
+  int per_path = 0;  // E3_OUT_PER_PATH
   std::vector<e3k::IrSpec> x, y, o;
   int P = 0, dx = 0, dy = 0, dout = 0;
   std::vector<int> pix, piy, pio;
@@ -84,11 +85,17 @@ e3_status parse(const e3_desc* d, Parsed& p) {
         }
       }
   p.P = int(p.pix.size());
+  p.per_path = (d->flags & E3_OUT_PER_PATH) ? 1 : 0;
+  if (p.per_path) {  // one output block per path
+    p.dout = 0;
+    for (int k : p.pio) p.dout += 2 * p.o[k].l + 1;
+  }
   return E3_OK;
 }
 
-const e3k::KernelSet* const kSets[] = {&e3k::kSetL1, &e3k::kSetL1to3, &e3k::kSetL2to3,
-                                       &e3k::kSetL3to3};
+const e3k::KernelSet* const kSets[] = {&e3k::kSetL1,     &e3k::kSetL1to3,   &e3k::kSetL2to3,
+                                       &e3k::kSetL3to3,   &e3k::kSetL1PP,    &e3k::kSetL1to3PP,
+                                       &e3k::kSetL2to3PP};
 
 bool same(const std::vector<e3k::IrSpec>& a, const e3k::IrSpec* b, int nb) {
   if (int(a.size()) != nb) return false;
@@ -99,7 +106,9 @@ bool same(const std::vector<e3k::IrSpec>& a, const e3k::IrSpec* b, int nb) {
 
 const e3k::KernelSet* find_set(const Parsed& p) {
   for (const e3k::KernelSet* k : kSets)
-    if (same(p.x, k->x, k->nx) && same(p.y, k->y, k->ny) && same(p.o, k->o, k->no)) return k;
+    if (k->per_path == p.per_path && same(p.x, k->x, k->nx) && same(p.y, k->y, k->ny) &&
+        same(p.o, k->o, k->no))
+      return k;
   return nullptr;
 }
 

@@ -58,6 +58,14 @@ constexpr int dim_of(const Ir (&v)[N]) {
   return d;
 }
 
+// Output mode of a signature: collapsed (paths landing on one output irrep
+// are summed) unless S declares kPerPath, in which case every path keeps
+// its own output block, in path order.
+template <class S, class = void>
+struct PerPathOf : std::false_type {};
+template <class S>
+struct PerPathOf<S, std::void_t<decltype(S::kPerPath)>> : std::bool_constant<S::kPerPath> {};
+
 template <class S>
 constexpr PathList<count_paths<S>()> make_paths() {
   PathList<count_paths<S>()> r{};
@@ -77,7 +85,23 @@ constexpr PathList<count_paths<S>()> make_paths() {
     }
     xo += 2 * S::X[i].l + 1;
   }
+  if (PerPathOf<S>::value) {
+    int oo = 0;
+    for (int i = 0; i < n; ++i) {
+      r.p[i].oo = oo;
+      oo += 2 * r.p[i].L + 1;
+    }
+  }
   return r;
+}
+
+template <class S>
+constexpr int out_dim() {
+  if (!PerPathOf<S>::value) return dim_of(S::O);
+  int d = 0;
+  const auto ps = make_paths<S>();
+  for (int i = 0; i < count_paths<S>(); ++i) d += 2 * ps.p[i].L + 1;
+  return d;
 }
 
 template <class S>
@@ -96,7 +120,7 @@ struct Plan {
   static_assert(degrees_supported<S>(), "irreps above the generated table's degree");
   static constexpr int DX = dim_of(S::X);
   static constexpr int DY = dim_of(S::Y);
-  static constexpr int DO = dim_of(S::O);
+  static constexpr int DO = out_dim<S>();
   static constexpr int NP = count_paths<S>();
   static constexpr PathList<NP> paths = make_paths<S>();
 };

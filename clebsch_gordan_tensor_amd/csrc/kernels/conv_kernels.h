@@ -137,13 +137,18 @@ __global__ void __launch_bounds__(kBlock)
   }
 
   T* mb = m + int64_t(b) * PL::DO * C + ch0;
-  if (G == 32 && PL::DO % 2 == 0) {  // two groups: halves trade their halves
-    halves_reduce_scatter<PL::DO, CPL>(acc);
-    const int off = g * (PL::DO / 2);
+  bool stored = false;
+  if constexpr (PL::DO % 2 == 0) {
+    if (G == 32) {  // two groups: halves trade their halves
+      halves_reduce_scatter<PL::DO, CPL>(acc);
+      const int off = g * (PL::DO / 2);
 #pragma unroll
-    for (int i = 0; i < PL::DO / 2; ++i)
-      store_ch_stream<T, CPL>(mb + int64_t(off + i) * C, acc[i]);
-  } else {
+      for (int i = 0; i < PL::DO / 2; ++i)
+        store_ch_stream<T, CPL>(mb + int64_t(off + i) * C, acc[i]);
+      stored = true;
+    }
+  }
+  if (!stored) {
     reduce_groups<PL::DO, CPL>(acc, G);
 #pragma unroll
     for (int i = 0; i < PL::DO; ++i)
@@ -451,6 +456,7 @@ KernelSet make_set(const char* name) {
   k.dy = Plan<S>::DY;
   k.dout = Plan<S>::DO;
   k.np = Plan<S>::NP;
+  k.per_path = PerPathOf<S>::value ? 1 : 0;
   sfor_host<0, 3>([&](auto c) {
     constexpr int CPL = 1 << c;
     k.fwd[0][0][c] = &launch_fwd<S, float, CPL, false>;

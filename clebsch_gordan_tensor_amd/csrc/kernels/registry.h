@@ -72,6 +72,7 @@ struct KernelSet {
   int nx, ny, no;
   IrSpec x[4], y[4], o[4];
   int dx, dy, dout, np;  // component and path counts of the signature
+  int per_path;          // 1: one output block per path
   // [dtype: 0 f32, 1 bf16][y given][channels per lane: 0 -> 1, 1 -> 2, 2 -> 4]
   FwdFn fwd[2][2][3];
   BwdFn bwd[2][2][3];
@@ -83,6 +84,9 @@ extern const KernelSet kSetL1;
 extern const KernelSet kSetL1to3;
 extern const KernelSet kSetL2to3;
 extern const KernelSet kSetL3to3;
+extern const KernelSet kSetL1PP;
+extern const KernelSet kSetL1to3PP;
+extern const KernelSet kSetL2to3PP;
 
 // Prepare-transpose and harmonics launchers (prep.hip).
 hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr, const int* sender,

@@ -39,4 +39,10 @@ struct SigL3to3 {
   static constexpr Ir O[NO] = {{0, 1}, {1, -1}, {2, 1}, {3, -1}};
 };
 
+// One output block per path (e3j's default) on signature B's paths.
+template <class B>
+struct PerPath : B {
+  static constexpr bool kPerPath = true;
+};
+
 }  // namespace e3k

@@ -66,16 +66,21 @@ def dim(irreps):
     return sum(2 * l + 1 for l, _ in irreps)
 
 
-def num_paths(x, y, out):
-    """Paths in canonical order: x irrep, then y irrep, then output irrep;
-    triangle rule and p_x p_y = p_out (parity rule of the e3j paper, B.1)."""
-    n = 0
-    for lx, px in x:
-        for ly, py in y:
-            for lo, po in out:
+def path_list(x, y, out):
+    """Paths (ix, iy, io) in canonical order: x irrep, then y irrep, then
+    output irrep; triangle rule and p_x p_y = p_out (parity rule of the e3j
+    paper, B.1).  Used to shape inputs (w has one slot per path)."""
+    res = []
+    for i, (lx, px) in enumerate(x):
+        for j, (ly, py) in enumerate(y):
+            for k, (lo, po) in enumerate(out):
                 if abs(lx - ly) <= lo <= lx + ly and px * py == po:
-                    n += 1
-    return n
+                    res.append((i, j, k))
+    return res
+
+
+def num_paths(x, y, out):
+    return len(path_list(x, y, out))
 
 
 # ---------------------------------------------------------------- draws

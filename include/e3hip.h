@@ -91,7 +91,11 @@ typedef struct {
 } e3_irreps;
 
 enum {
-  E3_Y_GIVEN = 1 /* conv: edge_vec_or_Y holds harmonics Y[E][dy], not vectors */
+  E3_Y_GIVEN = 1,     /* conv: edge_vec_or_Y holds harmonics Y[E][dy], not vectors */
+  E3_OUT_PER_PATH = 2 /* one output block per path, in path order, instead of one
+                         per output irrep (e3j's default layout; A.3, E.1):
+                         m, dm, z, dz become [rows][sum over paths of 2L+1][C],
+                         `out` still lists the irreps paths may land on */
 };
 
 typedef struct {
@@ -108,8 +112,10 @@ e3_status e3_path_info(const e3_desc* desc, int32_t i, int32_t* ix, int32_t* iy,
 /* 1 if the descriptor, storage type and channel count have convolution
  * kernels: the irreps triple must be one of the specialised signatures
  * (x 0e+1o, 0e+1o+2e or 0e+1o+2e+3o; y the harmonic bank 0e+1o or
- * 0e+1o+2e+3o; out 0e+1o or 0e+1o+2e+3o) and C a power of two with
- * 1 <= C <= 256.  The tensor-product calls accept the same. */
+ * 0e+1o+2e+3o; out 0e+1o or 0e+1o+2e+3o; with E3_OUT_PER_PATH the triples
+ * 0e+1o / Y<=1 / 0e+1o, 0e+1o / Y<=3 / 0e+1o+2e+3o and
+ * 0e+1o+2e / Y<=3 / 0e+1o+2e+3o) and C a power of two with 1 <= C <= 256.
+ * The tensor-product calls accept the same. */
 int32_t e3_supported(const e3_desc* desc, e3_dtype dtype);
 
 /* Real coupling block T[M][m1][m2] of (l1, l2, L), l <= 3, written to the

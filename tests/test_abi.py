@@ -78,6 +78,16 @@ def test_supported_signatures(lib):
         assert api.supported(d, api.E3_F32) and api.supported(d, api.E3_BF16)
     d = api.Desc.from_strings(*SIGNATURES[4][::2][:1], "0e+1o+2e", SIGNATURES[4][2])
     assert not api.supported(d)
+    # one output block per path: three signatures
+    sh3 = "0e+1o+2e+3o"
+    for xs, ys, os_, ok in (("8x0e+8x1o", "0e+1o", "8x0e+8x1o", True),
+                            ("8x0e+8x1o", sh3, "8x0e+8x1o+8x2e+8x3o", True),
+                            ("8x0e+8x1o+8x2e", sh3, "8x0e+8x1o+8x2e+8x3o", True),
+                            ("8x0e+8x1o+8x2e+8x3o", sh3, "8x0e+8x1o+8x2e+8x3o", False)):
+        d = api.Desc.from_strings(xs, ys, os_, api.E3_OUT_PER_PATH)
+        assert api.supported(d) == ok, xs
+    pp = api.Desc.from_strings("8x0e+8x1o", sh3, "8x0e+8x1o+8x2e+8x3o", api.E3_OUT_PER_PATH)
+    assert pp.dout == 40 and pp.with_flags(0).dout == 16
     # channel counts: 4 * 2^k up to 256
     for C_, ok in ((4, True), (8, True), (96, False), (256, True), (512, False), (6, False)):
         d = api.Desc([(0, 1), (1, -1)], [(0, 1), (1, -1)], [(0, 1), (1, -1)], C_)

@@ -1,0 +1,134 @@
+"""GPU parity of the per-path output mode (E3_OUT_PER_PATH: one output block
+per path, e3j's default layout) through the C ABI, against the fp64 oracle
+in the same mode.
+
+Tolerance: 2e-2 ahead of storage rounding for bf16, as elsewhere.  For fp32,
+max(|gpu - oracle| - 4 ulp |oracle|, 0) / RMS(oracle) <= 1e-5 per output
+tensor: without the sum over paths a single heavy edge dominates an element
+(water3k's radial weights diverge as 1/d at the closest pair, 0.155 A), so
+max/RMS reaches 30 and the literal gate would allow under 3 ulps of float32
+rounding at the largest element.  The allowance covers that rounding only;
+a wrong coefficient, sign or index is off by orders of magnitude more.
+"""
+import numpy as np
+import pytest
+
+from clebsch_gordan_tensor_amd import synth as S
+from oracle import oracle as O
+from tests.gpu_util import TOL_BF16, TOL_F32, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+ULPS = 4  # float32 rounding allowance per element (see the module docstring)
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    from clebsch_gordan_tensor_amd import api
+    api.lib()
+    return api
+
+
+def _descs(xi, yi, oi, C, flags=0):
+    from clebsch_gordan_tensor_amd import api
+    return (api.Desc(xi, yi, oi, C, flags | api.E3_OUT_PER_PATH),
+            O.Desc(xi, yi, oi, C, per_path=True))
+
+
+def _conv_case(name, dtype="f32"):
+    p = S.make_conv(name, with_dm=False)
+    d, od = _descs(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    rng = np.random.default_rng(140)
+    dm = rng.standard_normal((p.graph.n_nodes, od.dout, p.channels)).astype(np.float32)
+    x, w = p.x, p.w
+    if dtype == "bf16":
+        x, w, dm = S.round_bf16(x), S.round_bf16(w), S.round_bf16(dm)
+    return p, d, od, x, w, dm
+
+
+def _run(gpu, d, g, x, w, dm, dtype):
+    rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+    ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=ev)
+    xd, wd, dmd = dev(x, dtype), dev(w, dtype), dev(dm, dtype)
+    m = gpu.conv_forward(d, rowptr, sender, ev, xd, wd, workspace=ws)
+    dx, dw, dY = gpu.conv_backward(d, rowptr, sender, ws, ev, xd, wd, dmd)
+    torch.cuda.synchronize()
+    return host(m), host(dx), host(dw), host(dY)
+
+
+def _oracle(od, g, x, w, dm):
+    m = O.conv_forward(od, g.rowptr, g.sender, x, w, evec=g.evec)
+    dx = O.conv_backward_dx(od, g.rowptr, g.sender, w, dm, evec=g.evec)
+    dw, dY = O.conv_backward_edge(od, g.rowptr, g.sender, x, w, dm, evec=g.evec)
+    return m, dx, dw, dY
+
+
+@pytest.mark.parametrize("name", ["tiny", "water3k"])
+def test_per_path_conv_matches_oracle(gpu, name):
+    p, d, od, x, w, dm = _conv_case(name)
+    assert d.dout == od.dout
+    got = _run(gpu, d, p.graph, x, w, dm, "f32")
+    ref = _oracle(od, p.graph, x, w, dm)
+    for k, a, b in zip(("m", "dx", "dw", "dY"), got, ref):
+        assert_close(a, b, TOL_F32, f"{name} per-path:{k}", f32_ulps=ULPS)
+
+
+def test_per_path_conv_bf16(gpu):
+    p, d, od, x, w, dm = _conv_case("water3k", "bf16")
+    got = _run(gpu, d, p.graph, x, w, dm, "bf16")
+    ref = _oracle(od, p.graph, x, w, dm)
+    for k, a, b in zip(("m", "dx", "dw", "dY"), got, ref):
+        assert_close(a, b, TOL_BF16, f"water3k per-path bf16:{k}", bf16_out=k != "dY")
+
+
+def test_per_path_blocks_sum_to_collapsed_on_gpu(gpu):
+    # two different kernel instantiations must agree after the block sum
+    from clebsch_gordan_tensor_amd import api
+    p = S.make_conv("water3k", with_dm=False)
+    g = p.graph
+    dpp = api.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels, api.E3_OUT_PER_PATH)
+    dc = api.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+    mp = host(gpu.conv_forward(dpp, rowptr, sender, ev, dev(p.x), dev(p.w)))
+    mc = host(gpu.conv_forward(dc, rowptr, sender, ev, dev(p.x), dev(p.w)))
+    off_o = np.cumsum([0] + [2 * l + 1 for l, _ in p.out_irreps])
+    acc = np.zeros_like(mc, dtype=np.float64)
+    off = 0
+    for _, _, o in S.path_list(p.x_irreps, p.y_irreps, p.out_irreps):
+        n = 2 * p.out_irreps[o][0] + 1
+        acc[:, off_o[o]:off_o[o] + n] += mp[:, off:off + n]
+        off += n
+    assert_close(mc, acc, TOL_F32, "per-path sum vs collapsed", f32_ulps=ULPS)
+
+
+def test_per_path_tensor_product(gpu):
+    from clebsch_gordan_tensor_amd import api
+    xi, yi, oi = S.parse_irreps("0e+1o+2e")[1], S.sh_irreps(3), S.parse_irreps("0e+1o+2e+3o")[1]
+    C, B = 128, 1001
+    d, od = _descs(xi, yi, oi, C)
+    rng = np.random.default_rng(141)
+    x = rng.standard_normal((B, 9, C)).astype(np.float32)
+    y = O.sh(3, rng.standard_normal((B, 3))).astype(np.float32)
+    w = rng.standard_normal((B, 17, C)).astype(np.float32)
+    dz = rng.standard_normal((B, od.dout, C)).astype(np.float32)
+    z = gpu.tp_forward(d, dev(x), dev(y), dev(w))
+    dx, dw, dy = gpu.tp_backward(d, dev(x), dev(y), dev(w), dev(dz))
+    torch.cuda.synchronize()
+    assert_close(host(z), O.tp_forward(od, x, y, w), TOL_F32, "tp per-path:z", f32_ulps=ULPS)
+    for k, a, b in zip(("dx", "dw", "dy"), (dx, dw, dy), O.tp_backward(od, x, y, w, dz)):
+        assert_close(host(a), b, TOL_F32, f"tp per-path:{k}", f32_ulps=ULPS)
+    assert api.supported(d)
+
+
+def test_per_path_unsupported_signature(gpu):
+    from clebsch_gordan_tensor_amd import api
+    ir = S.parse_irreps("0e+1o+2e+3o")[1]
+    d = api.Desc(ir, S.sh_irreps(3), ir, 64, api.E3_OUT_PER_PATH)
+    assert not api.supported(d)
+    with pytest.raises(api.E3Error):
+        gpu.tp_forward(d, torch.zeros((4, 16, 64), device="cuda"),
+                       torch.zeros((4, 16), device="cuda"), torch.zeros((4, 23, 64), device="cuda"))
