@@ -25,6 +25,7 @@ HIP_SOURCES = [
     "kernels/inst_l1to3.hip",
     "kernels/inst_l2to3.hip",
     "kernels/inst_l3to3.hip",
+    "kernels/inst_l1to3all.hip",
     "kernels/inst_per_path.hip",
     "kernels/prep.hip",
     "kernels/linear.hip",

@@ -93,9 +93,9 @@ e3_status parse(const e3_desc* d, Parsed& p) {
   return E3_OK;
 }
 
-const e3k::KernelSet* const kSets[] = {&e3k::kSetL1,     &e3k::kSetL1to3,   &e3k::kSetL2to3,
-                                       &e3k::kSetL3to3,   &e3k::kSetL1PP,    &e3k::kSetL1to3PP,
-                                       &e3k::kSetL2to3PP};
+const e3k::KernelSet* const kSets[] = {&e3k::kSetL1,       &e3k::kSetL1to3,   &e3k::kSetL2to3,
+                                       &e3k::kSetL3to3,     &e3k::kSetL1to3All, &e3k::kSetL1PP,
+                                       &e3k::kSetL1to3PP,   &e3k::kSetL2to3PP};
 
 bool same(const std::vector<e3k::IrSpec>& a, const e3k::IrSpec* b, int nb) {
   if (int(a.size()) != nb) return false;

@@ -70,7 +70,7 @@ struct IrSpec {
 struct KernelSet {
   const char* name;
   int nx, ny, no;
-  IrSpec x[4], y[4], o[4];
+  IrSpec x[8], y[8], o[8];
   int dx, dy, dout, np;  // component and path counts of the signature
   int per_path;          // 1: one output block per path
   // [dtype: 0 f32, 1 bf16][y given][channels per lane: 0 -> 1, 1 -> 2, 2 -> 4]
@@ -84,6 +84,7 @@ extern const KernelSet kSetL1;
 extern const KernelSet kSetL1to3;
 extern const KernelSet kSetL2to3;
 extern const KernelSet kSetL3to3;
+extern const KernelSet kSetL1to3All;
 extern const KernelSet kSetL1PP;
 extern const KernelSet kSetL1to3PP;
 extern const KernelSet kSetL2to3PP;

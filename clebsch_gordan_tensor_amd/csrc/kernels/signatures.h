@@ -39,6 +39,15 @@ struct SigL3to3 {
   static constexpr Ir O[NO] = {{0, 1}, {1, -1}, {2, 1}, {3, -1}};
 };
 
+// 0e+1o (x) Y_0..3 -> every parity-allowed output up to l = 3, pseudotensors
+// included: 0e+1o+1e+2e+2o+3o+3e (13 paths)
+struct SigL1to3All {
+  static constexpr int NX = 2, NY = 4, NO = 7;
+  static constexpr Ir X[NX] = {{0, 1}, {1, -1}};
+  static constexpr Ir Y[NY] = {{0, 1}, {1, -1}, {2, 1}, {3, -1}};
+  static constexpr Ir O[NO] = {{0, 1}, {1, -1}, {1, 1}, {2, 1}, {2, -1}, {3, -1}, {3, 1}};
+};
+
 // One output block per path (e3j's default) on signature B's paths.
 template <class B>
 struct PerPath : B {

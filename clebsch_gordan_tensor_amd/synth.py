@@ -258,6 +258,10 @@ CONV_CONFIGS = {
     "mace64k": dict(n=64000, density=0.1, cutoff=5.0, x="128x0e+128x1o", lmax=3,
                     out="128x0e+128x1o+128x2e+128x3o", weights="normal", dtype="f32",
                     permute=False),
+    # the 64k workload with every parity-allowed output up to l = 3 (13 paths)
+    "mace64k_all": dict(n=64000, density=0.1, cutoff=5.0, x="128x0e+128x1o", lmax=3,
+                        out="128x0e+128x1o+128x1e+128x2e+128x2o+128x3o+128x3e",
+                        weights="normal", dtype="f32", permute=False),
     "ho20k": dict(n=20000, density=0.1, cutoff=5.0, x="64x0e+64x1o+64x2e+64x3o", lmax=3,
                   out="64x0e+64x1o+64x2e+64x3o", weights="normal", dtype="bf16", permute=True),
 }

@@ -112,7 +112,8 @@ e3_status e3_path_info(const e3_desc* desc, int32_t i, int32_t* ix, int32_t* iy,
 /* 1 if the descriptor, storage type and channel count have convolution
  * kernels: the irreps triple must be one of the specialised signatures
  * (x 0e+1o, 0e+1o+2e or 0e+1o+2e+3o; y the harmonic bank 0e+1o or
- * 0e+1o+2e+3o; out 0e+1o or 0e+1o+2e+3o; with E3_OUT_PER_PATH the triples
+ * 0e+1o+2e+3o; out 0e+1o or 0e+1o+2e+3o; also x 0e+1o with out
+ * 0e+1o+1e+2e+2o+3o+3e, pseudotensors included; with E3_OUT_PER_PATH the triples
  * 0e+1o / Y<=1 / 0e+1o, 0e+1o / Y<=3 / 0e+1o+2e+3o and
  * 0e+1o+2e / Y<=3 / 0e+1o+2e+3o) and C a power of two with 1 <= C <= 256.
  * The tensor-product calls accept the same. */
