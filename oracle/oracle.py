@@ -366,3 +366,26 @@ def linear_backward(in_irreps, out_irreps, x, W, dy):
     if n < 0:
         raise ValueError("oracle_linear_backward rejected its arguments")
     return dx, dW
+
+
+def conv_double_backward(d: Desc, rowptr, sender, Y, x, w, dm, ddx, ddY, ddw):
+    """Double backward of the convolution in the given-harmonics form (e3j
+    E.1 Eq.17-18): for variations (ddx, ddY, ddw) of the backward's outputs
+    (dx, dY, dw), the variations of its inputs
+
+      ddm = conv(ddx, Y, w) + conv(x, ddY, w) + conv(x, Y, ddw)
+      dx2 = [dx of conv_bwd(x, ddY, w, dm)] + [dx of conv_bwd(x, Y, ddw, dm)]
+      dY2 = [dY of conv_bwd(ddx, Y, w, dm)] + [dY of conv_bwd(x, Y, ddw, dm)]
+      dw2 = [dw of conv_bwd(ddx, Y, w, dm)] + [dw of conv_bwd(x, ddY, w, dm)]
+
+    composed from this module's convolution and its backward, in the pages'
+    order.  Returns (dx2, dY2, dw2, ddm)."""
+    fwd = lambda x_, Y_, w_: conv_forward(d, rowptr, sender, x_, w_, Y=Y_)
+    bdx = lambda Y_, w_: conv_backward_dx(d, rowptr, sender, w_, dm, Y=Y_)
+    bed = lambda x_, Y_, w_: conv_backward_edge(d, rowptr, sender, x_, w_, dm, Y=Y_)
+    ddm = fwd(ddx, Y, w) + fwd(x, ddY, w) + fwd(x, Y, ddw)
+    dx2 = bdx(ddY, w) + bdx(Y, ddw)
+    dwa, dYa = bed(ddx, Y, w)
+    dwb, _ = bed(x, ddY, w)
+    _, dYc = bed(x, Y, ddw)
+    return dx2, dYa + dYc, dwa + dwb, ddm

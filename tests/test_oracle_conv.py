@@ -457,3 +457,42 @@ def test_per_path_backward_euler_and_finite_differences():
         wp[idx] += h
         wm[idx] -= h
         assert (loss(wp) - loss(wm)) / (2 * h) == pytest.approx(dw[idx], rel=1e-7, abs=1e-9)
+
+
+# ------------------------------------------------------------ double backward
+
+def test_double_backward_is_the_gradient_of_the_backward_pairing():
+    # L(x, Y, w, dm) = <ddx, dx> + <ddY, dY> + <ddw, dw> with (dx, dY, dw) the
+    # backward; the double backward returns dL/d(x, Y, w, dm)
+    rng = np.random.default_rng(70)
+    g = S.random_graph(30, 6.0, 3.0, seed=70)
+    x_ir, o_ir = [(0, 1), (1, -1)], [(0, 1), (1, -1), (2, 1), (3, -1)]
+    C = 2
+    d = desc_of(x_ir, S.sh_irreps(3), o_ir, C)
+    P = O.num_paths(d)
+    x = rng.standard_normal((g.n_nodes, 4, C))
+    Y = O.sh(3, g.evec) + 0.1 * rng.standard_normal((g.n_edges, 16))
+    w = rng.standard_normal((g.n_edges, P, C))
+    dm = rng.standard_normal((g.n_nodes, 16, C))
+    ddx = rng.standard_normal(x.shape)
+    ddY = rng.standard_normal(Y.shape)
+    ddw = rng.standard_normal(w.shape)
+
+    def pairing(x, Y, w, dm):
+        dx = O.conv_backward_dx(d, g.rowptr, g.sender, w, dm, Y=Y)
+        dw, dY = O.conv_backward_edge(d, g.rowptr, g.sender, x, w, dm, Y=Y)
+        return np.vdot(ddx, dx) + np.vdot(ddY, dY) + np.vdot(ddw, dw)
+
+    grads = O.conv_double_backward(d, g.rowptr, g.sender, Y, x, w, dm, ddx, ddY, ddw)
+    args = [x, Y, w, dm]
+    h = 1e-4
+    for k, grad in enumerate(grads):
+        for _ in range(5):
+            idx = tuple(rng.integers(0, s) for s in args[k].shape)
+            ap, am = args[k].copy(), args[k].copy()
+            ap[idx] += h
+            am[idx] -= h
+            pa, ma = list(args), list(args)
+            pa[k], ma[k] = ap, am
+            fd = (pairing(*pa) - pairing(*ma)) / (2 * h)
+            assert fd == pytest.approx(grad[idx], rel=1e-7, abs=1e-9), (k, idx)
