@@ -45,7 +45,8 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_tp_backward", "e3_conv_forward", "e3_conv_workspace_size",
            "e3_conv_prepare_transpose", "e3_conv_backward", "e3_edge_grad_to_nodes",
            "e3_linear_num_weights", "e3_linear", "e3_linear_workspace_size",
-           "e3_linear_backward", "e3_last_error"]
+           "e3_linear_backward", "e3_conv_double_backward_scratch_size",
+           "e3_conv_double_backward", "e3_last_error"]
 
 
 def lib():
@@ -72,6 +73,9 @@ def lib():
     L.e3_linear_num_weights.argtypes = [ip, ip, C.POINTER(i32)]
     L.e3_linear.argtypes = [ip, ip, i64, vp, vp, vp, C.c_int, vp]
     L.e3_linear_workspace_size.argtypes = [ip, ip, C.POINTER(sz)]
+    L.e3_conv_double_backward_scratch_size.argtypes = [dp, i32, i32, C.c_int, C.POINTER(sz)]
+    L.e3_conv_double_backward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, vp, vp, sz, C.c_int, vp]
     L.e3_linear_backward.argtypes = [ip, ip, i64, vp, vp, vp, vp, vp, vp, sz, C.c_int, vp]
     L.e3_conv_forward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, C.c_int, vp]
     L.e3_conv_workspace_size.argtypes = [i32, i32, C.POINTER(sz)]
@@ -426,3 +430,34 @@ def linear_backward(in_irreps, out_irreps, x, W, dy, dx=None, dW=None, workspace
                                     workspace.numel() * workspace.element_size(),
                                     _dtype_code(x), _stream(stream)))
     return dx, dW
+
+
+def conv_double_backward(desc: Desc, rowptr, sender, workspace, Y, x, w, dm, ddx, ddY, ddw,
+                         scratch=None, stream=None):
+    """(dx2, dY2, dw2, ddm): the double backward of the convolution for the
+    variations (ddx, ddY, ddw) of the backward's outputs; desc needs
+    E3_Y_GIVEN and Y the given harmonics."""
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    P = num_paths(desc)
+    dt = x.dtype
+    _need(Y, "Y", shape=(E, desc.dy), dtype=torch.float32)
+    _need(ddY, "ddY", shape=(E, desc.dy), dtype=torch.float32)
+    for t, n, shp in ((x, "x", (N, desc.dx, desc.channels)), (ddx, "ddx", (N, desc.dx, desc.channels)),
+                      (w, "w", (E, P, desc.channels)), (ddw, "ddw", (E, P, desc.channels)),
+                      (dm, "dm", (N, desc.dout, desc.channels))):
+        _need(t, n, shape=shp, dtype=dt)
+    nb = C.c_size_t()
+    _check(lib().e3_conv_double_backward_scratch_size(C.byref(desc.c()), N, E, _dtype_code(x),
+                                                      C.byref(nb)))
+    if scratch is None:
+        scratch = torch.empty(nb.value, device=x.device, dtype=torch.uint8)
+    dx2, dw2 = torch.empty_like(x), torch.empty_like(w)
+    dY2 = torch.empty_like(Y)
+    ddm = torch.empty_like(dm)
+    _check(lib().e3_conv_double_backward(
+        C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(Y), _ptr(x), _ptr(w), _ptr(dm),
+        _ptr(ddx), _ptr(ddY), _ptr(ddw), _ptr(dx2), _ptr(dY2), _ptr(dw2), _ptr(ddm),
+        _ptr(scratch), scratch.numel() * scratch.element_size(), _dtype_code(x), _stream(stream)))
+    return dx2, dY2, dw2, ddm

@@ -398,6 +398,89 @@ e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges
 
 namespace {
 
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Scratch of the double backward: one m-, x-, Y- and w-sized temporary.
+size_t double_backward_scratch(const Parsed& p, int64_t n_nodes, int64_t n_edges, e3_dtype dt) {
+  const size_t es = dt == E3_BF16 ? 2 : 4;
+  return align256(size_t(n_nodes) * p.dout * p.C * es) +
+         align256(size_t(n_nodes) * p.dx * p.C * es) + align256(size_t(n_edges) * p.dy * 4) +
+         align256(size_t(n_edges) * p.P * p.C * es);
+}
+
+}  // namespace
+
+e3_status e3_conv_double_backward_scratch_size(const e3_desc* desc, int32_t n_nodes,
+                                               int32_t n_edges, e3_dtype dtype, size_t* bytes) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if (!bytes) return fail(E3_ERR_INVALID_ARG, "bytes is null");
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  *bytes = double_backward_scratch(p, n_nodes, n_edges, dtype);
+  return ok();
+}
+
+e3_status e3_conv_double_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                  const int32_t* rowptr, const int32_t* sender,
+                                  const void* workspace, size_t ws_bytes, const float* Y,
+                                  const void* x, const void* w, const void* dm, const void* ddx,
+                                  const float* ddY, const void* ddw, void* dx2, float* dY2,
+                                  void* dw2, void* ddm, void* scratch, size_t scratch_bytes,
+                                  e3_dtype dtype, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if (!(desc->flags & E3_Y_GIVEN))
+    return fail(E3_ERR_INVALID_ARG, "the double backward takes given harmonics (E3_Y_GIVEN)");
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes == 0) return ok();
+  const size_t need = double_backward_scratch(p, n_nodes, n_edges, dtype);
+  if (!scratch || scratch_bytes < need)
+    return fail(E3_ERR_WORKSPACE, "scratch needs " + std::to_string(need) + " bytes");
+  if (!aligned16(scratch)) return fail(E3_ERR_ALIGNMENT, "scratch must be 16-byte aligned");
+  if (!x || !dm || !ddx || !dx2 || !ddm || (n_edges > 0 && (!Y || !w || !ddY || !ddw || !dY2 || !dw2)))
+    return fail(E3_ERR_INVALID_ARG, "null pointer");
+  const size_t es = dtype == E3_BF16 ? 2 : 4;
+  char* sc = static_cast<char*>(scratch);
+  void* t_m = sc;
+  sc += align256(size_t(n_nodes) * p.dout * p.C * es);
+  void* t_x = sc;
+  sc += align256(size_t(n_nodes) * p.dx * p.C * es);
+  float* t_Y = reinterpret_cast<float*>(sc);
+  sc += align256(size_t(n_edges) * p.dy * 4);
+  void* t_w = sc;
+  const hipStream_t st = hipStream_t(stream);
+  const int bf = dtype == E3_BF16;
+  const int64_t nm = int64_t(n_nodes) * p.dout * p.C, nx = int64_t(n_nodes) * p.dx * p.C;
+  const int64_t nY = int64_t(n_edges) * p.dy, nw = int64_t(n_edges) * p.P * p.C;
+  auto fwd = [&](const void* xx, const float* yy, const void* ww, void* out) {
+    return e3_conv_forward(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes, yy, xx,
+                           ww, out, dtype, stream);
+  };
+  auto bwd = [&](const void* xx, const float* yy, const void* ww, void* ox, void* ow, float* oy) {
+    return e3_conv_backward(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes, yy, xx,
+                            ww, dm, ox, ow, oy, dtype, stream);
+  };
+  auto add = [&](void* dst, const void* src, int64_t n, int b16) {
+    return hip_status(e3k::launch_add(dst, src, n, b16, st), "double_backward");
+  };
+  // ddm = conv(ddx, Y, w) + conv(x, ddY, w) + conv(x, Y, ddw)        (e3j Eq.17)
+  if ((s = fwd(ddx, Y, w, ddm)) != E3_OK) return s;
+  if ((s = fwd(x, ddY, w, t_m)) != E3_OK || (s = add(ddm, t_m, nm, bf)) != E3_OK) return s;
+  if ((s = fwd(x, Y, ddw, t_m)) != E3_OK || (s = add(ddm, t_m, nm, bf)) != E3_OK) return s;
+  // the three backward calls of e3j Eq.18, unused cotangents to scratch
+  if ((s = bwd(ddx, Y, w, t_x, dw2, dY2)) != E3_OK) return s;
+  if ((s = bwd(x, ddY, w, dx2, t_w, t_Y)) != E3_OK || (s = add(dw2, t_w, nw, bf)) != E3_OK)
+    return s;
+  if ((s = bwd(x, Y, ddw, t_x, t_w, t_Y)) != E3_OK || (s = add(dx2, t_x, nx, bf)) != E3_OK ||
+      (s = add(dY2, t_Y, nY, 0)) != E3_OK)
+    return s;
+  return ok();
+}
+
+namespace {
+
 // Block lists of a channel mixing: every block of a list has one
 // multiplicity (the channel count of that side).
 e3_status parse_linear(const e3_irreps* in, const e3_irreps* out, std::vector<e3k::IrSpec>& li,

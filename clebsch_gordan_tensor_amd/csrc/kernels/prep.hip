@@ -606,4 +606,31 @@ hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr
   return hipGetLastError();
 }
 
+// dst[i] += src[i] for n elements of float or bf16 storage (fp32 sum,
+// one rounding for bf16).
+template <class T>
+__global__ void __launch_bounds__(256)
+    k_add(int64_t n, T* __restrict__ dst, const T* __restrict__ src) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    float a[1], b[1];
+    load_ch<T, 1>(dst + i, a);
+    load_ch<T, 1>(src + i, b);
+    a[0] += b[0];
+    store_ch<T, 1>(dst + i, a);
+  }
+}
+
+hipError_t launch_add(void* dst, const void* src, int64_t n, int bf16, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const dim3 g(grid_for(n, 256)), b(256);
+  if (bf16)
+    hipLaunchKernelGGL(k_add<bf16_t>, g, b, 0, s, n, static_cast<bf16_t*>(dst),
+                       static_cast<const bf16_t*>(src));
+  else
+    hipLaunchKernelGGL(k_add<float>, g, b, 0, s, n, static_cast<float*>(dst),
+                       static_cast<const float*>(src));
+  return hipGetLastError();
+}
+
 }  // namespace e3k

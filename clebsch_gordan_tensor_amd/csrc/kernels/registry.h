@@ -93,6 +93,7 @@ extern const KernelSet kSetL2to3PP;
 hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr, const int* sender,
                                     const float* evec, int* ws, hipStream_t s);
 hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hipStream_t s);
+hipError_t launch_add(void* dst, const void* src, int64_t n, int bf16, hipStream_t s);
 hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
                                  float* dvec, hipStream_t s);
 hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr,

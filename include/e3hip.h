@@ -155,6 +155,28 @@ e3_status e3_tp_backward(const e3_desc* desc, int64_t n_rows, const void* x, con
 e3_status e3_spherical_harmonics_backward(int32_t lmax, int64_t n, const float* vec,
                                           const float* dY, float* dvec, void* stream);
 
+/* Double backward of the convolution (e3j E.1 Eq.17-18) in the
+ * given-harmonics form (desc->flags must hold E3_Y_GIVEN): for variations
+ * ddx [N][dx][C], ddY [E][dy], ddw [E][P][C] of the backward's outputs, the
+ * variations of its inputs
+ *   ddm = conv(ddx, Y, w) + conv(x, ddY, w) + conv(x, Y, ddw)     [N][dout][C]
+ *   dx2 = dx of conv_bwd(x, ddY, w, dm) + dx of conv_bwd(x, Y, ddw, dm)
+ *   dY2 = dY of conv_bwd(ddx, Y, w, dm) + dY of conv_bwd(x, Y, ddw, dm)
+ *   dw2 = dw of conv_bwd(ddx, Y, w, dm) + dw of conv_bwd(x, ddY, w, dm)
+ * composed from the forward and backward kernels (three each) and additions.
+ * workspace: from e3_conv_prepare_transpose; scratch: caller-owned,
+ * e3_conv_double_backward_scratch_size bytes, 16-byte aligned.  Storage
+ * type and alignment as for e3_conv_backward; Y, ddY, dY2 float32. */
+e3_status e3_conv_double_backward_scratch_size(const e3_desc* desc, int32_t n_nodes,
+                                               int32_t n_edges, e3_dtype dtype, size_t* bytes);
+e3_status e3_conv_double_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                  const int32_t* rowptr, const int32_t* sender,
+                                  const void* workspace, size_t ws_bytes, const float* Y,
+                                  const void* x, const void* w, const void* dm, const void* ddx,
+                                  const float* ddY, const void* ddw, void* dx2, float* dY2,
+                                  void* dw2, void* ddm, void* scratch, size_t scratch_bytes,
+                                  e3_dtype dtype, void* stream);
+
 /* Per-node gradient from per-edge vector gradients, for r_e = pos[receiver]
  * - pos[sender]:
  *   node_grad[b] = sum_{e: receiver(e) = b} edge_grad[e]

@@ -180,6 +180,20 @@ def test_error_codes(lib):
     mixed = api._irreps_struct([(0, 1), (1, -1)], 16)
     mixed.v[1].mul = 8
     assert lib.e3_linear(C.byref(mixed), C.byref(ir_out), 5, fake, fake, fake, 0, None) == -2
+    # double backward: given harmonics only, scratch size and alignment
+    yg = good.with_flags(api.E3_Y_GIVEN)
+    assert lib.e3_conv_double_backward_scratch_size(_desc_c(yg), 10, 100, 0, C.byref(sz)) == 0
+    # m and x: 10*4*8*4 bytes each; Y: 100*4*4 -> 1792 aligned; w: 100 edges * 4 paths * 8 * 4
+    assert sz.value == 1280 + 1280 + 1792 + 12800
+    dbl = lambda d, scratch, nb: lib.e3_conv_double_backward(
+        _desc_c(d), 10, 100, fake, fake, fake, need, fake, fake, fake, fake, fake, fake, fake,
+        fake, fake, fake, fake, scratch, nb, 0, None)
+    assert dbl(good, fake, sz.value) == -1
+    assert dbl(yg, fake, sz.value - 1) == -6
+    assert dbl(yg, odd, sz.value) == -4
+    assert lib.e3_conv_double_backward(_desc_c(yg), 0, 0, None, None, None, 0, None, None, None,
+                                       None, None, None, None, None, None, None, None, None, 0, 0,
+                                       None) == 0
     out = np.zeros(10)
     assert lib.e3_cg_block(1, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
     assert lib.e3_cg_block(4, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1

@@ -1,0 +1,124 @@
+"""GPU parity of the convolution's double backward (e3j E.1 Eq.17-18) in the
+given-harmonics form, through the C ABI, against the oracle's composition of
+its fp64 convolution and backward.
+
+Tolerance: max|gpu - oracle| / RMS(oracle) <= 1e-5 per output (fp32).  With
+bf16 storage each output is the bf16 sum of terms that were themselves
+stored in bf16 (one convolution or backward launch each), so the gate is
+2e-2 ahead of one rounding of every term and of the sum:
+max(|gpu - oracle| - 2^-8 (sum_t |term_t| + |oracle|), 0) / RMS(oracle),
+the terms taken from the oracle.  The variations ddx, ddY, ddw are
+independent seeded normals (ddY need not be a harmonic: the harmonics are an
+input here).
+"""
+import numpy as np
+import pytest
+
+from clebsch_gordan_tensor_amd import synth as S
+from oracle import oracle as O
+from tests.gpu_util import TOL_BF16, TOL_F32, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    from clebsch_gordan_tensor_amd import api
+    api.lib()
+    return api
+
+
+def _case(name, seed, dtype="f32"):
+    p = S.make_conv(name)
+    g = p.graph
+    Y = O.sh(max(l for l, _ in p.y_irreps), g.evec.astype(np.float64)).astype(np.float32)
+    rng = np.random.default_rng(seed)
+    ddx = rng.standard_normal(p.x.shape).astype(np.float32)
+    ddY = rng.standard_normal(Y.shape).astype(np.float32)
+    ddw = rng.standard_normal(p.w.shape).astype(np.float32)
+    x, w, dm = p.x, p.w, p.dm
+    if dtype == "bf16":
+        x, w, dm, ddx, ddw = (S.round_bf16(a) for a in (x, w, dm, ddx, ddw))
+    return p, Y, x, w, dm, ddx, ddY, ddw
+
+
+def _run(gpu, p, Y, x, w, dm, ddx, ddY, ddw, dtype):
+    g = p.graph
+    d = gpu.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels, gpu.E3_Y_GIVEN)
+    rowptr, sender = dev(g.rowptr), dev(g.sender)
+    ws = gpu.conv_prepare_transpose(rowptr, sender)
+    out = gpu.conv_double_backward(d, rowptr, sender, ws, dev(Y), dev(x, dtype), dev(w, dtype),
+                                   dev(dm, dtype), dev(ddx, dtype), dev(ddY), dev(ddw, dtype))
+    torch.cuda.synchronize()
+    return [host(t) for t in out]
+
+
+def _oracle(p, Y, x, w, dm, ddx, ddY, ddw):
+    od = O.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    g = p.graph
+    return O.conv_double_backward(od, g.rowptr, g.sender, Y, x, w, dm, ddx, ddY, ddw)
+
+
+@pytest.mark.parametrize("name", ["tiny", "water3k"])
+def test_double_backward_matches_oracle(gpu, name):
+    case = _case(name, 150)
+    got = _run(gpu, *case, "f32")
+    ref = _oracle(*case)
+    for k, a, b in zip(("dx2", "dY2", "dw2", "ddm"), got, ref):
+        assert_close(a, b, TOL_F32, f"{name} double backward:{k}")
+
+
+def _terms(p, Y, x, w, dm, ddx, ddY, ddw):
+    # the stored terms of each output, in the order of (dx2, dY2, dw2, ddm)
+    od = O.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    g = p.graph
+    fwd = lambda x_, Y_, w_: O.conv_forward(od, g.rowptr, g.sender, x_, w_, Y=Y_)
+    bdx = lambda Y_, w_: O.conv_backward_dx(od, g.rowptr, g.sender, w_, dm, Y=Y_)
+    bed = lambda x_, Y_, w_: O.conv_backward_edge(od, g.rowptr, g.sender, x_, w_, dm, Y=Y_)
+    dwa, dYa = bed(ddx, Y, w)
+    dwb, _ = bed(x, ddY, w)
+    _, dYc = bed(x, Y, ddw)
+    return ([bdx(ddY, w), bdx(Y, ddw)], [dYa, dYc], [dwa, dwb],
+            [fwd(ddx, Y, w), fwd(x, ddY, w), fwd(x, Y, ddw)])
+
+
+def test_double_backward_bf16(gpu):
+    case = _case("water3k", 151, "bf16")
+    got = _run(gpu, *case, "bf16")
+    ref = _oracle(*case)
+    for k, a, b, ts in zip(("dx2", "dY2", "dw2", "ddm"), got, ref, _terms(*case)):
+        if k == "dY2":  # float32 storage throughout
+            assert_close(a, b, TOL_F32, "water3k double backward bf16:dY2")
+            continue
+        b = np.asarray(b, np.float64)
+        allow = 2.0 ** -8 * (sum(np.abs(t) for t in ts) + np.abs(b))
+        e = np.maximum(np.abs(a - b) - allow, 0.0).max() / np.sqrt(np.mean(b ** 2))
+        assert e <= TOL_BF16, f"water3k double backward bf16:{k}: {e:.3e}"
+
+
+def test_double_backward_linear_in_the_variations(gpu):
+    # the outputs are linear in (ddx, ddY, ddw): one variation at a time
+    # sums to all three at once (different launches, same kernels)
+    p, Y, x, w, dm, ddx, ddY, ddw = _case("tiny", 152)
+    z = lambda a: np.zeros_like(a)
+    parts = [_run(gpu, p, Y, x, w, dm, ddx, z(ddY), z(ddw), "f32"),
+             _run(gpu, p, Y, x, w, dm, z(ddx), ddY, z(ddw), "f32"),
+             _run(gpu, p, Y, x, w, dm, z(ddx), z(ddY), ddw, "f32")]
+    full = _run(gpu, p, Y, x, w, dm, ddx, ddY, ddw, "f32")
+    for i, k in enumerate(("dx2", "dY2", "dw2", "ddm")):
+        assert_close(full[i], parts[0][i] + parts[1][i] + parts[2][i], TOL_F32, f"linearity:{k}")
+
+
+def test_double_backward_needs_given_harmonics(gpu):
+    p, Y, x, w, dm, ddx, ddY, ddw = _case("tiny", 153)
+    g = p.graph
+    d = gpu.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    rowptr, sender = dev(g.rowptr), dev(g.sender)
+    ws = gpu.conv_prepare_transpose(rowptr, sender)
+    with pytest.raises(gpu.E3Error):
+        gpu.conv_double_backward(d, rowptr, sender, ws, dev(Y), dev(x), dev(w), dev(dm),
+                                 dev(ddx), dev(ddY), dev(ddw))
