@@ -46,7 +46,13 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_conv_prepare_transpose", "e3_conv_backward", "e3_edge_grad_to_nodes",
            "e3_linear_num_weights", "e3_linear", "e3_linear_workspace_size",
            "e3_linear_backward", "e3_conv_double_backward_scratch_size",
-           "e3_conv_double_backward", "e3_last_error"]
+           "e3_conv_double_backward", "e3_radial_mlp", "e3_conv_forward_radial",
+           "e3_last_error"]
+
+
+class _CRadial(C.Structure):
+    _fields_ = [("cutoff", C.c_float), ("n_basis", C.c_int32), ("hidden", C.c_int32),
+                ("W1", C.c_void_p), ("W2", C.c_void_p)]
 
 
 def lib():
@@ -73,6 +79,9 @@ def lib():
     L.e3_linear_num_weights.argtypes = [ip, ip, C.POINTER(i32)]
     L.e3_linear.argtypes = [ip, ip, i64, vp, vp, vp, C.c_int, vp]
     L.e3_linear_workspace_size.argtypes = [ip, ip, C.POINTER(sz)]
+    L.e3_radial_mlp.argtypes = [C.POINTER(_CRadial), i32, i32, vp, vp, vp]
+    L.e3_conv_forward_radial.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp,
+                                         C.POINTER(_CRadial), vp, vp]
     L.e3_conv_double_backward_scratch_size.argtypes = [dp, i32, i32, C.c_int, C.POINTER(sz)]
     L.e3_conv_double_backward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
                                           vp, vp, vp, vp, vp, vp, sz, C.c_int, vp]
@@ -461,3 +470,49 @@ def conv_double_backward(desc: Desc, rowptr, sender, workspace, Y, x, w, dm, ddx
         _ptr(ddx), _ptr(ddY), _ptr(ddw), _ptr(dx2), _ptr(dY2), _ptr(dw2), _ptr(ddm),
         _ptr(scratch), scratch.numel() * scratch.element_size(), _dtype_code(x), _stream(stream)))
     return dx2, dY2, dw2, ddm
+
+
+def _radial(cutoff, W1, W2):
+    import torch
+    _need(W1, "W1", dtype=torch.float32)
+    _need(W2, "W2", dtype=torch.float32)
+    if W1.dim() != 2 or W2.dim() != 2 or W1.shape[1] != W2.shape[0]:
+        raise ValueError("W1 [n_basis][hidden] and W2 [hidden][n_cols] expected")
+    return _CRadial(float(cutoff), W1.shape[0], W1.shape[1], W1.data_ptr(), W2.data_ptr())
+
+
+def radial_mlp(edge_vec, cutoff, W1, W2, out=None, stream=None):
+    """w[E][n_cols] = silu(B(|r|) W1) W2 with the 8-function Bessel basis."""
+    import torch
+    E = edge_vec.shape[0]
+    _need(edge_vec, "edge_vec", shape=(E, 3), dtype=torch.float32)
+    r = _radial(cutoff, W1, W2)
+    n_cols = W2.shape[1]
+    if out is None:
+        out = torch.empty((E, n_cols), device=edge_vec.device, dtype=torch.float32)
+    _need(out, "out", shape=(E, n_cols), dtype=torch.float32)
+    _check(lib().e3_radial_mlp(C.byref(r), E, n_cols, _ptr(edge_vec), _ptr(out), _stream(stream)))
+    return out
+
+
+def conv_forward_radial(desc: Desc, rowptr, sender, edge_vec, x, cutoff, W1, W2, out=None,
+                        workspace=None, stream=None):
+    """m = conv(x, Y(edge_vec), w) with w = radial_mlp(edge_vec) computed inside
+    the kernel (never stored); W2 is [64][P*C]."""
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    _need(edge_vec, "edge_vec", shape=(E, 3), dtype=torch.float32)
+    _need(x, "x", shape=(N, desc.dx, desc.channels), dtype=torch.float32)
+    r = _radial(cutoff, W1, W2)
+    if W2.shape[1] != num_paths(desc) * desc.channels:
+        raise ValueError("W2 must have P*C columns")
+    if out is None:
+        out = torch.empty((N, desc.dout, desc.channels), device=x.device, dtype=torch.float32)
+    _need(out, "out", shape=(N, desc.dout, desc.channels), dtype=torch.float32)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().e3_conv_forward_radial(C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender),
+                                        _ptr(workspace), wsb, _ptr(edge_vec), _ptr(x), C.byref(r),
+                                        _ptr(out), _stream(stream)))
+    return out

@@ -29,6 +29,7 @@ HIP_SOURCES = [
     "kernels/inst_per_path.hip",
     "kernels/prep.hip",
     "kernels/linear.hip",
+    "kernels/radial.hip",
     "api.cpp",
     "host/cg_ladder.cpp",
 ]

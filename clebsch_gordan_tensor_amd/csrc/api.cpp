@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -642,6 +643,68 @@ e3_status e3_linear_backward(const e3_irreps* in, const e3_irreps* out, int64_t 
       if ((s = hip_status(e3k::launch_linear_dw(a, bf, st), "linear_backward")) != E3_OK) return s;
     }
   return ok();
+}
+
+namespace {
+
+e3_status check_radial(const e3_radial* mlp) {
+  if (!mlp) return fail(E3_ERR_INVALID_ARG, "radial parameters are null");
+  if (!(mlp->cutoff > 0.0f) || !std::isfinite(mlp->cutoff))
+    return fail(E3_ERR_INVALID_ARG, "cutoff must be positive and finite");
+  if (mlp->n_basis != 8 || mlp->hidden != 64)
+    return fail(E3_ERR_UNSUPPORTED, "radial MLP must have 8 basis functions and 64 hidden units");
+  if (!mlp->W1 || !mlp->W2) return fail(E3_ERR_INVALID_ARG, "W1 or W2 is null");
+  return ok();
+}
+
+}  // namespace
+
+e3_status e3_radial_mlp(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
+                        const float* edge_vec, float* w, void* stream) {
+  e3_status s = check_radial(mlp);
+  if (s != E3_OK) return s;
+  if (n_edges < 0 || n_cols <= 0) return fail(E3_ERR_INVALID_ARG, "bad size");
+  if (n_cols % 16) return fail(E3_ERR_UNSUPPORTED, "n_cols must be a multiple of 16");
+  if (n_edges == 0) return ok();
+  if (!edge_vec || !w) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  return hip_status(e3k::launch_radial_mlp(n_edges, n_cols, edge_vec, mlp->cutoff, mlp->W1,
+                                           mlp->W2, w, hipStream_t(stream)),
+                    "radial_mlp");
+}
+
+e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                 const int32_t* rowptr, const int32_t* sender,
+                                 const void* workspace, size_t ws_bytes, const float* edge_vec,
+                                 const float* x, const e3_radial* mlp, float* m, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if ((s = check_radial(mlp)) != E3_OK) return s;
+  if (desc->flags & (E3_Y_GIVEN | E3_OUT_PER_PATH))
+    return fail(E3_ERR_UNSUPPORTED, "the radial convolution takes edge vectors and collapsed outputs");
+  const e3k::KernelSet* ks = find_set(p);
+  if (!ks || !e3k::radial_conv_supported(ks->name))
+    return fail(E3_ERR_UNSUPPORTED,
+                "no radial convolution kernel for this signature (supported: 0e+1o x harmonics "
+                "0e+1o+2e+3o -> 0e+1o+2e+3o)");
+  if (p.C != 32 && p.C != 64 && p.C != 128 && p.C != 256)
+    return fail(E3_ERR_UNSUPPORTED, "the radial convolution needs C in {32, 64, 128, 256}");
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes == 0) return ok();
+  if (!rowptr || !x || !m) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (n_edges > 0 && (!sender || !edge_vec)) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  const int* order = nullptr;
+  if (workspace) {
+    size_t need = 0;
+    e3_conv_workspace_size(n_nodes, n_edges, &need);
+    if (ws_bytes < need)
+      return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+    order = static_cast<const int*>(workspace) + e3k::transpose_layout(n_nodes, n_edges).order;
+  }
+  e3k::RadialConvArgs a{n_nodes, n_edges, p.C, order, rowptr, sender, edge_vec, x,
+                        mlp->W1, mlp->W2, mlp->cutoff, m};
+  return hip_status(e3k::launch_conv_fwd_radial(ks->name, a, hipStream_t(stream)),
+                    "conv_forward_radial");
 }
 
 const char* e3_last_error(void) { return g_last_error.c_str(); }

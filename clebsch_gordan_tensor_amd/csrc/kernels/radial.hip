@@ -1,0 +1,401 @@
+// Radial edge weights on the gfx950 matrix cores, and the convolution that
+// computes them on the fly so that w never reaches HBM.
+//
+// The e3j paper (A.3, the edge scalars of Eq.7; E.1, message weighting with
+// edge scalars) takes the per-edge, per-path, per-channel weights from an MLP
+// applied to a radial basis embedding of |r|; its model table (Table 3) uses
+// 8 basis functions.  The reading built here (the pages fix nothing else):
+//   B_n(d) = sqrt(2/r_c) sin(n pi d / r_c) / d,  n = 1..8
+//   h_k    = silu(sum_n B_n W1[n][k]),          k < 64
+//   w[j]   = sum_k h_k W2[k][j],                j < P*C  (layout w[e][P][C])
+//
+// k_radial_mlp writes w with fp32 MFMA (v_mfma_f32_16x16x4f32): exact fp32
+// products, fp32 accumulation.
+//
+// k_conv_fwd_radial fuses it into the forward convolution.  One 512-thread
+// workgroup per CU holds, for a 32-channel slab, W2 split into fp16 high and
+// low parts (W2 = hi + lo to 22 bits) in LDS; h is split the same way and
+// w = hi*hi + hi*lo + lo*hi is formed by three v_mfma_f32_16x16x32_f16 per
+// K-step (the lo*lo term is below 2^-22 of the product), accurate to a few
+// 1e-7 of |w| -- the fp32 convolution's tolerance holds.  Each wavefront
+// walks one receiver's edges in tiles of 16: per path the MFMAs leave
+// w[edge][channel] for 4 edges x 2 channels in every lane (rows 4*(lane/16)+r,
+// columns lane%16 of two 16-column blocks), and the CG contraction of those
+// 4 edges follows on the VALU with the weights still in registers.  Slabs
+// are spread over the XCDs (slab = XCD mod slabs), and each XCD walks its
+// share of the receivers in the locality order of the prepare step.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "common.h"
+#include "registry.h"
+#include "signatures.h"
+
+namespace e3k {
+namespace {
+
+constexpr int kRadBasis = 8;
+constexpr int kRadHidden = 64;
+constexpr int kRadXcds = 8;
+// Low parts of the fp16 splits are stored times 2^11 so that they stay
+// normal numbers (a low part is ~2^-12 of its value, often below fp16's
+// normal range); the cross products are scaled back once.
+constexpr float kLoScale = 2048.0f;
+constexpr float kLoUnscale = 1.0f / 2048.0f;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// B[n] = sqrt(2/rc) sin((n+1) pi d / rc) / d of the edge vector (vx, vy, vz),
+// at d = 0 the limit sqrt(2/rc) (n+1) pi / rc.  Evaluated in fp64 and rounded
+// once: the arguments (n+1) pi d / rc reach tens of radians, where an fp32
+// argument alone is off by ~1e-6 absolute -- more than the MLP's outputs
+// tolerate relative to their typical size.  sin((n+1)t) by the Chebyshev
+// recurrence s_{n+1} = 2 cos(t) s_n - s_{n-1}.
+__device__ __forceinline__ void bessel_basis(float vx, float vy, float vz, float rc,
+                                             float (&B)[kRadBasis]) {
+  const double d = sqrt(double(vx) * vx + double(vy) * vy + double(vz) * vz);
+  const double pref = sqrt(2.0 / double(rc));
+  if (d > 0.0) {
+    double s, c;
+    sincos(3.141592653589793 * d / double(rc), &s, &c);
+    const double inv = pref / d;
+    double sp = 0.0, sn = s;
+#pragma unroll
+    for (int n = 0; n < kRadBasis; ++n) {
+      B[n] = float(sn * inv);
+      const double nx = fma(2.0 * c, sn, -sp);
+      sp = sn;
+      sn = nx;
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < kRadBasis; ++n)
+      B[n] = float(pref * double(n + 1) * 3.141592653589793 / double(rc));
+  }
+}
+
+__device__ __forceinline__ float silu(float t) { return t / (1.0f + expf(-t)); }
+
+// ------------------------------------------------------------ radial MLP
+
+constexpr int kMlpCols = 128;  // columns per workgroup slab (8 MFMA blocks)
+
+// w[e][j] for all edges; workgroup = (column slab, edge-tile group), 4 waves,
+// one 16-edge tile per wave at a time.  W2's slab sits in LDS in the B
+// operand order of v_mfma_f32_16x16x4f32 (k = 4*ks + lane/16, column lane%16).
+__global__ void __launch_bounds__(256)
+    k_radial_mlp(int n_edges, int n_cols, int n_slabs, int n_groups, const float* __restrict__ vec,
+                 float rc, const float* __restrict__ W1, const float* __restrict__ W2,
+                 float* __restrict__ w) {
+  __shared__ float s_w2[kMlpCols / 16][kRadHidden / 4][64];
+  __shared__ float s_w1[kRadBasis * kRadHidden];
+  const int slab = blockIdx.x % n_slabs, group = blockIdx.x / n_slabs;
+  for (int i = threadIdx.x; i < (kMlpCols / 16) * (kRadHidden / 4) * 64; i += blockDim.x) {
+    const int cb = i / ((kRadHidden / 4) * 64), ks = (i / 64) % (kRadHidden / 4), l = i % 64;
+    const int k = 4 * ks + l / 16, col = slab * kMlpCols + cb * 16 + l % 16;
+    s_w2[cb][ks][l] = col < n_cols ? W2[int64_t(k) * n_cols + col] : 0.0f;
+  }
+  for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ntiles = (n_edges + 15) / 16;
+  const int ncb = min(kMlpCols, n_cols - slab * kMlpCols) / 16;
+  for (int tile = group * 4 + wave; tile < ntiles; tile += n_groups * 4) {
+    const int er = tile * 16 + (lane & 15);
+    float a[kRadHidden / 4];
+    {
+      float vx = 0.0f, vy = 0.0f, vz = 0.0f;
+      if (er < n_edges) {
+        const float* p = vec + int64_t(er) * 3;
+        vx = p[0];
+        vy = p[1];
+        vz = p[2];
+      }
+      float B[kRadBasis];
+      bessel_basis(vx, vy, vz, rc, B);
+#pragma unroll
+      for (int ks = 0; ks < kRadHidden / 4; ++ks) {
+        const int k = 4 * ks + (lane >> 4);
+        float pre = 0.0f;
+#pragma unroll
+        for (int n = 0; n < kRadBasis; ++n) pre = fmaf(B[n], s_w1[n * kRadHidden + k], pre);
+        a[ks] = er < n_edges ? silu(pre) : 0.0f;
+      }
+    }
+    for (int cb = 0; cb < ncb; ++cb) {
+      float4v D = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < kRadHidden / 4; ++ks)
+        D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks], s_w2[cb][ks][lane], D, 0, 0, 0);
+      const int col = slab * kMlpCols + cb * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = tile * 16 + 4 * (lane >> 4) + r;
+        if (e < n_edges) __builtin_nontemporal_store(D[r], w + int64_t(e) * n_cols + col);
+      }
+    }
+  }
+}
+
+// ------------------------------------------- fused radial convolution
+
+constexpr int kRadWaves = 8;  // 512-thread workgroups, one per CU
+
+// One path of e3j E.1 Eq.13 for one edge and CPL channels, with the edge's
+// harmonics of degree l2 in Yl (component m2 at Yl[m2]):
+//   acc[oo+M][k] += w[k] sum_{m1,m2} c(M,m1,m2) Yl[m2] x[xo+m1][k]
+// in the cheaper of the two orders (contract then weight, or weight x first).
+template <class S, int PI, int CPL>
+__device__ __forceinline__ void path_forward(const float* __restrict__ Yl,
+                                             const float (&xv)[Plan<S>::DX][CPL],
+                                             const float (&wp)[CPL],
+                                             float (&acc)[CPL][Plan<S>::DO]) {
+  constexpr PathC P = Plan<S>::paths.p[PI];
+  constexpr int n1 = 2 * P.l1 + 1, nL = 2 * P.L + 1;
+  float y[2 * P.l2 + 1];
+#pragma unroll
+  for (int i = 0; i < 2 * P.l2 + 1; ++i) y[i] = Yl[i];
+  if constexpr (n1 < nL) {
+    float u[n1][CPL];
+#pragma unroll
+    for (int a = 0; a < n1; ++a)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) u[a][k] = wp[k] * xv[P.xo + a][k];
+    float A = 0.0f;
+    sfor<0, P.rcnt>([&](auto r) {
+      constexpr CgRec R = kRec[P.roff + r];
+      if constexpr (group_first(P.roff, r))
+        A = R.c * y[R.m2];
+      else
+        A = fmaf(R.c, y[R.m2], A);
+      if constexpr (group_last(P.roff, P.rcnt, r)) {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) acc[k][P.oo + R.M] = fmaf(A, u[R.m1][k], acc[k][P.oo + R.M]);
+      }
+    });
+  } else {
+    float z[nL][CPL];
+#pragma unroll
+    for (int M = 0; M < nL; ++M)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) z[M][k] = 0.0f;
+    float A = 0.0f;
+    sfor<0, P.rcnt>([&](auto r) {
+      constexpr CgRec R = kRec[P.roff + r];
+      if constexpr (group_first(P.roff, r))
+        A = R.c * y[R.m2];
+      else
+        A = fmaf(R.c, y[R.m2], A);
+      if constexpr (group_last(P.roff, P.rcnt, r)) {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) z[R.M][k] = fmaf(A, xv[P.xo + R.m1][k], z[R.M][k]);
+      }
+    });
+#pragma unroll
+    for (int M = 0; M < nL; ++M)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) acc[k][P.oo + M] = fmaf(wp[k], z[M][k], acc[k][P.oo + M]);
+  }
+}
+
+template <class S>
+constexpr size_t radial_lds_bytes() {
+  using PL = Plan<S>;
+  return size_t(PL::NP) * 8 * 64 * sizeof(half8)              // W2 slab, hi and lo
+         + size_t(kRadBasis) * kRadHidden * sizeof(float)      // W1
+         + size_t(kRadWaves) * 16 * (PL::DY + 1) * sizeof(float)  // harmonics of a tile
+         + size_t(kRadWaves) * 16 * sizeof(int);                // senders of a tile
+}
+
+template <class S>
+__global__ void __launch_bounds__(64 * kRadWaves, 1)
+    k_conv_fwd_radial(int n_nodes, int n_edges, int C, int n_slabs, const int* __restrict__ order,
+                      const int* __restrict__ rowptr, const int* __restrict__ sender,
+                      const float* __restrict__ vec, const float* __restrict__ x,
+                      const float* __restrict__ W1, const float* __restrict__ W2, float rc,
+                      float* __restrict__ m) {
+  using PL = Plan<S>;
+  constexpr int NP = PL::NP, DX = PL::DX, DY = PL::DY, DO = PL::DO, YS = DY + 1;
+  extern __shared__ __align__(16) unsigned char smem[];
+  half8* s_w2 = reinterpret_cast<half8*>(smem);  // [NP][cb 2][ks 2][hi/lo 2][64 lanes]
+  float* s_w1 = reinterpret_cast<float*>(smem + size_t(NP) * 8 * 64 * sizeof(half8));
+  float* s_y = s_w1 + kRadBasis * kRadHidden;     // [wave][16][YS]
+  int* s_snd = reinterpret_cast<int*>(s_y + kRadWaves * 16 * YS);  // [wave][16]
+
+  const int xcd = blockIdx.x % kRadXcds, slot = blockIdx.x / kRadXcds;
+  const int slab = xcd % n_slabs, part = xcd / n_slabs, n_parts = kRadXcds / n_slabs;
+  const int64_t ncols = int64_t(NP) * C;
+  for (int i = threadIdx.x; i < NP * 4 * 64; i += blockDim.x) {
+    const int p = i / 256, cb = (i / 128) % 2, ks = (i / 64) % 2, l = i % 64;
+    const int64_t col = int64_t(p) * C + slab * 32 + cb * 16 + (l & 15);
+    const int k0 = ks * 32 + 8 * (l >> 4);
+    half8 hi, lo;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float v = W2[int64_t(k0 + t) * ncols + col];
+      hi[t] = static_cast<_Float16>(v);
+      lo[t] = static_cast<_Float16>((v - static_cast<float>(hi[t])) * kLoScale);
+    }
+    s_w2[(i / 64) * 128 + l] = hi;
+    s_w2[(i / 64) * 128 + 64 + l] = lo;
+  }
+  for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gq = lane >> 4, li = lane & 15;
+  float* ys = s_y + wave * 16 * YS;
+  int* sn = s_snd + wave * 16;
+  const int chan = slab * 32 + li;  // + 16 * cb
+  const int per_part = (n_nodes + n_parts - 1) / n_parts;
+  const int lo_pos = part * per_part, hi_pos = min(n_nodes, lo_pos + per_part);
+  const int waves_here = (gridDim.x / kRadXcds) * kRadWaves;
+
+  for (int pos = lo_pos + slot * kRadWaves + wave; pos < hi_pos; pos += waves_here) {
+    const int b = order ? order[pos] : pos;
+    float acc[2][DO];
+#pragma unroll
+    for (int o = 0; o < DO; ++o) acc[0][o] = acc[1][o] = 0.0f;
+    const int beg = max(rowptr[b], 0), end = min(rowptr[b + 1], n_edges);
+    for (int e0 = beg; e0 < end; e0 += 16) {
+      // the MFMA row of this lane: edge e0 + li
+      const int er = e0 + li;
+      int sr = -1;
+      float vx = 0.0f, vy = 0.0f, vz = 0.0f;
+      if (er < end) {
+        sr = sender[er];
+        vx = vec[int64_t(er) * 3];
+        vy = vec[int64_t(er) * 3 + 1];
+        vz = vec[int64_t(er) * 3 + 2];
+      }
+      const bool vr = sr >= 0 && sr < n_nodes;
+      wave_lds_fence();  // the previous tile's reads of ys / sn are done
+      if (gq == 0) {
+        sn[li] = vr ? sr : -1;
+        float Y[DY];
+        edge_y_from_vec<S>(vx, vy, vz, Y);
+#pragma unroll
+        for (int i = 0; i < DY; ++i) ys[li * YS + i] = Y[i];
+      }
+      half8 ah[2], al[2];
+      {
+        float B[kRadBasis];
+        bessel_basis(vx, vy, vz, rc, B);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int k = ks * 32 + 8 * gq + t;
+            float pre = 0.0f;
+#pragma unroll
+            for (int n = 0; n < kRadBasis; ++n) pre = fmaf(B[n], s_w1[n * kRadHidden + k], pre);
+            const float h = vr ? silu(pre) : 0.0f;
+            const _Float16 hh = static_cast<_Float16>(h);
+            ah[ks][t] = hh;
+            al[ks][t] = static_cast<_Float16>((h - static_cast<float>(hh)) * kLoScale);
+          }
+      }
+      wave_lds_fence();  // this tile's staging is visible to the wave
+      // x of this lane's contraction rows 4*gq + rr, channels chan + 16*cb
+      float xv[4][DX][2];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int s = sn[4 * gq + rr];
+#pragma unroll
+        for (int i = 0; i < DX; ++i)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            xv[rr][i][cb] = s >= 0 ? x[(int64_t(s) * DX + i) * C + chan + 16 * cb] : 0.0f;
+      }
+      sfor<0, NP>([&](auto pi) {
+        constexpr PathC P = PL::paths.p[pi];
+        const half8* wb = s_w2 + size_t(pi) * 512;
+        // hi*hi in D, the two cross products (low parts scaled by 2^11) in X
+        float4v D[2], X[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          D[cb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+          X[cb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const half8 bh = wb[(cb * 2 + ks) * 128 + lane];
+            const half8 bl = wb[(cb * 2 + ks) * 128 + 64 + lane];
+            D[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bh, D[cb], 0, 0, 0);
+            X[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bl, X[cb], 0, 0, 0);
+            X[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[ks], bh, X[cb], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float wp[2] = {fmaf(X[0][rr], kLoUnscale, D[0][rr]),
+                               fmaf(X[1][rr], kLoUnscale, D[1][rr])};
+          path_forward<S, pi, 2>(ys + (4 * gq + rr) * YS + P.yo, xv[rr], wp, acc);
+        }
+      });
+    }
+    // the four lane groups hold partial sums over different edges of the
+    // same channels: fixed butterfly, then group gq stores components o = gq mod 4
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int o = 0; o < DO; ++o) {
+        float v = acc[cb][o];
+        v += shfl_xor_c<16>(v);
+        v += shfl_xor_c<32>(v);
+        acc[cb][o] = v;
+      }
+    float* mb = m + int64_t(b) * DO * C + chan;
+#pragma unroll
+    for (int o = 0; o < DO; ++o)
+      if ((o & 3) == gq) {
+        __builtin_nontemporal_store(acc[0][o], mb + int64_t(o) * C);
+        __builtin_nontemporal_store(acc[1][o], mb + int64_t(o) * C + 16);
+      }
+  }
+}
+
+template <class S>
+hipError_t launch_fwd_radial(const RadialConvArgs& a, hipStream_t s) {
+  const size_t lds = radial_lds_bytes<S>();
+  static bool attr = false;  // set once per process: the attribute is per function
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_conv_fwd_radial<S>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int n_slabs = a.C / 32;
+  hipLaunchKernelGGL(k_conv_fwd_radial<S>, dim3(kRadXcds * 32), dim3(64 * kRadWaves), lds, s,
+                     a.n_nodes, a.n_edges, a.C, n_slabs, a.order, a.rowptr, a.sender, a.vec, a.x,
+                     a.W1, a.W2, a.cutoff, a.m);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool radial_conv_supported(const char* set_name) {
+  return set_name && std::strcmp(set_name, "L1to3") == 0;
+}
+
+hipError_t launch_conv_fwd_radial(const char* set_name, const RadialConvArgs& a, hipStream_t s) {
+  if (a.n_nodes <= 0) return hipSuccess;
+  if (set_name && std::strcmp(set_name, "L1to3") == 0) return launch_fwd_radial<SigL1to3>(a, s);
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cutoff,
+                             const float* W1, const float* W2, float* w, hipStream_t s) {
+  if (n_edges <= 0 || n_cols <= 0) return hipSuccess;
+  const int n_slabs = (n_cols + kMlpCols - 1) / kMlpCols;
+  const int ntiles = (n_edges + 15) / 16;
+  int n_groups = (2048 + n_slabs - 1) / n_slabs;
+  n_groups = max(1, min(n_groups, (ntiles + 3) / 4));
+  hipLaunchKernelGGL(k_radial_mlp, dim3(n_slabs * n_groups), dim3(256), 0, s, n_edges, n_cols,
+                     n_slabs, n_groups, vec, cutoff, W1, W2, w);
+  return hipGetLastError();
+}
+
+}  // namespace e3k

@@ -94,6 +94,25 @@ hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr,
                                     const float* evec, int* ws, hipStream_t s);
 hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hipStream_t s);
 hipError_t launch_add(void* dst, const void* src, int64_t n, int bf16, hipStream_t s);
+
+// Radial edge weights and the convolution that computes them on the fly
+// (radial.hip): 8 Bessel functions -> 64 SiLU units -> n_cols = P*C.
+struct RadialConvArgs {
+  int n_nodes, n_edges, C;
+  const int* order;  // traversal order of the receivers, or null
+  const int* rowptr;
+  const int* sender;
+  const float* vec;  // edge vectors [E][3]
+  const float* x;    // [N][dx][C] float32
+  const float* W1;   // [8][64]
+  const float* W2;   // [64][P*C]
+  float cutoff;
+  float* m;          // [N][dout][C] float32
+};
+bool radial_conv_supported(const char* set_name);
+hipError_t launch_conv_fwd_radial(const char* set_name, const RadialConvArgs& a, hipStream_t s);
+hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cutoff,
+                             const float* W1, const float* W2, float* w, hipStream_t s);
 hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
                                  float* dvec, hipStream_t s);
 hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr,

@@ -177,6 +177,43 @@ e3_status e3_conv_double_backward(const e3_desc* desc, int32_t n_nodes, int32_t 
                                   void* dw2, void* ddm, void* scratch, size_t scratch_bytes,
                                   e3_dtype dtype, void* stream);
 
+/* Radial edge weights.  The e3j paper (A.3, the edge scalars s_ab of Eq.7;
+ * E.1, message weighting with edge scalars) derives the per-edge weights
+ * from an MLP on a radial basis embedding of |r_ab|, with 8 basis functions
+ * in its model table (Table 3); the rest is this library's reading:
+ *   B_n(d) = sqrt(2/cutoff) sin(n pi d / cutoff) / d   (n = 1..8; limit at d = 0)
+ *   h_k    = silu(sum_n B_n(|r_e|) W1[n][k])           (k < 64; silu(t) = t/(1+e^-t))
+ *   w[e][j] = sum_k h_k W2[k][j]                       (j < n_cols)
+ * No envelope, no biases.  W1 [8][64] and W2 [64][n_cols] are float32
+ * device arrays owned by the caller. */
+typedef struct {
+  float cutoff;     /* > 0 */
+  int32_t n_basis;  /* must be 8 */
+  int32_t hidden;   /* must be 64 */
+  const float* W1;
+  const float* W2;
+} e3_radial;
+
+/* w[E][n_cols] (float32, caller-owned) for the edge vectors edge_vec[E][3];
+ * n_cols a multiple of 16 (P*C for a convolution's w[E][P][C]).  fp32 matrix
+ * cores, fp32 accumulation.  E3_ERR_UNSUPPORTED for other basis or hidden
+ * sizes. */
+e3_status e3_radial_mlp(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
+                        const float* edge_vec, float* w, void* stream);
+
+/* The forward convolution (as e3_conv_forward, edge-vector mode, float32
+ * storage) with w[e][P][C] = the radial MLP of edge e computed on the fly:
+ * w never reaches memory.  The MLP's second layer runs on the fp16 matrix
+ * cores with operands split into high and low fp16 parts (three products),
+ * which keeps w to about 1e-6 of its size; |W2| and |h| must stay below the
+ * fp16 range (65504).  Supported: x = Cx(0e+1o), harmonics 0e+1o+2e+3o,
+ * out = Cx(0e+1o+2e+3o), C in {32, 64, 128, 256}; flags must be 0.  The
+ * workspace (from e3_conv_prepare_transpose) is optional, as for the forward. */
+e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                 const int32_t* rowptr, const int32_t* sender,
+                                 const void* workspace, size_t ws_bytes, const float* edge_vec,
+                                 const float* x, const e3_radial* mlp, float* m, void* stream);
+
 /* Per-node gradient from per-edge vector gradients, for r_e = pos[receiver]
  * - pos[sender]:
  *   node_grad[b] = sum_{e: receiver(e) = b} edge_grad[e]

@@ -194,6 +194,27 @@ def test_error_codes(lib):
     assert lib.e3_conv_double_backward(_desc_c(yg), 0, 0, None, None, None, 0, None, None, None,
                                        None, None, None, None, None, None, None, None, None, 0, 0,
                                        None) == 0
+    # radial weights and the convolution computing them: parameter checks
+    W = C.c_void_p(0x20000)
+    rad = api._CRadial(5.0, 8, 64, W.value, W.value)
+    assert lib.e3_radial_mlp(None, 10, 32, fake, fake, None) == -1
+    assert lib.e3_radial_mlp(C.byref(api._CRadial(5.0, 4, 64, W.value, W.value)), 10, 32, fake,
+                             fake, None) == -3
+    assert lib.e3_radial_mlp(C.byref(api._CRadial(-1.0, 8, 64, W.value, W.value)), 10, 32, fake,
+                             fake, None) == -1
+    assert lib.e3_radial_mlp(C.byref(rad), 10, 24, fake, fake, None) == -3  # n_cols % 16
+    assert lib.e3_radial_mlp(C.byref(rad), 0, 32, None, None, None) == 0
+    assert lib.e3_radial_mlp(C.byref(rad), 10, 32, None, fake, None) == -1
+    sh3 = [(0, 1), (1, -1), (2, 1), (3, -1)]
+    d32 = api.Desc([(0, 1), (1, -1)], sh3, sh3, 32)
+    crad = lambda d, n=4: lib.e3_conv_forward_radial(_desc_c(d), n, 8, fake, fake, None, 0, fake,
+                                                     fake, C.byref(rad), fake, None)
+    assert crad(d32, 0) == 0
+    assert crad(api.Desc([(0, 1), (1, -1)], sh3, sh3, 8)) == -3          # C = 8
+    assert crad(d32.with_flags(api.E3_Y_GIVEN)) == -3
+    assert crad(api.Desc(sh3[:3], sh3, sh3, 32)) == -3                    # no fused kernel
+    assert lib.e3_conv_forward_radial(_desc_c(d32), 4, 8, fake, fake, None, 0, fake, fake, None,
+                                      fake, None) == -1
     out = np.zeros(10)
     assert lib.e3_cg_block(1, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
     assert lib.e3_cg_block(4, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1

@@ -1,0 +1,166 @@
+"""GPU parity of the radial edge weights (e3_radial_mlp) and of the
+convolution that computes them on the fly (e3_conv_forward_radial), through
+the C ABI, against the fp64 oracle (oracle/radial.py).
+
+Tolerance: max|gpu - oracle| / RMS(oracle) <= 1e-5 per output (the fp32
+gate).  The fused kernel forms the MLP's second layer from fp16 high/low
+parts (three products, about 2^-22 relative per product) and the first
+layer, basis and harmonics in fp32.  Inputs: W1 ~ N(0,1)/sqrt(8),
+W2 ~ N(0,1)/sqrt(64) (the water workload's reading of the radial MLP).
+"""
+import numpy as np
+import pytest
+
+from clebsch_gordan_tensor_amd import synth as S
+from oracle import oracle as O
+from oracle import radial as R
+from tests.gpu_util import TOL_F32, assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SH3 = [(0, 1), (1, -1), (2, 1), (3, -1)]
+X01 = [(0, 1), (1, -1)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible to torch")
+    from clebsch_gordan_tensor_amd import api
+    api.lib()
+    return api
+
+
+def _weights(n_cols, seed):
+    rng = np.random.default_rng(seed)
+    W1 = (rng.standard_normal((8, 64)) / np.sqrt(8.0)).astype(np.float32)
+    W2 = (rng.standard_normal((64, n_cols)) / 8.0).astype(np.float32)
+    return W1, W2
+
+
+@pytest.mark.parametrize("E,n_cols", [(3001, 1280), (17, 48), (1, 16)])
+def test_radial_mlp_matches_oracle(gpu, E, n_cols):
+    rng = np.random.default_rng(200 + E)
+    ev = (rng.standard_normal((E, 3)) * 2.0).astype(np.float32)
+    if E > 2:
+        ev[1] = 0.0  # coincident atoms: the basis at its d = 0 limit
+    W1, W2 = _weights(n_cols, 201)
+    w = host(gpu.radial_mlp(dev(ev), 5.0, dev(W1), dev(W2)))
+    assert_close(w, R.radial_mlp(ev, 5.0, W1, W2), TOL_F32, f"radial mlp E={E}")
+
+
+def _graph_c32():
+    # 400 atoms, padding edges in every segment, one hub receiver with every
+    # other atom as a neighbour (several 16-edge tiles), isolated receivers
+    from tests.test_oracle_conv import with_padding
+    g = S.random_graph(400, 16.0, 3.5, seed=210)
+    g = with_padding(g, n_pad_per_node=1, seed=211)
+    snd, rcv, ev = [], [], []
+    hub = 7
+    for b in range(g.n_nodes):
+        lo, hi = g.rowptr[b], g.rowptr[b + 1]
+        if b == hub:
+            others = [a for a in range(g.n_nodes) if a != hub]
+            snd += others
+            rcv += [b] * len(others)
+            ev += list(g.pos[hub] - g.pos[others])
+        elif b in (11, 12):
+            continue  # isolated receivers: m = 0
+        else:
+            snd += list(g.sender[lo:hi])
+            rcv += [b] * (hi - lo)
+            ev += list(g.evec[lo:hi])
+    counts = np.bincount(np.array(rcv), minlength=g.n_nodes)
+    rowptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return S.Graph(pos=g.pos, rowptr=rowptr, sender=np.array(snd, np.int32),
+                   receiver=np.array(rcv, np.int32), evec=np.array(ev, np.float32))
+
+
+def _run(gpu, d, g, x, W1, W2, cutoff, order=True):
+    rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+    ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=ev) if order else None
+    m = gpu.conv_forward_radial(d, rowptr, sender, ev, dev(x), cutoff, dev(W1), dev(W2),
+                                workspace=ws)
+    torch.cuda.synchronize()
+    return host(m)
+
+
+@pytest.mark.parametrize("C", [32, 64, 256])
+def test_radial_conv_padding_hub_isolated(gpu, C):
+    g = _graph_c32()
+    d = gpu.Desc(X01, SH3, SH3, C)
+    od = O.Desc(X01, SH3, SH3, C)
+    x = np.random.default_rng(212).standard_normal((g.n_nodes, 4, C)).astype(np.float32)
+    W1, W2 = _weights(O.num_paths(od) * C, 213)
+    m = _run(gpu, d, g, x, W1, W2, 3.5)
+    ref = R.conv_forward_radial(od, g.rowptr, g.sender, g.evec, x, 3.5, W1, W2)
+    assert_close(m, ref, TOL_F32, f"radial conv C={C}")
+    assert np.all(m[[11, 12]] == 0.0)
+
+
+def test_radial_conv_water3k(gpu):
+    p = S.make_conv("water3k", with_dm=False)
+    g = p.graph
+    d = gpu.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    od = O.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    W1, W2 = _weights(O.num_paths(od) * p.channels, 214)
+    m = _run(gpu, d, g, p.x, W1, W2, 5.0)
+    ref = R.conv_forward_radial(od, g.rowptr, g.sender, g.evec, p.x, 5.0, W1, W2)
+    assert_close(m, ref, TOL_F32, "radial conv water3k")
+    # the same without the locality order: every receiver is computed the same way
+    assert np.array_equal(_run(gpu, d, g, p.x, W1, W2, 5.0, order=False), m)
+
+
+def test_radial_conv_equals_mlp_then_conv(gpu):
+    # two different kernel paths: weights written by e3_radial_mlp and fed to
+    # e3_conv_forward, against the fused kernel
+    p = S.make_conv("water3k", with_dm=False)
+    g = p.graph
+    d = gpu.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    P = gpu.num_paths(d)
+    W1, W2 = _weights(P * p.channels, 215)
+    rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+    w = gpu.radial_mlp(ev, 5.0, dev(W1), dev(W2)).view(-1, P, p.channels)
+    m1 = gpu.conv_forward(d, rowptr, sender, ev, dev(p.x), w)
+    m2 = gpu.conv_forward_radial(d, rowptr, sender, ev, dev(p.x), 5.0, dev(W1), dev(W2))
+    torch.cuda.synchronize()
+    # each side is held to the fp32 gate against the oracle above; against each
+    # other the two roundings add up, so twice the gate
+    assert_close(host(m2), host(m1).astype(np.float64), 2 * TOL_F32, "fused vs composed")
+
+
+def test_radial_conv_full_size_sampled_and_deterministic(gpu):
+    # the 64k-atom graph (3.1M edges) in the launch configuration a benchmark
+    # uses (with the prepared locality order); sampled receivers against the oracle
+    cfg = S.CONV_CONFIGS["mace64k"]
+    n = cfg["n"]
+    g = S.random_graph(n, (n / cfg["density"]) ** (1.0 / 3.0), cfg["cutoff"], 0,
+                       permute_labels=cfg["permute"])
+    C, xi = S.parse_irreps(cfg["x"])
+    _, oi = S.parse_irreps(cfg["out"])
+    yi = S.sh_irreps(cfg["lmax"])
+    xh = S.normal((n, S.dim(xi), C), 0, S.TAG_X)
+    d = gpu.Desc(xi, yi, oi, C)
+    od = O.Desc(xi, yi, oi, C)
+    W1, W2 = _weights(O.num_paths(od) * C, 216)
+    rowptr, sender, ev, x = dev(g.rowptr), dev(g.sender), dev(g.evec), dev(xh)
+    ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=ev)
+    a = gpu.conv_forward_radial(d, rowptr, sender, ev, x, 5.0, dev(W1), dev(W2), workspace=ws)
+    b = gpu.conv_forward_radial(d, rowptr, sender, ev, x, 5.0, dev(W1), dev(W2), workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    rows = np.sort(np.random.default_rng(3).choice(g.n_nodes, 150, replace=False))
+    ref = R.conv_forward_radial(od, g.rowptr, g.sender, g.evec, xh, 5.0, W1, W2, rows=rows)
+    assert_close(host(a)[rows], ref, TOL_F32, "radial conv 64k sampled")
+
+
+def test_radial_conv_unsupported(gpu):
+    d = gpu.Desc(SH3, SH3, SH3, 64)
+    W1, W2 = _weights(23 * 64, 1)
+    z = lambda *s: torch.zeros(s, device="cuda")
+    with pytest.raises(gpu.E3Error):
+        gpu.conv_forward_radial(d, torch.zeros(5, dtype=torch.int32, device="cuda"),
+                                torch.zeros(0, dtype=torch.int32, device="cuda"), z(0, 3),
+                                z(4, 16, 64), 5.0, dev(W1), dev(W2))
