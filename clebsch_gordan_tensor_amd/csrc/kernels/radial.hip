@@ -76,6 +76,8 @@ __device__ __forceinline__ void bessel_basis(float vx, float vy, float vz, float
   }
 }
 
+// correctly rounded: a 1-ulp reciprocal here already moves the convolution's
+// outputs by 1e-5 of their RMS on heavy-tailed graphs
 __device__ __forceinline__ float silu(float t) { return t / (1.0f + expf(-t)); }
 
 // ------------------------------------------------------------ radial MLP
@@ -201,13 +203,16 @@ __device__ __forceinline__ void path_forward(const float* __restrict__ Yl,
   }
 }
 
+constexpr int kRadChunk = 64;  // edges staged per wavefront at a time (four 16-edge tiles)
+
 template <class S>
 constexpr size_t radial_lds_bytes() {
   using PL = Plan<S>;
-  return size_t(PL::NP) * 8 * 64 * sizeof(half8)              // W2 slab, hi and lo
-         + size_t(kRadBasis) * kRadHidden * sizeof(float)      // W1
-         + size_t(kRadWaves) * 16 * (PL::DY + 1) * sizeof(float)  // harmonics of a tile
-         + size_t(kRadWaves) * 16 * sizeof(int);                // senders of a tile
+  return size_t(PL::NP) * 8 * 64 * sizeof(half8)                           // W2 slab, hi and lo
+         + size_t(kRadBasis) * kRadHidden * sizeof(float)                   // W1
+         + size_t(kRadWaves) * kRadChunk * kRadBasis * sizeof(float)        // basis of a chunk
+         + size_t(kRadWaves) * kRadChunk * (PL::DY + 1) * sizeof(float)     // harmonics
+         + size_t(kRadWaves) * kRadChunk * sizeof(int);                     // senders
 }
 
 template <class S>
@@ -222,8 +227,9 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
   extern __shared__ __align__(16) unsigned char smem[];
   half8* s_w2 = reinterpret_cast<half8*>(smem);  // [NP][cb 2][ks 2][hi/lo 2][64 lanes]
   float* s_w1 = reinterpret_cast<float*>(smem + size_t(NP) * 8 * 64 * sizeof(half8));
-  float* s_y = s_w1 + kRadBasis * kRadHidden;     // [wave][16][YS]
-  int* s_snd = reinterpret_cast<int*>(s_y + kRadWaves * 16 * YS);  // [wave][16]
+  float* s_b = s_w1 + kRadBasis * kRadHidden;                  // [wave][64][8]
+  float* s_y = s_b + kRadWaves * kRadChunk * kRadBasis;        // [wave][64][YS]
+  int* s_snd = reinterpret_cast<int*>(s_y + kRadWaves * kRadChunk * YS);  // [wave][64]
 
   const int xcd = blockIdx.x % kRadXcds, slot = blockIdx.x / kRadXcds;
   const int slab = xcd % n_slabs, part = xcd / n_slabs, n_parts = kRadXcds / n_slabs;
@@ -247,8 +253,9 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int gq = lane >> 4, li = lane & 15;
-  float* ys = s_y + wave * 16 * YS;
-  int* sn = s_snd + wave * 16;
+  float* bs = s_b + wave * kRadChunk * kRadBasis;
+  float* ys = s_y + wave * kRadChunk * YS;
+  int* sn = s_snd + wave * kRadChunk;
   const int chan = slab * 32 + li;  // + 16 * cb
   const int per_part = (n_nodes + n_parts - 1) / n_parts;
   const int lo_pos = part * per_part, hi_pos = min(n_nodes, lo_pos + per_part);
@@ -260,81 +267,108 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
 #pragma unroll
     for (int o = 0; o < DO; ++o) acc[0][o] = acc[1][o] = 0.0f;
     const int beg = max(rowptr[b], 0), end = min(rowptr[b + 1], n_edges);
-    for (int e0 = beg; e0 < end; e0 += 16) {
-      // the MFMA row of this lane: edge e0 + li
-      const int er = e0 + li;
-      int sr = -1;
-      float vx = 0.0f, vy = 0.0f, vz = 0.0f;
-      if (er < end) {
-        sr = sender[er];
-        vx = vec[int64_t(er) * 3];
-        vy = vec[int64_t(er) * 3 + 1];
-        vz = vec[int64_t(er) * 3 + 2];
-      }
-      const bool vr = sr >= 0 && sr < n_nodes;
-      wave_lds_fence();  // the previous tile's reads of ys / sn are done
-      if (gq == 0) {
-        sn[li] = vr ? sr : -1;
-        float Y[DY];
-        edge_y_from_vec<S>(vx, vy, vz, Y);
-#pragma unroll
-        for (int i = 0; i < DY; ++i) ys[li * YS + i] = Y[i];
-      }
-      half8 ah[2], al[2];
+    for (int c0 = beg; c0 < end; c0 += kRadChunk) {
+      // stage one edge per lane: sender, radial basis and harmonics
+      wave_lds_fence();  // the previous chunk's reads are done
       {
+        const int e = c0 + lane;
+        int sr = -1;
+        float vx = 0.0f, vy = 0.0f, vz = 0.0f;
+        if (e < end) {
+          sr = sender[e];
+          vx = vec[int64_t(e) * 3];
+          vy = vec[int64_t(e) * 3 + 1];
+          vz = vec[int64_t(e) * 3 + 2];
+        }
+        sn[lane] = (sr >= 0 && sr < n_nodes) ? sr : -1;
         float B[kRadBasis];
         bessel_basis(vx, vy, vz, rc, B);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int n = 0; n < kRadBasis; ++n) bs[lane * kRadBasis + n] = B[n];
+        float Y[DY];
+        edge_y_from_vec<S>(vx, vy, vz, Y);
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int k = ks * 32 + 8 * gq + t;
-            float pre = 0.0f;
-#pragma unroll
-            for (int n = 0; n < kRadBasis; ++n) pre = fmaf(B[n], s_w1[n * kRadHidden + k], pre);
-            const float h = vr ? silu(pre) : 0.0f;
-            const _Float16 hh = static_cast<_Float16>(h);
-            ah[ks][t] = hh;
-            al[ks][t] = static_cast<_Float16>((h - static_cast<float>(hh)) * kLoScale);
-          }
+        for (int i = 0; i < DY; ++i) ys[lane * YS + i] = Y[i];
       }
-      wave_lds_fence();  // this tile's staging is visible to the wave
-      // x of this lane's contraction rows 4*gq + rr, channels chan + 16*cb
-      float xv[4][DX][2];
+      wave_lds_fence();
+      const int nt = (min(kRadChunk, end - c0) + 15) / 16;
+      for (int t = 0; t < nt; ++t) {
+        // keeps the tile's LDS reads (W1 above all) inside the loop instead of
+        // hoisted into registers for the whole chunk
+        wave_lds_fence();
+        // A operand: h of edge row t*16 + li, units ks*32 + 8*gq + (0..7)
+        half8 ah[2], al[2];
+        {
+          const int row = t * 16 + li;
+          const bool vr = sn[row] >= 0;
+          float B[kRadBasis];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int s = sn[4 * gq + rr];
-#pragma unroll
-        for (int i = 0; i < DX; ++i)
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
-            xv[rr][i][cb] = s >= 0 ? x[(int64_t(s) * DX + i) * C + chan + 16 * cb] : 0.0f;
-      }
-      sfor<0, NP>([&](auto pi) {
-        constexpr PathC P = PL::paths.p[pi];
-        const half8* wb = s_w2 + size_t(pi) * 512;
-        // hi*hi in D, the two cross products (low parts scaled by 2^11) in X
-        float4v D[2], X[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          D[cb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-          X[cb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int n = 0; n < kRadBasis; ++n) B[n] = bs[row * kRadBasis + n];
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const half8 bh = wb[(cb * 2 + ks) * 128 + lane];
-            const half8 bl = wb[(cb * 2 + ks) * 128 + 64 + lane];
-            D[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bh, D[cb], 0, 0, 0);
-            X[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bl, X[cb], 0, 0, 0);
-            X[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[ks], bh, X[cb], 0, 0, 0);
+            float pre[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) pre[q] = 0.0f;
+#pragma unroll
+            for (int n = 0; n < kRadBasis; ++n) {
+              const float4* w1 =
+                  reinterpret_cast<const float4*>(s_w1 + n * kRadHidden + ks * 32 + 8 * gq);
+              const float4 u = w1[0], v = w1[1];
+              pre[0] = fmaf(B[n], u.x, pre[0]);
+              pre[1] = fmaf(B[n], u.y, pre[1]);
+              pre[2] = fmaf(B[n], u.z, pre[2]);
+              pre[3] = fmaf(B[n], u.w, pre[3]);
+              pre[4] = fmaf(B[n], v.x, pre[4]);
+              pre[5] = fmaf(B[n], v.y, pre[5]);
+              pre[6] = fmaf(B[n], v.z, pre[6]);
+              pre[7] = fmaf(B[n], v.w, pre[7]);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const float h = vr ? silu(pre[q]) : 0.0f;
+              const _Float16 hh = static_cast<_Float16>(h);
+              ah[ks][q] = hh;
+              al[ks][q] = static_cast<_Float16>((h - static_cast<float>(hh)) * kLoScale);
+            }
           }
         }
+        // x of this lane's contraction rows t*16 + 4*gq + rr, channels chan + 16*cb
+        float xv[4][DX][2];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float wp[2] = {fmaf(X[0][rr], kLoUnscale, D[0][rr]),
-                               fmaf(X[1][rr], kLoUnscale, D[1][rr])};
-          path_forward<S, pi, 2>(ys + (4 * gq + rr) * YS + P.yo, xv[rr], wp, acc);
+          const int sidx = sn[t * 16 + 4 * gq + rr];
+#pragma unroll
+          for (int i = 0; i < DX; ++i)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+              xv[rr][i][cb] = sidx >= 0 ? x[(int64_t(sidx) * DX + i) * C + chan + 16 * cb] : 0.0f;
         }
-      });
+        // hi*hi in D, the two cross products (low parts scaled by 2^11) in X
+        sfor<0, NP>([&](auto pi) {
+          constexpr PathC P = PL::paths.p[pi];
+          const half8* wb = s_w2 + size_t(pi) * 512;
+          float4v D[2], X[2];
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            D[cb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+            X[cb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              const half8 bh = wb[(cb * 2 + ks) * 128 + lane];
+              const half8 bl = wb[(cb * 2 + ks) * 128 + 64 + lane];
+              D[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bh, D[cb], 0, 0, 0);
+              X[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bl, X[cb], 0, 0, 0);
+              X[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[ks], bh, X[cb], 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float wp[2] = {fmaf(X[0][rr], kLoUnscale, D[0][rr]),
+                                 fmaf(X[1][rr], kLoUnscale, D[1][rr])};
+            path_forward<S, pi, 2>(ys + (t * 16 + 4 * gq + rr) * YS + P.yo, xv[rr], wp, acc);
+          }
+        });
+      }
     }
     // the four lane groups hold partial sums over different edges of the
     // same channels: fixed butterfly, then group gq stores components o = gq mod 4
