@@ -667,6 +667,7 @@ e3_status e3_radial_mlp(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
   if (n_cols % 16) return fail(E3_ERR_UNSUPPORTED, "n_cols must be a multiple of 16");
   if (n_edges == 0) return ok();
   if (!edge_vec || !w) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(w)) return fail(E3_ERR_ALIGNMENT, "w must be 16-byte aligned");
   return hip_status(e3k::launch_radial_mlp(n_edges, n_cols, edge_vec, mlp->cutoff, mlp->W1,
                                            mlp->W2, w, hipStream_t(stream)),
                     "radial_mlp");

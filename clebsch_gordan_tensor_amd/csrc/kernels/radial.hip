@@ -9,8 +9,8 @@
 //   h_k    = silu(sum_n B_n W1[n][k]),          k < 64
 //   w[j]   = sum_k h_k W2[k][j],                j < P*C  (layout w[e][P][C])
 //
-// k_radial_mlp writes w with fp32 MFMA (v_mfma_f32_16x16x4f32): exact fp32
-// products, fp32 accumulation.
+// k_radial_mlp writes w with the same fp16 high/low product as the fused
+// convolution below.
 //
 // k_conv_fwd_radial fuses it into the forward convolution.  One 512-thread
 // workgroup per CU holds, for a 32-channel slab, W2 split into fp16 high and
@@ -84,30 +84,90 @@ __device__ __forceinline__ float silu(float t) { return t / (1.0f + expf(-t)); }
 
 constexpr int kMlpCols = 128;  // columns per workgroup slab (8 MFMA blocks)
 
+// The A operand of one 16-edge tile: h of edge row lane%16 for hidden units
+// 32*ks + 8*(lane/16) + (0..7), split into fp16 high and scaled low parts.
+__device__ __forceinline__ void hidden_operands(const float (&B)[kRadBasis], bool valid,
+                                                const float* __restrict__ s_w1, int gq,
+                                                half8 (&ah)[2], half8 (&al)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    float pre[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) pre[q] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < kRadBasis; ++n) {
+      const float4* w1 = reinterpret_cast<const float4*>(s_w1 + n * kRadHidden + ks * 32 + 8 * gq);
+      const float4 u = w1[0], v = w1[1];
+      pre[0] = fmaf(B[n], u.x, pre[0]);
+      pre[1] = fmaf(B[n], u.y, pre[1]);
+      pre[2] = fmaf(B[n], u.z, pre[2]);
+      pre[3] = fmaf(B[n], u.w, pre[3]);
+      pre[4] = fmaf(B[n], v.x, pre[4]);
+      pre[5] = fmaf(B[n], v.y, pre[5]);
+      pre[6] = fmaf(B[n], v.z, pre[6]);
+      pre[7] = fmaf(B[n], v.w, pre[7]);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float h = valid ? silu(pre[q]) : 0.0f;
+      const _Float16 hh = static_cast<_Float16>(h);
+      ah[ks][q] = hh;
+      al[ks][q] = static_cast<_Float16>((h - static_cast<float>(hh)) * kLoScale);
+    }
+  }
+}
+
 // w[e][j] for all edges; workgroup = (column slab, edge-tile group), 4 waves,
-// one 16-edge tile per wave at a time.  W2's slab sits in LDS in the B
-// operand order of v_mfma_f32_16x16x4f32 (k = 4*ks + lane/16, column lane%16).
+// one 16-edge tile per wave at a time.  The product h W2 runs on the fp16
+// matrix cores with the same high/low split as the fused convolution below
+// (hi*hi + hi*lo + lo*hi, low parts scaled by 2^11): 6 v_mfma_f32_16x16x32_f16
+// per 16 columns instead of 16 fp32 MFMAs at twice the cycles each.  W2's
+// slab sits in LDS in the B operand order (k = 32*ks + 8*(lane/16) + t,
+// column lane%16); the 16 x 128 result tile goes through LDS (rows padded by
+// 4 floats against bank conflicts) so that every store instruction writes two
+// 512-byte row segments, 16 bytes per lane.
+constexpr int kMlpTileStride = kMlpCols + 4;
+
+constexpr size_t mlp_lds_bytes() {
+  return size_t(kMlpCols / 16) * 2 * 2 * 64 * sizeof(half8)  // W2 slab, [cb][ks][hi/lo][lane]
+         + size_t(kRadBasis) * kRadHidden * sizeof(float)     // W1
+         + size_t(4) * 16 * kMlpTileStride * sizeof(float);   // result tiles
+}
+
 __global__ void __launch_bounds__(256)
     k_radial_mlp(int n_edges, int n_cols, int n_slabs, int n_groups, const float* __restrict__ vec,
                  float rc, const float* __restrict__ W1, const float* __restrict__ W2,
                  float* __restrict__ w) {
-  __shared__ float s_w2[kMlpCols / 16][kRadHidden / 4][64];
-  __shared__ float s_w1[kRadBasis * kRadHidden];
+  extern __shared__ __align__(16) unsigned char mlp_smem[];
+  half8* s_w2 = reinterpret_cast<half8*>(mlp_smem);
+  float* s_w1 = reinterpret_cast<float*>(mlp_smem + size_t(kMlpCols / 16) * 4 * 64 * sizeof(half8));
+  float* s_t = s_w1 + kRadBasis * kRadHidden;  // [wave][16][stride]
   const int slab = blockIdx.x % n_slabs, group = blockIdx.x / n_slabs;
-  for (int i = threadIdx.x; i < (kMlpCols / 16) * (kRadHidden / 4) * 64; i += blockDim.x) {
-    const int cb = i / ((kRadHidden / 4) * 64), ks = (i / 64) % (kRadHidden / 4), l = i % 64;
-    const int k = 4 * ks + l / 16, col = slab * kMlpCols + cb * 16 + l % 16;
-    s_w2[cb][ks][l] = col < n_cols ? W2[int64_t(k) * n_cols + col] : 0.0f;
+  for (int i = threadIdx.x; i < (kMlpCols / 16) * 2 * 64; i += blockDim.x) {
+    const int cb = i / 128, ks = (i / 64) % 2, l = i % 64;
+    const int col = slab * kMlpCols + cb * 16 + (l & 15);
+    const int k0 = ks * 32 + 8 * (l >> 4);
+    half8 hi, lo;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float v = col < n_cols ? W2[int64_t(k0 + t) * n_cols + col] : 0.0f;
+      hi[t] = static_cast<_Float16>(v);
+      lo[t] = static_cast<_Float16>((v - static_cast<float>(hi[t])) * kLoScale);
+    }
+    s_w2[(cb * 2 + ks) * 128 + l] = hi;
+    s_w2[(cb * 2 + ks) * 128 + 64 + l] = lo;
   }
   for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, gq = lane >> 4;
+  float* tile_lds = s_t + wave * 16 * kMlpTileStride;
   const int ntiles = (n_edges + 15) / 16;
-  const int ncb = min(kMlpCols, n_cols - slab * kMlpCols) / 16;
+  const int width = min(kMlpCols, n_cols - slab * kMlpCols);  // multiple of 16
+  const int ncb = width / 16;
   for (int tile = group * 4 + wave; tile < ntiles; tile += n_groups * 4) {
     const int er = tile * 16 + (lane & 15);
-    float a[kRadHidden / 4];
+    half8 ah[2], al[2];
     {
       float vx = 0.0f, vy = 0.0f, vz = 0.0f;
       if (er < n_edges) {
@@ -118,25 +178,38 @@ __global__ void __launch_bounds__(256)
       }
       float B[kRadBasis];
       bessel_basis(vx, vy, vz, rc, B);
-#pragma unroll
-      for (int ks = 0; ks < kRadHidden / 4; ++ks) {
-        const int k = 4 * ks + (lane >> 4);
-        float pre = 0.0f;
-#pragma unroll
-        for (int n = 0; n < kRadBasis; ++n) pre = fmaf(B[n], s_w1[n * kRadHidden + k], pre);
-        a[ks] = er < n_edges ? silu(pre) : 0.0f;
-      }
+      wave_lds_fence();  // the previous tile's LDS reads are done; keeps W1 reads here
+      hidden_operands(B, er < n_edges, s_w1, gq, ah, al);
     }
     for (int cb = 0; cb < ncb; ++cb) {
-      float4v D = {0.0f, 0.0f, 0.0f, 0.0f};
+      float4v D = {0.0f, 0.0f, 0.0f, 0.0f}, X = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ks = 0; ks < kRadHidden / 4; ++ks)
-        D = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks], s_w2[cb][ks][lane], D, 0, 0, 0);
-      const int col = slab * kMlpCols + cb * 16 + (lane & 15);
+      for (int ks = 0; ks < 2; ++ks) {
+        const half8 bh = s_w2[(cb * 2 + ks) * 128 + lane];
+        const half8 bl = s_w2[(cb * 2 + ks) * 128 + 64 + lane];
+        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bh, D, 0, 0, 0);
+        X = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bl, X, 0, 0, 0);
+        X = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[ks], bh, X, 0, 0, 0);
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = tile * 16 + 4 * (lane >> 4) + r;
-        if (e < n_edges) __builtin_nontemporal_store(D[r], w + int64_t(e) * n_cols + col);
+      for (int r = 0; r < 4; ++r)
+        tile_lds[(4 * gq + r) * kMlpTileStride + cb * 16 + (lane & 15)] =
+            fmaf(X[r], kLoUnscale, D[r]);
+    }
+    wave_lds_fence();
+    // two rows per instruction: lanes 0..31 row 2i, lanes 32..63 row 2i+1
+    const int q = lane & 31, half = lane >> 5;
+    if (4 * q < width) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 2 * i + half;
+        const int e = tile * 16 + row;
+        if (e < n_edges) {
+          const float4v v =
+              *reinterpret_cast<const float4v*>(tile_lds + row * kMlpTileStride + 4 * q);
+          __builtin_nontemporal_store(
+              v, reinterpret_cast<float4v*>(w + int64_t(e) * n_cols + slab * kMlpCols) + q);
+        }
       }
     }
   }
@@ -300,37 +373,10 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
         half8 ah[2], al[2];
         {
           const int row = t * 16 + li;
-          const bool vr = sn[row] >= 0;
           float B[kRadBasis];
 #pragma unroll
           for (int n = 0; n < kRadBasis; ++n) B[n] = bs[row * kRadBasis + n];
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            float pre[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) pre[q] = 0.0f;
-#pragma unroll
-            for (int n = 0; n < kRadBasis; ++n) {
-              const float4* w1 =
-                  reinterpret_cast<const float4*>(s_w1 + n * kRadHidden + ks * 32 + 8 * gq);
-              const float4 u = w1[0], v = w1[1];
-              pre[0] = fmaf(B[n], u.x, pre[0]);
-              pre[1] = fmaf(B[n], u.y, pre[1]);
-              pre[2] = fmaf(B[n], u.z, pre[2]);
-              pre[3] = fmaf(B[n], u.w, pre[3]);
-              pre[4] = fmaf(B[n], v.x, pre[4]);
-              pre[5] = fmaf(B[n], v.y, pre[5]);
-              pre[6] = fmaf(B[n], v.z, pre[6]);
-              pre[7] = fmaf(B[n], v.w, pre[7]);
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const float h = vr ? silu(pre[q]) : 0.0f;
-              const _Float16 hh = static_cast<_Float16>(h);
-              ah[ks][q] = hh;
-              al[ks][q] = static_cast<_Float16>((h - static_cast<float>(hh)) * kLoScale);
-            }
-          }
+          hidden_operands(B, sn[row] >= 0, s_w1, gq, ah, al);
         }
         // x of this lane's contraction rows t*16 + 4*gq + rr, channels chan + 16*cb
         float xv[4][DX][2];
@@ -427,8 +473,16 @@ hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cu
   const int ntiles = (n_edges + 15) / 16;
   int n_groups = (2048 + n_slabs - 1) / n_slabs;
   n_groups = max(1, min(n_groups, (ntiles + 3) / 4));
-  hipLaunchKernelGGL(k_radial_mlp, dim3(n_slabs * n_groups), dim3(256), 0, s, n_edges, n_cols,
-                     n_slabs, n_groups, vec, cutoff, W1, W2, w);
+  static bool attr = false;  // the attribute is per function: set once
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_radial_mlp),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       int(mlp_lds_bytes()));
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(k_radial_mlp, dim3(n_slabs * n_groups), dim3(256), mlp_lds_bytes(), s,
+                     n_edges, n_cols, n_slabs, n_groups, vec, cutoff, W1, W2, w);
   return hipGetLastError();
 }
 

@@ -195,8 +195,11 @@ typedef struct {
 } e3_radial;
 
 /* w[E][n_cols] (float32, caller-owned) for the edge vectors edge_vec[E][3];
- * n_cols a multiple of 16 (P*C for a convolution's w[E][P][C]).  fp32 matrix
- * cores, fp32 accumulation.  E3_ERR_UNSUPPORTED for other basis or hidden
+ * n_cols a multiple of 16 (P*C for a convolution's w[E][P][C]), w 16-byte
+ * aligned.  The second layer runs on the fp16 matrix cores with operands
+ * split into high and low fp16 parts (three products, fp32 accumulation),
+ * which keeps w to a few 1e-7 of its size; |W2| and |h| must stay below the
+ * fp16 range (65504).  The radial basis is evaluated in fp64.  E3_ERR_UNSUPPORTED for other basis or hidden
  * sizes. */
 e3_status e3_radial_mlp(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
                         const float* edge_vec, float* w, void* stream);
