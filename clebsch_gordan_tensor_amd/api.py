@@ -47,7 +47,7 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_linear_num_weights", "e3_linear", "e3_linear_workspace_size",
            "e3_linear_backward", "e3_conv_double_backward_scratch_size",
            "e3_conv_double_backward", "e3_radial_mlp", "e3_conv_forward_radial",
-           "e3_last_error"]
+           "e3_radial_mlp_backward_workspace_size", "e3_radial_mlp_backward", "e3_last_error"]
 
 
 class _CRadial(C.Structure):
@@ -82,6 +82,10 @@ def lib():
     L.e3_radial_mlp.argtypes = [C.POINTER(_CRadial), i32, i32, vp, vp, vp]
     L.e3_conv_forward_radial.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp,
                                          C.POINTER(_CRadial), vp, vp]
+    L.e3_radial_mlp_backward_workspace_size.argtypes = [C.POINTER(_CRadial), i32, i32,
+                                                        C.POINTER(sz)]
+    L.e3_radial_mlp_backward.argtypes = [C.POINTER(_CRadial), i32, i32, vp, vp, vp, vp, vp, vp,
+                                         sz, vp]
     L.e3_conv_double_backward_scratch_size.argtypes = [dp, i32, i32, C.c_int, C.POINTER(sz)]
     L.e3_conv_double_backward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp,
                                           vp, vp, vp, vp, vp, vp, sz, C.c_int, vp]
@@ -516,3 +520,23 @@ def conv_forward_radial(desc: Desc, rowptr, sender, edge_vec, x, cutoff, W1, W2,
                                         _ptr(workspace), wsb, _ptr(edge_vec), _ptr(x), C.byref(r),
                                         _ptr(out), _stream(stream)))
     return out
+
+
+def radial_mlp_backward(edge_vec, cutoff, W1, W2, dw, workspace=None, stream=None):
+    """(dW1, dW2, dvec) for the cotangent dw [E][n_cols] of radial_mlp; dvec is
+    the edge-vector gradient through |r| only."""
+    import torch
+    E, n_cols = dw.shape
+    _need(edge_vec, "edge_vec", shape=(E, 3), dtype=torch.float32)
+    _need(dw, "dw", shape=(E, n_cols), dtype=torch.float32)
+    r = _radial(cutoff, W1, W2)
+    nb = C.c_size_t()
+    _check(lib().e3_radial_mlp_backward_workspace_size(C.byref(r), E, n_cols, C.byref(nb)))
+    if workspace is None:
+        workspace = torch.empty(nb.value, device=dw.device, dtype=torch.uint8)
+    dW1, dW2 = torch.empty_like(W1), torch.empty_like(W2)
+    dvec = torch.empty_like(edge_vec)
+    _check(lib().e3_radial_mlp_backward(
+        C.byref(r), E, n_cols, _ptr(edge_vec), _ptr(dw), _ptr(dW1), _ptr(dW2), _ptr(dvec),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dW1, dW2, dvec

@@ -26,6 +26,7 @@
 // share of the receivers in the locality order of the prepare step.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 
 #include "common.h"
@@ -454,7 +455,187 @@ hipError_t launch_fwd_radial(const RadialConvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------ radial MLP backward
+
+// h[e][k] = silu(B(|r_e|) W1)[k], one thread per edge (the input of the
+// second layer's weight gradient and of dh = dw W2^T).
+__global__ void __launch_bounds__(256)
+    k_radial_hidden(int n_edges, const float* __restrict__ vec, float rc,
+                    const float* __restrict__ W1, float* __restrict__ h) {
+  __shared__ float s_w1[kRadBasis * kRadHidden];
+  for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
+  __syncthreads();
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n_edges) return;
+  float B[kRadBasis];
+  bessel_basis(vec[int64_t(e) * 3], vec[int64_t(e) * 3 + 1], vec[int64_t(e) * 3 + 2], rc, B);
+  float4v* out = reinterpret_cast<float4v*>(h + int64_t(e) * kRadHidden);
+#pragma unroll
+  for (int q = 0; q < kRadHidden / 4; ++q) {
+    float4v v;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float pre = 0.0f;
+#pragma unroll
+      for (int n = 0; n < kRadBasis; ++n) pre = fmaf(B[n], s_w1[n * kRadHidden + 4 * q + t], pre);
+      v[t] = silu(pre);
+    }
+    out[q] = v;
+  }
+}
+
+// dst[j][k][c] = src[k][j*cb + c] (to_blocks) or the inverse, for a
+// [rows][nb*cb] matrix and its nb column blocks of width cb.
+__global__ void __launch_bounds__(256)
+    k_column_blocks(int rows, int nb, int cb, int to_blocks, const float* __restrict__ src,
+                    float* __restrict__ dst) {
+  const int64_t n = int64_t(rows) * nb * cb;
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const int c = int(i % cb);
+    const int k = int((i / cb) % rows);
+    const int j = int(i / (int64_t(cb) * rows));
+    const int64_t flat = int64_t(k) * nb * cb + int64_t(j) * cb + c;  // [k][j*cb + c]
+    if (to_blocks)
+      dst[i] = src[flat];
+    else
+      dst[flat] = src[i];
+  }
+}
+
+constexpr int kTailBatch = 64;
+
+// Per edge, from dh = dw W2^T: dpre = dh * silu'(pre), the radial part of
+// the edge-vector gradient dvec = (sum_n B'_n(d) (dpre W1^T)_n) r / d, and
+// this chunk's partial dW1[n][k] = sum_e B_n(e) dpre_k(e) (fixed order).
+// One workgroup per chunk of edges, 64 edges per batch.
+__global__ void __launch_bounds__(256)
+    k_radial_tail(int n_edges, int n_chunks, const float* __restrict__ vec, float rc,
+                  const float* __restrict__ W1, const float* __restrict__ dh,
+                  float* __restrict__ dvec, float* __restrict__ dW1_part) {
+  __shared__ float s_w1[kRadBasis * kRadHidden];
+  __shared__ float s_b[kTailBatch][kRadBasis];
+  __shared__ float s_dp[kTailBatch][kRadHidden + 1];
+  for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
+  __syncthreads();
+  const int per = (n_edges + n_chunks - 1) / n_chunks;
+  const int lo = blockIdx.x * per, hi = min(n_edges, lo + per);
+  float acc0 = 0.0f, acc1 = 0.0f;  // pairs threadIdx.x and threadIdx.x + 256 of [8][64]
+  const int p0 = threadIdx.x, p1 = threadIdx.x + 256;
+  for (int e0 = lo; e0 < hi; e0 += kTailBatch) {
+    const int ne = min(kTailBatch, hi - e0);
+    if (threadIdx.x < kTailBatch) {
+      const int t = threadIdx.x;
+      if (t < ne) {
+        const int64_t e = e0 + t;
+        const float vx = vec[e * 3], vy = vec[e * 3 + 1], vz = vec[e * 3 + 2];
+        const double d = sqrt(double(vx) * vx + double(vy) * vy + double(vz) * vz);
+        const double pref = sqrt(2.0 / double(rc));
+        float B[kRadBasis], Bd[kRadBasis];
+        if (d > 0.0) {
+          double sn, cs;
+          const double th = 3.141592653589793 * d / double(rc);
+          sincos(th, &sn, &cs);
+          // sin(n th), cos(n th) by the angle-addition recurrence
+          double s_n = sn, c_n = cs;
+#pragma unroll
+          for (int n = 0; n < kRadBasis; ++n) {
+            const double kn = double(n + 1) * 3.141592653589793 / double(rc);
+            B[n] = float(pref * s_n / d);
+            Bd[n] = float(pref * (kn * c_n / d - s_n / (d * d)));
+            const double s_next = s_n * cs + c_n * sn, c_next = c_n * cs - s_n * sn;
+            s_n = s_next;
+            c_n = c_next;
+          }
+        } else {
+#pragma unroll
+          for (int n = 0; n < kRadBasis; ++n) {
+            B[n] = float(pref * double(n + 1) * 3.141592653589793 / double(rc));
+            Bd[n] = 0.0f;
+          }
+        }
+        float g[kRadBasis];
+#pragma unroll
+        for (int n = 0; n < kRadBasis; ++n) g[n] = 0.0f;
+        const float* dhe = dh + e * kRadHidden;
+        for (int k = 0; k < kRadHidden; ++k) {
+          float pre = 0.0f;
+#pragma unroll
+          for (int n = 0; n < kRadBasis; ++n) pre = fmaf(B[n], s_w1[n * kRadHidden + k], pre);
+          const float sg = 1.0f / (1.0f + expf(-pre));
+          const float dp = dhe[k] * sg * (1.0f + pre * (1.0f - sg));
+          s_dp[t][k] = dp;
+#pragma unroll
+          for (int n = 0; n < kRadBasis; ++n) g[n] = fmaf(dp, s_w1[n * kRadHidden + k], g[n]);
+        }
+        float dd = 0.0f;
+#pragma unroll
+        for (int n = 0; n < kRadBasis; ++n) {
+          dd = fmaf(Bd[n], g[n], dd);
+          s_b[t][n] = B[n];
+        }
+        const float inv = d > 0.0 ? float(1.0 / d) : 0.0f;
+        dvec[e * 3] = dd * vx * inv;
+        dvec[e * 3 + 1] = dd * vy * inv;
+        dvec[e * 3 + 2] = dd * vz * inv;
+      }
+    }
+    __syncthreads();
+    {
+      const int n0 = p0 / kRadHidden, k0 = p0 % kRadHidden;
+      const int n1 = p1 / kRadHidden, k1 = p1 % kRadHidden;
+      for (int t = 0; t < ne; ++t) {
+        acc0 = fmaf(s_b[t][n0], s_dp[t][k0], acc0);
+        acc1 = fmaf(s_b[t][n1], s_dp[t][k1], acc1);
+      }
+    }
+    __syncthreads();
+  }
+  dW1_part[int64_t(blockIdx.x) * 512 + p0] = acc0;
+  dW1_part[int64_t(blockIdx.x) * 512 + p1] = acc1;
+}
+
+// out[i] = sum_c part[c][i] over n_chunks partials, in chunk order.
+__global__ void __launch_bounds__(256)
+    k_sum_partials(int n_chunks, int n, const float* __restrict__ part, float* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int c = 0; c < n_chunks; ++c) s += part[int64_t(c) * n + i];
+  out[i] = s;
+}
+
 }  // namespace
+
+hipError_t launch_radial_hidden(int n_edges, const float* vec, float cutoff, const float* W1,
+                                float* h, hipStream_t s) {
+  if (n_edges <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_radial_hidden, dim3((n_edges + 255) / 256), dim3(256), 0, s, n_edges, vec,
+                     cutoff, W1, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_column_blocks(int rows, int nb, int cb, int to_blocks, const float* src,
+                                float* dst, hipStream_t s) {
+  const int64_t n = int64_t(rows) * nb * cb;
+  if (n <= 0) return hipSuccess;
+  const int grid = int(std::min<int64_t>((n + 255) / 256, 4096));
+  hipLaunchKernelGGL(k_column_blocks, dim3(grid), dim3(256), 0, s, rows, nb, cb, to_blocks, src,
+                     dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const float* W1,
+                              const float* dh, float* dvec, float* dW1_part, float* dW1,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(k_radial_tail, dim3(kRadialTailChunks), dim3(256), 0, s, n_edges,
+                     kRadialTailChunks, vec, cutoff, W1, dh, dvec, dW1_part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sum_partials, dim3(2), dim3(256), 0, s, kRadialTailChunks,
+                     kRadBasis * kRadHidden, dW1_part, dW1);
+  return hipGetLastError();
+}
 
 bool radial_conv_supported(const char* set_name) {
   return set_name && std::strcmp(set_name, "L1to3") == 0;

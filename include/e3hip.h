@@ -217,6 +217,21 @@ e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n
                                  const void* workspace, size_t ws_bytes, const float* edge_vec,
                                  const float* x, const e3_radial* mlp, float* m, void* stream);
 
+/* Backward of e3_radial_mlp for the cotangent dw [E][n_cols] (n_cols a
+ * multiple of 32): dW1 [8][64] and dW2 [64][n_cols] (summed over the edges
+ * through fixed partials: reproducible) and dvec [E][3], the part of the
+ * edge-vector gradient that flows through |r_e| (radial: dvec_e is parallel
+ * to r_e, zero at r_e = 0); add it to e3_spherical_harmonics_backward's
+ * for the full edge-vector gradient.  dh = dw W2^T and dW2 = h^T dw run as
+ * the backward of e3_linear (fp32 matrix cores).  workspace: caller-owned,
+ * e3_radial_mlp_backward_workspace_size bytes, 16-byte aligned; dw 16-byte
+ * aligned.  All arrays float32 on the device. */
+e3_status e3_radial_mlp_backward_workspace_size(const e3_radial* mlp, int32_t n_edges,
+                                                int32_t n_cols, size_t* bytes);
+e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
+                                 const float* edge_vec, const float* dw, float* dW1, float* dW2,
+                                 float* dvec, void* workspace, size_t ws_bytes, void* stream);
+
 /* Per-node gradient from per-edge vector gradients, for r_e = pos[receiver]
  * - pos[sender]:
  *   node_grad[b] = sum_{e: receiver(e) = b} edge_grad[e]

@@ -215,6 +215,16 @@ def test_error_codes(lib):
     assert crad(api.Desc(sh3[:3], sh3, sh3, 32)) == -3                    # no fused kernel
     assert lib.e3_conv_forward_radial(_desc_c(d32), 4, 8, fake, fake, None, 0, fake, fake, None,
                                       fake, None) == -1
+    assert lib.e3_radial_mlp_backward_workspace_size(C.byref(rad), 10, 48, C.byref(sz)) == -3
+    assert lib.e3_radial_mlp_backward_workspace_size(C.byref(rad), 10, 1280, C.byref(sz)) == 0
+    rneed = sz.value
+    assert rneed >= 2 * 10 * 64 * 4 + 2 * 64 * 1280 * 4
+    rb = lambda ws, nb, dw=fake: lib.e3_radial_mlp_backward(C.byref(rad), 10, 1280, fake, dw, fake,
+                                                           fake, fake, ws, nb, None)
+    assert rb(fake, rneed - 1) == -6
+    assert rb(None, rneed) == -6
+    assert rb(odd, rneed) == -4
+    assert rb(fake, rneed, None) == -1
     out = np.zeros(10)
     assert lib.e3_cg_block(1, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
     assert lib.e3_cg_block(4, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1

@@ -164,3 +164,41 @@ def test_radial_conv_unsupported(gpu):
         gpu.conv_forward_radial(d, torch.zeros(5, dtype=torch.int32, device="cuda"),
                                 torch.zeros(0, dtype=torch.int32, device="cuda"), z(0, 3),
                                 z(4, 16, 64), 5.0, dev(W1), dev(W2))
+
+
+# ------------------------------------------------------- MLP backward
+
+@pytest.mark.parametrize("E,n_cols", [(3001, 1280), (40, 64), (0, 32)])
+def test_radial_mlp_backward_matches_oracle(gpu, E, n_cols):
+    rng = np.random.default_rng(220 + E)
+    ev = (rng.standard_normal((E, 3)) * 2.0).astype(np.float32)
+    if E > 2:
+        ev[1] = 0.0
+    W1, W2 = _weights(n_cols, 221)
+    dw = rng.standard_normal((E, n_cols)).astype(np.float32)
+    dW1, dW2, dvec = gpu.radial_mlp_backward(dev(ev), 5.0, dev(W1), dev(W2), dev(dw))
+    torch.cuda.synchronize()
+    if E == 0:
+        assert torch.all(dW1 == 0) and torch.all(dW2 == 0)
+        return
+    rW1, rW2, rvec = R.radial_mlp_backward(ev, 5.0, W1, W2, dw)
+    assert_close(host(dW1), rW1, TOL_F32, f"radial dW1 E={E}")
+    assert_close(host(dW2), rW2, TOL_F32, f"radial dW2 E={E}")
+    assert_close(host(dvec), rvec, TOL_F32, f"radial dvec E={E}")
+    assert np.all(host(dvec)[1] == 0.0) if E > 2 else True
+
+
+def test_radial_mlp_backward_deterministic_and_radial(gpu):
+    rng = np.random.default_rng(230)
+    E, n_cols = 20000, 640
+    ev = dev((rng.standard_normal((E, 3)) * 2.0).astype(np.float32))
+    W1, W2 = (dev(a) for a in _weights(n_cols, 231))
+    dw = dev(rng.standard_normal((E, n_cols)).astype(np.float32))
+    a = gpu.radial_mlp_backward(ev, 5.0, W1, W2, dw)
+    b = gpu.radial_mlp_backward(ev, 5.0, W1, W2, dw)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+    # the weights depend on |r| only: the edge-vector gradient is parallel to r
+    cross = torch.linalg.cross(a[2].double(), ev.double())
+    assert cross.abs().max().item() <= 1e-6 * a[2].abs().max().item() * ev.abs().max().item()
