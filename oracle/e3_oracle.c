@@ -55,7 +55,7 @@
 #endif
 
 #define ORACLE_MAX_IRREPS 16
-#define ORACLE_MAX_L 3
+#define ORACLE_MAX_L 6 /* harmonics; CG blocks up to twice this */
 #define ORACLE_MAX_PATHS 256
 
 typedef struct {
@@ -78,32 +78,34 @@ int oracle_num_threads(void) {
 #endif
 }
 
-static double factorial(int n) {
-  double r = 1.0;
-  for (int i = 2; i <= n; ++i) r *= (double)i;
+static long double factorial(int n) {
+  long double r = 1.0L;
+  for (int i = 2; i <= n; ++i) r *= (long double)i;
   return r;
 }
 
-/* <l1 m1 l2 m2 | L M> by Racah's closed form (Condon-Shortley phase). */
+/* <l1 m1 l2 m2 | L M> by Racah's closed form (Condon-Shortley phase), in
+ * long double: the alternating sum cancels more with the degree, and the
+ * factorials stay exact up to 20!. */
 double oracle_cg_complex(int l1, int m1, int l2, int m2, int L, int M) {
   if (M != m1 + m2) return 0.0;
   if (L < abs(l1 - l2) || L > l1 + l2) return 0.0;
   if (abs(m1) > l1 || abs(m2) > l2 || abs(M) > L) return 0.0;
-  double pre = sqrt((2.0 * L + 1.0) * factorial(L + l1 - l2) * factorial(L - l1 + l2) *
-                    factorial(l1 + l2 - L) / factorial(l1 + l2 + L + 1));
-  pre *= sqrt(factorial(L + M) * factorial(L - M) * factorial(l1 - m1) * factorial(l1 + m1) *
-              factorial(l2 - m2) * factorial(l2 + m2));
-  double s = 0.0;
+  long double pre = sqrtl((2.0L * L + 1.0L) * factorial(L + l1 - l2) * factorial(L - l1 + l2) *
+                          factorial(l1 + l2 - L) / factorial(l1 + l2 + L + 1));
+  pre *= sqrtl(factorial(L + M) * factorial(L - M) * factorial(l1 - m1) * factorial(l1 + m1) *
+               factorial(l2 - m2) * factorial(l2 + m2));
+  long double s = 0.0L;
   for (int k = 0;; ++k) {
     int d1 = l1 + l2 - L - k, d2 = l1 - m1 - k, d3 = l2 + m2 - k;
     int d4 = L - l2 + m1 + k, d5 = L - l1 - m2 + k;
     if (d1 < 0 || d2 < 0 || d3 < 0) break; /* these only shrink with k */
     if (d4 < 0 || d5 < 0) continue;        /* these only grow with k */
-    double t = factorial(k) * factorial(d1) * factorial(d2) * factorial(d3) * factorial(d4) *
-               factorial(d5);
-    s += ((k & 1) ? -1.0 : 1.0) / t;
+    long double t = factorial(k) * factorial(d1) * factorial(d2) * factorial(d3) *
+                    factorial(d4) * factorial(d5);
+    s += ((k & 1) ? -1.0L : 1.0L) / t;
   }
-  return pre * s;
+  return (double)(pre * s);
 }
 
 /* Complex -> real change of basis U_l (row = real m, column = complex m'),
@@ -174,9 +176,60 @@ int oracle_cg_real(int l1, int l2, int L, double *out) {
   return 0;
 }
 
+/* Component-normalised real harmonics of any degree l from the textbook
+ * construction: complex Y_l^m = N_lm P_l^m(cos t) e^{i m phi} with the
+ * Condon-Shortley phase, moved to the real basis of umat() and scaled by
+ * sqrt(4 pi).  The phase factors cancel, leaving for m > 0
+ *   Y_{l, m} = sqrt(2 (2l+1) (l-m)!/(l+m)!) Q_l^m(z) Re (x + i y)^m
+ *   Y_{l,-m} = sqrt(2 (2l+1) (l-m)!/(l+m)!) Q_l^m(z) Im (x + i y)^m
+ *   Y_{l, 0} = sqrt(2l+1) P_l(z)
+ * with Q_l^m = P_l^m / sin^m t (without the phase) a polynomial in z:
+ * Q_m^m = (2m-1)!!, Q_{m+1}^m = (2m+1) z Q_m^m,
+ * (l-m) Q_l^m = (2l-1) z Q_{l-1}^m - (l+m-1) Q_{l-2}^m.
+ * Used for l >= 4 (and checked against the polynomials below for l <= 3). */
+int oracle_sh_general(int l, const double r[3], double *out) {
+  if (l < 0 || l > ORACLE_MAX_L) return -1;
+  double n = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+  double x = 0, y = 0, z = 0;
+  if (n > 0) {
+    x = r[0] / n;
+    y = r[1] / n;
+    z = r[2] / n;
+  }
+  double cr = 1.0, ci = 0.0; /* (x + i y)^m */
+  for (int m = 0; m <= l; ++m) {
+    double q_mm = 1.0; /* (2m-1)!! */
+    for (int k = 2 * m - 1; k > 1; k -= 2) q_mm *= k;
+    double q = q_mm;
+    if (l > m) {
+      double q_prev = q_mm, q_cur = (2 * m + 1) * z * q_mm;
+      for (int ll = m + 2; ll <= l; ++ll) {
+        double q_next = ((2 * ll - 1) * z * q_cur - (ll + m - 1) * q_prev) / (ll - m);
+        q_prev = q_cur;
+        q_cur = q_next;
+      }
+      q = q_cur;
+    }
+    double ratio = 1.0; /* (l-m)!/(l+m)! */
+    for (int k = l - m + 1; k <= l + m; ++k) ratio /= k;
+    if (m == 0) {
+      out[l] = sqrt(2.0 * l + 1.0) * q;
+    } else {
+      double c = sqrt(2.0 * (2.0 * l + 1.0) * ratio) * q;
+      out[l + m] = c * cr;
+      out[l - m] = c * ci;
+    }
+    double nr = cr * x - ci * y, ni = cr * y + ci * x;
+    cr = nr;
+    ci = ni;
+  }
+  return 0;
+}
+
 /* Component-normalised real harmonics of the unit vector r/|r|, written out
- * as polynomials, for one degree l <= 3.  out has 2l+1 entries, m = -l..l.
- * A zero vector yields the l = 0 value only (higher degrees are 0). */
+ * as polynomials for l <= 3, by oracle_sh_general above for l = 4..6.
+ * out has 2l+1 entries, m = -l..l.  A zero vector yields the l = 0 value
+ * only (higher degrees are 0, except Y_l0 of the general form at z = 0). */
 int oracle_sh_l(int l, const double r[3], double *out) {
   double n = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
   double x = 0, y = 0, z = 0;
@@ -217,7 +270,7 @@ int oracle_sh_l(int l, const double r[3], double *out) {
       return 0;
     }
     default:
-      return -1;
+      return oracle_sh_general(l, r, out);
   }
 }
 
@@ -665,8 +718,9 @@ int oracle_tp_backward(const oracle_desc *d, int64_t n_rows, const double *x, co
  * J = dY/dr.  Written from the closed forms of oracle_sh_l: with
  * u = r/|r| the harmonics are polynomials P(u), and
  * dP/dr = (I - u u^T) grad_u P / |r|.  A zero vector gives 0. */
+#define ORACLE_MAX_L_GRAD 3 /* the closed-form partials below */
 int oracle_sh_grad(int lmax, const double r[3], const double *dY, double out[3]) {
-  if (lmax < 0 || lmax > ORACLE_MAX_L) return -1;
+  if (lmax < 0 || lmax > ORACLE_MAX_L_GRAD) return -1;
   out[0] = out[1] = out[2] = 0.0;
   double n = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
   if (n == 0.0) return 0;
@@ -725,7 +779,7 @@ int oracle_sh_grad(int lmax, const double r[3], const double *dY, double out[3])
 }
 
 int oracle_sh_grad_batch(int lmax, int64_t n, const double *r, const double *dY, double *out) {
-  if (lmax < 0 || lmax > ORACLE_MAX_L) return -1;
+  if (lmax < 0 || lmax > ORACLE_MAX_L_GRAD) return -1;
   const int d = (lmax + 1) * (lmax + 1);
   for (int64_t i = 0; i < n; ++i) oracle_sh_grad(lmax, r + 3 * i, dY + i * d, out + 3 * i);
   return 0;

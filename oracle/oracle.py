@@ -43,6 +43,7 @@ def _load():
     lib.oracle_umat.argtypes = [C.c_int, dp, dp]
     lib.oracle_sh_batch.restype = C.c_int
     lib.oracle_sh_batch.argtypes = [C.c_int, C.c_int64, dp, dp]
+    lib.oracle_sh_general.argtypes = [C.c_int, dp, dp]
     lib.oracle_num_threads.restype = C.c_int
     lib.oracle_num_paths.restype = C.c_int
     lib.oracle_num_paths.argtypes = [C.c_void_p]
@@ -293,6 +294,17 @@ def tp_backward(d: Desc, x, y, w, dz, rows=None):
     if r != 0:
         raise ValueError("oracle_tp_backward rejected its arguments")
     return dx, dw, dy
+
+
+def sh_general(l: int, vecs) -> np.ndarray:
+    """Degree-l harmonics by the oracle's general (Legendre) construction,
+    [n][2l+1]; sh() uses it for l >= 4 and closed-form polynomials below."""
+    v = _f64(vecs).reshape(-1, 3)
+    out = np.zeros((v.shape[0], 2 * l + 1))
+    for i in range(v.shape[0]):
+        if _load().oracle_sh_general(l, _dp(v[i]), _dp(out[i])) != 0:
+            raise ValueError("degree out of range")
+    return out
 
 
 def sh_grad(lmax: int, vecs, dY) -> np.ndarray:
