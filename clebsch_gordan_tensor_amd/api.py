@@ -47,7 +47,9 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_linear_num_weights", "e3_linear", "e3_linear_workspace_size",
            "e3_linear_backward", "e3_conv_double_backward_scratch_size",
            "e3_conv_double_backward", "e3_radial_mlp", "e3_conv_forward_radial",
-           "e3_radial_mlp_backward_workspace_size", "e3_radial_mlp_backward", "e3_last_error"]
+           "e3_radial_mlp_backward_workspace_size", "e3_radial_mlp_backward",
+           "e3_generic_plan_size", "e3_generic_plan_build", "e3_tp_forward_generic",
+           "e3_last_error"]
 
 
 class _CRadial(C.Structure):
@@ -82,6 +84,9 @@ def lib():
     L.e3_radial_mlp.argtypes = [C.POINTER(_CRadial), i32, i32, vp, vp, vp]
     L.e3_conv_forward_radial.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp,
                                          C.POINTER(_CRadial), vp, vp]
+    L.e3_generic_plan_size.argtypes = [dp, C.POINTER(sz)]
+    L.e3_generic_plan_build.argtypes = [dp, vp, sz]
+    L.e3_tp_forward_generic.argtypes = [dp, i64, vp, sz, vp, vp, vp, vp, C.c_int, vp]
     L.e3_radial_mlp_backward_workspace_size.argtypes = [C.POINTER(_CRadial), i32, i32,
                                                         C.POINTER(sz)]
     L.e3_radial_mlp_backward.argtypes = [C.POINTER(_CRadial), i32, i32, vp, vp, vp, vp, vp, vp,
@@ -540,3 +545,40 @@ def radial_mlp_backward(edge_vec, cutoff, W1, W2, dw, workspace=None, stream=Non
         C.byref(r), E, n_cols, _ptr(edge_vec), _ptr(dw), _ptr(dW1), _ptr(dW2), _ptr(dvec),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return dW1, dW2, dvec
+
+
+_GENERIC_PLANS = {}
+
+
+def generic_plan(desc: Desc, device):
+    """The coefficient table of the generic tensor product for desc: built on
+    the host by the library, copied to device memory once per descriptor."""
+    import numpy as np
+    import torch
+    key = (repr(desc.x), repr(desc.y), repr(desc.out), desc.channels, desc.flags, str(device))
+    if key not in _GENERIC_PLANS:
+        nb = C.c_size_t()
+        _check(lib().e3_generic_plan_size(C.byref(desc.c()), C.byref(nb)))
+        host = np.zeros(nb.value // 4, dtype=np.int32)
+        _check(lib().e3_generic_plan_build(C.byref(desc.c()), host.ctypes.data, nb.value))
+        _GENERIC_PLANS[key] = torch.from_numpy(host).to(device)
+    return _GENERIC_PLANS[key]
+
+
+def tp_forward_generic(desc: Desc, x, y, w, out=None, stream=None):
+    """z = tensor product of x and y weighted by w (as tp_forward) through the
+    coefficient-table kernel: any signature with degrees up to 6."""
+    import torch
+    B = x.shape[0]
+    P = num_paths(desc)
+    _need(x, "x", shape=(B, desc.dx, desc.channels))
+    _need(y, "y", shape=(B, desc.dy), dtype=torch.float32)
+    _need(w, "w", shape=(B, P, desc.channels), dtype=x.dtype)
+    if out is None:
+        out = torch.empty((B, desc.dout, desc.channels), device=x.device, dtype=x.dtype)
+    _need(out, "out", shape=(B, desc.dout, desc.channels), dtype=x.dtype)
+    plan = generic_plan(desc, x.device)
+    _check(lib().e3_tp_forward_generic(C.byref(desc.c()), B, _ptr(plan), plan.numel() * 4, _ptr(x),
+                                       _ptr(y), _ptr(w), _ptr(out), _dtype_code(x),
+                                       _stream(stream)))
+    return out

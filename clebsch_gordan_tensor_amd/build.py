@@ -30,6 +30,7 @@ HIP_SOURCES = [
     "kernels/prep.hip",
     "kernels/linear.hip",
     "kernels/radial.hip",
+    "kernels/generic.hip",
     "api.cpp",
     "host/cg_ladder.cpp",
 ]

@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <cmath>
 #include <string>
 #include <vector>
@@ -26,6 +27,8 @@ e3_status ok() {
   g_last_error.clear();
   return E3_OK;
 }
+
+constexpr int kGenericLmax = 6;  // coefficient tables of the generic tensor product
 
 struct Parsed {
   int C = 0;
@@ -231,8 +234,8 @@ int32_t e3_supported(const e3_desc* desc, e3_dtype dtype) {
 
 e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out) {
   if (!out) return fail(E3_ERR_INVALID_ARG, "out is null");
-  if (l1 < 0 || l2 < 0 || L < 0 || l1 > 3 || l2 > 3 || L > 3)
-    return fail(E3_ERR_INVALID_ARG, "degrees must be in 0..3");
+  if (l1 < 0 || l2 < 0 || L < 0 || l1 > kGenericLmax || l2 > kGenericLmax || L > kGenericLmax)
+    return fail(E3_ERR_INVALID_ARG, "degrees must be in 0..6");
   std::vector<double> T;
   if (!e3::cg_real_block(l1, l2, L, T)) return fail(E3_ERR_INVALID_ARG, "triple does not couple");
   for (size_t k = 0; k < T.size(); ++k) out[k] = T[k];
@@ -805,6 +808,119 @@ e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t 
   return hip_status(e3k::launch_radial_tail(n_edges, edge_vec, mlp->cutoff, mlp->W1, dh, dvec,
                                             part, dW1, st),
                     "radial_mlp_backward");
+}
+
+namespace {
+
+// Coefficient table of the generic tensor product (layout in
+// kernels/generic.hip), from the ladder-built real CG blocks.
+e3_status build_generic(const e3_desc* desc, std::vector<int32_t>& out) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  for (const auto* v : {&p.x, &p.y, &p.o})
+    for (const auto& r : *v)
+      if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 6");
+  if (p.dx * 64 + p.dy > 4096 || p.dy >= 65536)
+    return fail(E3_ERR_UNSUPPORTED, "x has too many components for the generic kernel (dx <= 63)");
+  std::vector<int> xoff(p.x.size()), yoff(p.y.size()), ooff(p.o.size());
+  int o = 0;
+  for (size_t i = 0; i < p.x.size(); ++i) xoff[i] = o, o += 2 * p.x[i].l + 1;
+  o = 0;
+  for (size_t i = 0; i < p.y.size(); ++i) yoff[i] = o, o += 2 * p.y[i].l + 1;
+  o = 0;
+  for (size_t i = 0; i < p.o.size(); ++i) ooff[i] = o, o += 2 * p.o[i].l + 1;
+  struct Contrib {
+    int path, rb, re;
+  };
+  std::vector<std::vector<Contrib>> per_o(p.dout);
+  std::vector<int32_t> rec;
+  int oo_pp = 0;  // output offset of the current path in per-path mode
+  for (int pi = 0; pi < p.P; ++pi) {
+    const int l1 = p.x[p.pix[pi]].l, l2 = p.y[p.piy[pi]].l, L = p.o[p.pio[pi]].l;
+    const int xo = xoff[p.pix[pi]], yo = yoff[p.piy[pi]];
+    const int oo = p.per_path ? oo_pp : ooff[p.pio[pi]];
+    oo_pp += 2 * L + 1;
+    std::vector<double> T;
+    if (!e3::cg_real_block(l1, l2, L, T)) return fail(E3_ERR_IRREPS, "path does not couple");
+    const int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
+    for (int M = 0; M < 2 * L + 1; ++M) {
+      const int rb = int(rec.size() / 2);
+      for (int a = 0; a < n1; ++a)
+        for (int b = 0; b < n2; ++b) {
+          const double c = T[(size_t(M) * n1 + a) * n2 + b];
+          if (std::fabs(c) < 1e-12) continue;
+          const float cf = float(c);
+          int32_t bits;
+          std::memcpy(&bits, &cf, 4);
+          rec.push_back(int32_t((xo + a) | ((yo + b) << 16)));
+          rec.push_back(bits);
+        }
+      const int re = int(rec.size() / 2);
+      if (re > rb) per_o[oo + M].push_back(Contrib{pi, rb, re});
+    }
+  }
+  int n_contrib = 0;
+  for (auto& v : per_o) n_contrib += int(v.size());
+  out.clear();
+  out.reserve(size_t(e3k::kGenHeader) + p.dout + 1 + 3 * size_t(n_contrib) + rec.size());
+  for (int32_t v : {int32_t(e3k::kGenMagic), int32_t(p.dx), int32_t(p.dy), int32_t(p.dout),
+                    int32_t(p.P), int32_t(n_contrib), int32_t(rec.size() / 2)})
+    out.push_back(v);
+  int acc = 0;
+  for (int i = 0; i < p.dout; ++i) out.push_back(acc), acc += int(per_o[i].size());
+  out.push_back(acc);
+  for (auto& v : per_o)
+    for (auto& c : v) out.push_back(c.path), out.push_back(c.rb), out.push_back(c.re);
+  out.insert(out.end(), rec.begin(), rec.end());
+  return ok();
+}
+
+}  // namespace
+
+e3_status e3_generic_plan_size(const e3_desc* desc, size_t* bytes) {
+  if (!bytes) return fail(E3_ERR_INVALID_ARG, "bytes is null");
+  std::vector<int32_t> t;
+  e3_status s = build_generic(desc, t);
+  if (s != E3_OK) return s;
+  *bytes = t.size() * sizeof(int32_t);
+  return ok();
+}
+
+e3_status e3_generic_plan_build(const e3_desc* desc, void* host_plan, size_t bytes) {
+  if (!host_plan) return fail(E3_ERR_INVALID_ARG, "host_plan is null");
+  std::vector<int32_t> t;
+  e3_status s = build_generic(desc, t);
+  if (s != E3_OK) return s;
+  if (bytes < t.size() * sizeof(int32_t))
+    return fail(E3_ERR_WORKSPACE, "plan needs " + std::to_string(t.size() * 4) + " bytes");
+  std::memcpy(host_plan, t.data(), t.size() * sizeof(int32_t));
+  return ok();
+}
+
+e3_status e3_tp_forward_generic(const e3_desc* desc, int64_t n_rows, const void* plan,
+                                size_t plan_bytes, const void* x, const float* y, const void* w,
+                                void* z, e3_dtype dtype, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if (dtype != E3_F32 && dtype != E3_BF16) return fail(E3_ERR_INVALID_ARG, "unknown dtype");
+  for (const auto* v : {&p.x, &p.y, &p.o})
+    for (const auto& r : *v)
+      if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 6");
+  if (p.dx * 64 + p.dy > 4096)
+    return fail(E3_ERR_UNSUPPORTED, "x has too many components for the generic kernel (dx <= 63)");
+  if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows == 0) return ok();
+  if (!plan || !x || !y || !w || !z) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  const size_t min_words = size_t(e3k::kGenHeader) + p.dout + 1;
+  if (plan_bytes < min_words * sizeof(int32_t) || (plan_bytes % 4) != 0)
+    return fail(E3_ERR_WORKSPACE, "plan is too short for this descriptor");
+  if (!aligned16(plan)) return fail(E3_ERR_ALIGNMENT, "plan must be 16-byte aligned");
+  e3k::GenericTpArgs a{n_rows, p.C, p.dx, p.dy, p.dout, p.P, static_cast<const int*>(plan),
+                       int64_t(plan_bytes / 4), x, y, w, z};
+  return hip_status(e3k::launch_tp_generic(a, dtype == E3_BF16, hipStream_t(stream)),
+                    "tp_forward_generic");
 }
 
 const char* e3_last_error(void) { return g_last_error.c_str(); }

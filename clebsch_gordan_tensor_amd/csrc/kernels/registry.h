@@ -95,6 +95,22 @@ hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr,
 hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hipStream_t s);
 hipError_t launch_add(void* dst, const void* src, int64_t n, int bf16, hipStream_t s);
 
+// Tensor product from a coefficient table (generic.hip); the table layout
+// is documented there and built by the host (e3_generic_plan_build).
+constexpr int kGenHeader = 7;
+constexpr int kGenMagic = 0x31434745;
+struct GenericTpArgs {
+  int64_t n_rows;
+  int C, dx, dy, dout, np;
+  const int* prog;
+  int64_t n_words;
+  const void* x;
+  const float* y;
+  const void* w;
+  void* z;
+};
+hipError_t launch_tp_generic(const GenericTpArgs& a, int bf16, hipStream_t s);
+
 // Radial edge weights and the convolution that computes them on the fly
 // (radial.hip): 8 Bessel functions -> 64 SiLU units -> n_cols = P*C.
 struct RadialConvArgs {

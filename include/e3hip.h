@@ -119,9 +119,9 @@ e3_status e3_path_info(const e3_desc* desc, int32_t i, int32_t* ix, int32_t* iy,
  * The tensor-product calls accept the same. */
 int32_t e3_supported(const e3_desc* desc, e3_dtype dtype);
 
-/* Real coupling block T[M][m1][m2] of (l1, l2, L), l <= 3, written to the
- * HOST array out[(2L+1)(2l1+1)(2l2+1)] (the table the kernels are built
- * from; e3j G.2 construction). */
+/* Real coupling block T[M][m1][m2] of (l1, l2, L), l <= 6, written to the
+ * HOST array out[(2L+1)(2l1+1)(2l2+1)] (the blocks the kernels' tables are
+ * built from; e3j G.2 construction). */
 e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out);
 
 /* Harmonics Y[n][(lmax+1)^2] of vec[n][3] (e3j A.3 Eq.4), lmax <= 3. */
@@ -231,6 +231,26 @@ e3_status e3_radial_mlp_backward_workspace_size(const e3_radial* mlp, int32_t n_
 e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
                                  const float* edge_vec, const float* dw, float* dW1, float* dW2,
                                  float* dvec, void* workspace, size_t ws_bytes, void* stream);
+
+/* Tensor product (as e3_tp_forward: e3j E.1 Eq.10-11, any channel-wise
+ * signature, collapsed or per-path outputs) for irreps of degree up to 6,
+ * driven by a coefficient table instead of a compiled kernel (e3j treats
+ * the product as a bilinear coupling given by a sparse COO array of
+ * coefficients, E.1 and B.1; Figs 5-6 run it to L = 6 and beyond).
+ *   e3_generic_plan_size / e3_generic_plan_build: host-only; write the
+ *     table for desc into a HOST buffer; the caller copies it to device
+ *     memory it owns (16-byte aligned) and may reuse it for every call with
+ *     the same descriptor.
+ *   e3_tp_forward_generic: x [n][dx][C], y [n][dy] float32, w [n][P][C],
+ *     z [n][dout][C]; fp32 or bf16 storage, fp32 accumulation.  Needs every
+ *     degree <= 6 and dx*64 + dy <= 4096 (dx <= 63).  A table built for
+ *     another descriptor gives wrong values but never an out-of-bounds
+ *     access (every index read from it is clamped). */
+e3_status e3_generic_plan_size(const e3_desc* desc, size_t* bytes);
+e3_status e3_generic_plan_build(const e3_desc* desc, void* host_plan, size_t bytes);
+e3_status e3_tp_forward_generic(const e3_desc* desc, int64_t n_rows, const void* plan,
+                                size_t plan_bytes, const void* x, const float* y, const void* w,
+                                void* z, e3_dtype dtype, void* stream);
 
 /* Per-node gradient from per-edge vector gradients, for r_e = pos[receiver]
  * - pos[sender]:

@@ -65,10 +65,10 @@ def test_expected_path_counts():
 
 def test_host_cg_table_equals_oracle(lib):
     # two independent constructions: ladder operators (library) and Racah (oracle)
-    for l1, l2 in itertools.product(range(4), repeat=2):
-        for L in range(abs(l1 - l2), min(l1 + l2, 3) + 1):
+    for l1, l2 in itertools.product(range(7), repeat=2):
+        for L in range(abs(l1 - l2), min(l1 + l2, 6) + 1):
             np.testing.assert_allclose(api.cg_block(l1, l2, L), O.cg_real(l1, l2, L),
-                                       atol=1e-12, err_msg=str((l1, l2, L)))
+                                       atol=1e-11, err_msg=str((l1, l2, L)))
 
 
 def test_supported_signatures(lib):
@@ -227,4 +227,43 @@ def test_error_codes(lib):
     assert rb(fake, rneed, None) == -1
     out = np.zeros(10)
     assert lib.e3_cg_block(1, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
-    assert lib.e3_cg_block(4, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
+    assert lib.e3_cg_block(7, 1, 6, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
+
+
+def test_generic_plan_table(lib):
+    # the table of the generic tensor product: header, one range per output
+    # component, every record's coefficient equal to the ladder CG block
+    nat = [(l, 1 if l % 2 == 0 else -1) for l in range(5)]
+    d = api.Desc(nat, nat, nat, 64)
+    nb = C.c_size_t()
+    assert lib.e3_generic_plan_size(C.byref(d.c()), C.byref(nb)) == 0
+    t = np.zeros(nb.value // 4, dtype=np.int32)
+    assert lib.e3_generic_plan_build(C.byref(d.c()), t.ctypes.data, nb.value - 4) == -6
+    assert lib.e3_generic_plan_build(C.byref(d.c()), t.ctypes.data, nb.value) == 0
+    dx = dy = dout = 25
+    P, n_contrib, n_rec = t[4], t[5], t[6]
+    assert list(t[1:4]) == [dx, dy, dout] and P == api.num_paths(d) == 42
+    obeg = t[7:7 + dout + 1]
+    assert obeg[0] == 0 and obeg[-1] == n_contrib and np.all(np.diff(obeg) >= 0)
+    contrib = t[7 + dout + 1:7 + dout + 1 + 3 * n_contrib].reshape(-1, 3)
+    rec = t[7 + dout + 1 + 3 * n_contrib:].reshape(-1, 2)
+    assert rec.shape[0] == n_rec == 1158  # nonzeros of the 42 real blocks
+    offs = np.cumsum([0] + [2 * l + 1 for l, _ in nat])
+    paths = [api.path_info(d, i) for i in range(P)]
+    for o in (0, 7, 24):
+        for p, rb, re in contrib[obeg[o]:obeg[o + 1]]:
+            ix, iy, io = paths[p]
+            l1, l2, L = nat[ix][0], nat[iy][0], nat[io][0]
+            assert offs[io] <= o < offs[io] + 2 * L + 1
+            T = api.cg_block(l1, l2, L)
+            for packed, bits in rec[rb:re]:
+                xi, yi = packed & 0xFFFF, packed >> 16
+                c = np.array([bits], np.int32).view(np.float32)[0]
+                assert c == pytest.approx(T[o - offs[io], xi - offs[ix], yi - offs[iy]], abs=1e-7)
+    big = api.Desc([(7, 1)], [(0, 1)], [(7, 1)], 64)
+    assert lib.e3_generic_plan_size(C.byref(big.c()), C.byref(nb)) == -3
+    assert lib.e3_tp_forward_generic(C.byref(d.c()), 0, None, 0, None, None, None, None, 0,
+                                     None) == 0
+    fake = C.c_void_p(0x10000)
+    assert lib.e3_tp_forward_generic(C.byref(d.c()), 5, fake, 16, fake, fake, fake, fake, 0,
+                                     None) == -6
