@@ -856,23 +856,32 @@ e3_status build_generic(const e3_desc* desc, std::vector<int32_t>& out) {
           rec.push_back(int32_t((xo + a) | ((yo + b) << 16)));
           rec.push_back(bits);
         }
+      if (int(rec.size() / 2) > rb)  // pad the run to whole groups of 4 (zero records)
+        while ((rec.size() / 2) % 4) {
+          rec.push_back(int32_t(xo | (yo << 16)));
+          rec.push_back(0);
+        }
       const int re = int(rec.size() / 2);
       if (re > rb) per_o[oo + M].push_back(Contrib{pi, rb, re});
     }
   }
   int n_contrib = 0;
   for (auto& v : per_o) n_contrib += int(v.size());
-  out.clear();
-  out.reserve(size_t(e3k::kGenHeader) + p.dout + 1 + 3 * size_t(n_contrib) + rec.size());
-  for (int32_t v : {int32_t(e3k::kGenMagic), int32_t(p.dx), int32_t(p.dy), int32_t(p.dout),
-                    int32_t(p.P), int32_t(n_contrib), int32_t(rec.size() / 2)})
-    out.push_back(v);
+  const size_t rec_words = rec.size();
+  size_t rec_off = size_t(e3k::kGenHeader) + p.dout + 1 + 3 * size_t(n_contrib);
+  rec_off = (rec_off + 7) / 8 * 8;  // records start on a 32-byte boundary
+  out.assign(rec_off + rec_words, 0);
+  const int32_t head[e3k::kGenHeader] = {int32_t(e3k::kGenMagic), int32_t(p.dx), int32_t(p.dy),
+                                         int32_t(p.dout), int32_t(p.P), int32_t(n_contrib),
+                                         int32_t(rec_words / 2), int32_t(rec_off)};
+  for (int i = 0; i < e3k::kGenHeader; ++i) out[i] = head[i];
+  size_t w = e3k::kGenHeader;
   int acc = 0;
-  for (int i = 0; i < p.dout; ++i) out.push_back(acc), acc += int(per_o[i].size());
-  out.push_back(acc);
+  for (int i = 0; i < p.dout; ++i) out[w++] = acc, acc += int(per_o[i].size());
+  out[w++] = acc;
   for (auto& v : per_o)
-    for (auto& c : v) out.push_back(c.path), out.push_back(c.rb), out.push_back(c.re);
-  out.insert(out.end(), rec.begin(), rec.end());
+    for (auto& c : v) out[w++] = c.path, out[w++] = c.rb, out[w++] = c.re;
+  std::copy(rec.begin(), rec.end(), out.begin() + rec_off);
   return ok();
 }
 

@@ -9,10 +9,14 @@
 // table built on the host from the library's ladder CG (e3_generic_plan_build).
 //
 // Table (int32 words, built per descriptor):
-//   header  [kGenMagic, dx, dy, dout, P, n_contrib, n_rec]
+//   header  [kGenMagic, dx, dy, dout, P, n_contrib, n_rec, rec_off]
 //   obeg    [dout + 1]         contributions of output component o
 //   contrib [n_contrib][3]     {path, first record, end record}
-//   rec     [n_rec][2]         {x component | y component << 16, coefficient bits}
+//   rec     [n_rec][2]         at word rec_off (32-byte aligned):
+//                              {x component | y component << 16, coefficient bits}
+// Every record run is padded to a multiple of 4 with zero coefficients, so
+// the kernel takes records four at a time (one 32-byte scalar load, eight
+// LDS reads in flight, two partial sums).
 // Output-stationary: for every output component o of a row,
 //   z[o][c] = sum_contributions w[P][c] sum_records c_r y[yi] x[xi][c]
 // so each z element is written once and no accumulator is indexed at run
@@ -42,12 +46,14 @@ __global__ void __launch_bounds__(64 * kGenWaves)
                  const int* __restrict__ prog, int64_t n_words, const T* __restrict__ x,
                  const float* __restrict__ y, const T* __restrict__ w, T* __restrict__ z) {
   int n_contrib = prog[5], n_rec = prog[6];
+  const int64_t rec_off = prog[7];
   const int64_t fixed = kGenHeader + int64_t(dout) + 1;
-  if (n_contrib < 0 || n_rec < 0 || fixed + 3 * int64_t(n_contrib) + 2 * int64_t(n_rec) > n_words)
+  if (n_contrib < 0 || n_rec < 0 || rec_off < fixed + 3 * int64_t(n_contrib) || (rec_off & 7) ||
+      rec_off + 2 * int64_t(n_rec) > n_words)
     n_contrib = n_rec = 0;
   const int* obeg = prog + kGenHeader;
   const int* contrib = obeg + dout + 1;
-  const int* rec = contrib + 3 * n_contrib;
+  const int4* rec4 = reinterpret_cast<const int4*>(prog + (n_rec ? rec_off : 0));
   extern __shared__ float gsm[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int stride = dx * 64 + dy;
@@ -75,15 +81,24 @@ __global__ void __launch_bounds__(64 * kGenWaves)
         const int p = min(max(contrib[3 * j], 0), np - 1);
         float wv[1] = {0.0f};
         if (active) load_ch<T, 1>(w + (row * np + p) * C + c, wv);
-        const int rb = max(contrib[3 * j + 1], 0), re = min(contrib[3 * j + 2], n_rec);
-        float t = 0.0f;
-        for (int r = rb; r < re; ++r) {
-          const int packed = rec[2 * r];
-          const float cf = __int_as_float(rec[2 * r + 1]);
-          const int xi = min(packed & 0xffff, dx - 1), yi = min(int(unsigned(packed) >> 16), dy - 1);
-          t = fmaf(cf * ys[yi], xs[xi * 64 + lane], t);
+        // runs are whole groups of 4 records: [rb, re) in units of 4
+        const int gb = max(contrib[3 * j + 1], 0) >> 2, ge = min(contrib[3 * j + 2], n_rec) >> 2;
+        float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll 2
+        for (int g = gb; g < ge; ++g) {
+          const int4 a = rec4[2 * g], b = rec4[2 * g + 1];  // 4 records, 32 bytes
+          const int p0 = a.x, p1 = a.z, p2 = b.x, p3 = b.z;
+          auto xi = [&](int pk) { return min(pk & 0xffff, dx - 1); };
+          auto yi = [&](int pk) { return min(int(unsigned(pk) >> 16), dy - 1); };
+          const float y0 = ys[yi(p0)], y1 = ys[yi(p1)], y2 = ys[yi(p2)], y3 = ys[yi(p3)];
+          const float x0 = xs[xi(p0) * 64 + lane], x1 = xs[xi(p1) * 64 + lane];
+          const float x2 = xs[xi(p2) * 64 + lane], x3 = xs[xi(p3) * 64 + lane];
+          t0 = fmaf(__int_as_float(a.y) * y0, x0, t0);
+          t1 = fmaf(__int_as_float(a.w) * y1, x1, t1);
+          t0 = fmaf(__int_as_float(b.y) * y2, x2, t0);
+          t1 = fmaf(__int_as_float(b.w) * y3, x3, t1);
         }
-        acc = fmaf(wv[0], t, acc);
+        acc = fmaf(wv[0], t0 + t1, acc);
       }
       float out[1] = {acc};
       if (active) store_ch<T, 1>(z + (row * dout + o) * C + c, out);

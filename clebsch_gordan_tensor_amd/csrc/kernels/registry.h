@@ -97,7 +97,7 @@ hipError_t launch_add(void* dst, const void* src, int64_t n, int bf16, hipStream
 
 // Tensor product from a coefficient table (generic.hip); the table layout
 // is documented there and built by the host (e3_generic_plan_build).
-constexpr int kGenHeader = 7;
+constexpr int kGenHeader = 8;
 constexpr int kGenMagic = 0x31434745;
 struct GenericTpArgs {
   int64_t n_rows;

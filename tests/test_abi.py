@@ -241,13 +241,16 @@ def test_generic_plan_table(lib):
     assert lib.e3_generic_plan_build(C.byref(d.c()), t.ctypes.data, nb.value - 4) == -6
     assert lib.e3_generic_plan_build(C.byref(d.c()), t.ctypes.data, nb.value) == 0
     dx = dy = dout = 25
-    P, n_contrib, n_rec = t[4], t[5], t[6]
+    P, n_contrib, n_rec, rec_off = t[4], t[5], t[6], t[7]
     assert list(t[1:4]) == [dx, dy, dout] and P == api.num_paths(d) == 42
-    obeg = t[7:7 + dout + 1]
+    obeg = t[8:8 + dout + 1]
     assert obeg[0] == 0 and obeg[-1] == n_contrib and np.all(np.diff(obeg) >= 0)
-    contrib = t[7 + dout + 1:7 + dout + 1 + 3 * n_contrib].reshape(-1, 3)
-    rec = t[7 + dout + 1 + 3 * n_contrib:].reshape(-1, 2)
-    assert rec.shape[0] == n_rec == 1158  # nonzeros of the 42 real blocks
+    contrib = t[8 + dout + 1:8 + dout + 1 + 3 * n_contrib].reshape(-1, 3)
+    assert rec_off % 8 == 0 and rec_off >= 8 + dout + 1 + 3 * n_contrib
+    rec = t[rec_off:rec_off + 2 * n_rec].reshape(-1, 2)
+    coef = rec[:, 1].copy().view(np.float32)
+    assert np.count_nonzero(coef) == 1158  # nonzeros of the 42 real blocks
+    assert np.all(contrib[:, 1] % 4 == 0) and np.all(contrib[:, 2] % 4 == 0)  # runs of 4
     offs = np.cumsum([0] + [2 * l + 1 for l, _ in nat])
     paths = [api.path_info(d, i) for i in range(P)]
     for o in (0, 7, 24):
@@ -259,7 +262,9 @@ def test_generic_plan_table(lib):
             for packed, bits in rec[rb:re]:
                 xi, yi = packed & 0xFFFF, packed >> 16
                 c = np.array([bits], np.int32).view(np.float32)[0]
-                assert c == pytest.approx(T[o - offs[io], xi - offs[ix], yi - offs[iy]], abs=1e-7)
+                if c != 0.0:
+                    assert c == pytest.approx(T[o - offs[io], xi - offs[ix], yi - offs[iy]],
+                                              abs=1e-7)
     big = api.Desc([(7, 1)], [(0, 1)], [(7, 1)], 64)
     assert lib.e3_generic_plan_size(C.byref(big.c()), C.byref(nb)) == -3
     assert lib.e3_tp_forward_generic(C.byref(d.c()), 0, None, 0, None, None, None, None, 0,
