@@ -49,7 +49,8 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_conv_double_backward", "e3_radial_mlp", "e3_conv_forward_radial",
            "e3_radial_mlp_backward_workspace_size", "e3_radial_mlp_backward",
            "e3_generic_plan_size", "e3_generic_plan_build", "e3_tp_forward_generic",
-           "e3_last_error"]
+           "e3_tp_backward_generic", "e3_last_error"]
+E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW = 0, 1, 2
 
 
 class _CRadial(C.Structure):
@@ -84,8 +85,10 @@ def lib():
     L.e3_radial_mlp.argtypes = [C.POINTER(_CRadial), i32, i32, vp, vp, vp]
     L.e3_conv_forward_radial.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp,
                                          C.POINTER(_CRadial), vp, vp]
-    L.e3_generic_plan_size.argtypes = [dp, C.POINTER(sz)]
-    L.e3_generic_plan_build.argtypes = [dp, vp, sz]
+    L.e3_generic_plan_size.argtypes = [dp, i32, C.POINTER(sz)]
+    L.e3_generic_plan_build.argtypes = [dp, i32, vp, sz]
+    L.e3_tp_backward_generic.argtypes = [dp, i64, vp, sz, vp, sz, vp, sz, vp, vp, vp, vp, vp, vp,
+                                         vp, C.c_int, vp]
     L.e3_tp_forward_generic.argtypes = [dp, i64, vp, sz, vp, vp, vp, vp, C.c_int, vp]
     L.e3_radial_mlp_backward_workspace_size.argtypes = [C.POINTER(_CRadial), i32, i32,
                                                         C.POINTER(sz)]
@@ -550,17 +553,19 @@ def radial_mlp_backward(edge_vec, cutoff, W1, W2, dw, workspace=None, stream=Non
 _GENERIC_PLANS = {}
 
 
-def generic_plan(desc: Desc, device):
-    """The coefficient table of the generic tensor product for desc: built on
-    the host by the library, copied to device memory once per descriptor."""
+def generic_plan(desc: Desc, device, table=0):
+    """Coefficient table `table` (E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW) of the
+    generic tensor product for desc: built on the host by the library, copied
+    to device memory once per descriptor."""
     import numpy as np
     import torch
-    key = (repr(desc.x), repr(desc.y), repr(desc.out), desc.channels, desc.flags, str(device))
+    key = (repr(desc.x), repr(desc.y), repr(desc.out), desc.channels, desc.flags, str(device),
+           table)
     if key not in _GENERIC_PLANS:
         nb = C.c_size_t()
-        _check(lib().e3_generic_plan_size(C.byref(desc.c()), C.byref(nb)))
+        _check(lib().e3_generic_plan_size(C.byref(desc.c()), table, C.byref(nb)))
         host = np.zeros(nb.value // 4, dtype=np.int32)
-        _check(lib().e3_generic_plan_build(C.byref(desc.c()), host.ctypes.data, nb.value))
+        _check(lib().e3_generic_plan_build(C.byref(desc.c()), table, host.ctypes.data, nb.value))
         _GENERIC_PLANS[key] = torch.from_numpy(host).to(device)
     return _GENERIC_PLANS[key]
 
@@ -582,3 +587,22 @@ def tp_forward_generic(desc: Desc, x, y, w, out=None, stream=None):
                                        _ptr(y), _ptr(w), _ptr(out), _dtype_code(x),
                                        _stream(stream)))
     return out
+
+
+def tp_backward_generic(desc: Desc, x, y, w, dz, stream=None):
+    """(dx, dw, dy) of tp_forward_generic for the cotangent dz."""
+    import torch
+    B = x.shape[0]
+    P = num_paths(desc)
+    _need(x, "x", shape=(B, desc.dx, desc.channels))
+    _need(y, "y", shape=(B, desc.dy), dtype=torch.float32)
+    _need(w, "w", shape=(B, P, desc.channels), dtype=x.dtype)
+    _need(dz, "dz", shape=(B, desc.dout, desc.channels), dtype=x.dtype)
+    pf, px, pw = (generic_plan(desc, x.device, t) for t in (E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW))
+    dx, dw = torch.empty_like(x), torch.empty_like(w)
+    dy = torch.empty((B, desc.dy), device=x.device, dtype=torch.float32)
+    _check(lib().e3_tp_backward_generic(
+        C.byref(desc.c()), B, _ptr(pf), pf.numel() * 4, _ptr(px), px.numel() * 4, _ptr(pw),
+        pw.numel() * 4, _ptr(x), _ptr(y), _ptr(w), _ptr(dz), _ptr(dx), _ptr(dw), _ptr(dy),
+        _dtype_code(x), _stream(stream)))
+    return dx, dw, dy

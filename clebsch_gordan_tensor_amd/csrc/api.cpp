@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <cmath>
 #include <string>
 #include <vector>
@@ -814,15 +815,34 @@ namespace {
 
 // Coefficient table of the generic tensor product (layout in
 // kernels/generic.hip), from the ladder-built real CG blocks.
-e3_status build_generic(const e3_desc* desc, std::vector<int32_t>& out) {
-  Parsed p;
+// The three tables of a descriptor (layout in kernels/generic.hip).  Every
+// nonzero coefficient c of path P couples output component o, x component
+// xi and y component yi; a table keys the entries by what the kernel writes
+// and names which array acts as its per-lane operand ("x") and which as its
+// per-path scalar array ("w"):
+//   forward  z[o]  = sum_P w[P]  sum c y[yi] x[xi]     key o,  weight P, operand xi
+//   dx       dx[xi] = sum_P w[P]  sum c y[yi] dz[o]    key xi, weight P, operand o
+//   dw       dw[P]  = sum_o dz[o] sum c y[yi] x[xi]    key P,  weight o, operand xi
+// (e3j E.1 Eq.14-15: each cotangent is the same bilinear form with the
+// coefficient records permuted.)
+struct GenEntry {
+  int P, o, xi, yi;
+  float c;
+};
+
+struct GenDims {
+  int operand, y, keys, weights;  // kernel's view: x comps, y comps, outputs, w rows
+};
+
+e3_status generic_entries(const e3_desc* desc, Parsed& p, std::vector<GenEntry>& ent) {
   e3_status s = parse(desc, p);
   if (s != E3_OK) return s;
   for (const auto* v : {&p.x, &p.y, &p.o})
     for (const auto& r : *v)
       if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 6");
-  if (p.dx * 64 + p.dy > 4096 || p.dy >= 65536)
-    return fail(E3_ERR_UNSUPPORTED, "x has too many components for the generic kernel (dx <= 63)");
+  if (p.dx * 64 + p.dy > 4096 || p.dout * 64 + p.dy > 4096 || p.dy >= 65536)
+    return fail(E3_ERR_UNSUPPORTED,
+                "too many components for the generic kernel (dx, dout <= 63)");
   std::vector<int> xoff(p.x.size()), yoff(p.y.size()), ooff(p.o.size());
   int o = 0;
   for (size_t i = 0; i < p.x.size(); ++i) xoff[i] = o, o += 2 * p.x[i].l + 1;
@@ -830,11 +850,7 @@ e3_status build_generic(const e3_desc* desc, std::vector<int32_t>& out) {
   for (size_t i = 0; i < p.y.size(); ++i) yoff[i] = o, o += 2 * p.y[i].l + 1;
   o = 0;
   for (size_t i = 0; i < p.o.size(); ++i) ooff[i] = o, o += 2 * p.o[i].l + 1;
-  struct Contrib {
-    int path, rb, re;
-  };
-  std::vector<std::vector<Contrib>> per_o(p.dout);
-  std::vector<int32_t> rec;
+  ent.clear();
   int oo_pp = 0;  // output offset of the current path in per-path mode
   for (int pi = 0; pi < p.P; ++pi) {
     const int l1 = p.x[p.pix[pi]].l, l2 = p.y[p.piy[pi]].l, L = p.o[p.pio[pi]].l;
@@ -844,62 +860,96 @@ e3_status build_generic(const e3_desc* desc, std::vector<int32_t>& out) {
     std::vector<double> T;
     if (!e3::cg_real_block(l1, l2, L, T)) return fail(E3_ERR_IRREPS, "path does not couple");
     const int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1;
-    for (int M = 0; M < 2 * L + 1; ++M) {
-      const int rb = int(rec.size() / 2);
+    for (int M = 0; M < 2 * L + 1; ++M)
       for (int a = 0; a < n1; ++a)
         for (int b = 0; b < n2; ++b) {
           const double c = T[(size_t(M) * n1 + a) * n2 + b];
-          if (std::fabs(c) < 1e-12) continue;
-          const float cf = float(c);
-          int32_t bits;
-          std::memcpy(&bits, &cf, 4);
-          rec.push_back(int32_t((xo + a) | ((yo + b) << 16)));
-          rec.push_back(bits);
+          if (std::fabs(c) >= 1e-12) ent.push_back(GenEntry{pi, oo + M, xo + a, yo + b, float(c)});
         }
-      if (int(rec.size() / 2) > rb)  // pad the run to whole groups of 4 (zero records)
-        while ((rec.size() / 2) % 4) {
-          rec.push_back(int32_t(xo | (yo << 16)));
-          rec.push_back(0);
-        }
-      const int re = int(rec.size() / 2);
-      if (re > rb) per_o[oo + M].push_back(Contrib{pi, rb, re});
+  }
+  return ok();
+}
+
+GenDims generic_dims(const Parsed& p, int table) {
+  if (table == E3_GEN_DX) return GenDims{p.dout, p.dy, p.dx, p.P};
+  if (table == E3_GEN_DW) return GenDims{p.dx, p.dy, p.P, p.dout};
+  return GenDims{p.dx, p.dy, p.dout, p.P};
+}
+
+e3_status build_generic(const e3_desc* desc, int table, std::vector<int32_t>& out) {
+  if (table != E3_GEN_FORWARD && table != E3_GEN_DX && table != E3_GEN_DW)
+    return fail(E3_ERR_INVALID_ARG, "unknown table");
+  Parsed p;
+  std::vector<GenEntry> ent;
+  e3_status s = generic_entries(desc, p, ent);
+  if (s != E3_OK) return s;
+  const GenDims dm = generic_dims(p, table);
+  auto key = [&](const GenEntry& e) { return table == E3_GEN_DX ? e.xi : table == E3_GEN_DW ? e.P : e.o; };
+  auto weight = [&](const GenEntry& e) { return table == E3_GEN_DW ? e.o : e.P; };
+  auto operand = [&](const GenEntry& e) { return table == E3_GEN_DX ? e.o : e.xi; };
+  // group by (key, weight), keeping the coefficient order within a group
+  std::stable_sort(ent.begin(), ent.end(), [&](const GenEntry& a, const GenEntry& b) {
+    return key(a) != key(b) ? key(a) < key(b) : weight(a) < weight(b);
+  });
+  struct Contrib {
+    int weight, rb, re;
+  };
+  std::vector<std::vector<Contrib>> per_key(dm.keys);
+  std::vector<int32_t> rec;
+  for (size_t i = 0; i < ent.size();) {
+    size_t j = i;
+    while (j < ent.size() && key(ent[j]) == key(ent[i]) && weight(ent[j]) == weight(ent[i])) ++j;
+    const int rb = int(rec.size() / 2);
+    for (size_t k = i; k < j; ++k) {
+      int32_t bits;
+      std::memcpy(&bits, &ent[k].c, 4);
+      rec.push_back(int32_t(operand(ent[k]) | (ent[k].yi << 16)));
+      rec.push_back(bits);
     }
+    while ((rec.size() / 2) % 4) {  // pad the run to whole groups of 4 (zero records)
+      rec.push_back(int32_t(operand(ent[i]) | (ent[i].yi << 16)));
+      rec.push_back(0);
+    }
+    per_key[key(ent[i])].push_back(Contrib{weight(ent[i]), rb, int(rec.size() / 2)});
+    i = j;
   }
   int n_contrib = 0;
-  for (auto& v : per_o) n_contrib += int(v.size());
+  for (auto& v : per_key) n_contrib += int(v.size());
   const size_t rec_words = rec.size();
-  size_t rec_off = size_t(e3k::kGenHeader) + p.dout + 1 + 3 * size_t(n_contrib);
+  size_t rec_off = size_t(e3k::kGenHeader) + dm.keys + 1 + 3 * size_t(n_contrib);
   rec_off = (rec_off + 7) / 8 * 8;  // records start on a 32-byte boundary
   out.assign(rec_off + rec_words, 0);
-  const int32_t head[e3k::kGenHeader] = {int32_t(e3k::kGenMagic), int32_t(p.dx), int32_t(p.dy),
-                                         int32_t(p.dout), int32_t(p.P), int32_t(n_contrib),
-                                         int32_t(rec_words / 2), int32_t(rec_off)};
+  const int32_t head[e3k::kGenHeader] = {int32_t(e3k::kGenMagic), int32_t(dm.operand),
+                                         int32_t(dm.y),           int32_t(dm.keys),
+                                         int32_t(dm.weights),     int32_t(n_contrib),
+                                         int32_t(rec_words / 2),  int32_t(rec_off)};
   for (int i = 0; i < e3k::kGenHeader; ++i) out[i] = head[i];
   size_t w = e3k::kGenHeader;
   int acc = 0;
-  for (int i = 0; i < p.dout; ++i) out[w++] = acc, acc += int(per_o[i].size());
+  for (int i = 0; i < dm.keys; ++i) out[w++] = acc, acc += int(per_key[i].size());
   out[w++] = acc;
-  for (auto& v : per_o)
-    for (auto& c : v) out[w++] = c.path, out[w++] = c.rb, out[w++] = c.re;
+  for (auto& v : per_key)
+    for (auto& c : v) out[w++] = c.weight, out[w++] = c.rb, out[w++] = c.re;
   std::copy(rec.begin(), rec.end(), out.begin() + rec_off);
   return ok();
 }
 
 }  // namespace
 
-e3_status e3_generic_plan_size(const e3_desc* desc, size_t* bytes) {
+e3_status e3_generic_plan_size(const e3_desc* desc, int32_t table, size_t* bytes) {
   if (!bytes) return fail(E3_ERR_INVALID_ARG, "bytes is null");
   std::vector<int32_t> t;
-  e3_status s = build_generic(desc, t);
+  e3_status s = build_generic(desc, table, t);
   if (s != E3_OK) return s;
   *bytes = t.size() * sizeof(int32_t);
   return ok();
 }
 
-e3_status e3_generic_plan_build(const e3_desc* desc, void* host_plan, size_t bytes) {
+e3_status e3_generic_plan_build(const e3_desc* desc, int32_t table, void* host_plan,
+                                size_t bytes) {
   if (!host_plan) return fail(E3_ERR_INVALID_ARG, "host_plan is null");
   std::vector<int32_t> t;
-  e3_status s = build_generic(desc, t);
+  e3_status s = build_generic(desc, table, t);
   if (s != E3_OK) return s;
   if (bytes < t.size() * sizeof(int32_t))
     return fail(E3_ERR_WORKSPACE, "plan needs " + std::to_string(t.size() * 4) + " bytes");
@@ -907,29 +957,82 @@ e3_status e3_generic_plan_build(const e3_desc* desc, void* host_plan, size_t byt
   return ok();
 }
 
-e3_status e3_tp_forward_generic(const e3_desc* desc, int64_t n_rows, const void* plan,
-                                size_t plan_bytes, const void* x, const float* y, const void* w,
-                                void* z, e3_dtype dtype, void* stream) {
-  Parsed p;
+namespace {
+
+e3_status generic_parse(const e3_desc* desc, e3_dtype dtype, Parsed& p) {
   e3_status s = parse(desc, p);
   if (s != E3_OK) return s;
   if (dtype != E3_F32 && dtype != E3_BF16) return fail(E3_ERR_INVALID_ARG, "unknown dtype");
   for (const auto* v : {&p.x, &p.y, &p.o})
     for (const auto& r : *v)
       if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 6");
-  if (p.dx * 64 + p.dy > 4096)
-    return fail(E3_ERR_UNSUPPORTED, "x has too many components for the generic kernel (dx <= 63)");
+  if (p.dx * 64 + p.dy > 4096 || p.dout * 64 + p.dy > 4096)
+    return fail(E3_ERR_UNSUPPORTED, "too many components for the generic kernel (dx, dout <= 63)");
+  return ok();
+}
+
+e3_status generic_table_ok(const void* plan, size_t bytes, const GenDims& dm) {
+  const size_t min_words = size_t(e3k::kGenHeader) + dm.keys + 1;
+  if (!plan || bytes < min_words * sizeof(int32_t) || (bytes % 4) != 0)
+    return fail(E3_ERR_WORKSPACE, "plan is missing or too short for this descriptor");
+  if (!aligned16(plan)) return fail(E3_ERR_ALIGNMENT, "plan must be 16-byte aligned");
+  return ok();
+}
+
+}  // namespace
+
+e3_status e3_tp_forward_generic(const e3_desc* desc, int64_t n_rows, const void* plan,
+                                size_t plan_bytes, const void* x, const float* y, const void* w,
+                                void* z, e3_dtype dtype, void* stream) {
+  Parsed p;
+  e3_status s = generic_parse(desc, dtype, p);
+  if (s != E3_OK) return s;
   if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
   if (n_rows == 0) return ok();
-  if (!plan || !x || !y || !w || !z) return fail(E3_ERR_INVALID_ARG, "null pointer");
-  const size_t min_words = size_t(e3k::kGenHeader) + p.dout + 1;
-  if (plan_bytes < min_words * sizeof(int32_t) || (plan_bytes % 4) != 0)
-    return fail(E3_ERR_WORKSPACE, "plan is too short for this descriptor");
-  if (!aligned16(plan)) return fail(E3_ERR_ALIGNMENT, "plan must be 16-byte aligned");
-  e3k::GenericTpArgs a{n_rows, p.C, p.dx, p.dy, p.dout, p.P, static_cast<const int*>(plan),
-                       int64_t(plan_bytes / 4), x, y, w, z};
+  if (!x || !y || !w || !z) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  const GenDims dm = generic_dims(p, E3_GEN_FORWARD);
+  if ((s = generic_table_ok(plan, plan_bytes, dm)) != E3_OK) return s;
+  e3k::GenericTpArgs a{n_rows, p.C, dm.operand, dm.y, dm.keys, dm.weights,
+                       static_cast<const int*>(plan), int64_t(plan_bytes / 4), x, y, w, z};
   return hip_status(e3k::launch_tp_generic(a, dtype == E3_BF16, hipStream_t(stream)),
                     "tp_forward_generic");
+}
+
+e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_fwd,
+                                 size_t fwd_bytes, const void* plan_dx, size_t dx_bytes,
+                                 const void* plan_dw, size_t dw_bytes, const void* x,
+                                 const float* y, const void* w, const void* dz, void* dx, void* dw,
+                                 float* dy, e3_dtype dtype, void* stream) {
+  Parsed p;
+  e3_status s = generic_parse(desc, dtype, p);
+  if (s != E3_OK) return s;
+  if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows == 0) return ok();
+  if (!x || !y || !w || !dz || !dx || !dw || !dy) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (p.dx + p.dout + p.dy > 256)  // the dy kernel's LDS: (dx + dout + dy) x 64 floats
+    return fail(E3_ERR_UNSUPPORTED, "dx + dout + dy must be <= 256 for the generic backward");
+  const GenDims df = generic_dims(p, E3_GEN_FORWARD), dxd = generic_dims(p, E3_GEN_DX),
+                dwd = generic_dims(p, E3_GEN_DW);
+  if ((s = generic_table_ok(plan_fwd, fwd_bytes, df)) != E3_OK ||
+      (s = generic_table_ok(plan_dx, dx_bytes, dxd)) != E3_OK ||
+      (s = generic_table_ok(plan_dw, dw_bytes, dwd)) != E3_OK)
+    return s;
+  const hipStream_t st = hipStream_t(stream);
+  const int bf = dtype == E3_BF16;
+  // dx: the dx table over dz, weights w
+  e3k::GenericTpArgs ax{n_rows, p.C, dxd.operand, dxd.y, dxd.keys, dxd.weights,
+                        static_cast<const int*>(plan_dx), int64_t(dx_bytes / 4), dz, y, w, dx};
+  if ((s = hip_status(e3k::launch_tp_generic(ax, bf, st), "tp_backward_generic")) != E3_OK)
+    return s;
+  // dw: the dw table over x, with dz as the per-"path" array
+  e3k::GenericTpArgs aw{n_rows, p.C, dwd.operand, dwd.y, dwd.keys, dwd.weights,
+                        static_cast<const int*>(plan_dw), int64_t(dw_bytes / 4), x, y, dz, dw};
+  if ((s = hip_status(e3k::launch_tp_generic(aw, bf, st), "tp_backward_generic")) != E3_OK)
+    return s;
+  // dy: summed over channels, from the forward table
+  e3k::GenericTpArgs ay{n_rows, p.C, df.operand, df.y, df.keys, df.weights,
+                        static_cast<const int*>(plan_fwd), int64_t(fwd_bytes / 4), x, y, w, nullptr};
+  return hip_status(e3k::launch_tp_generic_dy(ay, dz, dy, bf, st), "tp_backward_generic");
 }
 
 const char* e3_last_error(void) { return g_last_error.c_str(); }

@@ -106,6 +106,90 @@ __global__ void __launch_bounds__(64 * kGenWaves)
   }
 }
 
+// dy[yi] = sum over channels of sum_records w[P][c] c_r x[xi][c] dz[o][c]
+// (the channel-summed cotangent of y), from the forward table.  One
+// wavefront per row walks the channels 64 at a time; per-lane partial sums
+// sit in LDS and are added over the lanes in a fixed order at the end.
+template <class T>
+__global__ void __launch_bounds__(64)
+    k_tp_generic_dy(int64_t n_rows, int C, int dx, int dy, int dout, int np,
+                    const int* __restrict__ prog, int64_t n_words, const T* __restrict__ x,
+                    const T* __restrict__ w, const T* __restrict__ dz, float* __restrict__ dyo) {
+  int n_contrib = prog[5], n_rec = prog[6];
+  const int64_t rec_off = prog[7];
+  const int64_t fixed = kGenHeader + int64_t(dout) + 1;
+  if (n_contrib < 0 || n_rec < 0 || rec_off < fixed + 3 * int64_t(n_contrib) || (rec_off & 7) ||
+      rec_off + 2 * int64_t(n_rec) > n_words)
+    n_contrib = n_rec = 0;
+  const int* obeg = prog + kGenHeader;
+  const int* contrib = obeg + dout + 1;
+  const int4* rec4 = reinterpret_cast<const int4*>(prog + (n_rec ? rec_off : 0));
+  extern __shared__ float dsm[];
+  const int lane = threadIdx.x;
+  float* xs = dsm;              // [dx][64]
+  float* gs = xs + dx * 64;     // [dout][64]
+  float* acc = gs + dout * 64;  // [dy][64]
+  for (int64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
+    wave_lds_fence();
+    for (int i = 0; i < dy; ++i) acc[i * 64 + lane] = 0.0f;
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      const int c = c0 + lane;
+      const bool active = c < C;
+      wave_lds_fence();
+      for (int i = 0; i < dx; ++i) {
+        float v[1] = {0.0f};
+        if (active) load_ch<T, 1>(x + (row * dx + i) * C + c, v);
+        xs[i * 64 + lane] = v[0];
+      }
+      for (int i = 0; i < dout; ++i) {
+        float v[1] = {0.0f};
+        if (active) load_ch<T, 1>(dz + (row * dout + i) * C + c, v);
+        gs[i * 64 + lane] = v[0];
+      }
+      wave_lds_fence();
+      for (int o = 0; o < dout; ++o) {
+        const float g = gs[o * 64 + lane];
+        const int jb = max(obeg[o], 0), je = min(obeg[o + 1], n_contrib);
+        for (int j = jb; j < je; ++j) {
+          const int p = min(max(contrib[3 * j], 0), np - 1);
+          float wv[1] = {0.0f};
+          if (active) load_ch<T, 1>(w + (row * np + p) * C + c, wv);
+          const float wg = wv[0] * g;
+          const int gb = max(contrib[3 * j + 1], 0) >> 2, ge = min(contrib[3 * j + 2], n_rec) >> 2;
+          for (int gr = gb; gr < ge; ++gr) {
+            const int4 a = rec4[2 * gr], b = rec4[2 * gr + 1];
+            const int pk[4] = {a.x, a.z, b.x, b.z};
+            const int cb[4] = {a.y, a.w, b.y, b.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int xi = min(pk[q] & 0xffff, dx - 1);
+              const int yi = min(int(unsigned(pk[q]) >> 16), dy - 1);
+              float* t = acc + yi * 64 + lane;
+              *t = fmaf(__int_as_float(cb[q]) * xs[xi * 64 + lane], wg, *t);
+            }
+          }
+        }
+      }
+    }
+    wave_lds_fence();
+    for (int i = lane; i < dy; i += 64) {
+      float sum = 0.0f;
+      for (int k = 0; k < 64; ++k) sum += acc[i * 64 + k];
+      dyo[row * dy + i] = sum;
+    }
+  }
+}
+
+template <class T>
+hipError_t launch_dy(const GenericTpArgs& a, const void* dz, float* dyo, hipStream_t s) {
+  const size_t lds = size_t(a.dx + a.dout + a.dy) * 64 * sizeof(float);
+  const int64_t blocks = std::min<int64_t>(a.n_rows, 256 * 16);
+  hipLaunchKernelGGL(k_tp_generic_dy<T>, dim3(unsigned(blocks)), dim3(64), lds, s, a.n_rows, a.C,
+                     a.dx, a.dy, a.dout, a.np, a.prog, a.n_words, static_cast<const T*>(a.x),
+                     static_cast<const T*>(a.w), static_cast<const T*>(dz), dyo);
+  return hipGetLastError();
+}
+
 template <class T>
 hipError_t launch(const GenericTpArgs& a, hipStream_t s) {
   const size_t lds = size_t(kGenWaves) * (a.dx * 64 + a.dy) * sizeof(float);
@@ -123,6 +207,12 @@ hipError_t launch(const GenericTpArgs& a, hipStream_t s) {
 hipError_t launch_tp_generic(const GenericTpArgs& a, int bf16, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   return bf16 ? launch<bf16_t>(a, s) : launch<float>(a, s);
+}
+
+hipError_t launch_tp_generic_dy(const GenericTpArgs& a, const void* dz, float* dy, int bf16,
+                                hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  return bf16 ? launch_dy<bf16_t>(a, dz, dy, s) : launch_dy<float>(a, dz, dy, s);
 }
 
 }  // namespace e3k

@@ -110,6 +110,9 @@ struct GenericTpArgs {
   void* z;
 };
 hipError_t launch_tp_generic(const GenericTpArgs& a, int bf16, hipStream_t s);
+// dy of the generic tensor product from the forward table (a.z unused)
+hipError_t launch_tp_generic_dy(const GenericTpArgs& a, const void* dz, float* dy, int bf16,
+                                hipStream_t s);
 
 // Radial edge weights and the convolution that computes them on the fly
 // (radial.hip): 8 Bessel functions -> 64 SiLU units -> n_cols = P*C.

@@ -233,24 +233,37 @@ e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t 
                                  float* dvec, void* workspace, size_t ws_bytes, void* stream);
 
 /* Tensor product (as e3_tp_forward: e3j E.1 Eq.10-11, any channel-wise
- * signature, collapsed or per-path outputs) for irreps of degree up to 6,
- * driven by a coefficient table instead of a compiled kernel (e3j treats
- * the product as a bilinear coupling given by a sparse COO array of
- * coefficients, E.1 and B.1; Figs 5-6 run it to L = 6 and beyond).
- *   e3_generic_plan_size / e3_generic_plan_build: host-only; write the
- *     table for desc into a HOST buffer; the caller copies it to device
- *     memory it owns (16-byte aligned) and may reuse it for every call with
- *     the same descriptor.
- *   e3_tp_forward_generic: x [n][dx][C], y [n][dy] float32, w [n][P][C],
- *     z [n][dout][C]; fp32 or bf16 storage, fp32 accumulation.  Needs every
- *     degree <= 6 and dx*64 + dy <= 4096 (dx <= 63).  A table built for
- *     another descriptor gives wrong values but never an out-of-bounds
- *     access (every index read from it is clamped). */
-e3_status e3_generic_plan_size(const e3_desc* desc, size_t* bytes);
-e3_status e3_generic_plan_build(const e3_desc* desc, void* host_plan, size_t bytes);
+ * signature, collapsed or per-path outputs) and its backward (as
+ * e3_tp_backward, Eq.14-16) for irreps of degree up to 6, driven by
+ * coefficient tables instead of compiled kernels (e3j treats the product as
+ * a bilinear coupling given by a sparse COO array of coefficients, E.1 and
+ * B.1; Figs 5-6 run it to L = 6 and beyond).
+ *   e3_generic_plan_size / e3_generic_plan_build: host-only; write table
+ *     `table` (E3_GEN_FORWARD, E3_GEN_DX or E3_GEN_DW) for desc into a HOST
+ *     buffer; the caller copies it to device memory it owns (16-byte
+ *     aligned) and may reuse it for every call with the same descriptor.
+ *   e3_tp_forward_generic: the forward table; x [n][dx][C], y [n][dy]
+ *     float32, w [n][P][C], z [n][dout][C].
+ *   e3_tp_backward_generic: all three tables; for dz [n][dout][C] writes
+ *     dx [n][dx][C], dw [n][P][C] and dy [n][dy] (float32, summed over the
+ *     channels in a fixed order).
+ * fp32 or bf16 storage, fp32 accumulation.  Needs every degree <= 6 and
+ * dx*64 + dy, dout*64 + dy <= 4096 (dx, dout <= 63), and for the backward
+ * dx + dout + dy <= 256.  A table built for
+ * another descriptor gives wrong values but never an out-of-bounds access
+ * (every index read from it is clamped). */
+enum { E3_GEN_FORWARD = 0, E3_GEN_DX = 1, E3_GEN_DW = 2 };
+e3_status e3_generic_plan_size(const e3_desc* desc, int32_t table, size_t* bytes);
+e3_status e3_generic_plan_build(const e3_desc* desc, int32_t table, void* host_plan,
+                                size_t bytes);
 e3_status e3_tp_forward_generic(const e3_desc* desc, int64_t n_rows, const void* plan,
                                 size_t plan_bytes, const void* x, const float* y, const void* w,
                                 void* z, e3_dtype dtype, void* stream);
+e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_fwd,
+                                 size_t fwd_bytes, const void* plan_dx, size_t dx_bytes,
+                                 const void* plan_dw, size_t dw_bytes, const void* x,
+                                 const float* y, const void* w, const void* dz, void* dx, void* dw,
+                                 float* dy, e3_dtype dtype, void* stream);
 
 /* Per-node gradient from per-edge vector gradients, for r_e = pos[receiver]
  * - pos[sender]:

@@ -236,10 +236,11 @@ def test_generic_plan_table(lib):
     nat = [(l, 1 if l % 2 == 0 else -1) for l in range(5)]
     d = api.Desc(nat, nat, nat, 64)
     nb = C.c_size_t()
-    assert lib.e3_generic_plan_size(C.byref(d.c()), C.byref(nb)) == 0
+    assert lib.e3_generic_plan_size(C.byref(d.c()), 0, C.byref(nb)) == 0
     t = np.zeros(nb.value // 4, dtype=np.int32)
-    assert lib.e3_generic_plan_build(C.byref(d.c()), t.ctypes.data, nb.value - 4) == -6
-    assert lib.e3_generic_plan_build(C.byref(d.c()), t.ctypes.data, nb.value) == 0
+    assert lib.e3_generic_plan_build(C.byref(d.c()), 0, t.ctypes.data, nb.value - 4) == -6
+    assert lib.e3_generic_plan_build(C.byref(d.c()), 0, t.ctypes.data, nb.value) == 0
+    assert lib.e3_generic_plan_size(C.byref(d.c()), 3, C.byref(nb)) == -1
     dx = dy = dout = 25
     P, n_contrib, n_rec, rec_off = t[4], t[5], t[6], t[7]
     assert list(t[1:4]) == [dx, dy, dout] and P == api.num_paths(d) == 42
@@ -265,8 +266,18 @@ def test_generic_plan_table(lib):
                 if c != 0.0:
                     assert c == pytest.approx(T[o - offs[io], xi - offs[ix], yi - offs[iy]],
                                               abs=1e-7)
+    # the dx and dw tables hold the same coefficients, keyed differently
+    for table in (1, 2):
+        assert lib.e3_generic_plan_size(C.byref(d.c()), table, C.byref(nb)) == 0
+        u = np.zeros(nb.value // 4, dtype=np.int32)
+        assert lib.e3_generic_plan_build(C.byref(d.c()), table, u.ctypes.data, nb.value) == 0
+        r = u[u[7]:u[7] + 2 * u[6]].reshape(-1, 2)[:, 1].copy().view(np.float32)
+        assert np.count_nonzero(r) == 1158
+        assert np.isclose(np.sort(np.abs(r[r != 0])).sum(), np.sort(np.abs(coef[coef != 0])).sum())
+    assert lib.e3_tp_backward_generic(C.byref(d.c()), 0, None, 0, None, 0, None, 0, None, None,
+                                      None, None, None, None, None, 0, None) == 0
     big = api.Desc([(7, 1)], [(0, 1)], [(7, 1)], 64)
-    assert lib.e3_generic_plan_size(C.byref(big.c()), C.byref(nb)) == -3
+    assert lib.e3_generic_plan_size(C.byref(big.c()), 0, C.byref(nb)) == -3
     assert lib.e3_tp_forward_generic(C.byref(d.c()), 0, None, 0, None, None, None, None, 0,
                                      None) == 0
     fake = C.c_void_p(0x10000)

@@ -1,4 +1,5 @@
-"""GPU parity of the coefficient-table tensor product (e3_tp_forward_generic)
+"""GPU parity of the coefficient-table tensor product (e3_tp_forward_generic,
+e3_tp_backward_generic)
 through the C ABI, against the fp64 oracle, at the degrees of e3j's
 tensor-product benchmarks (B.1 Figs 5-6: every irrep 0..L once, natural
 parity for the symmetric paths, (-1)^(l+1) for the skew-symmetric ones,
@@ -103,3 +104,51 @@ def test_generic_tp_full_size_sampled(gpu):
     rows = np.sort(np.random.default_rng(4).choice(32768, 60, replace=False))
     ref = O.tp_forward(od, x, y, w, rows=rows)
     assert_close(host(z)[rows], ref, TOL_F32, "generic tp L=6 sampled")
+
+
+# ----------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("L,skew,C", [(2, False, 64), (4, False, 128), (6, False, 128),
+                                      (5, True, 96)])
+def test_generic_tp_backward_matches_oracle(gpu, L, skew, C):
+    d, od, x, y, w = _case(L, C, 61, 360 + L, skew)
+    dz = np.random.default_rng(361 + L).standard_normal((61, d.dout, C)).astype(np.float32)
+    dx, dw, dy = gpu.tp_backward_generic(d, dev(x), dev(y), dev(w), dev(dz))
+    torch.cuda.synchronize()
+    rdx, rdw, rdy = O.tp_backward(od, x, y, w, dz)
+    for k, a, b in (("dx", dx, rdx), ("dw", dw, rdw), ("dy", dy, rdy)):
+        assert_close(host(a), b, TOL_F32, f"generic tp backward L={L} skew={skew}:{k}")
+
+
+def test_generic_tp_backward_per_path_and_bf16(gpu):
+    from tests.gpu_util import S
+    d, od, x, y, w = _case(2, 64, 40, 370, per_path=True)
+    dz = np.random.default_rng(371).standard_normal((40, d.dout, 64)).astype(np.float32)
+    got = gpu.tp_backward_generic(d, dev(x), dev(y), dev(w), dev(dz))
+    torch.cuda.synchronize()
+    for k, a, b in zip(("dx", "dw", "dy"), got, O.tp_backward(od, x, y, w, dz)):
+        assert_close(host(a), b, TOL_F32, f"generic tp backward per path:{k}")
+    d, od, x, y, w = _case(4, 128, 50, 372)
+    dz = np.random.default_rng(373).standard_normal((50, d.dout, 128)).astype(np.float32)
+    x, w, dz = S.round_bf16(x), S.round_bf16(w), S.round_bf16(dz)
+    got = gpu.tp_backward_generic(d, dev(x, "bf16"), dev(y), dev(w, "bf16"), dev(dz, "bf16"))
+    torch.cuda.synchronize()
+    for k, a, b in zip(("dx", "dw", "dy"), got, O.tp_backward(od, x, y, w, dz)):
+        assert_close(host(a), b, TOL_BF16, f"generic tp backward bf16:{k}", bf16_out=k != "dy")
+
+
+def test_generic_tp_backward_equals_compiled_kernel(gpu):
+    from clebsch_gordan_tensor_amd import api
+    xi, yi, oi = _irreps(2), _irreps(3), _irreps(3)
+    d = api.Desc(xi, yi, oi, 128)
+    rng = np.random.default_rng(380)
+    B = 700
+    x = dev(rng.standard_normal((B, d.dx, 128)).astype(np.float32))
+    y = dev(O.sh(3, rng.standard_normal((B, 3))).astype(np.float32))
+    w = dev(rng.standard_normal((B, api.num_paths(d), 128)).astype(np.float32))
+    dz = dev(rng.standard_normal((B, d.dout, 128)).astype(np.float32))
+    a = gpu.tp_backward_generic(d, x, y, w, dz)
+    b = gpu.tp_backward(d, x, y, w, dz)
+    torch.cuda.synchronize()
+    for k, u, v in zip(("dx", "dw", "dy"), a, b):
+        assert_close(host(u), host(v).astype(np.float64), 2 * TOL_F32, f"generic vs compiled:{k}")
