@@ -245,7 +245,7 @@ e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out) {
 
 e3_status e3_spherical_harmonics(int32_t lmax, int64_t n, const float* vec, float* Y,
                                  void* stream) {
-  if (lmax < 0 || lmax > 3) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..3");
+  if (lmax < 0 || lmax > 6) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..6");
   if (n < 0) return fail(E3_ERR_INVALID_ARG, "n < 0");
   if (n == 0) return ok();
   if (!vec || !Y) return fail(E3_ERR_INVALID_ARG, "null pointer");

@@ -15,6 +15,7 @@
 #include <cstdint>
 
 #include "common.h"
+#include "harmonics_hi.h"
 #include "registry.h"
 
 namespace e3k {
@@ -310,7 +311,7 @@ __global__ void __launch_bounds__(256)
     float x = vec[3 * i], y = vec[3 * i + 1], z = vec[3 * i + 2];
     unit_vector(x, y, z);
     float h[D];
-    sfor<0, LMAX + 1>([&](auto l) { harmonics_l<l>(x, y, z, h + l * l); });
+    harmonics_bank<LMAX>(x, y, z, h);
 #pragma unroll
     for (int k = 0; k < D; ++k) Y[i * D + k] = h[k];
   }
@@ -577,6 +578,9 @@ hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hip
     case 1: hipLaunchKernelGGL(k_harmonics<1>, g, b, 0, s, n, vec, Y); break;
     case 2: hipLaunchKernelGGL(k_harmonics<2>, g, b, 0, s, n, vec, Y); break;
     case 3: hipLaunchKernelGGL(k_harmonics<3>, g, b, 0, s, n, vec, Y); break;
+    case 4: hipLaunchKernelGGL(k_harmonics<4>, g, b, 0, s, n, vec, Y); break;
+    case 5: hipLaunchKernelGGL(k_harmonics<5>, g, b, 0, s, n, vec, Y); break;
+    case 6: hipLaunchKernelGGL(k_harmonics<6>, g, b, 0, s, n, vec, Y); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

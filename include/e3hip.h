@@ -124,7 +124,9 @@ int32_t e3_supported(const e3_desc* desc, e3_dtype dtype);
  * built from; e3j G.2 construction). */
 e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out);
 
-/* Harmonics Y[n][(lmax+1)^2] of vec[n][3] (e3j A.3 Eq.4), lmax <= 3. */
+/* Harmonics Y[n][(lmax+1)^2] of vec[n][3] (e3j A.3 Eq.4), lmax <= 6: degrees
+ * 0..3 from their closed forms, 4..6 by the coupling of Y_1 and Y_{L-1}
+ * (Gaunt relation; recursion records generated and checked at build time). */
 e3_status e3_spherical_harmonics(int32_t lmax, int64_t n, const float* vec, float* Y,
                                  void* stream);
 

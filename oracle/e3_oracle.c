@@ -190,6 +190,10 @@ int oracle_cg_real(int l1, int l2, int L, double *out) {
 int oracle_sh_general(int l, const double r[3], double *out) {
   if (l < 0 || l > ORACLE_MAX_L) return -1;
   double n = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+  if (n == 0.0) { /* no direction: 1 at l = 0, zeros above (as the closed forms) */
+    for (int m = 0; m < 2 * l + 1; ++m) out[m] = (l == 0) ? 1.0 : 0.0;
+    return 0;
+  }
   double x = 0, y = 0, z = 0;
   if (n > 0) {
     x = r[0] / n;
@@ -229,7 +233,7 @@ int oracle_sh_general(int l, const double r[3], double *out) {
 /* Component-normalised real harmonics of the unit vector r/|r|, written out
  * as polynomials for l <= 3, by oracle_sh_general above for l = 4..6.
  * out has 2l+1 entries, m = -l..l.  A zero vector yields the l = 0 value
- * only (higher degrees are 0, except Y_l0 of the general form at z = 0). */
+ * only (higher degrees are 0). */
 int oracle_sh_l(int l, const double r[3], double *out) {
   double n = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
   double x = 0, y = 0, z = 0;

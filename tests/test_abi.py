@@ -130,7 +130,7 @@ def test_error_codes(lib):
                                None) == -1  # unknown dtype
     assert lib.e3_tp_forward(_desc_c(good), 0, None, None, None, None, 0, None) == 0
     assert lib.e3_tp_forward(_desc_c(good), -2, None, None, None, None, 0, None) == -1
-    assert lib.e3_spherical_harmonics(4, 10, fake, fake, None) == -1
+    assert lib.e3_spherical_harmonics(7, 10, fake, fake, None) == -1
     assert lib.e3_spherical_harmonics(2, 0, None, None, None) == 0
     sz = C.c_size_t()
     assert lib.e3_conv_workspace_size(10, 100, C.byref(sz)) == 0

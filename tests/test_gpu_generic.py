@@ -152,3 +152,20 @@ def test_generic_tp_backward_equals_compiled_kernel(gpu):
     torch.cuda.synchronize()
     for k, u, v in zip(("dx", "dw", "dy"), a, b):
         assert_close(host(u), host(v).astype(np.float64), 2 * TOL_F32, f"generic vs compiled:{k}")
+
+
+# ---------------------------------------------------- harmonics up to degree 6
+
+def test_harmonics_to_degree_six_match_oracle(gpu):
+    # the library builds degrees 4..6 by coupling Y_1 with Y_{L-1} (Gaunt
+    # relation); the oracle by the Legendre construction
+    rng = np.random.default_rng(390)
+    v = (rng.standard_normal((5001, 3)) * rng.uniform(0.1, 10, (5001, 1))).astype(np.float32)
+    v[7] = 0.0
+    v[8] = [0.0, 0.0, 3.0]
+    Y = host(gpu.spherical_harmonics(6, dev(v)))
+    ref = O.sh(6, v)
+    for l in range(7):
+        sl = slice(l * l, (l + 1) * (l + 1))
+        assert_close(Y[:, sl], ref[:, sl], TOL_F32, f"harmonics l={l}")
+    assert np.all(Y[7, 1:] == 0.0) and Y[7, 0] == 1.0

@@ -128,3 +128,8 @@ def test_gaunt_identity_high_degree():
         v = np.einsum("Mij,ni,nj->nM", T, Y[:, OFF[l1]:OFF[l1 + 1]], Y[:, OFF[l2]:OFF[l2 + 1]])
         np.testing.assert_allclose(v, kappa * Y[:, OFF[L]:OFF[L + 1]], atol=1e-10,
                                    err_msg=str((l1, l2, L)))
+
+
+def test_zero_vector_high_degree():
+    Y = O.sh(6, np.zeros((1, 3)))[0]
+    assert Y[0] == 1.0 and np.all(Y[1:] == 0.0)
