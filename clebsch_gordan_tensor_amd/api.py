@@ -49,8 +49,9 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_conv_double_backward", "e3_radial_mlp", "e3_conv_forward_radial",
            "e3_radial_mlp_backward_workspace_size", "e3_radial_mlp_backward",
            "e3_generic_plan_size", "e3_generic_plan_build", "e3_tp_forward_generic",
-           "e3_tp_backward_generic", "e3_last_error"]
-E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW = 0, 1, 2
+           "e3_tp_backward_generic", "e3_conv_forward_generic", "e3_conv_backward_generic",
+           "e3_last_error"]
+E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY = 0, 1, 2, 3
 
 
 class _CRadial(C.Structure):
@@ -90,6 +91,10 @@ def lib():
     L.e3_tp_backward_generic.argtypes = [dp, i64, vp, sz, vp, sz, vp, sz, vp, vp, vp, vp, vp, vp,
                                          vp, C.c_int, vp]
     L.e3_tp_forward_generic.argtypes = [dp, i64, vp, sz, vp, vp, vp, vp, C.c_int, vp]
+    L.e3_conv_forward_generic.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, sz, vp, vp, vp, vp,
+                                          C.c_int, vp]
+    L.e3_conv_backward_generic.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, sz, vp, sz, vp, sz,
+                                           vp, vp, vp, vp, vp, vp, vp, C.c_int, vp]
     L.e3_radial_mlp_backward_workspace_size.argtypes = [C.POINTER(_CRadial), i32, i32,
                                                         C.POINTER(sz)]
     L.e3_radial_mlp_backward.argtypes = [C.POINTER(_CRadial), i32, i32, vp, vp, vp, vp, vp, vp,
@@ -554,8 +559,8 @@ _GENERIC_PLANS = {}
 
 
 def generic_plan(desc: Desc, device, table=0):
-    """Coefficient table `table` (E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW) of the
-    generic tensor product for desc: built on the host by the library, copied
+    """Coefficient table `table` (E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW,
+    E3_GEN_DY) of the generic tensor product for desc: built on the host by the library, copied
     to device memory once per descriptor."""
     import numpy as np
     import torch
@@ -598,11 +603,69 @@ def tp_backward_generic(desc: Desc, x, y, w, dz, stream=None):
     _need(y, "y", shape=(B, desc.dy), dtype=torch.float32)
     _need(w, "w", shape=(B, P, desc.channels), dtype=x.dtype)
     _need(dz, "dz", shape=(B, desc.dout, desc.channels), dtype=x.dtype)
-    pf, px, pw = (generic_plan(desc, x.device, t) for t in (E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW))
+    px, pw, py = (generic_plan(desc, x.device, t) for t in (E3_GEN_DX, E3_GEN_DW, E3_GEN_DY))
     dx, dw = torch.empty_like(x), torch.empty_like(w)
     dy = torch.empty((B, desc.dy), device=x.device, dtype=torch.float32)
     _check(lib().e3_tp_backward_generic(
-        C.byref(desc.c()), B, _ptr(pf), pf.numel() * 4, _ptr(px), px.numel() * 4, _ptr(pw),
-        pw.numel() * 4, _ptr(x), _ptr(y), _ptr(w), _ptr(dz), _ptr(dx), _ptr(dw), _ptr(dy),
+        C.byref(desc.c()), B, _ptr(px), px.numel() * 4, _ptr(pw), pw.numel() * 4, _ptr(py),
+        py.numel() * 4, _ptr(x), _ptr(y), _ptr(w), _ptr(dz), _ptr(dx), _ptr(dw), _ptr(dy),
         _dtype_code(x), _stream(stream)))
     return dx, dw, dy
+
+
+def conv_forward_generic(desc: Desc, rowptr, sender, edge_vec_or_Y, x, w, out=None,
+                         workspace=None, stream=None):
+    """m = conv(x, Y(edge_vec), w) (as conv_forward) through the
+    coefficient-table kernels: any signature with degrees up to 6."""
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    P = num_paths(desc)
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    ycols = desc.dy if desc.flags & E3_Y_GIVEN else 3
+    _need(edge_vec_or_Y, "edge_vec_or_Y", shape=(E, ycols), dtype=torch.float32)
+    _need(x, "x", shape=(N, desc.dx, desc.channels))
+    _need(w, "w", shape=(E, P, desc.channels), dtype=x.dtype)
+    if out is None:
+        out = torch.empty((N, desc.dout, desc.channels), device=x.device, dtype=x.dtype)
+    _need(out, "out", shape=(N, desc.dout, desc.channels), dtype=x.dtype)
+    plan = generic_plan(desc, x.device, E3_GEN_FORWARD)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().e3_conv_forward_generic(
+        C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender), _ptr(workspace), wsb, _ptr(plan),
+        plan.numel() * 4, _ptr(edge_vec_or_Y), _ptr(x), _ptr(w), _ptr(out), _dtype_code(x),
+        _stream(stream)))
+    return out
+
+
+def conv_backward_generic(desc: Desc, rowptr, sender, workspace, edge_vec_or_Y, x, w, dm,
+                          dx=None, dw=None, dY=None, stream=None):
+    """(dx, dw, dY) of conv_forward_generic for the cotangent dm; workspace
+    from conv_prepare_transpose on the same graph."""
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    P = num_paths(desc)
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    ycols = desc.dy if desc.flags & E3_Y_GIVEN else 3
+    _need(edge_vec_or_Y, "edge_vec_or_Y", shape=(E, ycols), dtype=torch.float32)
+    _need(x, "x", shape=(N, desc.dx, desc.channels))
+    _need(w, "w", shape=(E, P, desc.channels), dtype=x.dtype)
+    _need(dm, "dm", shape=(N, desc.dout, desc.channels), dtype=x.dtype)
+    dev, dt = x.device, x.dtype
+    if dx is None:
+        dx = torch.empty((N, desc.dx, desc.channels), device=dev, dtype=dt)
+    if dw is None:
+        dw = torch.empty((E, P, desc.channels), device=dev, dtype=dt)
+    if dY is None:
+        dY = torch.empty((E, desc.dy), device=dev, dtype=torch.float32)
+    _need(dx, "dx", shape=(N, desc.dx, desc.channels), dtype=dt)
+    _need(dw, "dw", shape=(E, P, desc.channels), dtype=dt)
+    _need(dY, "dY", shape=(E, desc.dy), dtype=torch.float32)
+    px, pw, py = (generic_plan(desc, x.device, t) for t in (E3_GEN_DX, E3_GEN_DW, E3_GEN_DY))
+    _check(lib().e3_conv_backward_generic(
+        C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(px), px.numel() * 4, _ptr(pw),
+        pw.numel() * 4, _ptr(py), py.numel() * 4, _ptr(edge_vec_or_Y), _ptr(x), _ptr(w), _ptr(dm),
+        _ptr(dx), _ptr(dw), _ptr(dY), _dtype_code(x), _stream(stream)))
+    return dx, dw, dY

@@ -813,17 +813,17 @@ e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t 
 
 namespace {
 
-// Coefficient table of the generic tensor product (layout in
-// kernels/generic.hip), from the ladder-built real CG blocks.
-// The three tables of a descriptor (layout in kernels/generic.hip).  Every
-// nonzero coefficient c of path P couples output component o, x component
-// xi and y component yi; a table keys the entries by what the kernel writes
-// and names which array acts as its per-lane operand ("x") and which as its
-// per-path scalar array ("w"):
-//   forward  z[o]  = sum_P w[P]  sum c y[yi] x[xi]     key o,  weight P, operand xi
-//   dx       dx[xi] = sum_P w[P]  sum c y[yi] dz[o]    key xi, weight P, operand o
-//   dw       dw[P]  = sum_o dz[o] sum c y[yi] x[xi]    key P,  weight o, operand xi
-// (e3j E.1 Eq.14-15: each cotangent is the same bilinear form with the
+// The coefficient tables of a descriptor (layout in kernels/generic.hip),
+// from the ladder-built real CG blocks.  Every nonzero coefficient c of
+// path P couples output component o, x component xi and y component yi; a
+// table keys the entries by what the kernel writes and names which array
+// acts as its per-lane operand, which as its per-row weight and which as
+// its second factor (the y slot of a record):
+//   forward  z[o]   = sum_P w[P]  sum c y[yi] x[xi]    key o,  weight P, operand xi, y yi
+//   dx       dx[xi] = sum_P w[P]  sum c y[yi] dz[o]    key xi, weight P, operand o,  y yi
+//   dw       dw[P]  = sum_o dz[o] sum c y[yi] x[xi]    key P,  weight o, operand xi, y yi
+//   dy       dy[yi] = sum_P w[P]  sum c dz[o] x[xi]    key yi, weight P, operand xi, y o
+// (e3j E.1 Eq.14-16: each cotangent is the same coupling with the
 // coefficient records permuted.)
 struct GenEntry {
   int P, o, xi, yi;
@@ -873,20 +873,24 @@ e3_status generic_entries(const e3_desc* desc, Parsed& p, std::vector<GenEntry>&
 GenDims generic_dims(const Parsed& p, int table) {
   if (table == E3_GEN_DX) return GenDims{p.dout, p.dy, p.dx, p.P};
   if (table == E3_GEN_DW) return GenDims{p.dx, p.dy, p.P, p.dout};
+  if (table == E3_GEN_DY) return GenDims{p.dx, p.dout, p.dy, p.P};
   return GenDims{p.dx, p.dy, p.dout, p.P};
 }
 
 e3_status build_generic(const e3_desc* desc, int table, std::vector<int32_t>& out) {
-  if (table != E3_GEN_FORWARD && table != E3_GEN_DX && table != E3_GEN_DW)
+  if (table != E3_GEN_FORWARD && table != E3_GEN_DX && table != E3_GEN_DW && table != E3_GEN_DY)
     return fail(E3_ERR_INVALID_ARG, "unknown table");
   Parsed p;
   std::vector<GenEntry> ent;
   e3_status s = generic_entries(desc, p, ent);
   if (s != E3_OK) return s;
   const GenDims dm = generic_dims(p, table);
-  auto key = [&](const GenEntry& e) { return table == E3_GEN_DX ? e.xi : table == E3_GEN_DW ? e.P : e.o; };
+  auto key = [&](const GenEntry& e) {
+    return table == E3_GEN_DX ? e.xi : table == E3_GEN_DW ? e.P : table == E3_GEN_DY ? e.yi : e.o;
+  };
   auto weight = [&](const GenEntry& e) { return table == E3_GEN_DW ? e.o : e.P; };
   auto operand = [&](const GenEntry& e) { return table == E3_GEN_DX ? e.o : e.xi; };
+  auto second = [&](const GenEntry& e) { return table == E3_GEN_DY ? e.o : e.yi; };
   // group by (key, weight), keeping the coefficient order within a group
   std::stable_sort(ent.begin(), ent.end(), [&](const GenEntry& a, const GenEntry& b) {
     return key(a) != key(b) ? key(a) < key(b) : weight(a) < weight(b);
@@ -903,11 +907,11 @@ e3_status build_generic(const e3_desc* desc, int table, std::vector<int32_t>& ou
     for (size_t k = i; k < j; ++k) {
       int32_t bits;
       std::memcpy(&bits, &ent[k].c, 4);
-      rec.push_back(int32_t(operand(ent[k]) | (ent[k].yi << 16)));
+      rec.push_back(int32_t(operand(ent[k]) | (second(ent[k]) << 16)));
       rec.push_back(bits);
     }
     while ((rec.size() / 2) % 4) {  // pad the run to whole groups of 4 (zero records)
-      rec.push_back(int32_t(operand(ent[i]) | (ent[i].yi << 16)));
+      rec.push_back(int32_t(operand(ent[i]) | (second(ent[i]) << 16)));
       rec.push_back(0);
     }
     per_key[key(ent[i])].push_back(Contrib{weight(ent[i]), rb, int(rec.size() / 2)});
@@ -998,9 +1002,9 @@ e3_status e3_tp_forward_generic(const e3_desc* desc, int64_t n_rows, const void*
                     "tp_forward_generic");
 }
 
-e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_fwd,
-                                 size_t fwd_bytes, const void* plan_dx, size_t dx_bytes,
-                                 const void* plan_dw, size_t dw_bytes, const void* x,
+e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_dx,
+                                 size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+                                 const void* plan_dy, size_t dy_bytes, const void* x,
                                  const float* y, const void* w, const void* dz, void* dx, void* dw,
                                  float* dy, e3_dtype dtype, void* stream) {
   Parsed p;
@@ -1009,13 +1013,11 @@ e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void
   if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
   if (n_rows == 0) return ok();
   if (!x || !y || !w || !dz || !dx || !dw || !dy) return fail(E3_ERR_INVALID_ARG, "null pointer");
-  if (p.dx + p.dout + p.dy > 256)  // the dy kernel's LDS: (dx + dout + dy) x 64 floats
-    return fail(E3_ERR_UNSUPPORTED, "dx + dout + dy must be <= 256 for the generic backward");
-  const GenDims df = generic_dims(p, E3_GEN_FORWARD), dxd = generic_dims(p, E3_GEN_DX),
+  const GenDims dyd = generic_dims(p, E3_GEN_DY), dxd = generic_dims(p, E3_GEN_DX),
                 dwd = generic_dims(p, E3_GEN_DW);
-  if ((s = generic_table_ok(plan_fwd, fwd_bytes, df)) != E3_OK ||
-      (s = generic_table_ok(plan_dx, dx_bytes, dxd)) != E3_OK ||
-      (s = generic_table_ok(plan_dw, dw_bytes, dwd)) != E3_OK)
+  if ((s = generic_table_ok(plan_dx, dx_bytes, dxd)) != E3_OK ||
+      (s = generic_table_ok(plan_dw, dw_bytes, dwd)) != E3_OK ||
+      (s = generic_table_ok(plan_dy, dy_bytes, dyd)) != E3_OK)
     return s;
   const hipStream_t st = hipStream_t(stream);
   const int bf = dtype == E3_BF16;
@@ -1029,10 +1031,121 @@ e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void
                         static_cast<const int*>(plan_dw), int64_t(dw_bytes / 4), x, y, dz, dw};
   if ((s = hip_status(e3k::launch_tp_generic(aw, bf, st), "tp_backward_generic")) != E3_OK)
     return s;
-  // dy: summed over channels, from the forward table
-  e3k::GenericTpArgs ay{n_rows, p.C, df.operand, df.y, df.keys, df.weights,
-                        static_cast<const int*>(plan_fwd), int64_t(fwd_bytes / 4), x, y, w, nullptr};
+  // dy: summed over channels, from the table keyed by the y component
+  e3k::GenericTpArgs ay{n_rows, p.C, p.dx, p.dy, p.dout, p.P,
+                        static_cast<const int*>(plan_dy), int64_t(dy_bytes / 4), x, nullptr, w,
+                        nullptr};
   return hip_status(e3k::launch_tp_generic_dy(ay, dz, dy, bf, st), "tp_backward_generic");
+}
+
+namespace {
+
+// How the convolution gets its y operand: the given rows (E3_Y_GIVEN, ly =
+// -1) or the harmonics of the edge vectors, one bank per y irrep (ly = the
+// highest degree; ym maps each y component to the harmonic l*l + m).
+e3_status generic_y_source(const e3_desc* desc, const Parsed& p, int& ly, e3k::YMap& ym) {
+  ly = -1;
+  std::memset(&ym, 0xff, sizeof ym);
+  if (desc->flags & E3_Y_GIVEN) return ok();
+  if (p.dy > 64)
+    return fail(E3_ERR_UNSUPPORTED, "harmonics from edge vectors need dy <= 64; use E3_Y_GIVEN");
+  int i = 0;
+  ly = 0;
+  for (const auto& r : p.y) {
+    ly = std::max(ly, r.l);
+    for (int m = 0; m < 2 * r.l + 1; ++m) ym.idx[i++] = static_cast<signed char>(r.l * r.l + m);
+  }
+  return ok();
+}
+
+// The graph arguments shared by both passes.
+e3_status generic_graph(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                        const int32_t* sender, const float* yv) {
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes > 0 && !rowptr) return fail(E3_ERR_INVALID_ARG, "rowptr is null");
+  if (n_edges > 0 && (!sender || !yv)) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  return ok();
+}
+
+}  // namespace
+
+e3_status e3_conv_forward_generic(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                  const int32_t* rowptr, const int32_t* sender,
+                                  const void* workspace, size_t ws_bytes, const void* plan,
+                                  size_t plan_bytes, const float* edge_vec_or_Y, const void* x,
+                                  const void* w, void* m, e3_dtype dtype, void* stream) {
+  Parsed p;
+  e3_status s = generic_parse(desc, dtype, p);
+  if (s != E3_OK) return s;
+  int ly;
+  e3k::YMap ym;
+  if ((s = generic_y_source(desc, p, ly, ym)) != E3_OK) return s;
+  if ((s = generic_graph(n_nodes, n_edges, rowptr, sender, edge_vec_or_Y)) != E3_OK) return s;
+  if (n_nodes == 0) return ok();
+  if (!x || !m || (n_edges > 0 && !w)) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  const GenDims dm = generic_dims(p, E3_GEN_FORWARD);
+  if ((s = generic_table_ok(plan, plan_bytes, dm)) != E3_OK) return s;
+  const int* order = nullptr;
+  if (workspace) {
+    size_t need = 0;
+    e3_conv_workspace_size(n_nodes, n_edges, &need);
+    if (ws_bytes < need)
+      return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+    order = static_cast<const int*>(workspace) + e3k::transpose_layout(n_nodes, n_edges).order;
+  }
+  e3k::GenericConvArgs a{n_nodes, n_edges, p.C, p.dx, p.dy, p.dout, p.P,
+                         static_cast<const int*>(plan), int64_t(plan_bytes / 4), order, rowptr,
+                         nullptr, sender, edge_vec_or_Y, ly, ym, x, w, m};
+  return hip_status(e3k::launch_conv_generic_seg(a, dtype == E3_BF16, hipStream_t(stream)),
+                    "conv_forward_generic");
+}
+
+e3_status e3_conv_backward_generic(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                   const int32_t* rowptr, const int32_t* sender,
+                                   const void* workspace, size_t ws_bytes, const void* plan_dx,
+                                   size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+                                   const void* plan_dy, size_t dy_bytes,
+                                   const float* edge_vec_or_Y, const void* x, const void* w,
+                                   const void* dm, void* dx, void* dw, float* dY, e3_dtype dtype,
+                                   void* stream) {
+  Parsed p;
+  e3_status s = generic_parse(desc, dtype, p);
+  if (s != E3_OK) return s;
+  int ly;
+  e3k::YMap ym;
+  if ((s = generic_y_source(desc, p, ly, ym)) != E3_OK) return s;
+  if ((s = generic_graph(n_nodes, n_edges, rowptr, sender, edge_vec_or_Y)) != E3_OK) return s;
+  if (n_nodes == 0) return ok();
+  size_t need = 0;
+  e3_conv_workspace_size(n_nodes, n_edges, &need);
+  if (!workspace || ws_bytes < need)
+    return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  if (!x || !dm || !dx || (n_edges > 0 && (!w || !dw || !dY)))
+    return fail(E3_ERR_INVALID_ARG, "null pointer");
+  const GenDims dxd = generic_dims(p, E3_GEN_DX), dwd = generic_dims(p, E3_GEN_DW),
+                dyd = generic_dims(p, E3_GEN_DY);
+  if ((s = generic_table_ok(plan_dx, dx_bytes, dxd)) != E3_OK ||
+      (s = generic_table_ok(plan_dw, dw_bytes, dwd)) != E3_OK ||
+      (s = generic_table_ok(plan_dy, dy_bytes, dyd)) != E3_OK)
+    return s;
+  const e3k::TransposeLayout L = e3k::transpose_layout(n_nodes, n_edges);
+  const int* ws = static_cast<const int*>(workspace);
+  const hipStream_t st = hipStream_t(stream);
+  const int bf = dtype == E3_BF16;
+  // dx: per sender over its out-edges (sender-ordered index), operand dm[receiver]
+  e3k::GenericConvArgs ax{n_nodes, n_edges, p.C, p.dout, p.dy, p.dx, p.P,
+                          static_cast<const int*>(plan_dx), int64_t(dx_bytes / 4), ws + L.order,
+                          ws + L.colptr, ws + L.perm, ws + L.recv, edge_vec_or_Y, ly, ym, dm, w,
+                          dx};
+  if ((s = hip_status(e3k::launch_conv_generic_seg(ax, bf, st), "conv_backward_generic")) != E3_OK)
+    return s;
+  // dw and dY: per edge, receiver by receiver
+  e3k::GenericConvEdgeArgs ae{n_nodes, n_edges, p.C, p.dx, p.dy, p.dout, p.P,
+                              static_cast<const int*>(plan_dw), int64_t(dw_bytes / 4),
+                              static_cast<const int*>(plan_dy), int64_t(dy_bytes / 4),
+                              ws + L.order, rowptr, sender, edge_vec_or_Y, ly, ym, x, w, dm, dw,
+                              dY};
+  return hip_status(e3k::launch_conv_generic_edge(ae, bf, st), "conv_backward_generic");
 }
 
 const char* e3_last_error(void) { return g_last_error.c_str(); }

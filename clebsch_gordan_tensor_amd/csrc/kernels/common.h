@@ -475,6 +475,23 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Sum of v over the 64 lanes of a wavefront, returned in every lane:
+// halves (swap32), 16-lane rows (swap16), then row mirror, half-row mirror
+// and the two quad permutations.  Fixed pairing order: bitwise reproducible.
+__device__ __forceinline__ float wave_sum(float v) {
+  float a = v, b = v;
+  swap32(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  swap16(a, b);
+  v = a + b;
+  v = v + dpp<0x140>(v);
+  v = v + dpp<0x141>(v);
+  v = v + dpp<0x1B>(v);
+  return v + dpp<0xB1>(v);
+}
+
 // Sum of N values over all 64 lanes of a wavefront, scattered: on return
 // v[0] of every lane with (lane & 3) == 0 holds the complete sum of value
 // index `first` (the return value), for first < N.  Pairings: lane halves

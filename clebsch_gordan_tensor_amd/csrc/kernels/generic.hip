@@ -1,63 +1,158 @@
-// Channel-wise tensor product for any irreps signature with degrees up to 6,
-// interpreted from a coefficient table instead of compiled per signature.
+// Channel-wise tensor product and message-passing convolution for any irreps
+// signature with degrees up to 6, interpreted from a coefficient table
+// instead of compiled per signature.
 //
 // e3j describes its tensor product as a generic bilinear coupling driven by
 // a sparse COO array of coefficients (E.1 Eq.10-11, B.1) and runs it to
-// degree L = 6..8 (B.1 Figs 5-6).  The specialised kernels unroll every
+// degree L = 6..8 (B.1 Figs 5-7).  The specialised kernels unroll every
 // record at compile time, which stops scaling near L = 4 (the unrolled code
-// outgrows the instruction cache); this kernel reads the records from a
-// table built on the host from the library's ladder CG (e3_generic_plan_build).
+// outgrows the instruction cache); these kernels read the records from a
+// table built on the host from the library's ladder CG
+// (e3_generic_plan_build).
 //
-// Table (int32 words, built per descriptor):
-//   header  [kGenMagic, dx, dy, dout, P, n_contrib, n_rec, rec_off]
-//   obeg    [dout + 1]         contributions of output component o
-//   contrib [n_contrib][3]     {path, first record, end record}
+// Table (int32 words, built per descriptor and per cotangent):
+//   header  [kGenMagic, operand dims, y dims, keys, weight rows,
+//            n_contrib, n_rec, rec_off]
+//   obeg    [keys + 1]         contributions of key k
+//   contrib [n_contrib][3]     {weight row, first record, end record}
 //   rec     [n_rec][2]         at word rec_off (32-byte aligned):
-//                              {x component | y component << 16, coefficient bits}
+//                              {operand component | y component << 16,
+//                               coefficient bits}
 // Every record run is padded to a multiple of 4 with zero coefficients, so
-// the kernel takes records four at a time (one 32-byte scalar load, eight
-// LDS reads in flight, two partial sums).
-// Output-stationary: for every output component o of a row,
-//   z[o][c] = sum_contributions w[P][c] sum_records c_r y[yi] x[xi][c]
-// so each z element is written once and no accumulator is indexed at run
-// time.  One wavefront handles one row and 64 channels: the row's x (one
-// value per lane and component) and y sit in LDS; the records are
-// wave-uniform and come through scalar loads.  Every index read from the
-// table is clamped to its array, so a table built for another descriptor
-// gives wrong numbers, never an out-of-bounds access.
+// the kernels take records four at a time (one 32-byte scalar load, eight
+// LDS reads in flight, two partial sums).  For every key k of a row
+//   out[k][c] = sum_contributions wgt[row][c] sum_records c_r y[yi] op[oi][c]
+// where y is one value per row (the harmonics) or, for the harmonic
+// cotangent, one value per channel.  Every index read from the table is
+// clamped to its array, so a table built for another descriptor gives wrong
+// numbers, never an out-of-bounds access.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 
 #include "common.h"
+#include "harmonics_hi.h"
 #include "registry.h"
 
 namespace e3k {
 namespace {
 
 constexpr int kGenWaves = 4;
+constexpr int kLdsBlockFloats = 16384;  // 64 KiB of LDS per workgroup at most
 
-// dx, dy, dout and np come from the caller's descriptor (they size the LDS
-// and the arrays); the table's own counts are trusted only as far as the
-// table's length (n_words) allows.
+// A table with its counts checked against its length: counts that would
+// read past the table are replaced by zero (no contributions).
+struct Table {
+  const int* obeg;
+  const int* contrib;
+  const int4* rec4;
+  int n_contrib, n_rec;
+};
+
+__device__ __forceinline__ Table table_view(const int* prog, int64_t n_words, int keys) {
+  Table t;
+  t.n_contrib = prog[5];
+  t.n_rec = prog[6];
+  const int64_t rec_off = prog[7];
+  const int64_t fixed = kGenHeader + int64_t(keys) + 1;
+  if (t.n_contrib < 0 || t.n_rec < 0 || rec_off < fixed + 3 * int64_t(t.n_contrib) ||
+      (rec_off & 7) || rec_off + 2 * int64_t(t.n_rec) > n_words)
+    t.n_contrib = t.n_rec = 0;
+  t.obeg = prog + kGenHeader;
+  t.contrib = t.obeg + keys + 1;
+  t.rec4 = reinterpret_cast<const int4*>(prog + (t.n_rec ? rec_off : 0));
+  return t;
+}
+
+// Value of key k for this lane: sum over the key's contributions of
+// wgt(row) * sum over the run's records of c * yv(y index) * ops[op index][lane].
+// ops is the lane's operand column in LDS ([n_op][64]); yv reads the y
+// operand (an LDS value shared by the wave or per lane).  The weight is
+// requested before the records are walked so its latency overlaps them.
+template <class WF, class YF>
+__device__ __forceinline__ float key_sum(const Table& t, int k, int n_op, int n_y, int n_w,
+                                         const float* ops, int lane, WF wgt, YF yv) {
+  float acc = 0.0f;
+  const int jb = max(t.obeg[k], 0), je = min(t.obeg[k + 1], t.n_contrib);
+  for (int j = jb; j < je; ++j) {
+    const float wv = wgt(min(max(t.contrib[3 * j], 0), n_w - 1));
+    // runs are whole groups of 4 records: [rb, re) in units of 4
+    const int gb = max(t.contrib[3 * j + 1], 0) >> 2, ge = min(t.contrib[3 * j + 2], t.n_rec) >> 2;
+    float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll 2
+    for (int g = gb; g < ge; ++g) {
+      const int4 a = t.rec4[2 * g], b = t.rec4[2 * g + 1];  // 4 records, 32 bytes
+      const int p0 = a.x, p1 = a.z, p2 = b.x, p3 = b.z;
+      auto oi = [&](int pk) { return min(pk & 0xffff, n_op - 1); };
+      auto yi = [&](int pk) { return min(int(unsigned(pk) >> 16), n_y - 1); };
+      const float y0 = yv(yi(p0)), y1 = yv(yi(p1)), y2 = yv(yi(p2)), y3 = yv(yi(p3));
+      const float x0 = ops[oi(p0) * 64 + lane], x1 = ops[oi(p1) * 64 + lane];
+      const float x2 = ops[oi(p2) * 64 + lane], x3 = ops[oi(p3) * 64 + lane];
+      t0 = fmaf(__int_as_float(a.y) * y0, x0, t0);
+      t1 = fmaf(__int_as_float(a.w) * y1, x1, t1);
+      t0 = fmaf(__int_as_float(b.y) * y2, x2, t0);
+      t1 = fmaf(__int_as_float(b.w) * y3, x3, t1);
+    }
+    acc = fmaf(wv, t0 + t1, acc);
+  }
+  return acc;
+}
+
+// One channel per lane of row `row` (n components of C) into LDS [n][64];
+// lanes past C get 0.
+template <class T>
+__device__ __forceinline__ void stage_rows(const T* __restrict__ src, int64_t row, int n, int C,
+                                           int c, bool active, float* dst, int lane) {
+  for (int i = 0; i < n; ++i) {
+    float v[1] = {0.0f};
+    if (active) load_ch<T, 1>(src + (row * n + i) * C + c, v);
+    dst[i * 64 + lane] = v[0];
+  }
+}
+
+template <class T>
+__device__ __forceinline__ float load1(const T* __restrict__ p, bool active) {
+  float v[1] = {0.0f};
+  if (active) load_ch<T, 1>(p, v);
+  return v[0];
+}
+
+// y operand of edge e into LDS: the given row Y[e][dy] (LY < 0), or the
+// harmonics of the edge vector: every lane computes degrees 0..LY and lane
+// i < dy stores the one its y component names (want = l*l + m, from the
+// y irreps; -1 for lanes past dy).
+template <int LY>
+__device__ __forceinline__ void stage_edge_y(const float* __restrict__ src, int64_t e, int dy,
+                                             int want, float* ys, int lane) {
+  if constexpr (LY < 0) {
+    for (int i = lane; i < dy; i += 64) ys[i] = src[e * dy + i];
+  } else {
+    constexpr int D = (LY + 1) * (LY + 1);
+    float x = src[3 * e], y = src[3 * e + 1], z = src[3 * e + 2];
+    unit_vector(x, y, z);
+    float h[D];
+    harmonics_bank<LY>(x, y, z, h);
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < D; ++q) v = want == q ? h[q] : v;
+    if (want >= 0) ys[lane] = v;
+  }
+}
+
+// ------------------------------------------------------------ tensor product
+
+// Forward, dx and dw of the product (the table decides which): one
+// wavefront per (row, 64 channels); the row's operand and y sit in LDS, the
+// per-row weights come from global memory.
 template <class T>
 __global__ void __launch_bounds__(64 * kGenWaves)
     k_tp_generic(int64_t n_rows, int C, int dx, int dy, int dout, int np,
                  const int* __restrict__ prog, int64_t n_words, const T* __restrict__ x,
                  const float* __restrict__ y, const T* __restrict__ w, T* __restrict__ z) {
-  int n_contrib = prog[5], n_rec = prog[6];
-  const int64_t rec_off = prog[7];
-  const int64_t fixed = kGenHeader + int64_t(dout) + 1;
-  if (n_contrib < 0 || n_rec < 0 || rec_off < fixed + 3 * int64_t(n_contrib) || (rec_off & 7) ||
-      rec_off + 2 * int64_t(n_rec) > n_words)
-    n_contrib = n_rec = 0;
-  const int* obeg = prog + kGenHeader;
-  const int* contrib = obeg + dout + 1;
-  const int4* rec4 = reinterpret_cast<const int4*>(prog + (n_rec ? rec_off : 0));
+  const Table t = table_view(prog, n_words, dout);
   extern __shared__ float gsm[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int stride = dx * 64 + dy;
-  float* xs = gsm + wave * stride;
+  float* xs = gsm + wave * (dx * 64 + dy);
   float* ys = xs + dx * 64;
   const int cw = (C + 63) / 64;  // waves per row
   const int64_t total = n_rows * cw;
@@ -67,126 +162,208 @@ __global__ void __launch_bounds__(64 * kGenWaves)
     const int c = int(item % cw) * 64 + lane;
     const bool active = c < C;
     wave_lds_fence();  // the previous row's reads are done
-    for (int i = 0; i < dx; ++i) {
-      float v[1] = {0.0f};
-      if (active) load_ch<T, 1>(x + (row * dx + i) * C + c, v);
-      xs[i * 64 + lane] = v[0];
-    }
+    stage_rows<T>(x, row, dx, C, c, active, xs, lane);
     for (int i = lane; i < dy; i += 64) ys[i] = y[row * dy + i];
     wave_lds_fence();
+    const T* wr = w + row * np * C + c;
     for (int o = 0; o < dout; ++o) {
-      float acc = 0.0f;
-      const int jb = max(obeg[o], 0), je = min(obeg[o + 1], n_contrib);
-      for (int j = jb; j < je; ++j) {
-        const int p = min(max(contrib[3 * j], 0), np - 1);
-        float wv[1] = {0.0f};
-        if (active) load_ch<T, 1>(w + (row * np + p) * C + c, wv);
-        // runs are whole groups of 4 records: [rb, re) in units of 4
-        const int gb = max(contrib[3 * j + 1], 0) >> 2, ge = min(contrib[3 * j + 2], n_rec) >> 2;
-        float t0 = 0.0f, t1 = 0.0f;
-#pragma unroll 2
-        for (int g = gb; g < ge; ++g) {
-          const int4 a = rec4[2 * g], b = rec4[2 * g + 1];  // 4 records, 32 bytes
-          const int p0 = a.x, p1 = a.z, p2 = b.x, p3 = b.z;
-          auto xi = [&](int pk) { return min(pk & 0xffff, dx - 1); };
-          auto yi = [&](int pk) { return min(int(unsigned(pk) >> 16), dy - 1); };
-          const float y0 = ys[yi(p0)], y1 = ys[yi(p1)], y2 = ys[yi(p2)], y3 = ys[yi(p3)];
-          const float x0 = xs[xi(p0) * 64 + lane], x1 = xs[xi(p1) * 64 + lane];
-          const float x2 = xs[xi(p2) * 64 + lane], x3 = xs[xi(p3) * 64 + lane];
-          t0 = fmaf(__int_as_float(a.y) * y0, x0, t0);
-          t1 = fmaf(__int_as_float(a.w) * y1, x1, t1);
-          t0 = fmaf(__int_as_float(b.y) * y2, x2, t0);
-          t1 = fmaf(__int_as_float(b.w) * y3, x3, t1);
-        }
-        acc = fmaf(wv[0], t0 + t1, acc);
-      }
-      float out[1] = {acc};
+      const float v = key_sum(
+          t, o, dx, dy, np, xs, lane, [&](int p) { return load1<T>(wr + int64_t(p) * C, active); },
+          [&](int i) { return ys[i]; });
+      float out[1] = {v};
       if (active) store_ch<T, 1>(z + (row * dout + o) * C + c, out);
     }
   }
 }
 
-// dy[yi] = sum over channels of sum_records w[P][c] c_r x[xi][c] dz[o][c]
-// (the channel-summed cotangent of y), from the forward table.  One
-// wavefront per row walks the channels 64 at a time; per-lane partial sums
-// sit in LDS and are added over the lanes in a fixed order at the end.
+// Cotangent of y, summed over the channels, from the table keyed by the y
+// component (records {x component | dz component << 16}, weight rows = the
+// paths):  dy[i] = sum_c sum_P w[P][c] sum_records c x[xi][c] dz[o][c].
+// One wavefront per row walks the channels 64 at a time; each key's lane
+// values are added across the wave in a fixed order and the per-chunk sums
+// are added in chunk order.
 template <class T>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
     k_tp_generic_dy(int64_t n_rows, int C, int dx, int dy, int dout, int np,
                     const int* __restrict__ prog, int64_t n_words, const T* __restrict__ x,
                     const T* __restrict__ w, const T* __restrict__ dz, float* __restrict__ dyo) {
-  int n_contrib = prog[5], n_rec = prog[6];
-  const int64_t rec_off = prog[7];
-  const int64_t fixed = kGenHeader + int64_t(dout) + 1;
-  if (n_contrib < 0 || n_rec < 0 || rec_off < fixed + 3 * int64_t(n_contrib) || (rec_off & 7) ||
-      rec_off + 2 * int64_t(n_rec) > n_words)
-    n_contrib = n_rec = 0;
-  const int* obeg = prog + kGenHeader;
-  const int* contrib = obeg + dout + 1;
-  const int4* rec4 = reinterpret_cast<const int4*>(prog + (n_rec ? rec_off : 0));
+  const Table t = table_view(prog, n_words, dy);
   extern __shared__ float dsm[];
-  const int lane = threadIdx.x;
-  float* xs = dsm;              // [dx][64]
-  float* gs = xs + dx * 64;     // [dout][64]
-  float* acc = gs + dout * 64;  // [dy][64]
-  for (int64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
-    wave_lds_fence();
-    for (int i = 0; i < dy; ++i) acc[i * 64 + lane] = 0.0f;
+  const int waves = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* xs = dsm + wave * ((dx + dout) * 64 + dy);  // [dx][64]
+  float* gs = xs + dx * 64;                           // [dout][64]
+  float* acc = gs + dout * 64;                        // [dy]
+  for (int64_t row = int64_t(blockIdx.x) * waves + wave; row < n_rows;
+       row += int64_t(gridDim.x) * waves) {
     for (int c0 = 0; c0 < C; c0 += 64) {
       const int c = c0 + lane;
       const bool active = c < C;
       wave_lds_fence();
-      for (int i = 0; i < dx; ++i) {
-        float v[1] = {0.0f};
-        if (active) load_ch<T, 1>(x + (row * dx + i) * C + c, v);
-        xs[i * 64 + lane] = v[0];
-      }
-      for (int i = 0; i < dout; ++i) {
-        float v[1] = {0.0f};
-        if (active) load_ch<T, 1>(dz + (row * dout + i) * C + c, v);
-        gs[i * 64 + lane] = v[0];
-      }
+      stage_rows<T>(x, row, dx, C, c, active, xs, lane);
+      stage_rows<T>(dz, row, dout, C, c, active, gs, lane);
       wave_lds_fence();
-      for (int o = 0; o < dout; ++o) {
-        const float g = gs[o * 64 + lane];
-        const int jb = max(obeg[o], 0), je = min(obeg[o + 1], n_contrib);
-        for (int j = jb; j < je; ++j) {
-          const int p = min(max(contrib[3 * j], 0), np - 1);
-          float wv[1] = {0.0f};
-          if (active) load_ch<T, 1>(w + (row * np + p) * C + c, wv);
-          const float wg = wv[0] * g;
-          const int gb = max(contrib[3 * j + 1], 0) >> 2, ge = min(contrib[3 * j + 2], n_rec) >> 2;
-          for (int gr = gb; gr < ge; ++gr) {
-            const int4 a = rec4[2 * gr], b = rec4[2 * gr + 1];
-            const int pk[4] = {a.x, a.z, b.x, b.z};
-            const int cb[4] = {a.y, a.w, b.y, b.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int xi = min(pk[q] & 0xffff, dx - 1);
-              const int yi = min(int(unsigned(pk[q]) >> 16), dy - 1);
-              float* t = acc + yi * 64 + lane;
-              *t = fmaf(__int_as_float(cb[q]) * xs[xi * 64 + lane], wg, *t);
-            }
-          }
-        }
+      const T* wr = w + row * np * C + c;
+      for (int i = 0; i < dy; ++i) {
+        const float v = key_sum(
+            t, i, dx, dout, np, xs, lane,
+            [&](int p) { return load1<T>(wr + int64_t(p) * C, active); },
+            [&](int o) { return gs[o * 64 + lane]; });
+        const float s = wave_sum(v);
+        if (lane == 0) acc[i] = c0 == 0 ? s : acc[i] + s;
       }
     }
     wave_lds_fence();
-    for (int i = lane; i < dy; i += 64) {
-      float sum = 0.0f;
-      for (int k = 0; k < 64; ++k) sum += acc[i * 64 + k];
-      dyo[row * dy + i] = sum;
+    for (int i = lane; i < dy; i += 64) dyo[row * dy + i] = C > 0 ? acc[i] : 0.0f;
+  }
+}
+
+// -------------------------------------------------------------- convolution
+
+// Segment sum over a node's edge list (e3j E.1 Eq.12-13; the receiver-side
+// accumulation in a shared-memory message buffer of its CUDA convolution):
+//   out[node][k] = sum_{j in seg[node]..seg[node+1]} key_k(op[nbr[j]], Y_e, w[e]),
+// e = emap[j] (or j).  With the forward table, seg = the receiver CSR and
+// nbr = sender: the convolution.  With the dx table over the sender-ordered
+// index (seg = colptr, emap = perm, nbr = recv, op = dm): the gradient of x.
+// One wavefront per (node, 64 channels); the accumulator [dkey][64] is in
+// LDS, the edges are taken in list order, so the result is reproducible.
+// Entries whose neighbour is out of [0, n_nodes) (padding) are skipped.
+template <class T, int LY>
+__global__ void __launch_bounds__(256)
+    k_conv_generic_seg(int n_nodes, int n_edges, int C, int dop, int dy, int dkey, int np,
+                       const int* __restrict__ prog, int64_t n_words,
+                       const int* __restrict__ order, const int* __restrict__ seg,
+                       const int* __restrict__ emap, const int* __restrict__ nbr,
+                       const float* __restrict__ yv, YMap ym, const T* __restrict__ op,
+                       const T* __restrict__ w, T* __restrict__ out) {
+  const Table t = table_view(prog, n_words, dkey);
+  extern __shared__ float csm[];
+  const int waves = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* xs = csm + wave * ((dop + dkey) * 64 + dy);  // [dop][64]
+  float* acc = xs + dop * 64;                          // [dkey][64]
+  float* ys = acc + dkey * 64;                         // [dy]
+  const int want = (LY >= 0 && lane < dy) ? ym.idx[lane] : -1;
+  const int cw = (C + 63) / 64;
+  const int64_t total = int64_t(n_nodes) * cw;
+  for (int64_t item = int64_t(blockIdx.x) * waves + wave; item < total;
+       item += int64_t(gridDim.x) * waves) {
+    const int slot = int(item / cw);
+    int node = order ? order[slot] : slot;
+    node = min(max(node, 0), n_nodes - 1);
+    const int c = int(item % cw) * 64 + lane;
+    const bool active = c < C;
+    for (int k = 0; k < dkey; ++k) acc[k * 64 + lane] = 0.0f;
+    const int jb = max(seg[node], 0), je = min(seg[node + 1], n_edges);
+    for (int j = jb; j < je; ++j) {
+      const int a = nbr[j];
+      const int e = emap ? emap[j] : j;
+      if (a < 0 || a >= n_nodes || e < 0 || e >= n_edges) continue;
+      wave_lds_fence();  // the previous edge's reads of xs and ys are done
+      stage_rows<T>(op, a, dop, C, c, active, xs, lane);
+      stage_edge_y<LY>(yv, e, dy, want, ys, lane);
+      wave_lds_fence();
+      const T* wr = w + int64_t(e) * np * C + c;
+      for (int k = 0; k < dkey; ++k) {
+        const float v = key_sum(
+            t, k, dop, dy, np, xs, lane,
+            [&](int p) { return load1<T>(wr + int64_t(p) * C, active); },
+            [&](int i) { return ys[i]; });
+        acc[k * 64 + lane] += v;
+      }
+    }
+    for (int k = 0; k < dkey; ++k) {
+      float v[1] = {acc[k * 64 + lane]};
+      if (active) store_ch<T, 1>(out + (int64_t(node) * dkey + k) * C + c, v);
     }
   }
 }
 
+// Per-edge cotangents of the convolution, receiver by receiver:
+//   dw[e][P][c] = sum_o dm[b][o][c] sum_records c y_e[yi] x[a][xi][c]   (dw table)
+//   dY[e][i]    = sum_c sum_P w[e][P][c] sum_records c x[a][xi][c] dm[b][o][c]
+//                                                                      (dy table)
+// for every edge e = (a -> b).  One wavefront per receiver b takes its edges
+// in order and, per edge, all channel chunks (dY sums over them in chunk
+// order).  Padding edges get dw = 0 and dY = 0.
+template <class T, int LY>
+__global__ void __launch_bounds__(256)
+    k_conv_generic_edge(int n_nodes, int n_edges, int C, int dx, int dy, int dout, int np,
+                        const int* __restrict__ pdw, int64_t dw_words,
+                        const int* __restrict__ pdy, int64_t dy_words,
+                        const int* __restrict__ order, const int* __restrict__ rowptr,
+                        const int* __restrict__ sender, const float* __restrict__ yv, YMap ym,
+                        const T* __restrict__ x, const T* __restrict__ w,
+                        const T* __restrict__ dm, T* __restrict__ dw, float* __restrict__ dY) {
+  const Table tw = table_view(pdw, dw_words, np), ty = table_view(pdy, dy_words, dy);
+  extern __shared__ float esm[];
+  const int waves = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* xs = esm + wave * ((dx + dout) * 64 + 2 * dy);  // [dx][64]
+  float* gs = xs + dx * 64;                                // [dout][64]
+  float* ys = gs + dout * 64;                              // [dy]
+  float* accy = ys + dy;                                   // [dy]
+  const int want = (LY >= 0 && lane < dy) ? ym.idx[lane] : -1;
+  for (int64_t slot = int64_t(blockIdx.x) * waves + wave; slot < n_nodes;
+       slot += int64_t(gridDim.x) * waves) {
+    int b = order ? order[slot] : int(slot);
+    b = min(max(b, 0), n_nodes - 1);
+    const int jb = max(rowptr[b], 0), je = min(rowptr[b + 1], n_edges);
+    for (int e = jb; e < je; ++e) {
+      const int a = sender[e];
+      if (a < 0 || a >= n_nodes) {  // padding
+        for (int c = lane; c < np * C; c += 64) {
+          float z[1] = {0.0f};
+          store_ch<T, 1>(dw + int64_t(e) * np * C + c, z);
+        }
+        for (int i = lane; i < dy; i += 64) dY[int64_t(e) * dy + i] = 0.0f;
+        continue;
+      }
+      wave_lds_fence();  // the previous edge's reads are done
+      stage_edge_y<LY>(yv, e, dy, want, ys, lane);
+      for (int c0 = 0; c0 < C; c0 += 64) {
+        const int c = c0 + lane;
+        const bool active = c < C;
+        wave_lds_fence();
+        stage_rows<T>(x, a, dx, C, c, active, xs, lane);
+        stage_rows<T>(dm, b, dout, C, c, active, gs, lane);
+        wave_lds_fence();
+        for (int p = 0; p < np; ++p) {
+          const float v = key_sum(
+              tw, p, dx, dy, dout, xs, lane, [&](int o) { return gs[o * 64 + lane]; },
+              [&](int i) { return ys[i]; });
+          float o1[1] = {v};
+          if (active) store_ch<T, 1>(dw + (int64_t(e) * np + p) * C + c, o1);
+        }
+        const T* wr = w + int64_t(e) * np * C + c;
+        for (int i = 0; i < dy; ++i) {
+          const float v = key_sum(
+              ty, i, dx, dout, np, xs, lane,
+              [&](int p) { return load1<T>(wr + int64_t(p) * C, active); },
+              [&](int o) { return gs[o * 64 + lane]; });
+          const float s = wave_sum(v);
+          if (lane == 0) accy[i] = c0 == 0 ? s : accy[i] + s;
+        }
+      }
+      wave_lds_fence();
+      for (int i = lane; i < dy; i += 64) dY[int64_t(e) * dy + i] = C > 0 ? accy[i] : 0.0f;
+    }
+  }
+}
+
+// Waves per workgroup for a per-wave LDS need (floats), within 64 KiB.
+int waves_for(int64_t per_wave) {
+  return int(std::max<int64_t>(1, std::min<int64_t>(4, kLdsBlockFloats / per_wave)));
+}
+
 template <class T>
-hipError_t launch_dy(const GenericTpArgs& a, const void* dz, float* dyo, hipStream_t s) {
-  const size_t lds = size_t(a.dx + a.dout + a.dy) * 64 * sizeof(float);
-  const int64_t blocks = std::min<int64_t>(a.n_rows, 256 * 16);
-  hipLaunchKernelGGL(k_tp_generic_dy<T>, dim3(unsigned(blocks)), dim3(64), lds, s, a.n_rows, a.C,
-                     a.dx, a.dy, a.dout, a.np, a.prog, a.n_words, static_cast<const T*>(a.x),
-                     static_cast<const T*>(a.w), static_cast<const T*>(dz), dyo);
+hipError_t launch_dy(const GenericTpArgs& a, const void* x, const void* w, const void* dz,
+                     float* dyo, hipStream_t s) {
+  const int64_t per_wave = int64_t(a.dx + a.dout) * 64 + a.dy;
+  const int wv = waves_for(per_wave);
+  const int64_t blocks = std::min<int64_t>((a.n_rows + wv - 1) / wv, 256 * 8);
+  hipLaunchKernelGGL(k_tp_generic_dy<T>, dim3(unsigned(blocks)), dim3(64 * wv),
+                     size_t(per_wave * wv) * sizeof(float), s, a.n_rows, a.C, a.dx, a.dy, a.dout,
+                     a.np, a.prog, a.n_words, static_cast<const T*>(x),
+                     static_cast<const T*>(w), static_cast<const T*>(dz), dyo);
   return hipGetLastError();
 }
 
@@ -202,6 +379,63 @@ hipError_t launch(const GenericTpArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <class T, int LY>
+hipError_t launch_seg(const GenericConvArgs& a, hipStream_t s) {
+  const int64_t per_wave = int64_t(a.dop + a.dkey) * 64 + a.dy;
+  const int wv = waves_for(per_wave);
+  const int64_t items = int64_t(a.n_nodes) * ((a.C + 63) / 64);
+  const int64_t blocks = std::min<int64_t>((items + wv - 1) / wv, 256 * 16);
+  hipLaunchKernelGGL((k_conv_generic_seg<T, LY>), dim3(unsigned(blocks)), dim3(64 * wv),
+                     size_t(per_wave * wv) * sizeof(float), s, a.n_nodes, a.n_edges, a.C, a.dop,
+                     a.dy, a.dkey, a.np, a.prog, a.n_words, a.order, a.seg, a.emap, a.nbr, a.yv, a.ym,
+                     static_cast<const T*>(a.op), static_cast<const T*>(a.w),
+                     static_cast<T*>(a.out));
+  return hipGetLastError();
+}
+
+template <class T, int LY>
+hipError_t launch_edge(const GenericConvEdgeArgs& a, hipStream_t s) {
+  const int64_t per_wave = int64_t(a.dx + a.dout) * 64 + 2 * a.dy;
+  const int wv = waves_for(per_wave);
+  const int64_t blocks = std::min<int64_t>((int64_t(a.n_nodes) + wv - 1) / wv, 256 * 16);
+  hipLaunchKernelGGL((k_conv_generic_edge<T, LY>), dim3(unsigned(blocks)), dim3(64 * wv),
+                     size_t(per_wave * wv) * sizeof(float), s, a.n_nodes, a.n_edges, a.C, a.dx,
+                     a.dy, a.dout, a.np, a.dw_prog, a.dw_words, a.dy_prog, a.dy_words, a.order,
+                     a.rowptr, a.sender, a.yv, a.ym, static_cast<const T*>(a.x),
+                     static_cast<const T*>(a.w), static_cast<const T*>(a.dm),
+                     static_cast<T*>(a.dw), a.dY);
+  return hipGetLastError();
+}
+
+// Degree of the harmonics computed in the kernel (-1: Y given) as a
+// template argument.
+template <class T, template <class, int> class F, class Args>
+hipError_t by_degree(int ly, const Args& a, hipStream_t s) {
+  switch (ly) {
+    case -1: return F<T, -1>::run(a, s);
+    case 0: return F<T, 0>::run(a, s);
+    case 1: return F<T, 1>::run(a, s);
+    case 2: return F<T, 2>::run(a, s);
+    case 3: return F<T, 3>::run(a, s);
+    case 4: return F<T, 4>::run(a, s);
+    case 5: return F<T, 5>::run(a, s);
+    case 6: return F<T, 6>::run(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class T, int LY>
+struct SegLaunch {
+  static hipError_t run(const GenericConvArgs& a, hipStream_t s) { return launch_seg<T, LY>(a, s); }
+};
+
+template <class T, int LY>
+struct EdgeLaunch {
+  static hipError_t run(const GenericConvEdgeArgs& a, hipStream_t s) {
+    return launch_edge<T, LY>(a, s);
+  }
+};
+
 }  // namespace
 
 hipError_t launch_tp_generic(const GenericTpArgs& a, int bf16, hipStream_t s) {
@@ -212,7 +446,19 @@ hipError_t launch_tp_generic(const GenericTpArgs& a, int bf16, hipStream_t s) {
 hipError_t launch_tp_generic_dy(const GenericTpArgs& a, const void* dz, float* dy, int bf16,
                                 hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  return bf16 ? launch_dy<bf16_t>(a, dz, dy, s) : launch_dy<float>(a, dz, dy, s);
+  return bf16 ? launch_dy<bf16_t>(a, a.x, a.w, dz, dy, s)
+              : launch_dy<float>(a, a.x, a.w, dz, dy, s);
+}
+
+hipError_t launch_conv_generic_seg(const GenericConvArgs& a, int bf16, hipStream_t s) {
+  if (a.n_nodes <= 0) return hipSuccess;
+  return bf16 ? by_degree<bf16_t, SegLaunch>(a.ly, a, s) : by_degree<float, SegLaunch>(a.ly, a, s);
+}
+
+hipError_t launch_conv_generic_edge(const GenericConvEdgeArgs& a, int bf16, hipStream_t s) {
+  if (a.n_nodes <= 0 || a.n_edges <= 0) return hipSuccess;
+  return bf16 ? by_degree<bf16_t, EdgeLaunch>(a.ly, a, s)
+              : by_degree<float, EdgeLaunch>(a.ly, a, s);
 }
 
 }  // namespace e3k

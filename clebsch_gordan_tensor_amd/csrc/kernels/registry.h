@@ -110,9 +110,60 @@ struct GenericTpArgs {
   void* z;
 };
 hipError_t launch_tp_generic(const GenericTpArgs& a, int bf16, hipStream_t s);
-// dy of the generic tensor product from the forward table (a.z unused)
+// dy of the generic tensor product from the table keyed by the y component
+// (a.dx operand comps, a.dout dz comps, a.dy keys, a.np weight rows; a.y and
+// a.z unused)
 hipError_t launch_tp_generic_dy(const GenericTpArgs& a, const void* dz, float* dy, int bf16,
                                 hipStream_t s);
+
+// Harmonic index l*l + m of every y component when the convolution computes
+// the harmonics of the edge vectors (dy <= 64).
+struct YMap {
+  signed char idx[64];
+};
+
+// Table-driven segment sum over a node's edge list: the convolution forward
+// (seg = rowptr, nbr = sender, emap null) or its gradient of x (seg = colptr,
+// emap = perm, nbr = recv of the sender-ordered index).
+struct GenericConvArgs {
+  int n_nodes, n_edges, C;
+  int dop, dy, dkey, np;  // operand comps, y comps, output comps, weight rows
+  const int* prog;
+  int64_t n_words;
+  const int* order;  // node visiting order, or null
+  const int* seg;    // [n_nodes + 1]
+  const int* emap;   // list position -> edge id, or null (identity)
+  const int* nbr;    // list position -> neighbour node
+  const float* yv;   // Y [E][dy] (ly < 0) or edge vectors [E][3]
+  int ly;            // harmonics 0..ly computed from the vectors, or -1
+  YMap ym;           // y component -> harmonic index (ly >= 0)
+  const void* op;    // [N][dop][C]
+  const void* w;     // [E][np][C]
+  void* out;         // [N][dkey][C]
+};
+hipError_t launch_conv_generic_seg(const GenericConvArgs& a, int bf16, hipStream_t s);
+
+// Table-driven per-edge cotangents dw [E][np][C] and dY [E][dy] of the
+// convolution (dw table and dy table), receiver by receiver.
+struct GenericConvEdgeArgs {
+  int n_nodes, n_edges, C, dx, dy, dout, np;
+  const int* dw_prog;
+  int64_t dw_words;
+  const int* dy_prog;
+  int64_t dy_words;
+  const int* order;
+  const int* rowptr;
+  const int* sender;
+  const float* yv;
+  int ly;
+  YMap ym;
+  const void* x;
+  const void* w;
+  const void* dm;
+  void* dw;
+  float* dY;
+};
+hipError_t launch_conv_generic_edge(const GenericConvEdgeArgs& a, int bf16, hipStream_t s);
 
 // Radial edge weights and the convolution that computes them on the fly
 // (radial.hip): 8 Bessel functions -> 64 SiLU units -> n_cols = P*C.

@@ -17,6 +17,9 @@ of its Table 1 (about 45 neighbours per node):
   mace64k   64,000 atoms at 0.1 atoms/A^3, cutoff 5 A, same irreps, N(0,1) weights
   ho20k     20,000 atoms, node labels randomly permuted, 64x(0e+1o+2e+3o) both
             sides, bf16 storage
+  deg<L>    (make_conv_degree) the higher-degree convolution of e3j B.1 Fig 7:
+            2,048 nodes, about 45 neighbours (26.75 A cube, cutoff 5 A),
+            128 channels, every irrep 0..L once on x and out, SH l <= L
 
 Graph rule: ordered pairs (a -> b), a != b, |pos_b - pos_a| <= cutoff, open
 cube (no periodic images), edges sorted by (receiver, sender); the edge vector
@@ -317,6 +320,31 @@ def make_conv(name: str, seed: int = 0, with_dm: bool = True) -> ConvProblem:
         dm = round_bf16(dm) if dm is not None else None
     return ConvProblem(name=name, x_irreps=xi, y_irreps=yi, out_irreps=oi, channels=C, graph=g,
                        x=x, w=w, dm=dm, dtype=cfg["dtype"], extra=dict(cfg, box=box))
+
+
+def degree_irreps(L: int, skew: bool = False):
+    """Every irrep 0..L once: parity (-1)^l, or (-1)^(l+1) when skew."""
+    return [(l, (1 if l % 2 == 0 else -1) * (-1 if skew else 1)) for l in range(L + 1)]
+
+
+def make_conv_degree(L: int, seed: int = 0, n_nodes: int = 2048, channels: int = 128,
+                     box: float = 26.75, cutoff: float = 5.0, dtype: str = "f32",
+                     with_dm: bool = True) -> ConvProblem:
+    """The convolution at degree L: x and out = every irrep 0..L (natural
+    parity), y = SH 0..L, N(0,1) node features, weights and cotangent."""
+    g = random_graph(n_nodes, box, cutoff, seed)
+    xi = oi = degree_irreps(L)
+    yi = sh_irreps(L)
+    P = num_paths(xi, yi, oi)
+    x = normal((n_nodes, dim(xi), channels), seed, TAG_X)
+    w = normal((g.n_edges, P, channels), seed, TAG_W)
+    dm = normal((n_nodes, dim(oi), channels), seed, TAG_DM) if with_dm else None
+    if dtype == "bf16":
+        x, w = round_bf16(x), round_bf16(w)
+        dm = round_bf16(dm) if dm is not None else None
+    return ConvProblem(name=f"deg{L}", x_irreps=xi, y_irreps=yi, out_irreps=oi,
+                       channels=channels, graph=g, x=x, w=w, dm=dm, dtype=dtype,
+                       extra=dict(n=n_nodes, box=box, cutoff=cutoff, lmax=L))
 
 
 def make_tp(seed: int = 0, rows: int | None = None, with_dz: bool = False) -> TPProblem:

@@ -241,31 +241,64 @@ e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t 
  * a bilinear coupling given by a sparse COO array of coefficients, E.1 and
  * B.1; Figs 5-6 run it to L = 6 and beyond).
  *   e3_generic_plan_size / e3_generic_plan_build: host-only; write table
- *     `table` (E3_GEN_FORWARD, E3_GEN_DX or E3_GEN_DW) for desc into a HOST
- *     buffer; the caller copies it to device memory it owns (16-byte
- *     aligned) and may reuse it for every call with the same descriptor.
+ *     `table` for desc into a HOST buffer; the caller copies it to device
+ *     memory it owns (16-byte aligned) and may reuse it for every call with
+ *     the same descriptor.  One table per cotangent: E3_GEN_FORWARD (the
+ *     forward), E3_GEN_DX (gradient of x), E3_GEN_DW (of w), E3_GEN_DY (of
+ *     y; the records keyed by the y component).
  *   e3_tp_forward_generic: the forward table; x [n][dx][C], y [n][dy]
  *     float32, w [n][P][C], z [n][dout][C].
- *   e3_tp_backward_generic: all three tables; for dz [n][dout][C] writes
- *     dx [n][dx][C], dw [n][P][C] and dy [n][dy] (float32, summed over the
- *     channels in a fixed order).
- * fp32 or bf16 storage, fp32 accumulation.  Needs every degree <= 6 and
- * dx*64 + dy, dout*64 + dy <= 4096 (dx, dout <= 63), and for the backward
- * dx + dout + dy <= 256.  A table built for
- * another descriptor gives wrong values but never an out-of-bounds access
- * (every index read from it is clamped). */
-enum { E3_GEN_FORWARD = 0, E3_GEN_DX = 1, E3_GEN_DW = 2 };
+ *   e3_tp_backward_generic: the DX, DW and DY tables; for dz [n][dout][C]
+ *     writes dx [n][dx][C], dw [n][P][C] and dy [n][dy] (float32, summed
+ *     over the channels in a fixed order).
+ * fp32 or bf16 storage, fp32 accumulation; no alignment beyond the element
+ * size.  Needs every degree <= 6 and dx*64 + dy, dout*64 + dy <= 4096
+ * (dx, dout <= 63).  A table built for another descriptor gives wrong
+ * values but never an out-of-bounds access (every index read from it is
+ * clamped). */
+enum { E3_GEN_FORWARD = 0, E3_GEN_DX = 1, E3_GEN_DW = 2, E3_GEN_DY = 3 };
 e3_status e3_generic_plan_size(const e3_desc* desc, int32_t table, size_t* bytes);
 e3_status e3_generic_plan_build(const e3_desc* desc, int32_t table, void* host_plan,
                                 size_t bytes);
 e3_status e3_tp_forward_generic(const e3_desc* desc, int64_t n_rows, const void* plan,
                                 size_t plan_bytes, const void* x, const float* y, const void* w,
                                 void* z, e3_dtype dtype, void* stream);
-e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_fwd,
-                                 size_t fwd_bytes, const void* plan_dx, size_t dx_bytes,
-                                 const void* plan_dw, size_t dw_bytes, const void* x,
+e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_dx,
+                                 size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+                                 const void* plan_dy, size_t dy_bytes, const void* x,
                                  const float* y, const void* w, const void* dz, void* dx, void* dw,
                                  float* dy, e3_dtype dtype, void* stream);
+
+/* Convolution forward and backward (as e3_conv_forward / e3_conv_backward:
+ * e3j A.3 Eq.7, E.1 Eq.12-16) for irreps of degree up to 6, from the
+ * coefficient tables above (e3j B.1 Fig 7 runs the convolution to L = 6).
+ * The messages of a receiver accumulate in an on-chip buffer over its edge
+ * list, as in the shared-memory accumulation of e3j's CUDA convolution
+ * (E.1), so m is written once per node and the sum is reproducible.
+ *   m[b]  = sum_{e in row b} sum_P w[e][P] (x[sender e] (x) Y_e)_P
+ *   dx[a] = sum over out-edges of a (sender-ordered index), dw[e], dY[e]
+ * edge_vec_or_Y: edge vectors [E][3] (the harmonics of every y irrep are
+ * computed from them: needs dy <= 64) or, with E3_Y_GIVEN, Y [E][dy].
+ * Forward: table E3_GEN_FORWARD; workspace optional (its node order, as
+ * e3_conv_forward).  Backward: tables E3_GEN_DX, E3_GEN_DW, E3_GEN_DY;
+ * workspace from e3_conv_prepare_transpose on the same graph (required);
+ * dY float32 [E][dy] is the cotangent of Y (of the harmonics in edge-vector
+ * mode; e3_spherical_harmonics_backward chains it to the vectors for
+ * degrees <= 3).  Padding edges (sender < 0) add nothing and get dw = 0,
+ * dY = 0.  Shapes, storage and limits as for the generic tensor product. */
+e3_status e3_conv_forward_generic(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                  const int32_t* rowptr, const int32_t* sender,
+                                  const void* workspace, size_t ws_bytes, const void* plan,
+                                  size_t plan_bytes, const float* edge_vec_or_Y, const void* x,
+                                  const void* w, void* m, e3_dtype dtype, void* stream);
+e3_status e3_conv_backward_generic(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                   const int32_t* rowptr, const int32_t* sender,
+                                   const void* workspace, size_t ws_bytes, const void* plan_dx,
+                                   size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+                                   const void* plan_dy, size_t dy_bytes,
+                                   const float* edge_vec_or_Y, const void* x, const void* w,
+                                   const void* dm, void* dx, void* dw, float* dY, e3_dtype dtype,
+                                   void* stream);
 
 /* Per-node gradient from per-edge vector gradients, for r_e = pos[receiver]
  * - pos[sender]:

@@ -240,7 +240,7 @@ def test_generic_plan_table(lib):
     t = np.zeros(nb.value // 4, dtype=np.int32)
     assert lib.e3_generic_plan_build(C.byref(d.c()), 0, t.ctypes.data, nb.value - 4) == -6
     assert lib.e3_generic_plan_build(C.byref(d.c()), 0, t.ctypes.data, nb.value) == 0
-    assert lib.e3_generic_plan_size(C.byref(d.c()), 3, C.byref(nb)) == -1
+    assert lib.e3_generic_plan_size(C.byref(d.c()), 4, C.byref(nb)) == -1
     dx = dy = dout = 25
     P, n_contrib, n_rec, rec_off = t[4], t[5], t[6], t[7]
     assert list(t[1:4]) == [dx, dy, dout] and P == api.num_paths(d) == 42
@@ -266,16 +266,50 @@ def test_generic_plan_table(lib):
                 if c != 0.0:
                     assert c == pytest.approx(T[o - offs[io], xi - offs[ix], yi - offs[iy]],
                                               abs=1e-7)
-    # the dx and dw tables hold the same coefficients, keyed differently
-    for table in (1, 2):
+    # the dx, dw and dy tables hold the same coefficients, keyed differently
+    for table in (1, 2, 3):
         assert lib.e3_generic_plan_size(C.byref(d.c()), table, C.byref(nb)) == 0
         u = np.zeros(nb.value // 4, dtype=np.int32)
         assert lib.e3_generic_plan_build(C.byref(d.c()), table, u.ctypes.data, nb.value) == 0
         r = u[u[7]:u[7] + 2 * u[6]].reshape(-1, 2)[:, 1].copy().view(np.float32)
         assert np.count_nonzero(r) == 1158
         assert np.isclose(np.sort(np.abs(r[r != 0])).sum(), np.sort(np.abs(coef[coef != 0])).sum())
+    # the dy table: keys are y components, records {x component | output
+    # component << 16}, weights the paths
+    assert lib.e3_generic_plan_size(C.byref(d.c()), 3, C.byref(nb)) == 0
+    u = np.zeros(nb.value // 4, dtype=np.int32)
+    assert lib.e3_generic_plan_build(C.byref(d.c()), 3, u.ctypes.data, nb.value) == 0
+    assert list(u[1:5]) == [dx, dout, dy, P]
+    ub = u[8:8 + dy + 1]
+    uc = u[8 + dy + 1:8 + dy + 1 + 3 * u[5]].reshape(-1, 3)
+    ur = u[u[7]:u[7] + 2 * u[6]].reshape(-1, 2)
+    for yk in (0, 5, 20):
+        for p, rb, re in uc[ub[yk]:ub[yk + 1]]:
+            ix, iy, io = paths[p]
+            l1, l2, L = nat[ix][0], nat[iy][0], nat[io][0]
+            assert offs[iy] <= yk < offs[iy] + 2 * l2 + 1
+            T = api.cg_block(l1, l2, L)
+            for packed, bits in ur[rb:re]:
+                xi, o = packed & 0xFFFF, packed >> 16
+                c = np.array([bits], np.int32).view(np.float32)[0]
+                if c != 0.0:
+                    assert c == pytest.approx(T[o - offs[io], xi - offs[ix], yk - offs[iy]],
+                                              abs=1e-7)
     assert lib.e3_tp_backward_generic(C.byref(d.c()), 0, None, 0, None, 0, None, 0, None, None,
                                       None, None, None, None, None, 0, None) == 0
+    # the generic convolution: empty graph, missing workspace, short tables
+    assert lib.e3_conv_forward_generic(C.byref(d.c()), 0, 0, None, None, None, 0, None, 0, None,
+                                       None, None, None, 0, None) == 0
+    fk = C.c_void_p(0x10000)
+    assert lib.e3_conv_forward_generic(C.byref(d.c()), 4, 8, fk, fk, None, 0, fk, 16, fk, fk, fk,
+                                       fk, 0, None) == -6
+    assert lib.e3_conv_forward_generic(C.byref(d.c()), 4, 8, fk, None, None, 0, fk, 16, fk, fk,
+                                       fk, fk, 0, None) == -1
+    assert lib.e3_conv_backward_generic(C.byref(d.c()), 4, 8, fk, fk, None, 0, fk, 4096, fk, 4096,
+                                        fk, 4096, fk, fk, fk, fk, fk, fk, fk, 0, None) == -6
+    wide = api.Desc([(4, 1), (4, 1), (4, 1)], [(l, 1) for l in range(7)] * 2, [(4, 1)], 8)
+    assert lib.e3_conv_forward_generic(C.byref(wide.c()), 4, 8, fk, fk, None, 0, fk, 4096, fk,
+                                       fk, fk, fk, 0, None) == -3  # dy > 64 from edge vectors
     big = api.Desc([(7, 1)], [(0, 1)], [(7, 1)], 64)
     assert lib.e3_generic_plan_size(C.byref(big.c()), 0, C.byref(nb)) == -3
     assert lib.e3_tp_forward_generic(C.byref(d.c()), 0, None, 0, None, None, None, None, 0,
