@@ -289,7 +289,7 @@ e3_status e3_tp_backward(const e3_desc* desc, int64_t n_rows, const void* x, con
 
 e3_status e3_spherical_harmonics_backward(int32_t lmax, int64_t n, const float* vec,
                                           const float* dY, float* dvec, void* stream) {
-  if (lmax < 0 || lmax > 3) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..3");
+  if (lmax < 0 || lmax > 6) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..6");
   if (n < 0) return fail(E3_ERR_INVALID_ARG, "n < 0");
   if (n == 0) return ok();
   if (!vec || !dY || !dvec) return fail(E3_ERR_INVALID_ARG, "null pointer");

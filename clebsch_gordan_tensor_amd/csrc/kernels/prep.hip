@@ -343,19 +343,8 @@ __global__ void __launch_bounds__(256)
       y *= inv;
       z *= inv;
       const float inv_norm = inv * is;
-      Dual3 h[D];
-      sfor<0, LMAX + 1>([&](auto l) {
-        harmonics_l<l>(Dual3(x, 1.0f, 0.0f, 0.0f), Dual3(y, 0.0f, 1.0f, 0.0f),
-                       Dual3(z, 0.0f, 0.0f, 1.0f), h + l * l);
-      });
       const float* gy = dY + i * D;
-#pragma unroll
-      for (int k = 0; k < D; ++k) {
-        const float c = gy[k];
-        g0 = fmaf(c, h[k].d0, g0);
-        g1 = fmaf(c, h[k].d1, g1);
-        g2 = fmaf(c, h[k].d2, g2);
-      }
+      harmonics_grad_bank<LMAX>(x, y, z, [&](int k) { return gy[k]; }, g0, g1, g2);
       const float ug = x * g0 + y * g1 + z * g2;
       g0 = (g0 - x * ug) * inv_norm;
       g1 = (g1 - y * ug) * inv_norm;
@@ -595,6 +584,9 @@ hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const fl
     case 1: hipLaunchKernelGGL(k_harmonics_grad<1>, g, b, 0, s, n, vec, dY, dvec); break;
     case 2: hipLaunchKernelGGL(k_harmonics_grad<2>, g, b, 0, s, n, vec, dY, dvec); break;
     case 3: hipLaunchKernelGGL(k_harmonics_grad<3>, g, b, 0, s, n, vec, dY, dvec); break;
+    case 4: hipLaunchKernelGGL(k_harmonics_grad<4>, g, b, 0, s, n, vec, dY, dvec); break;
+    case 5: hipLaunchKernelGGL(k_harmonics_grad<5>, g, b, 0, s, n, vec, dY, dvec); break;
+    case 6: hipLaunchKernelGGL(k_harmonics_grad<6>, g, b, 0, s, n, vec, dY, dvec); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

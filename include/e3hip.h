@@ -151,7 +151,7 @@ e3_status e3_tp_backward(const e3_desc* desc, int64_t n_rows, const void* x, con
  * the harmonic cotangent to the edge vector, toward conservative forces,
  * Tessera 2.2 Eq.3):
  *   dvec[i][k] = sum_j dY[i][j] dY_j(vec[i]) / dvec[i][k],
- * dY [n][(lmax+1)^2], vec and dvec [n][3], float32, lmax <= 3.  Since the
+ * dY [n][(lmax+1)^2], vec and dvec [n][3], float32, lmax <= 6.  Since the
  * harmonics depend on the direction only, dvec is orthogonal to vec; a zero
  * vector gets 0.  Feed it the dY of e3_conv_backward. */
 e3_status e3_spherical_harmonics_backward(int32_t lmax, int64_t n, const float* vec,
@@ -283,8 +283,7 @@ e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void
  * e3_conv_forward).  Backward: tables E3_GEN_DX, E3_GEN_DW, E3_GEN_DY;
  * workspace from e3_conv_prepare_transpose on the same graph (required);
  * dY float32 [E][dy] is the cotangent of Y (of the harmonics in edge-vector
- * mode; e3_spherical_harmonics_backward chains it to the vectors for
- * degrees <= 3).  Padding edges (sender < 0) add nothing and get dw = 0,
+ * mode; e3_spherical_harmonics_backward chains it to the vectors).  Padding edges (sender < 0) add nothing and get dw = 0,
  * dY = 0.  Shapes, storage and limits as for the generic tensor product. */
 e3_status e3_conv_forward_generic(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
                                   const int32_t* rowptr, const int32_t* sender,

@@ -317,6 +317,29 @@ def sh_grad(lmax: int, vecs, dY) -> np.ndarray:
     return out
 
 
+def sh_grad_fd(lmax: int, vecs, dY) -> np.ndarray:
+    """J^T dY of the harmonics of vecs [n][3] by fourth-order central
+    differences of sh() (fp64), for the degrees (4..6) that the closed-form
+    partials of sh_grad do not cover.  Step h = 1e-3 |r| per axis: the
+    truncation error is O(h^4 |d^5 Y|), about 1e-9 of the value at l = 6,
+    and the rounding error about 1e-13 |Y| / h.  A zero vector gets 0."""
+    v = _f64(vecs).reshape(-1, 3)
+    g = _f64(dY).reshape(v.shape[0], (lmax + 1) ** 2)
+    r = np.linalg.norm(v, axis=1)
+    h = 1e-3 * np.where(r > 0, r, 1.0)
+    out = np.zeros((v.shape[0], 3))
+    for k in range(3):
+        e = np.zeros_like(v)
+        e[:, k] = h
+
+        def f(s):
+            return (sh(lmax, v + s * e) * g).sum(axis=1)
+
+        out[:, k] = (-f(2) + 8 * f(1) - 8 * f(-1) + f(-2)) / (12 * h)
+    out[r == 0] = 0.0
+    return out
+
+
 def edge_grad_to_nodes(rowptr, sender, g) -> np.ndarray:
     """dpos [N][3] from edge-vector gradients g [E][3] (r_e = pos[recv] - pos[sender])."""
     rowptr, sender = _i32(rowptr), _i32(sender)

@@ -155,7 +155,7 @@ def test_error_codes(lib):
                               None) == -4
     assert lib.e3_tp_backward(_desc_c(uns), 5, fake, fake, fake, fake, fake, fake, fake, 0,
                               None) == -3
-    assert lib.e3_spherical_harmonics_backward(4, 10, fake, fake, fake, None) == -1
+    assert lib.e3_spherical_harmonics_backward(7, 10, fake, fake, fake, None) == -1
     assert lib.e3_spherical_harmonics_backward(3, -1, fake, fake, fake, None) == -1
     assert lib.e3_spherical_harmonics_backward(3, 10, fake, None, fake, None) == -1
     assert lib.e3_spherical_harmonics_backward(3, 0, None, None, None, None) == 0

@@ -169,3 +169,16 @@ def test_harmonics_to_degree_six_match_oracle(gpu):
         sl = slice(l * l, (l + 1) * (l + 1))
         assert_close(Y[:, sl], ref[:, sl], TOL_F32, f"harmonics l={l}")
     assert np.all(Y[7, 1:] == 0.0) and Y[7, 0] == 1.0
+
+
+@pytest.mark.parametrize("lmax", [4, 6])
+def test_harmonics_gradient_to_degree_six(gpu, lmax):
+    # the vector gradient through the coupling recursion, against the
+    # fourth-order differences of the oracle's harmonics
+    rng = np.random.default_rng(391 + lmax)
+    v = (rng.standard_normal((3001, 3)) * rng.uniform(0.1, 10, (3001, 1))).astype(np.float32)
+    v[5] = 0.0
+    dY = rng.standard_normal((3001, (lmax + 1) ** 2)).astype(np.float32)
+    g = host(gpu.spherical_harmonics_backward(lmax, dev(v), dev(dY)))
+    assert_close(g, O.sh_grad_fd(lmax, v, dY), TOL_F32, f"harmonics gradient l<={lmax}")
+    assert np.all(g[5] == 0.0)

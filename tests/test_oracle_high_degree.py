@@ -133,3 +133,43 @@ def test_gaunt_identity_high_degree():
 def test_zero_vector_high_degree():
     Y = O.sh(6, np.zeros((1, 3)))[0]
     assert Y[0] == 1.0 and np.all(Y[1:] == 0.0)
+
+
+# ------------------------------------------- harmonics gradient, degrees 4..6
+
+def test_sh_grad_fd_matches_closed_form_partials():
+    # the finite-difference gradient reproduces the closed-form one to l = 3
+    rng = np.random.default_rng(60)
+    v = rng.standard_normal((40, 3)) * rng.uniform(0.2, 5.0, (40, 1))
+    dY = rng.standard_normal((40, 16))
+    a, b = O.sh_grad_fd(3, v, dY), O.sh_grad(3, v, dY)
+    assert np.abs(a - b).max() <= 1e-8 * np.abs(b).max()
+
+
+def test_sh_grad_fd_high_degree_properties():
+    # the harmonics depend on the direction only: the gradient is orthogonal
+    # to r and scales as 1/|r|; a single component's gradient matches the
+    # derivative of the Legendre form along a tangent direction
+    rng = np.random.default_rng(61)
+    v = rng.standard_normal((30, 3))
+    dY = rng.standard_normal((30, 49))
+    g = O.sh_grad_fd(6, v, dY)
+    assert np.abs((g * v).sum(1)).max() <= 1e-8 * np.abs(g).max()
+    g3 = O.sh_grad_fd(6, 3.0 * v, dY)
+    assert np.abs(3.0 * g3 - g).max() <= 1e-8 * np.abs(g).max()
+    # d/dphi of the m = +6 component: Y_66 ~ sin^6(theta) cos(6 phi), so its
+    # derivative along e_phi is -6 Y_6,-6 / (|r| sin theta)
+    u = v / np.linalg.norm(v, axis=1, keepdims=True)
+    e_phi = np.stack([-u[:, 1], u[:, 0], np.zeros(30)], 1)
+    e_phi /= np.linalg.norm(e_phi, axis=1, keepdims=True)
+    sel = np.zeros((30, 49))
+    sel[:, 36 + 12] = 1.0  # (l, m) = (6, 6)
+    d = (O.sh_grad_fd(6, u, sel) * e_phi).sum(1)
+    sin_t = np.sqrt(u[:, 0] ** 2 + u[:, 1] ** 2)
+    Y = O.sh(6, u)
+    np.testing.assert_allclose(d, -6 * Y[:, 36] / sin_t, rtol=1e-7, atol=1e-8)
+
+
+def test_sh_grad_fd_zero_vector():
+    g = O.sh_grad_fd(5, np.zeros((2, 3)), np.ones((2, 36)))
+    assert np.all(g == 0.0)
