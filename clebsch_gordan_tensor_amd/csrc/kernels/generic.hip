@@ -98,6 +98,76 @@ __device__ __forceinline__ float key_sum(const Table& t, int k, int n_op, int n_
   return acc;
 }
 
+// key_sum for two channels per lane: ops holds a float2 per lane and
+// component ([n_op][64]), wgt returns the two channels' weights.  Each
+// channel's sum is formed in the same order as key_sum's.
+template <class WF, class YF>
+__device__ __forceinline__ float2 key_sum2(const Table& t, int k, int n_op, int n_y, int n_w,
+                                           const float2* ops, int lane, WF wgt, YF yv) {
+  float a0 = 0.0f, a1 = 0.0f;
+  const int jb = max(t.obeg[k], 0), je = min(t.obeg[k + 1], t.n_contrib);
+  for (int j = jb; j < je; ++j) {
+    const float2 wv = wgt(min(max(t.contrib[3 * j], 0), n_w - 1));
+    const int gb = max(t.contrib[3 * j + 1], 0) >> 2, ge = min(t.contrib[3 * j + 2], t.n_rec) >> 2;
+    float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
+#pragma unroll 2
+    for (int g = gb; g < ge; ++g) {
+      const int4 a = t.rec4[2 * g], b = t.rec4[2 * g + 1];
+      const int p0 = a.x, p1 = a.z, p2 = b.x, p3 = b.z;
+      auto oi = [&](int pk) { return min(pk & 0xffff, n_op - 1); };
+      auto yi = [&](int pk) { return min(int(unsigned(pk) >> 16), n_y - 1); };
+      const float c0 = __int_as_float(a.y) * yv(yi(p0)), c1 = __int_as_float(a.w) * yv(yi(p1));
+      const float c2 = __int_as_float(b.y) * yv(yi(p2)), c3 = __int_as_float(b.w) * yv(yi(p3));
+      const float2 x0 = ops[oi(p0) * 64 + lane], x1 = ops[oi(p1) * 64 + lane];
+      const float2 x2 = ops[oi(p2) * 64 + lane], x3 = ops[oi(p3) * 64 + lane];
+      t00 = fmaf(c0, x0.x, t00);
+      t01 = fmaf(c0, x0.y, t01);
+      t10 = fmaf(c1, x1.x, t10);
+      t11 = fmaf(c1, x1.y, t11);
+      t00 = fmaf(c2, x2.x, t00);
+      t01 = fmaf(c2, x2.y, t01);
+      t10 = fmaf(c3, x3.x, t10);
+      t11 = fmaf(c3, x3.y, t11);
+    }
+    a0 = fmaf(wv.x, t00 + t10, a0);
+    a1 = fmaf(wv.y, t01 + t11, a1);
+  }
+  return make_float2(a0, a1);
+}
+
+// Channels c and c + 1 of element p (c + 1 may be past C: then 0); a vector
+// access when the pair is aligned (C even).
+template <class T>
+__device__ __forceinline__ float2 load_pair(const T* __restrict__ p, int c, int C) {
+  float v[2] = {0.0f, 0.0f};
+  if (c + 1 < C && !(C & 1)) {
+    load_ch<T, 2>(p, v);
+  } else {
+    float u[1];
+    if (c < C) {
+      load_ch<T, 1>(p, u);
+      v[0] = u[0];
+    }
+    if (c + 1 < C) {
+      load_ch<T, 1>(p + 1, u);
+      v[1] = u[0];
+    }
+  }
+  return make_float2(v[0], v[1]);
+}
+
+template <class T>
+__device__ __forceinline__ void store_pair(T* __restrict__ p, int c, int C, float2 v) {
+  if (c + 1 < C && !(C & 1)) {
+    const float o[2] = {v.x, v.y};
+    store_ch<T, 2>(p, o);
+  } else {
+    const float o0[1] = {v.x}, o1[1] = {v.y};
+    if (c < C) store_ch<T, 1>(p, o0);
+    if (c + 1 < C) store_ch<T, 1>(p + 1, o1);
+  }
+}
+
 // One channel per lane of row `row` (n components of C) into LDS [n][64];
 // lanes past C get 0.
 template <class T>
@@ -172,6 +242,40 @@ __global__ void __launch_bounds__(64 * kGenWaves)
           [&](int i) { return ys[i]; });
       float out[1] = {v};
       if (active) store_ch<T, 1>(z + (row * dout + o) * C + c, out);
+    }
+  }
+}
+
+// k_tp_generic with two channels per lane (one wavefront per row and 128
+// channels): the per-record scalar work, the index arithmetic and the
+// harmonic reads are shared by the two channels.
+template <class T>
+__global__ void __launch_bounds__(256)
+    k_tp_generic2(int64_t n_rows, int C, int dx, int dy, int dout, int np,
+                  const int* __restrict__ prog, int64_t n_words, const T* __restrict__ x,
+                  const float* __restrict__ y, const T* __restrict__ w, T* __restrict__ z) {
+  const Table t = table_view(prog, n_words, dout);
+  extern __shared__ float gsm2[];
+  const int waves = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float2* xs = reinterpret_cast<float2*>(gsm2 + wave * (dx * 128 + ((dy + 1) & ~1)));
+  float* ys = reinterpret_cast<float*>(xs + dx * 64);
+  const int cw = (C + 127) / 128;  // waves per row
+  const int64_t total = n_rows * cw;
+  for (int64_t item = int64_t(blockIdx.x) * waves + wave; item < total;
+       item += int64_t(gridDim.x) * waves) {
+    const int64_t row = item / cw;
+    const int c = int(item % cw) * 128 + 2 * lane;
+    wave_lds_fence();  // the previous row's reads are done
+    for (int i = 0; i < dx; ++i) xs[i * 64 + lane] = load_pair<T>(x + (row * dx + i) * C + c, c, C);
+    for (int i = lane; i < dy; i += 64) ys[i] = y[row * dy + i];
+    wave_lds_fence();
+    const T* wr = w + row * np * C + c;
+    for (int o = 0; o < dout; ++o) {
+      const float2 v = key_sum2(
+          t, o, dx, dy, np, xs, lane,
+          [&](int p) { return load_pair<T>(wr + int64_t(p) * C, c, C); },
+          [&](int i) { return ys[i]; });
+      store_pair<T>(z + (row * dout + o) * C + c, c, C, v);
     }
   }
 }
@@ -368,7 +472,24 @@ hipError_t launch_dy(const GenericTpArgs& a, const void* x, const void* w, const
 }
 
 template <class T>
+hipError_t launch2(const GenericTpArgs& a, hipStream_t s) {
+  const int64_t per_wave = int64_t(a.dx) * 128 + ((a.dy + 1) & ~1);  // float2-aligned waves
+  const int wv = waves_for(per_wave);
+  const int64_t items = a.n_rows * ((a.C + 127) / 128);
+  const int64_t blocks = std::min<int64_t>((items + wv - 1) / wv, 256 * 16);
+  hipLaunchKernelGGL(k_tp_generic2<T>, dim3(unsigned(blocks)), dim3(64 * wv),
+                     size_t(per_wave * wv) * sizeof(float), s, a.n_rows, a.C, a.dx, a.dy, a.dout,
+                     a.np, a.prog, a.n_words, static_cast<const T*>(a.x), a.y,
+                     static_cast<const T*>(a.w), static_cast<T*>(a.z));
+  return hipGetLastError();
+}
+
+// Two channels per lane halve the per-record scalar and index work but
+// double the LDS row; above 16 KB per wavefront (degree 5 and up with every
+// irrep once) the lost occupancy costs more than that saves (measured).
+template <class T>
 hipError_t launch(const GenericTpArgs& a, hipStream_t s) {
+  if (a.C > 64 && int64_t(a.dx) * 128 + a.dy <= 4096) return launch2<T>(a, s);
   const size_t lds = size_t(kGenWaves) * (a.dx * 64 + a.dy) * sizeof(float);
   const int64_t items = a.n_rows * ((a.C + 63) / 64);
   const int64_t blocks = std::min<int64_t>((items + kGenWaves - 1) / kGenWaves, 256 * 8);

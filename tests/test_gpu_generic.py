@@ -55,7 +55,7 @@ def test_generic_tp_matches_oracle(gpu, L, skew):
     assert_close(z, O.tp_forward(od, x, y, w), TOL_F32, f"generic tp L={L} skew={skew}")
 
 
-@pytest.mark.parametrize("C", [1, 32, 192])
+@pytest.mark.parametrize("C", [1, 32, 97, 130, 192])
 def test_generic_tp_channel_counts(gpu, C):
     d, od, x, y, w = _case(4, C, 41, 310 + C)
     z = host(gpu.tp_forward_generic(d, dev(x), dev(y), dev(w)))
@@ -182,3 +182,14 @@ def test_harmonics_gradient_to_degree_six(gpu, lmax):
     g = host(gpu.spherical_harmonics_backward(lmax, dev(v), dev(dY)))
     assert_close(g, O.sh_grad_fd(lmax, v, dY), TOL_F32, f"harmonics gradient l<={lmax}")
     assert np.all(g[5] == 0.0)
+
+
+@pytest.mark.parametrize("C", [97, 130])
+def test_generic_tp_backward_odd_channel_counts(gpu, C):
+    # two channels per lane with an odd count or a partial second chunk
+    d, od, x, y, w = _case(3, C, 45, 395 + C)
+    dz = np.random.default_rng(396).standard_normal((45, d.dout, C)).astype(np.float32)
+    got = gpu.tp_backward_generic(d, dev(x), dev(y), dev(w), dev(dz))
+    torch.cuda.synchronize()
+    for k, a, b in zip(("dx", "dw", "dy"), got, O.tp_backward(od, x, y, w, dz)):
+        assert_close(host(a), b, TOL_F32, f"generic tp backward C={C}:{k}")
