@@ -323,16 +323,21 @@ __global__ void __launch_bounds__(256)
 
 // -------------------------------------------------------------- convolution
 
-// Segment sum over a node's edge list (e3j E.1 Eq.12-13; the receiver-side
-// accumulation in a shared-memory message buffer of its CUDA convolution):
+constexpr int kKeyBlock = 16;  // keys whose sums are held in registers per pass
+
+// Segment sum over a node's edge list (e3j E.1 Eq.12-13):
 //   out[node][k] = sum_{j in seg[node]..seg[node+1]} key_k(op[nbr[j]], Y_e, w[e]),
 // e = emap[j] (or j).  With the forward table, seg = the receiver CSR and
 // nbr = sender: the convolution.  With the dx table over the sender-ordered
 // index (seg = colptr, emap = perm, nbr = recv, op = dm): the gradient of x.
-// One wavefront per (node, 64 channels); the accumulator [dkey][64] is in
-// LDS, the edges are taken in list order, so the result is reproducible.
+// One wavefront per (node, 64 CPL channels).  e3j's CUDA convolution keeps
+// the node's messages in a shared-memory buffer; here the sums of
+// kKeyBlock keys at a time sit in registers and the edge list is walked
+// once per block of keys (the neighbour rows come again from L2), which
+// leaves LDS to the staged row alone and doubles the wavefronts per CU.
+// The edges are taken in list order, so the result is reproducible.
 // Entries whose neighbour is out of [0, n_nodes) (padding) are skipped.
-template <class T, int LY>
+template <class T, int LY, int CPL>
 __global__ void __launch_bounds__(256)
     k_conv_generic_seg(int n_nodes, int n_edges, int C, int dop, int dy, int dkey, int np,
                        const int* __restrict__ prog, int64_t n_words,
@@ -340,44 +345,70 @@ __global__ void __launch_bounds__(256)
                        const int* __restrict__ emap, const int* __restrict__ nbr,
                        const float* __restrict__ yv, YMap ym, const T* __restrict__ op,
                        const T* __restrict__ w, T* __restrict__ out) {
+  static_assert(CPL == 1 || CPL == 2, "one or two channels per lane");
   const Table t = table_view(prog, n_words, dkey);
   extern __shared__ float csm[];
   const int waves = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float* xs = csm + wave * ((dop + dkey) * 64 + dy);  // [dop][64]
-  float* acc = xs + dop * 64;                          // [dkey][64]
-  float* ys = acc + dkey * 64;                         // [dy]
+  float* xs = csm + wave * (dop * 64 * CPL + ((dy + 1) & ~1));  // [dop][64] x CPL
+  float* ys = xs + dop * 64 * CPL;                              // [dy]
   const int want = (LY >= 0 && lane < dy) ? ym.idx[lane] : -1;
-  const int cw = (C + 63) / 64;
+  constexpr int CW = 64 * CPL;
+  const int cw = (C + CW - 1) / CW;
   const int64_t total = int64_t(n_nodes) * cw;
   for (int64_t item = int64_t(blockIdx.x) * waves + wave; item < total;
        item += int64_t(gridDim.x) * waves) {
     const int slot = int(item / cw);
     int node = order ? order[slot] : slot;
     node = min(max(node, 0), n_nodes - 1);
-    const int c = int(item % cw) * 64 + lane;
+    const int c = int(item % cw) * CW + CPL * lane;
     const bool active = c < C;
-    for (int k = 0; k < dkey; ++k) acc[k * 64 + lane] = 0.0f;
     const int jb = max(seg[node], 0), je = min(seg[node + 1], n_edges);
-    for (int j = jb; j < je; ++j) {
-      const int a = nbr[j];
-      const int e = emap ? emap[j] : j;
-      if (a < 0 || a >= n_nodes || e < 0 || e >= n_edges) continue;
-      wave_lds_fence();  // the previous edge's reads of xs and ys are done
-      stage_rows<T>(op, a, dop, C, c, active, xs, lane);
-      stage_edge_y<LY>(yv, e, dy, want, ys, lane);
-      wave_lds_fence();
-      const T* wr = w + int64_t(e) * np * C + c;
-      for (int k = 0; k < dkey; ++k) {
-        const float v = key_sum(
-            t, k, dop, dy, np, xs, lane,
-            [&](int p) { return load1<T>(wr + int64_t(p) * C, active); },
-            [&](int i) { return ys[i]; });
-        acc[k * 64 + lane] += v;
+    for (int kb = 0; kb < dkey; kb += kKeyBlock) {
+      float acc[kKeyBlock][CPL] = {};
+      for (int j = jb; j < je; ++j) {
+        const int a = nbr[j];
+        const int e = emap ? emap[j] : j;
+        if (a < 0 || a >= n_nodes || e < 0 || e >= n_edges) continue;
+        wave_lds_fence();  // the previous edge's reads of xs and ys are done
+        if constexpr (CPL == 1) {
+          stage_rows<T>(op, a, dop, C, c, active, xs, lane);
+        } else {
+          float2* x2 = reinterpret_cast<float2*>(xs);
+          for (int i = 0; i < dop; ++i)
+            x2[i * 64 + lane] = load_pair<T>(op + (int64_t(a) * dop + i) * C + c, c, C);
+        }
+        stage_edge_y<LY>(yv, e, dy, want, ys, lane);
+        wave_lds_fence();
+        const T* wr = w + int64_t(e) * np * C + c;
+        sfor<0, kKeyBlock>([&](auto q) {
+          if (kb + q < dkey) {
+            if constexpr (CPL == 1) {
+              acc[q][0] += key_sum(
+                  t, kb + q, dop, dy, np, xs, lane,
+                  [&](int p) { return load1<T>(wr + int64_t(p) * C, active); },
+                  [&](int i) { return ys[i]; });
+            } else {
+              const float2 v = key_sum2(
+                  t, kb + q, dop, dy, np, reinterpret_cast<const float2*>(xs), lane,
+                  [&](int p) { return load_pair<T>(wr + int64_t(p) * C, c, C); },
+                  [&](int i) { return ys[i]; });
+              acc[q][0] += v.x;
+              acc[q][1] += v.y;
+            }
+          }
+        });
       }
-    }
-    for (int k = 0; k < dkey; ++k) {
-      float v[1] = {acc[k * 64 + lane]};
-      if (active) store_ch<T, 1>(out + (int64_t(node) * dkey + k) * C + c, v);
+      sfor<0, kKeyBlock>([&](auto q) {
+        if (kb + q < dkey) {
+          T* o = out + (int64_t(node) * dkey + kb + q) * C + c;
+          if constexpr (CPL == 1) {
+            const float v[1] = {acc[q][0]};
+            if (active) store_ch<T, 1>(o, v);
+          } else {
+            store_pair<T>(o, c, C, make_float2(acc[q][0], acc[q][1]));
+          }
+        }
+      });
     }
   }
 }
@@ -500,18 +531,25 @@ hipError_t launch(const GenericTpArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <class T, int LY>
-hipError_t launch_seg(const GenericConvArgs& a, hipStream_t s) {
-  const int64_t per_wave = int64_t(a.dop + a.dkey) * 64 + a.dy;
+template <class T, int LY, int CPL>
+hipError_t launch_seg_cpl(const GenericConvArgs& a, hipStream_t s) {
+  const int64_t per_wave = int64_t(a.dop) * 64 * CPL + ((a.dy + 1) & ~1);
   const int wv = waves_for(per_wave);
-  const int64_t items = int64_t(a.n_nodes) * ((a.C + 63) / 64);
+  const int64_t items = int64_t(a.n_nodes) * ((a.C + 64 * CPL - 1) / (64 * CPL));
   const int64_t blocks = std::min<int64_t>((items + wv - 1) / wv, 256 * 16);
-  hipLaunchKernelGGL((k_conv_generic_seg<T, LY>), dim3(unsigned(blocks)), dim3(64 * wv),
+  hipLaunchKernelGGL((k_conv_generic_seg<T, LY, CPL>), dim3(unsigned(blocks)), dim3(64 * wv),
                      size_t(per_wave * wv) * sizeof(float), s, a.n_nodes, a.n_edges, a.C, a.dop,
-                     a.dy, a.dkey, a.np, a.prog, a.n_words, a.order, a.seg, a.emap, a.nbr, a.yv, a.ym,
-                     static_cast<const T*>(a.op), static_cast<const T*>(a.w),
+                     a.dy, a.dkey, a.np, a.prog, a.n_words, a.order, a.seg, a.emap, a.nbr, a.yv,
+                     a.ym, static_cast<const T*>(a.op), static_cast<const T*>(a.w),
                      static_cast<T*>(a.out));
   return hipGetLastError();
+}
+
+// Two channels per lane when the row fits 16 KB of LDS (as for the product).
+template <class T, int LY>
+hipError_t launch_seg(const GenericConvArgs& a, hipStream_t s) {
+  if (a.C > 64 && int64_t(a.dop) * 128 + a.dy <= 4096) return launch_seg_cpl<T, LY, 2>(a, s);
+  return launch_seg_cpl<T, LY, 1>(a, s);
 }
 
 template <class T, int LY>

@@ -77,8 +77,8 @@ def _check(got, ref, tol, name):
         assert_close(a, b, tol, f"{name}:{k}", bf16_out=bf and k != "dY")
 
 
-@pytest.mark.parametrize("L,skew,C", [(1, False, 32), (2, False, 128), (4, False, 96),
-                                      (6, False, 128), (5, True, 64)])
+@pytest.mark.parametrize("L,skew,C", [(1, False, 32), (2, False, 128), (3, False, 97),
+                                      (4, False, 96), (6, False, 128), (5, True, 64)])
 def test_generic_conv_matches_oracle(gpu, L, skew, C):
     xi = oi = S.degree_irreps(L, skew)
     yi = S.sh_irreps(L)
