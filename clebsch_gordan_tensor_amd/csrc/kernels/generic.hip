@@ -413,30 +413,103 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// Per-edge cotangents of the convolution, receiver by receiver:
+// Weight cotangent of the convolution, receiver by receiver:
 //   dw[e][P][c] = sum_o dm[b][o][c] sum_records c y_e[yi] x[a][xi][c]   (dw table)
-//   dY[e][i]    = sum_c sum_P w[e][P][c] sum_records c x[a][xi][c] dm[b][o][c]
-//                                                                      (dy table)
-// for every edge e = (a -> b).  One wavefront per receiver b takes its edges
-// in order and, per edge, all channel chunks (dY sums over them in chunk
-// order).  Padding edges get dw = 0 and dY = 0.
-template <class T, int LY>
+// for every edge e = (a -> b).  One wavefront per (receiver b, 64 CPL
+// channels) takes its edges in order; per edge only x[a] and the harmonics
+// are staged in LDS, the weights dm[b][o] of the contributions come through
+// the cache (the same row for all of b's edges).  Padding edges get dw = 0.
+template <class T, int LY, int CPL>
 __global__ void __launch_bounds__(256)
-    k_conv_generic_edge(int n_nodes, int n_edges, int C, int dx, int dy, int dout, int np,
-                        const int* __restrict__ pdw, int64_t dw_words,
-                        const int* __restrict__ pdy, int64_t dy_words,
-                        const int* __restrict__ order, const int* __restrict__ rowptr,
-                        const int* __restrict__ sender, const float* __restrict__ yv, YMap ym,
-                        const T* __restrict__ x, const T* __restrict__ w,
-                        const T* __restrict__ dm, T* __restrict__ dw, float* __restrict__ dY) {
-  const Table tw = table_view(pdw, dw_words, np), ty = table_view(pdy, dy_words, dy);
+    k_conv_generic_dw(int n_nodes, int n_edges, int C, int dx, int dy, int dout, int np,
+                      const int* __restrict__ pdw, int64_t dw_words,
+                      const int* __restrict__ order, const int* __restrict__ rowptr,
+                      const int* __restrict__ sender, const float* __restrict__ yv, YMap ym,
+                      const T* __restrict__ x, const T* __restrict__ dm, T* __restrict__ dw) {
+  static_assert(CPL == 1 || CPL == 2, "one or two channels per lane");
+  const Table tw = table_view(pdw, dw_words, np);
+  extern __shared__ float wsm[];
+  const int waves = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* xs = wsm + wave * (dx * 64 * CPL + ((dy + 1) & ~1));  // [dx][64] x CPL
+  float* ys = xs + dx * 64 * CPL;                              // [dy]
+  const int want = (LY >= 0 && lane < dy) ? ym.idx[lane] : -1;
+  constexpr int CW = 64 * CPL;
+  const int cw = (C + CW - 1) / CW;
+  const int64_t total = int64_t(n_nodes) * cw;
+  for (int64_t item = int64_t(blockIdx.x) * waves + wave; item < total;
+       item += int64_t(gridDim.x) * waves) {
+    const int slot = int(item / cw);
+    int b = order ? order[slot] : slot;
+    b = min(max(b, 0), n_nodes - 1);
+    const int c = int(item % cw) * CW + CPL * lane;
+    const bool active = c < C;
+    const T* gr = dm + int64_t(b) * dout * C + c;
+    const int jb = max(rowptr[b], 0), je = min(rowptr[b + 1], n_edges);
+    for (int e = jb; e < je; ++e) {
+      const int a = sender[e];
+      T* de = dw + int64_t(e) * np * C + c;
+      if (a < 0 || a >= n_nodes) {  // padding
+        for (int p = 0; p < np; ++p) {
+          if constexpr (CPL == 1) {
+            const float z[1] = {0.0f};
+            if (active) store_ch<T, 1>(de + int64_t(p) * C, z);
+          } else {
+            store_pair<T>(de + int64_t(p) * C, c, C, make_float2(0.0f, 0.0f));
+          }
+        }
+        continue;
+      }
+      wave_lds_fence();  // the previous edge's reads are done
+      if constexpr (CPL == 1) {
+        stage_rows<T>(x, a, dx, C, c, active, xs, lane);
+      } else {
+        float2* x2 = reinterpret_cast<float2*>(xs);
+        for (int i = 0; i < dx; ++i)
+          x2[i * 64 + lane] = load_pair<T>(x + (int64_t(a) * dx + i) * C + c, c, C);
+      }
+      stage_edge_y<LY>(yv, e, dy, want, ys, lane);
+      wave_lds_fence();
+      for (int p = 0; p < np; ++p) {
+        if constexpr (CPL == 1) {
+          const float v = key_sum(
+              tw, p, dx, dy, dout, xs, lane,
+              [&](int o) { return load1<T>(gr + int64_t(o) * C, active); },
+              [&](int i) { return ys[i]; });
+          const float o1[1] = {v};
+          if (active) store_ch<T, 1>(de + int64_t(p) * C, o1);
+        } else {
+          const float2 v = key_sum2(
+              tw, p, dx, dy, dout, reinterpret_cast<const float2*>(xs), lane,
+              [&](int o) { return load_pair<T>(gr + int64_t(o) * C, c, C); },
+              [&](int i) { return ys[i]; });
+          store_pair<T>(de + int64_t(p) * C, c, C, v);
+        }
+      }
+    }
+  }
+}
+
+// Harmonic cotangent of the convolution, receiver by receiver:
+//   dY[e][i] = sum_c sum_P w[e][P][c] sum_records c x[a][xi][c] dm[b][o][c]  (dy table)
+// for every edge e = (a -> b).  One wavefront per receiver b takes its edges
+// in order and, per edge, all channel chunks: x[a] and dm[b] are staged (both
+// are per-lane factors of a record), each key is closed over the lanes with
+// wave_sum and the chunk sums are added in chunk order.  Padding edges get
+// dY = 0.
+template <class T>
+__global__ void __launch_bounds__(256)
+    k_conv_generic_dY(int n_nodes, int n_edges, int C, int dx, int dy, int dout, int np,
+                      const int* __restrict__ pdy, int64_t dy_words,
+                      const int* __restrict__ order, const int* __restrict__ rowptr,
+                      const int* __restrict__ sender, const T* __restrict__ x,
+                      const T* __restrict__ w, const T* __restrict__ dm,
+                      float* __restrict__ dY) {
+  const Table ty = table_view(pdy, dy_words, dy);
   extern __shared__ float esm[];
   const int waves = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float* xs = esm + wave * ((dx + dout) * 64 + 2 * dy);  // [dx][64]
-  float* gs = xs + dx * 64;                                // [dout][64]
-  float* ys = gs + dout * 64;                              // [dy]
-  float* accy = ys + dy;                                   // [dy]
-  const int want = (LY >= 0 && lane < dy) ? ym.idx[lane] : -1;
+  float* xs = esm + wave * ((dx + dout) * 64 + dy);  // [dx][64]
+  float* gs = xs + dx * 64;                           // [dout][64]
+  float* accy = gs + dout * 64;                       // [dy]
   for (int64_t slot = int64_t(blockIdx.x) * waves + wave; slot < n_nodes;
        slot += int64_t(gridDim.x) * waves) {
     int b = order ? order[slot] : int(slot);
@@ -445,29 +518,16 @@ __global__ void __launch_bounds__(256)
     for (int e = jb; e < je; ++e) {
       const int a = sender[e];
       if (a < 0 || a >= n_nodes) {  // padding
-        for (int c = lane; c < np * C; c += 64) {
-          float z[1] = {0.0f};
-          store_ch<T, 1>(dw + int64_t(e) * np * C + c, z);
-        }
         for (int i = lane; i < dy; i += 64) dY[int64_t(e) * dy + i] = 0.0f;
         continue;
       }
-      wave_lds_fence();  // the previous edge's reads are done
-      stage_edge_y<LY>(yv, e, dy, want, ys, lane);
       for (int c0 = 0; c0 < C; c0 += 64) {
         const int c = c0 + lane;
         const bool active = c < C;
-        wave_lds_fence();
+        wave_lds_fence();  // the previous chunk's (or edge's) reads are done
         stage_rows<T>(x, a, dx, C, c, active, xs, lane);
         stage_rows<T>(dm, b, dout, C, c, active, gs, lane);
         wave_lds_fence();
-        for (int p = 0; p < np; ++p) {
-          const float v = key_sum(
-              tw, p, dx, dy, dout, xs, lane, [&](int o) { return gs[o * 64 + lane]; },
-              [&](int i) { return ys[i]; });
-          float o1[1] = {v};
-          if (active) store_ch<T, 1>(dw + (int64_t(e) * np + p) * C + c, o1);
-        }
         const T* wr = w + int64_t(e) * np * C + c;
         for (int i = 0; i < dy; ++i) {
           const float v = key_sum(
@@ -552,17 +612,35 @@ hipError_t launch_seg(const GenericConvArgs& a, hipStream_t s) {
   return launch_seg_cpl<T, LY, 1>(a, s);
 }
 
+template <class T, int LY, int CPL>
+hipError_t launch_dw_cpl(const GenericConvEdgeArgs& a, hipStream_t s) {
+  const int64_t per_wave = int64_t(a.dx) * 64 * CPL + ((a.dy + 1) & ~1);
+  const int wv = waves_for(per_wave);
+  const int64_t items = int64_t(a.n_nodes) * ((a.C + 64 * CPL - 1) / (64 * CPL));
+  const int64_t blocks = std::min<int64_t>((items + wv - 1) / wv, 256 * 16);
+  hipLaunchKernelGGL((k_conv_generic_dw<T, LY, CPL>), dim3(unsigned(blocks)), dim3(64 * wv),
+                     size_t(per_wave * wv) * sizeof(float), s, a.n_nodes, a.n_edges, a.C, a.dx,
+                     a.dy, a.dout, a.np, a.dw_prog, a.dw_words, a.order, a.rowptr, a.sender, a.yv,
+                     a.ym, static_cast<const T*>(a.x), static_cast<const T*>(a.dm),
+                     static_cast<T*>(a.dw));
+  return hipGetLastError();
+}
+
+// dw (two channels per lane when the row fits, as for the forward), then dY.
 template <class T, int LY>
 hipError_t launch_edge(const GenericConvEdgeArgs& a, hipStream_t s) {
-  const int64_t per_wave = int64_t(a.dx + a.dout) * 64 + 2 * a.dy;
+  hipError_t err = (a.C > 64 && int64_t(a.dx) * 128 + a.dy <= 4096)
+                       ? launch_dw_cpl<T, LY, 2>(a, s)
+                       : launch_dw_cpl<T, LY, 1>(a, s);
+  if (err != hipSuccess) return err;
+  const int64_t per_wave = int64_t(a.dx + a.dout) * 64 + a.dy;
   const int wv = waves_for(per_wave);
   const int64_t blocks = std::min<int64_t>((int64_t(a.n_nodes) + wv - 1) / wv, 256 * 16);
-  hipLaunchKernelGGL((k_conv_generic_edge<T, LY>), dim3(unsigned(blocks)), dim3(64 * wv),
+  hipLaunchKernelGGL(k_conv_generic_dY<T>, dim3(unsigned(blocks)), dim3(64 * wv),
                      size_t(per_wave * wv) * sizeof(float), s, a.n_nodes, a.n_edges, a.C, a.dx,
-                     a.dy, a.dout, a.np, a.dw_prog, a.dw_words, a.dy_prog, a.dy_words, a.order,
-                     a.rowptr, a.sender, a.yv, a.ym, static_cast<const T*>(a.x),
-                     static_cast<const T*>(a.w), static_cast<const T*>(a.dm),
-                     static_cast<T*>(a.dw), a.dY);
+                     a.dy, a.dout, a.np, a.dy_prog, a.dy_words, a.order, a.rowptr, a.sender,
+                     static_cast<const T*>(a.x), static_cast<const T*>(a.w),
+                     static_cast<const T*>(a.dm), a.dY);
   return hipGetLastError();
 }
 
