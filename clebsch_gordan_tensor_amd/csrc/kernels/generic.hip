@@ -325,6 +325,16 @@ __global__ void __launch_bounds__(256)
 
 constexpr int kKeyBlock = 16;  // keys whose sums are held in registers per pass
 
+// The keys [k0, k1) of work slice blockIdx.y of gridDim.y: a node's keys are
+// split into slices of whole kKeyBlock blocks when the graph alone does not
+// give the chip enough wavefronts (each slice re-stages its neighbours' rows).
+__device__ __forceinline__ void key_slice(int keys, int& k0, int& k1) {
+  const int blocks = (keys + kKeyBlock - 1) / kKeyBlock;
+  const int per = (blocks + int(gridDim.y) - 1) / int(gridDim.y) * kKeyBlock;
+  k0 = int(blockIdx.y) * per;
+  k1 = min(keys, k0 + per);
+}
+
 // Segment sum over a node's edge list (e3j E.1 Eq.12-13):
 //   out[node][k] = sum_{j in seg[node]..seg[node+1]} key_k(op[nbr[j]], Y_e, w[e]),
 // e = emap[j] (or j).  With the forward table, seg = the receiver CSR and
@@ -363,7 +373,9 @@ __global__ void __launch_bounds__(256)
     const int c = int(item % cw) * CW + CPL * lane;
     const bool active = c < C;
     const int jb = max(seg[node], 0), je = min(seg[node + 1], n_edges);
-    for (int kb = 0; kb < dkey; kb += kKeyBlock) {
+    int k0, k1;
+    key_slice(dkey, k0, k1);
+    for (int kb = k0; kb < k1; kb += kKeyBlock) {
       float acc[kKeyBlock][CPL] = {};
       for (int j = jb; j < je; ++j) {
         const int a = nbr[j];
@@ -381,7 +393,7 @@ __global__ void __launch_bounds__(256)
         wave_lds_fence();
         const T* wr = w + int64_t(e) * np * C + c;
         sfor<0, kKeyBlock>([&](auto q) {
-          if (kb + q < dkey) {
+          if (kb + q < k1) {
             if constexpr (CPL == 1) {
               acc[q][0] += key_sum(
                   t, kb + q, dop, dy, np, xs, lane,
@@ -399,7 +411,7 @@ __global__ void __launch_bounds__(256)
         });
       }
       sfor<0, kKeyBlock>([&](auto q) {
-        if (kb + q < dkey) {
+        if (kb + q < k1) {
           T* o = out + (int64_t(node) * dkey + kb + q) * C + c;
           if constexpr (CPL == 1) {
             const float v[1] = {acc[q][0]};
@@ -444,12 +456,14 @@ __global__ void __launch_bounds__(256)
     const int c = int(item % cw) * CW + CPL * lane;
     const bool active = c < C;
     const T* gr = dm + int64_t(b) * dout * C + c;
+    int p0, p1;  // this slice's paths
+    key_slice(np, p0, p1);
     const int jb = max(rowptr[b], 0), je = min(rowptr[b + 1], n_edges);
     for (int e = jb; e < je; ++e) {
       const int a = sender[e];
       T* de = dw + int64_t(e) * np * C + c;
       if (a < 0 || a >= n_nodes) {  // padding
-        for (int p = 0; p < np; ++p) {
+        for (int p = p0; p < p1; ++p) {
           if constexpr (CPL == 1) {
             const float z[1] = {0.0f};
             if (active) store_ch<T, 1>(de + int64_t(p) * C, z);
@@ -469,7 +483,7 @@ __global__ void __launch_bounds__(256)
       }
       stage_edge_y<LY>(yv, e, dy, want, ys, lane);
       wave_lds_fence();
-      for (int p = 0; p < np; ++p) {
+      for (int p = p0; p < p1; ++p) {
         if constexpr (CPL == 1) {
           const float v = key_sum(
               tw, p, dx, dy, dout, xs, lane,
@@ -514,11 +528,13 @@ __global__ void __launch_bounds__(256)
        slot += int64_t(gridDim.x) * waves) {
     int b = order ? order[slot] : int(slot);
     b = min(max(b, 0), n_nodes - 1);
+    int i0, i1;  // this slice's harmonic components
+    key_slice(dy, i0, i1);
     const int jb = max(rowptr[b], 0), je = min(rowptr[b + 1], n_edges);
     for (int e = jb; e < je; ++e) {
       const int a = sender[e];
       if (a < 0 || a >= n_nodes) {  // padding
-        for (int i = lane; i < dy; i += 64) dY[int64_t(e) * dy + i] = 0.0f;
+        for (int i = i0 + lane; i < i1; i += 64) dY[int64_t(e) * dy + i] = 0.0f;
         continue;
       }
       for (int c0 = 0; c0 < C; c0 += 64) {
@@ -529,7 +545,7 @@ __global__ void __launch_bounds__(256)
         stage_rows<T>(dm, b, dout, C, c, active, gs, lane);
         wave_lds_fence();
         const T* wr = w + int64_t(e) * np * C + c;
-        for (int i = 0; i < dy; ++i) {
+        for (int i = i0; i < i1; ++i) {
           const float v = key_sum(
               ty, i, dx, dout, np, xs, lane,
               [&](int p) { return load1<T>(wr + int64_t(p) * C, active); },
@@ -539,9 +555,17 @@ __global__ void __launch_bounds__(256)
         }
       }
       wave_lds_fence();
-      for (int i = lane; i < dy; i += 64) dY[int64_t(e) * dy + i] = C > 0 ? accy[i] : 0.0f;
+      for (int i = i0 + lane; i < i1; i += 64) dY[int64_t(e) * dy + i] = C > 0 ? accy[i] : 0.0f;
     }
   }
+}
+
+// Key slices per (node, channel chunk) item: enough for about 16,384 work
+// items on small graphs, at most one per block of kKeyBlock keys.
+unsigned key_slices(int64_t node_items, int keys) {
+  const int blocks = (keys + kKeyBlock - 1) / kKeyBlock;
+  const int64_t want = (16384 + node_items - 1) / std::max<int64_t>(node_items, 1);
+  return unsigned(std::max<int64_t>(1, std::min<int64_t>(blocks, want)));
 }
 
 // Waves per workgroup for a per-wave LDS need (floats), within 64 KiB.
@@ -596,8 +620,9 @@ hipError_t launch_seg_cpl(const GenericConvArgs& a, hipStream_t s) {
   const int64_t per_wave = int64_t(a.dop) * 64 * CPL + ((a.dy + 1) & ~1);
   const int wv = waves_for(per_wave);
   const int64_t items = int64_t(a.n_nodes) * ((a.C + 64 * CPL - 1) / (64 * CPL));
-  const int64_t blocks = std::min<int64_t>((items + wv - 1) / wv, 256 * 16);
-  hipLaunchKernelGGL((k_conv_generic_seg<T, LY, CPL>), dim3(unsigned(blocks)), dim3(64 * wv),
+  const unsigned ks = key_slices(items, a.dkey);
+  const int64_t blocks = std::min<int64_t>((items + wv - 1) / wv, 256 * 16 / ks + 1);
+  hipLaunchKernelGGL((k_conv_generic_seg<T, LY, CPL>), dim3(unsigned(blocks), ks), dim3(64 * wv),
                      size_t(per_wave * wv) * sizeof(float), s, a.n_nodes, a.n_edges, a.C, a.dop,
                      a.dy, a.dkey, a.np, a.prog, a.n_words, a.order, a.seg, a.emap, a.nbr, a.yv,
                      a.ym, static_cast<const T*>(a.op), static_cast<const T*>(a.w),
@@ -617,8 +642,9 @@ hipError_t launch_dw_cpl(const GenericConvEdgeArgs& a, hipStream_t s) {
   const int64_t per_wave = int64_t(a.dx) * 64 * CPL + ((a.dy + 1) & ~1);
   const int wv = waves_for(per_wave);
   const int64_t items = int64_t(a.n_nodes) * ((a.C + 64 * CPL - 1) / (64 * CPL));
-  const int64_t blocks = std::min<int64_t>((items + wv - 1) / wv, 256 * 16);
-  hipLaunchKernelGGL((k_conv_generic_dw<T, LY, CPL>), dim3(unsigned(blocks)), dim3(64 * wv),
+  const unsigned ks = key_slices(items, a.np);
+  const int64_t blocks = std::min<int64_t>((items + wv - 1) / wv, 256 * 16 / ks + 1);
+  hipLaunchKernelGGL((k_conv_generic_dw<T, LY, CPL>), dim3(unsigned(blocks), ks), dim3(64 * wv),
                      size_t(per_wave * wv) * sizeof(float), s, a.n_nodes, a.n_edges, a.C, a.dx,
                      a.dy, a.dout, a.np, a.dw_prog, a.dw_words, a.order, a.rowptr, a.sender, a.yv,
                      a.ym, static_cast<const T*>(a.x), static_cast<const T*>(a.dm),
@@ -635,8 +661,9 @@ hipError_t launch_edge(const GenericConvEdgeArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   const int64_t per_wave = int64_t(a.dx + a.dout) * 64 + a.dy;
   const int wv = waves_for(per_wave);
-  const int64_t blocks = std::min<int64_t>((int64_t(a.n_nodes) + wv - 1) / wv, 256 * 16);
-  hipLaunchKernelGGL(k_conv_generic_dY<T>, dim3(unsigned(blocks)), dim3(64 * wv),
+  const unsigned ksy = key_slices(a.n_nodes, a.dy);
+  const int64_t blocks = std::min<int64_t>((int64_t(a.n_nodes) + wv - 1) / wv, 256 * 16 / ksy + 1);
+  hipLaunchKernelGGL(k_conv_generic_dY<T>, dim3(unsigned(blocks), ksy), dim3(64 * wv),
                      size_t(per_wave * wv) * sizeof(float), s, a.n_nodes, a.n_edges, a.C, a.dx,
                      a.dy, a.dout, a.np, a.dy_prog, a.dy_words, a.order, a.rowptr, a.sender,
                      static_cast<const T*>(a.x), static_cast<const T*>(a.w),
