@@ -717,40 +717,22 @@ namespace {
 // The radial MLP's second layer seen as a channel mixing: input 64x0e (h),
 // output nb blocks of cb x 0e (the columns of w in blocks of cb <= 256).
 struct RadialBwdPlan {
-  int nb = 0, cb = 0;
-  e3_irrep in_v[1], out_v[64];
-  e3_irreps in{}, out{};
-  size_t off_h = 0, off_dh = 0, off_w2p = 0, off_dwp = 0, off_lin = 0, off_part = 0, total = 0;
-  size_t lin_bytes = 0;
+  int ranges = 0;
+  size_t off_dh = 0, off_part2 = 0, off_part = 0, total = 0;
 };
 
 e3_status radial_bwd_plan(int n_edges, int n_cols, RadialBwdPlan& r) {
   if (n_cols <= 0 || n_cols % 32)
     return fail(E3_ERR_UNSUPPORTED, "the radial backward needs n_cols a multiple of 32");
-  for (int cb = 256; cb >= 32; cb -= 32)
-    if (n_cols % cb == 0 && n_cols / cb <= 64) {
-      r.cb = cb;
-      r.nb = n_cols / cb;
-      break;
-    }
-  if (!r.cb) return fail(E3_ERR_UNSUPPORTED, "n_cols too large for the radial backward");
-  r.in_v[0] = e3_irrep{64, 0, 1};
-  for (int j = 0; j < r.nb; ++j) r.out_v[j] = e3_irrep{r.cb, 0, 1};
-  r.in = e3_irreps{1, r.in_v};
-  r.out = e3_irreps{r.nb, r.out_v};
-  e3_status s = e3_linear_workspace_size(&r.in, &r.out, &r.lin_bytes);
-  if (s != E3_OK) return s;
+  r.ranges = e3k::radial_dw2_ranges(n_edges, n_cols);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o += align256(bytes);
     return at;
   };
-  r.off_h = take(size_t(n_edges) * 64 * 4);
   r.off_dh = take(size_t(n_edges) * 64 * 4);
-  r.off_w2p = take(size_t(64) * n_cols * 4);
-  r.off_dwp = take(size_t(64) * n_cols * 4);
-  r.off_lin = take(r.lin_bytes);
+  r.off_part2 = take(size_t(r.ranges) * 64 * n_cols * 4);
   r.off_part = take(size_t(e3k::kRadialTailChunks) * 512 * 4);
   r.total = o;
   return ok();
@@ -782,27 +764,20 @@ e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t 
   if (n_edges > 0 && (!edge_vec || !dw || !dvec)) return fail(E3_ERR_INVALID_ARG, "null pointer");
   if (!workspace || ws_bytes < r.total)
     return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(r.total) + " bytes");
-  if (!aligned16(workspace) || (n_edges > 0 && !aligned16(dw)))
-    return fail(E3_ERR_ALIGNMENT, "workspace and dw must be 16-byte aligned");
+  if (!aligned16(workspace) || !aligned16(mlp->W2) || (n_edges > 0 && !aligned16(dw)))
+    return fail(E3_ERR_ALIGNMENT, "workspace, W2 and dw must be 16-byte aligned");
   const hipStream_t st = hipStream_t(stream);
   char* ws = static_cast<char*>(workspace);
-  float* h = reinterpret_cast<float*>(ws + r.off_h);
   float* dh = reinterpret_cast<float*>(ws + r.off_dh);
-  float* w2p = reinterpret_cast<float*>(ws + r.off_w2p);
-  float* dwp = reinterpret_cast<float*>(ws + r.off_dwp);
+  float* part2 = reinterpret_cast<float*>(ws + r.off_part2);
   float* part = reinterpret_cast<float*>(ws + r.off_part);
-  // h = silu(B W1); W2 into the mixing's [block][64][cb] layout
-  if ((s = hip_status(e3k::launch_radial_hidden(n_edges, edge_vec, mlp->cutoff, mlp->W1, h, st),
+  // dh = dw W2^T, and dW2 = h^T dw through per-range partials (fp32 matrix
+  // cores; dw is read once by each)
+  if ((s = hip_status(e3k::launch_radial_dh_dw2(n_edges, n_cols, edge_vec, mlp->cutoff, mlp->W1,
+                                                mlp->W2, dw, dh, part2, r.ranges, st),
                       "radial_mlp_backward")) != E3_OK)
     return s;
-  if ((s = hip_status(e3k::launch_column_blocks(64, r.nb, r.cb, 1, mlp->W2, w2p, st),
-                      "radial_mlp_backward")) != E3_OK)
-    return s;
-  // dh = dw W2^T and dW2 = h^T dw: the channel-mixing backward of y = h W2
-  if ((s = e3_linear_backward(&r.in, &r.out, n_edges, h, w2p, n_edges > 0 ? dw : h, dh, dwp,
-                              ws + r.off_lin, r.lin_bytes, E3_F32, stream)) != E3_OK)
-    return s;
-  if ((s = hip_status(e3k::launch_column_blocks(64, r.nb, r.cb, 0, dwp, dW2, st),
+  if ((s = hip_status(e3k::launch_sum_partials(r.ranges, 64 * n_cols, part2, dW2, st),
                       "radial_mlp_backward")) != E3_OK)
     return s;
   // through SiLU and the first layer: dW1, and the radial part of dvec

@@ -457,52 +457,6 @@ hipError_t launch_fwd_radial(const RadialConvArgs& a, hipStream_t s) {
 
 // ------------------------------------------------ radial MLP backward
 
-// h[e][k] = silu(B(|r_e|) W1)[k], one thread per edge (the input of the
-// second layer's weight gradient and of dh = dw W2^T).
-__global__ void __launch_bounds__(256)
-    k_radial_hidden(int n_edges, const float* __restrict__ vec, float rc,
-                    const float* __restrict__ W1, float* __restrict__ h) {
-  __shared__ float s_w1[kRadBasis * kRadHidden];
-  for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
-  __syncthreads();
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= n_edges) return;
-  float B[kRadBasis];
-  bessel_basis(vec[int64_t(e) * 3], vec[int64_t(e) * 3 + 1], vec[int64_t(e) * 3 + 2], rc, B);
-  float4v* out = reinterpret_cast<float4v*>(h + int64_t(e) * kRadHidden);
-#pragma unroll
-  for (int q = 0; q < kRadHidden / 4; ++q) {
-    float4v v;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float pre = 0.0f;
-#pragma unroll
-      for (int n = 0; n < kRadBasis; ++n) pre = fmaf(B[n], s_w1[n * kRadHidden + 4 * q + t], pre);
-      v[t] = silu(pre);
-    }
-    out[q] = v;
-  }
-}
-
-// dst[j][k][c] = src[k][j*cb + c] (to_blocks) or the inverse, for a
-// [rows][nb*cb] matrix and its nb column blocks of width cb.
-__global__ void __launch_bounds__(256)
-    k_column_blocks(int rows, int nb, int cb, int to_blocks, const float* __restrict__ src,
-                    float* __restrict__ dst) {
-  const int64_t n = int64_t(rows) * nb * cb;
-  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
-       i += int64_t(gridDim.x) * blockDim.x) {
-    const int c = int(i % cb);
-    const int k = int((i / cb) % rows);
-    const int j = int(i / (int64_t(cb) * rows));
-    const int64_t flat = int64_t(k) * nb * cb + int64_t(j) * cb + c;  // [k][j*cb + c]
-    if (to_blocks)
-      dst[i] = src[flat];
-    else
-      dst[flat] = src[i];
-  }
-}
-
 constexpr int kTailBatch = 64;
 
 // Per edge, from dh = dw W2^T: dpre = dh * silu'(pre), the radial part of
@@ -595,6 +549,185 @@ __global__ void __launch_bounds__(256)
   dW1_part[int64_t(blockIdx.x) * 512 + p1] = acc1;
 }
 
+// The two products of the second layer's backward, each reading dw once, on
+// the fp32 matrix cores with v_mfma_f32_16x16x4f32: A[i][k] comes from lane
+// 16k + i, B[k][j] from lane 16k + j, and D[i][j] sits in register i % 4 of
+// lane j + 16 (i / 4).  A lane loads four consecutive values with one
+// 16-byte access and feeds them to four MFMAs (t = 0..3), so the four k (or
+// j) slots of one MFMA are four values apart in memory; a sum does not care
+// in which order its terms arrive.
+
+// dh[e][k] = sum_j dw[e][j] W2[k][j].  One wavefront per block of 32 edges
+// (two 16-edge row tiles) and all 64 hidden units (four column tiles), four
+// wavefronts per workgroup walking the columns together in blocks of 128:
+// each block's W2 slice [64][128] is staged once in LDS for the four (rows
+// padded by 4 floats: the 16 rows a B load touches fall in distinct banks),
+// and its sum is added to the total (shorter rounding chains than one
+// running sum over all columns).  Per 16 columns MFMA t takes columns
+// j + 4 kq + t.
+constexpr int kDhCols = 128;
+constexpr int kDhLd = kDhCols + 4;
+
+__global__ void __launch_bounds__(256)
+    k_radial_dh(int n_edges, int n_cols, const float* __restrict__ dw,
+                const float* __restrict__ W2, float* __restrict__ dh) {
+  __shared__ float4v s_w2[kRadHidden * kDhLd / 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, kq = lane >> 4;
+  const int64_t n_blocks = (int64_t(n_edges) + 127) / 128;  // 128 edges per workgroup
+  for (int64_t wb = blockIdx.x; wb < n_blocks; wb += gridDim.x) {
+    const int64_t e0 = wb * 128 + 32 * wave;
+    const float* arow[2];
+    bool aval[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int64_t e = e0 + 16 * mt + li;
+      aval[mt] = e < n_edges;
+      arow[mt] = dw + (aval[mt] ? e : 0) * n_cols + 4 * kq;
+    }
+    float4v acc[2][4], bs[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int jb = 0; jb < n_cols; jb += kDhCols) {
+      const int nc = min(kDhCols, n_cols - jb);  // a multiple of 16
+      __syncthreads();  // the previous block's reads of s_w2 are done
+      for (int idx = threadIdx.x; idx < kRadHidden * (nc / 4); idx += 256) {
+        const int k = idx / (nc / 4), c = 4 * (idx - k * (nc / 4));
+        s_w2[(k * kDhLd + c) / 4] =
+            *reinterpret_cast<const float4v*>(W2 + int64_t(k) * n_cols + jb + c);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) bs[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 2
+      for (int j = 0; j < nc; j += 16) {
+        float4v a[2], b[4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          a[mt] = aval[mt] ? *reinterpret_cast<const float4v*>(arow[mt] + jb + j)
+                           : float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) b[nt] = s_w2[((16 * nt + li) * kDhLd + j + 4 * kq) / 4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+              bs[mt][nt] =
+                  __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt][t], b[nt][t], bs[mt][nt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] += bs[mt][nt];
+    }
+    // D row = edge 16 mt + 4 kq + r, column = hidden unit 16 nt + li
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t e = e0 + 16 * mt + 4 * kq + r;
+        if (e < n_edges) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) dh[e * kRadHidden + 16 * nt + li] = acc[mt][nt][r];
+        }
+      }
+  }
+}
+
+constexpr int kDw2Waves = 4;
+constexpr int kDw2Cols = 64 * kDw2Waves;  // columns per workgroup: 64 per wavefront
+
+// Partial weight gradient of the second layer over one range of edges:
+//   part[range][k][c] = sum_{e in range} h[e][k] dw[e][c]
+// for the kDw2Cols-column slab of the workgroup (grid x = slabs, y = edge
+// ranges).  Per block of 64 edges h is recomputed from the edge vectors
+// into LDS (the arithmetic of the forward MLP's hidden layer); each
+// wavefront owns 64 columns, column c_wave + 4 li + t in MFMA t, and all 64
+// hidden units (16 accumulator tiles), so dw is read once, 16 bytes per lane
+// and edge.  The ranges' partials are added afterwards in range order.
+__global__ void __launch_bounds__(64 * kDw2Waves)
+    k_radial_dw2(int n_edges, int n_cols, const float* __restrict__ vec, float rc,
+                 const float* __restrict__ W1, const float* __restrict__ dw,
+                 float* __restrict__ part) {
+  __shared__ float s_w1[kRadBasis * kRadHidden];
+  __shared__ float s_b[64][kRadBasis];
+  __shared__ float s_h[64][kRadHidden + 1];  // [edge][hidden], padded
+  for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, kq = lane >> 4;
+  const int c4 = blockIdx.x * kDw2Cols + 64 * wave + 4 * li;  // this lane's 4 columns
+  const bool cval = c4 < n_cols;  // n_cols is a multiple of 4
+  const int per = ((n_edges + int(gridDim.y) - 1) / int(gridDim.y) + 63) / 64 * 64;
+  const int lo = int(blockIdx.y) * per, hi = min(n_edges, lo + per);
+  const int hk = threadIdx.x & 63;  // hidden unit of this thread's h values
+  float w1c[kRadBasis];
+#pragma unroll
+  for (int n = 0; n < kRadBasis; ++n) w1c[n] = s_w1[n * kRadHidden + hk];
+  float4v acc[4][4];  // [hidden tile][t]
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[mt][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int e0 = lo; e0 < hi; e0 += 64) {
+    if (threadIdx.x < 64) {
+      const int e = e0 + threadIdx.x;
+      float B[kRadBasis];
+      if (e < hi) {
+        bessel_basis(vec[int64_t(e) * 3], vec[int64_t(e) * 3 + 1], vec[int64_t(e) * 3 + 2], rc, B);
+      } else {
+#pragma unroll
+        for (int n = 0; n < kRadBasis; ++n) B[n] = 0.0f;
+      }
+#pragma unroll
+      for (int n = 0; n < kRadBasis; ++n) s_b[threadIdx.x][n] = B[n];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int q = 0; q < 64 / kDw2Waves; ++q) {
+      const int t = (threadIdx.x >> 6) + kDw2Waves * q;
+      float pre = 0.0f;
+#pragma unroll
+      for (int n = 0; n < kRadBasis; ++n) pre = fmaf(s_b[t][n], w1c[n], pre);
+      s_h[t][hk] = e0 + t < hi ? silu(pre) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int ks = 0; ks < 16; ++ks) {
+      const int el = 4 * ks + kq;  // edge of this lane's k slot
+      const int64_t e = e0 + el;
+      float a[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[mt] = s_h[el][16 * mt + li];
+      const float4v b = (e < hi && cval) ? *reinterpret_cast<const float4v*>(dw + e * n_cols + c4)
+                                         : float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt], b[t], acc[mt][t], 0, 0, 0);
+    }
+    __syncthreads();  // s_b and s_h are rewritten by the next block
+  }
+  // D row = hidden unit 16 mt + 4 kq + r, column = c4 + t (lane li's columns)
+  if (cval) {
+    float* pr = part + int64_t(blockIdx.y) * kRadHidden * n_cols + c4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4v v = {acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+        *reinterpret_cast<float4v*>(pr + int64_t(16 * mt + 4 * kq + r) * n_cols) = v;
+      }
+  }
+}
+
 // out[i] = sum_c part[c][i] over n_chunks partials, in chunk order.
 __global__ void __launch_bounds__(256)
     k_sum_partials(int n_chunks, int n, const float* __restrict__ part, float* __restrict__ out) {
@@ -606,24 +739,6 @@ __global__ void __launch_bounds__(256)
 }
 
 }  // namespace
-
-hipError_t launch_radial_hidden(int n_edges, const float* vec, float cutoff, const float* W1,
-                                float* h, hipStream_t s) {
-  if (n_edges <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_radial_hidden, dim3((n_edges + 255) / 256), dim3(256), 0, s, n_edges, vec,
-                     cutoff, W1, h);
-  return hipGetLastError();
-}
-
-hipError_t launch_column_blocks(int rows, int nb, int cb, int to_blocks, const float* src,
-                                float* dst, hipStream_t s) {
-  const int64_t n = int64_t(rows) * nb * cb;
-  if (n <= 0) return hipSuccess;
-  const int grid = int(std::min<int64_t>((n + 255) / 256, 4096));
-  hipLaunchKernelGGL(k_column_blocks, dim3(grid), dim3(256), 0, s, rows, nb, cb, to_blocks, src,
-                     dst);
-  return hipGetLastError();
-}
 
 hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const float* W1,
                               const float* dh, float* dvec, float* dW1_part, float* dW1,
@@ -639,6 +754,36 @@ hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const
 
 bool radial_conv_supported(const char* set_name) {
   return set_name && std::strcmp(set_name, "L1to3") == 0;
+}
+
+int radial_dw2_ranges(int n_edges, int n_cols) {
+  const int slabs = (n_cols + kDw2Cols - 1) / kDw2Cols;
+  const int blocks64 = std::max(1, (n_edges + 63) / 64);
+  return std::max(1, std::min(blocks64, (2048 + slabs - 1) / slabs));
+}
+
+hipError_t launch_radial_dh_dw2(int n_edges, int n_cols, const float* vec, float cutoff,
+                                const float* W1, const float* W2, const float* dw, float* dh,
+                                float* part, int ranges, hipStream_t s) {
+  if (n_edges > 0) {
+    const int64_t n_blocks = (int64_t(n_edges) + 127) / 128;
+    const int g1 = int(std::min<int64_t>(n_blocks, 256 * 8));
+    hipLaunchKernelGGL(k_radial_dh, dim3(g1), dim3(256), 0, s, n_edges, n_cols, dw, W2, dh);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  // with no edges the partials are written as zeros
+  const int slabs = (n_cols + kDw2Cols - 1) / kDw2Cols;
+  hipLaunchKernelGGL(k_radial_dw2, dim3(slabs, ranges), dim3(64 * kDw2Waves), 0, s, n_edges, n_cols, vec,
+                     cutoff, W1, dw, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_partials(int n_chunks, int n, const float* part, float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_sum_partials, dim3((n + 255) / 256), dim3(256), 0, s, n_chunks, n, part,
+                     out);
+  return hipGetLastError();
 }
 
 hipError_t launch_conv_fwd_radial(const char* set_name, const RadialConvArgs& a, hipStream_t s) {

@@ -183,15 +183,19 @@ bool radial_conv_supported(const char* set_name);
 hipError_t launch_conv_fwd_radial(const char* set_name, const RadialConvArgs& a, hipStream_t s);
 hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cutoff,
                              const float* W1, const float* W2, float* w, hipStream_t s);
-// pieces of the radial MLP's backward (the rest is the channel-mixing backward)
+// pieces of the radial MLP's backward
 constexpr int kRadialTailChunks = 1024;
-hipError_t launch_radial_hidden(int n_edges, const float* vec, float cutoff, const float* W1,
-                                float* h, hipStream_t s);
-hipError_t launch_column_blocks(int rows, int nb, int cb, int to_blocks, const float* src,
-                                float* dst, hipStream_t s);
 hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const float* W1,
                               const float* dh, float* dvec, float* dW1_part, float* dW1,
                               hipStream_t s);
+// The second layer's backward from dw [E][n_cols] (n_cols a multiple of
+// 4): dh [E][64] and per-range partials part [ranges][64][n_cols] of dW2
+// (add them with launch_sum_partials).
+int radial_dw2_ranges(int n_edges, int n_cols);
+hipError_t launch_radial_dh_dw2(int n_edges, int n_cols, const float* vec, float cutoff,
+                                const float* W1, const float* W2, const float* dw, float* dh,
+                                float* part, int ranges, hipStream_t s);
+hipError_t launch_sum_partials(int n_chunks, int n, const float* part, float* out, hipStream_t s);
 hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
                                  float* dvec, hipStream_t s);
 hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr,

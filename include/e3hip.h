@@ -224,10 +224,12 @@ e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n
  * through fixed partials: reproducible) and dvec [E][3], the part of the
  * edge-vector gradient that flows through |r_e| (radial: dvec_e is parallel
  * to r_e, zero at r_e = 0); add it to e3_spherical_harmonics_backward's
- * for the full edge-vector gradient.  dh = dw W2^T and dW2 = h^T dw run as
- * the backward of e3_linear (fp32 matrix cores).  workspace: caller-owned,
- * e3_radial_mlp_backward_workspace_size bytes, 16-byte aligned; dw 16-byte
- * aligned.  All arrays float32 on the device. */
+ * for the full edge-vector gradient.  dh = dw W2^T and dW2 = h^T dw run on
+ * the fp32 matrix cores, each reading dw once (dW2 through per-range partial
+ * sums added in a fixed order, h recomputed from the edge vectors).
+ * workspace: caller-owned,
+ * e3_radial_mlp_backward_workspace_size bytes, 16-byte aligned; dw and W2
+ * 16-byte aligned.  All arrays float32 on the device. */
 e3_status e3_radial_mlp_backward_workspace_size(const e3_radial* mlp, int32_t n_edges,
                                                 int32_t n_cols, size_t* bytes);
 e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
