@@ -192,3 +192,23 @@ def test_generic_conv_full_size_sampled(gpu):
     rdw, rdY = O.conv_backward_edge(od, rp, sn, p.x, p.w[ids], p.dm, evec=ev)
     assert_close(dw[edges], rdw, TOL_F32, "deg6:dw")
     assert_close(dY[edges], rdY, TOL_F32, "deg6:dY")
+
+
+def test_generic_conv_graph_without_edges(gpu):
+    # nodes but no edges: m = 0 and dx = 0, empty edge cotangents
+    xi = oi = S.degree_irreps(3)
+    yi = S.sh_irreps(3)
+    n, C = 20, 64
+    d = gpu.Desc(xi, yi, oi, C)
+    rowptr = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    sender = torch.zeros(0, dtype=torch.int32, device="cuda")
+    ev = torch.zeros((0, 3), device="cuda")
+    x = dev(np.random.default_rng(420).standard_normal((n, S.dim(xi), C)).astype(np.float32))
+    w = torch.zeros((0, S.num_paths(xi, yi, oi), C), device="cuda")
+    dm = dev(np.random.default_rng(421).standard_normal((n, S.dim(oi), C)).astype(np.float32))
+    ws = gpu.conv_prepare_transpose(rowptr, sender)
+    m = gpu.conv_forward_generic(d, rowptr, sender, ev, x, w, workspace=ws)
+    dx, dw, dY = gpu.conv_backward_generic(d, rowptr, sender, ws, ev, x, w, dm)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(m) == 0 and torch.count_nonzero(dx) == 0
+    assert dw.numel() == 0 and dY.numel() == 0

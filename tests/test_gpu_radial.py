@@ -202,3 +202,14 @@ def test_radial_mlp_backward_deterministic_and_radial(gpu):
     # the weights depend on |r| only: the edge-vector gradient is parallel to r
     cross = torch.linalg.cross(a[2].double(), ev.double())
     assert cross.abs().max().item() <= 1e-6 * a[2].abs().max().item() * ev.abs().max().item()
+
+
+def test_radial_mlp_backward_no_edges(gpu):
+    # no edges: the weight gradients are zero (written, not left as they were)
+    W1 = dev(np.random.default_rng(5).standard_normal((8, 64)).astype(np.float32))
+    W2 = dev(np.random.default_rng(6).standard_normal((64, 320)).astype(np.float32))
+    ev = torch.zeros((0, 3), device="cuda")
+    dw = torch.zeros((0, 320), device="cuda")
+    dW1, dW2, dvec = gpu.radial_mlp_backward(ev, 5.0, W1, W2, dw)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dW1) == 0 and torch.count_nonzero(dW2) == 0 and dvec.numel() == 0
