@@ -676,6 +676,15 @@ __global__ void __launch_bounds__(64 * kDw2Waves)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[mt][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   for (int e0 = lo; e0 < hi; e0 += 64) {
+    // this block's dw for the 16 k steps, requested before h is built so the
+    // loads' latency overlaps that work
+    float4v bq[16];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const int64_t e = e0 + 4 * ks + kq;
+      bq[ks] = (e < hi && cval) ? *reinterpret_cast<const float4v*>(dw + e * n_cols + c4)
+                                : float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     if (threadIdx.x < 64) {
       const int e = e0 + threadIdx.x;
       float B[kRadBasis];
@@ -698,20 +707,17 @@ __global__ void __launch_bounds__(64 * kDw2Waves)
       s_h[t][hk] = e0 + t < hi ? silu(pre) : 0.0f;
     }
     __syncthreads();
-#pragma unroll 4
+#pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       const int el = 4 * ks + kq;  // edge of this lane's k slot
-      const int64_t e = e0 + el;
       float a[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) a[mt] = s_h[el][16 * mt + li];
-      const float4v b = (e < hi && cval) ? *reinterpret_cast<const float4v*>(dw + e * n_cols + c4)
-                                         : float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt], b[t], acc[mt][t], 0, 0, 0);
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt], bq[ks][t], acc[mt][t], 0, 0, 0);
     }
     __syncthreads();  // s_b and s_h are rewritten by the next block
   }
