@@ -153,14 +153,19 @@ __global__ void __launch_bounds__(kLinBlock)
         mfma8(a, b);
       }
     }
-    // D[i][j]: column j = lane % 32 of each 32-column tile
+    // D[i][j]: column j = lane % 32 of each 32-column tile; the tile's first
+    // component (r0, m0) once, the rest by a 32-bit division of m0 + row
+    const int64_t r0 = (t * 32) / deg;
+    const int m0 = int(t * 32 - r0 * deg);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int row = 8 * (rr / 4) + 4 * s + (rr % 4);
       const int64_t qo = t * 32 + row;
       if (qo >= n_comp) continue;
-      const int64_t ro = qo / deg;
-      const int mo = int(qo - ro * deg);
+      const unsigned mq = unsigned(m0 + row);
+      const unsigned dr = mq / unsigned(deg);
+      const int64_t ro = r0 + dr;
+      const int mo = int(mq - dr * unsigned(deg));
       T* yr = y + (ro * dout + out_off + mo) * int64_t(cout) + col0 + i;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -171,6 +176,105 @@ __global__ void __launch_bounds__(kLinBlock)
           v[0] += o[0];
         }
         store_ch<T, 1>(yr + ct * 32, v);
+      }
+    }
+  }
+}
+
+// bf16 storage on the bf16 matrix cores: v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation, W rounded to bf16 (nearest even) once into the LDS slab.
+// Operand layouts (checked on the hardware): A[i][k] from lane i + 32 (k / 8)
+// element k % 8, B[k][j] from lane j + 32 (k / 8) element k % 8, D as for
+// 32x32x2.  The slab is stored transposed, Wt[column][k], so a lane reads
+// its eight k of one column with one 16-byte LDS load; rows padded by 8
+// bf16.  A lane's eight k of an x row are one 16-byte global load.  NKB =
+// cin / 16: a lane holds its row's whole A operand (NKB x 16 bytes) and
+// loads the next tile's while the matrix cores work on this one.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int kLinPadB = 8;  // bf16 padding of a slab row
+
+template <int NCT, int NKB>
+__global__ void __launch_bounds__(kLinBlock)
+    k_linear_bf16(int64_t n_rows, int din, int dout, int cin, int cout, int in_off, int out_off,
+                  int deg, int col0, const bf16_t* __restrict__ x, const float* __restrict__ W,
+                  int w_ld, int w_trans, bf16_t* __restrict__ y, int accumulate) {
+  extern __shared__ uint4 s_wt[];  // [CW][cin + kLinPadB] bf16, 16-byte units
+  constexpr int CW = NCT * 32;
+  constexpr int KL = 16 * NKB + kLinPadB;  // bf16 per slab row
+  uint16_t* wt = reinterpret_cast<uint16_t*>(s_wt);
+  for (int idx = threadIdx.x; idx < CW * 16 * NKB; idx += kLinBlock) {
+    int c, k;
+    if (!w_trans) {  // consecutive threads along the columns of W[k][.]
+      k = idx / CW;
+      c = idx - k * CW;
+    } else {  // W^T: consecutive threads along k of W[c][.]
+      c = idx / (16 * NKB);
+      k = idx - c * (16 * NKB);
+    }
+    const float v = w_trans ? W[int64_t(col0 + c) * w_ld + k] : W[int64_t(k) * w_ld + col0 + c];
+    wt[c * KL + k] = uint16_t(f32_to_bf16_rne(v));
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 31, kh = lane >> 5;
+  const int64_t n_comp = n_rows * deg;
+  const int64_t n_tiles = (n_comp + 31) / 32;
+  const int64_t waves = int64_t(gridDim.x) * (kLinBlock / 64);
+  auto fetch = [&](int64_t t, uint4 (&a)[NKB]) {
+    const int64_t q = t * 32 + i;
+    const bool valid = q < n_comp;
+    const int64_t qq = valid ? q : 0;
+    const int64_t r = qq / deg;
+    const int m = int(qq - r * deg);
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (r * din + in_off + m) * int64_t(cin)) + kh;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) a[kb] = valid ? xr[2 * kb] : uint4{0u, 0u, 0u, 0u};
+  };
+  int64_t t = int64_t(blockIdx.x) * (kLinBlock / 64) + (threadIdx.x >> 6);
+  uint4 abuf[NKB];
+  if (t < n_tiles) fetch(t, abuf);
+  for (; t < n_tiles; t += waves) {
+    uint4 anext[NKB];
+    if (t + waves < n_tiles) fetch(t + waves, anext);
+    f16v acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f16v{};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, abuf[kb]);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const uint4 bw = s_wt[((32 * ct + i) * KL + 16 * kb + 8 * kh) / 8];
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, bw), acc[ct],
+                                                          0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) abuf[kb] = anext[kb];
+    // D[i][j]: column j = lane % 32 of each 32-column tile; the tile's first
+    // component (r0, m0) once, the rest by a 32-bit division of m0 + row
+    const int64_t r0 = (t * 32) / deg;
+    const int m0 = int(t * 32 - r0 * deg);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int row = 8 * (rr / 4) + 4 * kh + (rr % 4);
+      const int64_t qo = t * 32 + row;
+      if (qo >= n_comp) continue;
+      const unsigned mq = unsigned(m0 + row);
+      const unsigned dr = mq / unsigned(deg);
+      const int64_t ro = r0 + dr;
+      const int mo = int(mq - dr * unsigned(deg));
+      bf16_t* yr = y + (ro * dout + out_off + mo) * int64_t(cout) + col0 + i;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        float v[1] = {acc[ct][rr]};
+        if (accumulate) {
+          float o[1];
+          load_ch<bf16_t, 1>(yr + ct * 32, o);
+          v[0] += o[0];
+        }
+        store_ch<bf16_t, 1>(yr + ct * 32, v);
       }
     }
   }
@@ -210,6 +314,49 @@ hipError_t launch_one(const LinearBlockArgs& a, int col0, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NCT, int NKB>
+hipError_t launch_bf16_one(const LinearBlockArgs& a, int col0, hipStream_t s) {
+  const size_t lds = size_t(NCT * 32) * (16 * NKB + kLinPadB) * 2;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_linear_bf16<NCT, NKB>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (attr != hipSuccess) return attr;
+  const int64_t tiles = (a.n_rows * a.deg + 31) / 32;
+  int64_t blocks = (tiles + 3) / 4;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL((k_linear_bf16<NCT, NKB>), dim3(unsigned(blocks)), dim3(kLinBlock), lds, s,
+                     a.n_rows, a.din, a.dout, a.cin, a.cout, a.in_off, a.out_off, a.deg, col0,
+                     static_cast<const bf16_t*>(a.x), a.W, a.w_trans ? a.cin : a.cout, a.w_trans,
+                     static_cast<bf16_t*>(a.y), a.accumulate);
+  return hipGetLastError();
+}
+
+template <int NKB>
+hipError_t launch_bf16_k(const LinearBlockArgs& a, hipStream_t s) {
+  for (int col0 = 0; col0 < a.cout; col0 += 128) {
+    const int cw = a.cout - col0 < 128 ? a.cout - col0 : 128;
+    hipError_t e;
+    switch (cw / 32) {
+      case 1: e = launch_bf16_one<1, NKB>(a, col0, s); break;
+      case 2: e = launch_bf16_one<2, NKB>(a, col0, s); break;
+      case 3: e = launch_bf16_one<3, NKB>(a, col0, s); break;
+      default: e = launch_bf16_one<4, NKB>(a, col0, s); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// bf16 storage with Cin in {64, 128, 256} (Cout a multiple of 32)
+hipError_t launch_bf16(const LinearBlockArgs& a, hipStream_t s) {
+  switch (a.cin) {
+    case 64: return launch_bf16_k<4>(a, s);
+    case 128: return launch_bf16_k<8>(a, s);
+    default: return launch_bf16_k<16>(a, s);
+  }
+}
+
 template <class T>
 hipError_t launch_linear_t(const LinearBlockArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
@@ -220,6 +367,9 @@ hipError_t launch_linear_t(const LinearBlockArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k_linear_zero<T>), dim3(unsigned(g)), dim3(256), 0, s, a.n_rows, a.dout,
                        a.cout, a.out_off, a.deg, static_cast<T*>(a.y));
     return hipGetLastError();
+  }
+  if constexpr (std::is_same_v<T, bf16_t>) {
+    if (a.cin == 64 || a.cin == 128 || a.cin == 256) return launch_bf16(a, s);
   }
   // column slabs of up to 128 channels
   for (int col0 = 0; col0 < a.cout; col0 += 128) {

@@ -373,8 +373,10 @@ e3_status e3_linear_num_weights(const e3_irreps* in, const e3_irreps* out, int32
  * y [n_rows][dout][Cout] in the storage type, W float32, all three 16-byte
  * aligned; W holds the e3_linear_num_weights matrices [Cin][Cout]
  * row-major, ordered by input block, then output block.  Output blocks
- * without a matching input block are zero.  Runs on the fp32 matrix cores; fp32 accumulation for both
- * storage types.  y must not overlap x. */
+ * without a matching input block are zero.  fp32 storage runs on the fp32
+ * matrix cores; bf16 storage with Cin in {64, 128, 256} on the bf16 matrix
+ * cores (W rounded to bf16 inside the call), other Cin on the fp32 ones;
+ * fp32 accumulation throughout.  y must not overlap x. */
 e3_status e3_linear(const e3_irreps* in, const e3_irreps* out, int64_t n_rows, const void* x,
                     const float* W, void* y, e3_dtype dtype, void* stream);
 

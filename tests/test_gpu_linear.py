@@ -157,3 +157,27 @@ def test_linear_backward_deterministic(gpu):
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+
+
+@pytest.mark.parametrize("cin,cout", [(64, 96), (256, 160), (128, 32)])
+def test_linear_bf16_matrix_core_shapes(gpu, cin, cout):
+    # bf16 storage runs on the bf16 matrix cores for Cin in {64, 128, 256}
+    # (W rounded to bf16 in the kernel); any Cout that is a multiple of 32
+    ins = outs = _ir("0e+1o+2e")
+    x, W = _case(ins, outs, 700, cin, cout, 130 + cin)
+    x = S.round_bf16(x)
+    y = host(gpu.linear(ins, outs, dev(x, "bf16"), dev(W)))
+    assert_close(y, O.linear(ins, outs, x, W), TOL_BF16, f"linear bf16 {cin}->{cout}",
+                 bf16_out=True)
+
+
+@pytest.mark.parametrize("cin,cout", [(64, 64), (128, 256)])
+def test_linear_backward_bf16_matrix_core_shapes(gpu, cin, cout):
+    # dx = dy W^T: the bf16 matrix-core path with Cout as the contraction
+    ins = outs = _ir("0e+1o")
+    x, W, dy = _bwd_case(ins, outs, 600, cin, cout, 140 + cout)
+    x, dy = S.round_bf16(x), S.round_bf16(dy)
+    dx, dW = gpu.linear_backward(ins, outs, dev(x, "bf16"), dev(W), dev(dy, "bf16"))
+    rdx, rdW = O.linear_backward(ins, outs, x, W, dy)
+    assert_close(host(dx), rdx, TOL_BF16, f"linear dx bf16 {cin}->{cout}", bf16_out=True)
+    assert_close(host(dW), rdW, TOL_F32, f"linear dW bf16 inputs {cin}->{cout}")
