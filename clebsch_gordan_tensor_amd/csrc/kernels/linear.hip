@@ -11,6 +11,7 @@
 #include <cstdint>
 
 #include "common.h"
+#include "partial_sums.h"
 #include "registry.h"
 
 namespace e3k {
@@ -433,21 +434,22 @@ __global__ void __launch_bounds__(kLinBlock)
       }
     }
   };
-  float ac[4], bc[4][NTB];
-  if (q_beg < q_end) fetch(q_beg, ac, bc);
-  for (int64_t q0 = q_beg; q0 < q_end; q0 += 8) {
-    float an[4], bn[4][NTB];
-    if (q0 + 8 < q_end) fetch(q0 + 8, an, bn);
+  // a ring of four 8-row slots: the rows 24 ahead are requested while these
+  // 8 are multiplied; the loop body covers all four slots, so every slot
+  // keeps its registers (no copies that would wait on the loads).  Rows
+  // past the chunk read as zero and add nothing.
+  float ar[4][4], br[4][4][NTB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+  for (int sl = 0; sl < 3; ++sl) fetch(q_beg + 8 * sl, ar[sl], br[sl]);
+  for (int64_t q0 = q_beg; q0 < q_end; q0 += 32) {
 #pragma unroll
-      for (int t = 0; t < NTB; ++t)
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(ac[u], bc[u][t], acc[t], 0, 0, 0);
+    for (int sl = 0; sl < 4; ++sl) {
+      fetch(q0 + 8 * sl + 24, ar[(sl + 3) % 4], br[(sl + 3) % 4]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ac[u] = an[u];
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int t = 0; t < NTB; ++t) bc[u][t] = bn[u][t];
+        for (int t = 0; t < NTB; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(ar[sl][u], br[sl][u][t], acc[t], 0, 0, 0);
     }
   }
   // D[i][j] -> part[chunk][32w + i'][32t + j]
@@ -457,18 +459,6 @@ __global__ void __launch_bounds__(kLinBlock)
     const int row = 8 * (rr / 4) + 4 * s + (rr % 4);
 #pragma unroll
     for (int t = 0; t < NTB; ++t) pc[int64_t(32 * w + row) * cout + 32 * t + i] = acc[t][rr];
-  }
-}
-
-// dW[e] (+)= sum over chunks c = 0..n-1 of part[c][e], in that order.
-__global__ void __launch_bounds__(256)
-    k_linear_dw_reduce(int n_chunks, int64_t n_elem, const float* __restrict__ part,
-                       float* __restrict__ dW, int accumulate) {
-  for (int64_t e = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; e < n_elem;
-       e += int64_t(gridDim.x) * blockDim.x) {
-    float sum = accumulate ? dW[e] : 0.0f;
-    for (int c = 0; c < n_chunks; ++c) sum += part[int64_t(c) * n_elem + e];
-    dW[e] = sum;
   }
 }
 
@@ -484,11 +474,7 @@ template <class T>
 hipError_t launch_dw(const LinearDwArgs& a, hipStream_t s) {
   const int64_t n_comp = a.n_rows * a.deg;
   const int64_t n_elem = int64_t(a.cin) * a.cout;
-  if (n_comp <= 0) {
-    hipLaunchKernelGGL(k_linear_dw_reduce, dim3(unsigned((n_elem + 255) / 256)), dim3(256), 0, s,
-                       0, n_elem, a.part, a.dW, a.accumulate);
-    return hipGetLastError();
-  }
+  if (n_comp <= 0) return sum_partials_fixed(0, n_elem, a.part, a.dW, a.accumulate, s);
   // chunks of a multiple of 8 rows, at most kLinDwChunks of them
   int64_t chunk = (n_comp + kLinDwChunks - 1) / kLinDwChunks;
   chunk = (chunk + 7) / 8 * 8;
@@ -505,10 +491,7 @@ hipError_t launch_dw(const LinearDwArgs& a, hipStream_t s) {
     default: e = launch_dw_t<T, 8>(a, n_chunks, chunk, s); break;
   }
   if (e != hipSuccess) return e;
-  int64_t g = (n_elem + 255) / 256;
-  hipLaunchKernelGGL(k_linear_dw_reduce, dim3(unsigned(g)), dim3(256), 0, s, n_chunks, n_elem,
-                     a.part, a.dW, a.accumulate);
-  return hipGetLastError();
+  return sum_partials_fixed(n_chunks, n_elem, a.part, a.dW, a.accumulate, s);
 }
 
 }  // namespace

@@ -30,6 +30,7 @@
 #include <cstring>
 
 #include "common.h"
+#include "partial_sums.h"
 #include "registry.h"
 #include "signatures.h"
 
@@ -650,7 +651,7 @@ constexpr int kDw2Cols = 64 * kDw2Waves;  // columns per workgroup: 64 per wavef
 // into LDS (the arithmetic of the forward MLP's hidden layer); each
 // wavefront owns 64 columns, column c_wave + 4 li + t in MFMA t, and all 64
 // hidden units (16 accumulator tiles), so dw is read once, 16 bytes per lane
-// and edge.  The ranges' partials are added afterwards in range order.
+// and edge.  The ranges' partials are added afterwards in a fixed order.
 __global__ void __launch_bounds__(64 * kDw2Waves)
     k_radial_dw2(int n_edges, int n_cols, const float* __restrict__ vec, float rc,
                  const float* __restrict__ W1, const float* __restrict__ dw,
@@ -734,16 +735,6 @@ __global__ void __launch_bounds__(64 * kDw2Waves)
   }
 }
 
-// out[i] = sum_c part[c][i] over n_chunks partials, in chunk order.
-__global__ void __launch_bounds__(256)
-    k_sum_partials(int n_chunks, int n, const float* __restrict__ part, float* __restrict__ out) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.0f;
-  for (int c = 0; c < n_chunks; ++c) s += part[int64_t(c) * n + i];
-  out[i] = s;
-}
-
 }  // namespace
 
 hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const float* W1,
@@ -753,9 +744,7 @@ hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const
                      kRadialTailChunks, vec, cutoff, W1, dh, dvec, dW1_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sum_partials, dim3(2), dim3(256), 0, s, kRadialTailChunks,
-                     kRadBasis * kRadHidden, dW1_part, dW1);
-  return hipGetLastError();
+  return sum_partials_fixed(kRadialTailChunks, kRadBasis * kRadHidden, dW1_part, dW1, 0, s);
 }
 
 bool radial_conv_supported(const char* set_name) {
@@ -785,11 +774,8 @@ hipError_t launch_radial_dh_dw2(int n_edges, int n_cols, const float* vec, float
   return hipGetLastError();
 }
 
-hipError_t launch_sum_partials(int n_chunks, int n, const float* part, float* out, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_sum_partials, dim3((n + 255) / 256), dim3(256), 0, s, n_chunks, n, part,
-                     out);
-  return hipGetLastError();
+hipError_t launch_sum_partials(int n_chunks, int n, float* part, float* out, hipStream_t s) {
+  return sum_partials_fixed(n_chunks, n, part, out, 0, s);
 }
 
 hipError_t launch_conv_fwd_radial(const char* set_name, const RadialConvArgs& a, hipStream_t s) {

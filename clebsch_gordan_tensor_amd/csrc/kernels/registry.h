@@ -190,12 +190,12 @@ hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const
                               hipStream_t s);
 // The second layer's backward from dw [E][n_cols] (n_cols a multiple of
 // 4): dh [E][64] and per-range partials part [ranges][64][n_cols] of dW2
-// (add them with launch_sum_partials).
+// (add them with launch_sum_partials, which overwrites them).
 int radial_dw2_ranges(int n_edges, int n_cols);
 hipError_t launch_radial_dh_dw2(int n_edges, int n_cols, const float* vec, float cutoff,
                                 const float* W1, const float* W2, const float* dw, float* dh,
                                 float* part, int ranges, hipStream_t s);
-hipError_t launch_sum_partials(int n_chunks, int n, const float* part, float* out, hipStream_t s);
+hipError_t launch_sum_partials(int n_chunks, int n, float* part, float* out, hipStream_t s);
 hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
                                  float* dvec, hipStream_t s);
 hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr,
@@ -220,7 +220,7 @@ hipError_t launch_linear(const LinearBlockArgs& a, int bf16, hipStream_t s);
 
 // Weight gradient of one block pair: dW [cin][cout] (+)= sum over the
 // block's rows of x^T dy, through per-chunk partial sums in `part`
-// (kLinDwChunks * cin * cout floats) added in chunk order.
+// (kLinDwChunks * cin * cout floats, overwritten) added in a fixed order.
 constexpr int kLinDwChunks = 1024;
 struct LinearDwArgs {
   int64_t n_rows;
