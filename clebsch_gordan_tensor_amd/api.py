@@ -50,7 +50,7 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_radial_mlp_backward_workspace_size", "e3_radial_mlp_backward",
            "e3_generic_plan_size", "e3_generic_plan_build", "e3_tp_forward_generic",
            "e3_tp_backward_generic", "e3_conv_forward_generic", "e3_conv_backward_generic",
-           "e3_last_error"]
+           "e3_conv_double_backward_generic", "e3_last_error"]
 E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY = 0, 1, 2, 3
 
 
@@ -95,6 +95,9 @@ def lib():
                                           C.c_int, vp]
     L.e3_conv_backward_generic.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, sz, vp, sz, vp, sz,
                                            vp, vp, vp, vp, vp, vp, vp, C.c_int, vp]
+    L.e3_conv_double_backward_generic.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, sz, vp, sz,
+                                                  vp, sz, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  vp, vp, vp, vp, sz, C.c_int, vp]
     L.e3_radial_mlp_backward_workspace_size.argtypes = [C.POINTER(_CRadial), i32, i32,
                                                         C.POINTER(sz)]
     L.e3_radial_mlp_backward.argtypes = [C.POINTER(_CRadial), i32, i32, vp, vp, vp, vp, vp, vp,
@@ -669,3 +672,37 @@ def conv_backward_generic(desc: Desc, rowptr, sender, workspace, edge_vec_or_Y, 
         pw.numel() * 4, _ptr(py), py.numel() * 4, _ptr(edge_vec_or_Y), _ptr(x), _ptr(w), _ptr(dm),
         _ptr(dx), _ptr(dw), _ptr(dY), _dtype_code(x), _stream(stream)))
     return dx, dw, dY
+
+
+def conv_double_backward_generic(desc: Desc, rowptr, sender, workspace, Y, x, w, dm, ddx, ddY,
+                                 ddw, scratch=None, stream=None):
+    """(dx2, dY2, dw2, ddm) as conv_double_backward through the coefficient
+    tables (degrees up to 6); desc needs E3_Y_GIVEN."""
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    P = num_paths(desc)
+    dt = x.dtype
+    _need(Y, "Y", shape=(E, desc.dy), dtype=torch.float32)
+    _need(ddY, "ddY", shape=(E, desc.dy), dtype=torch.float32)
+    for t, n, shp in ((x, "x", (N, desc.dx, desc.channels)), (ddx, "ddx", (N, desc.dx, desc.channels)),
+                      (w, "w", (E, P, desc.channels)), (ddw, "ddw", (E, P, desc.channels)),
+                      (dm, "dm", (N, desc.dout, desc.channels))):
+        _need(t, n, shape=shp, dtype=dt)
+    nb = C.c_size_t()
+    _check(lib().e3_conv_double_backward_scratch_size(C.byref(desc.c()), N, E, _dtype_code(x),
+                                                      C.byref(nb)))
+    if scratch is None:
+        scratch = torch.empty(nb.value, device=x.device, dtype=torch.uint8)
+    pf, px, pw, py = (generic_plan(desc, x.device, t)
+                      for t in (E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY))
+    dx2, dw2 = torch.empty_like(x), torch.empty_like(w)
+    dY2 = torch.empty_like(Y)
+    ddm = torch.empty_like(dm)
+    _check(lib().e3_conv_double_backward_generic(
+        C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(pf), pf.numel() * 4, _ptr(px),
+        px.numel() * 4, _ptr(pw), pw.numel() * 4, _ptr(py), py.numel() * 4, _ptr(Y), _ptr(x),
+        _ptr(w), _ptr(dm), _ptr(ddx), _ptr(ddY), _ptr(ddw), _ptr(dx2), _ptr(dY2), _ptr(dw2),
+        _ptr(ddm), _ptr(scratch), scratch.numel() * scratch.element_size(), _dtype_code(x),
+        _stream(stream)))
+    return dx2, dY2, dw2, ddm

@@ -426,26 +426,19 @@ e3_status e3_conv_double_backward_scratch_size(const e3_desc* desc, int32_t n_no
   return ok();
 }
 
-e3_status e3_conv_double_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
-                                  const int32_t* rowptr, const int32_t* sender,
-                                  const void* workspace, size_t ws_bytes, const float* Y,
-                                  const void* x, const void* w, const void* dm, const void* ddx,
-                                  const float* ddY, const void* ddw, void* dx2, float* dY2,
-                                  void* dw2, void* ddm, void* scratch, size_t scratch_bytes,
-                                  e3_dtype dtype, void* stream) {
-  Parsed p;
-  e3_status s = parse(desc, p);
-  if (s != E3_OK) return s;
-  if (!(desc->flags & E3_Y_GIVEN))
-    return fail(E3_ERR_INVALID_ARG, "the double backward takes given harmonics (E3_Y_GIVEN)");
-  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
-  if (n_nodes == 0) return ok();
-  const size_t need = double_backward_scratch(p, n_nodes, n_edges, dtype);
-  if (!scratch || scratch_bytes < need)
-    return fail(E3_ERR_WORKSPACE, "scratch needs " + std::to_string(need) + " bytes");
-  if (!aligned16(scratch)) return fail(E3_ERR_ALIGNMENT, "scratch must be 16-byte aligned");
-  if (!x || !dm || !ddx || !dx2 || !ddm || (n_edges > 0 && (!Y || !w || !ddY || !ddw || !dY2 || !dw2)))
-    return fail(E3_ERR_INVALID_ARG, "null pointer");
+}  // extern "C"
+
+namespace {
+
+// The double backward of e3j E.1 Eq.17-18 composed from three forward and
+// three backward calls (fwd, bwd) plus additions, the unused cotangents of
+// each backward call going to the scratch.  Arguments checked by the caller.
+template <class Fwd, class Bwd>
+e3_status double_backward_composed(const Parsed& p, int32_t n_nodes, int32_t n_edges,
+                                   const float* Y, const void* x, const void* w, const void* ddx,
+                                   const float* ddY, const void* ddw, void* dx2, float* dY2,
+                                   void* dw2, void* ddm, void* scratch, e3_dtype dtype,
+                                   hipStream_t st, Fwd fwd, Bwd bwd) {
   const size_t es = dtype == E3_BF16 ? 2 : 4;
   char* sc = static_cast<char*>(scratch);
   void* t_m = sc;
@@ -455,21 +448,13 @@ e3_status e3_conv_double_backward(const e3_desc* desc, int32_t n_nodes, int32_t 
   float* t_Y = reinterpret_cast<float*>(sc);
   sc += align256(size_t(n_edges) * p.dy * 4);
   void* t_w = sc;
-  const hipStream_t st = hipStream_t(stream);
   const int bf = dtype == E3_BF16;
   const int64_t nm = int64_t(n_nodes) * p.dout * p.C, nx = int64_t(n_nodes) * p.dx * p.C;
   const int64_t nY = int64_t(n_edges) * p.dy, nw = int64_t(n_edges) * p.P * p.C;
-  auto fwd = [&](const void* xx, const float* yy, const void* ww, void* out) {
-    return e3_conv_forward(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes, yy, xx,
-                           ww, out, dtype, stream);
-  };
-  auto bwd = [&](const void* xx, const float* yy, const void* ww, void* ox, void* ow, float* oy) {
-    return e3_conv_backward(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes, yy, xx,
-                            ww, dm, ox, ow, oy, dtype, stream);
-  };
   auto add = [&](void* dst, const void* src, int64_t n, int b16) {
     return hip_status(e3k::launch_add(dst, src, n, b16, st), "double_backward");
   };
+  e3_status s;
   // ddm = conv(ddx, Y, w) + conv(x, ddY, w) + conv(x, Y, ddw)        (e3j Eq.17)
   if ((s = fwd(ddx, Y, w, ddm)) != E3_OK) return s;
   if ((s = fwd(x, ddY, w, t_m)) != E3_OK || (s = add(ddm, t_m, nm, bf)) != E3_OK) return s;
@@ -482,6 +467,55 @@ e3_status e3_conv_double_backward(const e3_desc* desc, int32_t n_nodes, int32_t 
       (s = add(dY2, t_Y, nY, 0)) != E3_OK)
     return s;
   return ok();
+}
+
+e3_status double_backward_checks(const e3_desc* desc, const Parsed& p, int32_t n_nodes,
+                                 int32_t n_edges, const float* Y, const void* x, const void* w,
+                                 const void* dm, const void* ddx, const float* ddY,
+                                 const void* ddw, void* dx2, float* dY2, void* dw2, void* ddm,
+                                 void* scratch, size_t scratch_bytes, e3_dtype dtype) {
+  if (!(desc->flags & E3_Y_GIVEN))
+    return fail(E3_ERR_INVALID_ARG, "the double backward takes given harmonics (E3_Y_GIVEN)");
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes == 0) return ok();
+  const size_t need = double_backward_scratch(p, n_nodes, n_edges, dtype);
+  if (!scratch || scratch_bytes < need)
+    return fail(E3_ERR_WORKSPACE, "scratch needs " + std::to_string(need) + " bytes");
+  if (!aligned16(scratch)) return fail(E3_ERR_ALIGNMENT, "scratch must be 16-byte aligned");
+  if (!x || !dm || !ddx || !dx2 || !ddm ||
+      (n_edges > 0 && (!Y || !w || !ddY || !ddw || !dY2 || !dw2)))
+    return fail(E3_ERR_INVALID_ARG, "null pointer");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+e3_status e3_conv_double_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                  const int32_t* rowptr, const int32_t* sender,
+                                  const void* workspace, size_t ws_bytes, const float* Y,
+                                  const void* x, const void* w, const void* dm, const void* ddx,
+                                  const float* ddY, const void* ddw, void* dx2, float* dY2,
+                                  void* dw2, void* ddm, void* scratch, size_t scratch_bytes,
+                                  e3_dtype dtype, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if ((s = double_backward_checks(desc, p, n_nodes, n_edges, Y, x, w, dm, ddx, ddY, ddw, dx2, dY2,
+                                  dw2, ddm, scratch, scratch_bytes, dtype)) != E3_OK ||
+      n_nodes == 0)
+    return s;
+  auto fwd = [&](const void* xx, const float* yy, const void* ww, void* out) {
+    return e3_conv_forward(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes, yy, xx,
+                           ww, out, dtype, stream);
+  };
+  auto bwd = [&](const void* xx, const float* yy, const void* ww, void* ox, void* ow, float* oy) {
+    return e3_conv_backward(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes, yy, xx,
+                            ww, dm, ox, ow, oy, dtype, stream);
+  };
+  return double_backward_composed(p, n_nodes, n_edges, Y, x, w, ddx, ddY, ddw, dx2, dY2, dw2, ddm,
+                                  scratch, dtype, hipStream_t(stream), fwd, bwd);
 }
 
 namespace {
@@ -1121,6 +1155,33 @@ e3_status e3_conv_backward_generic(const e3_desc* desc, int32_t n_nodes, int32_t
                               ws + L.order, rowptr, sender, edge_vec_or_Y, ly, ym, x, w, dm, dw,
                               dY};
   return hip_status(e3k::launch_conv_generic_edge(ae, bf, st), "conv_backward_generic");
+}
+
+e3_status e3_conv_double_backward_generic(
+    const e3_desc* desc, int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+    const int32_t* sender, const void* workspace, size_t ws_bytes, const void* plan_fwd,
+    size_t fwd_bytes, const void* plan_dx, size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+    const void* plan_dy, size_t dy_bytes, const float* Y, const void* x, const void* w,
+    const void* dm, const void* ddx, const float* ddY, const void* ddw, void* dx2, float* dY2,
+    void* dw2, void* ddm, void* scratch, size_t scratch_bytes, e3_dtype dtype, void* stream) {
+  Parsed p;
+  e3_status s = generic_parse(desc, dtype, p);
+  if (s != E3_OK) return s;
+  if ((s = double_backward_checks(desc, p, n_nodes, n_edges, Y, x, w, dm, ddx, ddY, ddw, dx2, dY2,
+                                  dw2, ddm, scratch, scratch_bytes, dtype)) != E3_OK ||
+      n_nodes == 0)
+    return s;
+  auto fwd = [&](const void* xx, const float* yy, const void* ww, void* out) {
+    return e3_conv_forward_generic(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes,
+                                   plan_fwd, fwd_bytes, yy, xx, ww, out, dtype, stream);
+  };
+  auto bwd = [&](const void* xx, const float* yy, const void* ww, void* ox, void* ow, float* oy) {
+    return e3_conv_backward_generic(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes,
+                                    plan_dx, dx_bytes, plan_dw, dw_bytes, plan_dy, dy_bytes, yy, xx,
+                                    ww, dm, ox, ow, oy, dtype, stream);
+  };
+  return double_backward_composed(p, n_nodes, n_edges, Y, x, w, ddx, ddY, ddw, dx2, dY2, dw2, ddm,
+                                  scratch, dtype, hipStream_t(stream), fwd, bwd);
 }
 
 const char* e3_last_error(void) { return g_last_error.c_str(); }

@@ -301,6 +301,18 @@ e3_status e3_conv_backward_generic(const e3_desc* desc, int32_t n_nodes, int32_t
                                    const void* dm, void* dx, void* dw, float* dY, e3_dtype dtype,
                                    void* stream);
 
+/* Double backward (as e3_conv_double_backward, e3j E.1 Eq.17-18, given
+ * harmonics: desc needs E3_Y_GIVEN) for degrees up to 6, composed from the
+ * generic forward and backward with all four tables; scratch as
+ * e3_conv_double_backward_scratch_size gives for desc. */
+e3_status e3_conv_double_backward_generic(
+    const e3_desc* desc, int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+    const int32_t* sender, const void* workspace, size_t ws_bytes, const void* plan_fwd,
+    size_t fwd_bytes, const void* plan_dx, size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+    const void* plan_dy, size_t dy_bytes, const float* Y, const void* x, const void* w,
+    const void* dm, const void* ddx, const float* ddY, const void* ddw, void* dx2, float* dY2,
+    void* dw2, void* ddm, void* scratch, size_t scratch_bytes, e3_dtype dtype, void* stream);
+
 /* Per-node gradient from per-edge vector gradients, for r_e = pos[receiver]
  * - pos[sender]:
  *   node_grad[b] = sum_{e: receiver(e) = b} edge_grad[e]

@@ -122,3 +122,47 @@ def test_double_backward_needs_given_harmonics(gpu):
     with pytest.raises(gpu.E3Error):
         gpu.conv_double_backward(d, rowptr, sender, ws, dev(Y), dev(x), dev(w), dev(dm),
                                  dev(ddx), dev(ddY), dev(ddw))
+
+
+# ------------------------------------------------------- degrees up to 6
+
+@pytest.mark.parametrize("L,C", [(2, 64), (4, 96)])
+def test_generic_double_backward_matches_oracle(gpu, L, C):
+    # the composition through the coefficient tables, degrees above 3
+    xi = oi = S.degree_irreps(L)
+    yi = S.sh_irreps(L)
+    rng = np.random.default_rng(160 + L)
+    g = S.random_graph(40, 7.0, 3.5, 160 + L)
+    P = S.num_paths(xi, yi, oi)
+    x = rng.standard_normal((40, S.dim(xi), C)).astype(np.float32)
+    w = rng.standard_normal((g.n_edges, P, C)).astype(np.float32)
+    dm = rng.standard_normal((40, S.dim(oi), C)).astype(np.float32)
+    Y = O.sh(L, g.evec.astype(np.float64)).astype(np.float32)
+    ddx = rng.standard_normal(x.shape).astype(np.float32)
+    ddY = rng.standard_normal(Y.shape).astype(np.float32)
+    ddw = rng.standard_normal(w.shape).astype(np.float32)
+    d = gpu.Desc(xi, yi, oi, C, gpu.E3_Y_GIVEN)
+    rowptr, sender = dev(g.rowptr), dev(g.sender)
+    ws = gpu.conv_prepare_transpose(rowptr, sender)
+    got = gpu.conv_double_backward_generic(d, rowptr, sender, ws, dev(Y), dev(x), dev(w), dev(dm),
+                                           dev(ddx), dev(ddY), dev(ddw))
+    torch.cuda.synchronize()
+    ref = O.conv_double_backward(O.Desc(xi, yi, oi, C), g.rowptr, g.sender, Y, x, w, dm, ddx,
+                                 ddY, ddw)
+    for k, a, b in zip(("dx2", "dY2", "dw2", "ddm"), got, ref):
+        assert_close(host(a), b, TOL_F32, f"generic double backward L={L}:{k}")
+
+
+def test_generic_double_backward_equals_compiled(gpu):
+    case = _case("tiny", 170)
+    p, Y, x, w, dm, ddx, ddY, ddw = case
+    a = _run(gpu, *case, "f32")
+    g = p.graph
+    d = gpu.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels, gpu.E3_Y_GIVEN)
+    rowptr, sender = dev(g.rowptr), dev(g.sender)
+    ws = gpu.conv_prepare_transpose(rowptr, sender)
+    b = gpu.conv_double_backward_generic(d, rowptr, sender, ws, dev(Y), dev(x), dev(w), dev(dm),
+                                         dev(ddx), dev(ddY), dev(ddw))
+    torch.cuda.synchronize()
+    for k, u, v in zip(("dx2", "dY2", "dw2", "ddm"), a, b):
+        assert_close(u, host(v).astype(np.float64), 2 * TOL_F32, f"generic vs compiled:{k}")
