@@ -551,186 +551,380 @@ __global__ void __launch_bounds__(256)
 }
 
 // The two products of the second layer's backward, each reading dw once, on
-// the fp32 matrix cores with v_mfma_f32_16x16x4f32: A[i][k] comes from lane
-// 16k + i, B[k][j] from lane 16k + j, and D[i][j] sits in register i % 4 of
-// lane j + 16 (i / 4).  A lane loads four consecutive values with one
-// 16-byte access and feeds them to four MFMAs (t = 0..3), so the four k (or
-// j) slots of one MFMA are four values apart in memory; a sum does not care
-// in which order its terms arrive.
+// the bf16 matrix cores (v_mfma_f32_16x16x32_bf16).  Both operands are split
+// into three bf16 parts, a = a0 + a1 + a2 with a1 the rounding error of a0
+// and a2 that of a1: 24 significant bits and fp32's exponent range, so any
+// cotangent is representable without scaling.  Six of the nine cross
+// products are formed (a0b0, a0b1, a1b0, a0b2, a2b0, a1b1); the three left
+// out and the split's own residue are each below 2^-24 of the product, the
+// size of an fp32 rounding, and every product of two bf16 values is exact in
+// the fp32 accumulator.  Six of these MFMAs (16 cycles each) do the work of
+// sixteen v_mfma_f32_16x16x4f32 (32 cycles each), which leaves both products
+// bound by their read of dw rather than by the matrix cores.
+//
+// Operand layout (that of the fp16 form above): A[i][k] is element k % 8 of
+// lane i + 16 (k / 8), B[k][j] element k % 8 of lane j + 16 (k / 8), and
+// D[i][j] register i % 4 of lane j + 16 (i / 4).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// dh[e][k] = sum_j dw[e][j] W2[k][j].  One wavefront per block of 32 edges
-// (two 16-edge row tiles) and all 64 hidden units (four column tiles), four
-// wavefronts per workgroup walking the columns together in blocks of 128:
-// each block's W2 slice [64][128] is staged once in LDS for the four (rows
-// padded by 4 floats: the 16 rows a B load touches fall in distinct banks),
-// and its sum is added to the total (shorter rounding chains than one
-// running sum over all columns).  Per 16 columns MFMA t takes columns
-// j + 4 kq + t.
-constexpr int kDhCols = 128;
-constexpr int kDhLd = kDhCols + 4;
+struct Split3 {
+  bf16x8 p[3];
+};
 
-__global__ void __launch_bounds__(256)
-    k_radial_dh(int n_edges, int n_cols, const float* __restrict__ dw,
-                const float* __restrict__ W2, float* __restrict__ dh) {
-  __shared__ float4v s_w2[kRadHidden * kDhLd / 4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane & 15, kq = lane >> 4;
-  const int64_t n_blocks = (int64_t(n_edges) + 127) / 128;  // 128 edges per workgroup
-  for (int64_t wb = blockIdx.x; wb < n_blocks; wb += gridDim.x) {
-    const int64_t e0 = wb * 128 + 32 * wave;
-    const float* arow[2];
-    bool aval[2];
+__device__ __forceinline__ void split3(const float (&v)[8], Split3& s) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int64_t e = e0 + 16 * mt + li;
-      aval[mt] = e < n_edges;
-      arow[mt] = dw + (aval[mt] ? e : 0) * n_cols + 4 * kq;
-    }
-    float4v acc[2][4], bs[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int jb = 0; jb < n_cols; jb += kDhCols) {
-      const int nc = min(kDhCols, n_cols - jb);  // a multiple of 16
-      __syncthreads();  // the previous block's reads of s_w2 are done
-      for (int idx = threadIdx.x; idx < kRadHidden * (nc / 4); idx += 256) {
-        const int k = idx / (nc / 4), c = 4 * (idx - k * (nc / 4));
-        s_w2[(k * kDhLd + c) / 4] =
-            *reinterpret_cast<const float4v*>(W2 + int64_t(k) * n_cols + jb + c);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) bs[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 2
-      for (int j = 0; j < nc; j += 16) {
-        float4v a[2], b[4];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          a[mt] = aval[mt] ? *reinterpret_cast<const float4v*>(arow[mt] + jb + j)
-                           : float4v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) b[nt] = s_w2[((16 * nt + li) * kDhLd + j + 4 * kq) / 4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-              bs[mt][nt] =
-                  __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt][t], b[nt][t], bs[mt][nt], 0, 0, 0);
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] += bs[mt][nt];
-    }
-    // D row = edge 16 mt + 4 kq + r, column = hidden unit 16 nt + li
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t e = e0 + 16 * mt + 4 * kq + r;
-        if (e < n_edges) {
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) dh[e * kRadHidden + 16 * nt + li] = acc[mt][nt][r];
-        }
-      }
+  for (int t = 0; t < 8; ++t) {
+    const __bf16 a = static_cast<__bf16>(v[t]);  // nearest even
+    const float r = v[t] - static_cast<float>(a);  // exact
+    const __bf16 b = static_cast<__bf16>(r);
+    s.p[0][t] = a;
+    s.p[1][t] = b;
+    s.p[2][t] = static_cast<__bf16>(r - static_cast<float>(b));
   }
 }
 
-constexpr int kDw2Waves = 4;
-constexpr int kDw2Cols = 64 * kDw2Waves;  // columns per workgroup: 64 per wavefront
+__device__ __forceinline__ u32x4 as_u4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+__device__ __forceinline__ bf16x8 as_b8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ float4v mfma_bf16(bf16x8 a, bf16x8 b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// the five smaller cross products, the smallest first
+__device__ __forceinline__ float4v cross5(const Split3& a, const Split3& b, float4v c) {
+  c = mfma_bf16(a.p[1], b.p[1], c);
+  c = mfma_bf16(a.p[2], b.p[0], c);
+  c = mfma_bf16(a.p[0], b.p[2], c);
+  c = mfma_bf16(a.p[1], b.p[0], c);
+  return mfma_bf16(a.p[0], b.p[1], c);
+}
+
+constexpr int kW2Units = 4 * 3 * 64;  // 16-byte units per 32-column block: [nt][part][lane]
+
+// W2 [64][n_cols] in its three bf16 parts, in the B operand order of the dh
+// product: unit [cb][nt][part][lane] holds W2[16 nt + lane % 16]
+// [32 cb + 8 (lane / 16) + t], t = 0..7; blocks past n_cols / 32, up to a
+// whole LDS stage, are zeros.
+constexpr int kDhChunk = 4;  // 32-column blocks per LDS stage of the dh product
+
+__host__ __device__ constexpr int w2_split_blocks(int n_cols) {
+  return (n_cols / 32 + kDhChunk - 1) / kDhChunk * kDhChunk;
+}
+
+__global__ void __launch_bounds__(256)
+    k_radial_split_w2(int n_cols, const float* __restrict__ W2, u32x4* __restrict__ w2s) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;  // (cb, nt, lane)
+  if (idx >= w2_split_blocks(n_cols) * 256) return;
+  const int lane = idx & 63, nt = (idx >> 6) & 3, cb = idx >> 8;
+  float v[8];
+  if (cb < n_cols / 32) {
+    const float* src = W2 + int64_t(16 * nt + (lane & 15)) * n_cols + 32 * cb + 8 * (lane >> 4);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = src[t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = 0.0f;
+  }
+  Split3 sp;
+  split3(v, sp);
+  u32x4* dst = w2s + int64_t(cb) * kW2Units + nt * 192 + lane;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) dst[64 * q] = as_u4(sp.p[q]);
+}
+
+// dh[e][k] = sum_j dw[e][j] W2[k][j].  One wavefront per 32 edges (two
+// 16-edge row tiles) and all 64 hidden units (four column tiles), four per
+// workgroup; a workgroup takes edge blocks of 128 in a grid-stride sequence
+// and W2's parts in LDS stages of four 32-column blocks.  Lane (i, q) takes
+// columns 8q..8q+7 of its edge's block (two 16-byte loads).  The loads form
+// one stream over (edge block, column block), kept about 12 KB deep per
+// wavefront (HBM latency under load needs ~100 KB in flight per CU): a ring
+// of four blocks, one slot per block of a stage, each slot refilled with the
+// block four ahead as soon as its values are split; and each stage's W2
+// parts one stage ahead, in registers, written to LDS between two barriers.
+// The loop's issue order is the same in every stage (W2 parts, then four
+// blocks), so each wait covers only the loads it needs.  Rows and blocks
+// past the end are loaded clamped and zeroed.  The leading products a0 b0
+// accumulate apart from the five smaller ones, so the rounding chain of the
+// sum is n_cols / 32 MFMAs long; the two are added at the end.
+constexpr int kDhRows = 2;               // 16-edge row tiles per wavefront
+constexpr int kDhEdges = 64 * kDhRows;   // edges per workgroup block (four wavefronts)
+constexpr int kDhStageUnits = kDhChunk * kW2Units / 256;  // 16-byte units per thread and stage
+
+__global__ void __launch_bounds__(256)
+    k_radial_dh(int n_edges, int n_cols, const float* __restrict__ dw,
+                const u32x4* __restrict__ w2s, float* __restrict__ dh) {
+  __shared__ u32x4 s_b[kDhChunk * kW2Units];  // 48 KB
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, kq = lane >> 4;
+  const int n_cb = n_cols / 32;
+  const int per = w2_split_blocks(n_cols);  // column blocks per edge block, whole stages
+  const int n_st = per / kDhChunk;
+  const int64_t n_blocks = (int64_t(n_edges) + kDhEdges - 1) / kDhEdges;
+  if (int64_t(blockIdx.x) >= n_blocks) return;  // whole workgroup, before any barrier
+  const int n_iter = int((n_blocks - 1 - blockIdx.x) / gridDim.x) + 1;
+  auto first_edge = [&](int i) {
+    return (int64_t(blockIdx.x) + int64_t(i) * gridDim.x) * kDhEdges + 16 * kDhRows * wave + li;
+  };
+  // the load stream: next block (edge block ld_i, column block ld_cb)
+  int ld_i = 0, ld_cb = 0;
+  auto load_block = [&](float4v (&slot)[kDhRows][2]) {
+    const int i = min(ld_i, n_iter - 1), cb = min(ld_cb, n_cb - 1);
+    const int64_t eb = first_edge(i);
+#pragma unroll
+    for (int mt = 0; mt < kDhRows; ++mt) {
+      const int64_t e = min(eb + 16 * mt, int64_t(n_edges) - 1);
+      const float* p = dw + e * n_cols + 32 * cb + 8 * kq;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        slot[mt][h] = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(p + 4 * h));
+    }
+    if (++ld_cb == per) {
+      ld_cb = 0;
+      ++ld_i;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads where they are issued
+  };
+  auto load_stage = [&](int st, u32x4 (&stg)[kDhStageUnits]) {
+#pragma unroll
+    for (int j = 0; j < kDhStageUnits; ++j)
+      stg[j] = w2s[int64_t(st) * kDhChunk * kW2Units + j * 256 + threadIdx.x];
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  u32x4 stg[kDhStageUnits];
+  float4v ring[kDhChunk][kDhRows][2];
+  load_stage(0, stg);
+#pragma unroll
+  for (int c = 0; c < kDhChunk; ++c) load_block(ring[c]);
+  float4v D[kDhRows][4], X[kDhRows][4];
+#pragma unroll
+  for (int mt = 0; mt < kDhRows; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      D[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      X[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  int i = 0, st = 0;  // edge block and stage being computed
+  bool aval[kDhRows];
+#pragma unroll
+  for (int mt = 0; mt < kDhRows; ++mt) aval[mt] = first_edge(0) + 16 * mt < n_edges;
+  for (int q = 0; q < n_iter * n_st; ++q) {
+    __syncthreads();  // the previous stage's reads of s_b are done
+#pragma unroll
+    for (int j = 0; j < kDhStageUnits; ++j) s_b[j * 256 + threadIdx.x] = stg[j];
+    __syncthreads();
+    load_stage(st + 1 == n_st ? 0 : st + 1, stg);
+#pragma unroll
+    for (int c = 0; c < kDhChunk; ++c) {
+      const bool blk = st * kDhChunk + c < n_cb;
+      Split3 A[kDhRows];
+#pragma unroll
+      for (int mt = 0; mt < kDhRows; ++mt) {
+        const bool ok = blk && aval[mt];
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[t] = ok ? ring[c][mt][0][t] : 0.0f;
+          v[4 + t] = ok ? ring[c][mt][1][t] : 0.0f;
+        }
+        split3(v, A[mt]);
+      }
+      load_block(ring[c]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        Split3 B;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) B.p[p] = as_b8(s_b[c * kW2Units + nt * 192 + 64 * p + lane]);
+#pragma unroll
+        for (int mt = 0; mt < kDhRows; ++mt) {
+          D[mt][nt] = mfma_bf16(A[mt].p[0], B.p[0], D[mt][nt]);
+          X[mt][nt] = cross5(A[mt], B, X[mt][nt]);
+        }
+      }
+    }
+    if (++st == n_st) {
+      // D row = edge 16 mt + 4 kq + r, column = hidden unit 16 nt + li
+      const int64_t e0 = first_edge(i) - li;
+#pragma unroll
+      for (int mt = 0; mt < kDhRows; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t e = e0 + 16 * mt + 4 * kq + r;
+          if (e < n_edges) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+              dh[e * kRadHidden + 16 * nt + li] = D[mt][nt][r] + X[mt][nt][r];
+          }
+        }
+#pragma unroll
+      for (int mt = 0; mt < kDhRows; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          D[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+          X[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+      st = 0;
+      ++i;
+#pragma unroll
+      for (int mt = 0; mt < kDhRows; ++mt) aval[mt] = first_edge(i) + 16 * mt < n_edges;
+    }
+  }
+}
+
+constexpr int kDw2Waves = 8;
+constexpr int kDw2Cols = 32 * kDw2Waves;  // columns per workgroup: 32 per wavefront
+constexpr int kDw2Step = 32;              // edges per K step
+constexpr int kDw2Ring = 4;               // steps in the load ring
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// h of the backward's dW2 product.  Not the forward's correctly rounded
+// SiLU: h enters only sums over thousands of edges, where its last bits do
+// not show.
+__device__ __forceinline__ float silu_sum_operand(float t) {
+  return __fdividef(t, 1.0f + __expf(-t));
+}
 
 // Partial weight gradient of the second layer over one range of edges:
 //   part[range][k][c] = sum_{e in range} h[e][k] dw[e][c]
 // for the kDw2Cols-column slab of the workgroup (grid x = slabs, y = edge
-// ranges).  Per block of 64 edges h is recomputed from the edge vectors
-// into LDS (the arithmetic of the forward MLP's hidden layer); each
-// wavefront owns 64 columns, column c_wave + 4 li + t in MFMA t, and all 64
-// hidden units (16 accumulator tiles), so dw is read once, 16 bytes per lane
-// and edge.  The ranges' partials are added afterwards in a fixed order.
+// ranges).  Per step of 32 edges the workgroup recomputes h (the forward
+// MLP's hidden layer: thread (b, n) < 256 evaluates basis function n of edge
+// b, thread (k, g) unit k of edges 4g..4g+3) and stores its three parts in
+// LDS in the A operand order; each wavefront owns 32 columns and all 64
+// hidden units (8 accumulator tiles).  Lane (i, q) loads 8 bytes (columns
+// 2i, 2i+1) of each of the edges 8q..8q+7 and MFMA t takes column 2i + t
+// from them, so dw is read once, whole rows at a time.  A step's edge
+// vectors and dw rows are loaded four steps ahead (a ring, the loop unrolled
+// by four so the slots stay in place; about 12 KB in flight per wavefront);
+// rows past the range are loaded clamped and zeroed.  The ranges' partials
+// are added afterwards in a fixed order.
 __global__ void __launch_bounds__(64 * kDw2Waves)
     k_radial_dw2(int n_edges, int n_cols, const float* __restrict__ vec, float rc,
                  const float* __restrict__ W1, const float* __restrict__ dw,
                  float* __restrict__ part) {
   __shared__ float s_w1[kRadBasis * kRadHidden];
-  __shared__ float s_b[64][kRadBasis];
-  __shared__ float s_h[64][kRadHidden + 1];  // [edge][hidden], padded
+  __shared__ float s_b[kDw2Step][kRadBasis + 1];
+  __shared__ u32x2 s_h[4 * 3 * 64 * 2];  // [mt][part][lane][half]
   for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, kq = lane >> 4;
-  const int c4 = blockIdx.x * kDw2Cols + 64 * wave + 4 * li;  // this lane's 4 columns
-  const bool cval = c4 < n_cols;  // n_cols is a multiple of 4
-  const int per = ((n_edges + int(gridDim.y) - 1) / int(gridDim.y) + 63) / 64 * 64;
+  const int c2 = blockIdx.x * kDw2Cols + 32 * wave + 2 * li;  // this lane's 2 columns
+  const bool cval = c2 < n_cols;  // n_cols is a multiple of 32
+  const int c2c = cval ? c2 : 0;
+  const int per = ((n_edges + int(gridDim.y) - 1) / int(gridDim.y) + kDw2Step - 1) / kDw2Step *
+                  kDw2Step;
   const int lo = int(blockIdx.y) * per, hi = min(n_edges, lo + per);
-  const int hk = threadIdx.x & 63;  // hidden unit of this thread's h values
+  const int hk = threadIdx.x & 63, hg = threadIdx.x >> 6;  // hidden unit, group of 4 edges
+  const int be = (threadIdx.x >> 3) & 31, bn = threadIdx.x & 7;  // basis (threads < 256)
+  const bool bthr = threadIdx.x < 256;
   float w1c[kRadBasis];
 #pragma unroll
   for (int n = 0; n < kRadBasis; ++n) w1c[n] = s_w1[n * kRadHidden + hk];
-  float4v acc[4][4];  // [hidden tile][t]
+  const double pref = sqrt(2.0 / double(rc));
+  const double kn = double(bn + 1) * 3.141592653589793 / double(rc);
+  float4v acc[4][2];  // [hidden tile][t]
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[mt][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int e0 = lo; e0 < hi; e0 += 64) {
-    // this block's dw for the 16 k steps, requested before h is built so the
-    // loads' latency overlaps that work
-    float4v bq[16];
+    for (int t = 0; t < 2; ++t) acc[mt][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  const int n_steps = lo < hi ? (hi - lo + kDw2Step - 1) / kDw2Step : 0;
+  if (n_steps > 0) {  // the same for the whole workgroup
+    // Every step issues its loads unconditionally and in the same order
+    // (the first group only loads, the steps past the range compute on
+    // zeroed rows), so each wait covers exactly the loads it needs.
+    const int n_pad = (n_steps + kDw2Ring - 1) / kDw2Ring * kDw2Ring;
+    float2v bq[kDw2Ring][8];
+    float ev[kDw2Ring][3];
+    int ld = 0;  // next step to load
+    auto load_step = [&](float2v (&b)[8], float (&v3)[3]) {
+      const int e0 = lo + kDw2Step * min(ld, n_steps - 1);
+      ++ld;
+      const float* pv = vec + int64_t(min(e0 + be, hi - 1)) * 3;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const int64_t e = e0 + 4 * ks + kq;
-      bq[ks] = (e < hi && cval) ? *reinterpret_cast<const float4v*>(dw + e * n_cols + c4)
-                                : float4v{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    if (threadIdx.x < 64) {
-      const int e = e0 + threadIdx.x;
-      float B[kRadBasis];
-      if (e < hi) {
-        bessel_basis(vec[int64_t(e) * 3], vec[int64_t(e) * 3 + 1], vec[int64_t(e) * 3 + 2], rc, B);
-      } else {
+      for (int d = 0; d < 3; ++d) v3[d] = pv[d];
 #pragma unroll
-        for (int n = 0; n < kRadBasis; ++n) B[n] = 0.0f;
+      for (int s = 0; s < 8; ++s) {
+        const int64_t e = min(e0 + 8 * kq + s, hi - 1);
+        b[s] = __builtin_nontemporal_load(reinterpret_cast<const float2v*>(dw + e * n_cols + c2c));
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads where they are issued
+    };
+    for (int k0 = -kDw2Ring; k0 < n_pad; k0 += kDw2Ring) {
+      const bool act = k0 >= 0;  // the same for the whole workgroup
 #pragma unroll
-      for (int n = 0; n < kRadBasis; ++n) s_b[threadIdx.x][n] = B[n];
+      for (int u = 0; u < kDw2Ring; ++u) {
+        const int e0 = lo + kDw2Step * (k0 + u);
+        Split3 A[4], B[2];
+        if (act) {
+          if (bthr) {
+            // B_n(d) = sqrt(2/rc) sin((n+1) pi d / rc) / d in fp64, rounded once
+            const double x = ev[u][0], y = ev[u][1], z = ev[u][2];
+            const double d = sqrt(x * x + y * y + z * z);
+            const float bv = d > 0.0 ? float(pref * sin(kn * d) / d) : float(pref * kn);
+            s_b[be][bn] = e0 + be < hi ? bv : 0.0f;
+          }
+          __syncthreads();  // s_b written; every wavefront is done with the last step's s_h
+          {
+            float v8[8];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const int el = 4 * hg + s;
+              float pre = 0.0f;
+#pragma unroll
+              for (int n = 0; n < kRadBasis; ++n) pre = fmaf(s_b[el][n], w1c[n], pre);
+              v8[s] = e0 + el < hi ? silu_sum_operand(pre) : 0.0f;
+              v8[4 + s] = 0.0f;
+            }
+            Split3 H;
+            split3(v8, H);
+            // lane hk % 16 + 16 (hg / 2) of tile hk / 16, elements 4 (hg % 2) .. +3
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+              s_h[(((hk >> 4) * 3 + p) * 64 + (hk & 15) + 16 * (hg >> 1)) * 2 + (hg & 1)] =
+                  __builtin_bit_cast(u32x4, H.p[p]).xy;
+          }
+          __syncthreads();  // s_h written; s_b is free again
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+              const u32x2 lo2 = s_h[((mt * 3 + p) * 64 + lane) * 2];
+              const u32x2 hi2 = s_h[((mt * 3 + p) * 64 + lane) * 2 + 1];
+              A[mt].p[p] = as_b8(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
+            }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            float v[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+              v[s] = cval && e0 + 8 * kq + s < hi ? bq[u][s][t] : 0.0f;
+            split3(v, B[t]);
+          }
+        }
+        load_step(bq[u], ev[u]);
+        if (act) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+              acc[mt][t] = mfma_bf16(A[mt].p[0], B[t].p[0], cross5(A[mt], B[t], acc[mt][t]));
+        }
+      }
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int q = 0; q < 64 / kDw2Waves; ++q) {
-      const int t = (threadIdx.x >> 6) + kDw2Waves * q;
-      float pre = 0.0f;
-#pragma unroll
-      for (int n = 0; n < kRadBasis; ++n) pre = fmaf(s_b[t][n], w1c[n], pre);
-      s_h[t][hk] = e0 + t < hi ? silu(pre) : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const int el = 4 * ks + kq;  // edge of this lane's k slot
-      float a[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a[mt] = s_h[el][16 * mt + li];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt], bq[ks][t], acc[mt][t], 0, 0, 0);
-    }
-    __syncthreads();  // s_b and s_h are rewritten by the next block
   }
-  // D row = hidden unit 16 mt + 4 kq + r, column = c4 + t (lane li's columns)
+  // D row = hidden unit 16 mt + 4 kq + r, column = c2 + t (lane li's columns)
   if (cval) {
-    float* pr = part + int64_t(blockIdx.y) * kRadHidden * n_cols + c4;
+    float* pr = part + int64_t(blockIdx.y) * kRadHidden * n_cols + c2;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float4v v = {acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
-        *reinterpret_cast<float4v*>(pr + int64_t(16 * mt + 4 * kq + r) * n_cols) = v;
+        const float2v v = {acc[mt][0][r], acc[mt][1][r]};
+        *reinterpret_cast<float2v*>(pr + int64_t(16 * mt + 4 * kq + r) * n_cols) = v;
       }
   }
 }
@@ -753,17 +947,26 @@ bool radial_conv_supported(const char* set_name) {
 
 int radial_dw2_ranges(int n_edges, int n_cols) {
   const int slabs = (n_cols + kDw2Cols - 1) / kDw2Cols;
-  const int blocks64 = std::max(1, (n_edges + 63) / 64);
-  return std::max(1, std::min(blocks64, (2048 + slabs - 1) / slabs));
+  const int steps = std::max(1, (n_edges + kDw2Step - 1) / kDw2Step);
+  return std::max(1, std::min(steps, (2048 + slabs - 1) / slabs));
+}
+
+size_t radial_w2_split_bytes(int n_cols) {
+  return size_t(w2_split_blocks(n_cols)) * kW2Units * 16;
 }
 
 hipError_t launch_radial_dh_dw2(int n_edges, int n_cols, const float* vec, float cutoff,
                                 const float* W1, const float* W2, const float* dw, float* dh,
-                                float* part, int ranges, hipStream_t s) {
+                                float* part, int ranges, void* w2s, hipStream_t s) {
   if (n_edges > 0) {
-    const int64_t n_blocks = (int64_t(n_edges) + 127) / 128;
-    const int g1 = int(std::min<int64_t>(n_blocks, 256 * 8));
-    hipLaunchKernelGGL(k_radial_dh, dim3(g1), dim3(256), 0, s, n_edges, n_cols, dw, W2, dh);
+    u32x4* w2u = static_cast<u32x4*>(w2s);
+    hipLaunchKernelGGL(k_radial_split_w2, dim3(w2_split_blocks(n_cols)), dim3(256), 0, s, n_cols,
+                       W2, w2u);
+    // two workgroups per CU are resident (registers); each walks its edge
+    // blocks as one load stream
+    const int64_t n_blocks = (int64_t(n_edges) + kDhEdges - 1) / kDhEdges;
+    const int g1 = int(std::min<int64_t>(n_blocks, 256));
+    hipLaunchKernelGGL(k_radial_dh, dim3(g1), dim3(256), 0, s, n_edges, n_cols, dw, w2u, dh);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

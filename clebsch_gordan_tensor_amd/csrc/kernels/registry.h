@@ -189,12 +189,14 @@ hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const
                               const float* dh, float* dvec, float* dW1_part, float* dW1,
                               hipStream_t s);
 // The second layer's backward from dw [E][n_cols] (n_cols a multiple of
-// 4): dh [E][64] and per-range partials part [ranges][64][n_cols] of dW2
-// (add them with launch_sum_partials, which overwrites them).
+// 32): dh [E][64] and per-range partials part [ranges][64][n_cols] of dW2
+// (add them with launch_sum_partials, which overwrites them).  w2s is device
+// scratch of radial_w2_split_bytes(n_cols) bytes, 16-byte aligned.
 int radial_dw2_ranges(int n_edges, int n_cols);
+size_t radial_w2_split_bytes(int n_cols);
 hipError_t launch_radial_dh_dw2(int n_edges, int n_cols, const float* vec, float cutoff,
                                 const float* W1, const float* W2, const float* dw, float* dh,
-                                float* part, int ranges, hipStream_t s);
+                                float* part, int ranges, void* w2s, hipStream_t s);
 hipError_t launch_sum_partials(int n_chunks, int n, float* part, float* out, hipStream_t s);
 hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
                                  float* dvec, hipStream_t s);

@@ -225,7 +225,10 @@ e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n
  * edge-vector gradient that flows through |r_e| (radial: dvec_e is parallel
  * to r_e, zero at r_e = 0); add it to e3_spherical_harmonics_backward's
  * for the full edge-vector gradient.  dh = dw W2^T and dW2 = h^T dw run on
- * the fp32 matrix cores, each reading dw once (dW2 through per-range partial
+ * the bf16 matrix cores with every fp32 operand split into three bf16 parts
+ * (24 significant bits and fp32's exponent range, so any cotangent
+ * magnitude is kept; six of the nine cross products, the others below
+ * 2^-24 of a product), each reading dw once (dW2 through per-range partial
  * sums added in a fixed order, h recomputed from the edge vectors).
  * workspace: caller-owned,
  * e3_radial_mlp_backward_workspace_size bytes, 16-byte aligned; dw and W2
