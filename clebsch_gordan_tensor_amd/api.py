@@ -538,6 +538,14 @@ def conv_forward_radial(desc: Desc, rowptr, sender, edge_vec, x, cutoff, W1, W2,
     return out
 
 
+def radial_mlp_backward_workspace_bytes(W1, W2, n_edges, n_cols):
+    """Device workspace bytes radial_mlp_backward needs for n_edges x n_cols."""
+    r = _radial(5.0, W1, W2)
+    nb = C.c_size_t()
+    _check(lib().e3_radial_mlp_backward_workspace_size(C.byref(r), n_edges, n_cols, C.byref(nb)))
+    return nb.value
+
+
 def radial_mlp_backward(edge_vec, cutoff, W1, W2, dw, workspace=None, stream=None):
     """(dW1, dW2, dvec) for the cotangent dw [E][n_cols] of radial_mlp; dvec is
     the edge-vector gradient through |r| only."""

@@ -168,7 +168,10 @@ def test_radial_conv_unsupported(gpu):
 
 # ------------------------------------------------------- MLP backward
 
-@pytest.mark.parametrize("E,n_cols", [(3001, 1280), (40, 64), (0, 32)])
+# (5, 96): fewer edges than one 16-row tile, three 32-column blocks (a part
+# stage) and a column slab mostly past the end; (130, 288): one edge past a
+# 128-edge block, nine blocks (two stages and one block of a third)
+@pytest.mark.parametrize("E,n_cols", [(3001, 1280), (40, 64), (0, 32), (5, 96), (130, 288)])
 def test_radial_mlp_backward_matches_oracle(gpu, E, n_cols):
     rng = np.random.default_rng(220 + E)
     ev = (rng.standard_normal((E, 3)) * 2.0).astype(np.float32)
@@ -186,6 +189,24 @@ def test_radial_mlp_backward_matches_oracle(gpu, E, n_cols):
     assert_close(host(dW2), rW2, TOL_F32, f"radial dW2 E={E}")
     assert_close(host(dvec), rvec, TOL_F32, f"radial dvec E={E}")
     assert np.all(host(dvec)[1] == 0.0) if E > 2 else True
+
+
+@pytest.mark.parametrize("scale", [2.0**-70, 2.0**70])
+def test_radial_mlp_backward_cotangent_scale(gpu, scale):
+    # the products run on bf16 parts of the fp32 operands: a cotangent far
+    # from 1 in magnitude keeps its precision (a power of two scales the
+    # oracle's result exactly)
+    rng = np.random.default_rng(240)
+    E, n_cols = 700, 320
+    ev = (rng.standard_normal((E, 3)) * 2.0).astype(np.float32)
+    W1, W2 = _weights(n_cols, 241)
+    dw = rng.standard_normal((E, n_cols)).astype(np.float32)
+    dW1, dW2, dvec = gpu.radial_mlp_backward(dev(ev), 5.0, dev(W1), dev(W2), dev(dw * np.float32(scale)))
+    torch.cuda.synchronize()
+    rW1, rW2, rvec = R.radial_mlp_backward(ev, 5.0, W1, W2, dw)
+    assert_close(host(dW1) / scale, rW1, TOL_F32, f"radial dW1 scale {scale:g}")
+    assert_close(host(dW2) / scale, rW2, TOL_F32, f"radial dW2 scale {scale:g}")
+    assert_close(host(dvec) / scale, rvec, TOL_F32, f"radial dvec scale {scale:g}")
 
 
 def test_radial_mlp_backward_deterministic_and_radial(gpu):
