@@ -463,13 +463,20 @@ constexpr int kTailBatch = 64;
 // Per edge, from dh = dw W2^T: dpre = dh * silu'(pre), the radial part of
 // the edge-vector gradient dvec = (sum_n B'_n(d) (dpre W1^T)_n) r / d, and
 // this chunk's partial dW1[n][k] = sum_e B_n(e) dpre_k(e) (fixed order).
-// One workgroup per chunk of edges, 64 edges per batch.
+// One workgroup per chunk of edges, 64 edges per batch, in four phases: the
+// basis and its derivative per edge (fp64, one thread per edge); dpre with
+// thread (k, g) taking hidden unit k of every fourth edge, so a wavefront
+// reads an edge's dh row as one 256-byte access; g_n = sum_k dpre_k W1[n][k]
+// with four threads per edge, two n each; dvec per edge.  Every sum keeps
+// the order of a one-thread-per-edge evaluation.
 __global__ void __launch_bounds__(256)
     k_radial_tail(int n_edges, int n_chunks, const float* __restrict__ vec, float rc,
                   const float* __restrict__ W1, const float* __restrict__ dh,
                   float* __restrict__ dvec, float* __restrict__ dW1_part) {
   __shared__ float s_w1[kRadBasis * kRadHidden];
   __shared__ float s_b[kTailBatch][kRadBasis];
+  __shared__ float s_bd[kTailBatch][kRadBasis + 1];
+  __shared__ float s_g[kTailBatch][kRadBasis + 1];
   __shared__ float s_dp[kTailBatch][kRadHidden + 1];
   for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
   __syncthreads();
@@ -477,65 +484,78 @@ __global__ void __launch_bounds__(256)
   const int lo = blockIdx.x * per, hi = min(n_edges, lo + per);
   float acc0 = 0.0f, acc1 = 0.0f;  // pairs threadIdx.x and threadIdx.x + 256 of [8][64]
   const int p0 = threadIdx.x, p1 = threadIdx.x + 256;
+  const int hk = threadIdx.x & 63, hg = threadIdx.x >> 6;  // phase 2: hidden unit, edge group
+  const int ge = threadIdx.x >> 2, gq = threadIdx.x & 3;   // phase 3: edge, pair of n
+  float w1c[kRadBasis];
+#pragma unroll
+  for (int n = 0; n < kRadBasis; ++n) w1c[n] = s_w1[n * kRadHidden + hk];
   for (int e0 = lo; e0 < hi; e0 += kTailBatch) {
     const int ne = min(kTailBatch, hi - e0);
-    if (threadIdx.x < kTailBatch) {
+    if (threadIdx.x < ne) {
       const int t = threadIdx.x;
-      if (t < ne) {
-        const int64_t e = e0 + t;
-        const float vx = vec[e * 3], vy = vec[e * 3 + 1], vz = vec[e * 3 + 2];
-        const double d = sqrt(double(vx) * vx + double(vy) * vy + double(vz) * vz);
-        const double pref = sqrt(2.0 / double(rc));
-        float B[kRadBasis], Bd[kRadBasis];
-        if (d > 0.0) {
-          double sn, cs;
-          const double th = 3.141592653589793 * d / double(rc);
-          sincos(th, &sn, &cs);
-          // sin(n th), cos(n th) by the angle-addition recurrence
-          double s_n = sn, c_n = cs;
-#pragma unroll
-          for (int n = 0; n < kRadBasis; ++n) {
-            const double kn = double(n + 1) * 3.141592653589793 / double(rc);
-            B[n] = float(pref * s_n / d);
-            Bd[n] = float(pref * (kn * c_n / d - s_n / (d * d)));
-            const double s_next = s_n * cs + c_n * sn, c_next = c_n * cs - s_n * sn;
-            s_n = s_next;
-            c_n = c_next;
-          }
-        } else {
-#pragma unroll
-          for (int n = 0; n < kRadBasis; ++n) {
-            B[n] = float(pref * double(n + 1) * 3.141592653589793 / double(rc));
-            Bd[n] = 0.0f;
-          }
-        }
-        float g[kRadBasis];
-#pragma unroll
-        for (int n = 0; n < kRadBasis; ++n) g[n] = 0.0f;
-        const float* dhe = dh + e * kRadHidden;
-        for (int k = 0; k < kRadHidden; ++k) {
-          float pre = 0.0f;
-#pragma unroll
-          for (int n = 0; n < kRadBasis; ++n) pre = fmaf(B[n], s_w1[n * kRadHidden + k], pre);
-          const float sg = 1.0f / (1.0f + expf(-pre));
-          const float dp = dhe[k] * sg * (1.0f + pre * (1.0f - sg));
-          s_dp[t][k] = dp;
-#pragma unroll
-          for (int n = 0; n < kRadBasis; ++n) g[n] = fmaf(dp, s_w1[n * kRadHidden + k], g[n]);
-        }
-        float dd = 0.0f;
+      const int64_t e = e0 + t;
+      const float vx = vec[e * 3], vy = vec[e * 3 + 1], vz = vec[e * 3 + 2];
+      const double d = sqrt(double(vx) * vx + double(vy) * vy + double(vz) * vz);
+      const double pref = sqrt(2.0 / double(rc));
+      if (d > 0.0) {
+        double sn, cs;
+        const double th = 3.141592653589793 * d / double(rc);
+        sincos(th, &sn, &cs);
+        // sin(n th), cos(n th) by the angle-addition recurrence; one
+        // division (fp64 divisions are long instruction sequences)
+        const double inv = 1.0 / d, k1 = 3.141592653589793 / double(rc);
+        double s_n = sn, c_n = cs;
 #pragma unroll
         for (int n = 0; n < kRadBasis; ++n) {
-          dd = fmaf(Bd[n], g[n], dd);
-          s_b[t][n] = B[n];
+          const double kn = double(n + 1) * k1;
+          s_b[t][n] = float(pref * s_n * inv);
+          s_bd[t][n] = float(pref * (kn * c_n - s_n * inv) * inv);
+          const double s_next = s_n * cs + c_n * sn, c_next = c_n * cs - s_n * sn;
+          s_n = s_next;
+          c_n = c_next;
         }
-        const float inv = d > 0.0 ? float(1.0 / d) : 0.0f;
-        dvec[e * 3] = dd * vx * inv;
-        dvec[e * 3 + 1] = dd * vy * inv;
-        dvec[e * 3 + 2] = dd * vz * inv;
+      } else {
+#pragma unroll
+        for (int n = 0; n < kRadBasis; ++n) {
+          s_b[t][n] = float(pref * double(n + 1) * 3.141592653589793 / double(rc));
+          s_bd[t][n] = 0.0f;
+        }
       }
     }
     __syncthreads();
+    for (int t = hg; t < ne; t += 4) {
+      float pre = 0.0f;
+#pragma unroll
+      for (int n = 0; n < kRadBasis; ++n) pre = fmaf(s_b[t][n], w1c[n], pre);
+      const float sg = 1.0f / (1.0f + expf(-pre));
+      s_dp[t][hk] = dh[(int64_t(e0) + t) * kRadHidden + hk] * sg * (1.0f + pre * (1.0f - sg));
+    }
+    __syncthreads();
+    if (ge < ne) {
+      float g0 = 0.0f, g1 = 0.0f;
+      const float* wa = s_w1 + (2 * gq) * kRadHidden;
+      for (int k = 0; k < kRadHidden; ++k) {
+        const float dp = s_dp[ge][k];
+        g0 = fmaf(dp, wa[k], g0);
+        g1 = fmaf(dp, wa[kRadHidden + k], g1);
+      }
+      s_g[ge][2 * gq] = g0;
+      s_g[ge][2 * gq + 1] = g1;
+    }
+    __syncthreads();
+    if (threadIdx.x < ne) {
+      const int t = threadIdx.x;
+      const int64_t e = e0 + t;
+      float dd = 0.0f;
+#pragma unroll
+      for (int n = 0; n < kRadBasis; ++n) dd = fmaf(s_bd[t][n], s_g[t][n], dd);
+      const float vx = vec[e * 3], vy = vec[e * 3 + 1], vz = vec[e * 3 + 2];
+      const double d = sqrt(double(vx) * vx + double(vy) * vy + double(vz) * vz);
+      const float inv = d > 0.0 ? float(1.0 / d) : 0.0f;
+      dvec[e * 3] = dd * vx * inv;
+      dvec[e * 3 + 1] = dd * vy * inv;
+      dvec[e * 3 + 2] = dd * vz * inv;
+    }
     {
       const int n0 = p0 / kRadHidden, k0 = p0 % kRadHidden;
       const int n1 = p1 / kRadHidden, k1 = p1 % kRadHidden;
