@@ -49,9 +49,10 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_conv_double_backward", "e3_radial_mlp", "e3_conv_forward_radial",
            "e3_radial_mlp_backward_workspace_size", "e3_radial_mlp_backward",
            "e3_generic_plan_size", "e3_generic_plan_build", "e3_tp_forward_generic",
+           "e3_tp_forward_gemm",
            "e3_tp_backward_generic", "e3_conv_forward_generic", "e3_conv_backward_generic",
            "e3_conv_double_backward_generic", "e3_last_error"]
-E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY = 0, 1, 2, 3
+E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY, E3_GEN_GEMM = 0, 1, 2, 3, 4
 
 
 class _CRadial(C.Structure):
@@ -602,6 +603,25 @@ def tp_forward_generic(desc: Desc, x, y, w, out=None, stream=None):
     _check(lib().e3_tp_forward_generic(C.byref(desc.c()), B, _ptr(plan), plan.numel() * 4, _ptr(x),
                                        _ptr(y), _ptr(w), _ptr(out), _dtype_code(x),
                                        _stream(stream)))
+    return out
+
+
+def tp_forward_gemm(desc: Desc, x, y, w, out=None, stream=None):
+    """z = tensor product of x and y weighted by w (as tp_forward_generic) as
+    one dense product per output block on the fp32 matrix cores (float32,
+    C % 16 == 0, degrees up to 6)."""
+    import torch
+    B = x.shape[0]
+    P = num_paths(desc)
+    _need(x, "x", shape=(B, desc.dx, desc.channels), dtype=torch.float32)
+    _need(y, "y", shape=(B, desc.dy), dtype=torch.float32)
+    _need(w, "w", shape=(B, P, desc.channels), dtype=torch.float32)
+    if out is None:
+        out = torch.empty((B, desc.dout, desc.channels), device=x.device, dtype=torch.float32)
+    _need(out, "out", shape=(B, desc.dout, desc.channels), dtype=torch.float32)
+    plan = generic_plan(desc, x.device, E3_GEN_GEMM)
+    _check(lib().e3_tp_forward_gemm(C.byref(desc.c()), B, _ptr(plan), plan.numel() * 4, _ptr(x),
+                                    _ptr(y), _ptr(w), _ptr(out), _stream(stream)))
     return out
 
 

@@ -31,6 +31,7 @@ HIP_SOURCES = [
     "kernels/linear.hip",
     "kernels/radial.hip",
     "kernels/generic.hip",
+    "kernels/gemm.hip",
     "api.cpp",
     "host/cg_ladder.cpp",
 ]

@@ -8,6 +8,8 @@
 #include <cstring>
 #include <algorithm>
 #include <cmath>
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -845,13 +847,15 @@ struct GenDims {
   int operand, y, keys, weights;  // kernel's view: x comps, y comps, outputs, w rows
 };
 
-e3_status generic_entries(const e3_desc* desc, Parsed& p, std::vector<GenEntry>& ent) {
+e3_status generic_entries(const e3_desc* desc, Parsed& p, std::vector<GenEntry>& ent,
+                          bool table_limits = true) {
   e3_status s = parse(desc, p);
   if (s != E3_OK) return s;
   for (const auto* v : {&p.x, &p.y, &p.o})
     for (const auto& r : *v)
       if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 6");
-  if (p.dx * 64 + p.dy > 4096 || p.dout * 64 + p.dy > 4096 || p.dy >= 65536)
+  if (p.dy >= 65536) return fail(E3_ERR_UNSUPPORTED, "too many y components");
+  if (table_limits && (p.dx * 64 + p.dy > 4096 || p.dout * 64 + p.dy > 4096))
     return fail(E3_ERR_UNSUPPORTED,
                 "too many components for the generic kernel (dx, dout <= 63)");
   std::vector<int> xoff(p.x.size()), yoff(p.y.size()), ooff(p.o.size());
@@ -949,12 +953,157 @@ e3_status build_generic(const e3_desc* desc, int table, std::vector<int32_t>& ou
   return ok();
 }
 
+// The dense-product plan of the tensor product (kernels/gemm.hip).  Output
+// blocks are the output irreps (one per path with E3_OUT_PER_PATH); a block's
+// K list concatenates, in path order, the x components (P, m1) of its paths
+// and pads to a multiple of 4; A[M][k] = sum_{m2} C_P[M][m1][m2] y[m2] is
+// listed as groups of (y component, c) records, one group per nonzero entry.
+e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemmArgs& d) {
+  Parsed p;
+  std::vector<GenEntry> ent;
+  e3_status s = generic_entries(desc, p, ent, false);
+  if (s != E3_OK) return s;
+  if (p.P > 32767 || p.dx > 65535) return fail(E3_ERR_UNSUPPORTED, "too many paths");
+  std::vector<int> xoff(p.x.size()), ooff(p.o.size());
+  for (size_t i = 0, o = 0; i < p.x.size(); ++i) xoff[i] = int(o), o += 2 * p.x[i].l + 1;
+  for (size_t i = 0, o = 0; i < p.o.size(); ++i) ooff[i] = int(o), o += 2 * p.o[i].l + 1;
+  const int nb = p.per_path ? p.P : int(p.o.size());
+  std::vector<int> b_oo(nb), b_rows(nb), b_kb(nb), b_K(nb), b_abase(nb);
+  std::vector<int> path_block(p.P), path_koff(p.P);
+  std::vector<std::vector<int>> bpaths(nb);
+  for (int pi = 0, opp = 0; pi < p.P; ++pi) {
+    const int L = p.o[p.pio[pi]].l;
+    const int b = p.per_path ? pi : p.pio[pi];
+    path_block[pi] = b;
+    bpaths[b].push_back(pi);
+    b_rows[b] = 2 * L + 1;
+    b_oo[b] = p.per_path ? opp : ooff[p.pio[pi]];
+    opp += 2 * L + 1;
+  }
+  std::vector<int32_t> klist;
+  int abase = 0;
+  for (int b = 0; b < nb; ++b) {
+    if (b_rows[b] > 16) return fail(E3_ERR_UNSUPPORTED, "output degree above 7");
+    b_kb[b] = int(klist.size());
+    int k = 0;
+    for (int pi : bpaths[b]) {
+      path_koff[pi] = k;
+      const int n1 = 2 * p.x[p.pix[pi]].l + 1;
+      for (int m1 = 0; m1 < n1; ++m1) klist.push_back((pi << 16) | (xoff[p.pix[pi]] + m1));
+      k += n1;
+    }
+    while (k % 4) klist.push_back(-1), ++k;
+    b_K[b] = k;
+    b_abase[b] = abase;
+    abase += b_rows[b] * k;
+  }
+  struct GE {
+    int at, yi;
+    float c;
+  };
+  std::vector<GE> ge;
+  ge.reserve(ent.size());
+  for (const GenEntry& e : ent) {
+    const int b = path_block[e.P];
+    const int M = e.o - b_oo[b];
+    const int k = path_koff[e.P] + (e.xi - xoff[p.pix[e.P]]);
+    ge.push_back(GE{b_abase[b] + k * b_rows[b] + M, e.yi, e.c});  // A[k][M]
+  }
+  std::stable_sort(ge.begin(), ge.end(), [](const GE& a, const GE& b) { return a.at < b.at; });
+  // one entry per A element: {at, y1 | y2 << 16, c1, c2}; the real basis
+  // couples each (M, m1) to at most two m2
+  std::vector<int32_t> groups;
+  for (size_t i = 0; i < ge.size();) {
+    size_t j = i;
+    while (j < ge.size() && ge[j].at == ge[i].at) ++j;
+    if (j - i > 2) return fail(E3_ERR_UNSUPPORTED, "an A entry with more than two terms");
+    const GE& a = ge[i];
+    const GE& b = j - i == 2 ? ge[i + 1] : GE{a.at, a.yi, 0.0f};
+    int32_t ca, cb;
+    std::memcpy(&ca, &a.c, 4);
+    std::memcpy(&cb, &b.c, 4);
+    groups.insert(groups.end(), {a.at, int32_t(a.yi | (b.yi << 16)), ca, cb});
+    i = j;
+  }
+  const int n_groups = int(groups.size() / 4);
+  d = e3k::TpGemmArgs{};
+  d.n_blocks = nb;
+  d.dx = p.dx;
+  d.dy = p.dy;
+  d.dout = p.dout;
+  d.P = p.P;
+  d.n_klist = int(klist.size());
+  d.n_groups = n_groups;
+  d.n_recs = 0;
+  d.a_floats = std::max(abase, 1);
+  d.off_blocks = e3k::kGemmHeader;
+  d.off_klist = d.off_blocks + 4 * nb;
+  d.off_groups = (d.off_klist + d.n_klist + 3) / 4 * 4;  // 16-byte entries
+  d.off_recs = d.off_groups + int(groups.size());
+  out.assign(size_t(d.off_recs), 0);
+  const int32_t head[14] = {e3k::kGemmMagic, nb,         p.dx,         p.dy,
+                            p.dout,          p.P,        d.n_klist,    n_groups,
+                            d.n_recs,        d.a_floats, d.off_blocks, d.off_klist,
+                            d.off_groups,    d.off_recs};
+  std::copy(head, head + 14, out.begin());
+  for (int b = 0; b < nb; ++b) {
+    out[d.off_blocks + 4 * b] = b_oo[b];
+    out[d.off_blocks + 4 * b + 1] = b_rows[b];
+    out[d.off_blocks + 4 * b + 2] = b_kb[b];
+    out[d.off_blocks + 4 * b + 3] = b_K[b];
+  }
+  std::copy(klist.begin(), klist.end(), out.begin() + d.off_klist);
+  std::copy(groups.begin(), groups.end(), out.begin() + d.off_groups);
+  return ok();
+}
+
+// The plan's sizes per descriptor, built once (the kernel takes them from
+// the host, not from the caller's device copy).
+e3_status gemm_dims(const e3_desc* desc, e3k::TpGemmArgs& d, size_t& bytes) {
+  static std::mutex mu;
+  static std::map<std::string, std::pair<e3k::TpGemmArgs, size_t>> cache;
+  std::string key;
+  if (!desc) return fail(E3_ERR_INVALID_ARG, "desc is null");
+  for (const e3_irreps* v : {&desc->x, &desc->y, &desc->out}) {
+    if (v->n < 0 || (v->n > 0 && !v->v)) return fail(E3_ERR_IRREPS, "bad irreps list");
+    for (int i = 0; i < v->n; ++i)
+      key += std::to_string(v->v[i].mul) + "x" + std::to_string(v->v[i].l) +
+             (v->v[i].parity > 0 ? "e" : "o") + ",";
+    key += "|";
+  }
+  key += std::to_string(desc->flags & E3_OUT_PER_PATH);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      d = it->second.first;
+      bytes = it->second.second;
+      return ok();
+    }
+  }
+  std::vector<int32_t> words;
+  e3_status s = build_gemm(desc, words, d);
+  if (s != E3_OK) return s;
+  bytes = words.size() * 4;
+  std::lock_guard<std::mutex> g(mu);
+  cache[key] = {d, bytes};
+  return ok();
+}
+
+e3_status build_table(const e3_desc* desc, int table, std::vector<int32_t>& out) {
+  if (table == E3_GEN_GEMM) {
+    e3k::TpGemmArgs d;
+    return build_gemm(desc, out, d);
+  }
+  return build_generic(desc, table, out);
+}
+
 }  // namespace
 
 e3_status e3_generic_plan_size(const e3_desc* desc, int32_t table, size_t* bytes) {
   if (!bytes) return fail(E3_ERR_INVALID_ARG, "bytes is null");
   std::vector<int32_t> t;
-  e3_status s = build_generic(desc, table, t);
+  e3_status s = build_table(desc, table, t);
   if (s != E3_OK) return s;
   *bytes = t.size() * sizeof(int32_t);
   return ok();
@@ -964,7 +1113,7 @@ e3_status e3_generic_plan_build(const e3_desc* desc, int32_t table, void* host_p
                                 size_t bytes) {
   if (!host_plan) return fail(E3_ERR_INVALID_ARG, "host_plan is null");
   std::vector<int32_t> t;
-  e3_status s = build_generic(desc, table, t);
+  e3_status s = build_table(desc, table, t);
   if (s != E3_OK) return s;
   if (bytes < t.size() * sizeof(int32_t))
     return fail(E3_ERR_WORKSPACE, "plan needs " + std::to_string(t.size() * 4) + " bytes");
@@ -1011,6 +1160,49 @@ e3_status e3_tp_forward_generic(const e3_desc* desc, int64_t n_rows, const void*
                        static_cast<const int*>(plan), int64_t(plan_bytes / 4), x, y, w, z};
   return hip_status(e3k::launch_tp_generic(a, dtype == E3_BF16, hipStream_t(stream)),
                     "tp_forward_generic");
+}
+
+e3_status e3_tp_forward_gemm(const e3_desc* desc, int64_t n_rows, const void* plan,
+                             size_t plan_bytes, const float* x, const float* y, const float* w,
+                             float* z, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  e3k::TpGemmArgs a;
+  size_t need = 0;
+  if ((s = gemm_dims(desc, a, need)) != E3_OK) return s;
+  if (p.C % 16) return fail(E3_ERR_UNSUPPORTED, "the dense-product kernel needs C % 16 == 0");
+  if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows == 0) return ok();
+  if (!plan || plan_bytes < need)
+    return fail(E3_ERR_INVALID_ARG, "plan needs " + std::to_string(need) +
+                                        " bytes (E3_GEN_GEMM table of this descriptor)");
+  if (!x || !y || !w || !z) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(plan))
+    return fail(E3_ERR_ALIGNMENT, "x, w and the plan must be 16-byte aligned");
+  a.n_rows = n_rows;
+  a.C = p.C;
+  // the widest channel slab with two workgroups per CU, else with one
+  a.CS = 0;
+  for (size_t cap : {size_t(80) * 1024, size_t(160) * 1024}) {
+    for (int cs : {128, 64, 32, 16}) {
+      if (cs > p.C || p.C % cs) continue;
+      a.CS = cs;
+      if (e3k::tp_gemm_lds_bytes(a) <= cap) break;
+      a.CS = 0;
+    }
+    if (a.CS) break;
+  }
+  if (!a.CS) return fail(E3_ERR_UNSUPPORTED, "the dense-product plan does not fit in LDS");
+  if ((a.P + 1) * e3k::gemm_row_stride(a.CS) > 65535 || a.dx * e3k::gemm_row_stride(a.CS) > 65535)
+    return fail(E3_ERR_UNSUPPORTED, "too many x components or paths for the dense-product kernel");
+  a.lds_bytes = e3k::tp_gemm_lds_bytes(a);
+  a.plan = static_cast<const int*>(plan);
+  a.x = x;
+  a.y = y;
+  a.w = w;
+  a.z = z;
+  return hip_status(e3k::launch_tp_gemm(a, hipStream_t(stream)), "tp_forward_gemm");
 }
 
 e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_dx,

@@ -1,0 +1,172 @@
+// The channel-wise tensor product of high degree as dense products on the
+// fp32 matrix cores.
+//
+// e3j (E.1, Eq.10-11) forms, per path P = (l1, l2 -> L) and channel q,
+//   z_P[M][q] = sum_{m1,m2} C_P[M][m1][m2] y[m2] x[l1,m1][q],
+// weights it per channel, z[L][M][q] += w[P][q] z_P[M][q], and sums the paths
+// of each output block.  The coefficient sum over m2 does not depend on the
+// channel: A_P[M][m1] = sum_{m2} C_P[M][m1][m2] y[m2] is one small matrix per
+// row.  Folding the weight into x, xt_P[m1][q] = w[P][q] x[l1,m1][q], turns
+// each output block into one matrix product over the concatenated (P, m1):
+//   z[L][M][q] = sum_{(P,m1): P -> L} A_L[M][(P,m1)] xt[(P,m1)][q].
+// The product runs on v_mfma_f32_16x16x4f32 (fp32 operands, exact products,
+// fp32 accumulation): A_L is built per row in LDS, xt is formed per lane from
+// the row's x and w staged in LDS, so the per-channel arithmetic is one
+// multiply per product term instead of a walk over the coefficient records.
+//
+// Plan (host-built, see the GEMM table of the library):
+//   header kGemmHeader words: magic, n_blocks, dx, dy, dout, P, n_klist,
+//     n_groups, 0 (unused), a_floats, off_blocks, off_klist, off_groups, end
+//   blocks [n_blocks][4]: output offset, rows (2L+1), K-list start, K (x4)
+//   klist  [n_klist]: (P << 16) | x component, or -1 for a padding column
+//   groups [n_groups][4]: A index (block base + M * K + k), the two y
+//     components (y1 | y2 << 16), the two coefficients' bits (a real-basis
+//     entry A[M][m1] couples at most two m2; an unused second term has c = 0)
+// A is stored block after block, each transposed (A[k][M], stride rows =
+// 2L+1; the MFMA's rows past them read zero), so a k-step's 64 reads fall in
+// distinct banks; the staged x and w rows have a stride of 16 (mod 32)
+// floats for the same reason (the four k of a step read four rows).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "registry.h"
+
+namespace e3k {
+namespace {
+
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// One workgroup (four wavefronts) per (row, slab of CS channels), rows in a
+// grid-stride sequence.  LDS: A for every block (a_floats), the slab's x
+// [dx][CS] and w [P][CS], the row's y and the K list.  A wavefront takes the
+// 16-channel tiles wave, wave + 4, ... of the slab.  The sizes come from the
+// host (built from the descriptor); every index read from the plan is
+// clamped to them, so a plan of another descriptor gives wrong values but no
+// access outside the arrays.
+__global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
+  extern __shared__ __align__(16) float gsm[];
+  const int* __restrict__ blocks = g.plan + g.off_blocks;
+  const int* __restrict__ klist = g.plan + g.off_klist;
+  const int4* __restrict__ groups = reinterpret_cast<const int4*>(g.plan + g.off_groups);
+  const int CS = g.CS, C = g.C, XS = gemm_row_stride(CS);
+  const int lg4 = __builtin_ctz(CS / 4);  // CS is a power of two
+  float* s_a = gsm;
+  float* s_x = s_a + g.a_floats;
+  float* s_w = s_x + g.dx * XS;  // P rows and a zero row (the padding columns' weight)
+  float* s_y = s_w + (g.P + 1) * XS;
+  int* s_k = reinterpret_cast<int*>(s_y + g.dy);
+  // the K list as LDS offsets of its w and x rows (clamped here, once)
+  for (int i = threadIdx.x; i < g.n_klist; i += 256) {
+    const int ent = klist[i];
+    const int p = ent < 0 ? g.P : min(ent >> 16, g.P - 1);
+    const int xi = ent < 0 ? 0 : min(ent & 0xFFFF, g.dx - 1);
+    s_k[i] = p * XS | (xi * XS) << 16;
+  }
+  for (int i = threadIdx.x; i < XS; i += 256) s_w[g.P * XS + i] = 0.0f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, kq = lane >> 4;
+  const int n_slabs = C / CS, n_tiles = CS / 16;
+  const int64_t n_items = g.n_rows * n_slabs;
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int64_t row = item / n_slabs;
+    const int c0 = int(item - row * n_slabs) * CS;
+    __syncthreads();  // the previous item's LDS reads are done (and s_k is written)
+    // stage the slab of x and w and the row's y; clear A
+    for (int i = threadIdx.x; i < (g.dx << lg4); i += 256) {
+      const int r = i >> lg4, c = 4 * (i & ((1 << lg4) - 1));
+      *reinterpret_cast<float4v*>(s_x + r * XS + c) =
+          *reinterpret_cast<const float4v*>(g.x + (row * g.dx + r) * C + c0 + c);
+    }
+    for (int i = threadIdx.x; i < (g.P << lg4); i += 256) {
+      const int r = i >> lg4, c = 4 * (i & ((1 << lg4) - 1));
+      *reinterpret_cast<float4v*>(s_w + r * XS + c) =
+          *reinterpret_cast<const float4v*>(g.w + (row * g.P + r) * C + c0 + c);
+    }
+    for (int i = threadIdx.x; i < g.dy; i += 256) s_y[i] = g.y[row * g.dy + i];
+    for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
+    __syncthreads();
+    // A[k][M] = c1 y[y1] + c2 y[y2]: one independent 16-byte load per entry
+#pragma unroll 4
+    for (int q = threadIdx.x; q < g.n_groups; q += 256) {
+      const int4 e = groups[q];
+      const int at = min(max(e.x, 0), g.a_floats - 1);
+      const int y1 = min(e.y & 0xFFFF, g.dy - 1), y2 = min((e.y >> 16) & 0xFFFF, g.dy - 1);
+      s_a[at] = fmaf(__int_as_float(e.w), s_y[y2], __int_as_float(e.z) * s_y[y1]);
+    }
+    __syncthreads();
+    int abase = 0;
+    for (int b = 0; b < g.n_blocks; ++b) {
+      const int oo = blocks[4 * b], rows = min(max(blocks[4 * b + 1], 1), 16);
+      const int kb = min(max(blocks[4 * b + 2], 0), g.n_klist);
+      const int K = min(max(blocks[4 * b + 3], 0), g.n_klist - kb) & ~3;
+      if (abase + rows * K > g.a_floats) break;
+      // A[k = k0 + kq][M = li] at abase + k * rows + M; lanes past the rows read a
+      // valid entry and take zero
+      const bool aok = li < rows;
+      const float* ap = s_a + abase + kq * rows + min(li, rows - 1);
+      const int* kp = s_k + kb + kq;
+      for (int t0 = wave; t0 < n_tiles; t0 += 16) {
+        // up to four tiles of this wavefront at a time: t0, t0 + 4, ...
+        const int nu = min(4, (n_tiles - t0 + 3) / 4);
+        float4v D[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) D[u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+        const float* sw = s_w + 16 * t0 + li;
+        const float* sx = s_x + 16 * t0 + li;
+#pragma unroll 4
+        for (int k0 = 0; k0 < K; k0 += 4) {
+          const float av = ap[k0 * rows];
+          const float a = aok ? av : 0.0f;
+          const int ent = kp[k0];
+          const int wo = ent & 0xFFFF, xo = int(unsigned(ent) >> 16);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (u < nu) D[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                  a, sw[wo + 64 * u] * sx[xo + 64 * u], D[u], 0, 0, 0);
+          }
+        }
+        // D[i][j] in register i % 4 of lane j + 16 (i / 4): row 4 kq + r, channel li
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (u < nu) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = 4 * kq + r, o = oo + i;
+              if (i < rows && o >= 0 && o < g.dout)
+                g.z[(row * g.dout + o) * C + c0 + 16 * (t0 + 4 * u) + li] = D[u][r];
+            }
+          }
+        }
+      }
+      abase += rows * K;
+    }
+  }
+}
+
+}  // namespace
+
+size_t tp_gemm_lds_bytes(const TpGemmArgs& a) {
+  const int XS = gemm_row_stride(a.CS);
+  return size_t(a.a_floats + a.dx * XS + (a.P + 1) * XS + a.dy + a.n_klist) * 4;
+}
+
+hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  static bool attr = false;  // the attribute is per function: set once
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tp_gemm),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t items = a.n_rows * (a.C / a.CS);
+  if (a.lds_bytes > 160 * 1024) return hipErrorInvalidValue;
+  const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.lds_bytes, 1)));
+  const int grid = int(std::min<int64_t>(items, int64_t(256) * std::min(per_cu, 8)));
+  hipLaunchKernelGGL(k_tp_gemm, dim3(grid), dim3(256), a.lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace e3k

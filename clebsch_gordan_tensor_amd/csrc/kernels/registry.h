@@ -198,6 +198,26 @@ hipError_t launch_radial_dh_dw2(int n_edges, int n_cols, const float* vec, float
                                 const float* W1, const float* W2, const float* dw, float* dh,
                                 float* part, int ranges, void* w2s, hipStream_t s);
 hipError_t launch_sum_partials(int n_chunks, int n, float* part, float* out, hipStream_t s);
+// The tensor product as dense products per output block on the fp32 matrix
+// cores (gemm.hip); sizes from the host-built plan, plan in device memory.
+constexpr int kGemmHeader = 16;
+constexpr int kGemmMagic = 0x4D4D4547;
+struct TpGemmArgs {
+  int64_t n_rows;
+  int C, CS;  // channels; channel slab per workgroup (C % CS == 0, CS % 16 == 0)
+  int n_blocks, dx, dy, dout, P, n_klist, n_groups, n_recs, a_floats;
+  int off_blocks, off_klist, off_groups, off_recs;  // word offsets in plan
+  const int* plan;
+  const float* x;
+  const float* y;
+  const float* w;
+  float* z;
+  size_t lds_bytes;
+};
+// LDS row stride (floats) of a staged slab of CS channels: 16 (mod 32)
+__host__ __device__ constexpr int gemm_row_stride(int CS) { return CS / 32 * 32 + 16 + (CS % 32 ? 32 : 0); }
+size_t tp_gemm_lds_bytes(const TpGemmArgs& a);
+hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s);
 hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
                                  float* dvec, hipStream_t s);
 hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr,

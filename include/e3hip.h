@@ -261,13 +261,28 @@ e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t 
  * (dx, dout <= 63).  A table built for another descriptor gives wrong
  * values but never an out-of-bounds access (every index read from it is
  * clamped). */
-enum { E3_GEN_FORWARD = 0, E3_GEN_DX = 1, E3_GEN_DW = 2, E3_GEN_DY = 3 };
+enum { E3_GEN_FORWARD = 0, E3_GEN_DX = 1, E3_GEN_DW = 2, E3_GEN_DY = 3, E3_GEN_GEMM = 4 };
 e3_status e3_generic_plan_size(const e3_desc* desc, int32_t table, size_t* bytes);
 e3_status e3_generic_plan_build(const e3_desc* desc, int32_t table, void* host_plan,
                                 size_t bytes);
 e3_status e3_tp_forward_generic(const e3_desc* desc, int64_t n_rows, const void* plan,
                                 size_t plan_bytes, const void* x, const float* y, const void* w,
                                 void* z, e3_dtype dtype, void* stream);
+/* The same tensor product forward on the fp32 matrix cores (degrees up to 6,
+ * float32 only).  e3j E.1 Eq.10-11 contracted per output block as one dense
+ * product: A_L[M][(P,m1)] = sum_{m2} C_P[M][m1][m2] y[m2] (per row, shared by
+ * the channels) times xt[(P,m1)][q] = w[P][q] x[l1,m1][q], on
+ * v_mfma_f32_16x16x4f32 (exact fp32 products, fp32 accumulation).
+ *   plan: table E3_GEN_GEMM of e3_generic_plan_build for this descriptor,
+ *     copied to device memory (16-byte aligned).
+ *   x [n][dx][C], y [n][dy], w [n][P][C], z [n][dout][C] float32; x and w
+ *     16-byte aligned; C % 16 == 0.
+ * E3_ERR_UNSUPPORTED when C % 16 != 0 or a row's operands do not fit in one
+ * workgroup's LDS (160 KB) even with 16-channel slabs.  Indices read from the
+ * plan are clamped to the descriptor's sizes. */
+e3_status e3_tp_forward_gemm(const e3_desc* desc, int64_t n_rows, const void* plan,
+                             size_t plan_bytes, const float* x, const float* y, const float* w,
+                             float* z, void* stream);
 e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_dx,
                                  size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
                                  const void* plan_dy, size_t dy_bytes, const void* x,

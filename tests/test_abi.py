@@ -240,7 +240,16 @@ def test_generic_plan_table(lib):
     t = np.zeros(nb.value // 4, dtype=np.int32)
     assert lib.e3_generic_plan_build(C.byref(d.c()), 0, t.ctypes.data, nb.value - 4) == -6
     assert lib.e3_generic_plan_build(C.byref(d.c()), 0, t.ctypes.data, nb.value) == 0
-    assert lib.e3_generic_plan_size(C.byref(d.c()), 4, C.byref(nb)) == -1
+    assert lib.e3_generic_plan_size(C.byref(d.c()), 5, C.byref(nb)) == -1
+    # the dense-product plan (table 4): header, one block per output irrep
+    ng = C.c_size_t()
+    assert lib.e3_generic_plan_size(C.byref(d.c()), 4, C.byref(ng)) == 0
+    g = np.zeros(ng.value // 4, dtype=np.int32)
+    assert lib.e3_generic_plan_build(C.byref(d.c()), 4, g.ctypes.data, ng.value) == 0
+    assert g[0] == 0x4D4D4547 and list(g[1:6]) == [5, 25, 25, 25, 42]
+    blocks = g[g[10]:g[10] + 4 * 5].reshape(5, 4)
+    assert list(blocks[:, 1]) == [1, 3, 5, 7, 9] and np.all(blocks[:, 3] % 4 == 0)
+    assert list(blocks[:, 0]) == [0, 1, 4, 9, 16]  # output offsets
     dx = dy = dout = 25
     P, n_contrib, n_rec, rec_off = t[4], t[5], t[6], t[7]
     assert list(t[1:4]) == [dx, dy, dout] and P == api.num_paths(d) == 42
