@@ -45,6 +45,10 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 // host (built from the descriptor); every index read from the plan is
 // clamped to them, so a plan of another descriptor gives wrong values but no
 // access outside the arrays.
+// PRE: 16-byte units per thread loaded one item ahead (12 for plans whose
+// LDS leaves at most two workgroups per CU; 0 keeps the registers low so that
+// small plans run more workgroups per CU).
+template <int PRE>
 __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
   extern __shared__ __align__(16) float gsm[];
   const int* __restrict__ blocks = g.plan + g.off_blocks;
@@ -69,22 +73,46 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
   const int li = lane & 15, kq = lane >> 4;
   const int n_slabs = C / CS, n_tiles = CS / 16;
   const int64_t n_items = g.n_rows * n_slabs;
+  // The slab of x and w is 16-byte units u < U (x rows first): the first
+  // 256 * PRE of them are loaded for the next item into registers while this
+  // item's products run, the rest when the item is staged.
+  const int U = (g.dx + g.P) << lg4;
+  auto unit_src = [&](int u, int64_t row, int c0) {
+    const int r = u >> lg4, c = 4 * (u & ((1 << lg4) - 1));
+    return r < g.dx ? g.x + (row * g.dx + r) * C + c0 + c
+                    : g.w + (row * g.P + (r - g.dx)) * C + c0 + c;
+  };
+  auto unit_dst = [&](int u) {
+    const int r = u >> lg4, c = 4 * (u & ((1 << lg4) - 1));
+    return r < g.dx ? s_x + r * XS + c : s_w + (r - g.dx) * XS + c;
+  };
+  float4v pre[PRE > 0 ? PRE : 1];
+  float ypre = 0.0f;
+  auto prefetch = [&](int64_t item) {
+    const int64_t row = item / n_slabs;
+    const int c0 = int(item - row * n_slabs) * CS;
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) {
+      const int u = threadIdx.x + 256 * j;
+      if (u < U) pre[j] = *reinterpret_cast<const float4v*>(unit_src(u, row, c0));
+    }
+    if (threadIdx.x < g.dy) ypre = g.y[row * g.dy + threadIdx.x];
+  };
+  if (PRE > 0 && blockIdx.x < n_items) prefetch(blockIdx.x);
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int64_t row = item / n_slabs;
     const int c0 = int(item - row * n_slabs) * CS;
     __syncthreads();  // the previous item's LDS reads are done (and s_k is written)
     // stage the slab of x and w and the row's y; clear A
-    for (int i = threadIdx.x; i < (g.dx << lg4); i += 256) {
-      const int r = i >> lg4, c = 4 * (i & ((1 << lg4) - 1));
-      *reinterpret_cast<float4v*>(s_x + r * XS + c) =
-          *reinterpret_cast<const float4v*>(g.x + (row * g.dx + r) * C + c0 + c);
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) {
+      const int u = threadIdx.x + 256 * j;
+      if (u < U) *reinterpret_cast<float4v*>(unit_dst(u)) = pre[j];
     }
-    for (int i = threadIdx.x; i < (g.P << lg4); i += 256) {
-      const int r = i >> lg4, c = 4 * (i & ((1 << lg4) - 1));
-      *reinterpret_cast<float4v*>(s_w + r * XS + c) =
-          *reinterpret_cast<const float4v*>(g.w + (row * g.P + r) * C + c0 + c);
-    }
-    for (int i = threadIdx.x; i < g.dy; i += 256) s_y[i] = g.y[row * g.dy + i];
+    for (int u = threadIdx.x + 256 * PRE; u < U; u += 256)
+      *reinterpret_cast<float4v*>(unit_dst(u)) = *reinterpret_cast<const float4v*>(unit_src(u, row, c0));
+    for (int i = threadIdx.x; i < g.dy; i += 256)
+      s_y[i] = PRE > 0 && i < 256 ? ypre : g.y[row * g.dy + i];
     for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
     __syncthreads();
     // A[k][M] = c1 y[y1] + c2 y[y2]: one independent 16-byte load per entry
@@ -96,6 +124,8 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
       s_a[at] = fmaf(__int_as_float(e.w), s_y[y2], __int_as_float(e.z) * s_y[y1]);
     }
     __syncthreads();
+    // the next item's operands load while this item's products run
+    if (PRE > 0 && item + gridDim.x < n_items) prefetch(item + gridDim.x);
     int abase = 0;
     for (int b = 0; b < g.n_blocks; ++b) {
       const int oo = blocks[4 * b], rows = min(max(blocks[4 * b + 1], 1), 16);
@@ -152,21 +182,27 @@ size_t tp_gemm_lds_bytes(const TpGemmArgs& a) {
   return size_t(a.a_floats + a.dx * XS + (a.P + 1) * XS + a.dy + a.n_klist) * 4;
 }
 
-hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s) {
-  if (a.n_rows <= 0) return hipSuccess;
+template <int PRE>
+hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
   static bool attr = false;  // the attribute is per function: set once
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tp_gemm),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tp_gemm<PRE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int64_t items = a.n_rows * (a.C / a.CS);
+  const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
+  hipLaunchKernelGGL(k_tp_gemm<PRE>, dim3(grid), dim3(256), a.lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
   if (a.lds_bytes > 160 * 1024) return hipErrorInvalidValue;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.lds_bytes, 1)));
-  const int grid = int(std::min<int64_t>(items, int64_t(256) * std::min(per_cu, 8)));
-  hipLaunchKernelGGL(k_tp_gemm, dim3(grid), dim3(256), a.lds_bytes, s, a);
-  return hipGetLastError();
+  return per_cu <= 2 ? launch_tp_gemm_pre<12>(a, per_cu, s)
+                     : launch_tp_gemm_pre<0>(a, std::min(per_cu, 8), s);
 }
 
 }  // namespace e3k
