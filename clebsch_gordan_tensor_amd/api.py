@@ -49,7 +49,7 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_conv_double_backward", "e3_radial_mlp", "e3_conv_forward_radial",
            "e3_radial_mlp_backward_workspace_size", "e3_radial_mlp_backward",
            "e3_generic_plan_size", "e3_generic_plan_build", "e3_tp_forward_generic",
-           "e3_tp_forward_gemm",
+           "e3_tp_forward_gemm", "e3_conv_forward_gemm",
            "e3_tp_backward_generic", "e3_conv_forward_generic", "e3_conv_backward_generic",
            "e3_conv_double_backward_generic", "e3_last_error"]
 E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY, E3_GEN_GEMM = 0, 1, 2, 3, 4
@@ -622,6 +622,26 @@ def tp_forward_gemm(desc: Desc, x, y, w, out=None, stream=None):
     plan = generic_plan(desc, x.device, E3_GEN_GEMM)
     _check(lib().e3_tp_forward_gemm(C.byref(desc.c()), B, _ptr(plan), plan.numel() * 4, _ptr(x),
                                     _ptr(y), _ptr(w), _ptr(out), _stream(stream)))
+    return out
+
+
+def conv_forward_gemm(desc: Desc, rowptr, sender, Y, x, w, out=None, stream=None):
+    """m = the convolution (as conv_forward_generic with E3_Y_GIVEN) as dense
+    products per receiver and output block on the fp32 matrix cores; Y is the
+    edges' harmonics [E][dy]."""
+    import torch
+    N, E = rowptr.numel() - 1, sender.numel()
+    P = num_paths(desc)
+    _need(x, "x", shape=(N, desc.dx, desc.channels), dtype=torch.float32)
+    _need(Y, "Y", shape=(E, desc.dy), dtype=torch.float32)
+    _need(w, "w", shape=(E, P, desc.channels), dtype=torch.float32)
+    if out is None:
+        out = torch.empty((N, desc.dout, desc.channels), device=x.device, dtype=torch.float32)
+    _need(out, "out", shape=(N, desc.dout, desc.channels), dtype=torch.float32)
+    plan = generic_plan(desc, x.device, E3_GEN_GEMM)
+    _check(lib().e3_conv_forward_gemm(C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender),
+                                      _ptr(plan), plan.numel() * 4, _ptr(Y), _ptr(x), _ptr(w),
+                                      _ptr(out), _stream(stream)))
     return out
 
 

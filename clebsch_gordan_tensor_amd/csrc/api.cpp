@@ -1205,6 +1205,58 @@ e3_status e3_tp_forward_gemm(const e3_desc* desc, int64_t n_rows, const void* pl
   return hip_status(e3k::launch_tp_gemm(a, hipStream_t(stream)), "tp_forward_gemm");
 }
 
+e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                               const int32_t* rowptr, const int32_t* sender, const void* plan,
+                               size_t plan_bytes, const float* Y, const float* x, const float* w,
+                               float* m, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if (!(desc->flags & E3_Y_GIVEN))
+    return fail(E3_ERR_INVALID_ARG, "the dense-product convolution takes given harmonics (E3_Y_GIVEN)");
+  if (p.per_path) return fail(E3_ERR_UNSUPPORTED, "the dense-product convolution has collapsed outputs");
+  e3k::ConvGemmArgs a{};
+  size_t need = 0;
+  if ((s = gemm_dims(desc, a.t, need)) != E3_OK) return s;
+  if (a.t.n_blocks > 8) return fail(E3_ERR_UNSUPPORTED, "more than 8 output irreps");
+  if (p.C % 16) return fail(E3_ERR_UNSUPPORTED, "the dense-product kernel needs C % 16 == 0");
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes == 0) return ok();
+  if (!rowptr || !x || !m) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (n_edges > 0 && (!sender || !Y || !w)) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!plan || plan_bytes < need)
+    return fail(E3_ERR_INVALID_ARG, "plan needs " + std::to_string(need) +
+                                        " bytes (E3_GEN_GEMM table of this descriptor)");
+  if (!aligned16(x) || (n_edges > 0 && !aligned16(w)) || !aligned16(plan))
+    return fail(E3_ERR_ALIGNMENT, "x, w and the plan must be 16-byte aligned");
+  a.t.C = p.C;
+  a.t.CS = 0;
+  for (size_t cap : {size_t(80) * 1024, size_t(160) * 1024}) {
+    for (int cs : {128, 64, 32, 16}) {
+      if (cs > p.C || p.C % cs) continue;
+      a.t.CS = cs;
+      if (e3k::tp_gemm_lds_bytes(a.t) <= cap) break;
+      a.t.CS = 0;
+    }
+    if (a.t.CS) break;
+  }
+  if (!a.t.CS) return fail(E3_ERR_UNSUPPORTED, "the dense-product plan does not fit in LDS");
+  const int XS = e3k::gemm_row_stride(a.t.CS);
+  if ((a.t.P + 1) * XS > 65535 || a.t.dx * XS > 65535)
+    return fail(E3_ERR_UNSUPPORTED, "too many x components or paths for the dense-product kernel");
+  a.t.lds_bytes = e3k::tp_gemm_lds_bytes(a.t);
+  a.t.plan = static_cast<const int*>(plan);
+  a.t.x = x;
+  a.t.y = Y;
+  a.t.w = w;
+  a.t.z = m;
+  a.n_nodes = n_nodes;
+  a.rowptr = rowptr;
+  a.sender = sender;
+  a.m = m;
+  return hip_status(e3k::launch_conv_gemm(a, hipStream_t(stream)), "conv_forward_gemm");
+}
+
 e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_dx,
                                  size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
                                  const void* plan_dy, size_t dy_bytes, const void* x,

@@ -175,6 +175,159 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
   }
 }
 
+// The convolution forward (e3j A.3 Eq.7 with E.1 Eq.10-12) in the same
+// form: for receiver b, out[b][L] = sum over its in-edges e of A_{e,L} xt_e
+// with xt_e[(P,m1)][q] = w[e][P][q] x[sender e][l1,m1][q].  One workgroup per
+// (receiver, channel slab); per edge the slab of x[sender] and w[e] and Y[e]
+// are staged and A_e built as for one tensor-product row, and every output
+// block's tiles accumulate in registers over the edge list (at most 8 blocks:
+// collapsed outputs), so m is written once per receiver in edge order.
+// PRE as above, for the next edge of the same receiver (built with PRE = 0).
+constexpr int kConvGemmBlocks = 8;
+
+template <int PRE, int NU>
+__global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
+  extern __shared__ __align__(16) float gsm[];
+  const TpGemmArgs& g = cg.t;
+  const int* __restrict__ blocks = g.plan + g.off_blocks;
+  const int* __restrict__ klist = g.plan + g.off_klist;
+  const int4* __restrict__ groups = reinterpret_cast<const int4*>(g.plan + g.off_groups);
+  const int CS = g.CS, C = g.C, XS = gemm_row_stride(CS);
+  const int lg4 = __builtin_ctz(CS / 4);
+  float* s_a = gsm;
+  float* s_x = s_a + g.a_floats;
+  float* s_w = s_x + g.dx * XS;
+  float* s_y = s_w + (g.P + 1) * XS;
+  int* s_k = reinterpret_cast<int*>(s_y + g.dy);
+  for (int i = threadIdx.x; i < g.n_klist; i += 256) {
+    const int ent = klist[i];
+    const int p = ent < 0 ? g.P : min(ent >> 16, g.P - 1);
+    const int xi = ent < 0 ? 0 : min(ent & 0xFFFF, g.dx - 1);
+    s_k[i] = p * XS | (xi * XS) << 16;
+  }
+  for (int i = threadIdx.x; i < XS; i += 256) s_w[g.P * XS + i] = 0.0f;
+  // the blocks, read once
+  int b_oo[kConvGemmBlocks], b_rows[kConvGemmBlocks], b_kb[kConvGemmBlocks], b_K[kConvGemmBlocks],
+      b_ab[kConvGemmBlocks];
+  {
+    int abase = 0;
+#pragma unroll
+    for (int b = 0; b < kConvGemmBlocks; ++b) {
+      const bool on = b < g.n_blocks;
+      b_oo[b] = on ? blocks[4 * b] : 0;
+      b_rows[b] = on ? min(max(blocks[4 * b + 1], 1), 16) : 1;
+      b_kb[b] = on ? min(max(blocks[4 * b + 2], 0), g.n_klist) : 0;
+      b_K[b] = on ? min(max(blocks[4 * b + 3], 0), g.n_klist - b_kb[b]) & ~3 : 0;
+      if (abase + b_rows[b] * b_K[b] > g.a_floats) b_K[b] = 0;
+      b_ab[b] = abase;
+      abase += b_rows[b] * b_K[b];
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, kq = lane >> 4;
+  const int n_slabs = C / CS, n_tiles = CS / 16;
+  const int nu = wave < n_tiles ? min(NU, (n_tiles - wave + 3) / 4) : 0;  // tiles wave, wave + 4
+  const int64_t n_items = int64_t(cg.n_nodes) * n_slabs;
+  const int U = (g.dx + g.P) << lg4;
+  auto unit_dst = [&](int u) {
+    const int r = u >> lg4, c = 4 * (u & ((1 << lg4) - 1));
+    return r < g.dx ? s_x + r * XS + c : s_w + (r - g.dx) * XS + c;
+  };
+  auto unit_src = [&](int u, int e, int a, int c0) {
+    const int r = u >> lg4, c = 4 * (u & ((1 << lg4) - 1));
+    return r < g.dx ? g.x + (int64_t(a) * g.dx + r) * C + c0 + c
+                    : g.w + (int64_t(e) * g.P + (r - g.dx)) * C + c0 + c;
+  };
+  float4v pre[PRE > 0 ? PRE : 1];
+  float ypre = 0.0f;
+  auto prefetch = [&](int e, int c0) {
+    const int a = max(cg.sender[e], 0);
+#pragma unroll
+    for (int j = 0; j < PRE; ++j) {
+      const int u = threadIdx.x + 256 * j;
+      if (u < U) pre[j] = *reinterpret_cast<const float4v*>(unit_src(u, e, a, c0));
+    }
+    if (threadIdx.x < g.dy) ypre = g.y[int64_t(e) * g.dy + threadIdx.x];
+  };
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int node = int(item / n_slabs);
+    const int c0 = int(item - int64_t(node) * n_slabs) * CS;
+    const int e_lo = cg.rowptr[node], e_hi = cg.rowptr[node + 1];
+    float4v D[kConvGemmBlocks][NU];
+#pragma unroll
+    for (int b = 0; b < kConvGemmBlocks; ++b)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) D[b][u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    if (PRE > 0 && e_lo < e_hi) prefetch(e_lo, c0);
+    for (int e = e_lo; e < e_hi; ++e) {
+      const int a = cg.sender[e];
+      if (a < 0) {  // padding edge (the same for the whole workgroup): nothing to add
+        if (PRE > 0 && e + 1 < e_hi) prefetch(e + 1, c0);
+        continue;
+      }
+      __syncthreads();  // the previous edge's LDS reads are done (and s_k is written)
+#pragma unroll
+      for (int j = 0; j < PRE; ++j) {
+        const int u = threadIdx.x + 256 * j;
+        if (u < U) *reinterpret_cast<float4v*>(unit_dst(u)) = pre[j];
+      }
+      for (int u = threadIdx.x + 256 * PRE; u < U; u += 256)
+        *reinterpret_cast<float4v*>(unit_dst(u)) = *reinterpret_cast<const float4v*>(unit_src(u, e, a, c0));
+      for (int i = threadIdx.x; i < g.dy; i += 256)
+        s_y[i] = PRE > 0 && i < 256 ? ypre : g.y[int64_t(e) * g.dy + i];
+      for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
+      __syncthreads();
+#pragma unroll 4
+      for (int q = threadIdx.x; q < g.n_groups; q += 256) {
+        const int4 en = groups[q];
+        const int at = min(max(en.x, 0), g.a_floats - 1);
+        const int y1 = min(en.y & 0xFFFF, g.dy - 1), y2 = min((en.y >> 16) & 0xFFFF, g.dy - 1);
+        s_a[at] = fmaf(__int_as_float(en.w), s_y[y2], __int_as_float(en.z) * s_y[y1]);
+      }
+      __syncthreads();
+      if (PRE > 0 && e + 1 < e_hi) prefetch(e + 1, c0);
+      const float* sw = s_w + 16 * wave + li;
+      const float* sx = s_x + 16 * wave + li;
+#pragma unroll
+      for (int b = 0; b < kConvGemmBlocks; ++b) {
+        const int rows = b_rows[b], K = b_K[b];
+        const bool aok = li < rows;
+        const float* ap = s_a + b_ab[b] + kq * rows + min(li, rows - 1);
+        const int* kp = s_k + b_kb[b] + kq;
+#pragma unroll 4
+        for (int k0 = 0; k0 < K; k0 += 4) {
+          const float av = ap[k0 * rows];
+          const float af = aok ? av : 0.0f;
+          const int ent = kp[k0];
+          const int wo = ent & 0xFFFF, xo = int(unsigned(ent) >> 16);
+#pragma unroll
+          for (int u = 0; u < NU; ++u)
+            if (u < nu)
+              D[b][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(af, sw[wo + 64 * u] * sx[xo + 64 * u],
+                                                            D[b][u], 0, 0, 0);
+        }
+      }
+    }
+    // D[i][j] in register i % 4 of lane j + 16 (i / 4): row 4 kq + r, channel li
+#pragma unroll
+    for (int b = 0; b < kConvGemmBlocks; ++b) {
+      if (b < g.n_blocks) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          if (u < nu) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = 4 * kq + r, o = b_oo[b] + i;
+              if (i < b_rows[b] && o >= 0 && o < g.dout)
+                cg.m[(int64_t(node) * g.dout + o) * C + c0 + 16 * (wave + 4 * u) + li] = D[b][u][r];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 size_t tp_gemm_lds_bytes(const TpGemmArgs& a) {
@@ -195,6 +348,33 @@ hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
   hipLaunchKernelGGL(k_tp_gemm<PRE>, dim3(grid), dim3(256), a.lds_bytes, s, a);
   return hipGetLastError();
+}
+
+template <int PRE, int NU>
+hipError_t launch_conv_gemm_pre(const ConvGemmArgs& a, int per_cu, hipStream_t s) {
+  static bool attr = false;  // the attribute is per function: set once
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int64_t items = int64_t(a.n_nodes) * (a.t.C / a.t.CS);
+  const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
+  hipLaunchKernelGGL((k_conv_gemm<PRE, NU>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
+  if (a.n_nodes <= 0) return hipSuccess;
+  if (a.t.lds_bytes > 160 * 1024 || a.t.n_blocks > kConvGemmBlocks || a.t.CS > 128)
+    return hipErrorInvalidValue;
+  const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
+  // tiles per wavefront: 16-channel tiles of the slab over four wavefronts.
+  // The next edge's operands are not prefetched here: with the per-block
+  // accumulators the registers would leave one wavefront per SIMD.
+  if (a.t.CS > 64) return launch_conv_gemm_pre<0, 2>(a, std::min(per_cu, 8), s);
+  return launch_conv_gemm_pre<0, 1>(a, std::min(per_cu, 8), s);
 }
 
 hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s) {

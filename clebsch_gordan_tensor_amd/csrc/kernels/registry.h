@@ -218,6 +218,16 @@ struct TpGemmArgs {
 __host__ __device__ constexpr int gemm_row_stride(int CS) { return CS / 32 * 32 + 16 + (CS % 32 ? 32 : 0); }
 size_t tp_gemm_lds_bytes(const TpGemmArgs& a);
 hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s);
+// The convolution forward in the same form (t.n_rows unused; t.y = Y [E][dy];
+// t.x = node features, t.w = edge weights; collapsed outputs, <= 8 blocks).
+struct ConvGemmArgs {
+  TpGemmArgs t;
+  int n_nodes;
+  const int* rowptr;
+  const int* sender;
+  float* m;
+};
+hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s);
 hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
                                  float* dvec, hipStream_t s);
 hipError_t launch_edge_grad_to_nodes(int n_nodes, int n_edges, const int* rowptr,

@@ -94,3 +94,65 @@ def test_gemm_tp_full_size_sampled(gpu):
     rows = np.sort(np.random.default_rng(5).choice(32768, 60, replace=False))
     ref = O.tp_forward(od, x, y, w, rows=rows)
     assert_close(host(z)[rows], ref, TOL_F32, "gemm tp L=6 sampled")
+
+
+# --------------------------------------------------------- convolution
+
+def _conv_problem(L, C, n, seed, pad=0, skew=False):
+    from clebsch_gordan_tensor_amd import api
+    from clebsch_gordan_tensor_amd import synth as S
+    xi = oi = S.degree_irreps(L, skew)
+    yi = S.sh_irreps(L)
+    rng = np.random.default_rng(seed)
+    g = S.random_graph(n, 7.0, 3.5, seed)
+    if pad:
+        from tests.test_oracle_conv import with_padding
+        g = with_padding(g, pad, seed)
+    d = api.Desc(xi, yi, oi, C, api.E3_Y_GIVEN)
+    od = O.Desc(xi, yi, oi, C)
+    P = api.num_paths(d)
+    x = rng.standard_normal((n, d.dx, C)).astype(np.float32)
+    w = rng.standard_normal((g.n_edges, P, C)).astype(np.float32)
+    Y = O.sh(L, g.evec.astype(np.float64)).astype(np.float32)
+    return d, od, g, x, w, Y
+
+
+@pytest.mark.parametrize("L,C,skew", [(1, 64, False), (3, 128, False), (4, 64, False),
+                                      (6, 128, False), (6, 48, True)])
+def test_gemm_conv_matches_oracle(gpu, L, C, skew):
+    d, od, g, x, w, Y = _conv_problem(L, C, 40 if L >= 5 else 64, 600 + L, skew=skew)
+    rowptr, sender = dev(g.rowptr), dev(g.sender)
+    m = gpu.conv_forward_gemm(d, rowptr, sender, dev(Y), dev(x), dev(w))
+    m2 = gpu.conv_forward_gemm(d, rowptr, sender, dev(Y), dev(x), dev(w))
+    torch.cuda.synchronize()
+    assert torch.equal(m.view(torch.int32), m2.view(torch.int32))
+    ref = O.conv_forward(od, g.rowptr, g.sender, x, w, Y=Y)
+    assert_close(host(m), ref, TOL_F32, f"gemm conv L={L} C={C}")
+
+
+def test_gemm_conv_padding_and_empty_rows(gpu):
+    # padding edges (sender < 0) add nothing; receivers without edges get 0
+    d, od, g, x, w, Y = _conv_problem(3, 64, 50, 620, pad=7)
+    rowptr, sender = dev(g.rowptr), dev(g.sender)
+    m = host(gpu.conv_forward_gemm(d, rowptr, sender, dev(Y), dev(x), dev(w)))
+    ref = O.conv_forward(od, g.rowptr, g.sender, x, w, Y=Y)
+    assert_close(m, ref, TOL_F32, "gemm conv padding")
+    empty = np.flatnonzero(np.diff(g.rowptr) == 0)
+    assert np.all(m[empty] == 0)
+
+
+def test_gemm_conv_equals_table_kernel(gpu):
+    d, od, g, x, w, Y = _conv_problem(5, 128, 60, 630)
+    rowptr, sender = dev(g.rowptr), dev(g.sender)
+    a = gpu.conv_forward_gemm(d, rowptr, sender, dev(Y), dev(x), dev(w))
+    b = gpu.conv_forward_generic(d, rowptr, sender, dev(Y), dev(x), dev(w))
+    torch.cuda.synchronize()
+    assert_close(host(a), host(b).astype(np.float64), 2 * TOL_F32, "gemm conv vs table kernel")
+
+
+def test_gemm_conv_needs_given_harmonics(gpu):
+    from clebsch_gordan_tensor_amd import api
+    d, od, g, x, w, Y = _conv_problem(2, 64, 20, 640)
+    d2 = api.Desc(d.x, d.y, d.out, 64)
+    with pytest.raises(api.E3Error):
+        gpu.conv_forward_gemm(d2, dev(g.rowptr), dev(g.sender), dev(Y), dev(x), dev(w))
