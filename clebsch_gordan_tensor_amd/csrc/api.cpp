@@ -1034,17 +1034,16 @@ e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemm
   d.P = p.P;
   d.n_klist = int(klist.size());
   d.n_groups = n_groups;
-  d.n_recs = 0;
   d.a_floats = std::max(abase, 1);
   d.off_blocks = e3k::kGemmHeader;
   d.off_klist = d.off_blocks + 4 * nb;
   d.off_groups = (d.off_klist + d.n_klist + 3) / 4 * 4;  // 16-byte entries
-  d.off_recs = d.off_groups + int(groups.size());
-  out.assign(size_t(d.off_recs), 0);
+  d.plan_words = d.off_groups + int(groups.size());
+  out.assign(size_t(d.plan_words), 0);
   const int32_t head[14] = {e3k::kGemmMagic, nb,         p.dx,         p.dy,
                             p.dout,          p.P,        d.n_klist,    n_groups,
-                            d.n_recs,        d.a_floats, d.off_blocks, d.off_klist,
-                            d.off_groups,    d.off_recs};
+                            0,               d.a_floats, d.off_blocks, d.off_klist,
+                            d.off_groups,    d.plan_words};
   std::copy(head, head + 14, out.begin());
   for (int b = 0; b < nb; ++b) {
     out[d.off_blocks + 4 * b] = b_oo[b];

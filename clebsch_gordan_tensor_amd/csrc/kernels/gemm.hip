@@ -16,7 +16,7 @@
 //
 // Plan (host-built, see the GEMM table of the library):
 //   header kGemmHeader words: magic, n_blocks, dx, dy, dout, P, n_klist,
-//     n_groups, 0 (unused), a_floats, off_blocks, off_klist, off_groups, end
+//     n_groups, 0, a_floats, off_blocks, off_klist, off_groups, plan words
 //   blocks [n_blocks][4]: output offset, rows (2L+1), K-list start, K (x4)
 //   klist  [n_klist]: (P << 16) | x component, or -1 for a padding column
 //   groups [n_groups][4]: A index (block base + M * K + k), the two y

@@ -205,8 +205,8 @@ constexpr int kGemmMagic = 0x4D4D4547;
 struct TpGemmArgs {
   int64_t n_rows;
   int C, CS;  // channels; channel slab per workgroup (C % CS == 0, CS % 16 == 0)
-  int n_blocks, dx, dy, dout, P, n_klist, n_groups, n_recs, a_floats;
-  int off_blocks, off_klist, off_groups, off_recs;  // word offsets in plan
+  int n_blocks, dx, dy, dout, P, n_klist, n_groups, a_floats;
+  int off_blocks, off_klist, off_groups, plan_words;  // word offsets in plan; its length
   const int* plan;
   const float* x;
   const float* y;
