@@ -1229,9 +1229,11 @@ e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_e
   if (!aligned16(x) || (n_edges > 0 && !aligned16(w)) || !aligned16(plan))
     return fail(E3_ERR_ALIGNMENT, "x, w and the plan must be 16-byte aligned");
   a.t.C = p.C;
+  // slabs of at most 64 channels (one tile per wavefront): the per-block
+  // accumulators of two tiles would leave one wavefront per SIMD
   a.t.CS = 0;
   for (size_t cap : {size_t(80) * 1024, size_t(160) * 1024}) {
-    for (int cs : {128, 64, 32, 16}) {
+    for (int cs : {64, 32, 16}) {
       if (cs > p.C || p.C % cs) continue;
       a.t.CS = cs;
       if (e3k::tp_gemm_lds_bytes(a.t) <= cap) break;

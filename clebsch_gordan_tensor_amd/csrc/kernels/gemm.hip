@@ -38,17 +38,63 @@ namespace {
 
 typedef float float4v __attribute__((ext_vector_type(4)));
 
+// K steps [0, K) of one output block for NU tiles: D[u] += A[k][M] xt[k][c].
+// Four steps per batch, all their LDS reads issued before the products (the
+// w and x reads depend on the K-list read, so one step alone waits twice);
+// BATCH = false keeps one step at a time (fewer registers).
+template <int NU, bool BATCH = true>
+__device__ __forceinline__ void gemm_ksteps(float4v (&D)[NU], const float* ap, const int* kp,
+                                            int rows, bool aok, int K, const float* sw,
+                                            const float* sx) {
+  int k0 = 0;
+  for (; BATCH && k0 + 16 <= K; k0 += 16) {
+    int ent[4];
+    float av[4], wv[4][NU], xv[4][NU];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ent[j] = kp[k0 + 4 * j];
+      av[j] = ap[(k0 + 4 * j) * rows];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int wo = ent[j] & 0xFFFF, xo = int(unsigned(ent[j]) >> 16);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        wv[j][u] = sw[wo + 64 * u];
+        xv[j][u] = sx[xo + 64 * u];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = aok ? av[j] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        D[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, wv[j][u] * xv[j][u], D[u], 0, 0, 0);
+    }
+  }
+  for (; k0 < K; k0 += 4) {
+    const float av = ap[k0 * rows];
+    const float a = aok ? av : 0.0f;
+    const int ent = kp[k0];
+    const int wo = ent & 0xFFFF, xo = int(unsigned(ent) >> 16);
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      D[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sw[wo + 64 * u] * sx[xo + 64 * u], D[u], 0,
+                                                  0, 0);
+  }
+}
+
 // One workgroup (four wavefronts) per (row, slab of CS channels), rows in a
 // grid-stride sequence.  LDS: A for every block (a_floats), the slab's x
 // [dx][CS] and w [P][CS], the row's y and the K list.  A wavefront takes the
-// 16-channel tiles wave, wave + 4, ... of the slab.  The sizes come from the
+// NU 16-channel tiles wave, wave + 4 of the slab.  The sizes come from the
 // host (built from the descriptor); every index read from the plan is
 // clamped to them, so a plan of another descriptor gives wrong values but no
 // access outside the arrays.
 // PRE: 16-byte units per thread loaded one item ahead (12 for plans whose
 // LDS leaves at most two workgroups per CU; 0 keeps the registers low so that
 // small plans run more workgroups per CU).
-template <int PRE>
+template <int PRE, int NU>
 __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
   extern __shared__ __align__(16) float gsm[];
   const int* __restrict__ blocks = g.plan + g.off_blocks;
@@ -69,9 +115,11 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
     s_k[i] = p * XS | (xi * XS) << 16;
   }
   for (int i = threadIdx.x; i < XS; i += 256) s_w[g.P * XS + i] = 0.0f;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave-uniform (a scalar), so the tile tests below are scalar branches
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, kq = lane >> 4;
   const int n_slabs = C / CS, n_tiles = CS / 16;
+  const bool active = wave < n_tiles;  // tiles wave + 4u, u < NU (n_tiles = 4 NU or fewer than 4)
   const int64_t n_items = g.n_rows * n_slabs;
   // The slab of x and w is 16-byte units u < U (x rows first): the first
   // 256 * PRE of them are loaded for the next item into registers while this
@@ -137,38 +185,22 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
       const bool aok = li < rows;
       const float* ap = s_a + abase + kq * rows + min(li, rows - 1);
       const int* kp = s_k + kb + kq;
-      for (int t0 = wave; t0 < n_tiles; t0 += 16) {
-        // up to four tiles of this wavefront at a time: t0, t0 + 4, ...
-        const int nu = min(4, (n_tiles - t0 + 3) / 4);
-        float4v D[4];
+      if (active) {
+        float4v D[NU];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) D[u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-        const float* sw = s_w + 16 * t0 + li;
-        const float* sx = s_x + 16 * t0 + li;
-#pragma unroll 4
-        for (int k0 = 0; k0 < K; k0 += 4) {
-          const float av = ap[k0 * rows];
-          const float a = aok ? av : 0.0f;
-          const int ent = kp[k0];
-          const int wo = ent & 0xFFFF, xo = int(unsigned(ent) >> 16);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (u < nu) D[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                  a, sw[wo + 64 * u] * sx[xo + 64 * u], D[u], 0, 0, 0);
-          }
-        }
+        for (int u = 0; u < NU; ++u) D[u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+        const float* sw = s_w + 16 * wave + li;
+        const float* sx = s_x + 16 * wave + li;
+        gemm_ksteps<NU>(D, ap, kp, rows, aok, K, sw, sx);
         // D[i][j] in register i % 4 of lane j + 16 (i / 4): row 4 kq + r, channel li
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (u < nu) {
+        for (int u = 0; u < NU; ++u)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = 4 * kq + r, o = oo + i;
-              if (i < rows && o >= 0 && o < g.dout)
-                g.z[(row * g.dout + o) * C + c0 + 16 * (t0 + 4 * u) + li] = D[u][r];
-            }
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * kq + r, o = oo + i;
+            if (i < rows && o >= 0 && o < g.dout)
+              g.z[(row * g.dout + o) * C + c0 + 16 * (wave + 4 * u) + li] = D[u][r];
           }
-        }
       }
       abase += rows * K;
     }
@@ -185,7 +217,7 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
 // PRE as above, for the next edge of the same receiver (built with PRE = 0).
 constexpr int kConvGemmBlocks = 8;
 
-template <int PRE, int NU>
+template <int PRE, int NU, bool BATCH>
 __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
   extern __shared__ __align__(16) float gsm[];
   const TpGemmArgs& g = cg.t;
@@ -223,10 +255,10 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
       abase += b_rows[b] * b_K[b];
     }
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, kq = lane >> 4;
   const int n_slabs = C / CS, n_tiles = CS / 16;
-  const int nu = wave < n_tiles ? min(NU, (n_tiles - wave + 3) / 4) : 0;  // tiles wave, wave + 4
+  const bool active = wave < n_tiles;  // tiles wave + 4u, u < NU
   const int64_t n_items = int64_t(cg.n_nodes) * n_slabs;
   const int U = (g.dx + g.P) << lg4;
   auto unit_dst = [&](int u) {
@@ -286,6 +318,7 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
       }
       __syncthreads();
       if (PRE > 0 && e + 1 < e_hi) prefetch(e + 1, c0);
+      if (!active) continue;  // the same for the whole wavefront
       const float* sw = s_w + 16 * wave + li;
       const float* sx = s_x + 16 * wave + li;
 #pragma unroll
@@ -294,27 +327,16 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
         const bool aok = li < rows;
         const float* ap = s_a + b_ab[b] + kq * rows + min(li, rows - 1);
         const int* kp = s_k + b_kb[b] + kq;
-#pragma unroll 4
-        for (int k0 = 0; k0 < K; k0 += 4) {
-          const float av = ap[k0 * rows];
-          const float af = aok ? av : 0.0f;
-          const int ent = kp[k0];
-          const int wo = ent & 0xFFFF, xo = int(unsigned(ent) >> 16);
-#pragma unroll
-          for (int u = 0; u < NU; ++u)
-            if (u < nu)
-              D[b][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(af, sw[wo + 64 * u] * sx[xo + 64 * u],
-                                                            D[b][u], 0, 0, 0);
-        }
+        gemm_ksteps<NU, BATCH>(D[b], ap, kp, rows, aok, K, sw, sx);
       }
     }
     // D[i][j] in register i % 4 of lane j + 16 (i / 4): row 4 kq + r, channel li
 #pragma unroll
     for (int b = 0; b < kConvGemmBlocks; ++b) {
-      if (b < g.n_blocks) {
+      if (active && b < g.n_blocks) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-          if (u < nu) {
+          {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int i = 4 * kq + r, o = b_oo[b] + i;
@@ -335,33 +357,33 @@ size_t tp_gemm_lds_bytes(const TpGemmArgs& a) {
   return size_t(a.a_floats + a.dx * XS + (a.P + 1) * XS + a.dy + a.n_klist) * 4;
 }
 
-template <int PRE>
+template <int PRE, int NU>
 hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
   static bool attr = false;  // the attribute is per function: set once
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tp_gemm<PRE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tp_gemm<PRE, NU>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int64_t items = a.n_rows * (a.C / a.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
-  hipLaunchKernelGGL(k_tp_gemm<PRE>, dim3(grid), dim3(256), a.lds_bytes, s, a);
+  hipLaunchKernelGGL((k_tp_gemm<PRE, NU>), dim3(grid), dim3(256), a.lds_bytes, s, a);
   return hipGetLastError();
 }
 
-template <int PRE, int NU>
+template <int PRE, int NU, bool BATCH>
 hipError_t launch_conv_gemm_pre(const ConvGemmArgs& a, int per_cu, hipStream_t s) {
   static bool attr = false;  // the attribute is per function: set once
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int64_t items = int64_t(a.n_nodes) * (a.t.C / a.t.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
-  hipLaunchKernelGGL((k_conv_gemm<PRE, NU>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
+  hipLaunchKernelGGL((k_conv_gemm<PRE, NU, BATCH>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
   return hipGetLastError();
 }
 
@@ -370,19 +392,27 @@ hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
   if (a.t.lds_bytes > 160 * 1024 || a.t.n_blocks > kConvGemmBlocks || a.t.CS > 128)
     return hipErrorInvalidValue;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
-  // tiles per wavefront: 16-channel tiles of the slab over four wavefronts.
-  // The next edge's operands are not prefetched here: with the per-block
+  // one 16-channel tile per wavefront (slabs of at most 64 channels).  The
+  // next edge's operands are not prefetched here: with the per-block
   // accumulators the registers would leave one wavefront per SIMD.
-  if (a.t.CS > 64) return launch_conv_gemm_pre<0, 2>(a, std::min(per_cu, 8), s);
-  return launch_conv_gemm_pre<0, 1>(a, std::min(per_cu, 8), s);
+  // Batched K steps for plans whose LDS leaves at most two workgroups per CU;
+  // smaller plans keep the registers for a third wavefront per SIMD.
+  if (a.t.CS > 64) return hipErrorInvalidValue;
+  return per_cu <= 2 ? launch_conv_gemm_pre<0, 1, true>(a, per_cu, s)
+                     : launch_conv_gemm_pre<0, 1, false>(a, std::min(per_cu, 8), s);
 }
 
 hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   if (a.lds_bytes > 160 * 1024) return hipErrorInvalidValue;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.lds_bytes, 1)));
-  return per_cu <= 2 ? launch_tp_gemm_pre<12>(a, per_cu, s)
-                     : launch_tp_gemm_pre<0>(a, std::min(per_cu, 8), s);
+  // tiles per wavefront: a 128-channel slab has 8 tiles (2 per wavefront),
+  // smaller slabs at most 4 (1 per wavefront, some wavefronts idle below 64)
+  if (a.CS > 64)
+    return per_cu <= 2 ? launch_tp_gemm_pre<12, 2>(a, per_cu, s)
+                       : launch_tp_gemm_pre<0, 2>(a, std::min(per_cu, 8), s);
+  return per_cu <= 2 ? launch_tp_gemm_pre<12, 1>(a, per_cu, s)
+                     : launch_tp_gemm_pre<0, 1>(a, std::min(per_cu, 8), s);
 }
 
 }  // namespace e3k
