@@ -625,15 +625,17 @@ def tp_forward_gemm(desc: Desc, x, y, w, out=None, stream=None):
     return out
 
 
-def conv_forward_gemm(desc: Desc, rowptr, sender, Y, x, w, out=None, stream=None):
-    """m = the convolution (as conv_forward_generic with E3_Y_GIVEN) as dense
-    products per receiver and output block on the fp32 matrix cores; Y is the
-    edges' harmonics [E][dy]."""
+def conv_forward_gemm(desc: Desc, rowptr, sender, edge_vec_or_Y, x, w, out=None, stream=None):
+    """m = the convolution (as conv_forward_generic) as dense products per
+    receiver and output block on the fp32 matrix cores; edge_vec_or_Y is the
+    edge vectors [E][3] or, with E3_Y_GIVEN, the harmonics [E][dy]."""
     import torch
     N, E = rowptr.numel() - 1, sender.numel()
     P = num_paths(desc)
+    Y = edge_vec_or_Y
     _need(x, "x", shape=(N, desc.dx, desc.channels), dtype=torch.float32)
-    _need(Y, "Y", shape=(E, desc.dy), dtype=torch.float32)
+    _need(Y, "edge_vec_or_Y", shape=(E, desc.dy if desc.flags & E3_Y_GIVEN else 3),
+          dtype=torch.float32)
     _need(w, "w", shape=(E, P, desc.channels), dtype=torch.float32)
     if out is None:
         out = torch.empty((N, desc.dout, desc.channels), device=x.device, dtype=torch.float32)

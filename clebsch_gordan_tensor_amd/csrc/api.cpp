@@ -1206,18 +1206,31 @@ e3_status e3_tp_forward_gemm(const e3_desc* desc, int64_t n_rows, const void* pl
 
 e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
                                const int32_t* rowptr, const int32_t* sender, const void* plan,
-                               size_t plan_bytes, const float* Y, const float* x, const float* w,
-                               float* m, void* stream) {
+                               size_t plan_bytes, const float* edge_vec_or_Y, const float* x,
+                               const float* w, float* m, void* stream) {
+  const float* Y = edge_vec_or_Y;
   Parsed p;
   e3_status s = parse(desc, p);
   if (s != E3_OK) return s;
-  if (!(desc->flags & E3_Y_GIVEN))
-    return fail(E3_ERR_INVALID_ARG, "the dense-product convolution takes given harmonics (E3_Y_GIVEN)");
   if (p.per_path) return fail(E3_ERR_UNSUPPORTED, "the dense-product convolution has collapsed outputs");
   e3k::ConvGemmArgs a{};
   size_t need = 0;
   if ((s = gemm_dims(desc, a.t, need)) != E3_OK) return s;
   if (a.t.n_blocks > 8) return fail(E3_ERR_UNSUPPORTED, "more than 8 output irreps");
+  // the y operand: given rows, or the harmonics of the edge vectors (one bank
+  // per y irrep, y component -> harmonic l*l + m)
+  a.ly = -1;
+  std::memset(&a.ym, 0xff, sizeof a.ym);
+  if (!(desc->flags & E3_Y_GIVEN)) {
+    if (p.dy > 64)
+      return fail(E3_ERR_UNSUPPORTED, "harmonics from edge vectors need dy <= 64; use E3_Y_GIVEN");
+    int i = 0;
+    a.ly = 0;
+    for (const auto& r : p.y) {
+      a.ly = std::max(a.ly, r.l);
+      for (int m = 0; m < 2 * r.l + 1; ++m) a.ym.idx[i++] = static_cast<signed char>(r.l * r.l + m);
+    }
+  }
   if (p.C % 16) return fail(E3_ERR_UNSUPPORTED, "the dense-product kernel needs C % 16 == 0");
   if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
   if (n_nodes == 0) return ok();
@@ -1236,7 +1249,7 @@ e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_e
     for (int cs : {64, 32, 16}) {
       if (cs > p.C || p.C % cs) continue;
       a.t.CS = cs;
-      if (e3k::tp_gemm_lds_bytes(a.t) <= cap) break;
+      if (e3k::tp_gemm_lds_bytes(a.t) + 4 * e3k::kConvGemmExtraWords <= cap) break;
       a.t.CS = 0;
     }
     if (a.t.CS) break;
@@ -1245,10 +1258,10 @@ e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_e
   const int XS = e3k::gemm_row_stride(a.t.CS);
   if ((a.t.P + 1) * XS > 65535 || a.t.dx * XS > 65535)
     return fail(E3_ERR_UNSUPPORTED, "too many x components or paths for the dense-product kernel");
-  a.t.lds_bytes = e3k::tp_gemm_lds_bytes(a.t);
+  a.t.lds_bytes = e3k::tp_gemm_lds_bytes(a.t) + 4 * e3k::kConvGemmExtraWords;
   a.t.plan = static_cast<const int*>(plan);
   a.t.x = x;
-  a.t.y = Y;
+  a.t.y = Y;  // Y [E][dy], or the edge vectors [E][3]
   a.t.w = w;
   a.t.z = m;
   a.n_nodes = n_nodes;

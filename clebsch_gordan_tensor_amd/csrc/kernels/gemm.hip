@@ -31,6 +31,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "harmonics_hi.h"
 #include "registry.h"
 
 namespace e3k {
@@ -207,6 +208,31 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
   }
 }
 
+// The harmonics of degree 0..LMAX of one edge vector into the LDS bank
+// (component-normalised, l*l + m order).
+template <int LMAX>
+__device__ __forceinline__ void bank_of(const float* v, float* s_bank) {
+  float Y[(LMAX + 1) * (LMAX + 1)];
+  float x = v[0], y = v[1], z = v[2];
+  const float r = sqrtf(x * x + y * y + z * z);
+  const float inv = r > 0.0f ? 1.0f / r : 0.0f;
+  harmonics_bank<LMAX>(x * inv, y * inv, z * inv, Y);
+#pragma unroll
+  for (int i = 0; i < (LMAX + 1) * (LMAX + 1); ++i) s_bank[i] = Y[i];
+}
+
+__device__ __forceinline__ void edge_bank(int ly, const float* v, float* s_bank) {
+  switch (ly) {
+    case 0: bank_of<0>(v, s_bank); break;
+    case 1: bank_of<1>(v, s_bank); break;
+    case 2: bank_of<2>(v, s_bank); break;
+    case 3: bank_of<3>(v, s_bank); break;
+    case 4: bank_of<4>(v, s_bank); break;
+    case 5: bank_of<5>(v, s_bank); break;
+    default: bank_of<6>(v, s_bank); break;
+  }
+}
+
 // The convolution forward (e3j A.3 Eq.7 with E.1 Eq.10-12) in the same
 // form: for receiver b, out[b][L] = sum over its in-edges e of A_{e,L} xt_e
 // with xt_e[(P,m1)][q] = w[e][P][q] x[sender e][l1,m1][q].  One workgroup per
@@ -217,7 +243,7 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
 // PRE as above, for the next edge of the same receiver (built with PRE = 0).
 constexpr int kConvGemmBlocks = 8;
 
-template <int PRE, int NU, bool BATCH>
+template <int PRE, int NU, bool BATCH, bool VEC>
 __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
   extern __shared__ __align__(16) float gsm[];
   const TpGemmArgs& g = cg.t;
@@ -231,6 +257,8 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
   float* s_w = s_x + g.dx * XS;
   float* s_y = s_w + (g.P + 1) * XS;
   int* s_k = reinterpret_cast<int*>(s_y + g.dy);
+  float* s_bank = reinterpret_cast<float*>(s_k + g.n_klist);  // 64 floats
+  int* s_ym = reinterpret_cast<int*>(s_bank + 64);             // y map, 16 words
   for (int i = threadIdx.x; i < g.n_klist; i += 256) {
     const int ent = klist[i];
     const int p = ent < 0 ? g.P : min(ent >> 16, g.P - 1);
@@ -238,6 +266,19 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
     s_k[i] = p * XS | (xi * XS) << 16;
   }
   for (int i = threadIdx.x; i < XS; i += 256) s_w[g.P * XS + i] = 0.0f;
+  constexpr bool vec_y = VEC;  // harmonics from the edge vectors (cg.ly >= 0)
+  if (threadIdx.x < 16) {
+    int wd;
+    __builtin_memcpy(&wd, cg.ym.idx + 4 * threadIdx.x, 4);
+    s_ym[threadIdx.x] = wd;
+  }
+  const int nbank = (min(max(cg.ly, 0), 6) + 1) * (min(max(cg.ly, 0), 6) + 1);
+  // y component i of the edge: given, or the bank entry the map names (clamped)
+  auto yval = [&](int i) {
+    if constexpr (!VEC) return s_y[i];
+    const int b = reinterpret_cast<const signed char*>(s_ym)[i];
+    return s_bank[min(max(b, 0), nbank - 1)];
+  };
   // the blocks, read once
   int b_oo[kConvGemmBlocks], b_rows[kConvGemmBlocks], b_kb[kConvGemmBlocks], b_K[kConvGemmBlocks],
       b_ab[kConvGemmBlocks];
@@ -279,7 +320,7 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
       const int u = threadIdx.x + 256 * j;
       if (u < U) pre[j] = *reinterpret_cast<const float4v*>(unit_src(u, e, a, c0));
     }
-    if (threadIdx.x < g.dy) ypre = g.y[int64_t(e) * g.dy + threadIdx.x];
+    if (!vec_y && threadIdx.x < g.dy) ypre = g.y[int64_t(e) * g.dy + threadIdx.x];
   };
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int node = int(item / n_slabs);
@@ -305,8 +346,12 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
       }
       for (int u = threadIdx.x + 256 * PRE; u < U; u += 256)
         *reinterpret_cast<float4v*>(unit_dst(u)) = *reinterpret_cast<const float4v*>(unit_src(u, e, a, c0));
-      for (int i = threadIdx.x; i < g.dy; i += 256)
-        s_y[i] = PRE > 0 && i < 256 ? ypre : g.y[int64_t(e) * g.dy + i];
+      if constexpr (VEC) {
+        if (threadIdx.x == 0) edge_bank(cg.ly, g.y + int64_t(e) * 3, s_bank);
+      } else {
+        for (int i = threadIdx.x; i < g.dy; i += 256)
+          s_y[i] = PRE > 0 && i < 256 ? ypre : g.y[int64_t(e) * g.dy + i];
+      }
       for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
       __syncthreads();
 #pragma unroll 4
@@ -314,7 +359,7 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
         const int4 en = groups[q];
         const int at = min(max(en.x, 0), g.a_floats - 1);
         const int y1 = min(en.y & 0xFFFF, g.dy - 1), y2 = min((en.y >> 16) & 0xFFFF, g.dy - 1);
-        s_a[at] = fmaf(__int_as_float(en.w), s_y[y2], __int_as_float(en.z) * s_y[y1]);
+        s_a[at] = fmaf(__int_as_float(en.w), yval(y2), __int_as_float(en.z) * yval(y1));
       }
       __syncthreads();
       if (PRE > 0 && e + 1 < e_hi) prefetch(e + 1, c0);
@@ -372,24 +417,25 @@ hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int PRE, int NU, bool BATCH>
+template <int PRE, int NU, bool BATCH, bool VEC>
 hipError_t launch_conv_gemm_pre(const ConvGemmArgs& a, int per_cu, hipStream_t s) {
   static bool attr = false;  // the attribute is per function: set once
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH, VEC>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int64_t items = int64_t(a.n_nodes) * (a.t.C / a.t.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
-  hipLaunchKernelGGL((k_conv_gemm<PRE, NU, BATCH>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
+  hipLaunchKernelGGL((k_conv_gemm<PRE, NU, BATCH, VEC>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
   if (a.n_nodes <= 0) return hipSuccess;
-  if (a.t.lds_bytes > 160 * 1024 || a.t.n_blocks > kConvGemmBlocks || a.t.CS > 128)
+  if (a.t.lds_bytes > 160 * 1024 || a.t.n_blocks > kConvGemmBlocks || a.t.CS > 128 ||
+      a.ly > 6 || (a.ly >= 0 && a.t.dy > 64))
     return hipErrorInvalidValue;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
   // one 16-channel tile per wavefront (slabs of at most 64 channels).  The
@@ -398,8 +444,11 @@ hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
   // Batched K steps for plans whose LDS leaves at most two workgroups per CU;
   // smaller plans keep the registers for a third wavefront per SIMD.
   if (a.t.CS > 64) return hipErrorInvalidValue;
-  return per_cu <= 2 ? launch_conv_gemm_pre<0, 1, true>(a, per_cu, s)
-                     : launch_conv_gemm_pre<0, 1, false>(a, std::min(per_cu, 8), s);
+  // The harmonics of the edge vectors are a variant of their own (the bank's
+  // registers would otherwise cost the given-harmonics kernel its occupancy).
+  if (a.ly >= 0) return launch_conv_gemm_pre<0, 1, false, true>(a, std::min(per_cu, 8), s);
+  return per_cu <= 2 ? launch_conv_gemm_pre<0, 1, true, false>(a, per_cu, s)
+                     : launch_conv_gemm_pre<0, 1, false, false>(a, std::min(per_cu, 8), s);
 }
 
 hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s) {

@@ -226,7 +226,11 @@ struct ConvGemmArgs {
   const int* rowptr;
   const int* sender;
   float* m;
+  int ly;   // -1: t.y is Y [E][dy]; else t.y is edge vectors [E][3], harmonics to degree ly
+  YMap ym;  // y component -> harmonic l*l + m (ly >= 0)
 };
+// LDS words the convolution adds to tp_gemm_lds_bytes: the harmonic bank and the y map
+constexpr int kConvGemmExtraWords = 64 + 16;
 hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s);
 hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
                                  float* dvec, hipStream_t s);

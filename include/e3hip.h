@@ -287,15 +287,16 @@ e3_status e3_tp_forward_gemm(const e3_desc* desc, int64_t n_rows, const void* pl
  * form: per receiver b and output block L, the sum over its in-edges e of
  * A_{e,L} xt_e (A from Y[e], xt from w[e] and x[sender e]) accumulates in the
  * matrix cores' registers over the edge list in CSR order, so m is written
- * once per node and reproducibly.  Needs E3_Y_GIVEN (Y [E][dy] float32, e.g.
- * from e3_spherical_harmonics), collapsed outputs with at most 8 output
+ * once per node and reproducibly.  edge_vec_or_Y: edge vectors [E][3] (the
+ * harmonics of every y irrep are computed per edge: needs dy <= 64) or,
+ * with E3_Y_GIVEN, Y [E][dy]; collapsed outputs with at most 8 output
  * irreps, C % 16 == 0, float32.  plan: table E3_GEN_GEMM (as
  * e3_tp_forward_gemm).  x [N][dx][C], w [E][P][C] (16-byte aligned),
  * m [N][dout][C]; padding edges (sender < 0) add nothing. */
 e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
                                const int32_t* rowptr, const int32_t* sender, const void* plan,
-                               size_t plan_bytes, const float* Y, const float* x, const float* w,
-                               float* m, void* stream);
+                               size_t plan_bytes, const float* edge_vec_or_Y, const float* x,
+                               const float* w, float* m, void* stream);
 e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_dx,
                                  size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
                                  const void* plan_dy, size_t dy_bytes, const void* x,

@@ -150,9 +150,12 @@ def test_gemm_conv_equals_table_kernel(gpu):
     assert_close(host(a), host(b).astype(np.float64), 2 * TOL_F32, "gemm conv vs table kernel")
 
 
-def test_gemm_conv_needs_given_harmonics(gpu):
+@pytest.mark.parametrize("L", [2, 6])
+def test_gemm_conv_from_edge_vectors(gpu, L):
+    # the harmonics computed per edge from the vectors, against the oracle
     from clebsch_gordan_tensor_amd import api
-    d, od, g, x, w, Y = _conv_problem(2, 64, 20, 640)
-    d2 = api.Desc(d.x, d.y, d.out, 64)
-    with pytest.raises(api.E3Error):
-        gpu.conv_forward_gemm(d2, dev(g.rowptr), dev(g.sender), dev(Y), dev(x), dev(w))
+    d, od, g, x, w, Y = _conv_problem(L, 64, 40, 640 + L)
+    dv = api.Desc(d.x, d.y, d.out, 64)
+    m = host(gpu.conv_forward_gemm(dv, dev(g.rowptr), dev(g.sender), dev(g.evec), dev(x), dev(w)))
+    ref = O.conv_forward(od, g.rowptr, g.sender, x, w, evec=g.evec)
+    assert_close(m, ref, TOL_F32, f"gemm conv from vectors L={L}")
