@@ -116,6 +116,9 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
     s_k[i] = p * XS | (xi * XS) << 16;
   }
   for (int i = threadIdx.x; i < XS; i += 256) s_w[g.P * XS + i] = 0.0f;
+  // A's entries outside the plan's groups stay zero: every row (edge)
+  // rewrites all the others, so A is cleared once
+  for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
   // wave-uniform (a scalar), so the tile tests below are scalar branches
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, kq = lane >> 4;
@@ -152,7 +155,7 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
     const int64_t row = item / n_slabs;
     const int c0 = int(item - row * n_slabs) * CS;
     __syncthreads();  // the previous item's LDS reads are done (and s_k is written)
-    // stage the slab of x and w and the row's y; clear A
+    // stage the slab of x and w and the row's y
 #pragma unroll
     for (int j = 0; j < PRE; ++j) {
       const int u = threadIdx.x + 256 * j;
@@ -162,7 +165,6 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
       *reinterpret_cast<float4v*>(unit_dst(u)) = *reinterpret_cast<const float4v*>(unit_src(u, row, c0));
     for (int i = threadIdx.x; i < g.dy; i += 256)
       s_y[i] = PRE > 0 && i < 256 ? ypre : g.y[row * g.dy + i];
-    for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
     __syncthreads();
     // A[k][M] = c1 y[y1] + c2 y[y2]: one independent 16-byte load per entry
 #pragma unroll 4
@@ -266,6 +268,9 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
     s_k[i] = p * XS | (xi * XS) << 16;
   }
   for (int i = threadIdx.x; i < XS; i += 256) s_w[g.P * XS + i] = 0.0f;
+  // A's entries outside the plan's groups stay zero: every row (edge)
+  // rewrites all the others, so A is cleared once
+  for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
   constexpr bool vec_y = VEC;  // harmonics from the edge vectors (cg.ly >= 0)
   if (threadIdx.x < 16) {
     int wd;
@@ -352,7 +357,6 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
         for (int i = threadIdx.x; i < g.dy; i += 256)
           s_y[i] = PRE > 0 && i < 256 ? ypre : g.y[int64_t(e) * g.dy + i];
       }
-      for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
       __syncthreads();
 #pragma unroll 4
       for (int q = threadIdx.x; q < g.n_groups; q += 256) {
