@@ -408,13 +408,12 @@ size_t tp_gemm_lds_bytes(const TpGemmArgs& a) {
 
 template <int PRE, int NU>
 hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
-  static bool attr = false;  // the attribute is per function: set once
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tp_gemm<PRE, NU>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // the attribute is per function: set once (a thread-safe static)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_tp_gemm<PRE, NU>),
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      160 * 1024);
+  if (attr != hipSuccess) return attr;
   const int64_t items = a.n_rows * (a.C / a.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
   hipLaunchKernelGGL((k_tp_gemm<PRE, NU>), dim3(grid), dim3(256), a.lds_bytes, s, a);
@@ -423,13 +422,12 @@ hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
 
 template <int PRE, int NU, bool BATCH, bool VEC>
 hipError_t launch_conv_gemm_pre(const ConvGemmArgs& a, int per_cu, hipStream_t s) {
-  static bool attr = false;  // the attribute is per function: set once
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH, VEC>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // the attribute is per function: set once (a thread-safe static)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH, VEC>),
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      160 * 1024);
+  if (attr != hipSuccess) return attr;
   const int64_t items = int64_t(a.n_nodes) * (a.t.C / a.t.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
   hipLaunchKernelGGL((k_conv_gemm<PRE, NU, BATCH, VEC>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);

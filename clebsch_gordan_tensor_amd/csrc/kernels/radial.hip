@@ -442,13 +442,12 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
 template <class S>
 hipError_t launch_fwd_radial(const RadialConvArgs& a, hipStream_t s) {
   const size_t lds = radial_lds_bytes<S>();
-  static bool attr = false;  // set once per process: the attribute is per function
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_conv_fwd_radial<S>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // the attribute is per function: set once (a thread-safe static)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_conv_fwd_radial<S>),
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      int(lds));
+  if (attr != hipSuccess) return attr;
   const int n_slabs = a.C / 32;
   hipLaunchKernelGGL(k_conv_fwd_radial<S>, dim3(kRadXcds * 32), dim3(64 * kRadWaves), lds, s,
                      a.n_nodes, a.n_edges, a.C, n_slabs, a.order, a.rowptr, a.sender, a.vec, a.x,
@@ -1014,14 +1013,12 @@ hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cu
   const int ntiles = (n_edges + 15) / 16;
   int n_groups = (2048 + n_slabs - 1) / n_slabs;
   n_groups = max(1, min(n_groups, (ntiles + 3) / 4));
-  static bool attr = false;  // the attribute is per function: set once
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_radial_mlp),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       int(mlp_lds_bytes()));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  // the attribute is per function: set once (a thread-safe static)
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_radial_mlp),
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      int(mlp_lds_bytes()));
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(k_radial_mlp, dim3(n_slabs * n_groups), dim3(256), mlp_lds_bytes(), s,
                      n_edges, n_cols, n_slabs, n_groups, vec, cutoff, W1, W2, w);
   return hipGetLastError();
