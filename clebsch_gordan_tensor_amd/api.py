@@ -92,6 +92,8 @@ def lib():
     L.e3_tp_backward_generic.argtypes = [dp, i64, vp, sz, vp, sz, vp, sz, vp, vp, vp, vp, vp, vp,
                                          vp, C.c_int, vp]
     L.e3_tp_forward_generic.argtypes = [dp, i64, vp, sz, vp, vp, vp, vp, C.c_int, vp]
+    L.e3_tp_forward_gemm.argtypes = [dp, i64, vp, sz, vp, vp, vp, vp, vp]
+    L.e3_conv_forward_gemm.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, vp]
     L.e3_conv_forward_generic.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, sz, vp, vp, vp, vp,
                                           C.c_int, vp]
     L.e3_conv_backward_generic.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, sz, vp, sz, vp, sz,

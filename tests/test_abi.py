@@ -326,3 +326,30 @@ def test_generic_plan_table(lib):
     fake = C.c_void_p(0x10000)
     assert lib.e3_tp_forward_generic(C.byref(d.c()), 5, fake, 16, fake, fake, fake, fake, 0,
                                      None) == -6
+
+
+def test_gemm_entry_arg_errors(lib):
+    # the dense-product entry points reject bad arguments on the host, before
+    # any device work (the pointers below are never dereferenced)
+    nat = [(l, 1 if l % 2 == 0 else -1) for l in range(3)]
+    d = api.Desc(nat, nat, nat, 64)
+    nb = C.c_size_t()
+    assert lib.e3_generic_plan_size(C.byref(d.c()), 4, C.byref(nb)) == 0
+    fk, odd = C.c_void_p(0x10000), C.c_void_p(0x10004)
+    assert lib.e3_tp_forward_gemm(C.byref(d.c()), 0, None, 0, None, None, None, None, None) == 0
+    assert lib.e3_tp_forward_gemm(C.byref(d.c()), 4, None, 0, fk, fk, fk, fk, None) == -1
+    assert lib.e3_tp_forward_gemm(C.byref(d.c()), 4, fk, nb.value - 4, fk, fk, fk, fk, None) == -1
+    assert lib.e3_tp_forward_gemm(C.byref(d.c()), 4, fk, nb.value, odd, fk, fk, fk, None) == -4
+    d24 = api.Desc(nat, nat, nat, 24)
+    assert lib.e3_tp_forward_gemm(C.byref(d24.c()), 4, fk, nb.value, fk, fk, fk, fk, None) == -3
+    # the convolution: collapsed outputs of at most 8 irreps only
+    pp = api.Desc(nat, nat, nat, 64, api.E3_OUT_PER_PATH)
+    assert lib.e3_conv_forward_gemm(C.byref(pp.c()), 4, 8, fk, fk, fk, nb.value, fk, fk, fk, fk,
+                                    None) == -3
+    nine = api.Desc([(0, 1)], [(0, 1)], [(0, 1)] * 9, 64)
+    assert lib.e3_conv_forward_gemm(C.byref(nine.c()), 4, 8, fk, fk, fk, 1 << 20, fk, fk, fk, fk,
+                                    None) == -3
+    assert lib.e3_conv_forward_gemm(C.byref(d.c()), 0, 0, None, None, None, 0, None, None, None,
+                                    None, None) == 0
+    assert lib.e3_conv_forward_gemm(C.byref(d.c()), 4, 8, fk, fk, None, 0, fk, fk, fk, fk,
+                                    None) == -1
