@@ -20,6 +20,8 @@ _lib = None
 E3_F32, E3_BF16 = 0, 1
 E3_Y_GIVEN = 1
 E3_OUT_PER_PATH = 2
+E3_CHECK = 4
+E3_ERR_GRAPH = -5
 
 
 class E3Error(RuntimeError):
@@ -51,7 +53,9 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_generic_plan_size", "e3_generic_plan_build", "e3_tp_forward_generic",
            "e3_tp_forward_gemm", "e3_conv_forward_gemm",
            "e3_tp_backward_generic", "e3_conv_forward_generic", "e3_conv_backward_generic",
-           "e3_conv_double_backward_generic", "e3_last_error"]
+           "e3_conv_double_backward_generic", "e3_check_graph", "e3_check_graph_host",
+           "e3_release_all",
+           "e3_last_error"]
 E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY, E3_GEN_GEMM = 0, 1, 2, 3, 4
 
 
@@ -114,10 +118,14 @@ def lib():
     L.e3_conv_prepare_transpose.argtypes = [i32, i32, vp, vp, vp, vp, sz, vp]
     L.e3_conv_backward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp,
                                    C.c_int, vp]
+    L.e3_check_graph.argtypes = [i32, i32, vp, vp, vp]
+    L.e3_check_graph_host.argtypes = [i32, i32, vp, vp]
+    L.e3_release_all.argtypes = []
     L.e3_last_error.restype = C.c_char_p
     for name in EXPORTS:
-        if name != "e3_last_error" and name != "e3_supported":
+        if name not in ("e3_last_error", "e3_supported", "e3_release_all"):
             getattr(L, name).restype = C.c_int
+    L.e3_release_all.restype = None
     _lib = L
     return L
 
@@ -159,9 +167,9 @@ class Desc:
 
     @property
     def dout(self):
-        if self.flags & E3_OUT_PER_PATH:  # one output block per path
-            return sum(2 * self.out[o][0] + 1
-                       for _, _, o in synth.path_list(self.x, self.y, self.out))
+        if self.flags & E3_OUT_PER_PATH:  # one output block per path, as the library lists them
+            return sum(2 * self.out[path_info(self, i)[2]][0] + 1
+                       for i in range(num_paths(self)))
         return synth.dim(self.out)
 
     def c(self):
@@ -210,6 +218,32 @@ def _need(t, name, shape=None, dtype=None):
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t
+
+
+def check_graph(rowptr, sender, stream=None):
+    """Host-side check of a CSR graph on the GPU (e3_check_graph): raises
+    E3Error (status E3_ERR_GRAPH) naming the first violation.  Synchronises
+    the stream."""
+    import torch
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    _check(lib().e3_check_graph(rowptr.shape[0] - 1, sender.shape[0], _ptr(rowptr), _ptr(sender),
+                                _stream(stream)))
+
+
+def check_graph_host(rowptr, sender):
+    """e3_check_graph on host (numpy int32) arrays: raises E3Error
+    (status E3_ERR_GRAPH) naming the first violation."""
+    import numpy as np
+    rp = np.ascontiguousarray(rowptr, dtype=np.int32)
+    sn = np.ascontiguousarray(sender, dtype=np.int32)
+    _check(lib().e3_check_graph_host(rp.shape[0] - 1, sn.shape[0], rp.ctypes.data_as(C.c_void_p),
+                                     sn.ctypes.data_as(C.c_void_p)))
+
+
+def release_all():
+    """Frees the library's host-side plan cache (e3_release_all)."""
+    lib().e3_release_all()
 
 
 def num_paths(desc: Desc) -> int:

@@ -33,6 +33,54 @@ e3_status ok() {
 
 constexpr int kGenericLmax = 6;  // coefficient tables of the generic tensor product
 
+e3_status check_graph_host(int32_t n_nodes, int32_t n_edges, const int32_t* rp,
+                           const int32_t* sn);
+
+// Host-side check of a receiver-sorted CSR graph (E3_CHECK): rowptr[0] = 0,
+// rowptr non-decreasing, rowptr[N] = E, every sender in [-1, N) (-1 the
+// padding mark).  The arrays are copied back on `stream` after the work
+// already queued there, so the call synchronises that stream.
+e3_status check_graph(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                      const int32_t* sender, hipStream_t stream) {
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (!rowptr || (n_edges > 0 && !sender)) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  std::vector<int32_t> rp(static_cast<size_t>(n_nodes) + 1), sn(static_cast<size_t>(n_edges));
+  hipError_t e = hipMemcpyAsync(rp.data(), rowptr, rp.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess && n_edges > 0)
+    e = hipMemcpyAsync(sn.data(), sender, sn.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess)
+    return fail(E3_ERR_HIP, std::string("graph check copy: ") + hipGetErrorString(e));
+  return check_graph_host(n_nodes, n_edges, rp.data(), sn.data());
+}
+
+e3_status check_graph_host(int32_t n_nodes, int32_t n_edges, const int32_t* rp,
+                           const int32_t* sn) {
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (!rp || (n_edges > 0 && !sn)) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (rp[0] != 0) return fail(E3_ERR_GRAPH, "rowptr[0] = " + std::to_string(rp[0]) + ", not 0");
+  for (int32_t b = 0; b < n_nodes; ++b)
+    if (rp[b + 1] < rp[b])
+      return fail(E3_ERR_GRAPH, "rowptr decreases at node " + std::to_string(b) + " (" +
+                                    std::to_string(rp[b]) + " -> " + std::to_string(rp[b + 1]) +
+                                    ")");
+  if (rp[n_nodes] != n_edges)
+    return fail(E3_ERR_GRAPH, "rowptr[N] = " + std::to_string(rp[n_nodes]) + ", E = " +
+                                  std::to_string(n_edges));
+  for (int32_t i = 0; i < n_edges; ++i)
+    if (sn[i] < -1 || sn[i] >= n_nodes)
+      return fail(E3_ERR_GRAPH, "sender[" + std::to_string(i) + "] = " + std::to_string(sn[i]) +
+                                    " is outside [-1, N)");
+  return E3_OK;
+}
+
+// E3_CHECK on a descriptor: the graph check before any launch.
+e3_status maybe_check(const e3_desc* d, int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                      const int32_t* sender, void* stream) {
+  if (!d || !(d->flags & E3_CHECK)) return E3_OK;
+  return check_graph(n_nodes, n_edges, rowptr, sender, hipStream_t(stream));
+}
+
 struct Parsed {
   int C = 0;
   int per_path = 0;  // E3_OUT_PER_PATH
@@ -328,6 +376,7 @@ e3_status e3_conv_forward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
   if ((s = select(p, dtype, Kind::fwd, ks, G, ci)) != E3_OK) return s;
   if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
   if (n_nodes == 0) return ok();
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
   if (!rowptr || !m || !x) return fail(E3_ERR_INVALID_ARG, "null pointer");
   if (n_edges > 0 && (!sender || !edge_vec_or_Y || !w))
     return fail(E3_ERR_INVALID_ARG, "null pointer");
@@ -385,6 +434,7 @@ e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges
   if ((s = select(p, dtype, Kind::bwd, ks, G, ci)) != E3_OK) return s;
   if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
   if (n_nodes == 0) return ok();
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
   size_t need = 0;
   e3_conv_workspace_size(n_nodes, n_edges, &need);
   if (!workspace || ws_bytes < need)
@@ -508,6 +558,11 @@ e3_status e3_conv_double_backward(const e3_desc* desc, int32_t n_nodes, int32_t 
                                   dw2, ddm, scratch, scratch_bytes, dtype)) != E3_OK ||
       n_nodes == 0)
     return s;
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
+  // the composed calls below run on the graph just checked
+  e3_desc inner = *desc;
+  inner.flags &= ~E3_CHECK;
+  desc = &inner;
   auto fwd = [&](const void* xx, const float* yy, const void* ww, void* out) {
     return e3_conv_forward(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes, yy, xx,
                            ww, out, dtype, stream);
@@ -732,6 +787,7 @@ e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n
     return fail(E3_ERR_UNSUPPORTED, "the radial convolution needs C in {32, 64, 128, 256}");
   if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
   if (n_nodes == 0) return ok();
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
   if (!rowptr || !x || !m) return fail(E3_ERR_INVALID_ARG, "null pointer");
   if (n_edges > 0 && (!sender || !edge_vec)) return fail(E3_ERR_INVALID_ARG, "null pointer");
   const int* order = nullptr;
@@ -971,6 +1027,10 @@ e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemm
   std::vector<int> b_oo(nb), b_rows(nb), b_kb(nb), b_K(nb), b_abase(nb);
   std::vector<int> path_block(p.P), path_koff(p.P);
   std::vector<std::vector<int>> bpaths(nb);
+  // every output block covers its own 2L+1 rows, also one no path reaches
+  // (collapsed mode): its K is 0, so the kernels write zeros there
+  if (!p.per_path)
+    for (int b = 0; b < nb; ++b) b_oo[b] = ooff[b], b_rows[b] = 2 * p.o[b].l + 1;
   for (int pi = 0, opp = 0; pi < p.P; ++pi) {
     const int L = p.o[p.pio[pi]].l;
     const int b = p.per_path ? pi : p.pio[pi];
@@ -1058,9 +1118,12 @@ e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemm
 
 // The plan's sizes per descriptor, built once (the kernel takes them from
 // the host, not from the caller's device copy).
+std::mutex g_plan_mu;
+std::map<std::string, std::pair<e3k::TpGemmArgs, size_t>> g_plan_cache;
+
 e3_status gemm_dims(const e3_desc* desc, e3k::TpGemmArgs& d, size_t& bytes) {
-  static std::mutex mu;
-  static std::map<std::string, std::pair<e3k::TpGemmArgs, size_t>> cache;
+  std::mutex& mu = g_plan_mu;
+  auto& cache = g_plan_cache;
   std::string key;
   if (!desc) return fail(E3_ERR_INVALID_ARG, "desc is null");
   for (const e3_irreps* v : {&desc->x, &desc->y, &desc->out}) {
@@ -1234,6 +1297,7 @@ e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_e
   if (p.C % 16) return fail(E3_ERR_UNSUPPORTED, "the dense-product kernel needs C % 16 == 0");
   if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
   if (n_nodes == 0) return ok();
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
   if (!rowptr || !x || !m) return fail(E3_ERR_INVALID_ARG, "null pointer");
   if (n_edges > 0 && (!sender || !Y || !w)) return fail(E3_ERR_INVALID_ARG, "null pointer");
   if (!plan || plan_bytes < need)
@@ -1265,6 +1329,7 @@ e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_e
   a.t.w = w;
   a.t.z = m;
   a.n_nodes = n_nodes;
+  a.n_edges = n_edges;
   a.rowptr = rowptr;
   a.sender = sender;
   a.m = m;
@@ -1351,6 +1416,7 @@ e3_status e3_conv_forward_generic(const e3_desc* desc, int32_t n_nodes, int32_t 
   if ((s = generic_y_source(desc, p, ly, ym)) != E3_OK) return s;
   if ((s = generic_graph(n_nodes, n_edges, rowptr, sender, edge_vec_or_Y)) != E3_OK) return s;
   if (n_nodes == 0) return ok();
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
   if (!x || !m || (n_edges > 0 && !w)) return fail(E3_ERR_INVALID_ARG, "null pointer");
   const GenDims dm = generic_dims(p, E3_GEN_FORWARD);
   if ((s = generic_table_ok(plan, plan_bytes, dm)) != E3_OK) return s;
@@ -1385,6 +1451,7 @@ e3_status e3_conv_backward_generic(const e3_desc* desc, int32_t n_nodes, int32_t
   if ((s = generic_y_source(desc, p, ly, ym)) != E3_OK) return s;
   if ((s = generic_graph(n_nodes, n_edges, rowptr, sender, edge_vec_or_Y)) != E3_OK) return s;
   if (n_nodes == 0) return ok();
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
   size_t need = 0;
   e3_conv_workspace_size(n_nodes, n_edges, &need);
   if (!workspace || ws_bytes < need)
@@ -1431,6 +1498,11 @@ e3_status e3_conv_double_backward_generic(
                                   dw2, ddm, scratch, scratch_bytes, dtype)) != E3_OK ||
       n_nodes == 0)
     return s;
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
+  // the composed calls below run on the graph just checked
+  e3_desc inner = *desc;
+  inner.flags &= ~E3_CHECK;
+  desc = &inner;
   auto fwd = [&](const void* xx, const float* yy, const void* ww, void* out) {
     return e3_conv_forward_generic(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes,
                                    plan_fwd, fwd_bytes, yy, xx, ww, out, dtype, stream);
@@ -1445,5 +1517,22 @@ e3_status e3_conv_double_backward_generic(
 }
 
 const char* e3_last_error(void) { return g_last_error.c_str(); }
+
+e3_status e3_check_graph(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                         const int32_t* sender, void* stream) {
+  const e3_status s = check_graph(n_nodes, n_edges, rowptr, sender, hipStream_t(stream));
+  return s == E3_OK ? ok() : s;
+}
+
+e3_status e3_check_graph_host(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                              const int32_t* sender) {
+  const e3_status s = check_graph_host(n_nodes, n_edges, rowptr, sender);
+  return s == E3_OK ? ok() : s;
+}
+
+void e3_release_all(void) {
+  std::lock_guard<std::mutex> g(g_plan_mu);
+  g_plan_cache.clear();
+}
 
 }  // extern "C"

@@ -22,6 +22,7 @@ int main(int argc, char** argv) {
   struct R {
     int M, m1, m2;
     float c;
+    double cd;  // the coefficient before rounding to float
   };
   std::vector<R> recs;
   for (int l1 = 0; l1 <= LM; ++l1)
@@ -38,7 +39,7 @@ int main(int argc, char** argv) {
             for (int b = 0; b < n2; ++b) {
               const double v = T[(size_t(M) * n1 + a) * n2 + b];
               if (std::abs(v) < 1e-12) continue;
-              recs.push_back({M, a, b, float(v)});
+              recs.push_back({M, a, b, float(v), v});
               cnt[l1][l2][L]++;
             }
       }
@@ -97,7 +98,7 @@ int main(int argc, char** argv) {
         for (int b = 0; b < n2; ++b) {
           const double v = T[(size_t(M) * 3 + a) * n2 + b];
           if (std::abs(v) < 1e-12) continue;
-          srec.push_back({M, a, b, float(v)});
+          srec.push_back({M, a, b, float(v), v});
           scnt[L]++;
         }
   }
@@ -156,6 +157,14 @@ int main(int argc, char** argv) {
     std::fprintf(f, "%a%s", double(float(inv_kappa[L])), L < SL ? ", " : "};\n");
   std::fprintf(f, "inline constexpr CgRec kShRec[%zu] = {\n", srec.size());
   for (const R& r : srec) std::fprintf(f, "  {%d, %d, %d, %a},\n", r.M, r.m1, r.m2, double(r.c));
+  std::fprintf(f, "};\n\n");
+  // the same recursion with coefficients kept in double, for the harmonics
+  // evaluated in fp64 and rounded once
+  std::fprintf(f, "struct CgRecD {\n  int M, m1, m2;\n  double c;\n};\n\n");
+  std::fprintf(f, "inline constexpr double kShInvKappaD[%d] = {", SL + 1);
+  for (int L = 0; L <= SL; ++L) std::fprintf(f, "%a%s", inv_kappa[L], L < SL ? ", " : "};\n");
+  std::fprintf(f, "inline constexpr CgRecD kShRecD[%zu] = {\n", srec.size());
+  for (const R& r : srec) std::fprintf(f, "  {%d, %d, %d, %a},\n", r.M, r.m1, r.m2, r.cd);
   std::fprintf(f, "};\n\n}  // namespace e3k\n");
   std::fclose(f);
   return 0;

@@ -95,6 +95,24 @@ constexpr PathList<count_paths<S>()> make_paths() {
   return r;
 }
 
+// Occupancy hint of the convolution backward with 2^c channels per lane
+// (see signatures.h); 1 when the signature gives none.
+template <class S, class = void>
+struct BwdWavesOf {
+  static constexpr int get(int) { return 1; }
+};
+template <class S>
+struct BwdWavesOf<S, std::void_t<decltype(S::kBwdWaves)>> {
+  static constexpr int get(int c) { return S::kBwdWaves[c]; }
+};
+
+// Whether the convolution backward stages each chunk's harmonics in LDS
+// (kStageY, default true) or forms them per edge in its loop.
+template <class S, class = void>
+struct StageYOf : std::true_type {};
+template <class S>
+struct StageYOf<S, std::void_t<decltype(S::kStageY)>> : std::bool_constant<S::kStageY> {};
+
 template <class S>
 constexpr int out_dim() {
   if (!PerPathOf<S>::value) return dim_of(S::O);
@@ -297,78 +315,104 @@ __device__ __forceinline__ void store_ch_stream(T* __restrict__ p, const float (
 // ------------------------------------------------------------- harmonics
 
 // Value and gradient along the three axes, for differentiating the
-// harmonic polynomials below by forward-mode arithmetic.
-struct Dual3 {
-  float v, d0, d1, d2;
-  __device__ Dual3(float c = 0.0f) : v(c), d0(0.0f), d1(0.0f), d2(0.0f) {}
-  __device__ Dual3(float c, float a, float b, float e) : v(c), d0(a), d1(b), d2(e) {}
+// harmonic polynomials below by forward-mode arithmetic (R: float or double).
+template <class R>
+struct DualT {
+  R v, d0, d1, d2;
+  __device__ DualT(R c = R(0)) : v(c), d0(R(0)), d1(R(0)), d2(R(0)) {}
+  __device__ DualT(R c, R a, R b, R e) : v(c), d0(a), d1(b), d2(e) {}
 };
-__device__ __forceinline__ Dual3 operator+(Dual3 a, Dual3 b) {
+template <class R>
+__device__ __forceinline__ DualT<R> operator+(DualT<R> a, DualT<R> b) {
   return {a.v + b.v, a.d0 + b.d0, a.d1 + b.d1, a.d2 + b.d2};
 }
-__device__ __forceinline__ Dual3 operator-(Dual3 a, Dual3 b) {
+template <class R>
+__device__ __forceinline__ DualT<R> operator-(DualT<R> a, DualT<R> b) {
   return {a.v - b.v, a.d0 - b.d0, a.d1 - b.d1, a.d2 - b.d2};
 }
-__device__ __forceinline__ Dual3 operator*(Dual3 a, Dual3 b) {
-  return {a.v * b.v, fmaf(a.d0, b.v, a.v * b.d0), fmaf(a.d1, b.v, a.v * b.d1),
-          fmaf(a.d2, b.v, a.v * b.d2)};
+template <class R>
+__device__ __forceinline__ DualT<R> operator*(DualT<R> a, DualT<R> b) {
+  return {a.v * b.v, fma(a.d0, b.v, a.v * b.d0), fma(a.d1, b.v, a.v * b.d1),
+          fma(a.d2, b.v, a.v * b.d2)};
 }
-__device__ __forceinline__ Dual3 operator*(float c, Dual3 a) {
+template <class R>
+__device__ __forceinline__ DualT<R> operator*(R c, DualT<R> a) {
   return {c * a.v, c * a.d0, c * a.d1, c * a.d2};
 }
+using Dual3 = DualT<float>;
+using Dual3d = DualT<double>;
+
+// The real type under a scalar (the type of the polynomial coefficients).
+template <class Sc>
+struct RealOf {
+  using type = Sc;
+};
+template <class R>
+struct RealOf<DualT<R>> {
+  using type = R;
+};
 
 // Component-normalised real harmonics of degree l (m = -l..l) of the unit
-// vector (x, y, z), written into out[0..2l]; Sc is float, or Dual3 to get
-// the partial derivatives of each polynomial as well.
+// vector (x, y, z), written into out[0..2l]; Sc is float or double, or a
+// DualT of either to get the partial derivatives of each polynomial as well.
 template <int L, class Sc>
 __device__ __forceinline__ void harmonics_l(Sc x, Sc y, Sc z, Sc* out) {
+  using R = typename RealOf<Sc>::type;
   if constexpr (L == 0) {
-    out[0] = Sc(1.0f);
+    out[0] = Sc(R(1));
   } else if constexpr (L == 1) {
-    const float k = 1.7320508075688772f;  // sqrt(3)
+    const R k = R(1.7320508075688772);  // sqrt(3)
     out[0] = k * y;
     out[1] = k * z;
     out[2] = k * x;
   } else if constexpr (L == 2) {
-    const float k15 = 3.872983346207417f;        // sqrt(15)
-    const float k5h = 1.118033988749895f;        // sqrt(5)/2
+    const R k15 = R(3.872983346207417);        // sqrt(15)
+    const R k5h = R(1.118033988749895);        // sqrt(5)/2
+    const R k15h = R(1.9364916731037085);      // sqrt(15)/2
     const Sc xx = x * x, yy = y * y, zz = z * z;
-    out[0] = k15 * x * y;
-    out[1] = k15 * y * z;
-    out[2] = k5h * (2.0f * zz - xx - yy);
-    out[3] = k15 * x * z;
-    out[4] = 0.5f * k15 * (xx - yy);
+    out[0] = k15 * (x * y);
+    out[1] = k15 * (y * z);
+    out[2] = k5h * (R(2) * zz - xx - yy);
+    out[3] = k15 * (x * z);
+    out[4] = k15h * (xx - yy);
   } else {
     static_assert(L == 3, "degree above 3");
-    const float a = 2.091650066335189f;   // sqrt(35/8)
-    const float b = 10.246950765959598f;  // sqrt(105)
-    const float c = 1.620185174601965f;   // sqrt(21/8)
-    const float d = 1.3228756555322954f;  // sqrt(7)/2
+    const R a = R(2.091650066335189);   // sqrt(35/8)
+    const R b = R(10.246950765959598);  // sqrt(105)
+    const R bh = R(5.123475382979799);  // sqrt(105)/2
+    const R c = R(1.620185174601965);   // sqrt(21/8)
+    const R d = R(1.3228756555322954);  // sqrt(7)/2
     const Sc xx = x * x, yy = y * y, zz = z * z;
-    const Sc t = 4.0f * zz - xx - yy;
-    out[0] = a * (3.0f * xx - yy) * y;
-    out[1] = b * x * y * z;
-    out[2] = c * y * t;
-    out[3] = d * z * (2.0f * zz - 3.0f * xx - 3.0f * yy);
-    out[4] = c * x * t;
-    out[5] = 0.5f * b * (xx - yy) * z;
-    out[6] = a * (xx - 3.0f * yy) * x;
+    const Sc t = R(4) * zz - xx - yy;
+    out[0] = a * ((R(3) * xx - yy) * y);
+    out[1] = b * (x * y * z);
+    out[2] = c * (y * t);
+    out[3] = d * (z * (R(2) * zz - R(3) * xx - R(3) * yy));
+    out[4] = c * (x * t);
+    out[5] = bh * ((xx - yy) * z);
+    out[6] = a * ((xx - R(3) * yy) * x);
   }
 }
 
-// r / |r| for any finite r: scaled by its largest component first, so that
-// the squared norm lies in [1, 3] (no underflow or overflow); 0 stays 0.
+// r / |r| for any finite r, with fp32 rounding only where unavoidable: the
+// vector is first scaled by the power of two of its largest component (exact,
+// so the squared norm lies in [1/4, 3/4] with no underflow or overflow), then
+// the norm is a correctly rounded square root and each component one correctly
+// rounded division.  0 stays 0.  (An approximate reciprocal square root, or a
+// scale by a rounded 1/max, costs the direction an ulp or two, which the cubic
+// harmonics triple.)
 __device__ __forceinline__ void unit_vector(float& x, float& y, float& z) {
   const float s = fmaxf(fabsf(x), fmaxf(fabsf(y), fabsf(z)));
   if (s > 0.0f) {
-    const float is = 1.0f / s;
-    x *= is;
-    y *= is;
-    z *= is;
-    const float inv = rsqrtf(x * x + y * y + z * z);
-    x *= inv;
-    y *= inv;
-    z *= inv;
+    int e;
+    (void)frexpf(s, &e);
+    x = ldexpf(x, -e);
+    y = ldexpf(y, -e);
+    z = ldexpf(z, -e);
+    const float r = sqrtf(fmaf(x, x, fmaf(y, y, z * z)));
+    x = x / r;
+    y = y / r;
+    z = z / r;
   }
 }
 
@@ -380,6 +424,7 @@ constexpr int y_offset(int j) {
 }
 
 // Harmonics of every y irrep of S from one (unnormalised) edge vector.
+// The zero vector gives Y_0 = 1 and 0 for every l > 0.
 template <class S>
 __device__ __forceinline__ void edge_y_from_vec(float x, float y, float z,
                                                 float (&Y)[Plan<S>::DY]) {
@@ -394,6 +439,34 @@ __device__ __forceinline__ void edge_y_from_vec(float x, float y, float z,
   });
 }
 
+// The same harmonics written straight to dst[0..DY) (an LDS row).
+template <class S>
+__device__ __forceinline__ void stage_y_from_vec(float x, float y, float z,
+                                                 float* __restrict__ dst) {
+  unit_vector(x, y, z);
+  sfor<0, S::NY>([&](auto j) {
+    constexpr int l = S::Y[j].l;
+    constexpr int off = y_offset<S>(j);
+    float h[2 * l + 1];
+    harmonics_l<l>(x, y, z, h);
+#pragma unroll
+    for (int m = 0; m < 2 * l + 1; ++m) dst[off + m] = h[m];
+  });
+}
+
+// A staged harmonics row back from LDS (16-byte reads; DYS % 4 == 0).
+template <int DY>
+__device__ __forceinline__ void read_y_row(const float* __restrict__ src, float (&Y)[DY]) {
+#pragma unroll
+  for (int i = 0; i < DY; i += 4) {
+    const float4 t = *reinterpret_cast<const float4*>(src + i);
+    Y[i] = t.x;
+    if (i + 1 < DY) Y[i + 1] = t.y;
+    if (i + 2 < DY) Y[i + 2] = t.z;
+    if (i + 3 < DY) Y[i + 3] = t.w;
+  }
+}
+
 // Orders this wavefront's LDS accesses around a staging step: the compiler
 // may not move LDS reads or writes across it, and the LDS queue drains.
 __device__ __forceinline__ void wave_lds_fence() {
@@ -402,29 +475,14 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// y operand of one edge for signature S: harmonics of the edge vector, one
-// bank per y irrep, or a given row Y[e][dy] when YG.
-template <class S, bool YG>
-__device__ __forceinline__ void edge_y(const float* __restrict__ src, int64_t e,
-                                       float (&Y)[Plan<S>::DY]) {
+// Given harmonics of edge or row e: Y[e][dy].
+template <class S>
+__device__ __forceinline__ void edge_y_given(const float* __restrict__ src, int64_t e,
+                                             float (&Y)[Plan<S>::DY]) {
   constexpr int DY = Plan<S>::DY;
-  if constexpr (YG) {
-    const float* p = src + e * DY;
+  const float* p = src + e * DY;
 #pragma unroll
-    for (int i = 0; i < DY; ++i) Y[i] = p[i];
-  } else {
-    const float* p = src + e * 3;
-    float x = p[0], y = p[1], z = p[2];
-    unit_vector(x, y, z);
-    sfor<0, S::NY>([&](auto j) {
-      constexpr int l = S::Y[j].l;
-      constexpr int off = y_offset<S>(j);
-      float h[2 * l + 1];
-      harmonics_l<l>(x, y, z, h);
-#pragma unroll
-      for (int m = 0; m < 2 * l + 1; ++m) Y[off + m] = h[m];
-    });
-  }
+  for (int i = 0; i < DY; ++i) Y[i] = p[i];
 }
 
 // ------------------------------------------------------------ shuffles

@@ -40,7 +40,8 @@ __device__ __forceinline__ int node_of_wave(int n_nodes, const int* __restrict__
 
 // ------------------------------------------------------------- forward
 // m[b] = sum over the CSR segment of b of the weighted CG messages
-// (e3j A.3 Eq.7, E.1 Eq.12-13).  Padding edges (sender < 0) are skipped.
+// (e3j A.3 Eq.7, E.1 Eq.12-13).  Padding edges (a sender outside [0, N))
+// are skipped.
 template <class S, class T, int CPL, bool YG>
 __global__ void __launch_bounds__(kBlock)
     k_conv_fwd(int n_nodes, int n_edges, int C, int G, const int* __restrict__ order,
@@ -60,13 +61,15 @@ __global__ void __launch_bounds__(kBlock)
 #pragma unroll
     for (int k = 0; k < CPL; ++k) acc[i][k] = 0.0f;
 
-  // The segment is walked in chunks of 64 edges whose senders (and edge
-  // vectors) are first staged in LDS with one coalesced load per lane, so
-  // every edge then costs a single round trip to memory (x and w together).
+  // The segment is walked in chunks of 64 edges whose senders (and, from
+  // edge vectors, the harmonics: one edge per lane) are
+  // first staged in LDS, so every edge then costs a single round trip to
+  // memory (x and w together) and no lane repeats another's harmonics.
+  constexpr int DYS = (PL::DY + 3) & ~3;
   __shared__ int s_snd[kWavesPerBlock][64];
-  __shared__ float s_vec[kWavesPerBlock][YG ? 1 : 64 * 3];
+  __shared__ __align__(16) float s_y[kWavesPerBlock][YG ? 4 : 64 * DYS];
   int* snd = s_snd[threadIdx.x >> 6];
-  float* vec = s_vec[threadIdx.x >> 6];
+  float* ys = s_y[threadIdx.x >> 6];
   // a malformed rowptr cannot move the walk outside [0, n_edges)
   const int beg = max(rowptr[b], 0), end = min(rowptr[b + 1], n_edges);
   for (int c0 = beg; c0 < end; c0 += 64) {
@@ -76,12 +79,17 @@ __global__ void __launch_bounds__(kBlock)
       snd[lane] = sender[c0 + lane];
       if constexpr (!YG) {
         const float* r = ysrc + int64_t(c0 + lane) * 3;
-        vec[3 * lane] = r[0];
-        vec[3 * lane + 1] = r[1];
-        vec[3 * lane + 2] = r[2];
+        stage_y_from_vec<S>(r[0], r[1], r[2], ys + lane * DYS);
       }
     }
     wave_lds_fence();
+    auto edge_yv = [&](int jj, float (&Y)[PL::DY]) {
+      if constexpr (YG) {
+        edge_y_given<S>(ysrc, c0 + jj, Y);
+      } else {
+        read_y_row<PL::DY>(ys + jj * DYS, Y);
+      }
+    };
     // software pipeline: the loads of the group's next edge are in flight
     // while the current edge is contracted
     auto valid = [&](int j) { return j < cn && snd[j] >= 0 && snd[j] < n_nodes; };
@@ -101,10 +109,7 @@ __global__ void __launch_bounds__(kBlock)
         if (!valid(j)) continue;
         issue(j, xc, wc);
         float Y[PL::DY];
-        if constexpr (YG)
-          edge_y<S, true>(ysrc, c0 + j, Y);
-        else
-          edge_y_from_vec<S>(vec[3 * j], vec[3 * j + 1], vec[3 * j + 2], Y);
+        edge_yv(j, Y);
         edge_forward<S, CPL>(Y, xc, wc, acc);
       }
       continue;
@@ -117,10 +122,7 @@ __global__ void __launch_bounds__(kBlock)
       if (vn) issue(jn, xn, wn);
       if (vc) {
         float Y[PL::DY];
-        if constexpr (YG)
-          edge_y<S, true>(ysrc, c0 + j, Y);
-        else
-          edge_y_from_vec<S>(vec[3 * j], vec[3 * j + 1], vec[3 * j + 2], Y);
+        edge_yv(j, Y);
         edge_forward<S, CPL>(Y, xc, wc, acc);
       }
 #pragma unroll
@@ -194,6 +196,7 @@ __device__ __forceinline__ void store_group_sum(const float (&v)[N], int G, int 
 // E.4 replaces the atomics of E.3).
 template <class S, class T, int CPL, bool YG>
 __global__ void __launch_bounds__(kBlock)
+    __attribute__((amdgpu_waves_per_eu(BwdWavesOf<S>::get(CPL == 1 ? 0 : CPL == 2 ? 1 : 2))))
     k_conv_bwd(int n_nodes, int n_edges, int C, int G, const int* __restrict__ order,
                const int* __restrict__ colptr,
                const int* __restrict__ perm, const int* __restrict__ recv,
@@ -216,14 +219,21 @@ __global__ void __launch_bounds__(kBlock)
     for (int k = 0; k < CPL; ++k) dxa[i][k] = 0.0f;
   }
 
-  // Out-edges in chunks of 64: edge ids, receivers and edge vectors are
-  // staged in LDS (one load per lane), then each edge costs one round trip.
+  // Out-edges in chunks of 64: edge ids, receivers and (from edge vectors)
+  // the harmonics, one edge per lane, are staged in LDS, then each edge
+  // costs one round trip.
+  // (Signatures that set kStageY false stage the edge vectors instead and
+  // form the harmonics per edge in the loop, which their register budget
+  // takes better.)
+  constexpr bool SY = !YG && StageYOf<S>::value;
+  constexpr int DYS = (PL::DY + 3) & ~3;
+  constexpr int YROW = SY ? DYS : 3;
   __shared__ int s_e[kWavesPerBlock][64];
   __shared__ int s_b[kWavesPerBlock][64];
-  __shared__ float s_vec[kWavesPerBlock][YG ? 1 : 64 * 3];
+  __shared__ __align__(16) float s_y[kWavesPerBlock][YG ? 4 : 64 * YROW];
   int* se = s_e[threadIdx.x >> 6];
   int* sb = s_b[threadIdx.x >> 6];
-  float* vec = s_vec[threadIdx.x >> 6];
+  float* ys = s_y[threadIdx.x >> 6];
   // clamped so that a workspace built for another graph stays in bounds
   const int beg = max(colptr[a], 0), end = min(colptr[a + 1], n_edges);
   for (int c0 = beg; c0 < end; c0 += 64) {
@@ -237,9 +247,13 @@ __global__ void __launch_bounds__(kBlock)
       sb[lane] = b;
       if constexpr (!YG) {
         const float* r = ysrc + int64_t(e < 0 ? 0 : e) * 3;
-        vec[3 * lane] = r[0];
-        vec[3 * lane + 1] = r[1];
-        vec[3 * lane + 2] = r[2];
+        if constexpr (SY) {
+          stage_y_from_vec<S>(r[0], r[1], r[2], ys + lane * DYS);
+        } else {
+          ys[3 * lane] = r[0];
+          ys[3 * lane + 1] = r[1];
+          ys[3 * lane + 2] = r[2];
+        }
       }
     }
     wave_lds_fence();
@@ -249,9 +263,11 @@ __global__ void __launch_bounds__(kBlock)
     if (e < 0) continue;
     float Y[PL::DY];
     if constexpr (YG)
-      edge_y<S, true>(ysrc, e, Y);
+      edge_y_given<S>(ysrc, e, Y);
+    else if constexpr (SY)
+      read_y_row<PL::DY>(ys + jj * DYS, Y);
     else
-      edge_y_from_vec<S>(vec[3 * jj], vec[3 * jj + 1], vec[3 * jj + 2], Y);
+      edge_y_from_vec<S>(ys[3 * jj], ys[3 * jj + 1], ys[3 * jj + 2], Y);
     float wv[PL::NP][CPL], dmv[PL::DO][CPL];
     const T* we = w + int64_t(e) * PL::NP * C + ch0;
 #pragma unroll
@@ -308,7 +324,7 @@ __global__ void __launch_bounds__(kBlock)
   if (row >= n_rows) return;  // group-uniform; no shuffles follow
 
   float Y[PL::DY];
-  edge_y<S, true>(y, row, Y);
+  edge_y_given<S>(y, row, Y);
   // every operand is read once and z written once: streaming accesses
   float xv[PL::DX][CPL];
   const T* xr = x + row * PL::DX * C + c0;
@@ -348,7 +364,7 @@ __global__ void __launch_bounds__(kBlock)
   if (row >= n_rows) return;  // group-uniform (wave-uniform when G = 64)
 
   float Y[PL::DY];
-  edge_y<S, true>(y, row, Y);
+  edge_y_given<S>(y, row, Y);
   float xv[PL::DX][CPL], wv[PL::NP][CPL], dzv[PL::DO][CPL];
   const T* xr = x + row * PL::DX * C + c0;
 #pragma unroll

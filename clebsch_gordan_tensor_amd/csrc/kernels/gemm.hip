@@ -215,10 +215,7 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
 template <int LMAX>
 __device__ __forceinline__ void bank_of(const float* v, float* s_bank) {
   float Y[(LMAX + 1) * (LMAX + 1)];
-  float x = v[0], y = v[1], z = v[2];
-  const float r = sqrtf(x * x + y * y + z * z);
-  const float inv = r > 0.0f ? 1.0f / r : 0.0f;
-  harmonics_bank<LMAX>(x * inv, y * inv, z * inv, Y);
+  harmonics_bank_of_vec<LMAX>(v[0], v[1], v[2], Y);
 #pragma unroll
   for (int i = 0; i < (LMAX + 1) * (LMAX + 1); ++i) s_bank[i] = Y[i];
 }
@@ -318,8 +315,13 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
   };
   float4v pre[PRE > 0 ? PRE : 1];
   float ypre = 0.0f;
+  // a sender outside [0, n_nodes) marks a padding edge
+  auto sender_of = [&](int e) {
+    const int a = cg.sender[e];
+    return a >= 0 && a < cg.n_nodes ? a : -1;
+  };
   auto prefetch = [&](int e, int c0) {
-    const int a = max(cg.sender[e], 0);
+    const int a = max(sender_of(e), 0);
 #pragma unroll
     for (int j = 0; j < PRE; ++j) {
       const int u = threadIdx.x + 256 * j;
@@ -330,7 +332,8 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int node = int(item / n_slabs);
     const int c0 = int(item - int64_t(node) * n_slabs) * CS;
-    const int e_lo = cg.rowptr[node], e_hi = cg.rowptr[node + 1];
+    // a malformed rowptr cannot move the walk outside [0, n_edges)
+    const int e_lo = max(cg.rowptr[node], 0), e_hi = min(cg.rowptr[node + 1], cg.n_edges);
     float4v D[kConvGemmBlocks][NU];
 #pragma unroll
     for (int b = 0; b < kConvGemmBlocks; ++b)
@@ -338,7 +341,7 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
       for (int u = 0; u < NU; ++u) D[b][u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
     if (PRE > 0 && e_lo < e_hi) prefetch(e_lo, c0);
     for (int e = e_lo; e < e_hi; ++e) {
-      const int a = cg.sender[e];
+      const int a = sender_of(e);
       if (a < 0) {  // padding edge (the same for the whole workgroup): nothing to add
         if (PRE > 0 && e + 1 < e_hi) prefetch(e + 1, c0);
         continue;
@@ -408,12 +411,11 @@ size_t tp_gemm_lds_bytes(const TpGemmArgs& a) {
 
 template <int PRE, int NU>
 hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
-  // the attribute is per function: set once (a thread-safe static)
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_tp_gemm<PRE, NU>),
-      hipFuncAttributeMaxDynamicSharedMemorySize,
-      160 * 1024);
-  if (attr != hipSuccess) return attr;
+  // the attribute is per function: raised once, retried after a failure
+  static std::atomic<bool> lds_set{false};
+  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_tp_gemm<PRE, NU>), 160 * 1024);
+      e != hipSuccess)
+    return e;
   const int64_t items = a.n_rows * (a.C / a.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
   hipLaunchKernelGGL((k_tp_gemm<PRE, NU>), dim3(grid), dim3(256), a.lds_bytes, s, a);
@@ -422,12 +424,11 @@ hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
 
 template <int PRE, int NU, bool BATCH, bool VEC>
 hipError_t launch_conv_gemm_pre(const ConvGemmArgs& a, int per_cu, hipStream_t s) {
-  // the attribute is per function: set once (a thread-safe static)
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH, VEC>),
-      hipFuncAttributeMaxDynamicSharedMemorySize,
-      160 * 1024);
-  if (attr != hipSuccess) return attr;
+  // the attribute is per function: raised once, retried after a failure
+  static std::atomic<bool> lds_set{false};
+  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH, VEC>), 160 * 1024);
+      e != hipSuccess)
+    return e;
   const int64_t items = int64_t(a.n_nodes) * (a.t.C / a.t.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
   hipLaunchKernelGGL((k_conv_gemm<PRE, NU, BATCH, VEC>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);

@@ -198,10 +198,8 @@ __device__ __forceinline__ void stage_edge_y(const float* __restrict__ src, int6
     for (int i = lane; i < dy; i += 64) ys[i] = src[e * dy + i];
   } else {
     constexpr int D = (LY + 1) * (LY + 1);
-    float x = src[3 * e], y = src[3 * e + 1], z = src[3 * e + 2];
-    unit_vector(x, y, z);
     float h[D];
-    harmonics_bank<LY>(x, y, z, h);
+    harmonics_bank_of_vec<LY>(src[3 * e], src[3 * e + 1], src[3 * e + 2], h);
     float v = 0.0f;
 #pragma unroll
     for (int q = 0; q < D; ++q) v = want == q ? h[q] : v;

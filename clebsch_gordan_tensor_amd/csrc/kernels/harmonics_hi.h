@@ -11,46 +11,71 @@
 
 namespace e3k {
 
-template <int LMAX>
-__device__ __forceinline__ void harmonics_bank(float x, float y, float z,
-                                               float (&Y)[(LMAX + 1) * (LMAX + 1)]) {
+// Coefficients of the recursion at degree L in the working precision R.
+template <class R, int L, int I>
+__device__ __forceinline__ constexpr R sh_rec_c() {
+  if constexpr (std::is_same_v<R, double>)
+    return kShRecD[kShRecOff[L] + I].c;
+  else
+    return kShRec[kShRecOff[L] + I].c;
+}
+template <class R, int L>
+__device__ __forceinline__ constexpr R sh_inv_kappa() {
+  if constexpr (std::is_same_v<R, double>)
+    return kShInvKappaD[L];
+  else
+    return kShInvKappa[L];
+}
+
+template <int LMAX, class R>
+__device__ __forceinline__ void harmonics_bank(R x, R y, R z, R (&Y)[(LMAX + 1) * (LMAX + 1)]) {
   static_assert(LMAX <= kShLmax, "degree above the generated recursion");
   sfor<0, (LMAX < 3 ? LMAX : 3) + 1>([&](auto l) { harmonics_l<l>(x, y, z, Y + l * l); });
   sfor<4, LMAX + 1>([&](auto L) {
     constexpr int o = L * L, o1 = (L - 1) * (L - 1);
 #pragma unroll
-    for (int M = 0; M < 2 * L + 1; ++M) Y[o + M] = 0.0f;
+    for (int M = 0; M < 2 * L + 1; ++M) Y[o + M] = R(0);
     sfor<0, kShRecCnt[L]>([&](auto r) {
-      constexpr CgRec R = kShRec[kShRecOff[L] + r];
-      Y[o + R.M] = fmaf(R.c * Y[1 + R.m1], Y[o1 + R.m2], Y[o + R.M]);
+      constexpr CgRec Q = kShRec[kShRecOff[L] + r];
+      Y[o + Q.M] = fma(sh_rec_c<R, L, r>() * Y[1 + Q.m1], Y[o1 + Q.m2], Y[o + Q.M]);
     });
 #pragma unroll
-    for (int M = 0; M < 2 * L + 1; ++M) Y[o + M] *= kShInvKappa[L];
+    for (int M = 0; M < 2 * L + 1; ++M) Y[o + M] *= sh_inv_kappa<R, L>();
   });
+}
+
+// The bank of degree 0..LMAX of the (unnormalised) edge vector (x, y, z);
+// the zero vector gives Y_0 = 1 and 0 above.
+template <int LMAX>
+__device__ __forceinline__ void harmonics_bank_of_vec(float x, float y, float z,
+                                                      float (&Y)[(LMAX + 1) * (LMAX + 1)]) {
+  unit_vector(x, y, z);
+  harmonics_bank<LMAX>(x, y, z, Y);
 }
 
 // Gradient with respect to the unit vector u = (x, y, z) of
 // sum_{l <= LMAX, m} w(l*l + m) Y_lm(u), by forward-mode derivatives of the
 // same polynomials as harmonics_bank (degrees 0..3 closed form, 4..LMAX by
-// the coupling recursion).  Only the previous degree is kept while the
-// recursion climbs, and each degree is contracted with w as it is made.
-template <int LMAX, class WF>
-__device__ __forceinline__ void harmonics_grad_bank(float x, float y, float z, WF w, float& g0,
-                                                    float& g1, float& g2) {
+// the coupling recursion), in the precision R.  Only the previous degree is
+// kept while the recursion climbs, and each degree is contracted with w as
+// it is made.
+template <int LMAX, class R, class WF>
+__device__ __forceinline__ void harmonics_grad_bank(R x, R y, R z, WF w, R& g0, R& g1, R& g2) {
   static_assert(LMAX <= kShLmax, "degree above the generated recursion");
+  using D = DualT<R>;
   constexpr int L3 = LMAX < 3 ? LMAX : 3;
-  const Dual3 X(x, 1.0f, 0.0f, 0.0f), Yd(y, 0.0f, 1.0f, 0.0f), Z(z, 0.0f, 0.0f, 1.0f);
-  Dual3 y1[3];
+  const D X(x, R(1), R(0), R(0)), Yd(y, R(0), R(1), R(0)), Z(z, R(0), R(0), R(1));
+  D y1[3];
   harmonics_l<1>(X, Yd, Z, y1);
-  Dual3 prev[2 * LMAX + 1];
-  auto add = [&](int k, const Dual3& h) {
-    const float c = w(k);
-    g0 = fmaf(c, h.d0, g0);
-    g1 = fmaf(c, h.d1, g1);
-    g2 = fmaf(c, h.d2, g2);
+  D prev[2 * LMAX + 1];
+  auto add = [&](int k, const D& h) {
+    const R c = R(w(k));
+    g0 = fma(c, h.d0, g0);
+    g1 = fma(c, h.d1, g1);
+    g2 = fma(c, h.d2, g2);
   };
   sfor<0, L3 + 1>([&](auto l) {
-    Dual3 h[2 * l + 1];
+    D h[2 * l + 1];
     harmonics_l<l>(X, Yd, Z, h);
 #pragma unroll
     for (int m = 0; m < 2 * l + 1; ++m) {
@@ -59,14 +84,14 @@ __device__ __forceinline__ void harmonics_grad_bank(float x, float y, float z, W
     }
   });
   sfor<4, LMAX + 1>([&](auto L) {
-    Dual3 cur[2 * L + 1];
+    D cur[2 * L + 1];
     sfor<0, kShRecCnt[L]>([&](auto r) {
-      constexpr CgRec R = kShRec[kShRecOff[L] + r];
-      cur[R.M] = cur[R.M] + (R.c * y1[R.m1]) * prev[R.m2];
+      constexpr CgRec Q = kShRec[kShRecOff[L] + r];
+      cur[Q.M] = cur[Q.M] + (sh_rec_c<R, L, r>() * y1[Q.m1]) * prev[Q.m2];
     });
 #pragma unroll
     for (int M = 0; M < 2 * L + 1; ++M) {
-      cur[M] = kShInvKappa[L] * cur[M];
+      cur[M] = sh_inv_kappa<R, L>() * cur[M];
       add(L * L + M, cur[M]);
       prev[M] = cur[M];
     }

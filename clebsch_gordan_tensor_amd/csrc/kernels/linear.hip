@@ -298,11 +298,11 @@ __global__ void __launch_bounds__(256)
 template <class T, int NCT, int NK>
 hipError_t launch_one(const LinearBlockArgs& a, int col0, hipStream_t s) {
   const size_t lds = size_t(a.cin) * (NCT * 32 + kLinPad) * sizeof(float);
-  // the W slab may exceed the default 64 KB of dynamic LDS
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_linear<T, NCT, NK>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, int(linear_lds_bytes(256)));
-  if (attr != hipSuccess) return attr;
+  // the attribute is per function: raised once, retried after a failure
+  static std::atomic<bool> lds_set{false};
+  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_linear<T, NCT, NK>), int(linear_lds_bytes(256)));
+      e != hipSuccess)
+    return e;
   const int64_t tiles = (a.n_rows * a.deg + 31) / 32;
   // persistent: at most 2 workgroups per CU, 256 CUs
   int64_t blocks = (tiles + 3) / 4;
@@ -318,10 +318,11 @@ hipError_t launch_one(const LinearBlockArgs& a, int col0, hipStream_t s) {
 template <int NCT, int NKB>
 hipError_t launch_bf16_one(const LinearBlockArgs& a, int col0, hipStream_t s) {
   const size_t lds = size_t(NCT * 32) * (16 * NKB + kLinPadB) * 2;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_linear_bf16<NCT, NKB>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  if (attr != hipSuccess) return attr;
+  // the attribute is per function: raised once, retried after a failure
+  static std::atomic<bool> lds_set{false};
+  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_linear_bf16<NCT, NKB>), int(lds));
+      e != hipSuccess)
+    return e;
   const int64_t tiles = (a.n_rows * a.deg + 31) / 32;
   int64_t blocks = (tiles + 3) / 4;
   if (blocks > 1024) blocks = 1024;

@@ -26,6 +26,7 @@ constexpr int kScanBlock = 256;
 constexpr int kScanItems = 4;
 constexpr int kScanTile = kScanBlock * kScanItems;
 constexpr int kMortonBitsHost = 18;  // Morton cells: 6 bits per axis, 262,144 cells
+constexpr int kBfsLevels = 64;       // traversal launches (levels) per graph
 
 __global__ void __launch_bounds__(256) k_fill(int* __restrict__ p, int64_t n, int v) {
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
@@ -150,20 +151,24 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// Breadth-first traversal over in-edges, one level per launch: every
-// wavefront takes a node of the current level [lb, le) of `order` and claims
-// its unvisited senders; claims are counted with one atomic per wavefront and
-// appended to `order`.  The order inside a level depends on timing; it only
-// decides which wavefront handles which node later, never a result.
-// When edge vectors are given, a claimed sender also gets a position
+// Breadth-first traversal over in-edges, one level per launch, the level's
+// bounds on the device: lev[i] .. lev[i+1] of `order`.  Every wavefront takes
+// a node of the level and claims its unvisited senders; claims are counted
+// with one atomic per wavefront and appended to `order`.  The last workgroup
+// to finish (a counter of finished workgroups; nothing waits on it) writes
+// lev[i+2], the end of the next level, so the host never reads a bound and
+// the launches queue back to back.  The order inside a level depends on
+// timing; it only decides which wavefront handles which node later, never a
+// result.  When edge vectors are given, a claimed sender also gets a position
 // relative to the root along the traversal tree: pos[a] = pos[u] - r_e
 // (r_e = pos[receiver] - pos[sender]).
 __global__ void __launch_bounds__(256)
-    k_bfs_expand(int n_nodes, int n_edges, const int* __restrict__ rowptr,
-                 const int* __restrict__ sender, const float* __restrict__ evec,
-                 float* __restrict__ pos, int* __restrict__ order,
-                 int* __restrict__ visited, int* __restrict__ tail, int lb, int le) {
+    k_bfs_level(int n_nodes, int n_edges, const int* __restrict__ rowptr,
+                const int* __restrict__ sender, const float* __restrict__ evec,
+                float* __restrict__ pos, int* __restrict__ order, int* __restrict__ visited,
+                int* __restrict__ tail, int* __restrict__ lev, int* __restrict__ done, int i) {
   const int lane = threadIdx.x & 63;
+  const int lb = max(lev[i], 0), le = min(lev[i + 1], n_nodes);
   for (int f = lb + blockIdx.x * 4 + (threadIdx.x >> 6); f < le; f += gridDim.x * 4) {
     const int u = order[f];
     const int beg = max(rowptr[u], 0), end = min(rowptr[u + 1], n_edges);
@@ -191,13 +196,25 @@ __global__ void __launch_bounds__(256)
       }
     }
   }
+  __syncthreads();  // this workgroup's claims are issued
+  if (threadIdx.x == 0) {
+    __threadfence();
+    if (atomicAdd(done, 1) == int(gridDim.x) - 1) {
+      lev[i + 2] = atomicAdd(tail, 0);
+      *done = 0;
+    }
+  }
 }
 
 __global__ void k_bfs_seed(int* __restrict__ order, int* __restrict__ visited,
-                           int* __restrict__ tail, float* __restrict__ pos, int s) {
+                           int* __restrict__ tail, int* __restrict__ lev, int* __restrict__ done,
+                           float* __restrict__ pos, int s) {
   order[0] = s;
   visited[s] = 1;
   *tail = 1;
+  lev[0] = 0;
+  lev[1] = 1;
+  *done = 0;
   if (pos) pos[3 * s] = pos[3 * s + 1] = pos[3 * s + 2] = 0.0f;
 }
 
@@ -212,8 +229,9 @@ __device__ __forceinline__ float kfloat(int k) {
 
 // Bounding box of the reconstructed positions of order[0 .. n).
 __global__ void __launch_bounds__(256)
-    k_bbox(int n, const int* __restrict__ order, const float* __restrict__ pos,
-           int* __restrict__ box /* min xyz, max xyz as fkey */) {
+    k_bbox(const int* __restrict__ n_ptr, int n_max, const int* __restrict__ order,
+           const float* __restrict__ pos, int* __restrict__ box /* min xyz, max xyz as fkey */) {
+  const int n = min(*n_ptr, n_max);
   int lo[3] = {INT_MAX, INT_MAX, INT_MAX}, hi[3] = {INT_MIN, INT_MIN, INT_MIN};
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
     const int v = order[i];
@@ -241,8 +259,10 @@ __device__ __forceinline__ int spread6(int v) {
 
 // Morton code of the cell of each reached node; counts per cell.
 __global__ void __launch_bounds__(256)
-    k_morton_keys(int n, const int* __restrict__ order, const float* __restrict__ pos,
-                  const int* __restrict__ box, int* __restrict__ key, int* __restrict__ hist) {
+    k_morton_keys(const int* __restrict__ n_ptr, int n_max, const int* __restrict__ order,
+                  const float* __restrict__ pos, const int* __restrict__ box,
+                  int* __restrict__ key, int* __restrict__ hist) {
+  const int n = min(*n_ptr, n_max);
   float lo[3], inv[3];
 #pragma unroll
   for (int d = 0; d < 3; ++d) {
@@ -266,9 +286,10 @@ __global__ void __launch_bounds__(256)
 // Scatter order[0 .. n) into cell order (cells by Morton code; inside a
 // cell the order depends on timing, which only affects scheduling).
 __global__ void __launch_bounds__(256)
-    k_morton_scatter(int n, const int* __restrict__ order, const int* __restrict__ key,
-                     const int* __restrict__ start, int* __restrict__ cursor,
-                     int* __restrict__ out) {
+    k_morton_scatter(const int* __restrict__ n_ptr, int n_max, const int* __restrict__ order,
+                     const int* __restrict__ key, const int* __restrict__ start,
+                     int* __restrict__ cursor, int* __restrict__ out) {
+  const int n = min(*n_ptr, n_max);
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
     const int c = key[i];
     const int k = start[c] + atomicAdd(cursor + c, 1);
@@ -277,7 +298,9 @@ __global__ void __launch_bounds__(256)
 }
 
 __global__ void __launch_bounds__(256)
-    k_copy_i32(const int* __restrict__ src, int* __restrict__ dst, int n) {
+    k_copy_i32(const int* __restrict__ src, int* __restrict__ dst, const int* __restrict__ n_ptr,
+               int n_max) {
+  const int n = min(*n_ptr, n_max);
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
     dst[i] = src[i];
 }
@@ -290,10 +313,12 @@ __global__ void __launch_bounds__(256)
     flag[i] = (i < n_nodes && !visited[i]) ? 1 : 0;
 }
 
-// Unreached nodes go after the traversal, in index order.
+// Unreached nodes go after the traversal (which reached *start nodes), in
+// index order.
 __global__ void __launch_bounds__(256)
     k_append_unvisited(int n_nodes, const int* __restrict__ visited, const int* __restrict__ pos,
-                       int start, int* __restrict__ order) {
+                       const int* __restrict__ start_ptr, int* __restrict__ order) {
+  const int start = *start_ptr;
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n_nodes;
        i += int64_t(gridDim.x) * blockDim.x)
     if (!visited[i]) {
@@ -308,10 +333,8 @@ __global__ void __launch_bounds__(256)
   constexpr int D = (LMAX + 1) * (LMAX + 1);
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
        i += int64_t(gridDim.x) * blockDim.x) {
-    float x = vec[3 * i], y = vec[3 * i + 1], z = vec[3 * i + 2];
-    unit_vector(x, y, z);
     float h[D];
-    harmonics_bank<LMAX>(x, y, z, h);
+    harmonics_bank_of_vec<LMAX>(vec[3 * i], vec[3 * i + 1], vec[3 * i + 2], h);
 #pragma unroll
     for (int k = 0; k < D; ++k) Y[i * D + k] = h[k];
   }
@@ -319,9 +342,9 @@ __global__ void __launch_bounds__(256)
 
 // Gradient of the harmonics with respect to the unnormalised vector:
 // dvec[i] = sum_k dY[i][k] dY_k/dr.  The polynomials of the unit vector u
-// are differentiated by forward-mode arithmetic (Dual3), and the chain rule
-// through u = r/|r| projects out the radial part: dY/dr = (I - u u^T) dY/du
-// / |r|.  A zero vector gets 0.
+// are differentiated by forward-mode arithmetic (dual numbers), and the chain
+// rule through u = r/|r| projects out the radial part: dY/dr = (I - u u^T)
+// dY/du / |r|.  Evaluated in fp64 and rounded once.  A zero vector gets 0.
 template <int LMAX>
 __global__ void __launch_bounds__(256)
     k_harmonics_grad(int64_t n, const float* __restrict__ vec, const float* __restrict__ dY,
@@ -329,30 +352,24 @@ __global__ void __launch_bounds__(256)
   constexpr int D = (LMAX + 1) * (LMAX + 1);
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
        i += int64_t(gridDim.x) * blockDim.x) {
-    float x = vec[3 * i], y = vec[3 * i + 1], z = vec[3 * i + 2];
-    float g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;
-    // |r| through the same largest-component scaling as unit_vector
-    const float s = fmaxf(fabsf(x), fmaxf(fabsf(y), fabsf(z)));
-    if (s > 0.0f) {
-      const float is = 1.0f / s;
-      x *= is;
-      y *= is;
-      z *= is;
-      const float inv = rsqrtf(x * x + y * y + z * z);
+    double x = vec[3 * i], y = vec[3 * i + 1], z = vec[3 * i + 2];
+    double g0 = 0.0, g1 = 0.0, g2 = 0.0;
+    const double n2 = x * x + y * y + z * z;
+    if (n2 > 0.0) {
+      const double r = sqrt(n2), inv = 1.0 / r;
       x *= inv;
       y *= inv;
       z *= inv;
-      const float inv_norm = inv * is;
       const float* gy = dY + i * D;
       harmonics_grad_bank<LMAX>(x, y, z, [&](int k) { return gy[k]; }, g0, g1, g2);
-      const float ug = x * g0 + y * g1 + z * g2;
-      g0 = (g0 - x * ug) * inv_norm;
-      g1 = (g1 - y * ug) * inv_norm;
-      g2 = (g2 - z * ug) * inv_norm;
+      const double ug = x * g0 + y * g1 + z * g2;
+      g0 = (g0 - x * ug) / r;
+      g1 = (g1 - y * ug) / r;
+      g2 = (g2 - z * ug) / r;
     }
-    dvec[3 * i] = g0;
-    dvec[3 * i + 1] = g1;
-    dvec[3 * i + 2] = g2;
+    dvec[3 * i] = float(g0);
+    dvec[3 * i + 1] = float(g1);
+    dvec[3 * i + 2] = float(g2);
   }
 }
 
@@ -441,6 +458,8 @@ TransposeLayout transpose_layout(int64_t n_nodes, int64_t n_edges) {
   o += up(n_nodes);
   L.box = o;
   o += 64;
+  L.levels = o;
+  o += up(kBfsLevels + 2);
   L.cell = o;
   o += up((int64_t(1) << kMortonBitsHost) + 1);
   L.cell_cursor = o;
@@ -457,33 +476,33 @@ TransposeLayout transpose_layout(int64_t n_nodes, int64_t n_edges) {
 // Traversal order of the nodes for the convolution kernels (ws + L.order):
 // breadth-first from node 0 over in-edges; with edge vectors, the reached
 // nodes are then re-sorted by the Morton cell of their position rebuilt
-// along the traversal tree; every unreached node follows in index order.  Neighbouring nodes end up close in the order, so the
-// wavefronts that run together gather overlapping node rows.  One host
-// synchronisation per level (the level bounds come back to the host).
+// along the traversal tree; every unreached node follows in index order.
+// Neighbouring nodes end up close in the order, so the wavefronts that run
+// together gather overlapping node rows.  Nothing comes back to the host:
+// the traversal is kBfsLevels launches whose level bounds live on the device
+// (levels past the graph's depth are empty launches; nodes deeper than that
+// join the unreached ones), and every later step reads the reached count
+// from the device.
 hipError_t build_locality_order(int n_nodes, int n_edges, const int* rowptr, const int* sender,
                                 const float* evec, int* ws, const TransposeLayout& L,
                                 hipStream_t s) {
   int* order = ws + L.order;
   int* visited = ws + L.cursor;  // free once the buckets are ranked
   int* tail = ws + L.npad + 1;
+  int* done = ws + L.npad + 2;
+  int* lev = ws + L.levels;
   float* pos = evec ? reinterpret_cast<float*>(ws + L.pos) : nullptr;
   const int64_t n1 = int64_t(n_nodes) + 1;
   hipLaunchKernelGGL(k_fill, dim3(grid_for(n1, 256)), dim3(256), 0, s, visited, n1, 0);
-  hipLaunchKernelGGL(k_bfs_seed, dim3(1), dim3(1), 0, s, order, visited, tail, pos, 0);
-  int lb = 0, le = 1, h_tail = 1;
-  while (lb < le) {
-    const unsigned g = unsigned(std::min<int64_t>((int64_t(le - lb) + 3) / 4, 1 << 16));
-    hipLaunchKernelGGL(k_bfs_expand, dim3(g), dim3(256), 0, s, n_nodes, n_edges, rowptr, sender,
-                       evec, pos, order, visited, tail, lb, le);
-    hipError_t err = hipMemcpyAsync(&h_tail, tail, sizeof(int), hipMemcpyDeviceToHost, s);
-    if (err == hipSuccess) err = hipStreamSynchronize(s);
-    if (err != hipSuccess) return err;
-    if (h_tail < le || h_tail > n_nodes) return hipErrorUnknown;  // cannot happen
-    lb = le;
-    le = h_tail;
-  }
-  const int reached = h_tail;
-  if (pos && reached > 1) {
+  hipLaunchKernelGGL(k_bfs_seed, dim3(1), dim3(1), 0, s, order, visited, tail, lev, done, pos, 0);
+  // enough workgroups for a wide level, few enough that an empty one is cheap
+  const unsigned g = unsigned(std::min<int64_t>((int64_t(n_nodes) + 63) / 64, 512));
+  const int levels = int(std::min<int64_t>(kBfsLevels, n_nodes));
+  for (int i = 0; i < levels; ++i)
+    hipLaunchKernelGGL(k_bfs_level, dim3(g), dim3(256), 0, s, n_nodes, n_edges, rowptr, sender,
+                       evec, pos, order, visited, tail, lev, done, i);
+  const unsigned gn = grid_for(n_nodes, 256);
+  if (pos) {
     // spatially compact order of the reached nodes: Morton cells of the
     // reconstructed positions, counting-sorted
     int* box = ws + L.box;
@@ -495,22 +514,20 @@ hipError_t build_locality_order(int n_nodes, int n_edges, const int* rowptr, con
     hipLaunchKernelGGL(k_fill, dim3(1), dim3(64), 0, s, box + 3, int64_t(3), INT_MIN);
     hipLaunchKernelGGL(k_fill, dim3(grid_for(ncell + 1, 256)), dim3(256), 0, s, cell, ncell + 1, 0);
     hipLaunchKernelGGL(k_fill, dim3(grid_for(ncell, 256)), dim3(256), 0, s, cur, ncell, 0);
-    hipLaunchKernelGGL(k_bbox, dim3(grid_for(reached, 256)), dim3(256), 0, s, reached, order, pos,
-                       box);
-    hipLaunchKernelGGL(k_morton_keys, dim3(grid_for(reached, 256)), dim3(256), 0, s, reached, order,
-                       pos, box, key, cell);
+    hipLaunchKernelGGL(k_bbox, dim3(gn), dim3(256), 0, s, tail, n_nodes, order, pos, box);
+    hipLaunchKernelGGL(k_morton_keys, dim3(gn), dim3(256), 0, s, tail, n_nodes, order, pos, box,
+                       key, cell);
     const unsigned tiles = unsigned((ncell + 1 + kScanTile - 1) / kScanTile);
     hipLaunchKernelGGL(k_scan_tiles, dim3(tiles), dim3(kScanBlock), 0, s, cell, ncell + 1, cell,
                        ws + L.bsum);
     hipLaunchKernelGGL(k_scan_tile_sums, dim3(1), dim3(kScanBlock), 0, s, ws + L.bsum, int(tiles));
     hipLaunchKernelGGL(k_scan_add, dim3(tiles), dim3(kScanBlock), 0, s, cell, ncell + 1,
                        ws + L.bsum);
-    hipLaunchKernelGGL(k_morton_scatter, dim3(grid_for(reached, 256)), dim3(256), 0, s, reached,
-                       order, key, cell, cur, ws + L.order2);
-    hipLaunchKernelGGL(k_copy_i32, dim3(grid_for(reached, 256)), dim3(256), 0, s, ws + L.order2,
-                       order, reached);
+    hipLaunchKernelGGL(k_morton_scatter, dim3(gn), dim3(256), 0, s, tail, n_nodes, order, key, cell,
+                       cur, ws + L.order2);
+    hipLaunchKernelGGL(k_copy_i32, dim3(gn), dim3(256), 0, s, ws + L.order2, order, tail, n_nodes);
   }
-  if (h_tail < n_nodes) {
+  {
     int* flag = ws + L.flag;
     hipLaunchKernelGGL(k_unvisited_flags, dim3(grid_for(n1, 256)), dim3(256), 0, s, n_nodes, visited,
                        flag);
@@ -519,8 +536,8 @@ hipError_t build_locality_order(int n_nodes, int n_edges, const int* rowptr, con
                        ws + L.bsum);
     hipLaunchKernelGGL(k_scan_tile_sums, dim3(1), dim3(kScanBlock), 0, s, ws + L.bsum, int(tiles));
     hipLaunchKernelGGL(k_scan_add, dim3(tiles), dim3(kScanBlock), 0, s, flag, n1, ws + L.bsum);
-    hipLaunchKernelGGL(k_append_unvisited, dim3(grid_for(n_nodes, 256)), dim3(256), 0, s, n_nodes,
-                       visited, flag, h_tail, order);
+    hipLaunchKernelGGL(k_append_unvisited, dim3(gn), dim3(256), 0, s, n_nodes, visited, flag, tail,
+                       order);
   }
   return hipGetLastError();
 }

@@ -442,12 +442,11 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
 template <class S>
 hipError_t launch_fwd_radial(const RadialConvArgs& a, hipStream_t s) {
   const size_t lds = radial_lds_bytes<S>();
-  // the attribute is per function: set once (a thread-safe static)
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_conv_fwd_radial<S>),
-      hipFuncAttributeMaxDynamicSharedMemorySize,
-      int(lds));
-  if (attr != hipSuccess) return attr;
+  // the attribute is per function: raised once, retried after a failure
+  static std::atomic<bool> lds_set{false};
+  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_conv_fwd_radial<S>), int(lds));
+      e != hipSuccess)
+    return e;
   const int n_slabs = a.C / 32;
   hipLaunchKernelGGL(k_conv_fwd_radial<S>, dim3(kRadXcds * 32), dim3(64 * kRadWaves), lds, s,
                      a.n_nodes, a.n_edges, a.C, n_slabs, a.order, a.rowptr, a.sender, a.vec, a.x,
@@ -1013,12 +1012,11 @@ hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cu
   const int ntiles = (n_edges + 15) / 16;
   int n_groups = (2048 + n_slabs - 1) / n_slabs;
   n_groups = max(1, min(n_groups, (ntiles + 3) / 4));
-  // the attribute is per function: set once (a thread-safe static)
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_radial_mlp),
-      hipFuncAttributeMaxDynamicSharedMemorySize,
-      int(mlp_lds_bytes()));
-  if (attr != hipSuccess) return attr;
+  // the attribute is per function: raised once, retried after a failure
+  static std::atomic<bool> lds_set{false};
+  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_radial_mlp), int(mlp_lds_bytes()));
+      e != hipSuccess)
+    return e;
   hipLaunchKernelGGL(k_radial_mlp, dim3(n_slabs * n_groups), dim3(256), mlp_lds_bytes(), s,
                      n_edges, n_cols, n_slabs, n_groups, vec, cutoff, W1, W2, w);
   return hipGetLastError();

@@ -2,11 +2,24 @@
 // signature, holding launchers for every storage type and y mode.
 #pragma once
 
+#include <atomic>
+
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 namespace e3k {
+
+// Raises the dynamic-LDS limit of kernel f to `bytes` once per process: the
+// flag is set only after a successful call, so a failure is returned and the
+// next launch tries again.
+inline hipError_t set_max_lds_once(std::atomic<bool>& done, const void* f, int bytes) {
+  if (done.load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.store(true, std::memory_order_release);
+  return e;
+}
+
 
 struct FwdArgs {
   int n_nodes, n_edges, C, G;
@@ -223,6 +236,7 @@ hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s);
 struct ConvGemmArgs {
   TpGemmArgs t;
   int n_nodes;
+  int n_edges;
   const int* rowptr;
   const int* sender;
   float* m;
@@ -272,7 +286,7 @@ hipError_t launch_linear_dw(const LinearDwArgs& a, int bf16, hipStream_t s);
 // Workspace layout of the transposed edge index (int32 words).
 struct TransposeLayout {
   int64_t npad, colptr, cursor, tmp_e, tmp_b, perm, recv, padlist, order, flag, pos, key, order2,
-      box, cell, cell_cursor, bsum, total_words;
+      box, levels, cell, cell_cursor, bsum, total_words;
 };
 TransposeLayout transpose_layout(int64_t n_nodes, int64_t n_edges);
 

@@ -73,6 +73,7 @@ typedef enum {
   E3_ERR_IRREPS = -2,      /* malformed irreps (l < 0, parity not +-1, mixed multiplicities) */
   E3_ERR_UNSUPPORTED = -3, /* signature or channel count without a kernel */
   E3_ERR_ALIGNMENT = -4,   /* feature pointer not 16-byte aligned */
+  E3_ERR_GRAPH = -5,       /* malformed CSR graph (found by E3_CHECK / e3_check_graph) */
   E3_ERR_WORKSPACE = -6,   /* workspace missing or too small */
   E3_ERR_HIP = -7          /* the HIP runtime reported an error */
 } e3_status;
@@ -91,17 +92,41 @@ typedef struct {
 } e3_irreps;
 
 enum {
-  E3_Y_GIVEN = 1,     /* conv: edge_vec_or_Y holds harmonics Y[E][dy], not vectors */
-  E3_OUT_PER_PATH = 2 /* one output block per path, in path order, instead of one
-                         per output irrep (e3j's default layout; A.3, E.1):
-                         m, dm, z, dz become [rows][sum over paths of 2L+1][C],
-                         `out` still lists the irreps paths may land on */
+  E3_Y_GIVEN = 1,      /* conv: edge_vec_or_Y holds harmonics Y[E][dy], not vectors */
+  E3_OUT_PER_PATH = 2, /* one output block per path, in path order, instead of one
+                          per output irrep (e3j's default layout; A.3, E.1):
+                          m, dm, z, dz become [rows][sum over paths of 2L+1][C],
+                          `out` still lists the irreps paths may land on */
+  E3_CHECK = 4         /* debug: every convolution call first checks the graph as
+                          e3_check_graph does (rowptr and sender are then required,
+                          also by the backward) and returns E3_ERR_GRAPH, launching
+                          nothing, when it is malformed.  The check copies rowptr
+                          and sender to the host after the work queued on `stream`,
+                          so such a call synchronises the host with that stream */
 };
 
 typedef struct {
   e3_irreps x, y, out;
   int32_t flags;
 } e3_desc;
+
+/* Checks a receiver-sorted CSR graph (the padding edges of e3j 3.1.2 marked
+ * by sender -1): rowptr[0] = 0, rowptr non-decreasing, rowptr[N] = E and
+ * every sender in [-1, N).  rowptr [N+1] and sender [E] are device arrays;
+ * they are copied to the host on `stream` after the work already queued
+ * there, so the call synchronises the host with that stream (debug use).
+ * Returns E3_OK, E3_ERR_GRAPH (e3_last_error names the first violation),
+ * E3_ERR_INVALID_ARG or E3_ERR_HIP. */
+e3_status e3_check_graph(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                         const int32_t* sender, void* stream);
+/* The same checks on HOST arrays rowptr [N+1] and sender [E] (no GPU work). */
+e3_status e3_check_graph_host(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
+                              const int32_t* sender);
+
+/* Frees the library's host-side cache (the dense-product plans' sizes per
+ * descriptor; the library holds no device memory of its own).  Later calls
+ * rebuild what they need.  Must not run concurrently with other calls. */
+void e3_release_all(void);
 
 /* Number of paths P of a descriptor (host only, no GPU work). */
 e3_status e3_num_paths(const e3_desc* desc, int32_t* n_paths);
@@ -292,7 +317,8 @@ e3_status e3_tp_forward_gemm(const e3_desc* desc, int64_t n_rows, const void* pl
  * with E3_Y_GIVEN, Y [E][dy]; collapsed outputs with at most 8 output
  * irreps, C % 16 == 0, float32.  plan: table E3_GEN_GEMM (as
  * e3_tp_forward_gemm).  x [N][dx][C], w [E][P][C] (16-byte aligned),
- * m [N][dout][C]; padding edges (sender < 0) add nothing. */
+ * m [N][dout][C]; padding edges (a sender outside [0, N)) add nothing, and a
+ * row range outside [0, E) is clamped to it. */
 e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
                                const int32_t* rowptr, const int32_t* sender, const void* plan,
                                size_t plan_bytes, const float* edge_vec_or_Y, const float* x,
@@ -317,8 +343,8 @@ e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void
  * e3_conv_forward).  Backward: tables E3_GEN_DX, E3_GEN_DW, E3_GEN_DY;
  * workspace from e3_conv_prepare_transpose on the same graph (required);
  * dY float32 [E][dy] is the cotangent of Y (of the harmonics in edge-vector
- * mode; e3_spherical_harmonics_backward chains it to the vectors).  Padding edges (sender < 0) add nothing and get dw = 0,
- * dY = 0.  Shapes, storage and limits as for the generic tensor product. */
+ * mode; e3_spherical_harmonics_backward chains it to the vectors).  Padding
+ * edges (a sender outside [0, N)) add nothing and get dw = 0, dY = 0.  Shapes, storage and limits as for the generic tensor product. */
 e3_status e3_conv_forward_generic(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
                                   const int32_t* rowptr, const int32_t* sender,
                                   const void* workspace, size_t ws_bytes, const void* plan,

@@ -49,27 +49,9 @@ def rel_err_bf16(got, ref):
     return e / rms if rms > 0 else e
 
 
-F32_ULP = 2.0 ** -24  # half an ulp of float32, relative to the value
-
-
-def rel_err_ulps(got, ref, ulps):
-    """Error ahead of an allowance of `ulps` float32 ulps of each element:
-    max(|got - ref| - 2 ulps * F32_ULP * |ref|, 0) / RMS(ref)."""
-    ref = np.asarray(ref, dtype=np.float64)
-    got = np.asarray(got, dtype=np.float64)
-    if ref.size == 0:
-        return 0.0
-    rms = np.sqrt(np.mean(ref ** 2))
-    excess = np.abs(got - ref) - 2 * ulps * F32_ULP * np.abs(ref)
-    e = float(np.maximum(excess, 0.0).max())
-    return e / rms if rms > 0 else e
-
-
-def assert_close(got, ref, tol, what="", bf16_out=False, f32_ulps=0):
+def assert_close(got, ref, tol, what="", bf16_out=False):
     if bf16_out:
         e = rel_err_bf16(got, ref)
-    elif f32_ulps:
-        e = rel_err_ulps(got, ref, f32_ulps)
     else:
         e = rel_err(got, ref)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"

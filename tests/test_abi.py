@@ -24,7 +24,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     hdr = open(os.path.join(ROOT, "include", "e3hip.h")).read()
-    names = set(re.findall(r"^\s*(?:e3_status|int32_t|const char\*)\s+(e3_\w+)\s*\(", hdr, re.M))
+    names = set(re.findall(r"^\s*(?:e3_status|int32_t|const char\*|void)\s+(e3_\w+)\s*\(", hdr,
+                           re.M))
     assert len(names) >= 11
     for n in names:
         assert hasattr(lib, n), n
@@ -353,3 +354,45 @@ def test_gemm_entry_arg_errors(lib):
                                     None, None) == 0
     assert lib.e3_conv_forward_gemm(C.byref(d.c()), 4, 8, fk, fk, None, 0, fk, fk, fk, fk,
                                     None) == -1
+
+
+def test_graph_check_codes(lib):
+    # the host form of e3_check_graph (E3_CHECK runs the same checks after
+    # copying the device arrays back): one case per documented violation
+    g = S.make_conv("tiny", with_dm=False).graph
+    api.check_graph_host(g.rowptr, g.sender)  # well formed
+    snd = g.sender.copy()
+    snd[5] = -1  # the padding mark is accepted
+    api.check_graph_host(g.rowptr, snd)
+    cases = {
+        "rowptr[0]": (np.concatenate([[1], g.rowptr[1:]]), g.sender),
+        "decreases": (np.where(np.arange(g.rowptr.size) == 10, g.rowptr[9] - 1, g.rowptr),
+                      g.sender),
+        "rowptr[N]": (g.rowptr, g.sender[:-1]),
+        "sender[": (g.rowptr, np.where(np.arange(g.sender.size) == 7, g.n_nodes, g.sender)),
+    }
+    for what, (rp, sn) in cases.items():
+        with pytest.raises(api.E3Error) as ei:
+            api.check_graph_host(rp, sn)
+        assert ei.value.status == api.E3_ERR_GRAPH and what in str(ei.value), what
+    with pytest.raises(api.E3Error) as ei:  # -2 is not the padding mark
+        api.check_graph_host(g.rowptr, np.where(np.arange(g.sender.size) == 3, -2, g.sender))
+    assert ei.value.status == api.E3_ERR_GRAPH
+    # an empty graph, and nodes without edges
+    api.check_graph_host(np.zeros(5, np.int32), np.zeros(0, np.int32))
+    assert lib.e3_check_graph_host(-1, 0, None, None) == -1  # E3_ERR_INVALID_ARG
+    assert lib.e3_check_graph_host(4, 0, None, None) == -1
+
+
+def test_release_all_then_rebuild(lib):
+    # the host plan cache is dropped and rebuilt on demand: the same sizes
+    xi = S.degree_irreps(4)
+    d = api.Desc(xi, S.sh_irreps(4), xi, 32)
+    def size():
+        n = C.c_size_t()
+        assert lib.e3_generic_plan_size(C.byref(d.c()), api.E3_GEN_GEMM, C.byref(n)) == 0
+        return n.value
+    n1 = size()
+    api.release_all()
+    api.release_all()  # twice is fine
+    assert size() == n1 > 0

@@ -13,7 +13,7 @@ import pytest
 
 from clebsch_gordan_tensor_amd import synth as S
 from oracle import oracle as O
-from tests.gpu_util import TOL_BF16, TOL_F32, assert_close, dev, host
+from tests.gpu_util import TOL_BF16, TOL_F32, assert_close, dev, host, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -242,10 +242,16 @@ def water3k_chain():
     return p, rdY, ev64, scale_e[:, None], scale_n[:, None]
 
 
-def _ratio(got, ref, scale, what):
+def _ratio(got, ref, scale, what, literal=False):
+    """The propagated gate above; the literal figure max|err|/RMS(ref) is
+    printed beside it, and gated too when `literal`."""
     e = float((np.abs(got.astype(np.float64) - ref) / scale).max())
+    lit = rel_err(got, ref)
+    print(f"[gate] {what}: propagated {e:.3e}, literal max|err|/rms {lit:.3e}", flush=True)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     assert e <= TOL_F32, f"{what}: max |err| / propagated scale = {e:.3e}"
+    if literal:
+        assert lit <= TOL_F32, f"{what}: literal max|err|/rms = {lit:.3e}"
     return e
 
 
@@ -262,7 +268,8 @@ def test_force_kernels_water3k_from_oracle_cotangent(gpu, water3k_chain):
     dvec = gpu.spherical_harmonics_backward(3, ev, dev(dY32))
     dpos = gpu.edge_grad_to_nodes(rowptr, sender, ws, dvec)
     torch.cuda.synchronize()
-    _ratio(host(dvec), rdvec, scale_e, "water3k:dvec (oracle dY)")
+    # the harmonics gradient runs in fp64 and rounds once: the literal gate
+    _ratio(host(dvec), rdvec, scale_e, "water3k:dvec (oracle dY)", literal=True)
     _ratio(host(dpos), rdpos, scale_n, "water3k:dpos (oracle dY)")
 
 

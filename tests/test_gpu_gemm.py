@@ -159,3 +159,46 @@ def test_gemm_conv_from_edge_vectors(gpu, L):
     m = host(gpu.conv_forward_gemm(dv, dev(g.rowptr), dev(g.sender), dev(g.evec), dev(x), dev(w)))
     ref = O.conv_forward(od, g.rowptr, g.sender, x, w, evec=g.evec)
     assert_close(m, ref, TOL_F32, f"gemm conv from vectors L={L}")
+
+
+def test_gemm_pathless_output_block(gpu):
+    # 0o is reached by no path of 0e+1o (x) 0e+1o: its rows are zero and the
+    # blocks that paths do reach keep their own values (the plan gives every
+    # output block its own rows)
+    from clebsch_gordan_tensor_amd import api
+    from clebsch_gordan_tensor_amd import synth as S
+    xi, yi, oi = [(0, 1), (1, -1)], [(0, 1), (1, -1)], [(0, 1), (1, -1), (0, -1)]
+    C, B = 16, 33
+    d, od = api.Desc(xi, yi, oi, C), O.Desc(xi, yi, oi, C)
+    rng = np.random.default_rng(575)
+    x = rng.standard_normal((B, 4, C)).astype(np.float32)
+    y = O.sh(1, rng.standard_normal((B, 3))).astype(np.float32)
+    w = rng.standard_normal((B, api.num_paths(d), C)).astype(np.float32)
+    ref = O.tp_forward(od, x, y, w)
+    assert np.all(ref[:, 4] == 0) and np.abs(ref[:, 0]).max() > 0
+    z = host(gpu.tp_forward_gemm(d, dev(x), dev(y), dev(w)))
+    assert_close(z, ref, TOL_F32, "gemm tp with a pathless block")
+    assert np.all(z[:, 4] == 0)
+    g = S.random_graph(48, 6.0, 3.0, 576)
+    dg = api.Desc(xi, yi, oi, C, api.E3_Y_GIVEN)
+    xn = rng.standard_normal((48, 4, C)).astype(np.float32)
+    wn = rng.standard_normal((g.n_edges, api.num_paths(d), C)).astype(np.float32)
+    Y = O.sh(1, g.evec.astype(np.float64)).astype(np.float32)
+    m = host(gpu.conv_forward_gemm(dg, dev(g.rowptr), dev(g.sender), dev(Y), dev(xn), dev(wn)))
+    ref = O.conv_forward(od, g.rowptr, g.sender, xn, wn, Y=Y)
+    assert_close(m, ref, TOL_F32, "gemm conv with a pathless block")
+    assert np.all(m[:, 4] == 0)
+
+
+def test_gemm_conv_sender_out_of_range_is_padding(gpu):
+    # any sender outside [0, N) marks a padding edge: sender = N adds nothing
+    d, od, g, x, w, Y = _conv_problem(3, 64, 50, 650)
+    snd = g.sender.copy()
+    hit = np.random.default_rng(651).choice(g.n_edges, 9, replace=False)
+    snd[hit] = g.n_nodes
+    snd[hit[:3]] = g.n_nodes + 1000
+    m = host(gpu.conv_forward_gemm(d, dev(g.rowptr), dev(snd), dev(Y), dev(x), dev(w)))
+    ref_snd = snd.copy()
+    ref_snd[hit] = -1
+    ref = O.conv_forward(od, g.rowptr, ref_snd, x, w, Y=Y)
+    assert_close(m, ref, TOL_F32, "gemm conv, senders past N")

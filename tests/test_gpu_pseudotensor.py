@@ -8,7 +8,7 @@ import pytest
 from clebsch_gordan_tensor_amd import synth as S
 from oracle import oracle as O
 from tests.gpu_util import TOL_F32, assert_close, dev, host
-from tests.test_gpu_parity import _sampled_conv_check, desc_pair, oracle_all, run_conv
+from tests.test_gpu_parity import _full_conv_check, desc_pair, oracle_all, run_conv
 
 pytestmark = pytest.mark.gpu
 
@@ -60,5 +60,6 @@ def test_all_outputs_inversion_parity(gpu):
     assert_close(mi, so * m, TOL_F32, "inversion")
 
 
-def test_all_outputs_mace64k_sampled(gpu):
-    _sampled_conv_check(gpu, S.make_conv("mace64k_all"), TOL_F32)
+@pytest.mark.timeout(900)
+def test_all_outputs_mace64k_full(gpu):
+    _full_conv_check(gpu, S.make_conv("mace64k_all"), TOL_F32)
