@@ -394,13 +394,10 @@ __device__ __forceinline__ void harmonics_l(Sc x, Sc y, Sc z, Sc* out) {
   }
 }
 
-// r / |r| for any finite r, with fp32 rounding only where unavoidable: the
-// vector is first scaled by the power of two of its largest component (exact,
-// so the squared norm lies in [1/4, 3/4] with no underflow or overflow), then
-// the norm is a correctly rounded square root and each component one correctly
-// rounded division.  0 stays 0.  (An approximate reciprocal square root, or a
-// scale by a rounded 1/max, costs the direction an ulp or two, which the cubic
-// harmonics triple.)
+// r / |r| in float32 for any finite r: scaled first by the exact power of
+// two of its largest component (the squared norm then lies in [1/4, 3/4],
+// with no underflow or overflow), then a correctly rounded square root and
+// one correctly rounded division per component.  0 stays 0.
 __device__ __forceinline__ void unit_vector(float& x, float& y, float& z) {
   const float s = fmaxf(fabsf(x), fmaxf(fabsf(y), fabsf(z)));
   if (s > 0.0f) {
@@ -423,35 +420,53 @@ constexpr int y_offset(int j) {
   return o;
 }
 
-// Harmonics of every y irrep of S from one (unnormalised) edge vector.
-// The zero vector gives Y_0 = 1 and 0 for every l > 0.
-template <class S>
-__device__ __forceinline__ void edge_y_from_vec(float x, float y, float z,
-                                                float (&Y)[Plan<S>::DY]) {
-  unit_vector(x, y, z);
+// Direction of the edge vector (vx, vy, vz) in fp64: the products of fp32
+// values are exact in fp64 and no fp32 input can underflow or overflow the
+// squared norm, so no rescaling is needed.  The zero vector gives 0.
+__device__ __forceinline__ void unit_dir_f64(float vx, float vy, float vz, double& x, double& y,
+                                             double& z) {
+  x = vx;
+  y = vy;
+  z = vz;
+  const double n2 = x * x + y * y + z * z;
+  const double inv = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
+  x *= inv;
+  y *= inv;
+  z *= inv;
+}
+
+// Harmonics of every y irrep of S from one (unnormalised) edge vector,
+// written to dst[0..DY): evaluated in fp64 on the fp64 direction and rounded
+// once, so every value is the float32 nearest to the exact harmonic of the
+// stored vector (up to rare ties).  In float32 throughout, the direction's
+// rounding alone costs an ulp or two that the cubic harmonics triple, which
+// heavy-tailed edge weights carry into the largest outputs.  The zero vector
+// gives Y_0 = 1 and 0 for every l > 0.
+template <class S, class Dst>
+__device__ __forceinline__ void y_from_vec_f64(float vx, float vy, float vz, Dst&& dst) {
+  double x, y, z;
+  unit_dir_f64(vx, vy, vz, x, y, z);
   sfor<0, S::NY>([&](auto j) {
     constexpr int l = S::Y[j].l;
     constexpr int off = y_offset<S>(j);
-    float h[2 * l + 1];
+    double h[2 * l + 1];
     harmonics_l<l>(x, y, z, h);
 #pragma unroll
-    for (int m = 0; m < 2 * l + 1; ++m) Y[off + m] = h[m];
+    for (int m = 0; m < 2 * l + 1; ++m) dst(off + m, float(h[m]));
   });
+}
+
+template <class S>
+__device__ __forceinline__ void edge_y_from_vec(float vx, float vy, float vz,
+                                                float (&Y)[Plan<S>::DY]) {
+  y_from_vec_f64<S>(vx, vy, vz, [&](int i, float v) { Y[i] = v; });
 }
 
 // The same harmonics written straight to dst[0..DY) (an LDS row).
 template <class S>
-__device__ __forceinline__ void stage_y_from_vec(float x, float y, float z,
+__device__ __forceinline__ void stage_y_from_vec(float vx, float vy, float vz,
                                                  float* __restrict__ dst) {
-  unit_vector(x, y, z);
-  sfor<0, S::NY>([&](auto j) {
-    constexpr int l = S::Y[j].l;
-    constexpr int off = y_offset<S>(j);
-    float h[2 * l + 1];
-    harmonics_l<l>(x, y, z, h);
-#pragma unroll
-    for (int m = 0; m < 2 * l + 1; ++m) dst[off + m] = h[m];
-  });
+  y_from_vec_f64<S>(vx, vy, vz, [&](int i, float v) { dst[i] = v; });
 }
 
 // A staged harmonics row back from LDS (16-byte reads; DYS % 4 == 0).

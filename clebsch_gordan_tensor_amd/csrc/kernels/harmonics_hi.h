@@ -44,13 +44,28 @@ __device__ __forceinline__ void harmonics_bank(R x, R y, R z, R (&Y)[(LMAX + 1) 
   });
 }
 
-// The bank of degree 0..LMAX of the (unnormalised) edge vector (x, y, z);
-// the zero vector gives Y_0 = 1 and 0 above.
+// The bank of degree 0..LMAX of the (unnormalised) edge vector (x, y, z) in
+// float32 (unit_vector, then the polynomials and the recursion); the zero
+// vector gives Y_0 = 1 and 0 above.  The coefficient-table and dense-product
+// kernels form it per edge, where fp64 would cost them registers.
 template <int LMAX>
 __device__ __forceinline__ void harmonics_bank_of_vec(float x, float y, float z,
                                                       float (&Y)[(LMAX + 1) * (LMAX + 1)]) {
   unit_vector(x, y, z);
   harmonics_bank<LMAX>(x, y, z, Y);
+}
+
+// The same bank in fp64 on the fp64 direction, rounded once (as the
+// specialised convolution kernels' harmonics of degree <= 3).
+template <int LMAX>
+__device__ __forceinline__ void harmonics_bank_of_vec_f64(float vx, float vy, float vz,
+                                                          float (&Y)[(LMAX + 1) * (LMAX + 1)]) {
+  double x, y, z;
+  unit_dir_f64(vx, vy, vz, x, y, z);
+  double h[(LMAX + 1) * (LMAX + 1)];
+  harmonics_bank<LMAX>(x, y, z, h);
+#pragma unroll
+  for (int i = 0; i < (LMAX + 1) * (LMAX + 1); ++i) Y[i] = float(h[i]);
 }
 
 // Gradient with respect to the unit vector u = (x, y, z) of

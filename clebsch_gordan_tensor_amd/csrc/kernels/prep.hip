@@ -334,7 +334,7 @@ __global__ void __launch_bounds__(256)
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
        i += int64_t(gridDim.x) * blockDim.x) {
     float h[D];
-    harmonics_bank_of_vec<LMAX>(vec[3 * i], vec[3 * i + 1], vec[3 * i + 2], h);
+    harmonics_bank_of_vec_f64<LMAX>(vec[3 * i], vec[3 * i + 1], vec[3 * i + 2], h);
 #pragma unroll
     for (int k = 0; k < D; ++k) Y[i * D + k] = h[k];
   }

@@ -54,6 +54,7 @@ def assert_close(got, ref, tol, what="", bf16_out=False):
         e = rel_err_bf16(got, ref)
     else:
         e = rel_err(got, ref)
+    print(f"[err] {what}: {e:.3e} (gate {tol:.0e})", flush=True)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     assert e <= tol, f"{what}: max|err|/rms = {e:.3e} > {tol:.1e}"
     return e
