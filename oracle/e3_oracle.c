@@ -78,6 +78,17 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Thread count of the later parallel loops (n > 0); used to time the oracle
+ * on one thread.  No arithmetic depends on it: every output row is computed
+ * by one thread in a fixed order. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 static long double factorial(int n) {
   long double r = 1.0L;
   for (int i = 2; i <= n; ++i) r *= (long double)i;

@@ -45,6 +45,8 @@ def _load():
     lib.oracle_sh_batch.argtypes = [C.c_int, C.c_int64, dp, dp]
     lib.oracle_sh_general.argtypes = [C.c_int, dp, dp]
     lib.oracle_num_threads.restype = C.c_int
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [C.c_int]
     lib.oracle_num_paths.restype = C.c_int
     lib.oracle_num_paths.argtypes = [C.c_void_p]
     lib.oracle_path_info.restype = C.c_int
@@ -157,6 +159,12 @@ def _f64(a):
 
 def _i32(a):
     return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (results do not
+    depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def num_threads() -> int:
