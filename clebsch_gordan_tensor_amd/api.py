@@ -53,7 +53,7 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_generic_plan_size", "e3_generic_plan_build", "e3_tp_forward_generic",
            "e3_tp_forward_gemm", "e3_conv_forward_gemm",
            "e3_tp_backward_generic", "e3_conv_forward_generic", "e3_conv_backward_generic",
-           "e3_conv_double_backward_generic", "e3_check_graph", "e3_check_graph_host",
+           "e3_conv_double_backward_generic", "e3_check_graph", "e3_check_graph_host", "e3_conv_backward_noalloc",
            "e3_release_all",
            "e3_last_error"]
 E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY, E3_GEN_GEMM = 0, 1, 2, 3, 4
@@ -119,6 +119,8 @@ def lib():
     L.e3_conv_backward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp,
                                    C.c_int, vp]
     L.e3_check_graph.argtypes = [i32, i32, vp, vp, vp]
+    L.e3_conv_backward_noalloc.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           C.c_int, vp]
     L.e3_check_graph_host.argtypes = [i32, i32, vp, vp]
     L.e3_release_all.argtypes = []
     L.e3_last_error.restype = C.c_char_p
@@ -409,6 +411,38 @@ def conv_backward(desc: Desc, rowptr, sender, workspace, edge_vec_or_Y, x, w, dm
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _ptr(edge_vec_or_Y), _ptr(x), _ptr(w), _ptr(dm), _ptr(dx),
                                   _ptr(dw), _ptr(dY), _dtype_code(x), _stream(stream)))
+    return dx, dw, dY
+
+
+def conv_backward_noalloc(desc: Desc, rowptr, sender, edge_vec_or_Y, x, w, dm, dx=None, dw=None,
+                          dY=None, stream=None):
+    """The backward with its per-graph index built inside the call in the
+    library's fixed device scratch (e3_conv_backward_noalloc); the library
+    allocates nothing (this wrapper allocates the outputs it is not given)."""
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    P = num_paths(desc)
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    ycols = desc.dy if desc.flags & E3_Y_GIVEN else 3
+    _need(edge_vec_or_Y, "edge_vec_or_Y", shape=(E, ycols), dtype=torch.float32)
+    _need(x, "x", shape=(N, desc.dx, desc.channels))
+    _need(w, "w", shape=(E, P, desc.channels), dtype=x.dtype)
+    _need(dm, "dm", shape=(N, desc.dout, desc.channels), dtype=x.dtype)
+    dev, dt = x.device, x.dtype
+    if dx is None:
+        dx = torch.empty((N, desc.dx, desc.channels), device=dev, dtype=dt)
+    if dw is None:
+        dw = torch.empty((E, P, desc.channels), device=dev, dtype=dt)
+    if dY is None:
+        dY = torch.empty((E, desc.dy), device=dev, dtype=torch.float32)
+    _need(dx, "dx", shape=(N, desc.dx, desc.channels), dtype=dt)
+    _need(dw, "dw", shape=(E, P, desc.channels), dtype=dt)
+    _need(dY, "dY", shape=(E, desc.dy), dtype=torch.float32)
+    _check(lib().e3_conv_backward_noalloc(C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender),
+                                          _ptr(edge_vec_or_Y), _ptr(x), _ptr(w), _ptr(dm),
+                                          _ptr(dx), _ptr(dw), _ptr(dY), _dtype_code(x),
+                                          _stream(stream)))
     return dx, dw, dY
 
 

@@ -453,6 +453,51 @@ e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges
   return hip_status(ks->bwd[dtype][yg][ci](a, hipStream_t(stream)), "conv_backward");
 }
 
+e3_status e3_conv_backward_noalloc(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                   const int32_t* rowptr, const int32_t* sender,
+                                   const float* edge_vec_or_Y, const void* x, const void* w,
+                                   const void* dm, void* dx, void* dw, float* dY, e3_dtype dtype,
+                                   void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  const e3k::KernelSet* ks;
+  int G, ci;
+  if ((s = select(p, dtype, Kind::bwd, ks, G, ci)) != E3_OK) return s;
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes > e3k::kNoAllocMaxNodes || n_edges > e3k::kNoAllocMaxEdges)
+    return fail(E3_ERR_UNSUPPORTED,
+                "e3_conv_backward_noalloc takes at most " + std::to_string(e3k::kNoAllocMaxNodes) +
+                    " nodes and " + std::to_string(e3k::kNoAllocMaxEdges) + " edges (got " +
+                    std::to_string(n_nodes) + " and " + std::to_string(n_edges) +
+                    "); use e3_conv_prepare_transpose and e3_conv_backward");
+  if (n_nodes == 0) return ok();
+  if (!rowptr || !x || !dx || !dm) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (n_edges > 0 && (!sender || !edge_vec_or_Y || !w || !dw || !dY))
+    return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(x) || !aligned16(dm) || !aligned16(dx) ||
+      (n_edges > 0 && (!aligned16(w) || !aligned16(dw))))
+    return fail(E3_ERR_ALIGNMENT, "x, w, dm, dx and dw must be 16-byte aligned");
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
+  const e3k::TransposeLayout L = e3k::transpose_layout(n_nodes, n_edges);
+  if (L.total_words > e3k::noalloc_scratch_words())
+    return fail(E3_ERR_UNSUPPORTED, "the index does not fit the fixed scratch");
+  int* ws = nullptr;  // the fixed scratch of the current device
+  if ((s = hip_status(e3k::noalloc_scratch(&ws), "conv_backward_noalloc")) != E3_OK) return s;
+  const hipStream_t st = hipStream_t(stream);
+  const bool yg = (desc->flags & E3_Y_GIVEN) != 0;
+  // the sender-ordered index of this graph into the scratch (the previous
+  // call's contents are overwritten; every counter is cleared by a kernel)
+  if ((s = hip_status(e3k::launch_prepare_transpose(n_nodes, n_edges, rowptr, sender,
+                                                    (yg || n_edges == 0) ? nullptr : edge_vec_or_Y,
+                                                    ws, st),
+                      "conv_backward_noalloc")) != E3_OK)
+    return s;
+  e3k::BwdArgs a{n_nodes, p.C, G, ws + L.order, ws + L.colptr, ws + L.perm, ws + L.recv, ws + L.npad,
+                 ws + L.padlist, n_edges, edge_vec_or_Y, x, w, dm, dx, dw, dY};
+  return hip_status(ks->bwd[dtype][yg][ci](a, st), "conv_backward_noalloc");
+}
+
 namespace {
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }

@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "common.h"
 #include "harmonics_hi.h"
@@ -574,6 +575,49 @@ hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || n_nodes == 0) return err;
   return build_locality_order(n_nodes, n_edges, rowptr, sender, evec, ws, L, s);
+}
+
+// ------------------------------------------------ fixed scratch (no allocation)
+//
+// The index of e3_conv_backward_noalloc lives in one file-scope device array
+// sized for kNoAllocMaxNodes nodes and kNoAllocMaxEdges edges (each GPU the
+// library runs on holds its own copy until the process ends).  Host code
+// never uses the array's name as an address: its device address is fetched
+// once per device with hipGetSymbolAddress and kept.
+
+namespace {
+
+// transpose_layout's arrays at the limits (five per edge, nine per node, the
+// Morton cells twice, plus alignment); the entry point checks the layout of
+// every call against it
+constexpr int64_t kNoAllocWords =
+    (int64_t(5) * kNoAllocMaxEdges + int64_t(9) * kNoAllocMaxNodes +
+     2 * (int64_t(1) << kMortonBitsHost) + 16384 + 63) / 64 * 64;
+
+__device__ __align__(256) int scratch[kNoAllocWords];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+int64_t noalloc_scratch_words() { return kNoAllocWords; }
+
+hipError_t noalloc_scratch(int** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<int*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hipStream_t s) {

@@ -106,6 +106,12 @@ extern const KernelSet kSetL2to3PP;
 hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr, const int* sender,
                                     const float* evec, int* ws, hipStream_t s);
 hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hipStream_t s);
+// The fixed device scratch of the no-allocation backward: limits, its size in
+// int32 words, and its address on the current device (fetched once per device).
+constexpr int kNoAllocMaxNodes = 1 << 17;
+constexpr int kNoAllocMaxEdges = 1 << 22;
+int64_t noalloc_scratch_words();
+hipError_t noalloc_scratch(int** out);
 hipError_t launch_add(void* dst, const void* src, int64_t n, int bf16, hipStream_t s);
 
 // Tensor product from a coefficient table (generic.hip); the table layout

@@ -429,6 +429,24 @@ e3_status e3_conv_backward(const e3_desc* desc, int32_t n_nodes, int32_t n_edges
                            const void* w, const void* dm, void* dx, void* dw, float* dY,
                            e3_dtype dtype, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * backward as e3_conv_backward, with the sender-ordered index that
+ * e3_conv_prepare_transpose would build made inside the call, in a fixed
+ * device array the library holds on each GPU it runs on (87 MiB, for at
+ * most 131,072 nodes and 4,194,304 edges; larger graphs return
+ * E3_ERR_UNSUPPORTED).  No allocation of any kind happens in the call; the
+ * index is rebuilt every call (about the cost of e3_conv_prepare_transpose)
+ * and kept in the array until the next one.  rowptr and sender are required.
+ * Calls that overlap on one GPU (two streams, or two threads) share the array
+ * and race: serialise them.  Arguments, layouts and errors otherwise as
+ * e3_conv_backward; results are bitwise those of e3_conv_backward. */
+e3_status e3_conv_backward_noalloc(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                   const int32_t* rowptr, const int32_t* sender,
+                                   const float* edge_vec_or_Y, const void* x, const void* w,
+                                   const void* dm, void* dx, void* dw, float* dY, e3_dtype dtype,
+                                   void* stream);
+
 /* Number of weight matrices of the channel mixing from `in` to `out`: one
  * per (input block, output block) pair of equal degree and parity (host). */
 e3_status e3_linear_num_weights(const e3_irreps* in, const e3_irreps* out, int32_t* n_pairs);
