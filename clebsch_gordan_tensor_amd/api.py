@@ -54,9 +54,11 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_tp_forward_gemm", "e3_conv_forward_gemm",
            "e3_tp_backward_generic", "e3_conv_forward_generic", "e3_conv_backward_generic",
            "e3_conv_double_backward_generic", "e3_check_graph", "e3_check_graph_host", "e3_conv_backward_noalloc",
+           "e3_tp_backward_gemm", "e3_conv_backward_gemm",
            "e3_release_all",
            "e3_last_error"]
 E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY, E3_GEN_GEMM = 0, 1, 2, 3, 4
+E3_GEN_GEMM_DX, E3_GEN_GEMM_DW, E3_GEN_GEMM_DY = 5, 6, 7
 
 
 class _CRadial(C.Structure):
@@ -119,6 +121,10 @@ def lib():
     L.e3_conv_backward.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp,
                                    C.c_int, vp]
     L.e3_check_graph.argtypes = [i32, i32, vp, vp, vp]
+    L.e3_tp_backward_gemm.argtypes = [dp, i64, vp, sz, vp, sz, vp, sz, vp, vp, vp, vp, vp, vp, vp,
+                                      vp]
+    L.e3_conv_backward_gemm.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, sz, vp, sz, vp, sz, vp,
+                                        vp, vp, vp, vp, vp, vp, vp]
     L.e3_conv_backward_noalloc.argtypes = [dp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            C.c_int, vp]
     L.e3_check_graph_host.argtypes = [i32, i32, vp, vp]
@@ -715,6 +721,59 @@ def conv_forward_gemm(desc: Desc, rowptr, sender, edge_vec_or_Y, x, w, out=None,
                                       _ptr(plan), plan.numel() * 4, _ptr(Y), _ptr(x), _ptr(w),
                                       _ptr(out), _stream(stream)))
     return out
+
+
+def tp_backward_gemm(desc: Desc, x, y, w, dz, dx=None, dw=None, dy=None, stream=None):
+    """(dx, dw, dy) of tp_forward_gemm for the cotangent dz, as dense products
+    on the fp32 matrix cores (tables E3_GEN_GEMM_DX, _DW, _DY)."""
+    import torch
+    B = x.shape[0]
+    P = num_paths(desc)
+    f32 = torch.float32
+    _need(x, "x", shape=(B, desc.dx, desc.channels), dtype=f32)
+    _need(y, "y", shape=(B, desc.dy), dtype=f32)
+    _need(w, "w", shape=(B, P, desc.channels), dtype=f32)
+    _need(dz, "dz", shape=(B, desc.dout, desc.channels), dtype=f32)
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty_like(w) if dw is None else dw
+    dy = torch.empty_like(y) if dy is None else dy
+    for t, n, ref in ((dx, "dx", x), (dw, "dw", w), (dy, "dy", y)):
+        _need(t, n, shape=tuple(ref.shape), dtype=f32)
+    px, pw, py = (generic_plan(desc, x.device, t)
+                  for t in (E3_GEN_GEMM_DX, E3_GEN_GEMM_DW, E3_GEN_GEMM_DY))
+    _check(lib().e3_tp_backward_gemm(C.byref(desc.c()), B, _ptr(px), px.numel() * 4, _ptr(pw),
+                                     pw.numel() * 4, _ptr(py), py.numel() * 4, _ptr(x), _ptr(y),
+                                     _ptr(w), _ptr(dz), _ptr(dx), _ptr(dw), _ptr(dy),
+                                     _stream(stream)))
+    return dx, dw, dy
+
+
+def conv_backward_gemm(desc: Desc, rowptr, sender, workspace, Y, x, w, dm, dx=None, dw=None,
+                       dY=None, stream=None):
+    """(dx, dw, dY) of conv_forward_gemm with given harmonics (desc needs
+    E3_Y_GIVEN), as dense products on the fp32 matrix cores; workspace from
+    conv_prepare_transpose on the same graph."""
+    import torch
+    N, E = rowptr.numel() - 1, sender.numel()
+    P = num_paths(desc)
+    f32 = torch.float32
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    _need(Y, "Y", shape=(E, desc.dy), dtype=f32)
+    _need(x, "x", shape=(N, desc.dx, desc.channels), dtype=f32)
+    _need(w, "w", shape=(E, P, desc.channels), dtype=f32)
+    _need(dm, "dm", shape=(N, desc.dout, desc.channels), dtype=f32)
+    dx = torch.empty_like(x) if dx is None else dx
+    dw = torch.empty_like(w) if dw is None else dw
+    dY = torch.empty_like(Y) if dY is None else dY
+    px, pw, py = (generic_plan(desc, x.device, t)
+                  for t in (E3_GEN_GEMM_DX, E3_GEN_GEMM_DW, E3_GEN_GEMM_DY))
+    _check(lib().e3_conv_backward_gemm(C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender),
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _ptr(px), px.numel() * 4, _ptr(pw), pw.numel() * 4,
+                                       _ptr(py), py.numel() * 4, _ptr(Y), _ptr(x), _ptr(w),
+                                       _ptr(dm), _ptr(dx), _ptr(dw), _ptr(dY), _stream(stream)))
+    return dx, dw, dY
 
 
 def tp_backward_generic(desc: Desc, x, y, w, dz, stream=None):

@@ -2,6 +2,7 @@
 // and kernel launches.  No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -329,6 +330,7 @@ e3_status e3_tp_backward(const e3_desc* desc, int64_t n_rows, const void* x, con
   int G, ci;
   if ((s = select(p, dtype, Kind::tpb, ks, G, ci)) != E3_OK) return s;
   if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows > INT32_MAX) return fail(E3_ERR_UNSUPPORTED, "more than 2^31 - 1 rows");
   if (n_rows == 0) return ok();
   if (!x || !y || !w || !dz || !dx || !dw || !dy) return fail(E3_ERR_INVALID_ARG, "null pointer");
   if (!aligned16(x) || !aligned16(w) || !aligned16(dz) || !aligned16(dx) || !aligned16(dw))
@@ -1059,32 +1061,56 @@ e3_status build_generic(const e3_desc* desc, int table, std::vector<int32_t>& ou
 // K list concatenates, in path order, the x components (P, m1) of its paths
 // and pads to a multiple of 4; A[M][k] = sum_{m2} C_P[M][m1][m2] y[m2] is
 // listed as groups of (y component, c) records, one group per nonzero entry.
-e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemmArgs& d) {
+// Dense-product plans.  Each is one matrix product per block over a K list
+// of (path, input component) columns, A[k][M] built per row from y:
+//   kind 0 (E3_GEN_GEMM, the forward): blocks = output irreps (or paths
+//     with E3_OUT_PER_PATH), input x, out[o] += A w[P] x[xi];
+//   kind 1 (E3_GEN_GEMM_DX, the gradient of x): the same entries with the
+//     roles of x and the output swapped -- blocks = x irreps, input dz,
+//     dx[xi] += A w[P] dz[o] (A'[m1][(P,M)] = sum_m2 C_P[M][m1][m2] y[m2]);
+//   kind 2 (E3_GEN_GEMM_DW, the gradient of w): blocks = paths, input x,
+//     no weight: dw[P] = sum_M dz[oo_P + M] (A_P x)[M].
+// Every block owns its rows (a block no path reaches gets K = 0).
+e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& out,
+                          e3k::TpGemmArgs& d) {
   Parsed p;
   std::vector<GenEntry> ent;
   e3_status s = generic_entries(desc, p, ent, false);
   if (s != E3_OK) return s;
-  if (p.P > 32767 || p.dx > 65535) return fail(E3_ERR_UNSUPPORTED, "too many paths");
-  std::vector<int> xoff(p.x.size()), ooff(p.o.size());
+  if (p.P > 32767 || p.dx > 65535 || p.dout > 65535)
+    return fail(E3_ERR_UNSUPPORTED, "too many paths or components");
+  std::vector<int> xoff(p.x.size()), ooff(p.o.size()), oo_path(p.P);
   for (size_t i = 0, o = 0; i < p.x.size(); ++i) xoff[i] = int(o), o += 2 * p.x[i].l + 1;
   for (size_t i = 0, o = 0; i < p.o.size(); ++i) ooff[i] = int(o), o += 2 * p.o[i].l + 1;
-  const int nb = p.per_path ? p.P : int(p.o.size());
-  std::vector<int> b_oo(nb), b_rows(nb), b_kb(nb), b_K(nb), b_abase(nb);
-  std::vector<int> path_block(p.P), path_koff(p.P);
-  std::vector<std::vector<int>> bpaths(nb);
-  // every output block covers its own 2L+1 rows, also one no path reaches
-  // (collapsed mode): its K is 0, so the kernels write zeros there
-  if (!p.per_path)
-    for (int b = 0; b < nb; ++b) b_oo[b] = ooff[b], b_rows[b] = 2 * p.o[b].l + 1;
   for (int pi = 0, opp = 0; pi < p.P; ++pi) {
-    const int L = p.o[p.pio[pi]].l;
-    const int b = p.per_path ? pi : p.pio[pi];
-    path_block[pi] = b;
-    bpaths[b].push_back(pi);
-    b_rows[b] = 2 * L + 1;
-    b_oo[b] = p.per_path ? opp : ooff[p.pio[pi]];
-    opp += 2 * L + 1;
+    oo_path[pi] = p.per_path ? opp : ooff[p.pio[pi]];
+    opp += 2 * p.o[p.pio[pi]].l + 1;
   }
+  const bool per_path_blocks = kind == 2 || (kind == 0 && p.per_path);
+  const int nb = per_path_blocks ? p.P : kind == 1 ? int(p.x.size()) : int(p.o.size());
+  auto block_of = [&](int pi) { return per_path_blocks ? pi : kind == 1 ? p.pix[pi] : p.pio[pi]; };
+  auto in_off = [&](int pi) { return kind == 1 ? oo_path[pi] : xoff[p.pix[pi]]; };
+  auto in_width = [&](int pi) {
+    return 2 * (kind == 1 ? p.o[p.pio[pi]].l : p.x[p.pix[pi]].l) + 1;
+  };
+  auto out_comp = [&](const GenEntry& e) { return kind == 1 ? e.xi : e.o; };
+  auto in_comp = [&](const GenEntry& e) { return kind == 1 ? e.o : e.xi; };
+  std::vector<int> b_oo(nb), b_rows(nb), b_kb(nb), b_K(nb), b_abase(nb);
+  for (int b = 0; b < nb; ++b) {
+    if (per_path_blocks) {
+      b_oo[b] = oo_path[b];
+      b_rows[b] = 2 * p.o[p.pio[b]].l + 1;
+    } else if (kind == 1) {
+      b_oo[b] = xoff[b];
+      b_rows[b] = 2 * p.x[b].l + 1;
+    } else {
+      b_oo[b] = ooff[b];
+      b_rows[b] = 2 * p.o[b].l + 1;
+    }
+  }
+  std::vector<int> path_koff(p.P);
+  std::vector<std::vector<int>> bpaths(nb);
+  for (int pi = 0; pi < p.P; ++pi) bpaths[block_of(pi)].push_back(pi);
   std::vector<int32_t> klist;
   int abase = 0;
   for (int b = 0; b < nb; ++b) {
@@ -1093,9 +1119,8 @@ e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemm
     int k = 0;
     for (int pi : bpaths[b]) {
       path_koff[pi] = k;
-      const int n1 = 2 * p.x[p.pix[pi]].l + 1;
-      for (int m1 = 0; m1 < n1; ++m1) klist.push_back((pi << 16) | (xoff[p.pix[pi]] + m1));
-      k += n1;
+      for (int m = 0; m < in_width(pi); ++m) klist.push_back((pi << 16) | (in_off(pi) + m));
+      k += in_width(pi);
     }
     while (k % 4) klist.push_back(-1), ++k;
     b_K[b] = k;
@@ -1109,9 +1134,9 @@ e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemm
   std::vector<GE> ge;
   ge.reserve(ent.size());
   for (const GenEntry& e : ent) {
-    const int b = path_block[e.P];
-    const int M = e.o - b_oo[b];
-    const int k = path_koff[e.P] + (e.xi - xoff[p.pix[e.P]]);
+    const int b = block_of(e.P);
+    const int M = out_comp(e) - b_oo[b];
+    const int k = path_koff[e.P] + (in_comp(e) - in_off(e.P));
     ge.push_back(GE{b_abase[b] + k * b_rows[b] + M, e.yi, e.c});  // A[k][M]
   }
   std::stable_sort(ge.begin(), ge.end(), [](const GE& a, const GE& b) { return a.at < b.at; });
@@ -1131,11 +1156,13 @@ e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemm
     i = j;
   }
   const int n_groups = int(groups.size() / 4);
+  // the kernel's view: input components (dx), output components (dout)
+  const int in_dim = kind == 1 ? p.dout : p.dx, out_dim = kind == 1 ? p.dx : p.dout;
   d = e3k::TpGemmArgs{};
   d.n_blocks = nb;
-  d.dx = p.dx;
+  d.dx = in_dim;
   d.dy = p.dy;
-  d.dout = p.dout;
+  d.dout = out_dim;
   d.P = p.P;
   d.n_klist = int(klist.size());
   d.n_groups = n_groups;
@@ -1145,10 +1172,10 @@ e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemm
   d.off_groups = (d.off_klist + d.n_klist + 3) / 4 * 4;  // 16-byte entries
   d.plan_words = d.off_groups + int(groups.size());
   out.assign(size_t(d.plan_words), 0);
-  const int32_t head[14] = {e3k::kGemmMagic, nb,         p.dx,         p.dy,
-                            p.dout,          p.P,        d.n_klist,    n_groups,
-                            0,               d.a_floats, d.off_blocks, d.off_klist,
-                            d.off_groups,    d.plan_words};
+  const int32_t head[14] = {e3k::kGemmMagic + kind, nb,      in_dim,       p.dy,
+                            out_dim,           p.P,          d.n_klist,    n_groups,
+                            0,                 d.a_floats,   d.off_blocks, d.off_klist,
+                            d.off_groups,      d.plan_words};
   std::copy(head, head + 14, out.begin());
   for (int b = 0; b < nb; ++b) {
     out[d.off_blocks + 4 * b] = b_oo[b];
@@ -1161,12 +1188,100 @@ e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemm
   return ok();
 }
 
+e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemmArgs& d) {
+  return build_gemm_kind(desc, 0, out, d);
+}
+
+// The gradient of y (E3_GEN_GEMM_DY): per row and x irrep i,
+//   G_i[(P,M)][m1] = sum_q w[P][q] dz[oo_P + M][q] x[xoff_i + m1][q]
+// (rows: the (path, M) pairs of the paths from x irrep i, in path order,
+// padded to a multiple of 16; columns m1 < 16), then
+//   dy[yi] = sum over the CG entries (P, M, m1, yi, c) of c G_i[(P,M)][m1].
+// Layout: header kGemmHeader words (magic + 7, n_blocks, dx, dy, dout, P,
+// n_rows, n_ent, 0, 0, off_blocks, off_rows, off_yptr, off_yent, words);
+// blocks [nb][4]: x offset, columns (2l1+1), first G row, rows (x16);
+// rows [n_rows]: (P << 16) | dz component, -1 for padding; yptr [dy+1];
+// yent [n_ent][2]: G index (row * 16 + column), coefficient bits -- the
+// entries of each y component in a fixed order.
+e3_status build_gemm_dy(const e3_desc* desc, std::vector<int32_t>& out, int* dims) {
+  Parsed p;
+  std::vector<GenEntry> ent;
+  e3_status s = generic_entries(desc, p, ent, false);
+  if (s != E3_OK) return s;
+  if (p.P > 32767 || p.dx > 65535 || p.dout > 65535)
+    return fail(E3_ERR_UNSUPPORTED, "too many paths or components");
+  std::vector<int> xoff(p.x.size()), ooff(p.o.size()), oo_path(p.P);
+  for (size_t i = 0, o = 0; i < p.x.size(); ++i) xoff[i] = int(o), o += 2 * p.x[i].l + 1;
+  for (size_t i = 0, o = 0; i < p.o.size(); ++i) ooff[i] = int(o), o += 2 * p.o[i].l + 1;
+  for (int pi = 0, opp = 0; pi < p.P; ++pi) {
+    oo_path[pi] = p.per_path ? opp : ooff[p.pio[pi]];
+    opp += 2 * p.o[p.pio[pi]].l + 1;
+  }
+  const int nb = int(p.x.size());
+  std::vector<int> b_row0(nb), b_nrows(nb), path_row(p.P);
+  std::vector<int32_t> rows;
+  for (int b = 0; b < nb; ++b) {
+    if (2 * p.x[b].l + 1 > 16) return fail(E3_ERR_UNSUPPORTED, "x degree above 7");
+    b_row0[b] = int(rows.size());
+    for (int pi = 0; pi < p.P; ++pi) {
+      if (p.pix[pi] != b) continue;
+      path_row[pi] = int(rows.size());
+      for (int M = 0; M < 2 * p.o[p.pio[pi]].l + 1; ++M) rows.push_back((pi << 16) | (oo_path[pi] + M));
+    }
+    while ((rows.size() - b_row0[b]) % 16) rows.push_back(-1);
+    b_nrows[b] = int(rows.size()) - b_row0[b];
+  }
+  std::vector<std::vector<std::pair<int, float>>> by_y(p.dy);
+  for (const GenEntry& e : ent) {
+    const int b = p.pix[e.P];
+    const int row = path_row[e.P] + (e.o - oo_path[e.P]);
+    by_y[e.yi].push_back({row * 16 + (e.xi - xoff[b]), e.c});
+  }
+  const int off_blocks = e3k::kGemmHeader, off_rows = off_blocks + 4 * nb;
+  const int off_yptr = off_rows + int(rows.size());
+  const int off_yent = off_yptr + p.dy + 1;
+  int n_ent = 0;
+  for (const auto& v : by_y) n_ent += int(v.size());
+  const int words = off_yent + 2 * n_ent;
+  out.assign(size_t(words), 0);
+  const int32_t head[14] = {e3k::kGemmMagic + 7, nb, p.dx, p.dy, p.dout, p.P, int(rows.size()),
+                            n_ent, 0, 0, off_blocks, off_rows, off_yptr, words};
+  std::copy(head, head + 14, out.begin());
+  out[e3k::kGemmHeader - 2] = off_yent;  // the header's last spare word
+  for (int b = 0; b < nb; ++b) {
+    out[off_blocks + 4 * b] = xoff[b];
+    out[off_blocks + 4 * b + 1] = 2 * p.x[b].l + 1;
+    out[off_blocks + 4 * b + 2] = b_row0[b];
+    out[off_blocks + 4 * b + 3] = b_nrows[b];
+  }
+  std::copy(rows.begin(), rows.end(), out.begin() + off_rows);
+  int k = 0;
+  for (int y = 0; y < p.dy; ++y) {
+    out[off_yptr + y] = k;
+    for (const auto& [g, c] : by_y[y]) {
+      int32_t cb;
+      std::memcpy(&cb, &c, 4);
+      out[off_yent + 2 * k] = g;
+      out[off_yent + 2 * k + 1] = cb;
+      ++k;
+    }
+  }
+  out[off_yptr + p.dy] = k;
+  if (dims) {
+    dims[0] = nb;
+    dims[1] = int(rows.size());
+    dims[2] = n_ent;
+    dims[3] = words;
+  }
+  return ok();
+}
+
 // The plan's sizes per descriptor, built once (the kernel takes them from
 // the host, not from the caller's device copy).
 std::mutex g_plan_mu;
 std::map<std::string, std::pair<e3k::TpGemmArgs, size_t>> g_plan_cache;
 
-e3_status gemm_dims(const e3_desc* desc, e3k::TpGemmArgs& d, size_t& bytes) {
+e3_status gemm_dims(const e3_desc* desc, e3k::TpGemmArgs& d, size_t& bytes, int kind = 0) {
   std::mutex& mu = g_plan_mu;
   auto& cache = g_plan_cache;
   std::string key;
@@ -1178,7 +1293,7 @@ e3_status gemm_dims(const e3_desc* desc, e3k::TpGemmArgs& d, size_t& bytes) {
              (v->v[i].parity > 0 ? "e" : "o") + ",";
     key += "|";
   }
-  key += std::to_string(desc->flags & E3_OUT_PER_PATH);
+  key += std::to_string(desc->flags & E3_OUT_PER_PATH) + "/" + std::to_string(kind);
   {
     std::lock_guard<std::mutex> g(mu);
     auto it = cache.find(key);
@@ -1189,7 +1304,7 @@ e3_status gemm_dims(const e3_desc* desc, e3k::TpGemmArgs& d, size_t& bytes) {
     }
   }
   std::vector<int32_t> words;
-  e3_status s = build_gemm(desc, words, d);
+  e3_status s = build_gemm_kind(desc, kind, words, d);
   if (s != E3_OK) return s;
   bytes = words.size() * 4;
   std::lock_guard<std::mutex> g(mu);
@@ -1198,10 +1313,12 @@ e3_status gemm_dims(const e3_desc* desc, e3k::TpGemmArgs& d, size_t& bytes) {
 }
 
 e3_status build_table(const e3_desc* desc, int table, std::vector<int32_t>& out) {
-  if (table == E3_GEN_GEMM) {
+  if (table == E3_GEN_GEMM || table == E3_GEN_GEMM_DX || table == E3_GEN_GEMM_DW) {
     e3k::TpGemmArgs d;
-    return build_gemm(desc, out, d);
+    return build_gemm_kind(desc, table == E3_GEN_GEMM ? 0 : table == E3_GEN_GEMM_DX ? 1 : 2, out,
+                           d);
   }
+  if (table == E3_GEN_GEMM_DY) return build_gemm_dy(desc, out, nullptr);
   return build_generic(desc, table, out);
 }
 
@@ -1312,6 +1429,244 @@ e3_status e3_tp_forward_gemm(const e3_desc* desc, int64_t n_rows, const void* pl
   return hip_status(e3k::launch_tp_gemm(a, hipStream_t(stream)), "tp_forward_gemm");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Sizes of the dense backward's dy plan per descriptor (built once).
+struct DyDims {
+  int n_blocks, n_grows, n_ent, words, off_rows, off_yptr, off_yent;
+};
+std::map<std::string, DyDims> g_dy_cache;
+
+e3_status gemm_dy_dims(const e3_desc* desc, DyDims& d) {
+  std::string key;
+  for (const e3_irreps* v : {&desc->x, &desc->y, &desc->out}) {
+    if (v->n < 0 || (v->n > 0 && !v->v)) return fail(E3_ERR_IRREPS, "bad irreps list");
+    for (int i = 0; i < v->n; ++i)
+      key += std::to_string(v->v[i].mul) + "x" + std::to_string(v->v[i].l) +
+             (v->v[i].parity > 0 ? "e" : "o") + ",";
+    key += "|";
+  }
+  key += std::to_string(desc->flags & E3_OUT_PER_PATH);
+  {
+    std::lock_guard<std::mutex> g(g_plan_mu);
+    auto it = g_dy_cache.find(key);
+    if (it != g_dy_cache.end()) {
+      d = it->second;
+      return ok();
+    }
+  }
+  std::vector<int32_t> words;
+  int dims[4];
+  e3_status s = build_gemm_dy(desc, words, dims);
+  if (s != E3_OK) return s;
+  d = DyDims{dims[0], dims[1], dims[2], dims[3], words[11], words[12], words[14]};
+  std::lock_guard<std::mutex> g(g_plan_mu);
+  g_dy_cache[key] = d;
+  return ok();
+}
+
+// Widest channel slab (CS | C, CS <= 128) whose LDS leaves two workgroups per
+// CU, else one; 0 when none fits.
+template <class F>
+int pick_slab(int C, F lds_of) {
+  for (size_t cap : {size_t(80) * 1024, size_t(160) * 1024})
+    for (int cs : {128, 64, 32, 16})
+      if (cs <= C && C % cs == 0 && lds_of(cs) <= cap) return cs;
+  return 0;
+}
+
+// The three plans of the dense backward checked against the descriptor and
+// set up: dx (TpGemmArgs on dz), dw and dy (GemmBwdArgs).
+e3_status gemm_backward_setup(const e3_desc* desc, const Parsed& p, const void* plan_dx,
+                              size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+                              const void* plan_dy, size_t dy_bytes, e3k::TpGemmArgs& tdx,
+                              e3k::GemmBwdArgs& bdw, e3k::GemmBwdArgs& bdy) {
+  e3_status s;
+  size_t need_dx = 0, need_dw = 0;
+  if ((s = gemm_dims(desc, tdx, need_dx, 1)) != E3_OK) return s;
+  bdw = e3k::GemmBwdArgs{};
+  if ((s = gemm_dims(desc, bdw.t, need_dw, 2)) != E3_OK) return s;
+  DyDims dd;
+  if ((s = gemm_dy_dims(desc, dd)) != E3_OK) return s;
+  if (p.C % 16) return fail(E3_ERR_UNSUPPORTED, "the dense-product kernels need C % 16 == 0");
+  if (!plan_dx || dx_bytes < need_dx || !plan_dw || dw_bytes < need_dw || !plan_dy ||
+      dy_bytes < size_t(dd.words) * 4)
+    return fail(E3_ERR_INVALID_ARG,
+                "plans need " + std::to_string(need_dx) + ", " + std::to_string(need_dw) + " and " +
+                    std::to_string(size_t(dd.words) * 4) +
+                    " bytes (tables E3_GEN_GEMM_DX, _DW, _DY of this descriptor)");
+  if (!aligned16(plan_dx) || !aligned16(plan_dw) || !aligned16(plan_dy))
+    return fail(E3_ERR_ALIGNMENT, "the plans must be 16-byte aligned");
+  tdx.C = bdw.t.C = p.C;
+  tdx.CS = pick_slab(p.C, [&](int cs) {
+    e3k::TpGemmArgs t = tdx;
+    t.CS = cs;
+    return e3k::tp_gemm_lds_bytes(t);
+  });
+  bdw.t.CS = pick_slab(p.C, [&](int cs) {
+    e3k::TpGemmArgs t = bdw.t;
+    t.CS = cs;
+    return e3k::gemm_dw_lds_bytes(t);
+  });
+  bdy = e3k::GemmBwdArgs{};
+  bdy.t.n_blocks = dd.n_blocks;
+  bdy.t.dx = p.dx;
+  bdy.t.dy = p.dy;
+  bdy.t.dout = p.dout;
+  bdy.t.P = p.P;
+  bdy.t.C = p.C;
+  bdy.t.off_blocks = e3k::kGemmHeader;
+  bdy.n_grows = dd.n_grows;
+  bdy.n_ent = dd.n_ent;
+  bdy.off_rows = dd.off_rows;
+  bdy.off_yptr = dd.off_yptr;
+  bdy.off_yent = dd.off_yent;
+  bdy.t.CS = pick_slab(p.C, [&](int cs) {
+    e3k::GemmBwdArgs t = bdy;
+    t.t.CS = cs;
+    return e3k::gemm_dy_lds_bytes(t);
+  });
+  if (!tdx.CS || !bdw.t.CS || !bdy.t.CS)
+    return fail(E3_ERR_UNSUPPORTED, "a dense-product backward plan does not fit in LDS");
+  const int XS = e3k::gemm_row_stride(std::max(tdx.CS, bdw.t.CS));
+  if ((p.P + 1) * XS > 65535 || std::max(p.dx, p.dout) * XS > 65535 ||
+      std::max(p.P, p.dout) * (bdy.t.CS + 4) > 65535)
+    return fail(E3_ERR_UNSUPPORTED, "too many components or paths for the dense-product kernels");
+  tdx.lds_bytes = e3k::tp_gemm_lds_bytes(tdx);
+  bdw.t.lds_bytes = e3k::gemm_dw_lds_bytes(bdw.t);
+  bdy.t.lds_bytes = e3k::gemm_dy_lds_bytes(bdy);
+  tdx.plan = static_cast<const int*>(plan_dx);
+  bdw.t.plan = static_cast<const int*>(plan_dw);
+  bdy.t.plan = static_cast<const int*>(plan_dy);
+  return E3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+e3_status e3_tp_backward_gemm(const e3_desc* desc, int64_t n_rows, const void* plan_dx,
+                              size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+                              const void* plan_dy, size_t dy_bytes, const float* x, const float* y,
+                              const float* w, const float* dz, float* dx, float* dw, float* dy,
+                              void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  e3k::TpGemmArgs tdx;
+  e3k::GemmBwdArgs bdw, bdy;
+  if ((s = gemm_backward_setup(desc, p, plan_dx, dx_bytes, plan_dw, dw_bytes, plan_dy, dy_bytes,
+                               tdx, bdw, bdy)) != E3_OK)
+    return s;
+  if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows > INT32_MAX) return fail(E3_ERR_UNSUPPORTED, "more than 2^31 - 1 rows");
+  if (n_rows == 0) return ok();
+  if (!x || !y || !w || !dz || !dx || !dw || !dy) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(dz))
+    return fail(E3_ERR_ALIGNMENT, "x, w and dz must be 16-byte aligned");
+  const hipStream_t st = hipStream_t(stream);
+  // dx: the forward's product with the roles of x and the output swapped
+  tdx.n_rows = n_rows;
+  tdx.x = dz;
+  tdx.y = y;
+  tdx.w = w;
+  tdx.z = dx;
+  if ((s = hip_status(e3k::launch_tp_gemm(tdx, st), "tp_backward_gemm")) != E3_OK) return s;
+  for (e3k::GemmBwdArgs* b : {&bdw, &bdy}) {
+    b->t.n_rows = n_rows;
+    b->t.x = x;
+    b->t.y = y;
+    b->t.w = w;
+    b->dz = dz;
+    b->n_x = int(n_rows);
+    b->n_zrows = b->n_x;
+  }
+  bdw.out = dw;
+  bdy.out = dy;
+  if ((s = hip_status(e3k::launch_gemm_dw(bdw, st), "tp_backward_gemm")) != E3_OK) return s;
+  return hip_status(e3k::launch_gemm_dy(bdy, st), "tp_backward_gemm");
+}
+
+e3_status e3_conv_backward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                const int32_t* rowptr, const int32_t* sender,
+                                const void* workspace, size_t ws_bytes, const void* plan_dx,
+                                size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+                                const void* plan_dy, size_t dy_bytes, const float* Y,
+                                const float* x, const float* w, const float* dm, float* dx,
+                                float* dw, float* dY, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if (!(desc->flags & E3_Y_GIVEN))
+    return fail(E3_ERR_UNSUPPORTED,
+                "the dense-product backward takes given harmonics (E3_Y_GIVEN); form them with "
+                "e3_spherical_harmonics and chain dY with e3_spherical_harmonics_backward");
+  if (p.per_path) return fail(E3_ERR_UNSUPPORTED, "the dense-product convolution has collapsed outputs");
+  e3k::TpGemmArgs tdx;
+  e3k::GemmBwdArgs bdw, bdy;
+  if ((s = gemm_backward_setup(desc, p, plan_dx, dx_bytes, plan_dw, dw_bytes, plan_dy, dy_bytes,
+                               tdx, bdw, bdy)) != E3_OK)
+    return s;
+  if (tdx.n_blocks > 8) return fail(E3_ERR_UNSUPPORTED, "more than 8 x irreps");
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes == 0) return ok();
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
+  size_t need = 0;
+  e3_conv_workspace_size(n_nodes, n_edges, &need);
+  if (!workspace || ws_bytes < need)
+    return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  if (!rowptr || !x || !dm || !dx) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (n_edges > 0 && (!sender || !Y || !w || !dw || !dY))
+    return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(x) || !aligned16(dm) || (n_edges > 0 && !aligned16(w)))
+    return fail(E3_ERR_ALIGNMENT, "x, w and dm must be 16-byte aligned");
+  if (tdx.CS > 64) {  // the convolution's dense kernel keeps one 16-channel tile per wavefront
+    tdx.CS = 64;
+    tdx.lds_bytes = e3k::tp_gemm_lds_bytes(tdx) + 4 * e3k::kConvGemmExtraWords;
+  } else {
+    tdx.lds_bytes += 4 * e3k::kConvGemmExtraWords;
+  }
+  if (p.C % tdx.CS || tdx.lds_bytes > 160 * 1024)
+    return fail(E3_ERR_UNSUPPORTED, "the dense-product plan does not fit in LDS");
+  const e3k::TransposeLayout L = e3k::transpose_layout(n_nodes, n_edges);
+  const int* ws = static_cast<const int*>(workspace);
+  const hipStream_t st = hipStream_t(stream);
+  // dx: per sender over its out-edges (the transposed index), operand dm
+  e3k::ConvGemmArgs a{};
+  a.t = tdx;
+  a.t.x = dm;
+  a.t.y = Y;
+  a.t.w = w;
+  a.t.z = dx;
+  a.n_nodes = n_nodes;
+  a.n_edges = n_edges;
+  a.rowptr = ws + L.colptr;
+  a.sender = ws + L.recv;
+  a.perm = ws + L.perm;
+  a.m = dx;
+  a.ly = -1;
+  std::memset(&a.ym, 0xff, sizeof a.ym);
+  if ((s = hip_status(e3k::launch_conv_gemm(a, st), "conv_backward_gemm")) != E3_OK) return s;
+  if (n_edges == 0) return ok();
+  for (e3k::GemmBwdArgs* b : {&bdw, &bdy}) {
+    b->t.n_rows = n_edges;
+    b->t.x = x;
+    b->t.y = Y;
+    b->t.w = w;
+    b->dz = dm;
+    b->xrow = sender;
+    b->rowptr = rowptr;
+    b->n_x = n_nodes;
+    b->n_zrows = n_nodes;
+  }
+  bdw.out = dw;
+  bdy.out = dY;
+  if ((s = hip_status(e3k::launch_gemm_dw(bdw, st), "conv_backward_gemm")) != E3_OK) return s;
+  return hip_status(e3k::launch_gemm_dy(bdy, st), "conv_backward_gemm");
+}
+
 e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
                                const int32_t* rowptr, const int32_t* sender, const void* plan,
                                size_t plan_bytes, const float* edge_vec_or_Y, const float* x,
@@ -1390,6 +1745,7 @@ e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void
   e3_status s = generic_parse(desc, dtype, p);
   if (s != E3_OK) return s;
   if (n_rows < 0) return fail(E3_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows > INT32_MAX) return fail(E3_ERR_UNSUPPORTED, "more than 2^31 - 1 rows");
   if (n_rows == 0) return ok();
   if (!x || !y || !w || !dz || !dx || !dw || !dy) return fail(E3_ERR_INVALID_ARG, "null pointer");
   const GenDims dyd = generic_dims(p, E3_GEN_DY), dxd = generic_dims(p, E3_GEN_DX),
@@ -1578,6 +1934,7 @@ e3_status e3_check_graph_host(int32_t n_nodes, int32_t n_edges, const int32_t* r
 void e3_release_all(void) {
   std::lock_guard<std::mutex> g(g_plan_mu);
   g_plan_cache.clear();
+  g_dy_cache.clear();
 }
 
 }  // extern "C"

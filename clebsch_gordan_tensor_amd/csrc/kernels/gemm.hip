@@ -315,17 +315,25 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
   };
   float4v pre[PRE > 0 ? PRE : 1];
   float ypre = 0.0f;
-  // a sender outside [0, n_nodes) marks a padding edge
-  auto sender_of = [&](int e) {
-    const int a = cg.sender[e];
-    return a >= 0 && a < cg.n_nodes ? a : -1;
+  // the edge id of CSR position j (its w and Y rows): j itself, or perm[j]
+  // when the walk runs over another order (the transposed index); -1 when
+  // perm names no edge
+  auto edge_id = [&](int j) {
+    if (!cg.perm) return j;
+    const int e = cg.perm[j];
+    return e >= 0 && e < cg.n_edges ? e : -1;
   };
-  auto prefetch = [&](int e, int c0) {
-    const int a = max(sender_of(e), 0);
+  // a sender outside [0, n_nodes) marks a padding edge
+  auto sender_of = [&](int j) {
+    const int a = cg.sender[j];
+    return a >= 0 && a < cg.n_nodes && edge_id(j) >= 0 ? a : -1;
+  };
+  auto prefetch = [&](int j, int c0) {
+    const int a = max(sender_of(j), 0), e = max(edge_id(j), 0);
 #pragma unroll
-    for (int j = 0; j < PRE; ++j) {
-      const int u = threadIdx.x + 256 * j;
-      if (u < U) pre[j] = *reinterpret_cast<const float4v*>(unit_src(u, e, a, c0));
+    for (int i = 0; i < PRE; ++i) {
+      const int u = threadIdx.x + 256 * i;
+      if (u < U) pre[i] = *reinterpret_cast<const float4v*>(unit_src(u, e, a, c0));
     }
     if (!vec_y && threadIdx.x < g.dy) ypre = g.y[int64_t(e) * g.dy + threadIdx.x];
   };
@@ -340,12 +348,13 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) D[b][u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
     if (PRE > 0 && e_lo < e_hi) prefetch(e_lo, c0);
-    for (int e = e_lo; e < e_hi; ++e) {
-      const int a = sender_of(e);
+    for (int j = e_lo; j < e_hi; ++j) {
+      const int a = sender_of(j);
       if (a < 0) {  // padding edge (the same for the whole workgroup): nothing to add
-        if (PRE > 0 && e + 1 < e_hi) prefetch(e + 1, c0);
+        if (PRE > 0 && j + 1 < e_hi) prefetch(j + 1, c0);
         continue;
       }
+      const int e = edge_id(j);
       __syncthreads();  // the previous edge's LDS reads are done (and s_k is written)
 #pragma unroll
       for (int j = 0; j < PRE; ++j) {
@@ -369,7 +378,7 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
         s_a[at] = fmaf(__int_as_float(en.w), yval(y2), __int_as_float(en.z) * yval(y1));
       }
       __syncthreads();
-      if (PRE > 0 && e + 1 < e_hi) prefetch(e + 1, c0);
+      if (PRE > 0 && j + 1 < e_hi) prefetch(j + 1, c0);
       if (!active) continue;  // the same for the whole wavefront
       const float* sw = s_w + 16 * wave + li;
       const float* sx = s_x + 16 * wave + li;
@@ -398,6 +407,213 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
           }
         }
       }
+    }
+  }
+}
+
+// Receiver of edge e in a CSR by receiver: the largest b with rowptr[b] <= e
+// (so empty rows are passed over), clamped to [0, n_nodes).
+__host__ __device__ constexpr int gemm_dy_row_stride(int CS) { return CS + 4; }
+
+__device__ __forceinline__ int receiver_of(const int* __restrict__ rowptr, int n_nodes, int64_t e) {
+  int lo = 0, hi = n_nodes;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (rowptr[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  return min(lo, n_nodes - 1);
+}
+
+// The gradient of w in the dense form (plan E3_GEN_GEMM_DW: one block per
+// path P, K over its m1): per row (or edge) and path,
+//   dw[P][q] = sum_M dz[oo_P + M][q] (A_P x)[M][q],
+// (A_P x) on the fp32 matrix cores as in k_tp_gemm with a weight of one, the
+// sum over M as the product's epilogue: each lane adds its four rows, then
+// the four row groups of a column (lanes li, li + 16, li + 32, li + 48) in a
+// fixed butterfly.  One workgroup per (row, slab of CS channels).
+template <int NU>
+__global__ void __launch_bounds__(256) k_gemm_dw(GemmBwdArgs a) {
+  extern __shared__ __align__(16) float gsm[];
+  const TpGemmArgs& g = a.t;
+  const int* __restrict__ blocks = g.plan + g.off_blocks;
+  const int* __restrict__ klist = g.plan + g.off_klist;
+  const int4* __restrict__ groups = reinterpret_cast<const int4*>(g.plan + g.off_groups);
+  const int CS = g.CS, C = g.C, XS = gemm_row_stride(CS);
+  const int lg4 = __builtin_ctz(CS / 4);
+  float* s_a = gsm;
+  float* s_x = s_a + g.a_floats;
+  float* s_w = s_x + g.dx * XS;  // a row of ones (real columns) and a row of zeros (padding)
+  float* s_y = s_w + 2 * XS;
+  int* s_k = reinterpret_cast<int*>(s_y + g.dy);
+  for (int i = threadIdx.x; i < g.n_klist; i += 256) {
+    const int ent = klist[i];
+    const int xi = ent < 0 ? 0 : min(ent & 0xFFFF, g.dx - 1);
+    s_k[i] = (ent < 0 ? XS : 0) | (xi * XS) << 16;
+  }
+  for (int i = threadIdx.x; i < XS; i += 256) {
+    s_w[i] = 1.0f;
+    s_w[XS + i] = 0.0f;
+  }
+  for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, kq = lane >> 4;
+  const int n_slabs = C / CS, n_tiles = CS / 16;
+  const bool active = wave < n_tiles;
+  const int64_t n_items = g.n_rows * n_slabs;
+  const int U = g.dx << lg4;
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int64_t row = item / n_slabs;
+    const int c0 = int(item - row * n_slabs) * CS;
+    const int xr = a.xrow ? a.xrow[row] : int(row);
+    float* dwr = a.out + row * g.P * C + c0;
+    __syncthreads();  // the previous item's LDS reads are done (and s_k is written)
+    if (xr < 0 || xr >= a.n_x) {  // padding edge (uniform): zero gradient
+      for (int i = threadIdx.x; i < g.P * CS; i += 256) dwr[(i / CS) * C + i % CS] = 0.0f;
+      continue;
+    }
+    const int64_t zr = a.rowptr ? receiver_of(a.rowptr, a.n_zrows, row) : row;
+    for (int u = threadIdx.x; u < U; u += 256) {
+      const int r = u >> lg4, c = 4 * (u & ((1 << lg4) - 1));
+      *reinterpret_cast<float4v*>(s_x + r * XS + c) =
+          *reinterpret_cast<const float4v*>(g.x + (int64_t(xr) * g.dx + r) * C + c0 + c);
+    }
+    for (int i = threadIdx.x; i < g.dy; i += 256) s_y[i] = g.y[row * g.dy + i];
+    __syncthreads();
+#pragma unroll 4
+    for (int q = threadIdx.x; q < g.n_groups; q += 256) {
+      const int4 e = groups[q];
+      const int at = min(max(e.x, 0), g.a_floats - 1);
+      const int y1 = min(e.y & 0xFFFF, g.dy - 1), y2 = min((e.y >> 16) & 0xFFFF, g.dy - 1);
+      s_a[at] = fmaf(__int_as_float(e.w), s_y[y2], __int_as_float(e.z) * s_y[y1]);
+    }
+    __syncthreads();
+    if (!active) continue;
+    const float* dzr = a.dz + zr * g.dout * C + c0;
+    int abase = 0;
+    for (int b = 0; b < g.n_blocks; ++b) {
+      const int oo = blocks[4 * b], rows = min(max(blocks[4 * b + 1], 1), 16);
+      const int kb = min(max(blocks[4 * b + 2], 0), g.n_klist);
+      const int K = min(max(blocks[4 * b + 3], 0), g.n_klist - kb) & ~3;
+      if (abase + rows * K > g.a_floats) break;
+      const bool aok = li < rows;
+      const float* ap = s_a + abase + kq * rows + min(li, rows - 1);
+      const int* kp = s_k + kb + kq;
+      float4v D[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) D[u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      gemm_ksteps<NU>(D, ap, kp, rows, aok, K, s_w + li, s_x + 16 * wave + li);
+      // D[u][r]: row M = 4 kq + r, channel 16 (wave + 4u) + li
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int c = 16 * (wave + 4 * u) + li;
+        float part = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * kq + r, o = oo + i;
+          if (i < rows && o >= 0 && o < g.dout) part = fmaf(dzr[int64_t(o) * C + c], D[u][r], part);
+        }
+        part += shfl_xor_c<16>(part);
+        part += shfl_xor_c<32>(part);
+        if (kq == 0 && b < g.P) dwr[int64_t(b) * C + c] = part;
+      }
+      abase += rows * K;
+    }
+  }
+}
+
+// The gradient of y in the dense form (plan E3_GEN_GEMM_DY): per row (or
+// edge), one workgroup over every channel slab in turn:
+//   G_i[(P,M)][m1] = sum_q w[P][q] dz[oo_P + M][q] x[xoff_i + m1][q]
+// on the fp32 matrix cores with the channel sum as the product's K (the A
+// operand w dz formed per lane from the staged slabs, B = x), 16-row tiles
+// of G owned by one wavefront each and added up over the slabs in LDS, then
+// dy[yi] = sum of c G over the plan's entries of yi, in the plan's order.
+__global__ void __launch_bounds__(256) k_gemm_dy(GemmBwdArgs a) {
+  extern __shared__ __align__(16) float gsm[];
+  const TpGemmArgs& g = a.t;
+  const int* __restrict__ blocks = g.plan + g.off_blocks;
+  const int* __restrict__ grows = g.plan + a.off_rows;
+  const int* __restrict__ yptr = g.plan + a.off_yptr;
+  const int* __restrict__ yent = g.plan + a.off_yent;
+  // rows staged with a stride of 4 (mod 32) floats: a K step reads 16 rows
+  // at four consecutive channels, which then fall in distinct banks
+  const int CS = g.CS, C = g.C, XS = gemm_dy_row_stride(CS);
+  const int lg4 = __builtin_ctz(CS / 4);
+  float* s_x = gsm;
+  float* s_w = s_x + g.dx * XS;
+  float* s_z = s_w + g.P * XS;
+  float* s_g = s_z + g.dout * XS;                          // G [n_grows][16]
+  int* s_r = reinterpret_cast<int*>(s_g + a.n_grows * 16);  // per G row: w and dz offsets
+  int* s_b = s_r + a.n_grows;                               // per G row: x block offset, columns
+  for (int i = threadIdx.x; i < a.n_grows; i += 256) {
+    const int ent = grows[i];
+    const int P = ent < 0 ? 0 : min(ent >> 16, g.P - 1);
+    const int o = ent < 0 ? 0 : min(ent & 0xFFFF, g.dout - 1);
+    s_r[i] = ent < 0 ? -1 : (P * XS) | (o * XS) << 16;
+    s_b[i] = 0;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < g.n_blocks; b += 256) {
+    const int xo = min(max(blocks[4 * b], 0), g.dx - 1);
+    const int nc = min(max(blocks[4 * b + 1], 0), 16);
+    const int r0 = max(blocks[4 * b + 2], 0), nr = max(blocks[4 * b + 3], 0);
+    for (int r = r0; r < min(r0 + nr, a.n_grows); ++r) s_b[r] = xo | nc << 16;
+  }
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, kq = lane >> 4;
+  const int n_slabs = C / CS, n_gt = a.n_grows / 16;
+  const int U = (g.dx + g.P + g.dout) << lg4;
+  for (int64_t row = blockIdx.x; row < g.n_rows; row += gridDim.x) {
+    const int xr = a.xrow ? a.xrow[row] : int(row);
+    float* dyr = a.out + row * g.dy;
+    __syncthreads();  // the previous row's LDS reads are done
+    if (xr < 0 || xr >= a.n_x) {  // padding edge (uniform): zero gradient
+      for (int i = threadIdx.x; i < g.dy; i += 256) dyr[i] = 0.0f;
+      continue;
+    }
+    const int64_t zr = a.rowptr ? receiver_of(a.rowptr, a.n_zrows, row) : row;
+    for (int i = threadIdx.x; i < a.n_grows * 16; i += 256) s_g[i] = 0.0f;
+    for (int sl = 0; sl < n_slabs; ++sl) {
+      const int c0 = sl * CS;
+      __syncthreads();  // the previous slab's LDS reads are done (and s_g is cleared)
+      for (int u = threadIdx.x; u < U; u += 256) {
+        const int r = u >> lg4, c = 4 * (u & ((1 << lg4) - 1));
+        const float* src = r < g.dx ? g.x + (int64_t(xr) * g.dx + r) * C
+                         : r < g.dx + g.P ? g.w + (row * g.P + (r - g.dx)) * C
+                                          : a.dz + (zr * g.dout + (r - g.dx - g.P)) * C;
+        *reinterpret_cast<float4v*>(s_x + r * XS + c) =
+            *reinterpret_cast<const float4v*>(src + c0 + c);
+      }
+      __syncthreads();
+      for (int t = wave; t < n_gt; t += 4) {
+        const int gr = 16 * t + li;  // the A operand's G row for this lane
+        const int ro = s_r[gr];
+        const int bx = s_b[16 * t];  // x block of the tile (uniform)
+        const int xo = bx & 0xFFFF, nc = bx >> 16;
+        const float* wp = s_w + (ro < 0 ? 0 : ro & 0xFFFF) + kq;
+        const float* zp = s_z + (ro < 0 ? 0 : ro >> 16) + kq;
+        const float* xp = s_x + min(xo + min(li, max(nc - 1, 0)), g.dx - 1) * XS + kq;
+        const bool aok = ro >= 0, bok = li < nc;
+        float4v D = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int q = 0; q < CS; q += 4) {
+          const float av = aok ? wp[q] * zp[q] : 0.0f;
+          const float bv = bok ? xp[q] : 0.0f;
+          D = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, D, 0, 0, 0);
+        }
+        // D[r]: G row 16 t + 4 kq + r, column li
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_g[(16 * t + 4 * kq + r) * 16 + li] += D[r];
+      }
+    }
+    __syncthreads();
+    for (int y = threadIdx.x; y < g.dy; y += 256) {
+      float acc = 0.0f;
+      const int k0 = max(yptr[y], 0), k1 = min(yptr[y + 1], a.n_ent);
+      for (int k = k0; k < k1; ++k) {
+        const int gi = min(max(yent[2 * k], 0), a.n_grows * 16 - 1);
+        acc = fmaf(__int_as_float(yent[2 * k + 1]), s_g[gi], acc);
+      }
+      dyr[y] = acc;
     }
   }
 }
@@ -452,6 +668,50 @@ hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
   if (a.ly >= 0) return launch_conv_gemm_pre<0, 1, false, true>(a, std::min(per_cu, 8), s);
   return per_cu <= 2 ? launch_conv_gemm_pre<0, 1, true, false>(a, per_cu, s)
                      : launch_conv_gemm_pre<0, 1, false, false>(a, std::min(per_cu, 8), s);
+}
+
+size_t gemm_dw_lds_bytes(const TpGemmArgs& a) {
+  const int XS = gemm_row_stride(a.CS);
+  return size_t(a.a_floats + a.dx * XS + 2 * XS + a.dy + a.n_klist) * 4;
+}
+
+size_t gemm_dy_lds_bytes(const GemmBwdArgs& a) {
+  const int XS = gemm_dy_row_stride(a.t.CS);
+  return size_t((a.t.dx + a.t.P + a.t.dout) * XS + a.n_grows * 16 + 2 * a.n_grows) * 4;
+}
+
+template <int NU>
+hipError_t launch_gemm_dw_nu(const GemmBwdArgs& a, hipStream_t s) {
+  static std::atomic<bool> lds_set{false};
+  if (const hipError_t e =
+          set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_gemm_dw<NU>), 160 * 1024);
+      e != hipSuccess)
+    return e;
+  const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
+  const int64_t items = a.t.n_rows * (a.t.C / a.t.CS);
+  const int grid = int(std::min<int64_t>(items, int64_t(256) * std::min(per_cu, 8)));
+  hipLaunchKernelGGL((k_gemm_dw<NU>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_dw(const GemmBwdArgs& a, hipStream_t s) {
+  if (a.t.n_rows <= 0) return hipSuccess;
+  if (a.t.lds_bytes > 160 * 1024 || a.t.CS > 128) return hipErrorInvalidValue;
+  return a.t.CS > 64 ? launch_gemm_dw_nu<2>(a, s) : launch_gemm_dw_nu<1>(a, s);
+}
+
+hipError_t launch_gemm_dy(const GemmBwdArgs& a, hipStream_t s) {
+  if (a.t.n_rows <= 0) return hipSuccess;
+  if (a.t.lds_bytes > 160 * 1024 || a.n_grows % 16) return hipErrorInvalidValue;
+  static std::atomic<bool> lds_set{false};
+  if (const hipError_t e =
+          set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_gemm_dy), 160 * 1024);
+      e != hipSuccess)
+    return e;
+  const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
+  const int grid = int(std::min<int64_t>(a.t.n_rows, int64_t(256) * std::min(per_cu, 8)));
+  hipLaunchKernelGGL(k_gemm_dy, dim3(grid), dim3(256), a.t.lds_bytes, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s) {

@@ -245,10 +245,30 @@ struct ConvGemmArgs {
   int n_edges;
   const int* rowptr;
   const int* sender;
+  const int* perm;  // edge id of CSR position j (nullptr: j); w and Y rows follow it
   float* m;
   int ly;   // -1: t.y is Y [E][dy]; else t.y is edge vectors [E][3], harmonics to degree ly
   YMap ym;  // y component -> harmonic l*l + m (ly >= 0)
 };
+// The dense-product backward's per-row (TP) or per-edge (convolution)
+// kernels: dw (plan E3_GEN_GEMM_DW) and dy (plan E3_GEN_GEMM_DY).  Rows are
+// TP rows, or edges with x gathered by sender and dz by receiver (found in
+// rowptr); an edge whose sender is outside [0, n_x) gets zero outputs.
+struct GemmBwdArgs {
+  TpGemmArgs t;          // plan sizes (dw) and x, y, w; t.z unused
+  const float* dz;       // [rows or nodes][dout][C]
+  float* out;            // dw [rows][P][C] or dy [rows][dy]
+  const int* xrow;       // convolution: sender of each edge (nullptr: x row = row)
+  const int* rowptr;     // convolution: receiver CSR (nullptr: dz row = row)
+  int n_x;               // rows of x (convolution: nodes)
+  int n_zrows;           // rows of dz
+  // dy plan
+  int n_grows, n_ent, off_rows, off_yptr, off_yent;
+};
+size_t gemm_dw_lds_bytes(const TpGemmArgs& a);
+size_t gemm_dy_lds_bytes(const GemmBwdArgs& a);
+hipError_t launch_gemm_dw(const GemmBwdArgs& a, hipStream_t s);
+hipError_t launch_gemm_dy(const GemmBwdArgs& a, hipStream_t s);
 // LDS words the convolution adds to tp_gemm_lds_bytes: the harmonic bank and the y map
 constexpr int kConvGemmExtraWords = 64 + 16;
 hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s);

@@ -286,7 +286,16 @@ e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t 
  * (dx, dout <= 63).  A table built for another descriptor gives wrong
  * values but never an out-of-bounds access (every index read from it is
  * clamped). */
-enum { E3_GEN_FORWARD = 0, E3_GEN_DX = 1, E3_GEN_DW = 2, E3_GEN_DY = 3, E3_GEN_GEMM = 4 };
+enum {
+  E3_GEN_FORWARD = 0,
+  E3_GEN_DX = 1,
+  E3_GEN_DW = 2,
+  E3_GEN_DY = 3,
+  E3_GEN_GEMM = 4,    /* dense products: the forward */
+  E3_GEN_GEMM_DX = 5, /* dense products: the gradient of x (the forward's roles swapped) */
+  E3_GEN_GEMM_DW = 6, /* dense products: the gradient of w (one block per path) */
+  E3_GEN_GEMM_DY = 7  /* dense products: the gradient of y (channel sums per x irrep) */
+};
 e3_status e3_generic_plan_size(const e3_desc* desc, int32_t table, size_t* bytes);
 e3_status e3_generic_plan_build(const e3_desc* desc, int32_t table, void* host_plan,
                                 size_t bytes);
@@ -323,6 +332,42 @@ e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_e
                                const int32_t* rowptr, const int32_t* sender, const void* plan,
                                size_t plan_bytes, const float* edge_vec_or_Y, const float* x,
                                const float* w, float* m, void* stream);
+/* The backward of e3_tp_forward_gemm (e3j E.1 Eq.14-16) as dense products
+ * on the fp32 matrix cores, for the same descriptors (degrees up to 6,
+ * float32, C % 16 == 0): with A_L[M][(P,m1)] = sum_m2 C_P[M][m1][m2] y[m2]
+ * per row,
+ *   dx   = the forward's product with the roles of x and the output swapped:
+ *          dx[i][m1] = sum_{(P,M)} A'[m1][(P,M)] w[P] dz[L_P][M]  (table
+ *          E3_GEN_GEMM_DX, one block per x irrep);
+ *   dw[P] = sum_M dz[L_P][M] (A_P x)[M], the per-path product without weight
+ *          and its sum over M in the product's epilogue (E3_GEN_GEMM_DW);
+ *   dy[m2] = sum over the CG entries (P, M, m1, m2, c) of c G[(P,M)][m1],
+ *          G[(P,M)][m1] = sum_q w[P][q] dz[L_P][M][q] x[l1][m1][q] on the
+ *          matrix cores with the channel sum as K (E3_GEN_GEMM_DY).
+ * Three launches on `stream`; every sum in a fixed order (reproducible).
+ * Plans from e3_generic_plan_build with those tables (16-byte aligned device
+ * copies); x [B][dx][C], y [B][dy], w [B][P][C], dz [B][dout][C] -> dx, dw,
+ * dy of the same shapes (float32). */
+e3_status e3_tp_backward_gemm(const e3_desc* desc, int64_t n_rows, const void* plan_dx,
+                              size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+                              const void* plan_dy, size_t dy_bytes, const float* x, const float* y,
+                              const float* w, const float* dz, float* dx, float* dw, float* dy,
+                              void* stream);
+/* The backward of e3_conv_forward_gemm (e3j E.1 Eq.16) in the same dense
+ * form, given harmonics only (E3_Y_GIVEN; from edge vectors, form Y with
+ * e3_spherical_harmonics and chain dY with e3_spherical_harmonics_backward),
+ * collapsed outputs, at most 8 x irreps: dx per sender over its out-edges
+ * (the workspace of e3_conv_prepare_transpose on this graph, required), the
+ * products accumulated in registers in the index's order; dw and dY per
+ * edge, x gathered by sender and dm by receiver.  Padding edges (a sender
+ * outside [0, N)) get dw = 0 and dY = 0 and add nothing to dx. */
+e3_status e3_conv_backward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                const int32_t* rowptr, const int32_t* sender,
+                                const void* workspace, size_t ws_bytes, const void* plan_dx,
+                                size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
+                                const void* plan_dy, size_t dy_bytes, const float* Y,
+                                const float* x, const float* w, const float* dm, float* dx,
+                                float* dw, float* dY, void* stream);
 e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void* plan_dx,
                                  size_t dx_bytes, const void* plan_dw, size_t dw_bytes,
                                  const void* plan_dy, size_t dy_bytes, const void* x,

@@ -241,7 +241,7 @@ def test_generic_plan_table(lib):
     t = np.zeros(nb.value // 4, dtype=np.int32)
     assert lib.e3_generic_plan_build(C.byref(d.c()), 0, t.ctypes.data, nb.value - 4) == -6
     assert lib.e3_generic_plan_build(C.byref(d.c()), 0, t.ctypes.data, nb.value) == 0
-    assert lib.e3_generic_plan_size(C.byref(d.c()), 5, C.byref(nb)) == -1
+    assert lib.e3_generic_plan_size(C.byref(d.c()), 8, C.byref(nb)) == -1  # no such table
     # the dense-product plan (table 4): header, one block per output irrep
     ng = C.c_size_t()
     assert lib.e3_generic_plan_size(C.byref(d.c()), 4, C.byref(ng)) == 0

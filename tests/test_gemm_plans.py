@@ -1,0 +1,136 @@
+"""CPU checks of the dense-product plans the library builds on the host
+(tables E3_GEN_GEMM, E3_GEN_GEMM_DX, E3_GEN_GEMM_DW, E3_GEN_GEMM_DY): a numpy
+reading of each plan, doing what the matrix-core kernels do with it (A built
+per row from y, one product per block over its K list), against the fp64
+oracle's tensor product and its backward, at degrees 1-6 with natural and
+skew parities, collapsed and per-path outputs, and an output irrep no path
+reaches.  These pin the host logic; the GPU tests pin the kernels."""
+import ctypes as C
+
+import numpy as np
+import pytest
+
+from clebsch_gordan_tensor_amd import api
+from clebsch_gordan_tensor_amd import synth as S
+from oracle import oracle as O
+
+HDR = 16
+
+
+def _plan(d, table):
+    L = api.lib()
+    n = C.c_size_t()
+    assert L.e3_generic_plan_size(C.byref(d.c()), table, C.byref(n)) == 0, L.e3_last_error()
+    buf = np.zeros(n.value // 4, np.int32)
+    assert L.e3_generic_plan_build(C.byref(d.c()), table, buf.ctypes.data, n.value) == 0
+    return buf
+
+
+def _A(plan, y):
+    """A (all blocks) for each row: A[at] = c1 y[y1] + c2 y[y2]."""
+    a_floats, off_groups, n_groups = plan[9], plan[12], plan[7]
+    g = plan[off_groups:off_groups + 4 * n_groups].reshape(-1, 4)
+    c = g[:, 2:].copy().view(np.float32).astype(np.float64)
+    y1, y2 = g[:, 1] & 0xFFFF, (g[:, 1] >> 16) & 0xFFFF
+    A = np.zeros((y.shape[0], a_floats))
+    A[:, g[:, 0]] = c[:, 0] * y[:, y1] + c[:, 1] * y[:, y2]
+    return A
+
+
+def _blocks(plan):
+    nb, off_b, off_k = plan[1], plan[10], plan[11]
+    blocks = plan[off_b:off_b + 4 * nb].reshape(nb, 4)
+    klist = plan[off_k:off_k + plan[6]]
+    base, out = 0, []
+    for oo, rows, kb, K in blocks:
+        out.append((oo, rows, klist[kb:kb + K], base))
+        base += rows * K
+    return out
+
+
+def run_gemm(plan, y, xin, w, dout):
+    """out[o] += A w[P] xin[xi] per block (kinds forward and dx)."""
+    A = _A(plan, y)
+    out = np.zeros((xin.shape[0], dout, xin.shape[2]))
+    for oo, rows, kl, base in _blocks(plan):
+        for k, ent in enumerate(kl):
+            if ent < 0:
+                continue
+            P, xi = ent >> 16, ent & 0xFFFF
+            a = A[:, base + k * rows: base + (k + 1) * rows]          # [B][rows]
+            out[:, oo:oo + rows] += a[:, :, None] * (w[:, P] * xin[:, xi])[:, None, :]
+    return out
+
+
+def run_dw(plan, y, x, dz):
+    """dw[P] = sum_M dz[oo + M] (A_P x)[M], one block per path."""
+    A = _A(plan, y)
+    dw = np.zeros((x.shape[0], plan[5], x.shape[2]))
+    for b, (oo, rows, kl, base) in enumerate(_blocks(plan)):
+        z = np.zeros((x.shape[0], rows, x.shape[2]))
+        for k, ent in enumerate(kl):
+            if ent >= 0:
+                z += A[:, base + k * rows: base + (k + 1) * rows, None] * x[:, ent & 0xFFFF][:, None, :]
+        dw[:, b] = (dz[:, oo:oo + rows] * z).sum(axis=1)
+    return dw
+
+
+def run_dy(plan, x, w, dz, dy_dim):
+    nb, off_b, off_r, off_yp, off_ye = plan[1], plan[10], plan[11], plan[12], plan[14]
+    blocks = plan[off_b:off_b + 4 * nb].reshape(nb, 4)
+    rows = plan[off_r:off_r + plan[6]]
+    G = np.zeros((x.shape[0], rows.shape[0], 16))
+    for xo, ncol, r0, nr in blocks:
+        for r in range(r0, r0 + nr):
+            if rows[r] < 0:
+                continue
+            P, o = rows[r] >> 16, rows[r] & 0xFFFF
+            G[:, r, :ncol] = np.einsum("bq,bcq->bc", w[:, P] * dz[:, o], x[:, xo:xo + ncol])
+    yptr = plan[off_yp:off_yp + dy_dim + 1]
+    ye = plan[off_ye:off_ye + 2 * yptr[-1]].reshape(-1, 2)
+    cf = ye[:, 1].copy().view(np.float32).astype(np.float64)
+    Gf = G.reshape(x.shape[0], -1)
+    return np.stack([(Gf[:, ye[yptr[k]:yptr[k + 1], 0]] * cf[yptr[k]:yptr[k + 1]]).sum(axis=1)
+                     for k in range(dy_dim)], axis=1)
+
+
+def _case(L, skew=False, per_path=False, out=None, C=4, B=5, seed=0):
+    xi = S.degree_irreps(L, skew)
+    oi = out if out is not None else xi
+    yi = S.sh_irreps(L)
+    d = api.Desc(xi, yi, oi, C, api.E3_OUT_PER_PATH if per_path else 0)
+    od = O.Desc(xi, yi, oi, C, per_path=per_path)
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, d.dx, C))
+    y = O.sh(L, rng.standard_normal((B, 3)))
+    w = rng.standard_normal((B, api.num_paths(d), C))
+    dz = rng.standard_normal((B, d.dout, C))
+    return d, od, x, y, w, dz
+
+
+CASES = [(1, False, False), (2, False, False), (3, True, False), (4, False, False),
+         (5, False, True), (6, False, False), (6, True, False)]
+
+
+@pytest.mark.parametrize("L,skew,pp", CASES)
+def test_dense_plans_against_oracle(L, skew, pp):
+    d, od, x, y, w, dz = _case(L, skew, pp, seed=L)
+    z = run_gemm(_plan(d, api.E3_GEN_GEMM), y, x, w, d.dout)
+    np.testing.assert_allclose(z, O.tp_forward(od, x, y, w), atol=1e-5, rtol=1e-5)
+    rdx, rdw, rdy = O.tp_backward(od, x, y, w, dz)
+    dx = run_gemm(_plan(d, api.E3_GEN_GEMM_DX), y, dz, w, d.dx)
+    np.testing.assert_allclose(dx, rdx, atol=1e-5, rtol=1e-5)
+    dw = run_dw(_plan(d, api.E3_GEN_GEMM_DW), y, x, dz)
+    np.testing.assert_allclose(dw, rdw, atol=1e-5, rtol=1e-5)
+    dy = run_dy(_plan(d, api.E3_GEN_GEMM_DY), x, w, dz, d.dy)
+    np.testing.assert_allclose(dy, rdy, atol=1e-4, rtol=1e-5)
+
+
+def test_dense_plans_pathless_output_block():
+    d, od, x, y, w, dz = _case(1, out=[(0, 1), (1, -1), (0, -1)], seed=9)
+    z = run_gemm(_plan(d, api.E3_GEN_GEMM), y, x, w, d.dout)
+    np.testing.assert_allclose(z, O.tp_forward(od, x, y, w), atol=1e-6)
+    rdx, rdw, rdy = O.tp_backward(od, x, y, w, dz)
+    np.testing.assert_allclose(run_gemm(_plan(d, api.E3_GEN_GEMM_DX), y, dz, w, d.dx), rdx, atol=1e-6)
+    np.testing.assert_allclose(run_dw(_plan(d, api.E3_GEN_GEMM_DW), y, x, dz), rdw, atol=1e-6)
+    np.testing.assert_allclose(run_dy(_plan(d, api.E3_GEN_GEMM_DY), x, w, dz, d.dy), rdy, atol=1e-5)
