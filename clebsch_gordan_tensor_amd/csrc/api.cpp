@@ -1470,10 +1470,12 @@ e3_status gemm_dy_dims(const e3_desc* desc, DyDims& d) {
 // Widest channel slab (CS | C, CS <= 128) whose LDS leaves two workgroups per
 // CU, else one; 0 when none fits.
 template <class F>
-int pick_slab(int C, F lds_of) {
-  for (size_t cap : {size_t(80) * 1024, size_t(160) * 1024})
+int pick_slab(int C, F lds_of, bool widest = false) {
+  for (size_t cap : {size_t(80) * 1024, size_t(160) * 1024}) {
+    if (widest && cap < 160 * 1024) continue;
     for (int cs : {128, 64, 32, 16})
       if (cs <= C && C % cs == 0 && lds_of(cs) <= cap) return cs;
+  }
   return 0;
 }
 

@@ -382,13 +382,21 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
       if (!active) continue;  // the same for the whole wavefront
       const float* sw = s_w + 16 * wave + li;
       const float* sx = s_x + 16 * wave + li;
+      // each edge's product starts from zero and joins the node's sum once,
+      // so the long sum over the edge list rounds once per edge rather than
+      // once per K step
 #pragma unroll
       for (int b = 0; b < kConvGemmBlocks; ++b) {
         const int rows = b_rows[b], K = b_K[b];
         const bool aok = li < rows;
         const float* ap = s_a + b_ab[b] + kq * rows + min(li, rows - 1);
         const int* kp = s_k + b_kb[b] + kq;
-        gemm_ksteps<NU, BATCH>(D[b], ap, kp, rows, aok, K, sw, sx);
+        float4v De[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) De[u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+        gemm_ksteps<NU, BATCH>(De, ap, kp, rows, aok, K, sw, sx);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) D[b][u] += De[u];
       }
     }
     // D[i][j] in register i % 4 of lane j + 16 (i / 4): row 4 kq + r, channel li
@@ -443,7 +451,8 @@ __global__ void __launch_bounds__(256) k_gemm_dw(GemmBwdArgs a) {
   float* s_a = gsm;
   float* s_x = s_a + g.a_floats;
   float* s_w = s_x + g.dx * XS;  // a row of ones (real columns) and a row of zeros (padding)
-  float* s_y = s_w + 2 * XS;
+  float* s_z = s_w + 2 * XS;     // the row's dz slab [dout][XS]
+  float* s_y = s_z + g.dout * XS;
   int* s_k = reinterpret_cast<int*>(s_y + g.dy);
   for (int i = threadIdx.x; i < g.n_klist; i += 256) {
     const int ent = klist[i];
@@ -460,7 +469,7 @@ __global__ void __launch_bounds__(256) k_gemm_dw(GemmBwdArgs a) {
   const int n_slabs = C / CS, n_tiles = CS / 16;
   const bool active = wave < n_tiles;
   const int64_t n_items = g.n_rows * n_slabs;
-  const int U = g.dx << lg4;
+  const int U = (g.dx + g.dout) << lg4;
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int64_t row = item / n_slabs;
     const int c0 = int(item - row * n_slabs) * CS;
@@ -474,8 +483,10 @@ __global__ void __launch_bounds__(256) k_gemm_dw(GemmBwdArgs a) {
     const int64_t zr = a.rowptr ? receiver_of(a.rowptr, a.n_zrows, row) : row;
     for (int u = threadIdx.x; u < U; u += 256) {
       const int r = u >> lg4, c = 4 * (u & ((1 << lg4) - 1));
-      *reinterpret_cast<float4v*>(s_x + r * XS + c) =
-          *reinterpret_cast<const float4v*>(g.x + (int64_t(xr) * g.dx + r) * C + c0 + c);
+      const float* src = r < g.dx ? g.x + (int64_t(xr) * g.dx + r) * C
+                                  : a.dz + (zr * g.dout + (r - g.dx)) * C;
+      float* dst = r < g.dx ? s_x + r * XS : s_z + (r - g.dx) * XS;
+      *reinterpret_cast<float4v*>(dst + c) = *reinterpret_cast<const float4v*>(src + c0 + c);
     }
     for (int i = threadIdx.x; i < g.dy; i += 256) s_y[i] = g.y[row * g.dy + i];
     __syncthreads();
@@ -488,7 +499,6 @@ __global__ void __launch_bounds__(256) k_gemm_dw(GemmBwdArgs a) {
     }
     __syncthreads();
     if (!active) continue;
-    const float* dzr = a.dz + zr * g.dout * C + c0;
     int abase = 0;
     for (int b = 0; b < g.n_blocks; ++b) {
       const int oo = blocks[4 * b], rows = min(max(blocks[4 * b + 1], 1), 16);
@@ -510,7 +520,7 @@ __global__ void __launch_bounds__(256) k_gemm_dw(GemmBwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * kq + r, o = oo + i;
-          if (i < rows && o >= 0 && o < g.dout) part = fmaf(dzr[int64_t(o) * C + c], D[u][r], part);
+          if (i < rows && o >= 0 && o < g.dout) part = fmaf(s_z[o * XS + c], D[u][r], part);
         }
         part += shfl_xor_c<16>(part);
         part += shfl_xor_c<32>(part);
@@ -585,35 +595,63 @@ __global__ void __launch_bounds__(256) k_gemm_dy(GemmBwdArgs a) {
             *reinterpret_cast<const float4v*>(src + c0 + c);
       }
       __syncthreads();
-      for (int t = wave; t < n_gt; t += 4) {
-        const int gr = 16 * t + li;  // the A operand's G row for this lane
-        const int ro = s_r[gr];
-        const int bx = s_b[16 * t];  // x block of the tile (uniform)
-        const int xo = bx & 0xFFFF, nc = bx >> 16;
-        const float* wp = s_w + (ro < 0 ? 0 : ro & 0xFFFF) + kq;
-        const float* zp = s_z + (ro < 0 ? 0 : ro >> 16) + kq;
-        const float* xp = s_x + min(xo + min(li, max(nc - 1, 0)), g.dx - 1) * XS + kq;
-        const bool aok = ro >= 0, bok = li < nc;
-        float4v D = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int q = 0; q < CS; q += 4) {
-          const float av = aok ? wp[q] * zp[q] : 0.0f;
-          const float bv = bok ? xp[q] : 0.0f;
-          D = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, D, 0, 0, 0);
-        }
-        // D[r]: G row 16 t + 4 kq + r, column li
+      // two tiles at a time (independent accumulators), four K steps per
+      // batch with their LDS reads issued first
+      for (int t0 = 2 * wave; t0 < n_gt; t0 += 8) {
+        const float* wp[2];
+        const float* zp[2];
+        const float* xp[2];
+        bool aok[2], bok[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s_g[(16 * t + 4 * kq + r) * 16 + li] += D[r];
+        for (int h = 0; h < 2; ++h) {
+          const int t = min(t0 + h, n_gt - 1);
+          const int ro = s_r[16 * t + li];
+          const int bx = s_b[16 * t];  // x block of the tile (uniform)
+          const int xo = bx & 0xFFFF, nc = bx >> 16;
+          wp[h] = s_w + (ro < 0 ? 0 : ro & 0xFFFF) + kq;
+          zp[h] = s_z + (ro < 0 ? 0 : ro >> 16) + kq;
+          xp[h] = s_x + min(xo + min(li, max(nc - 1, 0)), g.dx - 1) * XS + kq;
+          aok[h] = ro >= 0 && t0 + h < n_gt;
+          bok[h] = li < nc;
+        }
+        float4v D[2] = {float4v{0.0f, 0.0f, 0.0f, 0.0f}, float4v{0.0f, 0.0f, 0.0f, 0.0f}};
+        for (int q = 0; q < CS; q += 16) {
+          float av[2][4], zv[2][4], bv[2][4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              av[h][j] = wp[h][q + 4 * j];
+              zv[h][j] = zp[h][q + 4 * j];
+              bv[h][j] = xp[h][q + 4 * j];
+            }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              D[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(aok[h] ? av[h][j] * zv[h][j] : 0.0f,
+                                                          bok[h] ? bv[h][j] : 0.0f, D[h], 0, 0, 0);
+        }
+        // D[h][r]: G row 16 t + 4 kq + r, column li
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (t0 + h < n_gt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_g[(16 * (t0 + h) + 4 * kq + r) * 16 + li] += D[h][r];
       }
     }
     __syncthreads();
-    for (int y = threadIdx.x; y < g.dy; y += 256) {
+    // dy[y]: a wavefront per component, its entries strided over the lanes,
+    // then the fixed-order wavefront sum
+    for (int y = wave; y < g.dy; y += 4) {
       float acc = 0.0f;
       const int k0 = max(yptr[y], 0), k1 = min(yptr[y + 1], a.n_ent);
-      for (int k = k0; k < k1; ++k) {
+      for (int k = k0 + lane; k < k1; k += 64) {
         const int gi = min(max(yent[2 * k], 0), a.n_grows * 16 - 1);
         acc = fmaf(__int_as_float(yent[2 * k + 1]), s_g[gi], acc);
       }
-      dyr[y] = acc;
+      acc = wave_sum(acc);
+      if (lane == 0) dyr[y] = acc;
     }
   }
 }
@@ -672,7 +710,7 @@ hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
 
 size_t gemm_dw_lds_bytes(const TpGemmArgs& a) {
   const int XS = gemm_row_stride(a.CS);
-  return size_t(a.a_floats + a.dx * XS + 2 * XS + a.dy + a.n_klist) * 4;
+  return size_t(a.a_floats + (a.dx + a.dout + 2) * XS + a.dy + a.n_klist) * 4;
 }
 
 size_t gemm_dy_lds_bytes(const GemmBwdArgs& a) {
