@@ -1068,11 +1068,39 @@ e3_status build_generic(const e3_desc* desc, int table, std::vector<int32_t>& ou
 //   kind 1 (E3_GEN_GEMM_DX, the gradient of x): the same entries with the
 //     roles of x and the output swapped -- blocks = x irreps, input dz,
 //     dx[xi] += A w[P] dz[o] (A'[m1][(P,M)] = sum_m2 C_P[M][m1][m2] y[m2]);
-//   kind 2 (E3_GEN_GEMM_DW, the gradient of w): blocks = paths, input x,
-//     no weight: dw[P] = sum_M dz[oo_P + M] (A_P x)[M].
+//   kind 2 (E3_GEN_GEMM_DW, the gradient of w): build_gemm_dw.
 // Every block owns its rows (a block no path reaches gets K = 0).
+// Groups {A index, y1 | y2 << 16, c1, c2} from (A index, y component, c)
+// terms: one group per A element; the real basis couples each (M, m1) to at
+// most two m2.
+struct AGroupTerm {
+  int at, yi;
+  float c;
+};
+e3_status a_groups(std::vector<AGroupTerm>& ge, std::vector<int32_t>& groups) {
+  std::stable_sort(ge.begin(), ge.end(),
+                   [](const AGroupTerm& a, const AGroupTerm& b) { return a.at < b.at; });
+  groups.clear();
+  for (size_t i = 0; i < ge.size();) {
+    size_t j = i;
+    while (j < ge.size() && ge[j].at == ge[i].at) ++j;
+    if (j - i > 2) return fail(E3_ERR_UNSUPPORTED, "an A entry with more than two terms");
+    const AGroupTerm& a = ge[i];
+    const AGroupTerm& b = j - i == 2 ? ge[i + 1] : AGroupTerm{a.at, a.yi, 0.0f};
+    int32_t ca, cb;
+    std::memcpy(&ca, &a.c, 4);
+    std::memcpy(&cb, &b.c, 4);
+    groups.insert(groups.end(), {a.at, int32_t(a.yi | (b.yi << 16)), ca, cb});
+    i = j;
+  }
+  return ok();
+}
+
+e3_status build_gemm_dw(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemmArgs& d);
+
 e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& out,
                           e3k::TpGemmArgs& d) {
+  if (kind == 2) return build_gemm_dw(desc, out, d);
   Parsed p;
   std::vector<GenEntry> ent;
   e3_status s = generic_entries(desc, p, ent, false);
@@ -1086,7 +1114,7 @@ e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& o
     oo_path[pi] = p.per_path ? opp : ooff[p.pio[pi]];
     opp += 2 * p.o[p.pio[pi]].l + 1;
   }
-  const bool per_path_blocks = kind == 2 || (kind == 0 && p.per_path);
+  const bool per_path_blocks = kind == 0 && p.per_path;
   const int nb = per_path_blocks ? p.P : kind == 1 ? int(p.x.size()) : int(p.o.size());
   auto block_of = [&](int pi) { return per_path_blocks ? pi : kind == 1 ? p.pix[pi] : p.pio[pi]; };
   auto in_off = [&](int pi) { return kind == 1 ? oo_path[pi] : xoff[p.pix[pi]]; };
@@ -1127,34 +1155,16 @@ e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& o
     b_abase[b] = abase;
     abase += b_rows[b] * k;
   }
-  struct GE {
-    int at, yi;
-    float c;
-  };
-  std::vector<GE> ge;
+  std::vector<AGroupTerm> ge;
   ge.reserve(ent.size());
   for (const GenEntry& e : ent) {
     const int b = block_of(e.P);
     const int M = out_comp(e) - b_oo[b];
     const int k = path_koff[e.P] + (in_comp(e) - in_off(e.P));
-    ge.push_back(GE{b_abase[b] + k * b_rows[b] + M, e.yi, e.c});  // A[k][M]
+    ge.push_back(AGroupTerm{b_abase[b] + k * b_rows[b] + M, e.yi, e.c});  // A[k][M]
   }
-  std::stable_sort(ge.begin(), ge.end(), [](const GE& a, const GE& b) { return a.at < b.at; });
-  // one entry per A element: {at, y1 | y2 << 16, c1, c2}; the real basis
-  // couples each (M, m1) to at most two m2
   std::vector<int32_t> groups;
-  for (size_t i = 0; i < ge.size();) {
-    size_t j = i;
-    while (j < ge.size() && ge[j].at == ge[i].at) ++j;
-    if (j - i > 2) return fail(E3_ERR_UNSUPPORTED, "an A entry with more than two terms");
-    const GE& a = ge[i];
-    const GE& b = j - i == 2 ? ge[i + 1] : GE{a.at, a.yi, 0.0f};
-    int32_t ca, cb;
-    std::memcpy(&ca, &a.c, 4);
-    std::memcpy(&cb, &b.c, 4);
-    groups.insert(groups.end(), {a.at, int32_t(a.yi | (b.yi << 16)), ca, cb});
-    i = j;
-  }
+  if ((s = a_groups(ge, groups)) != E3_OK) return s;
   const int n_groups = int(groups.size() / 4);
   // the kernel's view: input components (dx), output components (dout)
   const int in_dim = kind == 1 ? p.dout : p.dx, out_dim = kind == 1 ? p.dx : p.dout;
@@ -1190,6 +1200,132 @@ e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& o
 
 e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemmArgs& d) {
   return build_gemm_kind(desc, 0, out, d);
+}
+
+// The gradient of w (E3_GEN_GEMM_DW): per row and path P,
+//   dw[P][q] = sum_M dz[oo_P + M][q] (A_P x)[M][q],  A_P[M][m1] = sum_m2 C_P[M][m1][m2] y[m2].
+// The rows (P, M) of each path, in runs of four (quads; a path's last quad
+// padded with rows that read a zero dz row), are stacked in path order, so
+// that the paths of one x irrep are consecutive, and cut into tiles of at
+// most four quads that never mix x irreps or groups of 16 paths (16 t ..
+// 16 t + 15): a tile is one product A x over its irrep's components (the K
+// list, shared by the irrep's tiles), each quad's four rows are added up
+// in the lane that holds them, and the quads' sums per path are a second
+// product with a 0/1 matrix into the group's 16 paths.
+// Layout: header kGemmHeader words (magic + 2, n_blocks, dx, dy, dout, P,
+// n_klist, n_groups, off_rowtab, a_floats, off_blocks, off_klist,
+// off_groups, words); blocks [nb][4]: path group t, rows (4 per quad), K
+// list start, K (a multiple of 4, at most 16); K list: x components, -1 for
+// padding; row table [nb][16] (16-byte aligned, after the K list):
+// (P - 16 t) | (dz component + 1) << 10 per row, 0 in place of the
+// component + 1 for a padding row, 16 for the rows of a missing quad;
+// groups as in the other dense plans, A[k][row] at the tile's base +
+// 16 k + row (the tiles' bases advance by 16 K).
+e3_status build_gemm_dw(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemmArgs& d) {
+  Parsed p;
+  std::vector<GenEntry> ent;
+  e3_status s = generic_entries(desc, p, ent, false);
+  if (s != E3_OK) return s;
+  if (p.P > 32767 || p.dx > 65535 || p.dout > 65535)
+    return fail(E3_ERR_UNSUPPORTED, "too many paths or components");
+  std::vector<int> xoff(p.x.size()), oo_path(p.P);
+  {
+    std::vector<int> ooff(p.o.size());
+    for (size_t i = 0, o = 0; i < p.x.size(); ++i) xoff[i] = int(o), o += 2 * p.x[i].l + 1;
+    for (size_t i = 0, o = 0; i < p.o.size(); ++i) ooff[i] = int(o), o += 2 * p.o[i].l + 1;
+    for (int pi = 0, opp = 0; pi < p.P; ++pi) {
+      oo_path[pi] = p.per_path ? opp : ooff[p.pio[pi]];
+      opp += 2 * p.o[p.pio[pi]].l + 1;
+    }
+  }
+  for (int pi = 1; pi < p.P; ++pi)
+    if (p.pix[pi] < p.pix[pi - 1]) return fail(E3_ERR_UNSUPPORTED, "paths not grouped by x irrep");
+  std::vector<int32_t> blocks, klist, rowtab;
+  std::vector<int> tile_base;
+  std::vector<std::vector<std::pair<int, int>>> path_rows(p.P);  // (P, M) -> tile, row
+  for (int pi = 0; pi < p.P; ++pi) path_rows[pi].resize(size_t(2 * p.o[p.pio[pi]].l + 1));
+  int abase = 0;
+  for (int pa = 0; pa < p.P;) {
+    int pb = pa;
+    while (pb < p.P && p.pix[pb] == p.pix[pa]) ++pb;
+    const int l1 = p.x[p.pix[pa]].l, width = 2 * l1 + 1;
+    if (width > 16) return fail(E3_ERR_UNSUPPORTED, "x degree above 7");
+    const int kb = int(klist.size()), K = (width + 3) / 4 * 4;
+    for (int m = 0; m < K; ++m) klist.push_back(m < width ? xoff[p.pix[pa]] + m : -1);
+    // quads: each path's rows (P, M) in runs of four, the last one padded
+    struct Quad {
+      int P, M0, n;
+    };
+    std::vector<Quad> quads;
+    for (int pi = pa; pi < pb; ++pi) {
+      const int w = 2 * p.o[p.pio[pi]].l + 1;
+      for (int M0 = 0; M0 < w; M0 += 4) quads.push_back(Quad{pi, M0, std::min(4, w - M0)});
+    }
+    // tiles: at most four quads, all of one group of 16 paths
+    for (size_t q0 = 0; q0 < quads.size();) {
+      const int t = quads[q0].P / 16;
+      int n = 0;
+      while (n < 4 && q0 + n < quads.size() && quads[q0 + n].P / 16 == t) ++n;
+      const int tile = int(blocks.size() / 4);
+      for (int j = 0; j < 4; ++j) {
+        for (int i = 0; i < 4; ++i) {
+          if (j >= n) {
+            rowtab.push_back(16);  // no path, the zero row
+            continue;
+          }
+          const Quad& qd = quads[q0 + j];
+          const int rel = qd.P - 16 * t;
+          if (i < qd.n) {
+            const int M = qd.M0 + i;
+            path_rows[qd.P][M] = {tile, 4 * j + i};
+            rowtab.push_back(rel | ((oo_path[qd.P] + M + 1) << 10));
+          } else {
+            rowtab.push_back(rel);
+          }
+        }
+      }
+      tile_base.push_back(abase);
+      blocks.insert(blocks.end(), {t, 4 * n, kb, K});
+      abase += 16 * K;
+      q0 += size_t(n);
+    }
+    pa = pb;
+  }
+  const int nb = int(blocks.size() / 4);
+  std::vector<AGroupTerm> ge;
+  ge.reserve(ent.size());
+  for (const GenEntry& e : ent) {
+    const auto [tile, r] = path_rows[e.P][size_t(e.o - oo_path[e.P])];
+    const int k = e.xi - xoff[p.pix[e.P]];
+    ge.push_back(AGroupTerm{tile_base[tile] + k * 16 + r, e.yi, e.c});
+  }
+  std::vector<int32_t> groups;
+  if ((s = a_groups(ge, groups)) != E3_OK) return s;
+  d = e3k::TpGemmArgs{};
+  d.n_blocks = nb;
+  d.dx = p.dx;
+  d.dy = p.dy;
+  d.dout = p.dout;
+  d.P = p.P;
+  d.n_klist = int(klist.size());
+  d.n_groups = int(groups.size() / 4);
+  d.a_floats = std::max(abase, 4);
+  d.off_blocks = e3k::kGemmHeader;
+  d.off_klist = d.off_blocks + 4 * nb;
+  const int off_rowtab = e3k::gemm_dw_rowtab_offset(d);
+  d.off_groups = off_rowtab + 16 * nb;
+  d.plan_words = d.off_groups + int(groups.size());
+  out.assign(size_t(d.plan_words), 0);
+  const int32_t head[14] = {e3k::kGemmMagic + 2, nb,          p.dx,         p.dy,
+                            p.dout,              p.P,         d.n_klist,    d.n_groups,
+                            off_rowtab,          d.a_floats,  d.off_blocks, d.off_klist,
+                            d.off_groups,        d.plan_words};
+  std::copy(head, head + 14, out.begin());
+  std::copy(blocks.begin(), blocks.end(), out.begin() + d.off_blocks);
+  std::copy(klist.begin(), klist.end(), out.begin() + d.off_klist);
+  std::copy(rowtab.begin(), rowtab.end(), out.begin() + off_rowtab);
+  std::copy(groups.begin(), groups.end(), out.begin() + d.off_groups);
+  return ok();
 }
 
 // The gradient of y (E3_GEN_GEMM_DY): per row and x irrep i,
@@ -1507,11 +1643,13 @@ e3_status gemm_backward_setup(const e3_desc* desc, const Parsed& p, const void* 
     t.CS = cs;
     return e3k::tp_gemm_lds_bytes(t);
   });
+  // dw: the widest slab (A is built once per slab; the workgroup has a
+  // wavefront per 16 channels)
   bdw.t.CS = pick_slab(p.C, [&](int cs) {
     e3k::TpGemmArgs t = bdw.t;
     t.CS = cs;
     return e3k::gemm_dw_lds_bytes(t);
-  });
+  }, true);
   bdy = e3k::GemmBwdArgs{};
   bdy.t.n_blocks = dd.n_blocks;
   bdy.t.dx = p.dx;

@@ -432,42 +432,67 @@ __device__ __forceinline__ int receiver_of(const int* __restrict__ rowptr, int n
   return min(lo, n_nodes - 1);
 }
 
-// The gradient of w in the dense form (plan E3_GEN_GEMM_DW: one block per
-// path P, K over its m1): per row (or edge) and path,
-//   dw[P][q] = sum_M dz[oo_P + M][q] (A_P x)[M][q],
-// (A_P x) on the fp32 matrix cores as in k_tp_gemm with a weight of one, the
-// sum over M as the product's epilogue: each lane adds its four rows, then
-// the four row groups of a column (lanes li, li + 16, li + 32, li + 48) in a
-// fixed butterfly.  One workgroup per (row, slab of CS channels).
-template <int NU>
-__global__ void __launch_bounds__(256) k_gemm_dw(GemmBwdArgs a) {
+// The gradient of w in the dense form (plan E3_GEN_GEMM_DW): per row (or
+// edge) and path P,
+//   dw[P][q] = sum_M dz[oo_P + M][q] (A_P x)[M][q].
+// The plan stacks each path's rows (P, M) in quads of four (a path's last
+// quad padded) into tiles of at most four quads, all of one x irrep and of
+// one group of 16 paths.  Per tile, on the fp32 matrix cores: D = A x over
+// the irrep's K steps (their x operand held in registers across the
+// irrep's tiles); the lane holding a quad's four rows forms
+// sum_i D[row i] dz[row i] (in row order; padding rows read a zero row);
+// and the quads' sums go into the group's 16 paths as a second product
+// S E with S[P][quad] = 1 where the quad belongs to P, accumulated over the
+// group's tiles and stored once the tiles have moved past it.  A is kept
+// with a row stride of 16 (rows past a tile's end stay zero), so a K step's
+// A read is one fixed offset.  One workgroup of NW wavefronts per (row,
+// slab of CS = 16 NW NU channels).
+__host__ __device__ constexpr int gemm_dw_a_slack() { return 256; }
+
+template <int NU, int NW>
+__global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
+  constexpr int NT = 64 * NW;
   extern __shared__ __align__(16) float gsm[];
   const TpGemmArgs& g = a.t;
   const int* __restrict__ blocks = g.plan + g.off_blocks;
   const int* __restrict__ klist = g.plan + g.off_klist;
+  const int* __restrict__ rowtab = g.plan + gemm_dw_rowtab_offset(g);
   const int4* __restrict__ groups = reinterpret_cast<const int4*>(g.plan + g.off_groups);
   const int CS = g.CS, C = g.C, XS = gemm_row_stride(CS);
   const int lg4 = __builtin_ctz(CS / 4);
-  float* s_a = gsm;
-  float* s_x = s_a + g.a_floats;
-  float* s_w = s_x + g.dx * XS;  // a row of ones (real columns) and a row of zeros (padding)
-  float* s_z = s_w + 2 * XS;     // the row's dz slab [dout][XS]
-  float* s_y = s_z + g.dout * XS;
-  int* s_k = reinterpret_cast<int*>(s_y + g.dy);
-  for (int i = threadIdx.x; i < g.n_klist; i += 256) {
+  const int a4 = ((g.a_floats + 3) & ~3) + gemm_dw_a_slack();
+  float* s_a = gsm;                    // A [tiles][K][16], then slack for reads past the last
+  float* s_x = s_a + a4;               // [dx + 1][XS]: x slab, then a row of zeros (K padding)
+  float* s_z = s_x + (g.dx + 1) * XS;  // the row's dz slab [dout][XS]
+  int* s_rt = reinterpret_cast<int*>(s_z + g.dout * XS);  // rows [n_blocks][16], staged
+  int* s_bd = s_rt + 16 * g.n_blocks;                        // descriptors [n_blocks][4]
+  int* s_k = s_bd + 4 * g.n_blocks;                          // K list as x row offsets
+  float* s_y = reinterpret_cast<float*>(s_k + g.n_klist);
+  for (int i = threadIdx.x; i < g.n_klist; i += NT) {
     const int ent = klist[i];
-    const int xi = ent < 0 ? 0 : min(ent & 0xFFFF, g.dx - 1);
-    s_k[i] = (ent < 0 ? XS : 0) | (xi * XS) << 16;
+    s_k[i] = (ent < 0 || ent >= g.dx ? g.dx : ent) * XS;
   }
-  for (int i = threadIdx.x; i < XS; i += 256) {
-    s_w[i] = 1.0f;
-    s_w[XS + i] = 0.0f;
+  // rows: word offset from s_x of the row's dz row (row dx of s_x: zeros) |
+  // its path in the group of 16 << 20 (16: none)
+  for (int i = threadIdx.x; i < 16 * g.n_blocks; i += NT) {
+    const int e = rowtab[i];
+    const int z = e < 0 ? 0 : min(e >> 10, g.dout), rel = e < 0 ? 16 : min(e & 31, 16);
+    s_rt[i] = (g.dx + z) * XS | rel << 20;
   }
-  for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
+  for (int b = threadIdx.x; b < g.n_blocks; b += NT) {  // clamped to the plan's extents
+    const int kb = min(max(blocks[4 * b + 2], 0), max(g.n_klist - 1, 0));
+    const int K = min(min(max(blocks[4 * b + 3], 0), g.n_klist - kb), 16) & ~3;
+    s_bd[4 * b] = blocks[4 * b];
+    s_bd[4 * b + 1] = 0;
+    s_bd[4 * b + 2] = kb;
+    s_bd[4 * b + 3] = K;
+  }
+  for (int i = threadIdx.x; i < XS; i += NT) s_x[g.dx * XS + i] = 0.0f;
+  for (int i = threadIdx.x; i < a4; i += NT) s_a[i] = 0.0f;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, kq = lane >> 4;
-  const int n_slabs = C / CS, n_tiles = CS / 16;
-  const bool active = wave < n_tiles;
+  const int n_slabs = C / CS;
+  const bool active = wave < CS / (16 * NU);
   const int64_t n_items = g.n_rows * n_slabs;
   const int U = (g.dx + g.dout) << lg4;
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -475,23 +500,23 @@ __global__ void __launch_bounds__(256) k_gemm_dw(GemmBwdArgs a) {
     const int c0 = int(item - row * n_slabs) * CS;
     const int xr = a.xrow ? a.xrow[row] : int(row);
     float* dwr = a.out + row * g.P * C + c0;
-    __syncthreads();  // the previous item's LDS reads are done (and s_k is written)
+    __syncthreads();  // the previous item's LDS reads are done (and the tables are written)
     if (xr < 0 || xr >= a.n_x) {  // padding edge (uniform): zero gradient
-      for (int i = threadIdx.x; i < g.P * CS; i += 256) dwr[(i / CS) * C + i % CS] = 0.0f;
+      for (int i = threadIdx.x; i < g.P * CS; i += NT) dwr[(i / CS) * C + i % CS] = 0.0f;
       continue;
     }
     const int64_t zr = a.rowptr ? receiver_of(a.rowptr, a.n_zrows, row) : row;
-    for (int u = threadIdx.x; u < U; u += 256) {
+    for (int u = threadIdx.x; u < U; u += NT) {
       const int r = u >> lg4, c = 4 * (u & ((1 << lg4) - 1));
       const float* src = r < g.dx ? g.x + (int64_t(xr) * g.dx + r) * C
                                   : a.dz + (zr * g.dout + (r - g.dx)) * C;
       float* dst = r < g.dx ? s_x + r * XS : s_z + (r - g.dx) * XS;
       *reinterpret_cast<float4v*>(dst + c) = *reinterpret_cast<const float4v*>(src + c0 + c);
     }
-    for (int i = threadIdx.x; i < g.dy; i += 256) s_y[i] = g.y[row * g.dy + i];
+    for (int i = threadIdx.x; i < g.dy; i += NT) s_y[i] = g.y[row * g.dy + i];
     __syncthreads();
 #pragma unroll 4
-    for (int q = threadIdx.x; q < g.n_groups; q += 256) {
+    for (int q = threadIdx.x; q < g.n_groups; q += NT) {
       const int4 e = groups[q];
       const int at = min(max(e.x, 0), g.a_floats - 1);
       const int y1 = min(e.y & 0xFFFF, g.dy - 1), y2 = min((e.y >> 16) & 0xFFFF, g.dy - 1);
@@ -499,35 +524,81 @@ __global__ void __launch_bounds__(256) k_gemm_dw(GemmBwdArgs a) {
     }
     __syncthreads();
     if (!active) continue;
-    int abase = 0;
+    // acc: paths 16 cur + [0, 16); register r of lane (li, kq) holds path
+    // 16 cur + 4 kq + r at channel 16 (wave + NW u) + li
+    float4v acc[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc[u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    auto flush = [&](int t) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int P = 16 * t + 4 * kq + r;
+          if (P >= 0 && P < g.P) dwr[int64_t(P) * C + 16 * (wave + NW * u) + li] = acc[u][r];
+        }
+    };
+    const float* zl = s_x + 16 * wave + li;  // this lane's channel in an x or dz row
+    int cur = 0, cur_kb = -1, cur_K = -1, abase = 0;
+    float xb[4][NU];
+    // the tiles' descriptors from LDS, the next one read while this one runs
+    int4 bd = g.n_blocks > 0 ? *reinterpret_cast<const int4*>(s_bd) : int4{0, 0, 0, 0};
     for (int b = 0; b < g.n_blocks; ++b) {
-      const int oo = blocks[4 * b], rows = min(max(blocks[4 * b + 1], 1), 16);
-      const int kb = min(max(blocks[4 * b + 2], 0), g.n_klist);
-      const int K = min(max(blocks[4 * b + 3], 0), g.n_klist - kb) & ~3;
-      if (abase + rows * K > g.a_floats) break;
-      const bool aok = li < rows;
-      const float* ap = s_a + abase + kq * rows + min(li, rows - 1);
-      const int* kp = s_k + kb + kq;
+      const int t = __builtin_amdgcn_readfirstlane(bd.x);
+      const int kb = __builtin_amdgcn_readfirstlane(bd.z);
+      const int K = __builtin_amdgcn_readfirstlane(bd.w);
+      if (b + 1 < g.n_blocks) bd = *reinterpret_cast<const int4*>(s_bd + 4 * (b + 1));
+      if (abase + 16 * K > g.a_floats) break;
+      // A of the tile, its four K steps' reads issued together (past the
+      // tile's K they read the next tile's A or the slack, unused)
+      const float* ap = s_a + abase + 16 * kq + li;
+      float av[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = ap[64 * j];
+      const int4 rt = *reinterpret_cast<const int4*>(s_rt + 16 * b + 4 * kq);
+      if (t != cur) {  // the tiles have moved past path group cur
+        flush(cur);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) acc[u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+        cur = t;
+      }
+      if (kb != cur_kb || K != cur_K) {  // a new x irrep: its K steps' x operand
+        int xo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xo[j] = s_k[min(kb + 4 * j + kq, g.n_klist - 1)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            const float v = s_x[xo[j] + 16 * (wave + NW * u) + li];
+            xb[j][u] = 4 * j < K ? v : 0.0f;
+          }
+        cur_kb = kb;
+        cur_K = K;
+      }
       float4v D[NU];
 #pragma unroll
       for (int u = 0; u < NU; ++u) D[u] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-      gemm_ksteps<NU>(D, ap, kp, rows, aok, K, s_w + li, s_x + 16 * wave + li);
-      // D[u][r]: row M = 4 kq + r, channel 16 (wave + 4u) + li
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * j < K) {
+#pragma unroll
+          for (int u = 0; u < NU; ++u)
+            D[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], xb[j][u], D[u], 0, 0, 0);
+        }
+      // D[u][r]: row 4 kq + r of the tile (quad kq), channel 16 (wave + NW u) + li
+      const float sv = ((rt.x >> 20) & 31) == li ? 1.0f : 0.0f;
+      const int zo[4] = {rt.x & 0xFFFFF, rt.y & 0xFFFFF, rt.z & 0xFFFFF, rt.w & 0xFFFFF};
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const int c = 16 * (wave + 4 * u) + li;
-        float part = 0.0f;
+        float e = D[u][0] * zl[zo[0] + 16 * NW * u];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * kq + r, o = oo + i;
-          if (i < rows && o >= 0 && o < g.dout) part = fmaf(s_z[o * XS + c], D[u][r], part);
-        }
-        part += shfl_xor_c<16>(part);
-        part += shfl_xor_c<32>(part);
-        if (kq == 0 && b < g.P) dwr[int64_t(b) * C + c] = part;
+        for (int r = 1; r < 4; ++r) e = fmaf(D[u][r], zl[zo[r] + 16 * NW * u], e);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(sv, e, acc[u], 0, 0, 0);
       }
-      abase += rows * K;
+      abase += 16 * K;
     }
+    flush(cur);
   }
 }
 
@@ -710,7 +781,8 @@ hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
 
 size_t gemm_dw_lds_bytes(const TpGemmArgs& a) {
   const int XS = gemm_row_stride(a.CS);
-  return size_t(a.a_floats + (a.dx + a.dout + 2) * XS + a.dy + a.n_klist) * 4;
+  return size_t(((a.a_floats + 3) & ~3) + gemm_dw_a_slack() + (a.dx + 1 + a.dout) * XS +
+                20 * a.n_blocks + a.n_klist + a.dy) * 4;
 }
 
 size_t gemm_dy_lds_bytes(const GemmBwdArgs& a) {
@@ -718,24 +790,31 @@ size_t gemm_dy_lds_bytes(const GemmBwdArgs& a) {
   return size_t((a.t.dx + a.t.P + a.t.dout) * XS + a.n_grows * 16 + 2 * a.n_grows) * 4;
 }
 
-template <int NU>
+template <int NU, int NW>
 hipError_t launch_gemm_dw_nu(const GemmBwdArgs& a, hipStream_t s) {
   static std::atomic<bool> lds_set{false};
-  if (const hipError_t e =
-          set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_gemm_dw<NU>), 160 * 1024);
+  if (const hipError_t e = set_max_lds_once(
+          lds_set, reinterpret_cast<const void*>(&k_gemm_dw<NU, NW>), 160 * 1024);
       e != hipSuccess)
     return e;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
   const int64_t items = a.t.n_rows * (a.t.C / a.t.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * std::min(per_cu, 8)));
-  hipLaunchKernelGGL((k_gemm_dw<NU>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
+  hipLaunchKernelGGL((k_gemm_dw<NU, NW>), dim3(grid), dim3(64 * NW), a.t.lds_bytes, s, a);
   return hipGetLastError();
 }
 
+// one 16-channel tile per wavefront
 hipError_t launch_gemm_dw(const GemmBwdArgs& a, hipStream_t s) {
   if (a.t.n_rows <= 0) return hipSuccess;
-  if (a.t.lds_bytes > 160 * 1024 || a.t.CS > 128) return hipErrorInvalidValue;
-  return a.t.CS > 64 ? launch_gemm_dw_nu<2>(a, s) : launch_gemm_dw_nu<1>(a, s);
+  if (a.t.lds_bytes > 160 * 1024) return hipErrorInvalidValue;
+  switch (a.t.CS) {
+    case 128: return launch_gemm_dw_nu<1, 8>(a, s);
+    case 64: return launch_gemm_dw_nu<1, 4>(a, s);
+    case 32: return launch_gemm_dw_nu<1, 2>(a, s);
+    case 16: return launch_gemm_dw_nu<1, 1>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemm_dy(const GemmBwdArgs& a, hipStream_t s) {

@@ -265,6 +265,8 @@ struct GemmBwdArgs {
   // dy plan
   int n_grows, n_ent, off_rows, off_yptr, off_yent;
 };
+// dw plan: its row table [n_blocks][16] follows the K list, 16-byte aligned
+constexpr int gemm_dw_rowtab_offset(const TpGemmArgs& a) { return (a.off_klist + a.n_klist + 3) / 4 * 4; }
 size_t gemm_dw_lds_bytes(const TpGemmArgs& a);
 size_t gemm_dy_lds_bytes(const GemmBwdArgs& a);
 hipError_t launch_gemm_dw(const GemmBwdArgs& a, hipStream_t s);

@@ -63,15 +63,35 @@ def run_gemm(plan, y, xin, w, dout):
 
 
 def run_dw(plan, y, x, dz):
-    """dw[P] = sum_M dz[oo + M] (A_P x)[M], one block per path."""
+    """dw[P] = sum over the rows (P, M) of dz[o] (A x)[row]: tiles of four
+    quads of rows stacked per x irrep (A stored with a row stride of 16),
+    each quad one path's (16 t + rel) and each row naming its dz row."""
     A = _A(plan, y)
-    dw = np.zeros((x.shape[0], plan[5], x.shape[2]))
-    for b, (oo, rows, kl, base) in enumerate(_blocks(plan)):
-        z = np.zeros((x.shape[0], rows, x.shape[2]))
-        for k, ent in enumerate(kl):
+    nb, P, off_b, off_k, off_rt = plan[1], plan[5], plan[10], plan[11], plan[8]
+    blocks = plan[off_b:off_b + 4 * nb].reshape(nb, 4)
+    rowtab = plan[off_rt:off_rt + 16 * nb].reshape(nb, 16)
+    dw = np.zeros((x.shape[0], P, x.shape[2]))
+    base = 0
+    for b, (t, rows, kb, K) in enumerate(blocks):
+        assert 4 <= rows <= 16 and rows % 4 == 0 and K % 4 == 0 and K <= 16
+        z = np.zeros((x.shape[0], 16, x.shape[2]))
+        for k in range(K):
+            ent = plan[off_k + kb + k]
             if ent >= 0:
-                z += A[:, base + k * rows: base + (k + 1) * rows, None] * x[:, ent & 0xFFFF][:, None, :]
-        dw[:, b] = (dz[:, oo:oo + rows] * z).sum(axis=1)
+                z += A[:, base + 16 * k: base + 16 * (k + 1), None] * x[:, ent][:, None, :]
+        for r in range(16):
+            e = rowtab[b, r]
+            rel, o = e & 1023, e >> 10
+            assert rel == rowtab[b, r - r % 4] & 1023  # one path per quad
+            if r >= rows:
+                assert e == 16
+            if o == 0:  # a padding row: A stays zero there
+                assert not A[:, base + r: base + 16 * K: 16].any()
+                continue
+            assert rel < 16
+            dw[:, 16 * t + rel] += dz[:, o - 1] * z[:, r]
+        base += 16 * K
+    assert base == plan[9]
     return dw
 
 
