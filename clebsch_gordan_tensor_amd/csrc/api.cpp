@@ -1328,23 +1328,28 @@ e3_status build_gemm_dw(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpG
   return ok();
 }
 
-// The gradient of y (E3_GEN_GEMM_DY): per row and x irrep i,
-//   G_i[(P,M)][m1] = sum_q w[P][q] dz[oo_P + M][q] x[xoff_i + m1][q]
-// (rows: the (path, M) pairs of the paths from x irrep i, in path order,
-// padded to a multiple of 16; columns m1 < 16), then
-//   dy[yi] = sum over the CG entries (P, M, m1, yi, c) of c G_i[(P,M)][m1].
+// The gradient of y (E3_GEN_GEMM_DY): per row, the channel sums
+//   G_P[M][m1] = sum_q w[P][q] dz[oo_P + M][q] x[xoff_P + m1][q]
+// as matrix products with the channel sum as K, then
+//   dy[yi] = sum over the CG entries (P, M, m1, yi, c) of c G_P[M][m1].
+// A block is a group of paths sharing its columns: the components m1 of x
+// irrep i, rows (P, M) for the paths from i with l1 >= l3 (every path with
+// E3_OUT_PER_PATH); or the components M of output irrep k, rows (P, m1) for
+// the paths into k with l1 < l3 -- so the 16 columns are the wider side.
+// Rows are padded to a multiple of 16.  The operands come from one staged
+// slab of rows: x [0, dx), w [dx, dx + P), dz [dx + P, dx + P + dout).
 // Layout: header kGemmHeader words (magic + 7, n_blocks, dx, dy, dout, P,
-// n_rows, n_ent, 0, 0, off_blocks, off_rows, off_yptr, off_yent, words);
-// blocks [nb][4]: x offset, columns (2l1+1), first G row, rows (x16);
-// rows [n_rows]: (P << 16) | dz component, -1 for padding; yptr [dy+1];
-// yent [n_ent][2]: G index (row * 16 + column), coefficient bits -- the
-// entries of each y component in a fixed order.
+// n_rows, n_ent, 0, 0, off_blocks, off_rows, off_yptr, words, off_yent);
+// blocks [nb][4]: first column's slab row, columns, first G row, rows (x16);
+// rows [n_rows]: P | (slab row of the row's own operand) << 16, -1 for
+// padding; yptr [dy+1]; yent [n_ent][2]: G index (row * 16 + column),
+// coefficient bits -- the entries of each y component in a fixed order.
 e3_status build_gemm_dy(const e3_desc* desc, std::vector<int32_t>& out, int* dims) {
   Parsed p;
   std::vector<GenEntry> ent;
   e3_status s = generic_entries(desc, p, ent, false);
   if (s != E3_OK) return s;
-  if (p.P > 32767 || p.dx > 65535 || p.dout > 65535)
+  if (p.P > 32767 || p.dx + p.P + p.dout > 65535)
     return fail(E3_ERR_UNSUPPORTED, "too many paths or components");
   std::vector<int> xoff(p.x.size()), ooff(p.o.size()), oo_path(p.P);
   for (size_t i = 0, o = 0; i < p.x.size(); ++i) xoff[i] = int(o), o += 2 * p.x[i].l + 1;
@@ -1353,25 +1358,45 @@ e3_status build_gemm_dy(const e3_desc* desc, std::vector<int32_t>& out, int* dim
     oo_path[pi] = p.per_path ? opp : ooff[p.pio[pi]];
     opp += 2 * p.o[p.pio[pi]].l + 1;
   }
-  const int nb = int(p.x.size());
-  std::vector<int> b_row0(nb), b_nrows(nb), path_row(p.P);
-  std::vector<int32_t> rows;
-  for (int b = 0; b < nb; ++b) {
-    if (2 * p.x[b].l + 1 > 16) return fail(E3_ERR_UNSUPPORTED, "x degree above 7");
-    b_row0[b] = int(rows.size());
+  const int zrow0 = p.dx + p.P;  // slab row of dz component 0
+  auto x_keyed = [&](int pi) { return p.per_path || p.x[p.pix[pi]].l >= p.o[p.pio[pi]].l; };
+  std::vector<int32_t> blocks, rows;
+  std::vector<int> path_row(p.P);
+  auto add_block = [&](int col_row, int ncols, auto&& member, auto&& own_row, auto&& n_own) {
+    bool any = false;
+    for (int pi = 0; pi < p.P; ++pi) any = any || member(pi);
+    if (!any) return true;
+    if (ncols > 16) return false;
+    const int r0 = int(rows.size());
     for (int pi = 0; pi < p.P; ++pi) {
-      if (p.pix[pi] != b) continue;
+      if (!member(pi)) continue;
       path_row[pi] = int(rows.size());
-      for (int M = 0; M < 2 * p.o[p.pio[pi]].l + 1; ++M) rows.push_back((pi << 16) | (oo_path[pi] + M));
+      for (int i = 0; i < n_own(pi); ++i) rows.push_back(pi | own_row(pi, i) << 16);
     }
-    while ((rows.size() - b_row0[b]) % 16) rows.push_back(-1);
-    b_nrows[b] = int(rows.size()) - b_row0[b];
-  }
+    while ((rows.size() - r0) % 16) rows.push_back(-1);
+    blocks.insert(blocks.end(), {col_row, ncols, r0, int(rows.size()) - r0});
+    return true;
+  };
+  for (size_t i = 0; i < p.x.size(); ++i)
+    if (!add_block(
+            xoff[i], 2 * p.x[i].l + 1,
+            [&](int pi) { return p.pix[pi] == int(i) && x_keyed(pi); },
+            [&](int pi, int M) { return zrow0 + oo_path[pi] + M; },
+            [&](int pi) { return 2 * p.o[p.pio[pi]].l + 1; }))
+      return fail(E3_ERR_UNSUPPORTED, "x degree above 7");
+  for (size_t k = 0; k < p.o.size(); ++k)
+    if (!add_block(
+            zrow0 + ooff[k], 2 * p.o[k].l + 1,
+            [&](int pi) { return p.pio[pi] == int(k) && !x_keyed(pi); },
+            [&](int pi, int m1) { return xoff[p.pix[pi]] + m1; },
+            [&](int pi) { return 2 * p.x[p.pix[pi]].l + 1; }))
+      return fail(E3_ERR_UNSUPPORTED, "output degree above 7");
+  const int nb = int(blocks.size() / 4);
   std::vector<std::vector<std::pair<int, float>>> by_y(p.dy);
   for (const GenEntry& e : ent) {
-    const int b = p.pix[e.P];
-    const int row = path_row[e.P] + (e.o - oo_path[e.P]);
-    by_y[e.yi].push_back({row * 16 + (e.xi - xoff[b]), e.c});
+    const int M = e.o - oo_path[e.P], m1 = e.xi - xoff[p.pix[e.P]];
+    const int gi = x_keyed(e.P) ? (path_row[e.P] + M) * 16 + m1 : (path_row[e.P] + m1) * 16 + M;
+    by_y[e.yi].push_back({gi, e.c});
   }
   const int off_blocks = e3k::kGemmHeader, off_rows = off_blocks + 4 * nb;
   const int off_yptr = off_rows + int(rows.size());
@@ -1384,12 +1409,7 @@ e3_status build_gemm_dy(const e3_desc* desc, std::vector<int32_t>& out, int* dim
                             n_ent, 0, 0, off_blocks, off_rows, off_yptr, words};
   std::copy(head, head + 14, out.begin());
   out[e3k::kGemmHeader - 2] = off_yent;  // the header's last spare word
-  for (int b = 0; b < nb; ++b) {
-    out[off_blocks + 4 * b] = xoff[b];
-    out[off_blocks + 4 * b + 1] = 2 * p.x[b].l + 1;
-    out[off_blocks + 4 * b + 2] = b_row0[b];
-    out[off_blocks + 4 * b + 3] = b_nrows[b];
-  }
+  std::copy(blocks.begin(), blocks.end(), out.begin() + off_blocks);
   std::copy(rows.begin(), rows.end(), out.begin() + off_rows);
   int k = 0;
   for (int y = 0; y < p.dy; ++y) {
@@ -1671,8 +1691,7 @@ e3_status gemm_backward_setup(const e3_desc* desc, const Parsed& p, const void* 
   if (!tdx.CS || !bdw.t.CS || !bdy.t.CS)
     return fail(E3_ERR_UNSUPPORTED, "a dense-product backward plan does not fit in LDS");
   const int XS = e3k::gemm_row_stride(std::max(tdx.CS, bdw.t.CS));
-  if ((p.P + 1) * XS > 65535 || std::max(p.dx, p.dout) * XS > 65535 ||
-      std::max(p.P, p.dout) * (bdy.t.CS + 4) > 65535)
+  if ((p.P + 1) * XS > 65535 || std::max(p.dx, p.dout) * XS > 65535)
     return fail(E3_ERR_UNSUPPORTED, "too many components or paths for the dense-product kernels");
   tdx.lds_bytes = e3k::tp_gemm_lds_bytes(tdx);
   bdw.t.lds_bytes = e3k::gemm_dw_lds_bytes(bdw.t);

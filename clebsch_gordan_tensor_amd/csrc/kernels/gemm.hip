@@ -604,12 +604,17 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
 
 // The gradient of y in the dense form (plan E3_GEN_GEMM_DY): per row (or
 // edge), one workgroup over every channel slab in turn:
-//   G_i[(P,M)][m1] = sum_q w[P][q] dz[oo_P + M][q] x[xoff_i + m1][q]
-// on the fp32 matrix cores with the channel sum as the product's K (the A
-// operand w dz formed per lane from the staged slabs, B = x), 16-row tiles
-// of G owned by one wavefront each and added up over the slabs in LDS, then
-// dy[yi] = sum of c G over the plan's entries of yi, in the plan's order.
-__global__ void __launch_bounds__(256) k_gemm_dy(GemmBwdArgs a) {
+//   G_P[M][m1] = sum_q w[P][q] dz[oo_P + M][q] x[xoff_P + m1][q]
+// on the fp32 matrix cores with the channel sum as the product's K: per
+// block, the columns are the components of one x irrep (rows (P, M)) or of
+// one output irrep (rows (P, m1)); the A operand w times the row's own
+// operand is formed per lane from the staged slab, B is the column operand.
+// 16-row tiles of G are owned by one wavefront each and added up over the
+// slabs in LDS, then dy[yi] = sum of c G over the plan's entries of yi, in
+// the plan's order.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
+  constexpr int NT = 64 * NW;
   extern __shared__ __align__(16) float gsm[];
   const TpGemmArgs& g = a.t;
   const int* __restrict__ blocks = g.plan + g.off_blocks;
@@ -624,18 +629,19 @@ __global__ void __launch_bounds__(256) k_gemm_dy(GemmBwdArgs a) {
   float* s_w = s_x + g.dx * XS;
   float* s_z = s_w + g.P * XS;
   float* s_g = s_z + g.dout * XS;                          // G [n_grows][16]
-  int* s_r = reinterpret_cast<int*>(s_g + a.n_grows * 16);  // per G row: w and dz offsets
-  int* s_b = s_r + a.n_grows;                               // per G row: x block offset, columns
-  for (int i = threadIdx.x; i < a.n_grows; i += 256) {
+  int* s_r = reinterpret_cast<int*>(s_g + a.n_grows * 16);  // per G row: w row | own row << 16
+  int* s_b = s_r + a.n_grows;  // per G row: its block's first column row | columns << 16
+  const int n_srows = g.dx + g.P + g.dout;  // slab rows: x, w, dz
+  for (int i = threadIdx.x; i < a.n_grows; i += NT) {
     const int ent = grows[i];
-    const int P = ent < 0 ? 0 : min(ent >> 16, g.P - 1);
-    const int o = ent < 0 ? 0 : min(ent & 0xFFFF, g.dout - 1);
-    s_r[i] = ent < 0 ? -1 : (P * XS) | (o * XS) << 16;
+    const int P = ent < 0 ? 0 : min(ent & 0xFFFF, g.P - 1);
+    const int own = ent < 0 ? 0 : min(ent >> 16, n_srows - 1);
+    s_r[i] = ent < 0 ? -1 : P | own << 16;
     s_b[i] = 0;
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < g.n_blocks; b += 256) {
-    const int xo = min(max(blocks[4 * b], 0), g.dx - 1);
+  for (int b = threadIdx.x; b < g.n_blocks; b += NT) {
+    const int xo = min(max(blocks[4 * b], 0), n_srows - 1);
     const int nc = min(max(blocks[4 * b + 1], 0), 16);
     const int r0 = max(blocks[4 * b + 2], 0), nr = max(blocks[4 * b + 3], 0);
     for (int r = r0; r < min(r0 + nr, a.n_grows); ++r) s_b[r] = xo | nc << 16;
@@ -649,15 +655,15 @@ __global__ void __launch_bounds__(256) k_gemm_dy(GemmBwdArgs a) {
     float* dyr = a.out + row * g.dy;
     __syncthreads();  // the previous row's LDS reads are done
     if (xr < 0 || xr >= a.n_x) {  // padding edge (uniform): zero gradient
-      for (int i = threadIdx.x; i < g.dy; i += 256) dyr[i] = 0.0f;
+      for (int i = threadIdx.x; i < g.dy; i += NT) dyr[i] = 0.0f;
       continue;
     }
     const int64_t zr = a.rowptr ? receiver_of(a.rowptr, a.n_zrows, row) : row;
-    for (int i = threadIdx.x; i < a.n_grows * 16; i += 256) s_g[i] = 0.0f;
+    for (int i = threadIdx.x; i < a.n_grows * 16; i += NT) s_g[i] = 0.0f;
     for (int sl = 0; sl < n_slabs; ++sl) {
       const int c0 = sl * CS;
       __syncthreads();  // the previous slab's LDS reads are done (and s_g is cleared)
-      for (int u = threadIdx.x; u < U; u += 256) {
+      for (int u = threadIdx.x; u < U; u += NT) {
         const int r = u >> lg4, c = 4 * (u & ((1 << lg4) - 1));
         const float* src = r < g.dx ? g.x + (int64_t(xr) * g.dx + r) * C
                          : r < g.dx + g.P ? g.w + (row * g.P + (r - g.dx)) * C
@@ -668,7 +674,7 @@ __global__ void __launch_bounds__(256) k_gemm_dy(GemmBwdArgs a) {
       __syncthreads();
       // two tiles at a time (independent accumulators), four K steps per
       // batch with their LDS reads issued first
-      for (int t0 = 2 * wave; t0 < n_gt; t0 += 8) {
+      for (int t0 = 2 * wave; t0 < n_gt; t0 += 2 * NW) {
         const float* wp[2];
         const float* zp[2];
         const float* xp[2];
@@ -677,11 +683,11 @@ __global__ void __launch_bounds__(256) k_gemm_dy(GemmBwdArgs a) {
         for (int h = 0; h < 2; ++h) {
           const int t = min(t0 + h, n_gt - 1);
           const int ro = s_r[16 * t + li];
-          const int bx = s_b[16 * t];  // x block of the tile (uniform)
+          const int bx = s_b[16 * t];  // column block of the tile (uniform)
           const int xo = bx & 0xFFFF, nc = bx >> 16;
-          wp[h] = s_w + (ro < 0 ? 0 : ro & 0xFFFF) + kq;
-          zp[h] = s_z + (ro < 0 ? 0 : ro >> 16) + kq;
-          xp[h] = s_x + min(xo + min(li, max(nc - 1, 0)), g.dx - 1) * XS + kq;
+          wp[h] = s_w + (ro < 0 ? 0 : ro & 0xFFFF) * XS + kq;
+          zp[h] = s_x + (ro < 0 ? 0 : ro >> 16) * XS + kq;
+          xp[h] = s_x + min(xo + min(li, max(nc - 1, 0)), n_srows - 1) * XS + kq;
           aok[h] = ro >= 0 && t0 + h < n_gt;
           bok[h] = li < nc;
         }
@@ -714,7 +720,7 @@ __global__ void __launch_bounds__(256) k_gemm_dy(GemmBwdArgs a) {
     __syncthreads();
     // dy[y]: a wavefront per component, its entries strided over the lanes,
     // then the fixed-order wavefront sum
-    for (int y = wave; y < g.dy; y += 4) {
+    for (int y = wave; y < g.dy; y += NW) {
       float acc = 0.0f;
       const int k0 = max(yptr[y], 0), k1 = min(yptr[y + 1], a.n_ent);
       for (int k = k0 + lane; k < k1; k += 64) {
@@ -817,17 +823,19 @@ hipError_t launch_gemm_dw(const GemmBwdArgs& a, hipStream_t s) {
   }
 }
 
+// eight wavefronts: the LDS (slabs and G) allows about one workgroup per CU
 hipError_t launch_gemm_dy(const GemmBwdArgs& a, hipStream_t s) {
+  constexpr int NW = 8;
   if (a.t.n_rows <= 0) return hipSuccess;
   if (a.t.lds_bytes > 160 * 1024 || a.n_grows % 16) return hipErrorInvalidValue;
   static std::atomic<bool> lds_set{false};
   if (const hipError_t e =
-          set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_gemm_dy), 160 * 1024);
+          set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_gemm_dy<NW>), 160 * 1024);
       e != hipSuccess)
     return e;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
   const int grid = int(std::min<int64_t>(a.t.n_rows, int64_t(256) * std::min(per_cu, 8)));
-  hipLaunchKernelGGL(k_gemm_dy, dim3(grid), dim3(256), a.t.lds_bytes, s, a);
+  hipLaunchKernelGGL(k_gemm_dy<NW>, dim3(grid), dim3(64 * NW), a.t.lds_bytes, s, a);
   return hipGetLastError();
 }
 

@@ -96,16 +96,20 @@ def run_dw(plan, y, x, dz):
 
 
 def run_dy(plan, x, w, dz, dy_dim):
+    """G[row][col] = sum_q w[P] own[q] col[q] over the slab rows [x; w; dz],
+    then dy[yi] = sum of c G over yi's entries."""
     nb, off_b, off_r, off_yp, off_ye = plan[1], plan[10], plan[11], plan[12], plan[14]
     blocks = plan[off_b:off_b + 4 * nb].reshape(nb, 4)
     rows = plan[off_r:off_r + plan[6]]
+    slab = np.concatenate([x, w, dz], axis=1)
     G = np.zeros((x.shape[0], rows.shape[0], 16))
-    for xo, ncol, r0, nr in blocks:
+    for co, ncol, r0, nr in blocks:
+        assert 1 <= ncol <= 16 and nr % 16 == 0
         for r in range(r0, r0 + nr):
             if rows[r] < 0:
                 continue
-            P, o = rows[r] >> 16, rows[r] & 0xFFFF
-            G[:, r, :ncol] = np.einsum("bq,bcq->bc", w[:, P] * dz[:, o], x[:, xo:xo + ncol])
+            P, own = rows[r] & 0xFFFF, rows[r] >> 16
+            G[:, r, :ncol] = np.einsum("bq,bcq->bc", w[:, P] * slab[:, own], slab[:, co:co + ncol])
     yptr = plan[off_yp:off_yp + dy_dim + 1]
     ye = plan[off_ye:off_ye + 2 * yptr[-1]].reshape(-1, 2)
     cf = ye[:, 1].copy().view(np.float32).astype(np.float64)
