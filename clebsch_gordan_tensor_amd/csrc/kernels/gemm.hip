@@ -421,7 +421,7 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
 
 // Receiver of edge e in a CSR by receiver: the largest b with rowptr[b] <= e
 // (so empty rows are passed over), clamped to [0, n_nodes).
-__host__ __device__ constexpr int gemm_dy_row_stride(int CS) { return CS + 4; }
+__host__ __device__ constexpr int gemm_dy_row_stride(int CS) { return CS + 2; }
 
 __device__ __forceinline__ int receiver_of(const int* __restrict__ rowptr, int n_nodes, int64_t e) {
   int lo = 0, hi = n_nodes;
@@ -621,8 +621,9 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
   const int* __restrict__ grows = g.plan + a.off_rows;
   const int* __restrict__ yptr = g.plan + a.off_yptr;
   const int* __restrict__ yent = g.plan + a.off_yent;
-  // rows staged with a stride of 4 (mod 32) floats: a K step reads 16 rows
-  // at four consecutive channels, which then fall in distinct banks
+  // rows staged with a stride of 2 (mod 32) floats: a K step's read takes
+  // 16 rows at consecutive channels, and each half wavefront (two channels
+  // of 16 rows) then falls in 32 distinct banks
   const int CS = g.CS, C = g.C, XS = gemm_dy_row_stride(CS);
   const int lg4 = __builtin_ctz(CS / 4);
   float* s_x = gsm;
@@ -668,8 +669,10 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
         const float* src = r < g.dx ? g.x + (int64_t(xr) * g.dx + r) * C
                          : r < g.dx + g.P ? g.w + (row * g.P + (r - g.dx)) * C
                                           : a.dz + (zr * g.dout + (r - g.dx - g.P)) * C;
-        *reinterpret_cast<float4v*>(s_x + r * XS + c) =
-            *reinterpret_cast<const float4v*>(src + c0 + c);
+        const float4v v = *reinterpret_cast<const float4v*>(src + c0 + c);
+        float* d = s_x + r * XS + c;  // 8-byte aligned (XS is even)
+        *reinterpret_cast<float2*>(d) = float2{v[0], v[1]};
+        *reinterpret_cast<float2*>(d + 2) = float2{v[2], v[3]};
       }
       __syncthreads();
       // two tiles at a time (independent accumulators), four K steps per
