@@ -448,6 +448,9 @@ __device__ __forceinline__ int receiver_of(const int* __restrict__ rowptr, int n
 // A read is one fixed offset.  One workgroup of NW wavefronts per (row,
 // slab of CS = 16 NW NU channels).
 __host__ __device__ constexpr int gemm_dw_a_slack() { return 256; }
+// rows staged with a stride of 4 (mod 32) floats: a quad's rows four apart
+// (the next quad of one path) then fall in the other half of the banks
+__host__ __device__ constexpr int gemm_dw_row_stride(int CS) { return CS + 4; }
 
 template <int NU, int NW>
 __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
@@ -458,7 +461,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
   const int* __restrict__ klist = g.plan + g.off_klist;
   const int* __restrict__ rowtab = g.plan + gemm_dw_rowtab_offset(g);
   const int4* __restrict__ groups = reinterpret_cast<const int4*>(g.plan + g.off_groups);
-  const int CS = g.CS, C = g.C, XS = gemm_row_stride(CS);
+  const int CS = g.CS, C = g.C, XS = gemm_dw_row_stride(CS);
   const int lg4 = __builtin_ctz(CS / 4);
   const int a4 = ((g.a_floats + 3) & ~3) + gemm_dw_a_slack();
   float* s_a = gsm;                    // A [tiles][K][16], then slack for reads past the last
@@ -789,7 +792,7 @@ hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
 }
 
 size_t gemm_dw_lds_bytes(const TpGemmArgs& a) {
-  const int XS = gemm_row_stride(a.CS);
+  const int XS = gemm_dw_row_stride(a.CS);
   return size_t(((a.a_floats + 3) & ~3) + gemm_dw_a_slack() + (a.dx + 1 + a.dout) * XS +
                 20 * a.n_blocks + a.n_klist + a.dy) * 4;
 }
