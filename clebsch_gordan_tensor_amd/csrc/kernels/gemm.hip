@@ -439,7 +439,8 @@ __device__ __forceinline__ int receiver_of(const int* __restrict__ rowptr, int n
 // quad padded) into tiles of at most four quads, all of one x irrep and of
 // one group of 16 paths.  Per tile, on the fp32 matrix cores: D = A x over
 // the irrep's K steps (their x operand held in registers across the
-// irrep's tiles); the lane holding a quad's four rows forms
+// irrep's tiles, read from x in memory); the lane holding a quad's four
+// rows forms
 // sum_i D[row i] dz[row i] (in row order; padding rows read a zero row);
 // and the quads' sums go into the group's 16 paths as a second product
 // S E with S[P][quad] = 1 where the quad belongs to P, accumulated over the
@@ -464,23 +465,22 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
   const int CS = g.CS, C = g.C, XS = gemm_dw_row_stride(CS);
   const int lg4 = __builtin_ctz(CS / 4);
   const int a4 = ((g.a_floats + 3) & ~3) + gemm_dw_a_slack();
-  float* s_a = gsm;                    // A [tiles][K][16], then slack for reads past the last
-  float* s_x = s_a + a4;               // [dx + 1][XS]: x slab, then a row of zeros (K padding)
-  float* s_z = s_x + (g.dx + 1) * XS;  // the row's dz slab [dout][XS]
-  int* s_rt = reinterpret_cast<int*>(s_z + g.dout * XS);  // rows [n_blocks][16], staged
-  int* s_bd = s_rt + 16 * g.n_blocks;                        // descriptors [n_blocks][4]
-  int* s_k = s_bd + 4 * g.n_blocks;                          // K list as x row offsets
+  float* s_a = gsm;                         // A [tiles][K][16], then slack for reads past the last
+  float* s_z = s_a + a4;                    // [dout + 1][XS]: a row of zeros, then the dz slab
+  int* s_rt = reinterpret_cast<int*>(s_z + (g.dout + 1) * XS);  // rows [n_blocks][16], staged
+  int* s_bd = s_rt + 16 * g.n_blocks;                              // descriptors [n_blocks][4]
+  int* s_k = s_bd + 4 * g.n_blocks;                                // K list: x component or -1
   float* s_y = reinterpret_cast<float*>(s_k + g.n_klist);
   for (int i = threadIdx.x; i < g.n_klist; i += NT) {
     const int ent = klist[i];
-    s_k[i] = (ent < 0 || ent >= g.dx ? g.dx : ent) * XS;
+    s_k[i] = ent < 0 || ent >= g.dx ? -1 : ent;
   }
-  // rows: word offset from s_x of the row's dz row (row dx of s_x: zeros) |
-  // its path in the group of 16 << 20 (16: none)
+  // rows: word offset in s_z of the row's dz row (row 0: zeros) | its path
+  // in the group of 16 << 20 (16: none)
   for (int i = threadIdx.x; i < 16 * g.n_blocks; i += NT) {
     const int e = rowtab[i];
     const int z = e < 0 ? 0 : min(e >> 10, g.dout), rel = e < 0 ? 16 : min(e & 31, 16);
-    s_rt[i] = (g.dx + z) * XS | rel << 20;
+    s_rt[i] = z * XS | rel << 20;
   }
   for (int b = threadIdx.x; b < g.n_blocks; b += NT) {  // clamped to the plan's extents
     const int kb = min(max(blocks[4 * b + 2], 0), max(g.n_klist - 1, 0));
@@ -490,14 +490,14 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
     s_bd[4 * b + 2] = kb;
     s_bd[4 * b + 3] = K;
   }
-  for (int i = threadIdx.x; i < XS; i += NT) s_x[g.dx * XS + i] = 0.0f;
+  for (int i = threadIdx.x; i < XS; i += NT) s_z[i] = 0.0f;
   for (int i = threadIdx.x; i < a4; i += NT) s_a[i] = 0.0f;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, kq = lane >> 4;
   const int n_slabs = C / CS;
   const bool active = wave < CS / (16 * NU);
   const int64_t n_items = g.n_rows * n_slabs;
-  const int U = (g.dx + g.dout) << lg4;
+  const int U = g.dout << lg4;
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int64_t row = item / n_slabs;
     const int c0 = int(item - row * n_slabs) * CS;
@@ -511,10 +511,8 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
     const int64_t zr = a.rowptr ? receiver_of(a.rowptr, a.n_zrows, row) : row;
     for (int u = threadIdx.x; u < U; u += NT) {
       const int r = u >> lg4, c = 4 * (u & ((1 << lg4) - 1));
-      const float* src = r < g.dx ? g.x + (int64_t(xr) * g.dx + r) * C
-                                  : a.dz + (zr * g.dout + (r - g.dx)) * C;
-      float* dst = r < g.dx ? s_x + r * XS : s_z + (r - g.dx) * XS;
-      *reinterpret_cast<float4v*>(dst + c) = *reinterpret_cast<const float4v*>(src + c0 + c);
+      *reinterpret_cast<float4v*>(s_z + (r + 1) * XS + c) =
+          *reinterpret_cast<const float4v*>(a.dz + (zr * g.dout + r) * C + c0 + c);
     }
     for (int i = threadIdx.x; i < g.dy; i += NT) s_y[i] = g.y[row * g.dy + i];
     __syncthreads();
@@ -541,7 +539,8 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
           if (P >= 0 && P < g.P) dwr[int64_t(P) * C + 16 * (wave + NW * u) + li] = acc[u][r];
         }
     };
-    const float* zl = s_x + 16 * wave + li;  // this lane's channel in an x or dz row
+    const float* zl = s_z + 16 * wave + li;  // this lane's channel in a dz row
+    const float* xl = g.x + int64_t(xr) * g.dx * C + c0 + 16 * wave + li;  // and in x
     int cur = 0, cur_kb = -1, cur_K = -1, abase = 0;
     float xb[4][NU];
     // the tiles' descriptors from LDS, the next one read while this one runs
@@ -566,16 +565,14 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
         cur = t;
       }
       if (kb != cur_kb || K != cur_K) {  // a new x irrep: its K steps' x operand
-        int xo[4];
+        int xi[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xo[j] = s_k[min(kb + 4 * j + kq, g.n_klist - 1)];
+        for (int j = 0; j < 4; ++j) xi[j] = 4 * j < K ? s_k[min(kb + 4 * j + kq, g.n_klist - 1)] : -1;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int u = 0; u < NU; ++u) {
-            const float v = s_x[xo[j] + 16 * (wave + NW * u) + li];
-            xb[j][u] = 4 * j < K ? v : 0.0f;
-          }
+          for (int u = 0; u < NU; ++u)
+            xb[j][u] = xi[j] >= 0 ? xl[int64_t(xi[j]) * C + 16 * NW * u] : 0.0f;
         cur_kb = kb;
         cur_K = K;
       }
@@ -793,7 +790,7 @@ hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
 
 size_t gemm_dw_lds_bytes(const TpGemmArgs& a) {
   const int XS = gemm_dw_row_stride(a.CS);
-  return size_t(((a.a_floats + 3) & ~3) + gemm_dw_a_slack() + (a.dx + 1 + a.dout) * XS +
+  return size_t(((a.a_floats + 3) & ~3) + gemm_dw_a_slack() + (a.dout + 1) * XS +
                 20 * a.n_blocks + a.n_klist + a.dy) * 4;
 }
 
