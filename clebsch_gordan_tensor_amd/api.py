@@ -55,6 +55,7 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_tp_backward_generic", "e3_conv_forward_generic", "e3_conv_backward_generic",
            "e3_conv_double_backward_generic", "e3_check_graph", "e3_check_graph_host", "e3_conv_backward_noalloc",
            "e3_tp_backward_gemm", "e3_conv_backward_gemm",
+           "e3_radial_hidden_size", "e3_radial_hidden", "e3_conv_forward_radial_hidden",
            "e3_release_all",
            "e3_last_error"]
 E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY, E3_GEN_GEMM = 0, 1, 2, 3, 4
@@ -93,6 +94,10 @@ def lib():
     L.e3_radial_mlp.argtypes = [C.POINTER(_CRadial), i32, i32, vp, vp, vp]
     L.e3_conv_forward_radial.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp,
                                          C.POINTER(_CRadial), vp, vp]
+    L.e3_radial_hidden_size.argtypes = [i32, C.POINTER(sz)]
+    L.e3_radial_hidden.argtypes = [C.POINTER(_CRadial), i32, vp, vp, sz, vp]
+    L.e3_conv_forward_radial_hidden.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp,
+                                                C.POINTER(_CRadial), vp, sz, vp, vp]
     L.e3_generic_plan_size.argtypes = [dp, i32, C.POINTER(sz)]
     L.e3_generic_plan_build.argtypes = [dp, i32, vp, sz]
     L.e3_tp_backward_generic.argtypes = [dp, i64, vp, sz, vp, sz, vp, sz, vp, vp, vp, vp, vp, vp,
@@ -612,6 +617,46 @@ def conv_forward_radial(desc: Desc, rowptr, sender, edge_vec, x, cutoff, W1, W2,
     _check(lib().e3_conv_forward_radial(C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender),
                                         _ptr(workspace), wsb, _ptr(edge_vec), _ptr(x), C.byref(r),
                                         _ptr(out), _stream(stream)))
+    return out
+
+
+def radial_hidden(edge_vec, cutoff, W1, W2, out=None, stream=None):
+    """The radial MLP's hidden layer of every edge in the packed operand form
+    conv_forward_radial_hidden reads (uint8 [E * 256])."""
+    import torch
+    E = edge_vec.shape[0]
+    _need(edge_vec, "edge_vec", shape=(E, 3), dtype=torch.float32)
+    r = _radial(cutoff, W1, W2)
+    n = C.c_size_t()
+    _check(lib().e3_radial_hidden_size(E, C.byref(n)))
+    if out is None:
+        out = torch.empty(n.value, device=edge_vec.device, dtype=torch.uint8)
+    nb = out.numel() * out.element_size()
+    _check(lib().e3_radial_hidden(C.byref(r), E, _ptr(edge_vec), _ptr(out), nb, _stream(stream)))
+    return out
+
+
+def conv_forward_radial_hidden(desc: Desc, rowptr, sender, edge_vec, x, cutoff, W1, W2, hidden,
+                               out=None, workspace=None, stream=None):
+    """conv_forward_radial with the hidden layer from radial_hidden."""
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    _need(edge_vec, "edge_vec", shape=(E, 3), dtype=torch.float32)
+    _need(x, "x", shape=(N, desc.dx, desc.channels), dtype=torch.float32)
+    r = _radial(cutoff, W1, W2)
+    if W2.shape[1] != num_paths(desc) * desc.channels:
+        raise ValueError("W2 must have P*C columns")
+    if out is None:
+        out = torch.empty((N, desc.dout, desc.channels), device=x.device, dtype=torch.float32)
+    _need(out, "out", shape=(N, desc.dout, desc.channels), dtype=torch.float32)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    hb = hidden.numel() * hidden.element_size()
+    _check(lib().e3_conv_forward_radial_hidden(C.byref(desc.c()), N, E, _ptr(rowptr),
+                                               _ptr(sender), _ptr(workspace), wsb, _ptr(edge_vec),
+                                               _ptr(x), C.byref(r), _ptr(hidden), hb, _ptr(out),
+                                               _stream(stream)))
     return out
 
 

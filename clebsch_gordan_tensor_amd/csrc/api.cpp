@@ -815,10 +815,39 @@ e3_status e3_radial_mlp(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
                     "radial_mlp");
 }
 
-e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
-                                 const int32_t* rowptr, const int32_t* sender,
-                                 const void* workspace, size_t ws_bytes, const float* edge_vec,
-                                 const float* x, const e3_radial* mlp, float* m, void* stream) {
+e3_status e3_radial_hidden_size(int32_t n_edges, size_t* bytes) {
+  if (!bytes) return fail(E3_ERR_INVALID_ARG, "bytes is null");
+  if (n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  *bytes = size_t(n_edges) * e3k::kRadialHiddenBytes;
+  return ok();
+}
+
+e3_status e3_radial_hidden(const e3_radial* mlp, int32_t n_edges, const float* edge_vec,
+                           void* hidden, size_t h_bytes, void* stream) {
+  e3_status s = check_radial(mlp);
+  if (s != E3_OK) return s;
+  if (n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_edges == 0) return ok();
+  if (!edge_vec || !hidden) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (h_bytes < size_t(n_edges) * e3k::kRadialHiddenBytes)
+    return fail(E3_ERR_WORKSPACE, "hidden needs " +
+                                      std::to_string(size_t(n_edges) * e3k::kRadialHiddenBytes) +
+                                      " bytes");
+  if (!aligned16(hidden)) return fail(E3_ERR_ALIGNMENT, "hidden must be 16-byte aligned");
+  return hip_status(e3k::launch_radial_hidden(n_edges, edge_vec, mlp->cutoff, mlp->W1, hidden,
+                                              hipStream_t(stream)),
+                    "radial_hidden");
+}
+
+}  // extern "C"
+
+namespace {
+
+e3_status conv_forward_radial_impl(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                   const int32_t* rowptr, const int32_t* sender,
+                                   const void* workspace, size_t ws_bytes, const float* edge_vec,
+                                   const float* x, const e3_radial* mlp, const void* hidden,
+                                   size_t h_bytes, float* m, void* stream) {
   Parsed p;
   e3_status s = parse(desc, p);
   if (s != E3_OK) return s;
@@ -845,10 +874,40 @@ e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n
       return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
     order = static_cast<const int*>(workspace) + e3k::transpose_layout(n_nodes, n_edges).order;
   }
+  if (hidden) {
+    if (h_bytes < size_t(n_edges) * e3k::kRadialHiddenBytes)
+      return fail(E3_ERR_WORKSPACE, "hidden needs " +
+                                        std::to_string(size_t(n_edges) * e3k::kRadialHiddenBytes) +
+                                        " bytes");
+    if (!aligned16(hidden)) return fail(E3_ERR_ALIGNMENT, "hidden must be 16-byte aligned");
+  }
   e3k::RadialConvArgs a{n_nodes, n_edges, p.C, order, rowptr, sender, edge_vec, x,
-                        mlp->W1, mlp->W2, mlp->cutoff, m};
+                        mlp->W1, mlp->W2, mlp->cutoff, m, hidden};
   return hip_status(e3k::launch_conv_fwd_radial(ks->name, a, hipStream_t(stream)),
                     "conv_forward_radial");
+}
+
+}  // namespace
+
+extern "C" {
+
+e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                 const int32_t* rowptr, const int32_t* sender,
+                                 const void* workspace, size_t ws_bytes, const float* edge_vec,
+                                 const float* x, const e3_radial* mlp, float* m, void* stream) {
+  return conv_forward_radial_impl(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes,
+                                  edge_vec, x, mlp, nullptr, 0, m, stream);
+}
+
+e3_status e3_conv_forward_radial_hidden(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                        const int32_t* rowptr, const int32_t* sender,
+                                        const void* workspace, size_t ws_bytes,
+                                        const float* edge_vec, const float* x,
+                                        const e3_radial* mlp, const void* hidden, size_t h_bytes,
+                                        float* m, void* stream) {
+  if (!hidden) return fail(E3_ERR_INVALID_ARG, "hidden is null");
+  return conv_forward_radial_impl(desc, n_nodes, n_edges, rowptr, sender, workspace, ws_bytes,
+                                  edge_vec, x, mlp, hidden, h_bytes, m, stream);
 }
 
 namespace {

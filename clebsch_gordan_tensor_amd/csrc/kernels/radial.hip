@@ -119,6 +119,47 @@ __device__ __forceinline__ void hidden_operands(const float (&B)[kRadBasis], boo
   }
 }
 
+// The hidden layer of every edge in the operand form the fused convolution
+// reads (kRadialHiddenBytes per edge): the basis of the workgroup's 64 edges
+// first (one thread per edge, into LDS), then thread (edge, quarter q) forms
+// units 32 ks + 8 q + (0..7) for ks = 0, 1 exactly as the convolution would,
+// and stores the fp16 high and scaled low parts at [e][ks][q][hi, lo].
+// Every edge is written (its sender is not known here; the convolution
+// zeroes the operands of padding edges itself).
+__global__ void __launch_bounds__(256)
+    k_radial_hidden(int n_edges, const float* __restrict__ vec, float rc,
+                    const float* __restrict__ W1, half8* __restrict__ h) {
+  __shared__ __align__(16) float s_w1[kRadBasis * kRadHidden];
+  __shared__ float s_bas[64][kRadBasis + 1];
+  for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
+  const int64_t e0 = int64_t(blockIdx.x) * 64;
+  if (threadIdx.x < 64) {
+    const int64_t e = e0 + threadIdx.x;
+    float B[kRadBasis];
+    if (e < n_edges)
+      bessel_basis(vec[e * 3], vec[e * 3 + 1], vec[e * 3 + 2], rc, B);
+    else
+      bessel_basis(0.0f, 0.0f, 0.0f, rc, B);
+#pragma unroll
+    for (int n = 0; n < kRadBasis; ++n) s_bas[threadIdx.x][n] = B[n];
+  }
+  __syncthreads();
+  const int64_t e = e0 + (threadIdx.x >> 2);
+  const int q = int(threadIdx.x & 3);
+  if (e >= n_edges) return;
+  float B[kRadBasis];
+#pragma unroll
+  for (int n = 0; n < kRadBasis; ++n) B[n] = s_bas[threadIdx.x >> 2][n];
+  half8 ah[2], al[2];
+  hidden_operands(B, true, s_w1, q, ah, al);
+  half8* o = h + e * 16;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    o[(ks * 4 + q) * 2] = ah[ks];
+    o[(ks * 4 + q) * 2 + 1] = al[ks];
+  }
+}
+
 // w[e][j] for all edges; workgroup = (column slab, edge-tile group), 4 waves,
 // one 16-edge tile per wave at a time.  The product h W2 runs on the fp16
 // matrix cores with the same high/low split as the fused convolution below
@@ -290,13 +331,15 @@ constexpr size_t radial_lds_bytes() {
          + size_t(kRadWaves) * kRadChunk * sizeof(int);                     // senders
 }
 
-template <class S>
+// HG: the hidden layer's operands come from k_radial_hidden (hid) instead of
+// being formed here, once per 32-channel slab, from the edge's basis.
+template <class S, bool HG>
 __global__ void __launch_bounds__(64 * kRadWaves, 1)
     k_conv_fwd_radial(int n_nodes, int n_edges, int C, int n_slabs, const int* __restrict__ order,
                       const int* __restrict__ rowptr, const int* __restrict__ sender,
                       const float* __restrict__ vec, const float* __restrict__ x,
                       const float* __restrict__ W1, const float* __restrict__ W2, float rc,
-                      float* __restrict__ m) {
+                      const half8* __restrict__ hid, float* __restrict__ m) {
   using PL = Plan<S>;
   constexpr int NP = PL::NP, DX = PL::DX, DY = PL::DY, DO = PL::DO, YS = DY + 1;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -356,10 +399,12 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
           vz = vec[int64_t(e) * 3 + 2];
         }
         sn[lane] = (sr >= 0 && sr < n_nodes) ? sr : -1;
-        float B[kRadBasis];
-        bessel_basis(vx, vy, vz, rc, B);
+        if constexpr (!HG) {
+          float B[kRadBasis];
+          bessel_basis(vx, vy, vz, rc, B);
 #pragma unroll
-        for (int n = 0; n < kRadBasis; ++n) bs[lane * kRadBasis + n] = B[n];
+          for (int n = 0; n < kRadBasis; ++n) bs[lane * kRadBasis + n] = B[n];
+        }
         float Y[DY];
         edge_y_from_vec<S>(vx, vy, vz, Y);
 #pragma unroll
@@ -375,10 +420,23 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
         half8 ah[2], al[2];
         {
           const int row = t * 16 + li;
-          float B[kRadBasis];
+          if constexpr (HG) {
+            // a padding edge (or a row past the list) takes zero operands;
+            // otherwise the row's edge c0 + row < end is in [0, n_edges)
+            const bool ok = sn[row] >= 0;
+            const half8* hp = hid + int64_t(ok ? c0 + row : 0) * 16 + gq * 2;
 #pragma unroll
-          for (int n = 0; n < kRadBasis; ++n) B[n] = bs[row * kRadBasis + n];
-          hidden_operands(B, sn[row] >= 0, s_w1, gq, ah, al);
+            for (int ks = 0; ks < 2; ++ks) {
+              const half8 vh = hp[ks * 8], vl = hp[ks * 8 + 1];
+              ah[ks] = ok ? vh : half8{};
+              al[ks] = ok ? vl : half8{};
+            }
+          } else {
+            float B[kRadBasis];
+#pragma unroll
+            for (int n = 0; n < kRadBasis; ++n) B[n] = bs[row * kRadBasis + n];
+            hidden_operands(B, sn[row] >= 0, s_w1, gq, ah, al);
+          }
         }
         // x of this lane's contraction rows t*16 + 4*gq + rr, channels chan + 16*cb
         float xv[4][DX][2];
@@ -439,19 +497,25 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
   }
 }
 
-template <class S>
-hipError_t launch_fwd_radial(const RadialConvArgs& a, hipStream_t s) {
+template <class S, bool HG>
+hipError_t launch_fwd_radial_hg(const RadialConvArgs& a, hipStream_t s) {
   const size_t lds = radial_lds_bytes<S>();
   // the attribute is per function: raised once, retried after a failure
   static std::atomic<bool> lds_set{false};
-  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_conv_fwd_radial<S>), int(lds));
+  if (const hipError_t e = set_max_lds_once(
+          lds_set, reinterpret_cast<const void*>(&k_conv_fwd_radial<S, HG>), int(lds));
       e != hipSuccess)
     return e;
   const int n_slabs = a.C / 32;
-  hipLaunchKernelGGL(k_conv_fwd_radial<S>, dim3(kRadXcds * 32), dim3(64 * kRadWaves), lds, s,
+  hipLaunchKernelGGL((k_conv_fwd_radial<S, HG>), dim3(kRadXcds * 32), dim3(64 * kRadWaves), lds, s,
                      a.n_nodes, a.n_edges, a.C, n_slabs, a.order, a.rowptr, a.sender, a.vec, a.x,
-                     a.W1, a.W2, a.cutoff, a.m);
+                     a.W1, a.W2, a.cutoff, static_cast<const half8*>(a.hidden), a.m);
   return hipGetLastError();
+}
+
+template <class S>
+hipError_t launch_fwd_radial(const RadialConvArgs& a, hipStream_t s) {
+  return a.hidden ? launch_fwd_radial_hg<S, true>(a, s) : launch_fwd_radial_hg<S, false>(a, s);
 }
 
 // ------------------------------------------------ radial MLP backward
@@ -1003,6 +1067,14 @@ hipError_t launch_conv_fwd_radial(const char* set_name, const RadialConvArgs& a,
   if (a.n_nodes <= 0) return hipSuccess;
   if (set_name && std::strcmp(set_name, "L1to3") == 0) return launch_fwd_radial<SigL1to3>(a, s);
   return hipErrorNotSupported;
+}
+
+hipError_t launch_radial_hidden(int n_edges, const float* vec, float cutoff, const float* W1,
+                                void* h, hipStream_t s) {
+  if (n_edges <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_radial_hidden, dim3(unsigned((int64_t(n_edges) + 63) / 64)), dim3(256), 0,
+                     s, n_edges, vec, cutoff, W1, static_cast<half8*>(h));
+  return hipGetLastError();
 }
 
 hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cutoff,

@@ -197,8 +197,14 @@ struct RadialConvArgs {
   const float* W2;   // [64][P*C]
   float cutoff;
   float* m;          // [N][dout][C] float32
+  const void* hidden = nullptr;  // the hidden layer's packed operands per edge, or null
 };
 bool radial_conv_supported(const char* set_name);
+// The radial MLP's hidden layer per edge in the fused convolution's operand
+// form: [E][2 ks][4 quarters][hi, lo] fp16 x 8 (256 bytes per edge).
+constexpr size_t kRadialHiddenBytes = 256;
+hipError_t launch_radial_hidden(int n_edges, const float* vec, float cutoff, const float* W1,
+                                void* h, hipStream_t s);
 hipError_t launch_conv_fwd_radial(const char* set_name, const RadialConvArgs& a, hipStream_t s);
 hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cutoff,
                              const float* W1, const float* W2, float* w, hipStream_t s);

@@ -244,6 +244,29 @@ e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n
                                  const void* workspace, size_t ws_bytes, const float* edge_vec,
                                  const float* x, const e3_radial* mlp, float* m, void* stream);
 
+/* The radial MLP's hidden layer h = silu(B(|r_e|) W1) of every edge (e3j
+ * A.3, Eq.7's edge scalars; the reading above), computed once per edge and
+ * stored in the operand form e3_conv_forward_radial_hidden reads:
+ * e3_radial_hidden_size bytes (256 per edge: per edge, for k-halves 0..1 and
+ * quarters 0..3, the fp16 high part and the 2^11-scaled fp16 low part of
+ * units 32 k + 8 q .. 32 k + 8 q + 7, each 8 halves).  It depends only on
+ * the edge vectors, the cutoff and W1.  hidden: caller-owned device memory,
+ * 16-byte aligned; E3_ERR_WORKSPACE when h_bytes is too small. */
+e3_status e3_radial_hidden_size(int32_t n_edges, size_t* bytes);
+e3_status e3_radial_hidden(const e3_radial* mlp, int32_t n_edges, const float* edge_vec,
+                           void* hidden, size_t h_bytes, void* stream);
+/* e3_conv_forward_radial with the hidden layer read from `hidden` (written
+ * by e3_radial_hidden for the same edge vectors, cutoff and W1) instead of
+ * being formed again for every 32-channel slab of the output: bitwise the
+ * same m.  The other arguments and limits are those of
+ * e3_conv_forward_radial. */
+e3_status e3_conv_forward_radial_hidden(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                        const int32_t* rowptr, const int32_t* sender,
+                                        const void* workspace, size_t ws_bytes,
+                                        const float* edge_vec, const float* x,
+                                        const e3_radial* mlp, const void* hidden, size_t h_bytes,
+                                        float* m, void* stream);
+
 /* Backward of e3_radial_mlp for the cotangent dw [E][n_cols] (n_cols a
  * multiple of 32): dW1 [8][64] and dW2 [64][n_cols] (summed over the edges
  * through fixed partials: reproducible) and dvec [E][3], the part of the

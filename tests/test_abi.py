@@ -396,3 +396,28 @@ def test_release_all_then_rebuild(lib):
     api.release_all()
     api.release_all()  # twice is fine
     assert size() == n1 > 0
+
+
+def test_radial_hidden_arg_errors(lib):
+    # the hidden-layer entry points check sizes and alignment on the host,
+    # before any device work (the pointers below are never dereferenced)
+    nb = C.c_size_t()
+    assert lib.e3_radial_hidden_size(1000, C.byref(nb)) == 0 and nb.value == 256 * 1000
+    assert lib.e3_radial_hidden_size(-1, C.byref(nb)) == -1
+    fk, odd = C.c_void_p(0x10000), C.c_void_p(0x10004)
+    r = api._CRadial(5.0, 8, 64, fk, fk)
+    assert lib.e3_radial_hidden(C.byref(r), 0, None, None, 0, None) == 0
+    assert lib.e3_radial_hidden(C.byref(r), 10, fk, fk, 256 * 10 - 1, None) == -6  # WORKSPACE
+    assert lib.e3_radial_hidden(C.byref(r), 10, fk, odd, 256 * 10, None) == -4  # ALIGNMENT
+    assert lib.e3_radial_hidden(C.byref(r), 10, None, fk, 256 * 10, None) == -1
+    bad = api._CRadial(5.0, 8, 32, fk, fk)
+    assert lib.e3_radial_hidden(C.byref(bad), 10, fk, fk, 256 * 10, None) == -3
+    x01 = [(0, 1), (1, -1)]
+    sh3 = [(0, 1), (1, -1), (2, 1), (3, -1)]
+    d = api.Desc(x01, sh3, sh3, 32)
+    assert lib.e3_conv_forward_radial_hidden(C.byref(d.c()), 4, 8, fk, fk, None, 0, fk, fk,
+                                             C.byref(r), None, 0, fk, None) == -1
+    assert lib.e3_conv_forward_radial_hidden(C.byref(d.c()), 4, 8, fk, fk, None, 0, fk, fk,
+                                             C.byref(r), fk, 8 * 256 - 16, fk, None) == -6
+    assert lib.e3_conv_forward_radial_hidden(C.byref(d.c()), 4, 8, fk, fk, None, 0, fk, fk,
+                                             C.byref(r), odd, 8 * 256, fk, None) == -4

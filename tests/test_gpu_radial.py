@@ -149,11 +149,52 @@ def test_radial_conv_full_size_sampled_and_deterministic(gpu):
     ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=ev)
     a = gpu.conv_forward_radial(d, rowptr, sender, ev, x, 5.0, dev(W1), dev(W2), workspace=ws)
     b = gpu.conv_forward_radial(d, rowptr, sender, ev, x, 5.0, dev(W1), dev(W2), workspace=ws)
+    h = gpu.radial_hidden(ev, 5.0, dev(W1), dev(W2))
+    c = gpu.conv_forward_radial_hidden(d, rowptr, sender, ev, x, 5.0, dev(W1), dev(W2), h,
+                                       workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(a.view(torch.int32), c.view(torch.int32))
     rows = np.sort(np.random.default_rng(3).choice(g.n_nodes, 150, replace=False))
     ref = R.conv_forward_radial(od, g.rowptr, g.sender, g.evec, xh, 5.0, W1, W2, rows=rows)
     assert_close(host(a)[rows], ref, TOL_F32, "radial conv 64k sampled")
+
+
+def test_radial_hidden_conv_bitwise(gpu):
+    # the hidden layer computed once per edge (e3_radial_hidden) and read by
+    # the convolution gives bitwise the m of the kernel that forms it per
+    # slab: padding edges, a hub of several tiles, isolated receivers, C = 64
+    # (two slabs) and 256; water3k with and without the locality order
+    g = _graph_c32()
+    for C in (64, 256):
+        d = gpu.Desc(X01, SH3, SH3, C)
+        x = np.random.default_rng(217).standard_normal((g.n_nodes, 4, C)).astype(np.float32)
+        W1, W2 = _weights(gpu.num_paths(d) * C, 218)
+        rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+        W1d, W2d = dev(W1), dev(W2)
+        h = gpu.radial_hidden(ev, 3.5, W1d, W2d)
+        a = gpu.conv_forward_radial(d, rowptr, sender, ev, dev(x), 3.5, W1d, W2d)
+        b = gpu.conv_forward_radial_hidden(d, rowptr, sender, ev, dev(x), 3.5, W1d, W2d, h)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), C
+    p = S.make_conv("water3k", with_dm=False)
+    g = p.graph
+    d = gpu.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    od = O.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    W1, W2 = _weights(O.num_paths(od) * p.channels, 219)
+    rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+    W1d, W2d = dev(W1), dev(W2)
+    ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=ev)
+    h = gpu.radial_hidden(ev, 5.0, W1d, W2d)
+    m = gpu.conv_forward_radial_hidden(d, rowptr, sender, ev, dev(p.x), 5.0, W1d, W2d, h,
+                                       workspace=ws)
+    m0 = gpu.conv_forward_radial_hidden(d, rowptr, sender, ev, dev(p.x), 5.0, W1d, W2d, h)
+    ref = gpu.conv_forward_radial(d, rowptr, sender, ev, dev(p.x), 5.0, W1d, W2d, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(m.view(torch.int32), ref.view(torch.int32))
+    assert torch.equal(m0.view(torch.int32), ref.view(torch.int32))
+    oref = R.conv_forward_radial(od, g.rowptr, g.sender, g.evec, p.x, 5.0, W1, W2)
+    assert_close(host(m), oref, TOL_F32, "radial conv with given hidden layer, water3k")
 
 
 def test_radial_conv_unsupported(gpu):
