@@ -26,7 +26,7 @@ namespace {
 constexpr int kScanBlock = 256;
 constexpr int kScanItems = 4;
 constexpr int kScanTile = kScanBlock * kScanItems;
-constexpr int kMortonBitsHost = 18;  // Morton cells: 6 bits per axis, 262,144 cells
+constexpr int kCellBitsHost = 18;  // cells: 6 bits per axis, 262,144 cells
 constexpr int kBfsLevels = 64;       // traversal launches (levels) per graph
 
 __global__ void __launch_bounds__(256) k_fill(int* __restrict__ p, int64_t n, int v) {
@@ -251,16 +251,45 @@ __global__ void __launch_bounds__(256)
 }
 
 // Spread the low 6 bits of v to every third bit.
-__device__ __forceinline__ int spread6(int v) {
-  int r = 0;
+// Index along the 3-d Hilbert curve of the cell (x, y, z) of a 64^3 grid,
+// by Skilling's transpose method ("Programming the Hilbert curve", AIP
+// Conf. Proc. 707, 2004): undo the curve's excess rotations and
+// reflections level by level from the top bit, Gray-encode across the axes,
+// then read the index off the bits of the three transposed coordinates,
+// most significant level first with x's bit above y's above z's.
+// Consecutive indices are face-adjacent cells, so a range of the order is a
+// connected piece of space (a Morton range can jump across the box).
+__device__ __forceinline__ int hilbert_key6(unsigned x, unsigned y, unsigned z) {
+  unsigned X[3] = {x, y, z};
+  for (unsigned q = 32u; q > 1u; q >>= 1) {
+    const unsigned p = q - 1u;
 #pragma unroll
-  for (int b = 0; b < 6; ++b) r |= ((v >> b) & 1) << (3 * b);
-  return r;
+    for (int i = 0; i < 3; ++i) {
+      if (X[i] & q) {
+        X[0] ^= p;
+      } else {
+        const unsigned t = (X[0] ^ X[i]) & p;
+        X[0] ^= t;
+        X[i] ^= t;
+      }
+    }
+  }
+  X[1] ^= X[0];
+  X[2] ^= X[1];
+  unsigned t = 0;
+  for (unsigned q = 32u; q > 1u; q >>= 1)
+    if (X[2] & q) t ^= q - 1u;
+  int key = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) key |= int(((X[i] ^ t) >> b) & 1u) << (3 * b + 2 - i);
+  return key;
 }
 
-// Morton code of the cell of each reached node; counts per cell.
+// Hilbert index of the cell of each reached node; counts per cell.
 __global__ void __launch_bounds__(256)
-    k_morton_keys(const int* __restrict__ n_ptr, int n_max, const int* __restrict__ order,
+    k_cell_keys(const int* __restrict__ n_ptr, int n_max, const int* __restrict__ order,
                   const float* __restrict__ pos, const int* __restrict__ box,
                   int* __restrict__ key, int* __restrict__ hist) {
   const int n = min(*n_ptr, n_max);
@@ -273,21 +302,20 @@ __global__ void __launch_bounds__(256)
   }
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
     const int v = order[i];
-    int c = 0;
+    unsigned q[3];
 #pragma unroll
-    for (int d = 0; d < 3; ++d) {
-      const int q = min(63, max(0, int((pos[3 * v + d] - lo[d]) * inv[d])));
-      c |= spread6(q) << d;
-    }
+    for (int d = 0; d < 3; ++d)
+      q[d] = unsigned(min(63, max(0, int((pos[3 * v + d] - lo[d]) * inv[d]))));
+    const int c = hilbert_key6(q[0], q[1], q[2]);
     key[i] = c;
     atomicAdd(hist + c, 1);
   }
 }
 
-// Scatter order[0 .. n) into cell order (cells by Morton code; inside a
+// Scatter order[0 .. n) into cell order (cells by Hilbert index; inside a
 // cell the order depends on timing, which only affects scheduling).
 __global__ void __launch_bounds__(256)
-    k_morton_scatter(const int* __restrict__ n_ptr, int n_max, const int* __restrict__ order,
+    k_cell_scatter(const int* __restrict__ n_ptr, int n_max, const int* __restrict__ order,
                      const int* __restrict__ key, const int* __restrict__ start,
                      int* __restrict__ cursor, int* __restrict__ out) {
   const int n = min(*n_ptr, n_max);
@@ -462,12 +490,12 @@ TransposeLayout transpose_layout(int64_t n_nodes, int64_t n_edges) {
   L.levels = o;
   o += up(kBfsLevels + 2);
   L.cell = o;
-  o += up((int64_t(1) << kMortonBitsHost) + 1);
+  o += up((int64_t(1) << kCellBitsHost) + 1);
   L.cell_cursor = o;
-  o += up(int64_t(1) << kMortonBitsHost);
+  o += up(int64_t(1) << kCellBitsHost);
   L.bsum = o;
   // tile sums of the largest scan (the cell counts or the node counts)
-  o += up((std::max<int64_t>(n_nodes + 1, (int64_t(1) << kMortonBitsHost) + 1) + kScanTile - 1) /
+  o += up((std::max<int64_t>(n_nodes + 1, (int64_t(1) << kCellBitsHost) + 1) + kScanTile - 1) /
               kScanTile +
           1);
   L.total_words = o;
@@ -476,7 +504,7 @@ TransposeLayout transpose_layout(int64_t n_nodes, int64_t n_edges) {
 
 // Traversal order of the nodes for the convolution kernels (ws + L.order):
 // breadth-first from node 0 over in-edges; with edge vectors, the reached
-// nodes are then re-sorted by the Morton cell of their position rebuilt
+// nodes are then re-sorted by the Hilbert-curve cell of their position rebuilt
 // along the traversal tree; every unreached node follows in index order.
 // Neighbouring nodes end up close in the order, so the wavefronts that run
 // together gather overlapping node rows.  Nothing comes back to the host:
@@ -504,19 +532,19 @@ hipError_t build_locality_order(int n_nodes, int n_edges, const int* rowptr, con
                        evec, pos, order, visited, tail, lev, done, i);
   const unsigned gn = grid_for(n_nodes, 256);
   if (pos) {
-    // spatially compact order of the reached nodes: Morton cells of the
+    // spatially compact order of the reached nodes: Hilbert cells of the
     // reconstructed positions, counting-sorted
     int* box = ws + L.box;
     int* key = ws + L.key;
     int* cell = ws + L.cell;
     int* cur = ws + L.cell_cursor;
-    const int64_t ncell = int64_t(1) << kMortonBitsHost;
+    const int64_t ncell = int64_t(1) << kCellBitsHost;
     hipLaunchKernelGGL(k_fill, dim3(1), dim3(64), 0, s, box, int64_t(3), INT_MAX);
     hipLaunchKernelGGL(k_fill, dim3(1), dim3(64), 0, s, box + 3, int64_t(3), INT_MIN);
     hipLaunchKernelGGL(k_fill, dim3(grid_for(ncell + 1, 256)), dim3(256), 0, s, cell, ncell + 1, 0);
     hipLaunchKernelGGL(k_fill, dim3(grid_for(ncell, 256)), dim3(256), 0, s, cur, ncell, 0);
     hipLaunchKernelGGL(k_bbox, dim3(gn), dim3(256), 0, s, tail, n_nodes, order, pos, box);
-    hipLaunchKernelGGL(k_morton_keys, dim3(gn), dim3(256), 0, s, tail, n_nodes, order, pos, box,
+    hipLaunchKernelGGL(k_cell_keys, dim3(gn), dim3(256), 0, s, tail, n_nodes, order, pos, box,
                        key, cell);
     const unsigned tiles = unsigned((ncell + 1 + kScanTile - 1) / kScanTile);
     hipLaunchKernelGGL(k_scan_tiles, dim3(tiles), dim3(kScanBlock), 0, s, cell, ncell + 1, cell,
@@ -524,7 +552,7 @@ hipError_t build_locality_order(int n_nodes, int n_edges, const int* rowptr, con
     hipLaunchKernelGGL(k_scan_tile_sums, dim3(1), dim3(kScanBlock), 0, s, ws + L.bsum, int(tiles));
     hipLaunchKernelGGL(k_scan_add, dim3(tiles), dim3(kScanBlock), 0, s, cell, ncell + 1,
                        ws + L.bsum);
-    hipLaunchKernelGGL(k_morton_scatter, dim3(gn), dim3(256), 0, s, tail, n_nodes, order, key, cell,
+    hipLaunchKernelGGL(k_cell_scatter, dim3(gn), dim3(256), 0, s, tail, n_nodes, order, key, cell,
                        cur, ws + L.order2);
     hipLaunchKernelGGL(k_copy_i32, dim3(gn), dim3(256), 0, s, ws + L.order2, order, tail, n_nodes);
   }
@@ -588,11 +616,11 @@ hipError_t launch_prepare_transpose(int n_nodes, int n_edges, const int* rowptr,
 namespace {
 
 // transpose_layout's arrays at the limits (five per edge, nine per node, the
-// Morton cells twice, plus alignment); the entry point checks the layout of
+// cell counts twice, plus alignment); the entry point checks the layout of
 // every call against it
 constexpr int64_t kNoAllocWords =
     (int64_t(5) * kNoAllocMaxEdges + int64_t(9) * kNoAllocMaxNodes +
-     2 * (int64_t(1) << kMortonBitsHost) + 16384 + 63) / 64 * 64;
+     2 * (int64_t(1) << kCellBitsHost) + 16384 + 63) / 64 * 64;
 
 __device__ __align__(256) int scratch[kNoAllocWords];
 

@@ -474,7 +474,7 @@ e3_status e3_conv_workspace_size(int32_t n_nodes, int32_t n_edges, size_t* bytes
  *  - a locality order of the nodes in which both passes visit them:
  *    breadth-first over in-edges from node 0; when edge_vec [E][3] (device,
  *    r = pos[receiver] - pos[sender]) is given, the reached nodes are then
- *    sorted by the Morton cell of their position rebuilt along the traversal
+ *    sorted by the Hilbert-curve cell of their position rebuilt along the traversal
  *    tree; unreached nodes follow in index order.  edge_vec may be NULL.
  * The order only changes which wavefront handles which node: results are
  * the same with any order.  Once per graph.  ws_bytes must be >=

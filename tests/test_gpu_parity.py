@@ -250,6 +250,27 @@ def test_transpose_index(gpu):
     assert np.array_equal(w2[o + 2 * up(E): o + 2 * up(E) + nr], perm[:nr])
 
 
+def test_locality_order_is_spatial(gpu):
+    # with edge vectors the order follows a space-filling curve over the
+    # rebuilt positions: consecutive nodes are close (a random order's steps
+    # average the box's mean pair distance, about half its side)
+    from clebsch_gordan_tensor_amd import api
+    g = S.random_graph(4000, 34.2, 5.0, seed=9)
+    ws = api.conv_prepare_transpose(dev(g.rowptr), dev(g.sender), edge_vec=dev(g.evec))
+    torch.cuda.synchronize()
+    words = ws.view(torch.int32).cpu().numpy()
+    up = lambda v: (v + 63) // 64 * 64
+    N, E = g.n_nodes, g.n_edges
+    o2 = 64 + 2 * up(N + 1) + 5 * up(E)
+    order = words[o2:o2 + N]
+    assert np.array_equal(np.sort(order), np.arange(N))
+    step = np.linalg.norm(g.pos[order[1:]] - g.pos[order[:-1]], axis=1)
+    rnd = np.linalg.norm(g.pos[1:] - g.pos[:-1], axis=1)
+    print(f"[order] median step {np.median(step):.2f} A, mean {step.mean():.2f} A "
+          f"(index order: {rnd.mean():.2f} A)", flush=True)
+    assert np.median(step) < 3.5 and step.mean() < 0.2 * rnd.mean()
+
+
 # ---------------------------------------------------- tensor product (rows)
 
 def _tp_check(gpu, rows, sample=None):
