@@ -56,6 +56,7 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_conv_double_backward_generic", "e3_check_graph", "e3_check_graph_host", "e3_conv_backward_noalloc",
            "e3_tp_backward_gemm", "e3_conv_backward_gemm",
            "e3_radial_hidden_size", "e3_radial_hidden", "e3_conv_forward_radial_hidden",
+           "e3_radial_mlp_hidden",
            "e3_release_all",
            "e3_last_error"]
 E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY, E3_GEN_GEMM = 0, 1, 2, 3, 4
@@ -96,6 +97,7 @@ def lib():
                                          C.POINTER(_CRadial), vp, vp]
     L.e3_radial_hidden_size.argtypes = [i32, C.POINTER(sz)]
     L.e3_radial_hidden.argtypes = [C.POINTER(_CRadial), i32, vp, vp, sz, vp]
+    L.e3_radial_mlp_hidden.argtypes = [C.POINTER(_CRadial), i32, i32, vp, sz, vp, vp]
     L.e3_conv_forward_radial_hidden.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp,
                                                 C.POINTER(_CRadial), vp, sz, vp, vp]
     L.e3_generic_plan_size.argtypes = [dp, i32, C.POINTER(sz)]
@@ -633,6 +635,20 @@ def radial_hidden(edge_vec, cutoff, W1, W2, out=None, stream=None):
         out = torch.empty(n.value, device=edge_vec.device, dtype=torch.uint8)
     nb = out.numel() * out.element_size()
     _check(lib().e3_radial_hidden(C.byref(r), E, _ptr(edge_vec), _ptr(out), nb, _stream(stream)))
+    return out
+
+
+def radial_mlp_hidden(hidden, n_edges, cutoff, W1, W2, out=None, stream=None):
+    """radial_mlp with the hidden layer from radial_hidden."""
+    import torch
+    r = _radial(cutoff, W1, W2)
+    n_cols = W2.shape[1]
+    if out is None:
+        out = torch.empty((n_edges, n_cols), device=hidden.device, dtype=torch.float32)
+    _need(out, "out", shape=(n_edges, n_cols), dtype=torch.float32)
+    hb = hidden.numel() * hidden.element_size()
+    _check(lib().e3_radial_mlp_hidden(C.byref(r), n_edges, n_cols, _ptr(hidden), hb, _ptr(out),
+                                      _stream(stream)))
     return out
 
 

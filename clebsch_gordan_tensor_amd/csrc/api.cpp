@@ -815,6 +815,25 @@ e3_status e3_radial_mlp(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
                     "radial_mlp");
 }
 
+e3_status e3_radial_mlp_hidden(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
+                               const void* hidden, size_t h_bytes, float* w, void* stream) {
+  e3_status s = check_radial(mlp);
+  if (s != E3_OK) return s;
+  if (n_edges < 0 || n_cols <= 0) return fail(E3_ERR_INVALID_ARG, "bad size");
+  if (n_cols % 16) return fail(E3_ERR_UNSUPPORTED, "n_cols must be a multiple of 16");
+  if (n_edges == 0) return ok();
+  if (!hidden || !w) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (h_bytes < size_t(n_edges) * e3k::kRadialHiddenBytes)
+    return fail(E3_ERR_WORKSPACE, "hidden needs " +
+                                      std::to_string(size_t(n_edges) * e3k::kRadialHiddenBytes) +
+                                      " bytes");
+  if (!aligned16(w) || !aligned16(hidden))
+    return fail(E3_ERR_ALIGNMENT, "w and hidden must be 16-byte aligned");
+  return hip_status(e3k::launch_radial_mlp(n_edges, n_cols, nullptr, mlp->cutoff, mlp->W1,
+                                           mlp->W2, w, hipStream_t(stream), hidden),
+                    "radial_mlp_hidden");
+}
+
 e3_status e3_radial_hidden_size(int32_t n_edges, size_t* bytes) {
   if (!bytes) return fail(E3_ERR_INVALID_ARG, "bytes is null");
   if (n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");

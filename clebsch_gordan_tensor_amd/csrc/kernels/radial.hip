@@ -177,10 +177,13 @@ constexpr size_t mlp_lds_bytes() {
          + size_t(4) * 16 * kMlpTileStride * sizeof(float);   // result tiles
 }
 
+// HG: the hidden layer's operands come from k_radial_hidden (hid) instead of
+// being formed here for every column slab.
+template <bool HG>
 __global__ void __launch_bounds__(256)
     k_radial_mlp(int n_edges, int n_cols, int n_slabs, int n_groups, const float* __restrict__ vec,
                  float rc, const float* __restrict__ W1, const float* __restrict__ W2,
-                 float* __restrict__ w) {
+                 const half8* __restrict__ hid, float* __restrict__ w) {
   extern __shared__ __align__(16) unsigned char mlp_smem[];
   half8* s_w2 = reinterpret_cast<half8*>(mlp_smem);
   float* s_w1 = reinterpret_cast<float*>(mlp_smem + size_t(kMlpCols / 16) * 4 * 64 * sizeof(half8));
@@ -211,7 +214,17 @@ __global__ void __launch_bounds__(256)
   for (int tile = group * 4 + wave; tile < ntiles; tile += n_groups * 4) {
     const int er = tile * 16 + (lane & 15);
     half8 ah[2], al[2];
-    {
+    if constexpr (HG) {
+      const bool ok = er < n_edges;
+      const half8* hp = hid + int64_t(ok ? er : 0) * 16 + gq * 2;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const half8 vh = hp[ks * 8], vl = hp[ks * 8 + 1];
+        ah[ks] = ok ? vh : half8{};
+        al[ks] = ok ? vl : half8{};
+      }
+      wave_lds_fence();  // the previous tile's LDS reads are done
+    } else {
       float vx = 0.0f, vy = 0.0f, vz = 0.0f;
       if (er < n_edges) {
         const float* p = vec + int64_t(er) * 3;
@@ -1077,8 +1090,10 @@ hipError_t launch_radial_hidden(int n_edges, const float* vec, float cutoff, con
   return hipGetLastError();
 }
 
-hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cutoff,
-                             const float* W1, const float* W2, float* w, hipStream_t s) {
+template <bool HG>
+hipError_t launch_radial_mlp_hg(int n_edges, int n_cols, const float* vec, float cutoff,
+                                const float* W1, const float* W2, const void* hidden, float* w,
+                                hipStream_t s) {
   if (n_edges <= 0 || n_cols <= 0) return hipSuccess;
   const int n_slabs = (n_cols + kMlpCols - 1) / kMlpCols;
   const int ntiles = (n_edges + 15) / 16;
@@ -1086,12 +1101,21 @@ hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cu
   n_groups = max(1, min(n_groups, (ntiles + 3) / 4));
   // the attribute is per function: raised once, retried after a failure
   static std::atomic<bool> lds_set{false};
-  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_radial_mlp), int(mlp_lds_bytes()));
+  if (const hipError_t e = set_max_lds_once(
+          lds_set, reinterpret_cast<const void*>(&k_radial_mlp<HG>), int(mlp_lds_bytes()));
       e != hipSuccess)
     return e;
-  hipLaunchKernelGGL(k_radial_mlp, dim3(n_slabs * n_groups), dim3(256), mlp_lds_bytes(), s,
-                     n_edges, n_cols, n_slabs, n_groups, vec, cutoff, W1, W2, w);
+  hipLaunchKernelGGL(k_radial_mlp<HG>, dim3(n_slabs * n_groups), dim3(256), mlp_lds_bytes(), s,
+                     n_edges, n_cols, n_slabs, n_groups, vec, cutoff, W1, W2,
+                     static_cast<const half8*>(hidden), w);
   return hipGetLastError();
+}
+
+hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cutoff,
+                             const float* W1, const float* W2, float* w, hipStream_t s,
+                             const void* hidden) {
+  return hidden ? launch_radial_mlp_hg<true>(n_edges, n_cols, vec, cutoff, W1, W2, hidden, w, s)
+                : launch_radial_mlp_hg<false>(n_edges, n_cols, vec, cutoff, W1, W2, nullptr, w, s);
 }
 
 }  // namespace e3k

@@ -206,8 +206,10 @@ constexpr size_t kRadialHiddenBytes = 256;
 hipError_t launch_radial_hidden(int n_edges, const float* vec, float cutoff, const float* W1,
                                 void* h, hipStream_t s);
 hipError_t launch_conv_fwd_radial(const char* set_name, const RadialConvArgs& a, hipStream_t s);
+// hidden: the hidden layer from launch_radial_hidden, or null (formed per slab)
 hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cutoff,
-                             const float* W1, const float* W2, float* w, hipStream_t s);
+                             const float* W1, const float* W2, float* w, hipStream_t s,
+                             const void* hidden = nullptr);
 // pieces of the radial MLP's backward
 constexpr int kRadialTailChunks = 1024;
 hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const float* W1,

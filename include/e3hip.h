@@ -255,6 +255,13 @@ e3_status e3_conv_forward_radial(const e3_desc* desc, int32_t n_nodes, int32_t n
 e3_status e3_radial_hidden_size(int32_t n_edges, size_t* bytes);
 e3_status e3_radial_hidden(const e3_radial* mlp, int32_t n_edges, const float* edge_vec,
                            void* hidden, size_t h_bytes, void* stream);
+/* e3_radial_mlp with the hidden layer read from `hidden` (e3_radial_hidden of
+ * the same edge vectors, cutoff and W1) instead of being formed again for
+ * every 128-column slab of w: bitwise the same w.  No edge vectors needed;
+ * sizes, alignment and errors as e3_radial_mlp, plus E3_ERR_WORKSPACE when
+ * h_bytes is below e3_radial_hidden_size. */
+e3_status e3_radial_mlp_hidden(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,
+                               const void* hidden, size_t h_bytes, float* w, void* stream);
 /* e3_conv_forward_radial with the hidden layer read from `hidden` (written
  * by e3_radial_hidden for the same edge vectors, cutoff and W1) instead of
  * being formed again for every 32-channel slab of the output: bitwise the

@@ -410,6 +410,10 @@ def test_radial_hidden_arg_errors(lib):
     assert lib.e3_radial_hidden(C.byref(r), 10, fk, fk, 256 * 10 - 1, None) == -6  # WORKSPACE
     assert lib.e3_radial_hidden(C.byref(r), 10, fk, odd, 256 * 10, None) == -4  # ALIGNMENT
     assert lib.e3_radial_hidden(C.byref(r), 10, None, fk, 256 * 10, None) == -1
+    assert lib.e3_radial_mlp_hidden(C.byref(r), 10, 32, fk, 256 * 10 - 1, fk, None) == -6
+    assert lib.e3_radial_mlp_hidden(C.byref(r), 10, 32, fk, 256 * 10, odd, None) == -4
+    assert lib.e3_radial_mlp_hidden(C.byref(r), 10, 24, fk, 256 * 10, fk, None) == -3
+    assert lib.e3_radial_mlp_hidden(C.byref(r), 10, 32, None, 256 * 10, fk, None) == -1
     bad = api._CRadial(5.0, 8, 32, fk, fk)
     assert lib.e3_radial_hidden(C.byref(bad), 10, fk, fk, 256 * 10, None) == -3
     x01 = [(0, 1), (1, -1)]

@@ -197,6 +197,23 @@ def test_radial_hidden_conv_bitwise(gpu):
     assert_close(host(m), oref, TOL_F32, "radial conv with given hidden layer, water3k")
 
 
+@pytest.mark.parametrize("E,n_cols", [(3001, 1280), (17, 48), (1, 16)])
+def test_radial_mlp_hidden_bitwise(gpu, E, n_cols):
+    # w from the hidden layer computed once per edge equals e3_radial_mlp's
+    rng = np.random.default_rng(220 + E)
+    ev = (rng.standard_normal((E, 3)) * 2.0).astype(np.float32)
+    if E > 2:
+        ev[1] = 0.0
+    W1, W2 = _weights(n_cols, 221)
+    W1d, W2d, evd = dev(W1), dev(W2), dev(ev)
+    h = gpu.radial_hidden(evd, 5.0, W1d, W2d)
+    a = gpu.radial_mlp(evd, 5.0, W1d, W2d)
+    b = gpu.radial_mlp_hidden(h, E, 5.0, W1d, W2d)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert_close(host(b), R.radial_mlp(ev, 5.0, W1, W2), TOL_F32, f"radial mlp from hidden E={E}")
+
+
 def test_radial_conv_unsupported(gpu):
     d = gpu.Desc(SH3, SH3, SH3, 64)
     W1, W2 = _weights(23 * 64, 1)
