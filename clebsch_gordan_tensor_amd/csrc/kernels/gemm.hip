@@ -782,8 +782,11 @@ hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
   // smaller plans keep the registers for a third wavefront per SIMD.
   if (a.t.CS > 64) return hipErrorInvalidValue;
   // The harmonics of the edge vectors are a variant of their own (the bank's
-  // registers would otherwise cost the given-harmonics kernel its occupancy).
-  if (a.ly >= 0) return launch_conv_gemm_pre<0, 1, false, true>(a, std::min(per_cu, 8), s);
+  // registers would otherwise cost the given-harmonics kernel its occupancy),
+  // batched on the same rule.
+  if (a.ly >= 0)
+    return per_cu <= 2 ? launch_conv_gemm_pre<0, 1, true, true>(a, per_cu, s)
+                       : launch_conv_gemm_pre<0, 1, false, true>(a, std::min(per_cu, 8), s);
   return per_cu <= 2 ? launch_conv_gemm_pre<0, 1, true, false>(a, per_cu, s)
                      : launch_conv_gemm_pre<0, 1, false, false>(a, std::min(per_cu, 8), s);
 }
