@@ -934,8 +934,8 @@ namespace {
 // The radial MLP's second layer seen as a channel mixing: input 64x0e (h),
 // output nb blocks of cb x 0e (the columns of w in blocks of cb <= 256).
 struct RadialBwdPlan {
-  int ranges = 0;
-  size_t off_dh = 0, off_part2 = 0, off_part = 0, off_w2s = 0, total = 0;
+  int ranges = 0, slabs = 0;
+  size_t off_dh = 0, off_part2 = 0, off_part = 0, off_w2s = 0, off_basis = 0, total = 0;
 };
 
 e3_status radial_bwd_plan(int n_edges, int n_cols, RadialBwdPlan& r) {
@@ -948,10 +948,12 @@ e3_status radial_bwd_plan(int n_edges, int n_cols, RadialBwdPlan& r) {
     o += align256(bytes);
     return at;
   };
-  r.off_dh = take(size_t(n_edges) * 64 * 4);
+  r.slabs = e3k::radial_dw2_slabs(n_cols);
+  r.off_dh = take(size_t(r.slabs) * size_t(n_edges) * 64 * 4);
   r.off_part2 = take(size_t(r.ranges) * 64 * n_cols * 4);
   r.off_part = take(size_t(e3k::kRadialTailChunks) * 512 * 4);
   r.off_w2s = take(e3k::radial_w2_split_bytes(n_cols));
+  r.off_basis = take(size_t(n_edges) * 16 * 4);
   r.total = o;
   return ok();
 }
@@ -989,19 +991,21 @@ e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t 
   float* dh = reinterpret_cast<float*>(ws + r.off_dh);
   float* part2 = reinterpret_cast<float*>(ws + r.off_part2);
   float* part = reinterpret_cast<float*>(ws + r.off_part);
-  // dh = dw W2^T, and dW2 = h^T dw through per-range partials (bf16 matrix
-  // cores on three-part splits of the fp32 operands; dw is read once by each)
+  // dh = dw W2^T through per-slab partials, and dW2 = h^T dw through
+  // per-range partials (bf16 matrix cores on three-part splits of the fp32
+  // operands; one read of dw for both)
   if ((s = hip_status(e3k::launch_radial_dh_dw2(n_edges, n_cols, edge_vec, mlp->cutoff, mlp->W1,
                                                 mlp->W2, dw, dh, part2, r.ranges, ws + r.off_w2s,
-                                                st),
+                                                reinterpret_cast<float*>(ws + r.off_basis), st),
                       "radial_mlp_backward")) != E3_OK)
     return s;
   if ((s = hip_status(e3k::launch_sum_partials(r.ranges, 64 * n_cols, part2, dW2, st),
                       "radial_mlp_backward")) != E3_OK)
     return s;
   // through SiLU and the first layer: dW1, and the radial part of dvec
-  return hip_status(e3k::launch_radial_tail(n_edges, edge_vec, mlp->cutoff, mlp->W1, dh, dvec,
-                                            part, dW1, st),
+  return hip_status(e3k::launch_radial_tail(n_edges, edge_vec, mlp->W1,
+                                            reinterpret_cast<const float*>(ws + r.off_basis), dh,
+                                            r.slabs, dvec, part, dW1, st),
                     "radial_mlp_backward");
 }
 

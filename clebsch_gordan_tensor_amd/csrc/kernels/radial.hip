@@ -535,19 +535,41 @@ hipError_t launch_fwd_radial(const RadialConvArgs& a, hipStream_t s) {
 
 constexpr int kTailBatch = 64;
 
-// Per edge, from dh = dw W2^T: dpre = dh * silu'(pre), the radial part of
+// dh = the column slabs' partials added in slab order, into part 0:
+// part[0][i] = part[0][i] + part[1][i] + ... (16 bytes per thread).
+__global__ void __launch_bounds__(256)
+    k_radial_sum_slabs(int64_t n4, int n_parts, int64_t stride4, float4v* __restrict__ part) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4v v[8];
+  float4v acc = part[i];
+  for (int q0 = 1; q0 < n_parts; q0 += 8) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q0 + q < n_parts) v[q] = __builtin_nontemporal_load(part + (q0 + q) * stride4 + i);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q0 + q < n_parts) acc += v[q];
+  }
+  part[i] = acc;
+}
+
+// Per edge, from dh = dw W2^T [E][64] and the basis with its derivative
+// ([E][16], k_radial_basis):
+// dpre = dh * silu'(pre), the radial part of
 // the edge-vector gradient dvec = (sum_n B'_n(d) (dpre W1^T)_n) r / d, and
 // this chunk's partial dW1[n][k] = sum_e B_n(e) dpre_k(e) (fixed order).
 // One workgroup per chunk of edges, 64 edges per batch, in four phases: the
-// basis and its derivative per edge (fp64, one thread per edge); dpre with
+// basis and its derivative per edge (read); dpre with
 // thread (k, g) taking hidden unit k of every fourth edge, so a wavefront
 // reads an edge's dh row as one 256-byte access; g_n = sum_k dpre_k W1[n][k]
 // with four threads per edge, two n each; dvec per edge.  Every sum keeps
 // the order of a one-thread-per-edge evaluation.
 __global__ void __launch_bounds__(256)
-    k_radial_tail(int n_edges, int n_chunks, const float* __restrict__ vec, float rc,
-                  const float* __restrict__ W1, const float* __restrict__ dh,
-                  float* __restrict__ dvec, float* __restrict__ dW1_part) {
+    k_radial_tail(int n_edges, int n_chunks, const float* __restrict__ vec,
+                  const float* __restrict__ W1, const float* __restrict__ basis,
+                  const float* __restrict__ dh, float* __restrict__ dvec,
+                  float* __restrict__ dW1_part) {
   __shared__ float s_w1[kRadBasis * kRadHidden];
   __shared__ float s_b[kTailBatch][kRadBasis];
   __shared__ float s_bd[kTailBatch][kRadBasis + 1];
@@ -566,44 +588,34 @@ __global__ void __launch_bounds__(256)
   for (int n = 0; n < kRadBasis; ++n) w1c[n] = s_w1[n * kRadHidden + hk];
   for (int e0 = lo; e0 < hi; e0 += kTailBatch) {
     const int ne = min(kTailBatch, hi - e0);
-    if (threadIdx.x < ne) {
-      const int t = threadIdx.x;
-      const int64_t e = e0 + t;
-      const float vx = vec[e * 3], vy = vec[e * 3 + 1], vz = vec[e * 3 + 2];
-      const double d = sqrt(double(vx) * vx + double(vy) * vy + double(vz) * vz);
-      const double pref = sqrt(2.0 / double(rc));
-      if (d > 0.0) {
-        double sn, cs;
-        const double th = 3.141592653589793 * d / double(rc);
-        sincos(th, &sn, &cs);
-        // sin(n th), cos(n th) by the angle-addition recurrence; one
-        // division (fp64 divisions are long instruction sequences)
-        const double inv = 1.0 / d, k1 = 3.141592653589793 / double(rc);
-        double s_n = sn, c_n = cs;
+    // dh of this thread's edges (unit hk of edges hg + 4j); the loads go out
+    // before the basis is staged
+    float g[kTailBatch / 4];
 #pragma unroll
-        for (int n = 0; n < kRadBasis; ++n) {
-          const double kn = double(n + 1) * k1;
-          s_b[t][n] = float(pref * s_n * inv);
-          s_bd[t][n] = float(pref * (kn * c_n - s_n * inv) * inv);
-          const double s_next = s_n * cs + c_n * sn, c_next = c_n * cs - s_n * sn;
-          s_n = s_next;
-          c_n = c_next;
-        }
-      } else {
-#pragma unroll
-        for (int n = 0; n < kRadBasis; ++n) {
-          s_b[t][n] = float(pref * double(n + 1) * 3.141592653589793 / double(rc));
-          s_bd[t][n] = 0.0f;
-        }
-      }
+    for (int j = 0; j < kTailBatch / 4; ++j) {
+      const int t = hg + 4 * j;
+      g[j] = t < ne ? dh[(int64_t(e0) + t) * kRadHidden + hk] : 0.0f;
+    }
+    // the basis and its derivative of the batch's edges (16 floats each)
+    for (int i = threadIdx.x; i < ne * 2 * kRadBasis; i += 256) {
+      const int t = i >> 4, c = i & 15;
+      const float v = basis[(int64_t(e0) + t) * 2 * kRadBasis + c];
+      if (c < kRadBasis)
+        s_b[t][c] = v;
+      else
+        s_bd[t][c - kRadBasis] = v;
     }
     __syncthreads();
-    for (int t = hg; t < ne; t += 4) {
-      float pre = 0.0f;
 #pragma unroll
-      for (int n = 0; n < kRadBasis; ++n) pre = fmaf(s_b[t][n], w1c[n], pre);
-      const float sg = 1.0f / (1.0f + expf(-pre));
-      s_dp[t][hk] = dh[(int64_t(e0) + t) * kRadHidden + hk] * sg * (1.0f + pre * (1.0f - sg));
+    for (int j = 0; j < kTailBatch / 4; ++j) {
+      const int t = hg + 4 * j;
+      if (t < ne) {
+        float pre = 0.0f;
+#pragma unroll
+        for (int n = 0; n < kRadBasis; ++n) pre = fmaf(s_b[t][n], w1c[n], pre);
+        const float sg = 1.0f / (1.0f + expf(-pre));
+        s_dp[t][hk] = g[j] * sg * (1.0f + pre * (1.0f - sg));
+      }
     }
     __syncthreads();
     if (ge < ne) {
@@ -700,11 +712,13 @@ constexpr int kW2Units = 4 * 3 * 64;  // 16-byte units per 32-column block: [nt]
 // W2 [64][n_cols] in its three bf16 parts, in the B operand order of the dh
 // product: unit [cb][nt][part][lane] holds W2[16 nt + lane % 16]
 // [32 cb + 8 (lane / 16) + t], t = 0..7; blocks past n_cols / 32, up to a
-// whole LDS stage, are zeros.
-constexpr int kDhChunk = 4;  // 32-column blocks per LDS stage of the dh product
+// whole slab of the kernel below, are zeros.
+constexpr int kDhwWaves = 8;
+constexpr int kDhwCols = 32 * kDhwWaves;  // columns per slab: 32 per wavefront
+constexpr int kDhwBlocks = kDhwCols / 32;  // 32-column blocks per slab
 
 __host__ __device__ constexpr int w2_split_blocks(int n_cols) {
-  return (n_cols / 32 + kDhChunk - 1) / kDhChunk * kDhChunk;
+  return (n_cols / 32 + kDhwBlocks - 1) / kDhwBlocks * kDhwBlocks;
 }
 
 __global__ void __launch_bounds__(256)
@@ -728,150 +742,6 @@ __global__ void __launch_bounds__(256)
   for (int q = 0; q < 3; ++q) dst[64 * q] = as_u4(sp.p[q]);
 }
 
-// dh[e][k] = sum_j dw[e][j] W2[k][j].  One wavefront per 32 edges (two
-// 16-edge row tiles) and all 64 hidden units (four column tiles), four per
-// workgroup; a workgroup takes edge blocks of 128 in a grid-stride sequence
-// and W2's parts in LDS stages of four 32-column blocks.  Lane (i, q) takes
-// columns 8q..8q+7 of its edge's block (two 16-byte loads).  The loads form
-// one stream over (edge block, column block), kept about 12 KB deep per
-// wavefront (HBM latency under load needs ~100 KB in flight per CU): a ring
-// of four blocks, one slot per block of a stage, each slot refilled with the
-// block four ahead as soon as its values are split; and each stage's W2
-// parts one stage ahead, in registers, written to LDS between two barriers.
-// The loop's issue order is the same in every stage (W2 parts, then four
-// blocks), so each wait covers only the loads it needs.  Rows and blocks
-// past the end are loaded clamped and zeroed.  The leading products a0 b0
-// accumulate apart from the five smaller ones, so the rounding chain of the
-// sum is n_cols / 32 MFMAs long; the two are added at the end.
-constexpr int kDhRows = 2;               // 16-edge row tiles per wavefront
-constexpr int kDhEdges = 64 * kDhRows;   // edges per workgroup block (four wavefronts)
-constexpr int kDhStageUnits = kDhChunk * kW2Units / 256;  // 16-byte units per thread and stage
-
-__global__ void __launch_bounds__(256)
-    k_radial_dh(int n_edges, int n_cols, const float* __restrict__ dw,
-                const u32x4* __restrict__ w2s, float* __restrict__ dh) {
-  __shared__ u32x4 s_b[kDhChunk * kW2Units];  // 48 KB
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane & 15, kq = lane >> 4;
-  const int n_cb = n_cols / 32;
-  const int per = w2_split_blocks(n_cols);  // column blocks per edge block, whole stages
-  const int n_st = per / kDhChunk;
-  const int64_t n_blocks = (int64_t(n_edges) + kDhEdges - 1) / kDhEdges;
-  if (int64_t(blockIdx.x) >= n_blocks) return;  // whole workgroup, before any barrier
-  const int n_iter = int((n_blocks - 1 - blockIdx.x) / gridDim.x) + 1;
-  auto first_edge = [&](int i) {
-    return (int64_t(blockIdx.x) + int64_t(i) * gridDim.x) * kDhEdges + 16 * kDhRows * wave + li;
-  };
-  // the load stream: next block (edge block ld_i, column block ld_cb)
-  int ld_i = 0, ld_cb = 0;
-  auto load_block = [&](float4v (&slot)[kDhRows][2]) {
-    const int i = min(ld_i, n_iter - 1), cb = min(ld_cb, n_cb - 1);
-    const int64_t eb = first_edge(i);
-#pragma unroll
-    for (int mt = 0; mt < kDhRows; ++mt) {
-      const int64_t e = min(eb + 16 * mt, int64_t(n_edges) - 1);
-      const float* p = dw + e * n_cols + 32 * cb + 8 * kq;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        slot[mt][h] = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(p + 4 * h));
-    }
-    if (++ld_cb == per) {
-      ld_cb = 0;
-      ++ld_i;
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads where they are issued
-  };
-  auto load_stage = [&](int st, u32x4 (&stg)[kDhStageUnits]) {
-#pragma unroll
-    for (int j = 0; j < kDhStageUnits; ++j)
-      stg[j] = w2s[int64_t(st) * kDhChunk * kW2Units + j * 256 + threadIdx.x];
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  u32x4 stg[kDhStageUnits];
-  float4v ring[kDhChunk][kDhRows][2];
-  load_stage(0, stg);
-#pragma unroll
-  for (int c = 0; c < kDhChunk; ++c) load_block(ring[c]);
-  float4v D[kDhRows][4], X[kDhRows][4];
-#pragma unroll
-  for (int mt = 0; mt < kDhRows; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      D[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-      X[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-  int i = 0, st = 0;  // edge block and stage being computed
-  bool aval[kDhRows];
-#pragma unroll
-  for (int mt = 0; mt < kDhRows; ++mt) aval[mt] = first_edge(0) + 16 * mt < n_edges;
-  for (int q = 0; q < n_iter * n_st; ++q) {
-    __syncthreads();  // the previous stage's reads of s_b are done
-#pragma unroll
-    for (int j = 0; j < kDhStageUnits; ++j) s_b[j * 256 + threadIdx.x] = stg[j];
-    __syncthreads();
-    load_stage(st + 1 == n_st ? 0 : st + 1, stg);
-#pragma unroll
-    for (int c = 0; c < kDhChunk; ++c) {
-      const bool blk = st * kDhChunk + c < n_cb;
-      Split3 A[kDhRows];
-#pragma unroll
-      for (int mt = 0; mt < kDhRows; ++mt) {
-        const bool ok = blk && aval[mt];
-        float v[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          v[t] = ok ? ring[c][mt][0][t] : 0.0f;
-          v[4 + t] = ok ? ring[c][mt][1][t] : 0.0f;
-        }
-        split3(v, A[mt]);
-      }
-      load_block(ring[c]);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        Split3 B;
-#pragma unroll
-        for (int p = 0; p < 3; ++p) B.p[p] = as_b8(s_b[c * kW2Units + nt * 192 + 64 * p + lane]);
-#pragma unroll
-        for (int mt = 0; mt < kDhRows; ++mt) {
-          D[mt][nt] = mfma_bf16(A[mt].p[0], B.p[0], D[mt][nt]);
-          X[mt][nt] = cross5(A[mt], B, X[mt][nt]);
-        }
-      }
-    }
-    if (++st == n_st) {
-      // D row = edge 16 mt + 4 kq + r, column = hidden unit 16 nt + li
-      const int64_t e0 = first_edge(i) - li;
-#pragma unroll
-      for (int mt = 0; mt < kDhRows; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t e = e0 + 16 * mt + 4 * kq + r;
-          if (e < n_edges) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-              dh[e * kRadHidden + 16 * nt + li] = D[mt][nt][r] + X[mt][nt][r];
-          }
-        }
-#pragma unroll
-      for (int mt = 0; mt < kDhRows; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          D[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-          X[mt][nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-      st = 0;
-      ++i;
-#pragma unroll
-      for (int mt = 0; mt < kDhRows; ++mt) aval[mt] = first_edge(i) + 16 * mt < n_edges;
-    }
-  }
-}
-
-constexpr int kDw2Waves = 8;
-constexpr int kDw2Cols = 32 * kDw2Waves;  // columns per workgroup: 32 per wavefront
-constexpr int kDw2Step = 32;              // edges per K step
-constexpr int kDw2Ring = 4;               // steps in the load ring
-
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -879,137 +749,284 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // SiLU: h enters only sums over thousands of edges, where its last bits do
 // not show.
 __device__ __forceinline__ float silu_sum_operand(float t) {
-  return __fdividef(t, 1.0f + __expf(-t));
+  return t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
 }
 
-// Partial weight gradient of the second layer over one range of edges:
-//   part[range][k][c] = sum_{e in range} h[e][k] dw[e][c]
-// for the kDw2Cols-column slab of the workgroup (grid x = slabs, y = edge
-// ranges).  Per step of 32 edges the workgroup recomputes h (the forward
-// MLP's hidden layer: thread (b, n) < 256 evaluates basis function n of edge
-// b, thread (k, g) unit k of edges 4g..4g+3) and stores its three parts in
-// LDS in the A operand order; each wavefront owns 32 columns and all 64
-// hidden units (8 accumulator tiles).  Lane (i, q) loads 8 bytes (columns
-// 2i, 2i+1) of each of the edges 8q..8q+7 and MFMA t takes column 2i + t
-// from them, so dw is read once, whole rows at a time.  A step's edge
-// vectors and dw rows are loaded four steps ahead (a ring, the loop unrolled
-// by four so the slots stay in place; about 12 KB in flight per wavefront);
-// rows past the range are loaded clamped and zeroed.  The ranges' partials
-// are added afterwards in a fixed order.
-__global__ void __launch_bounds__(64 * kDw2Waves)
-    k_radial_dw2(int n_edges, int n_cols, const float* __restrict__ vec, float rc,
-                 const float* __restrict__ W1, const float* __restrict__ dw,
-                 float* __restrict__ part) {
-  __shared__ float s_w1[kRadBasis * kRadHidden];
-  __shared__ float s_b[kDw2Step][kRadBasis + 1];
-  __shared__ u32x2 s_h[4 * 3 * 64 * 2];  // [mt][part][lane][half]
-  for (int i = threadIdx.x; i < kRadBasis * kRadHidden; i += blockDim.x) s_w1[i] = W1[i];
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// The radial basis of every edge and its derivative in d, [E][16] (B_n then
+// dB_n/dd), for the backward's kernels to read instead of evaluating them in
+// fp64 per column slab or batch:
+//   B_n = sqrt(2/rc) sin(k_n d) / d,  dB_n/dd = sqrt(2/rc) (k_n cos(k_n d) - sin(k_n d) / d) / d
+// with k_n = (n+1) pi / rc, in fp64 (sin and cos of (n+1) t by the
+// angle-addition recurrence from one sincos, one division) and rounded once;
+// at d = 0 the limits sqrt(2/rc) k_n and 0.
+__global__ void __launch_bounds__(256)
+    k_radial_basis(int n_edges, const float* __restrict__ vec, float rc, float* __restrict__ basis) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n_edges) return;
+  const float vx = vec[int64_t(e) * 3], vy = vec[int64_t(e) * 3 + 1], vz = vec[int64_t(e) * 3 + 2];
+  const double d = sqrt(double(vx) * vx + double(vy) * vy + double(vz) * vz);
+  const double pref = sqrt(2.0 / double(rc)), k1 = 3.141592653589793 / double(rc);
+  float B[2 * kRadBasis];
+  if (d > 0.0) {
+    double sn, cs;
+    sincos(k1 * d, &sn, &cs);
+    const double inv = 1.0 / d;
+    double s_n = sn, c_n = cs;
+#pragma unroll
+    for (int n = 0; n < kRadBasis; ++n) {
+      const double kn = double(n + 1) * k1;
+      B[n] = float(pref * s_n * inv);
+      B[kRadBasis + n] = float(pref * (kn * c_n - s_n * inv) * inv);
+      const double s_next = s_n * cs + c_n * sn, c_next = c_n * cs - s_n * sn;
+      s_n = s_next;
+      c_n = c_next;
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < kRadBasis; ++n) {
+      B[n] = float(pref * double(n + 1) * k1);
+      B[kRadBasis + n] = 0.0f;
+    }
+  }
+  float4v* dst = reinterpret_cast<float4v*>(basis + int64_t(e) * 2 * kRadBasis);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dst[q] = float4v{B[4 * q], B[4 * q + 1], B[4 * q + 2], B[4 * q + 3]};
+}
+
+// LDS of the kernel below, per buffer (two of each, alternating by step):
+// the step's dw in three bf16 parts [part][32 rows][256 columns] (rows of
+// 528 bytes, 16-byte aligned for the dh operand reads, and each group of 8
+// rows 64 bytes further on, so that the four row groups of a staging store
+// fall in distinct banks), h's parts in the A
+// operand order of the dW2 product, the basis of the step's edges, and the
+// dh partials of the wavefronts (two halves per hidden tile).
+constexpr int kDhwStep = 32;                        // edges per step
+constexpr int kDhwRowB = 2 * kDhwCols + 16;         // bytes per staged row of one part
+constexpr int kDhwPartB = kDhwStep * kDhwRowB + kDhwStep / 8 * 64;  // one part of a step
+constexpr int kDhwStageB = 3 * kDhwPartB;
+constexpr int kDhwHB = 4 * 3 * 64 * 16;             // [tile][part][lane] x 16 bytes
+constexpr int kDhwBasisB = kDhwStep * (kRadBasis + 1) * 4;
+constexpr int kDhwRedB = 8 * 2 * 64 * 16;           // [wave][edge tile][lane] float4
+constexpr int kDhwOffH = 2 * kDhwStageB;
+constexpr int kDhwOffBasis = kDhwOffH + 2 * kDhwHB;
+constexpr int kDhwOffRed = kDhwOffBasis + 2 * kDhwBasisB;
+constexpr int kDhwLds = kDhwOffRed + 2 * kDhwRedB;  // 162,560 bytes
+static_assert(kDhwLds <= 160 * 1024, "one workgroup's LDS");
+static_assert(kDhwOffH % 16 == 0 && kDhwOffBasis % 16 == 0 && kDhwOffRed % 16 == 0, "alignment");
+
+// Both products of the second layer's backward from one read of dw:
+//   dh_part[slab][e][k] = sum_{j in slab} dw[e][j] W2[k][j]
+//   part[range][k][j]   = sum_{e in range} h[e][k] dw[e][j]    (j in slab)
+// Grid x = 256-column slabs, y = edge ranges; one 512-thread workgroup per
+// CU (LDS), walking its range in steps of 32 edges.  Wavefront w loads the
+// 32 x 32 block of dw at columns 32 w of the slab: lane (i, q) 8 bytes
+// (columns 2i, 2i+1) of rows 8q..8q+7.  Splitting those values gives the B
+// operand of its dW2 product directly (column 2i + t of MFMA t, K = the 32
+// edges; A = h's parts, formed per step from the basis: thread (k, g) unit
+// k of edges 4g..4g+3), and the same parts, stored once in LDS, are the A
+// operand of the dh product (rows = edges, K = columns).  For dh,
+// wavefront w owns hidden tile w % 4 over half w / 4 of the slab's columns,
+// with W2's parts for them in registers for the whole kernel; the two
+// halves go through LDS and are added in a fixed order one step later, each
+// wavefront storing one edge tile of one hidden tile.
+// One barrier per step: after it, step s's products run while step s+1's
+// operands are formed (h, the split of dw) into the other buffers, so the
+// matrix cores and the VALU work of the two steps overlap; dw is loaded
+// three steps ahead of its products (two ahead of its split), the basis
+// two.  The slabs' dh partials are added in a fixed order by the tail
+// kernel, the ranges' dW2 partials by launch_sum_partials.  Rows past the
+// range are loaded clamped and zeroed; columns past n_cols are zeros in dw
+// and W2.
+__global__ void __launch_bounds__(64 * kDhwWaves)
+    k_radial_dhw2(int n_edges, int n_cols, const float* __restrict__ basis,
+                  const float* __restrict__ W1, const float* __restrict__ dw,
+                  const u32x4* __restrict__ w2s, float* __restrict__ dh_part,
+                  float* __restrict__ part) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, kq = lane >> 4;
-  const int c2 = blockIdx.x * kDw2Cols + 32 * wave + 2 * li;  // this lane's 2 columns
-  const bool cval = c2 < n_cols;  // n_cols is a multiple of 32
+  const int sb = blockIdx.x;
+  const int c2 = sb * kDhwCols + 32 * wave + 2 * li;  // this lane's 2 columns
+  const bool cval = c2 < n_cols;                       // n_cols is a multiple of 32
   const int c2c = cval ? c2 : 0;
-  const int per = ((n_edges + int(gridDim.y) - 1) / int(gridDim.y) + kDw2Step - 1) / kDw2Step *
-                  kDw2Step;
+  const int kt = wave & 3, hf = wave >> 2;  // dh: hidden tile, half of the slab
+  const int per = ((n_edges + int(gridDim.y) - 1) / int(gridDim.y) + kDhwStep - 1) / kDhwStep *
+                  kDhwStep;
   const int lo = int(blockIdx.y) * per, hi = min(n_edges, lo + per);
+  const int n_steps = lo < hi ? (hi - lo + kDhwStep - 1) / kDhwStep : 0;
   const int hk = threadIdx.x & 63, hg = threadIdx.x >> 6;  // hidden unit, group of 4 edges
-  const int be = (threadIdx.x >> 3) & 31, bn = threadIdx.x & 7;  // basis (threads < 256)
-  const bool bthr = threadIdx.x < 256;
+  const int be = (threadIdx.x >> 3) & 31, bn = threadIdx.x & 7;  // basis value (edge, n)
   float w1c[kRadBasis];
 #pragma unroll
-  for (int n = 0; n < kRadBasis; ++n) w1c[n] = s_w1[n * kRadHidden + hk];
-  const double pref = sqrt(2.0 / double(rc));
-  const double kn = double(bn + 1) * 3.141592653589793 / double(rc);
-  float4v acc[4][2];  // [hidden tile][t]
+  for (int n = 0; n < kRadBasis; ++n) w1c[n] = W1[n * kRadHidden + hk];
+  Split3 W[4];  // W2's parts for the dh product: column blocks 4 hf + ks of the slab
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int cb = sb * kDhwBlocks + 4 * hf + ks;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) W[ks].p[p] = as_b8(w2s[int64_t(cb) * kW2Units + kt * 192 + 64 * p + lane]);
+  }
+  float4v acc[4][2];  // dW2 [hidden tile][t]
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int t = 0; t < 2; ++t) acc[mt][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-  const int n_steps = lo < hi ? (hi - lo + kDw2Step - 1) / kDw2Step : 0;
+  auto s_p = [&](int u) { return reinterpret_cast<unsigned*>(lds + u * kDhwStageB); };
+  auto s_h = [&](int u) { return reinterpret_cast<u32x2*>(lds + kDhwOffH + u * kDhwHB); };
+  auto s_b = [&](int u) { return reinterpret_cast<float*>(lds + kDhwOffBasis + u * kDhwBasisB); };
+  auto s_r = [&](int u) { return reinterpret_cast<float4v*>(lds + kDhwOffRed + u * kDhwRedB); };
   if (n_steps > 0) {  // the same for the whole workgroup
-    // Every step issues its loads unconditionally and in the same order
-    // (the first group only loads, the steps past the range compute on
-    // zeroed rows), so each wait covers exactly the loads it needs.
-    const int n_pad = (n_steps + kDw2Ring - 1) / kDw2Ring * kDw2Ring;
-    float2v bq[kDw2Ring][8];
-    float ev[kDw2Ring][3];
+    // Every step issues its loads unconditionally and in the same order (the
+    // steps past the range compute on zeroed rows), so each wait covers
+    // exactly the loads it needs.
+    float2v bq[2][8];
+    float bv[2];
     int ld = 0;  // next step to load
-    auto load_step = [&](float2v (&b)[8], float (&v3)[3]) {
-      const int e0 = lo + kDw2Step * min(ld, n_steps - 1);
+    // Rows past the range are other ranges' (finite) rows, read but never
+    // used: their h is zero and their dh is not stored; rows past the last
+    // edge are clamped to it.  Columns past n_cols read columns 0 and 1
+    // (finite), which meet zeros in W2 and whose dW2 is not stored.
+    auto load_step = [&](float2v (&b)[8], float& v) {
+      const int e0 = lo + kDhwStep * min(ld, n_steps - 1);
       ++ld;
-      const float* pv = vec + int64_t(min(e0 + be, hi - 1)) * 3;
-#pragma unroll
-      for (int d = 0; d < 3; ++d) v3[d] = pv[d];
+      v = basis[int64_t(min(e0 + be, n_edges - 1)) * 2 * kRadBasis + bn];
+      const float* base = dw + int64_t(e0) * n_cols;  // the same for the workgroup
+      const int rlim = min(kDhwStep - 1, n_edges - 1 - e0);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const int64_t e = min(e0 + 8 * kq + s, hi - 1);
-        b[s] = __builtin_nontemporal_load(reinterpret_cast<const float2v*>(dw + e * n_cols + c2c));
+        const unsigned off = unsigned(min(8 * kq + s, rlim)) * unsigned(n_cols) + unsigned(c2c);
+        b[s] = __builtin_nontemporal_load(reinterpret_cast<const float2v*>(base + off));
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the loads where they are issued
     };
-    for (int k0 = -kDw2Ring; k0 < n_pad; k0 += kDw2Ring) {
-      const bool act = k0 >= 0;  // the same for the whole workgroup
+    auto put_basis = [&](float v, float* sb_) {
+      sb_[be * (kRadBasis + 1) + bn] = v;  // threads past 256 store the same values again
+    };
+    // h of the step's edges, split, in the A operand order of the dW2
+    // product: lane hk % 16 + 16 (hg / 2) of tile hk / 16, elements 4 (hg % 2) .. +3
+    auto hidden = [&](int st, const float* sb_, u32x2* sh) {
+      const int e0 = lo + kDhwStep * st;
+      float v8[8];
 #pragma unroll
-      for (int u = 0; u < kDw2Ring; ++u) {
-        const int e0 = lo + kDw2Step * (k0 + u);
-        Split3 A[4], B[2];
-        if (act) {
-          if (bthr) {
-            // B_n(d) = sqrt(2/rc) sin((n+1) pi d / rc) / d in fp64, rounded once
-            const double x = ev[u][0], y = ev[u][1], z = ev[u][2];
-            const double d = sqrt(x * x + y * y + z * z);
-            const float bv = d > 0.0 ? float(pref * sin(kn * d) / d) : float(pref * kn);
-            s_b[be][bn] = e0 + be < hi ? bv : 0.0f;
-          }
-          __syncthreads();  // s_b written; every wavefront is done with the last step's s_h
-          {
-            float v8[8];
+      for (int s = 0; s < 4; ++s) {
+        const int el = 4 * hg + s;
+        float pre = 0.0f;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const int el = 4 * hg + s;
-              float pre = 0.0f;
+        for (int n = 0; n < kRadBasis; ++n) pre = fmaf(sb_[el * (kRadBasis + 1) + n], w1c[n], pre);
+        v8[s] = e0 + el < hi ? silu_sum_operand(pre) : 0.0f;
+        v8[4 + s] = 0.0f;
+      }
+      Split3 H;
+      split3(v8, H);
 #pragma unroll
-              for (int n = 0; n < kRadBasis; ++n) pre = fmaf(s_b[el][n], w1c[n], pre);
-              v8[s] = e0 + el < hi ? silu_sum_operand(pre) : 0.0f;
-              v8[4 + s] = 0.0f;
-            }
-            Split3 H;
-            split3(v8, H);
-            // lane hk % 16 + 16 (hg / 2) of tile hk / 16, elements 4 (hg % 2) .. +3
+      for (int p = 0; p < 3; ++p)
+        sh[(((hk >> 4) * 3 + p) * 64 + (hk & 15) + 16 * (hg >> 1)) * 2 + (hg & 1)] =
+            __builtin_bit_cast(u32x4, H.p[p]).xy;
+    };
+    // split the step's values (the dW2 product's B operands) and store the
+    // parts; word i of a part holds rows 2i (low half) and 2i + 1 of one column
+    auto stage = [&](const float2v (&b)[8], unsigned* sp, Split3 (&B)[2]) {
+      float v[2][8];
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
-              s_h[(((hk >> 4) * 3 + p) * 64 + (hk & 15) + 16 * (hg >> 1)) * 2 + (hg & 1)] =
-                  __builtin_bit_cast(u32x4, H.p[p]).xy;
-          }
-          __syncthreads();  // s_h written; s_b is free again
+      for (int s = 0; s < 8; ++s) {
+        v[0][s] = b[s].x;
+        v[1][s] = b[s].y;
+      }
+      split3(v[0], B[0]);
+      split3(v[1], B[1]);
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+      for (int p = 0; p < 3; ++p) {
+        const u32x4 x = as_u4(B[0].p[p]), y = as_u4(B[1].p[p]);
 #pragma unroll
-            for (int p = 0; p < 3; ++p) {
-              const u32x2 lo2 = s_h[((mt * 3 + p) * 64 + lane) * 2];
-              const u32x2 hi2 = s_h[((mt * 3 + p) * 64 + lane) * 2 + 1];
-              A[mt].p[p] = as_b8(u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
-            }
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            float v[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-              v[s] = cval && e0 + 8 * kq + s < hi ? bq[u][s][t] : 0.0f;
-            split3(v, B[t]);
-          }
-        }
-        load_step(bq[u], ev[u]);
-        if (act) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-              acc[mt][t] = mfma_bf16(A[mt].p[0], B[t].p[0], cross5(A[mt], B[t], acc[mt][t]));
+        for (int i = 0; i < 4; ++i) {
+          unsigned* row = sp + p * (kDhwPartB / 4) + (8 * kq + 2 * i) * (kDhwRowB / 4) + 16 * kq +
+                          16 * wave + li;
+          row[0] = __builtin_amdgcn_perm(y[i], x[i], 0x05040100u);             // low halves
+          row[kDhwRowB / 4] = __builtin_amdgcn_perm(y[i], x[i], 0x07060302u);  // high halves
         }
       }
+    };
+    // dh of step st for hidden tile kt and edge tile hf: half 0 + half 1
+    auto reduce = [&](int st, const float4v* sr) {
+      const int e0 = lo + kDhwStep * st;
+      const float4v k0 = sr[(kt * 2 + hf) * 64 + lane], o = sr[((kt + 4) * 2 + hf) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + 16 * hf + 4 * kq + r;
+        if (e < hi)
+          dh_part[(int64_t(sb) * n_edges + e) * kRadHidden + 16 * kt + li] = k0[r] + o[r];
+      }
+    };
+    // prologue: steps 0 and 1 loaded, their basis in LDS, step 0's operands
+    // formed, step 2 loading
+    Split3 B[2];
+    load_step(bq[0], bv[0]);
+    load_step(bq[1], bv[1]);
+    put_basis(bv[0], s_b(0));
+    put_basis(bv[1], s_b(1));
+    __syncthreads();
+    hidden(0, s_b(0), s_h(0));
+    stage(bq[0], s_p(0), B);
+    load_step(bq[0], bv[0]);  // step 2
+    const int n_pad = (n_steps + 1) / 2 * 2;
+    for (int s0 = 0; s0 < n_pad; s0 += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // slot u holds step st + 2 (basis and dw), slot u ^ 1 step st + 1
+        const int st = s0 + u;
+        __syncthreads();  // step st's operands are in LDS; the halves of st - 1 too
+        if (st > 0) reduce(st - 1, s_r(u ^ 1));
+        // dW2: A = h's parts (hidden tile mt), B = this lane's columns
+        const u32x2* sh = s_h(u);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          Split3 H;
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            const u32x2 a = sh[((mt * 3 + p) * 64 + lane) * 2];
+            const u32x2 b = sh[((mt * 3 + p) * 64 + lane) * 2 + 1];
+            H.p[p] = as_b8(u32x4{a.x, a.y, b.x, b.y});
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            acc[mt][t] = mfma_bf16(H.p[0], B[t].p[0], cross5(H, B[t], acc[mt][t]));
+        }
+        // dh: A = the staged parts (rows = edges of tile et, K = columns), B = W2
+        // (two accumulators per edge tile, even and odd K steps, added at the end)
+        float4v dd[2], de[2];
+        const unsigned char* spb = reinterpret_cast<const unsigned char*>(s_p(u));
+#pragma unroll
+        for (int et = 0; et < 2; ++et) {
+          dd[et] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+          de[et] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+          const unsigned char* rowp = spb + (16 * et + li) * kDhwRowB + (2 * et + (li >> 3)) * 64;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            Split3 A;
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+              A.p[p] = as_b8(*reinterpret_cast<const u32x4*>(
+                  rowp + p * kDhwPartB + 2 * (32 * (4 * hf + ks) + 8 * kq)));
+            float4v& c = ks & 1 ? de[et] : dd[et];
+            c = mfma_bf16(A.p[0], W[ks].p[0], cross5(A, W[ks], c));
+          }
+          dd[et] += de[et];
+        }
+        {
+          float4v* sr = s_r(u);
+#pragma unroll
+          for (int et = 0; et < 2; ++et) sr[(wave * 2 + et) * 64 + lane] = dd[et];
+        }
+        // step st + 1's operands into the other buffers, its slot reloaded
+        // with step st + 3, and step st + 2's basis into LDS
+        hidden(st + 1, s_b(u ^ 1), s_h(u ^ 1));
+        stage(bq[u ^ 1], s_p(u ^ 1), B);
+        load_step(bq[u ^ 1], bv[u ^ 1]);
+        put_basis(bv[u], s_b(u));
+      }
     }
+    __syncthreads();
+    reduce(n_pad - 1, s_r((n_pad - 1) & 1));
   }
   // D row = hidden unit 16 mt + 4 kq + r, column = c2 + t (lane li's columns)
   if (cval) {
@@ -1026,11 +1043,18 @@ __global__ void __launch_bounds__(64 * kDw2Waves)
 
 }  // namespace
 
-hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const float* W1,
-                              const float* dh, float* dvec, float* dW1_part, float* dW1,
-                              hipStream_t s) {
+hipError_t launch_radial_tail(int n_edges, const float* vec, const float* W1,
+                              const float* basis, float* dh, int n_parts, float* dvec,
+                              float* dW1_part, float* dW1, hipStream_t s) {
+  if (n_edges > 0 && n_parts > 1) {
+    const int64_t n4 = int64_t(n_edges) * kRadHidden / 4;
+    hipLaunchKernelGGL(k_radial_sum_slabs, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, s, n4,
+                       n_parts, n4, reinterpret_cast<float4v*>(dh));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_radial_tail, dim3(kRadialTailChunks), dim3(256), 0, s, n_edges,
-                     kRadialTailChunks, vec, cutoff, W1, dh, dvec, dW1_part);
+                     kRadialTailChunks, vec, W1, basis, dh, dvec, dW1_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return sum_partials_fixed(kRadialTailChunks, kRadBasis * kRadHidden, dW1_part, dW1, 0, s);
@@ -1040,10 +1064,13 @@ bool radial_conv_supported(const char* set_name) {
   return set_name && std::strcmp(set_name, "L1to3") == 0;
 }
 
+int radial_dw2_slabs(int n_cols) { return (n_cols + kDhwCols - 1) / kDhwCols; }
+
 int radial_dw2_ranges(int n_edges, int n_cols) {
-  const int slabs = (n_cols + kDw2Cols - 1) / kDw2Cols;
-  const int steps = std::max(1, (n_edges + kDw2Step - 1) / kDw2Step);
-  return std::max(1, std::min(steps, (2048 + slabs - 1) / slabs));
+  // one workgroup per CU (LDS): slabs x ranges fills the 256 CUs once
+  const int slabs = radial_dw2_slabs(n_cols);
+  const int steps = std::max(1, (n_edges + kDhwStep - 1) / kDhwStep);
+  return std::max(1, std::min(steps, 256 / slabs));
 }
 
 size_t radial_w2_split_bytes(int n_cols) {
@@ -1051,24 +1078,27 @@ size_t radial_w2_split_bytes(int n_cols) {
 }
 
 hipError_t launch_radial_dh_dw2(int n_edges, int n_cols, const float* vec, float cutoff,
-                                const float* W1, const float* W2, const float* dw, float* dh,
-                                float* part, int ranges, void* w2s, hipStream_t s) {
-  if (n_edges > 0) {
-    u32x4* w2u = static_cast<u32x4*>(w2s);
-    hipLaunchKernelGGL(k_radial_split_w2, dim3(w2_split_blocks(n_cols)), dim3(256), 0, s, n_cols,
-                       W2, w2u);
-    // two workgroups per CU are resident (registers); each walks its edge
-    // blocks as one load stream
-    const int64_t n_blocks = (int64_t(n_edges) + kDhEdges - 1) / kDhEdges;
-    const int g1 = int(std::min<int64_t>(n_blocks, 256));
-    hipLaunchKernelGGL(k_radial_dh, dim3(g1), dim3(256), 0, s, n_edges, n_cols, dw, w2u, dh);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  // with no edges the partials are written as zeros
-  const int slabs = (n_cols + kDw2Cols - 1) / kDw2Cols;
-  hipLaunchKernelGGL(k_radial_dw2, dim3(slabs, ranges), dim3(64 * kDw2Waves), 0, s, n_edges, n_cols, vec,
-                     cutoff, W1, dw, part);
+                                const float* W1, const float* W2, const float* dw,
+                                float* dh_part, float* part, int ranges, void* w2s,
+                                float* basis, hipStream_t s) {
+  // the attribute is per function: raised once, retried after a failure
+  static std::atomic<bool> lds_set{false};
+  if (const hipError_t e =
+          set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_radial_dhw2), kDhwLds);
+      e != hipSuccess)
+    return e;
+  u32x4* w2u = static_cast<u32x4*>(w2s);
+  hipLaunchKernelGGL(k_radial_split_w2, dim3(w2_split_blocks(n_cols)), dim3(256), 0, s, n_cols,
+                     W2, w2u);
+  if (n_edges > 0)
+    hipLaunchKernelGGL(k_radial_basis, dim3(unsigned((int64_t(n_edges) + 255) / 256)), dim3(256), 0,
+                       s, n_edges, vec, cutoff, basis);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // with no edges the dW2 partials are written as zeros
+  hipLaunchKernelGGL(k_radial_dhw2, dim3(radial_dw2_slabs(n_cols), ranges),
+                     dim3(64 * kDhwWaves), kDhwLds, s, n_edges, n_cols, basis, W1, dw, w2u,
+                     dh_part, part);
   return hipGetLastError();
 }
 

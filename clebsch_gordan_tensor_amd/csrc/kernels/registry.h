@@ -211,19 +211,27 @@ hipError_t launch_radial_mlp(int n_edges, int n_cols, const float* vec, float cu
                              const float* W1, const float* W2, float* w, hipStream_t s,
                              const void* hidden = nullptr);
 // pieces of the radial MLP's backward
-constexpr int kRadialTailChunks = 1024;
-hipError_t launch_radial_tail(int n_edges, const float* vec, float cutoff, const float* W1,
-                              const float* dh, float* dvec, float* dW1_part, float* dW1,
-                              hipStream_t s);
+constexpr int kRadialTailChunks = 4096;
+// dh given as n_parts partials [n_parts][E][64] (added in part order, into
+// part 0, which they overwrite); basis the per-edge basis and derivative
+// [E][16] that launch_radial_dh_dw2 wrote
+hipError_t launch_radial_tail(int n_edges, const float* vec, const float* W1, const float* basis,
+                              float* dh, int n_parts, float* dvec, float* dW1_part,
+                              float* dW1, hipStream_t s);
 // The second layer's backward from dw [E][n_cols] (n_cols a multiple of
-// 32): dh [E][64] and per-range partials part [ranges][64][n_cols] of dW2
-// (add them with launch_sum_partials, which overwrites them).  w2s is device
-// scratch of radial_w2_split_bytes(n_cols) bytes, 16-byte aligned.
+// 32), one read of dw: dh as per-slab partials dh_part [slabs][E][64]
+// (slabs = radial_dw2_slabs(n_cols)) and dW2 as per-range partials part
+// [ranges][64][n_cols] (add them with launch_sum_partials, which overwrites
+// them).  w2s is device scratch of radial_w2_split_bytes(n_cols) bytes,
+// basis of n_edges * 16 floats (written here: each edge's basis and its
+// derivative, for launch_radial_tail), both 16-byte aligned.
+int radial_dw2_slabs(int n_cols);
 int radial_dw2_ranges(int n_edges, int n_cols);
 size_t radial_w2_split_bytes(int n_cols);
 hipError_t launch_radial_dh_dw2(int n_edges, int n_cols, const float* vec, float cutoff,
-                                const float* W1, const float* W2, const float* dw, float* dh,
-                                float* part, int ranges, void* w2s, hipStream_t s);
+                                const float* W1, const float* W2, const float* dw,
+                                float* dh_part, float* part, int ranges, void* w2s,
+                                float* basis, hipStream_t s);
 hipError_t launch_sum_partials(int n_chunks, int n, float* part, float* out, hipStream_t s);
 // The tensor product as dense products per output block on the fp32 matrix
 // cores (gemm.hip); sizes from the host-built plan, plan in device memory.

@@ -283,11 +283,13 @@ e3_status e3_conv_forward_radial_hidden(const e3_desc* desc, int32_t n_nodes, in
  * the bf16 matrix cores with every fp32 operand split into three bf16 parts
  * (24 significant bits and fp32's exponent range, so any cotangent
  * magnitude is kept; six of the nine cross products, the others below
- * 2^-24 of a product), each reading dw once (dW2 through per-range partial
- * sums added in a fixed order, h recomputed from the edge vectors).
+ * 2^-24 of a product), both from one read of dw (dh through per-slab
+ * partials over 256-column slabs and dW2 through per-range partials, each
+ * added in a fixed order; h recomputed from the edge vectors).
  * workspace: caller-owned,
- * e3_radial_mlp_backward_workspace_size bytes, 16-byte aligned; dw and W2
- * 16-byte aligned.  All arrays float32 on the device. */
+ * e3_radial_mlp_backward_workspace_size bytes (about E * 256 bytes per
+ * 256-column slab), 16-byte aligned; dw and W2 16-byte aligned.  All
+ * arrays float32 on the device. */
 e3_status e3_radial_mlp_backward_workspace_size(const e3_radial* mlp, int32_t n_edges,
                                                 int32_t n_cols, size_t* bytes);
 e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t n_cols,

@@ -226,10 +226,12 @@ def test_radial_conv_unsupported(gpu):
 
 # ------------------------------------------------------- MLP backward
 
-# (5, 96): fewer edges than one 16-row tile, three 32-column blocks (a part
-# stage) and a column slab mostly past the end; (130, 288): one edge past a
-# 128-edge block, nine blocks (two stages and one block of a third)
-@pytest.mark.parametrize("E,n_cols", [(3001, 1280), (40, 64), (0, 32), (5, 96), (130, 288)])
+# (5, 96): fewer edges than one 16-row tile and a 256-column slab mostly
+# past the end; (130, 288): ranges of one 32-edge step (an odd count, so the
+# two-step loop runs one step on zeros) and a second slab of one 32-column
+# block; (6007, 544): three slabs, ranges of three steps, the last one ragged
+@pytest.mark.parametrize("E,n_cols", [(3001, 1280), (40, 64), (0, 32), (5, 96), (130, 288),
+                                      (6007, 544)])
 def test_radial_mlp_backward_matches_oracle(gpu, E, n_cols):
     rng = np.random.default_rng(220 + E)
     ev = (rng.standard_normal((E, 3)) * 2.0).astype(np.float32)
