@@ -801,6 +801,7 @@ __global__ void __launch_bounds__(256)
 // operand order of the dW2 product, the basis of the step's edges, and the
 // dh partials of the wavefronts (two halves per hidden tile).
 constexpr int kDhwStep = 32;                        // edges per step
+constexpr int kDhwMaxSteps = 256;                   // steps per edge range at most
 constexpr int kDhwRowB = 2 * kDhwCols + 16;         // bytes per staged row of one part
 constexpr int kDhwPartB = kDhwStep * kDhwRowB + kDhwStep / 8 * 64;  // one part of a step
 constexpr int kDhwStageB = 3 * kDhwPartB;
@@ -856,9 +857,7 @@ __global__ void __launch_bounds__(64 * kDhwWaves)
   const int n_steps = lo < hi ? (hi - lo + kDhwStep - 1) / kDhwStep : 0;
   const int hk = threadIdx.x & 63, hg = threadIdx.x >> 6;  // hidden unit, group of 4 edges
   const int be = (threadIdx.x >> 3) & 31, bn = threadIdx.x & 7;  // basis value (edge, n)
-  float w1c[kRadBasis];
-#pragma unroll
-  for (int n = 0; n < kRadBasis; ++n) w1c[n] = W1[n * kRadHidden + hk];
+  const float* __restrict__ w1c = W1 + hk;  // W1[n][hk] at w1c[n * 64] (cached; no registers held)
   Split3 W[4];  // W2's parts for the dh product: column blocks 4 hf + ks of the slab
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -866,11 +865,20 @@ __global__ void __launch_bounds__(64 * kDhwWaves)
 #pragma unroll
     for (int p = 0; p < 3; ++p) W[ks].p[p] = as_b8(w2s[int64_t(cb) * kW2Units + kt * 192 + 64 * p + lane]);
   }
-  float4v acc[4][2];  // dW2 [hidden tile][t]
+  // dW2 [hidden tile][t]: the leading products a0 b0 and the five smaller
+  // ones in accumulators of their own.  A matrix-core accumulation drops the
+  // bits of addends far below its accumulator's magnitude toward minus
+  // infinity (a bias of one sign for every edge, which a sum over millions
+  // of edges with cancelling signs does not hide); kept apart, each
+  // accumulator's addends are within a few binades of it.
+  float4v acc[4][2], axc[4][2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) acc[mt][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < 2; ++t) {
+      acc[mt][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+      axc[mt][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    }
   auto s_p = [&](int u) { return reinterpret_cast<unsigned*>(lds + u * kDhwStageB); };
   auto s_h = [&](int u) { return reinterpret_cast<u32x2*>(lds + kDhwOffH + u * kDhwHB); };
   auto s_b = [&](int u) { return reinterpret_cast<float*>(lds + kDhwOffBasis + u * kDhwBasisB); };
@@ -912,7 +920,8 @@ __global__ void __launch_bounds__(64 * kDhwWaves)
         const int el = 4 * hg + s;
         float pre = 0.0f;
 #pragma unroll
-        for (int n = 0; n < kRadBasis; ++n) pre = fmaf(sb_[el * (kRadBasis + 1) + n], w1c[n], pre);
+        for (int n = 0; n < kRadBasis; ++n)
+          pre = fmaf(sb_[el * (kRadBasis + 1) + n], w1c[n * kRadHidden], pre);
         v8[s] = e0 + el < hi ? silu_sum_operand(pre) : 0.0f;
         v8[4 + s] = 0.0f;
       }
@@ -988,17 +997,19 @@ __global__ void __launch_bounds__(64 * kDhwWaves)
             H.p[p] = as_b8(u32x4{a.x, a.y, b.x, b.y});
           }
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-            acc[mt][t] = mfma_bf16(H.p[0], B[t].p[0], cross5(H, B[t], acc[mt][t]));
+          for (int t = 0; t < 2; ++t) {
+            acc[mt][t] = mfma_bf16(H.p[0], B[t].p[0], acc[mt][t]);
+            axc[mt][t] = cross5(H, B[t], axc[mt][t]);
+          }
         }
         // dh: A = the staged parts (rows = edges of tile et, K = columns), B = W2
-        // (two accumulators per edge tile, even and odd K steps, added at the end)
-        float4v dd[2], de[2];
+        // (per edge tile the leading products and the smaller ones apart,
+        // added at the end and stored for the reduction)
         const unsigned char* spb = reinterpret_cast<const unsigned char*>(s_p(u));
+        float4v* sr = s_r(u);
 #pragma unroll
         for (int et = 0; et < 2; ++et) {
-          dd[et] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-          de[et] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+          float4v dd = {0.0f, 0.0f, 0.0f, 0.0f}, de = {0.0f, 0.0f, 0.0f, 0.0f};
           const unsigned char* rowp = spb + (16 * et + li) * kDhwRowB + (2 * et + (li >> 3)) * 64;
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
@@ -1007,15 +1018,10 @@ __global__ void __launch_bounds__(64 * kDhwWaves)
             for (int p = 0; p < 3; ++p)
               A.p[p] = as_b8(*reinterpret_cast<const u32x4*>(
                   rowp + p * kDhwPartB + 2 * (32 * (4 * hf + ks) + 8 * kq)));
-            float4v& c = ks & 1 ? de[et] : dd[et];
-            c = mfma_bf16(A.p[0], W[ks].p[0], cross5(A, W[ks], c));
+            dd = mfma_bf16(A.p[0], W[ks].p[0], dd);
+            de = cross5(A, W[ks], de);
           }
-          dd[et] += de[et];
-        }
-        {
-          float4v* sr = s_r(u);
-#pragma unroll
-          for (int et = 0; et < 2; ++et) sr[(wave * 2 + et) * 64 + lane] = dd[et];
+          sr[(wave * 2 + et) * 64 + lane] = dd + de;
         }
         // step st + 1's operands into the other buffers, its slot reloaded
         // with step st + 3, and step st + 2's basis into LDS
@@ -1035,7 +1041,7 @@ __global__ void __launch_bounds__(64 * kDhwWaves)
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float2v v = {acc[mt][0][r], acc[mt][1][r]};
+        const float2v v = {acc[mt][0][r] + axc[mt][0][r], acc[mt][1][r] + axc[mt][1][r]};
         *reinterpret_cast<float2v*>(pr + int64_t(16 * mt + 4 * kq + r) * n_cols) = v;
       }
   }
@@ -1067,10 +1073,14 @@ bool radial_conv_supported(const char* set_name) {
 int radial_dw2_slabs(int n_cols) { return (n_cols + kDhwCols - 1) / kDhwCols; }
 
 int radial_dw2_ranges(int n_edges, int n_cols) {
-  // one workgroup per CU (LDS): slabs x ranges fills the 256 CUs once
+  // one workgroup per CU (LDS): slabs x ranges fills the 256 CUs at least
+  // once, and no range is longer than kDhwMaxSteps steps (the rounding of
+  // the matrix cores' long sums grows with the length of each range's)
   const int slabs = radial_dw2_slabs(n_cols);
   const int steps = std::max(1, (n_edges + kDhwStep - 1) / kDhwStep);
-  return std::max(1, std::min(steps, 256 / slabs));
+  const int wave = std::max(1, 256 / slabs);  // ranges of one round of workgroups
+  const int by_length = (steps + kDhwMaxSteps - 1) / kDhwMaxSteps;
+  return std::max(1, std::min(steps, (by_length + wave - 1) / wave * wave));
 }
 
 size_t radial_w2_split_bytes(int n_cols) {

@@ -14,7 +14,7 @@ import pytest
 from clebsch_gordan_tensor_amd import synth as S
 from oracle import oracle as O
 from oracle import radial as R
-from tests.gpu_util import TOL_F32, assert_close, dev, host
+from tests.gpu_util import TOL_F32, assert_close, dev, host, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -249,6 +249,51 @@ def test_radial_mlp_backward_matches_oracle(gpu, E, n_cols):
     assert_close(host(dW2), rW2, TOL_F32, f"radial dW2 E={E}")
     assert_close(host(dvec), rvec, TOL_F32, f"radial dvec E={E}")
     assert np.all(host(dvec)[1] == 0.0) if E > 2 else True
+
+
+def test_radial_mlp_backward_full_size(gpu):
+    # the mace64k edge count (3,140,252) with n_cols = 10 paths x 128
+    # channels, every slab and edge range of the launch the bench times.
+    # dw = a b^T with b powers of two, so each fp32 element is the exact
+    # product; the backward is linear in dw with dh = a (W2 b)^T, so the
+    # oracle's own backward on the factored problem (W2 b as a one-column
+    # W2, a as its cotangent) gives dW1 and dvec, and dW2 = (h^T a) b^T
+    E, n_cols = 3140252, 1280
+    rng = np.random.default_rng(260)
+    ev = (rng.standard_normal((E, 3)) * 2.0).astype(np.float32)
+    W1, W2 = _weights(n_cols, 261)
+    a = rng.standard_normal(E).astype(np.float32)
+    b = (np.exp2(rng.integers(-3, 4, n_cols)) * rng.choice([-1.0, 1.0], n_cols)).astype(np.float32)
+    dw = torch.outer(dev(a), dev(b))
+    dW1, dW2, dvec = gpu.radial_mlp_backward(dev(ev), 5.0, dev(W1), dev(W2), dw)
+    torch.cuda.synchronize()
+    del dw
+    w2b = (W2.astype(np.float64) @ b.astype(np.float64))[:, None]
+    rW1, rW2a, rvec = R.radial_mlp_backward(ev, 5.0, W1, w2b, a[:, None])
+    rW2 = rW2a @ b.astype(np.float64)[None, :]
+    # the weight gradients (sums over all 3.1M edges) at the literal gate
+    assert_close(host(dW1), rW1, TOL_F32, "radial dW1 full size")
+    assert_close(host(dW2), rW2, TOL_F32, "radial dW2 full size")
+    # dvec per edge against its propagated scale, as for the chain to
+    # forces: max|dvec|/RMS is about 50 here and a float32 evaluation of the
+    # oracle's own steps already reaches max|err|/RMS = 1.4e-5.  An error of
+    # 1e-5 of RMS(dh) in dh (its own gate), plus float32 rounding relative
+    # to the edge's own terms, moves dd_e = sum_n B'_n sum_k dpre_k W1[n][k]
+    # by at most 1e-5 s_e with
+    #   s_e = sum_n |B'_n| sum_k |W1[n][k]| (|silu'(pre_k)| RMS(dh) + |dpre_k|)
+    d = np.linalg.norm(ev.astype(np.float64), axis=1)
+    pre = R.bessel_basis(d, 5.0, 8) @ W1.astype(np.float64)
+    sd = R.silu_deriv(pre)
+    dh = a.astype(np.float64)[:, None] * w2b[None, :, 0]
+    rms_dh = np.sqrt(np.mean(dh ** 2))
+    t = np.abs(sd) * rms_dh + np.abs(dh * sd)
+    scale = np.sum(np.abs(R.bessel_basis_deriv(d, 5.0, 8)) * (t @ np.abs(W1.astype(np.float64)).T), axis=1)
+    got = host(dvec).astype(np.float64)
+    e = float((np.abs(got - rvec).max(axis=1) / scale).max())
+    print(f"[gate] radial dvec full size: propagated {e:.3e}, literal max|err|/rms "
+          f"{rel_err(got, rvec):.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert e <= TOL_F32, f"radial dvec full size: max |err| / propagated scale = {e:.3e}"
 
 
 @pytest.mark.parametrize("scale", [2.0**-70, 2.0**70])
