@@ -487,8 +487,8 @@ e3_status e3_conv_workspace_size(int32_t n_nodes, int32_t n_edges, size_t* bytes
  *    tree; unreached nodes follow in index order.  edge_vec may be NULL.
  * The order only changes which wavefront handles which node: results are
  * the same with any order.  Once per graph.  ws_bytes must be >=
- * e3_conv_workspace_size().  This call synchronises `stream` with the host
- * once per breadth-first level. */
+ * e3_conv_workspace_size().  Asynchronous on `stream`: no host
+ * synchronisation (the traversal's level bounds stay on the device). */
 e3_status e3_conv_prepare_transpose(int32_t n_nodes, int32_t n_edges, const int32_t* rowptr,
                                     const int32_t* sender, const float* edge_vec, void* workspace,
                                     size_t ws_bytes, void* stream);
