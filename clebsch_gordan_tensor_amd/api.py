@@ -56,7 +56,8 @@ EXPORTS = ["e3_num_paths", "e3_path_info", "e3_supported", "e3_cg_block",
            "e3_conv_double_backward_generic", "e3_check_graph", "e3_check_graph_host", "e3_conv_backward_noalloc",
            "e3_tp_backward_gemm", "e3_conv_backward_gemm",
            "e3_radial_hidden_size", "e3_radial_hidden", "e3_conv_forward_radial_hidden",
-           "e3_radial_mlp_hidden",
+           "e3_radial_mlp_hidden", "e3_conv_backward_radial_scratch_size",
+           "e3_conv_backward_radial_hidden",
            "e3_release_all",
            "e3_last_error"]
 E3_GEN_FORWARD, E3_GEN_DX, E3_GEN_DW, E3_GEN_DY, E3_GEN_GEMM = 0, 1, 2, 3, 4
@@ -100,6 +101,10 @@ def lib():
     L.e3_radial_mlp_hidden.argtypes = [C.POINTER(_CRadial), i32, i32, vp, sz, vp, vp]
     L.e3_conv_forward_radial_hidden.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp,
                                                 C.POINTER(_CRadial), vp, sz, vp, vp]
+    L.e3_conv_backward_radial_scratch_size.argtypes = [dp, i32, C.POINTER(sz)]
+    L.e3_conv_backward_radial_hidden.argtypes = [dp, i32, i32, vp, vp, vp, sz, vp, vp,
+                                                 C.POINTER(_CRadial), vp, sz, vp, vp, vp, vp, vp,
+                                                 sz, vp]
     L.e3_generic_plan_size.argtypes = [dp, i32, C.POINTER(sz)]
     L.e3_generic_plan_build.argtypes = [dp, i32, vp, sz]
     L.e3_tp_backward_generic.argtypes = [dp, i64, vp, sz, vp, sz, vp, sz, vp, vp, vp, vp, vp, vp,
@@ -674,6 +679,50 @@ def conv_forward_radial_hidden(desc: Desc, rowptr, sender, edge_vec, x, cutoff, 
                                                _ptr(x), C.byref(r), _ptr(hidden), hb, _ptr(out),
                                                _stream(stream)))
     return out
+
+
+def conv_backward_radial_scratch_bytes(desc: Desc, n_edges):
+    """Device scratch bytes conv_backward_radial_hidden needs."""
+    nb = C.c_size_t()
+    _check(lib().e3_conv_backward_radial_scratch_size(C.byref(desc.c()), n_edges, C.byref(nb)))
+    return max(nb.value, 16)
+
+
+def conv_backward_radial_hidden(desc: Desc, rowptr, sender, workspace, edge_vec, x, cutoff, W1,
+                                W2, hidden, dm, dx=None, dw=None, dY=None, scratch=None,
+                                stream=None):
+    """(dx, dw, dY) of the fused radial forward: conv_backward with w formed
+    from the hidden layer (radial_hidden of the same edge vectors)."""
+    import torch
+    N, E = rowptr.shape[0] - 1, sender.shape[0]
+    P = num_paths(desc)
+    _need(rowptr, "rowptr", dtype=torch.int32)
+    _need(sender, "sender", dtype=torch.int32)
+    _need(edge_vec, "edge_vec", shape=(E, 3), dtype=torch.float32)
+    _need(x, "x", shape=(N, desc.dx, desc.channels), dtype=torch.float32)
+    _need(dm, "dm", shape=(N, desc.dout, desc.channels), dtype=torch.float32)
+    r = _radial(cutoff, W1, W2)
+    if W2.shape[1] != P * desc.channels:
+        raise ValueError("W2 must have P*C columns")
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((N, desc.dx, desc.channels), device=dev, dtype=torch.float32)
+    if dw is None:
+        dw = torch.empty((E, P, desc.channels), device=dev, dtype=torch.float32)
+    if dY is None:
+        dY = torch.empty((E, desc.dy), device=dev, dtype=torch.float32)
+    _need(dx, "dx", shape=(N, desc.dx, desc.channels), dtype=torch.float32)
+    _need(dw, "dw", shape=(E, P, desc.channels), dtype=torch.float32)
+    _need(dY, "dY", shape=(E, desc.dy), dtype=torch.float32)
+    if scratch is None:
+        scratch = torch.empty(conv_backward_radial_scratch_bytes(desc, E), device=dev,
+                              dtype=torch.uint8)
+    _check(lib().e3_conv_backward_radial_hidden(
+        C.byref(desc.c()), N, E, _ptr(rowptr), _ptr(sender), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(edge_vec), _ptr(x), C.byref(r),
+        _ptr(hidden), hidden.numel() * hidden.element_size(), _ptr(dm), _ptr(dx), _ptr(dw),
+        _ptr(dY), _ptr(scratch), scratch.numel() * scratch.element_size(), _stream(stream)))
+    return dx, dw, dY
 
 
 def radial_mlp_backward_workspace_bytes(W1, W2, n_edges, n_cols):

@@ -929,6 +929,67 @@ e3_status e3_conv_forward_radial_hidden(const e3_desc* desc, int32_t n_nodes, in
                                   edge_vec, x, mlp, hidden, h_bytes, m, stream);
 }
 
+e3_status e3_conv_backward_radial_scratch_size(const e3_desc* desc, int32_t n_edges,
+                                               size_t* bytes) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if (!bytes) return fail(E3_ERR_INVALID_ARG, "bytes is null");
+  if (n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (p.C < 32 || p.C % 32) return fail(E3_ERR_UNSUPPORTED, "the radial convolution needs C in {32, 64, 128, 256}");
+  *bytes = e3k::conv_bwd_radial_scratch_bytes(n_edges, p.C, p.dy);
+  return ok();
+}
+
+e3_status e3_conv_backward_radial_hidden(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                         const int32_t* rowptr, const int32_t* sender,
+                                         const void* workspace, size_t ws_bytes,
+                                         const float* edge_vec, const float* x,
+                                         const e3_radial* mlp, const void* hidden, size_t h_bytes,
+                                         const float* dm, float* dx, float* dw, float* dY,
+                                         void* scratch, size_t scratch_bytes, void* stream) {
+  Parsed p;
+  e3_status s = parse(desc, p);
+  if (s != E3_OK) return s;
+  if ((s = check_radial(mlp)) != E3_OK) return s;
+  if (desc->flags & (E3_Y_GIVEN | E3_OUT_PER_PATH))
+    return fail(E3_ERR_UNSUPPORTED, "the radial convolution takes edge vectors and collapsed outputs");
+  const e3k::KernelSet* ks = find_set(p);
+  if (!ks || !e3k::radial_conv_supported(ks->name))
+    return fail(E3_ERR_UNSUPPORTED,
+                "no radial convolution kernel for this signature (supported: 0e+1o x harmonics "
+                "0e+1o+2e+3o -> 0e+1o+2e+3o)");
+  if (p.C != 32 && p.C != 64 && p.C != 128 && p.C != 256)
+    return fail(E3_ERR_UNSUPPORTED, "the radial convolution needs C in {32, 64, 128, 256}");
+  if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
+  if (n_nodes == 0) return ok();
+  if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
+  size_t need = 0;
+  e3_conv_workspace_size(n_nodes, n_edges, &need);
+  if (!workspace || ws_bytes < need)
+    return fail(E3_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+  if (!x || !dm || !dx) return fail(E3_ERR_INVALID_ARG, "null pointer");
+  if (n_edges > 0 && (!edge_vec || !hidden || !dw || !dY))
+    return fail(E3_ERR_INVALID_ARG, "null pointer");
+  const size_t sneed = e3k::conv_bwd_radial_scratch_bytes(n_edges, p.C, p.dy);
+  if (n_edges > 0 && (!scratch || scratch_bytes < sneed))
+    return fail(E3_ERR_WORKSPACE, "scratch needs " + std::to_string(sneed) + " bytes");
+  if (n_edges > 0 && h_bytes < size_t(n_edges) * e3k::kRadialHiddenBytes)
+    return fail(E3_ERR_WORKSPACE, "hidden needs " +
+                                      std::to_string(size_t(n_edges) * e3k::kRadialHiddenBytes) +
+                                      " bytes");
+  if (!aligned16(x) || !aligned16(dm) || !aligned16(dx) ||
+      (n_edges > 0 && (!aligned16(hidden) || !aligned16(dw))))
+    return fail(E3_ERR_ALIGNMENT, "x, dm, dx, dw and hidden must be 16-byte aligned");
+  const e3k::TransposeLayout L = e3k::transpose_layout(n_nodes, n_edges);
+  const int* ws = static_cast<const int*>(workspace);
+  e3k::RadialBwdArgs a{n_nodes, n_edges, p.C, ws + L.order, ws + L.colptr, ws + L.perm,
+                       ws + L.recv, ws + L.npad, ws + L.padlist, edge_vec, x, mlp->W2, hidden,
+                       dm, dx, dw, dY, static_cast<float*>(scratch)};
+  return hip_status(e3k::launch_conv_bwd_radial(ks->name, a, hipStream_t(stream)),
+                    "conv_backward_radial");
+}
+
 namespace {
 
 // The radial MLP's second layer seen as a channel mixing: input 64x0e (h),

@@ -531,6 +531,322 @@ hipError_t launch_fwd_radial(const RadialConvArgs& a, hipStream_t s) {
   return a.hidden ? launch_fwd_radial_hg<S, true>(a, s) : launch_fwd_radial_hg<S, false>(a, s);
 }
 
+// ------------------------------------------ fused radial convolution backward
+
+// Backward of one edge for this lane's two channels chan and chan + 16 (as
+// edge_backward, e3j E.1 Eq.16 with one scalar per path): dx gains
+// w[P] B_P, dw[P] = sum_m1 x B_P is stored at dwe + P C (+16), and dYl
+// collects this lane's part of dY.
+template <class S>
+__device__ __forceinline__ void edge_backward_pair(const float (&Y)[Plan<S>::DY],
+                                                   const float (&xv)[Plan<S>::DX][2],
+                                                   const float (&wv)[Plan<S>::NP][2],
+                                                   const float (&dmv)[Plan<S>::DO][2],
+                                                   float (&dxa)[Plan<S>::DX][2],
+                                                   float* __restrict__ dwe, int C, bool store,
+                                                   float (&dYl)[Plan<S>::DY]) {
+  using PL = Plan<S>;
+  float t[PL::DX][2];
+#pragma unroll
+  for (int i = 0; i < PL::DX; ++i) t[i][0] = t[i][1] = 0.0f;
+  sfor<0, PL::NP>([&](auto pi) {
+    constexpr PathC P = PL::paths.p[pi];
+    constexpr int n1 = 2 * P.l1 + 1;
+    float B[n1][2], xw[n1][2];
+#pragma unroll
+    for (int a = 0; a < n1; ++a)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        B[a][k] = 0.0f;
+        xw[a][k] = wv[pi][k] * xv[P.xo + a][k];
+      }
+    float A = 0.0f, T = 0.0f;
+    sfor<0, P.rcnt>([&](auto r) {
+      constexpr CgRec R = kRec[P.roff + r];
+      if constexpr (group_first(P.roff, r)) {
+        A = R.c * Y[P.yo + R.m2];
+        T = fmaf(xw[R.m1][1], dmv[P.oo + R.M][1], xw[R.m1][0] * dmv[P.oo + R.M][0]);
+      } else {
+        A = fmaf(R.c, Y[P.yo + R.m2], A);
+      }
+      dYl[P.yo + R.m2] = fmaf(R.c, T, dYl[P.yo + R.m2]);
+      if constexpr (group_last(P.roff, P.rcnt, r)) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) B[R.m1][k] = fmaf(A, dmv[P.oo + R.M][k], B[R.m1][k]);
+      }
+    });
+    float dwp[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float s = 0.0f;
+#pragma unroll
+      for (int a = 0; a < n1; ++a) {
+        t[P.xo + a][k] = fmaf(wv[pi][k], B[a][k], t[P.xo + a][k]);
+        s = fmaf(xv[P.xo + a][k], B[a][k], s);
+      }
+      dwp[k] = s;
+    }
+    if (store) {
+      __builtin_nontemporal_store(dwp[0], dwe + int64_t(pi) * C);
+      __builtin_nontemporal_store(dwp[1], dwe + int64_t(pi) * C + 16);
+    }
+  });
+#pragma unroll
+  for (int i = 0; i < PL::DX; ++i) {
+    dxa[i][0] += t[i][0];
+    dxa[i][1] += t[i][1];
+  }
+}
+
+template <class S>
+constexpr size_t radial_bwd_lds_bytes() {
+  using PL = Plan<S>;
+  return size_t(PL::NP) * 8 * 64 * sizeof(half8)                        // W2 slab, hi and lo
+         + size_t(kRadWaves) * kRadChunk * (PL::DY + 1) * sizeof(float)  // harmonics
+         + size_t(kRadWaves) * kRadChunk * 2 * sizeof(int);              // edge ids, receivers
+}
+
+// The convolution backward with w formed on the fly from the radial MLP's
+// hidden layer (k_radial_hidden's operands), as the fused forward forms it:
+// w never reaches HBM.  Sender-ordered walk over the transposed index (as
+// k_conv_bwd: dx[a] sums over a's out-edges in registers, dw[e] and dY[e]
+// are edge-local), one 32-channel slab per wavefront with W2's slab split
+// into fp16 parts in LDS, slabs spread over the XCDs.  Per 16-edge tile of
+// a sender's out-edges the MFMAs leave w for 4 edges x 2 channels in every
+// lane (edges 4 (lane/16) + r, channels chan and chan + 16), so lane group
+// g = lane / 16 takes edges 4g..4g+3 of the tile: it gathers their dm rows
+// for its channels and runs the edge's backward.  dY of an edge is summed
+// over the group's 16 lanes (a fixed reduce-scatter) and stored per slab
+// (dY_part [slab][E][DY], added over the slabs afterwards); dx is summed
+// over the four groups with a fixed butterfly.  Padding edges are not
+// visited (zeroed afterwards).
+template <class S>
+__global__ void __launch_bounds__(64 * kRadWaves, 1)
+    k_conv_bwd_radial(int n_nodes, int n_edges, int C, int n_slabs, const int* __restrict__ order,
+                      const int* __restrict__ colptr, const int* __restrict__ perm,
+                      const int* __restrict__ recv, const float* __restrict__ vec,
+                      const float* __restrict__ x, const float* __restrict__ W2,
+                      const half8* __restrict__ hid, const float* __restrict__ dm,
+                      float* __restrict__ dx, float* __restrict__ dw,
+                      float* __restrict__ dY_part) {
+  using PL = Plan<S>;
+  constexpr int NP = PL::NP, DX = PL::DX, DY = PL::DY, DO = PL::DO, YS = DY + 1;
+  extern __shared__ __align__(16) unsigned char smem[];
+  half8* s_w2 = reinterpret_cast<half8*>(smem);  // [NP][cb 2][ks 2][hi/lo 2][64 lanes]
+  float* s_y = reinterpret_cast<float*>(smem + size_t(NP) * 8 * 64 * sizeof(half8));
+  int* s_e = reinterpret_cast<int*>(s_y + kRadWaves * kRadChunk * YS);  // [wave][64]
+  int* s_r = s_e + kRadWaves * kRadChunk;                                // [wave][64]
+
+  const int xcd = blockIdx.x % kRadXcds, slot = blockIdx.x / kRadXcds;
+  const int slab = xcd % n_slabs, part = xcd / n_slabs, n_parts = kRadXcds / n_slabs;
+  const int64_t ncols = int64_t(NP) * C;
+  for (int i = threadIdx.x; i < NP * 4 * 64; i += blockDim.x) {
+    const int p = i / 256, cb = (i / 128) % 2, ks = (i / 64) % 2, l = i % 64;
+    const int64_t col = int64_t(p) * C + slab * 32 + cb * 16 + (l & 15);
+    const int k0 = ks * 32 + 8 * (l >> 4);
+    half8 hi, lo;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float v = W2[int64_t(k0 + t) * ncols + col];
+      hi[t] = static_cast<_Float16>(v);
+      lo[t] = static_cast<_Float16>((v - static_cast<float>(hi[t])) * kLoScale);
+    }
+    s_w2[(i / 64) * 128 + l] = hi;
+    s_w2[(i / 64) * 128 + 64 + l] = lo;
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gq = lane >> 4, li = lane & 15;
+  float* ys = s_y + wave * kRadChunk * YS;
+  int* se = s_e + wave * kRadChunk;
+  int* sr = s_r + wave * kRadChunk;
+  const int chan = slab * 32 + li;  // and chan + 16
+  const int per_part = (n_nodes + n_parts - 1) / n_parts;
+  const int lo_pos = part * per_part, hi_pos = min(n_nodes, lo_pos + per_part);
+  const int waves_here = (gridDim.x / kRadXcds) * kRadWaves;
+
+  for (int pos = lo_pos + slot * kRadWaves + wave; pos < hi_pos; pos += waves_here) {
+    const int a = order ? order[pos] : pos;
+    float xv[DX][2], dxa[DX][2];
+#pragma unroll
+    for (int i = 0; i < DX; ++i)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        xv[i][cb] = x[(int64_t(a) * DX + i) * C + chan + 16 * cb];
+        dxa[i][cb] = 0.0f;
+      }
+    // clamped so that a workspace built for another graph stays in bounds
+    const int beg = max(colptr[a], 0), end = min(colptr[a + 1], n_edges);
+    for (int c0 = beg; c0 < end; c0 += kRadChunk) {
+      // stage one out-edge per lane: edge id, receiver and harmonics
+      wave_lds_fence();  // the previous chunk's reads are done
+      {
+        const int j = c0 + lane;
+        int e = -1, b = -1;
+        if (j < end) {
+          e = perm[j];
+          b = recv[j];
+          if (e < 0 || e >= n_edges || b < 0 || b >= n_nodes) e = -1;  // only for malformed CSR
+        }
+        se[lane] = e;
+        sr[lane] = e >= 0 ? b : 0;
+        float vx = 0.0f, vy = 0.0f, vz = 0.0f;
+        if (e >= 0) {
+          vx = vec[int64_t(e) * 3];
+          vy = vec[int64_t(e) * 3 + 1];
+          vz = vec[int64_t(e) * 3 + 2];
+        }
+        float Y[DY];
+        edge_y_from_vec<S>(vx, vy, vz, Y);
+#pragma unroll
+        for (int i = 0; i < DY; ++i) ys[lane * YS + i] = Y[i];
+      }
+      wave_lds_fence();
+      const int nt = (min(kRadChunk, end - c0) + 15) / 16;
+      for (int t = 0; t < nt; ++t) {
+        wave_lds_fence();
+        // A operand: h of edge row t*16 + li (zeros for rows past the list)
+        half8 ah[2], al[2];
+        {
+          const int er = se[t * 16 + li];
+          const bool ok = er >= 0;
+          const half8* hp = hid + int64_t(ok ? er : 0) * 16 + gq * 2;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const half8 vh = hp[ks * 8], vl = hp[ks * 8 + 1];
+            ah[ks] = ok ? vh : half8{};
+            al[ks] = ok ? vl : half8{};
+          }
+        }
+        // w of edges t*16 + 4 gq + r, channels chan + 16 cb, for every path:
+        // hi*hi in D, the two cross products (low parts scaled by 2^11) in X
+        float4v wq[NP][2];
+        sfor<0, NP>([&](auto pi) {
+          const half8* wb = s_w2 + size_t(pi) * 512;
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            float4v D = {0.0f, 0.0f, 0.0f, 0.0f}, X = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              const half8 bh = wb[(cb * 2 + ks) * 128 + lane];
+              const half8 bl = wb[(cb * 2 + ks) * 128 + 64 + lane];
+              D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bh, D, 0, 0, 0);
+              X = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], bl, X, 0, 0, 0);
+              X = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[ks], bh, X, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wq[pi][cb][r] = fmaf(X[r], kLoUnscale, D[r]);
+          }
+        });
+        // one edge at a time (not unrolled: each copy of the edge's backward
+        // would hold its own registers); wq rotates so that component 0 is
+        // always the current edge's
+#pragma unroll 1
+        for (int rr = 0; rr < 4; ++rr) {
+          const int jj = t * 16 + 4 * gq + rr;
+          const int e = se[jj], b = sr[jj];
+          const bool valid = e >= 0;
+          float dmv[DO][2];
+#pragma unroll
+          for (int o = 0; o < DO; ++o)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+              dmv[o][cb] = valid ? dm[(int64_t(b) * DO + o) * C + chan + 16 * cb] : 0.0f;
+          float Y[DY], dYl[DY];
+#pragma unroll
+          for (int i = 0; i < DY; ++i) {
+            Y[i] = ys[jj * YS + i];
+            dYl[i] = 0.0f;
+          }
+          float wv[NP][2];
+#pragma unroll
+          for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+              wv[p][cb] = wq[p][cb][0];
+              wq[p][cb] = float4v{wq[p][cb][1], wq[p][cb][2], wq[p][cb][3], 0.0f};
+            }
+          edge_backward_pair<S>(Y, xv, wv, dmv, dxa,
+                                dw + int64_t(valid ? e : 0) * NP * C + chan, C, valid, dYl);
+          // this slab's part of dY[e]: the group's 16 lanes, fixed order
+          Scatter<DY> sc;
+          reduce_scatter<DY>(dYl, 16, lane, sc);
+          if (valid && sc.first < DY)
+            dY_part[(int64_t(slab) * n_edges + e) * DY + sc.first] = sc.v[0];
+        }
+      }
+    }
+    // the four lane groups hold partial sums over different edges of the
+    // same channels: fixed butterfly, then group gq stores components i = gq mod 4
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < DX; ++i) {
+        float v = dxa[i][cb];
+        v += shfl_xor_c<16>(v);
+        v += shfl_xor_c<32>(v);
+        dxa[i][cb] = v;
+      }
+    float* xb = dx + int64_t(a) * DX * C + chan;
+#pragma unroll
+    for (int i = 0; i < DX; ++i)
+      if ((i & 3) == gq) {
+        xb[int64_t(i) * C] = dxa[i][0];
+        xb[int64_t(i) * C + 16] = dxa[i][1];
+      }
+  }
+}
+
+// dY[e] = the slabs' parts added in slab order (padding edges' rows are
+// zeroed afterwards by the padding kernel).
+__global__ void __launch_bounds__(256)
+    k_sum_dy_slabs(int64_t n, int n_slabs, const float* __restrict__ part, float* __restrict__ dY) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = part[i];
+  for (int q = 1; q < n_slabs; ++q) s += part[int64_t(q) * n + i];
+  dY[i] = s;
+}
+
+// zero the dw and dY rows of padding edges (the walk does not visit them)
+__global__ void __launch_bounds__(256)
+    k_zero_padding_rows(const int* __restrict__ npad, const int* __restrict__ padlist,
+                        int n_edges, int row, int dy, float* __restrict__ dw,
+                        float* __restrict__ dY) {
+  const int n = min(*npad, n_edges);
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int64_t e = padlist[i];
+    if (e < 0 || e >= n_edges) continue;
+    for (int k = threadIdx.x; k < row; k += blockDim.x) dw[e * row + k] = 0.0f;
+    for (int k = threadIdx.x; k < dy; k += blockDim.x) dY[e * dy + k] = 0.0f;
+  }
+}
+
+template <class S>
+hipError_t launch_bwd_radial(const RadialBwdArgs& a, hipStream_t s) {
+  using PL = Plan<S>;
+  const size_t lds = radial_bwd_lds_bytes<S>();
+  static std::atomic<bool> lds_set{false};
+  if (const hipError_t e = set_max_lds_once(
+          lds_set, reinterpret_cast<const void*>(&k_conv_bwd_radial<S>), int(lds));
+      e != hipSuccess)
+    return e;
+  const int n_slabs = a.C / 32;
+  hipLaunchKernelGGL((k_conv_bwd_radial<S>), dim3(kRadXcds * 32), dim3(64 * kRadWaves), lds, s,
+                     a.n_nodes, a.n_edges, a.C, n_slabs, a.order, a.colptr, a.perm, a.recv, a.vec,
+                     a.x, a.W2, static_cast<const half8*>(a.hidden), a.dm, a.dx, a.dw, a.dY_part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.n_edges <= 0) return err;
+  const int64_t n = int64_t(a.n_edges) * PL::DY;
+  hipLaunchKernelGGL(k_sum_dy_slabs, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, n, n_slabs,
+                     a.dY_part, a.dY);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_zero_padding_rows, dim3(256), dim3(256), 0, s, a.npad, a.padlist,
+                     a.n_edges, PL::NP * a.C, PL::DY, a.dw, a.dY);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------ radial MLP backward
 
 constexpr int kTailBatch = 64;
@@ -1119,6 +1435,16 @@ hipError_t launch_sum_partials(int n_chunks, int n, float* part, float* out, hip
 hipError_t launch_conv_fwd_radial(const char* set_name, const RadialConvArgs& a, hipStream_t s) {
   if (a.n_nodes <= 0) return hipSuccess;
   if (set_name && std::strcmp(set_name, "L1to3") == 0) return launch_fwd_radial<SigL1to3>(a, s);
+  return hipErrorNotSupported;
+}
+
+size_t conv_bwd_radial_scratch_bytes(int n_edges, int C, int dy) {
+  return size_t(C / 32) * size_t(n_edges) * size_t(dy) * sizeof(float);
+}
+
+hipError_t launch_conv_bwd_radial(const char* set_name, const RadialBwdArgs& a, hipStream_t s) {
+  if (a.n_nodes <= 0) return hipSuccess;
+  if (set_name && std::strcmp(set_name, "L1to3") == 0) return launch_bwd_radial<SigL1to3>(a, s);
   return hipErrorNotSupported;
 }
 

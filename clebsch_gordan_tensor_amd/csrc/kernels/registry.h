@@ -200,6 +200,29 @@ struct RadialConvArgs {
   const void* hidden = nullptr;  // the hidden layer's packed operands per edge, or null
 };
 bool radial_conv_supported(const char* set_name);
+// The convolution backward with w formed from the hidden layer (never read
+// or written): the transposed index of the prepare step, dY_part scratch of
+// conv_bwd_radial_scratch_bytes (per 32-channel slab parts of dY).
+struct RadialBwdArgs {
+  int n_nodes, n_edges, C;
+  const int* order;   // traversal order of the senders, or null
+  const int* colptr;
+  const int* perm;
+  const int* recv;
+  const int* npad;
+  const int* padlist;
+  const float* vec;   // edge vectors [E][3]
+  const float* x;     // [N][dx][C] float32
+  const float* W2;    // [64][P*C]
+  const void* hidden; // the hidden layer's packed operands per edge
+  const float* dm;    // [N][dout][C]
+  float* dx;          // [N][dx][C]
+  float* dw;          // [E][P][C]
+  float* dY;          // [E][dy]
+  float* dY_part;     // [C/32][E][dy]
+};
+size_t conv_bwd_radial_scratch_bytes(int n_edges, int C, int dy);
+hipError_t launch_conv_bwd_radial(const char* set_name, const RadialBwdArgs& a, hipStream_t s);
 // The radial MLP's hidden layer per edge in the fused convolution's operand
 // form: [E][2 ks][4 quarters][hi, lo] fp16 x 8 (256 bytes per edge).
 constexpr size_t kRadialHiddenBytes = 256;

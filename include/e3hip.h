@@ -274,6 +274,30 @@ e3_status e3_conv_forward_radial_hidden(const e3_desc* desc, int32_t n_nodes, in
                                         const e3_radial* mlp, const void* hidden, size_t h_bytes,
                                         float* m, void* stream);
 
+/* Convolution backward (as e3_conv_backward: e3j E.1 Eq.16 with one scalar
+ * per path) with the per-edge weights formed on the fly from the radial
+ * MLP's hidden layer, as e3_conv_forward_radial_hidden forms them (e3j A.3,
+ * the edge scalars of Eq.7): w is neither read nor written.  For the dm of
+ * the fused radial forward's m it gives dx [N][dx][C], dw [E][P][C] (the
+ * cotangent of w, for e3_radial_mlp_backward) and dY [E][dy] (for
+ * e3_spherical_harmonics_backward), all float32.  hidden: e3_radial_hidden
+ * of the same edge vectors (h_bytes >= e3_radial_hidden_size); workspace:
+ * from e3_conv_prepare_transpose on the same graph (required); scratch:
+ * caller-owned device memory of e3_conv_backward_radial_scratch_size bytes
+ * (per 32-channel slab partial sums of dY, added in slab order).  Same
+ * signature, channel counts and flags as the fused forward; x, dm, dx, dw,
+ * hidden 16-byte aligned; errors as e3_conv_backward plus E3_ERR_WORKSPACE
+ * for a short hidden or scratch.  Padding edges get zero dw and dY. */
+e3_status e3_conv_backward_radial_scratch_size(const e3_desc* desc, int32_t n_edges,
+                                               size_t* bytes);
+e3_status e3_conv_backward_radial_hidden(const e3_desc* desc, int32_t n_nodes, int32_t n_edges,
+                                         const int32_t* rowptr, const int32_t* sender,
+                                         const void* workspace, size_t ws_bytes,
+                                         const float* edge_vec, const float* x,
+                                         const e3_radial* mlp, const void* hidden, size_t h_bytes,
+                                         const float* dm, float* dx, float* dw, float* dY,
+                                         void* scratch, size_t scratch_bytes, void* stream);
+
 /* Backward of e3_radial_mlp for the cotangent dw [E][n_cols] (n_cols a
  * multiple of 32): dW1 [8][64] and dW2 [64][n_cols] (summed over the edges
  * through fixed partials: reproducible) and dvec [E][3], the part of the

@@ -339,3 +339,131 @@ def test_radial_mlp_backward_no_edges(gpu):
     dW1, dW2, dvec = gpu.radial_mlp_backward(ev, 5.0, W1, W2, dw)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dW1) == 0 and torch.count_nonzero(dW2) == 0 and dvec.numel() == 0
+
+
+# ------------------------------------------- fused radial convolution backward
+
+def _hub_sender_graph():
+    # _graph_c32 with every edge reversed (receivers become senders): atom 7
+    # sends to every other atom (25 tiles of 16 out-edges), atoms 11 and 12
+    # send nothing; then one padding edge per segment again
+    from tests.test_oracle_conv import with_padding
+    g = _graph_c32()
+    recv = np.repeat(np.arange(g.n_nodes), np.diff(g.rowptr))
+    keep = g.sender >= 0
+    r2, s2, v2 = g.sender[keep], recv[keep], -g.evec[keep]
+    o = np.argsort(r2, kind="stable")
+    r2, s2, v2 = r2[o], s2[o], v2[o]
+    rowptr = np.concatenate([[0], np.cumsum(np.bincount(r2, minlength=g.n_nodes))]).astype(np.int32)
+    g2 = S.Graph(pos=g.pos, rowptr=rowptr, sender=s2.astype(np.int32),
+                 receiver=r2.astype(np.int32), evec=v2.astype(np.float32))
+    return with_padding(g2, n_pad_per_node=1, seed=212)
+
+
+def _radial_bwd_case(gpu, g, C, seed, cutoff=3.5):
+    d = gpu.Desc(X01, SH3, SH3, C)
+    od = O.Desc(X01, SH3, SH3, C)
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((g.n_nodes, 4, C)).astype(np.float32)
+    dm = rng.standard_normal((g.n_nodes, 16, C)).astype(np.float32)
+    W1, W2 = _weights(gpu.num_paths(d) * C, seed + 1)
+    rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+    W1d, W2d = dev(W1), dev(W2)
+    ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=ev)
+    h = gpu.radial_hidden(ev, cutoff, W1d, W2d)
+    dx, dw, dY = gpu.conv_backward_radial_hidden(d, rowptr, sender, ws, ev, dev(x), cutoff, W1d,
+                                                  W2d, h, dev(dm))
+    # the composed path: w written by the MLP (from the same hidden layer), then
+    # the convolution backward reading it
+    w = gpu.radial_mlp_hidden(h, g.n_edges, cutoff, W1d, W2d).view(g.n_edges, -1, C)
+    cdx, cdw, cdY = gpu.conv_backward(d, rowptr, sender, ws, ev, dev(x), w, dev(dm))
+    torch.cuda.synchronize()
+    return d, od, x, dm, W1, W2, (dx, dw, dY), (cdx, cdw, cdY)
+
+
+@pytest.mark.parametrize("graph,C", [("c32", 32), ("hub_sender", 64), ("c32", 256)])
+def test_conv_backward_radial_matches_oracle(gpu, graph, C):
+    # padding edges in every segment, isolated atoms, a hub sender (25 tiles)
+    # or hub receiver; C = 32, 64 (two slabs), 256 (eight slabs)
+    g = _graph_c32() if graph == "c32" else _hub_sender_graph()
+    d, od, x, dm, W1, W2, (dx, dw, dY), (cdx, cdw, cdY) = _radial_bwd_case(gpu, g, C, 270 + C)
+    w = R.radial_mlp(g.evec, 3.5, W1, W2).reshape(g.n_edges, -1, C)
+    w[g.sender < 0] = 0.0
+    rdx = O.conv_backward_dx(od, g.rowptr, g.sender, w, dm, evec=g.evec)
+    rdw, rdY = O.conv_backward_edge(od, g.rowptr, g.sender, x, w, dm, evec=g.evec)
+    assert_close(host(dx), rdx, TOL_F32, f"radial conv bwd dx {graph} C={C}")
+    assert_close(host(dw), rdw, TOL_F32, f"radial conv bwd dw {graph} C={C}")
+    assert_close(host(dY), rdY, TOL_F32, f"radial conv bwd dY {graph} C={C}")
+    pad = torch.from_numpy(g.sender < 0).cuda()
+    assert torch.count_nonzero(dw[pad]) == 0 and torch.count_nonzero(dY[pad]) == 0
+    # dw is the same arithmetic on the same bits of w as the composed path's
+    assert torch.equal(dw.view(torch.int32), cdw.view(torch.int32))
+
+
+def test_conv_backward_radial_water3k_and_deterministic(gpu):
+    p = S.make_conv("water3k", with_dm=True)
+    g = p.graph
+    d = gpu.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    od = O.Desc(p.x_irreps, p.y_irreps, p.out_irreps, p.channels)
+    W1, W2 = _weights(O.num_paths(od) * p.channels, 280)
+    rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+    W1d, W2d = dev(W1), dev(W2)
+    ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=ev)
+    h = gpu.radial_hidden(ev, 5.0, W1d, W2d)
+    a = gpu.conv_backward_radial_hidden(d, rowptr, sender, ws, ev, dev(p.x), 5.0, W1d, W2d, h,
+                                        dev(p.dm))
+    b = gpu.conv_backward_radial_hidden(d, rowptr, sender, ws, ev, dev(p.x), 5.0, W1d, W2d, h,
+                                        dev(p.dm))
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+    w = R.radial_mlp(g.evec, 5.0, W1, W2).reshape(g.n_edges, -1, p.channels)
+    w[g.sender < 0] = 0.0
+    rdx = O.conv_backward_dx(od, g.rowptr, g.sender, w, p.dm, evec=g.evec)
+    rdw, rdY = O.conv_backward_edge(od, g.rowptr, g.sender, p.x, w, p.dm, evec=g.evec)
+    assert_close(host(a[0]), rdx, TOL_F32, "radial conv bwd dx water3k")
+    assert_close(host(a[1]), rdw, TOL_F32, "radial conv bwd dw water3k")
+    assert_close(host(a[2]), rdY, TOL_F32, "radial conv bwd dY water3k")
+
+
+def test_conv_backward_radial_full_size(gpu):
+    # the 64k-atom graph (3.1M edges) with the prepared order: dw bitwise the
+    # composed path's over every edge; dx of sampled senders and dw, dY of
+    # sampled edges against the oracle
+    cfg = S.CONV_CONFIGS["mace64k"]
+    n = cfg["n"]
+    g = S.random_graph(n, (n / cfg["density"]) ** (1.0 / 3.0), cfg["cutoff"], 0,
+                       permute_labels=cfg["permute"])
+    C, xi = S.parse_irreps(cfg["x"])
+    _, oi = S.parse_irreps(cfg["out"])
+    yi = S.sh_irreps(cfg["lmax"])
+    d = gpu.Desc(xi, yi, oi, C)
+    od = O.Desc(xi, yi, oi, C)
+    xh = S.normal((n, S.dim(xi), C), 0, S.TAG_X)
+    dmh = np.random.default_rng(290).standard_normal((n, S.dim(oi), C)).astype(np.float32)
+    W1, W2 = _weights(O.num_paths(od) * C, 291)
+    rowptr, sender, ev = dev(g.rowptr), dev(g.sender), dev(g.evec)
+    W1d, W2d = dev(W1), dev(W2)
+    ws = gpu.conv_prepare_transpose(rowptr, sender, edge_vec=ev)
+    h = gpu.radial_hidden(ev, 5.0, W1d, W2d)
+    dx, dw, dY = gpu.conv_backward_radial_hidden(d, rowptr, sender, ws, ev, dev(xh), 5.0, W1d,
+                                                  W2d, h, dev(dmh))
+    torch.cuda.synchronize()
+    w = gpu.radial_mlp_hidden(h, g.n_edges, 5.0, W1d, W2d).view(g.n_edges, -1, C)
+    _, cdw, _ = gpu.conv_backward(d, rowptr, sender, ws, ev, dev(xh), w, dev(dmh))
+    torch.cuda.synchronize()
+    assert torch.equal(dw.view(torch.int32), cdw.view(torch.int32))
+    del w, cdw
+    rng = np.random.default_rng(292)
+    rows = np.sort(rng.choice(n, 150, replace=False))
+    edges = np.sort(rng.choice(g.n_edges, 600, replace=False))
+    # the oracle's weights only where they are read: the edges out of the
+    # sampled senders and the sampled edges
+    need = np.union1d(np.nonzero(np.isin(g.sender, rows))[0], edges)
+    wr = np.zeros((g.n_edges, O.num_paths(od), C))
+    wr[need] = R.radial_mlp(g.evec[need], 5.0, W1, W2).reshape(len(need), -1, C)
+    rdx = O.conv_backward_dx(od, g.rowptr, g.sender, wr, dmh, evec=g.evec, rows=rows)
+    rdw, rdY = O.conv_backward_edge(od, g.rowptr, g.sender, xh, wr, dmh, evec=g.evec, edges=edges)
+    assert_close(host(dx)[rows], rdx, TOL_F32, "radial conv bwd dx 64k sampled")
+    assert_close(host(dw)[edges], rdw, TOL_F32, "radial conv bwd dw 64k sampled")
+    assert_close(host(dY)[edges], rdY, TOL_F32, "radial conv bwd dY 64k sampled")
