@@ -425,3 +425,49 @@ def test_radial_hidden_arg_errors(lib):
                                              C.byref(r), fk, 8 * 256 - 16, fk, None) == -6
     assert lib.e3_conv_forward_radial_hidden(C.byref(d.c()), 4, 8, fk, fk, None, 0, fk, fk,
                                              C.byref(r), odd, 8 * 256, fk, None) == -4
+
+
+def test_conv_backward_radial_arg_errors(lib):
+    # the fused radial backward checks its descriptor, sizes, workspace,
+    # scratch and alignment on the host, before any device work (the pointers
+    # below are never dereferenced)
+    fk, odd = C.c_void_p(0x10000), C.c_void_p(0x10004)
+    r = api._CRadial(5.0, 8, 64, fk, fk)
+    x01 = [(0, 1), (1, -1)]
+    sh3 = [(0, 1), (1, -1), (2, 1), (3, -1)]
+    n_nodes, n_edges = 4, 8
+    wsn = C.c_size_t()
+    assert lib.e3_conv_workspace_size(n_nodes, n_edges, C.byref(wsn)) == 0
+    ws = wsn.value
+    d = api.Desc(x01, sh3, sh3, 32)
+    nb = C.c_size_t()
+    assert lib.e3_conv_backward_radial_scratch_size(C.byref(d.c()), n_edges, C.byref(nb)) == 0
+    assert nb.value == 1 * n_edges * 16 * 4  # one 32-channel slab, dy = 16
+    d128 = api.Desc(x01, sh3, sh3, 128)
+    assert lib.e3_conv_backward_radial_scratch_size(C.byref(d128.c()), n_edges, C.byref(nb)) == 0
+    assert nb.value == 4 * n_edges * 16 * 4
+    assert lib.e3_conv_backward_radial_scratch_size(C.byref(d.c()), -1, C.byref(nb)) == -1
+    hb, sb = n_edges * 256, n_edges * 16 * 4
+
+    def call(desc=d, n=n_nodes, e=n_edges, wsp=fk, wsb=ws, hid=fk, hbytes=hb, scr=fk, sbytes=sb,
+             x=fk, dw=fk, rad=r):
+        return lib.e3_conv_backward_radial_hidden(C.byref(desc.c()), n, e, fk, fk, wsp, wsb, fk, x,
+                                                  C.byref(rad), hid, hbytes, fk, fk, dw, fk, scr,
+                                                  sbytes, None)
+
+    assert call(n=0) == 0                      # nothing to do
+    assert call(e=-1) == -1                    # negative size
+    assert call(wsp=None) == -6                # the transposed index is required
+    assert call(wsb=ws - 4) == -6
+    assert call(hid=None) == -1
+    assert call(hbytes=hb - 16) == -6          # short hidden layer
+    assert call(scr=None) == -6                # scratch required with edges
+    assert call(sbytes=sb - 4) == -6
+    assert call(x=odd) == -4                   # alignment
+    assert call(hid=odd) == -4
+    assert call(dw=odd) == -4
+    assert call(rad=api._CRadial(5.0, 8, 32, fk, fk)) == -3  # only 64 hidden units
+    # other signatures, channel counts and layouts are not built for it
+    assert call(desc=api.Desc(x01, [(0, 1), (1, -1)], [(0, 1), (1, -1)], 32)) == -3
+    assert call(desc=api.Desc(x01, sh3, sh3, 48)) == -3
+    assert call(desc=api.Desc(x01, sh3, sh3, 32, flags=api.E3_OUT_PER_PATH)) == -3
