@@ -535,8 +535,8 @@ hipError_t launch_fwd_radial(const RadialConvArgs& a, hipStream_t s) {
 
 // Backward of one edge for this lane's two channels chan and chan + 16 (as
 // edge_backward, e3j E.1 Eq.16 with one scalar per path): dx gains
-// w[P] B_P, dw[P] = sum_m1 x B_P is stored at dwe + P C (+16), and dYl
-// collects this lane's part of dY.
+// w[P] B_P, dw[P] = sum_m1 x B_P is stored at dwe + P C (+16) after the
+// last path, and dYl collects this lane's part of dY.
 template <class S>
 __device__ __forceinline__ void edge_backward_pair(const float (&Y)[Plan<S>::DY],
                                                    const float (&xv)[Plan<S>::DX][2],
@@ -546,7 +546,7 @@ __device__ __forceinline__ void edge_backward_pair(const float (&Y)[Plan<S>::DY]
                                                    float* __restrict__ dwe, int C, bool store,
                                                    float (&dYl)[Plan<S>::DY]) {
   using PL = Plan<S>;
-  float t[PL::DX][2];
+  float t[PL::DX][2], dwv[PL::NP][2];
 #pragma unroll
   for (int i = 0; i < PL::DX; ++i) t[i][0] = t[i][1] = 0.0f;
   sfor<0, PL::NP>([&](auto pi) {
@@ -575,7 +575,6 @@ __device__ __forceinline__ void edge_backward_pair(const float (&Y)[Plan<S>::DY]
         for (int k = 0; k < 2; ++k) B[R.m1][k] = fmaf(A, dmv[P.oo + R.M][k], B[R.m1][k]);
       }
     });
-    float dwp[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       float s = 0.0f;
@@ -584,13 +583,16 @@ __device__ __forceinline__ void edge_backward_pair(const float (&Y)[Plan<S>::DY]
         t[P.xo + a][k] = fmaf(wv[pi][k], B[a][k], t[P.xo + a][k]);
         s = fmaf(xv[P.xo + a][k], B[a][k], s);
       }
-      dwp[k] = s;
-    }
-    if (store) {
-      __builtin_nontemporal_store(dwp[0], dwe + int64_t(pi) * C);
-      __builtin_nontemporal_store(dwp[1], dwe + int64_t(pi) * C + 16);
+      dwv[pi][k] = s;
     }
   });
+  if (store) {  // one branch for the edge's stores
+#pragma unroll
+    for (int p = 0; p < PL::NP; ++p) {
+      __builtin_nontemporal_store(dwv[p][0], dwe + int64_t(p) * C);
+      __builtin_nontemporal_store(dwv[p][1], dwe + int64_t(p) * C + 16);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < PL::DX; ++i) {
     dxa[i][0] += t[i][0];
@@ -747,12 +749,16 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
           const int jj = t * 16 + 4 * gq + rr;
           const int e = se[jj], b = sr[jj];
           const bool valid = e >= 0;
+          // loaded unconditionally (an invalid row's receiver is node 0) and
+          // zeroed after, so no load waits behind a branch
           float dmv[DO][2];
 #pragma unroll
           for (int o = 0; o < DO; ++o)
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-              dmv[o][cb] = valid ? dm[(int64_t(b) * DO + o) * C + chan + 16 * cb] : 0.0f;
+            for (int cb = 0; cb < 2; ++cb) {
+              const float v = dm[(int64_t(b) * DO + o) * C + chan + 16 * cb];
+              dmv[o][cb] = valid ? v : 0.0f;
+            }
           float Y[DY], dYl[DY];
 #pragma unroll
           for (int i = 0; i < DY; ++i) {
