@@ -692,7 +692,7 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
           if (e < 0 || e >= n_edges || b < 0 || b >= n_nodes) e = -1;  // only for malformed CSR
         }
         se[lane] = e;
-        sr[lane] = e >= 0 ? b : 0;
+        sr[lane] = e >= 0 ? b : a;  // an invalid row reads the sender's own dm row (not a shared one)
         float vx = 0.0f, vy = 0.0f, vz = 0.0f;
         if (e >= 0) {
           vx = vec[int64_t(e) * 3];
@@ -749,8 +749,8 @@ __global__ void __launch_bounds__(64 * kRadWaves, 1)
           const int jj = t * 16 + 4 * gq + rr;
           const int e = se[jj], b = sr[jj];
           const bool valid = e >= 0;
-          // loaded unconditionally (an invalid row's receiver is node 0) and
-          // zeroed after, so no load waits behind a branch
+          // loaded unconditionally (an invalid row reads the sender's own
+          // row) and zeroed after, so no load waits behind a branch
           float dmv[DO][2];
 #pragma unroll
           for (int o = 0; o < DO; ++o)
