@@ -55,7 +55,8 @@
 #endif
 
 #define ORACLE_MAX_IRREPS 16
-#define ORACLE_MAX_L 6 /* harmonics; CG blocks up to twice this */
+#define ORACLE_MAX_L 8 /* harmonics; CG blocks up to twice this */
+#define ORACLE_MAX_DY 128 /* y components per row (the per-edge y buffer) */
 #define ORACLE_MAX_PATHS 256
 
 typedef struct {
@@ -242,7 +243,7 @@ int oracle_sh_general(int l, const double r[3], double *out) {
 }
 
 /* Component-normalised real harmonics of the unit vector r/|r|, written out
- * as polynomials for l <= 3, by oracle_sh_general above for l = 4..6.
+ * as polynomials for l <= 3, by oracle_sh_general above for l = 4..8.
  * out has 2l+1 entries, m = -l..l.  A zero vector yields the l = 0 value
  * only (higher degrees are 0). */
 int oracle_sh_l(int l, const double r[3], double *out) {
@@ -334,7 +335,7 @@ static int plan_build(const oracle_desc *d, oplan *pl) {
     ooff[i] = pl->dout;
     pl->dout += 2 * d->ol[i] + 1;
   }
-  if (pl->dy > 64) return -1; /* per-edge y buffer below */
+  if (pl->dy > ORACLE_MAX_DY) return -1; /* per-edge y buffer below */
   pl->np = 0;
   for (int ix = 0; ix < d->nx; ++ix)
     for (int iy = 0; iy < d->ny; ++iy)
@@ -447,7 +448,7 @@ int oracle_conv_forward(const oracle_desc *d, int n_nodes, int64_t n_edges, cons
       bad = 1;
       continue;
     }
-    double Ye[64];
+    double Ye[ORACLE_MAX_DY];
     for (int64_t e = rowptr[b]; e < rowptr[b + 1]; ++e) {
       int a = sender[e];
       if (a < 0) continue; /* padding edge */
@@ -569,7 +570,7 @@ int oracle_conv_backward_dx(const oracle_desc *d, int n_nodes, int64_t n_edges, 
     int a = rows[i];
     if (a < 0 || a >= n_nodes) continue;
     int s = slot[a];
-    double Ye[64];
+    double Ye[ORACLE_MAX_DY];
     for (int64_t k = cnt[s]; k < cnt[s + 1]; ++k) {
       int64_t e = lst[k];
       int b = recv[e];
@@ -638,7 +639,7 @@ int oracle_conv_backward_edge(const oracle_desc *d, int n_nodes, int64_t n_edges
     int a = sender[e];
     if (a < 0) continue;
     int b = recv[e];
-    double Ye[64];
+    double Ye[ORACLE_MAX_DY];
     edge_y(d, pl, e, evec, Yg, Ye);
     const double *xa = x + (int64_t)a * dx * C;
     const double *we = w + e * P * C;

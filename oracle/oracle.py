@@ -327,10 +327,11 @@ def sh_grad(lmax: int, vecs, dY) -> np.ndarray:
 
 def sh_grad_fd(lmax: int, vecs, dY) -> np.ndarray:
     """J^T dY of the harmonics of vecs [n][3] by fourth-order central
-    differences of sh() (fp64), for the degrees (4..6) that the closed-form
+    differences of sh() (fp64), for the degrees (4..8) that the closed-form
     partials of sh_grad do not cover.  Step h = 1e-3 |r| per axis: the
-    truncation error is O(h^4 |d^5 Y|), about 1e-9 of the value at l = 6,
-    and the rounding error about 1e-13 |Y| / h.  A zero vector gets 0."""
+    truncation error is O(h^4 |d^5 Y|), about 1e-9 of the value at l = 6
+    and 3e-8 at l = 8, and the rounding error about 1e-13 |Y| / h.  A zero
+    vector gets 0."""
     v = _f64(vecs).reshape(-1, 3)
     g = _f64(dY).reshape(v.shape[0], (lmax + 1) ** 2)
     r = np.linalg.norm(v, axis=1)

@@ -1,5 +1,5 @@
-"""Pins of the oracle at degrees 4..6 (the tensor products of e3j B.1,
-Figs 5-6, run to L = 6 and beyond): the general harmonics against scipy's
+"""Pins of the oracle at degrees 4..8 (the tensor products and convolutions
+of e3j B.1, Figs 5-7, run to L = 8): the general harmonics against scipy's
 complex harmonics through the change of basis, their norm, z-axis values,
 parity, harmonicity and rotation behaviour, and against the closed-form
 polynomials at l <= 3; the Racah coefficients against a numpy
@@ -15,8 +15,9 @@ import pytest
 from oracle import oracle as O
 from tests.test_oracle_cg import _cg_by_eigh, _rand_rot, _real_sh_scipy, wigner_d
 
-HI = range(4, 7)
-OFF = [l * l for l in range(8)]
+LH = 8  # highest degree pinned
+HI = range(4, LH + 1)
+OFF = [l * l for l in range(LH + 2)]
 
 
 def unit(rng, n):
@@ -27,8 +28,8 @@ def unit(rng, n):
 def test_general_harmonics_against_scipy():
     rng = np.random.default_rng(40)
     P = unit(rng, 60)
-    Y = O.sh(6, P)
-    for l in range(7):
+    Y = O.sh(LH, P)
+    for l in range(LH + 1):
         np.testing.assert_allclose(Y[:, OFF[l]:OFF[l + 1]], _real_sh_scipy(l, P), atol=1e-11,
                                    err_msg=f"l={l}")
 
@@ -44,8 +45,8 @@ def test_general_construction_equals_closed_forms_at_low_degree():
 def test_high_degree_norm_axis_parity_scale():
     rng = np.random.default_rng(42)
     P = rng.standard_normal((40, 3))
-    Y, Yn, Ys = O.sh(6, P), O.sh(6, -P), O.sh(6, 0.37 * P)
-    Z = O.sh(6, np.array([[0.0, 0.0, 1.7]]))[0]
+    Y, Yn, Ys = O.sh(LH, P), O.sh(LH, -P), O.sh(LH, 0.37 * P)
+    Z = O.sh(LH, np.array([[0.0, 0.0, 1.7]]))[0]
     for l in HI:
         sl = slice(OFF[l], OFF[l + 1])
         np.testing.assert_allclose((Y[:, sl] ** 2).sum(1), 2 * l + 1, rtol=1e-12)
@@ -58,13 +59,14 @@ def test_high_degree_norm_axis_parity_scale():
 
 def test_high_degree_harmonic_polynomials():
     # r^l Y_l(r/|r|) has zero Laplacian (fourth-order central differences:
-    # the second-order stencil's h^2 error is too large at degree 6)
+    # the second-order stencil's h^2 error is too large at degree 6; the
+    # fourth-order one's h^4 error grows as l^6, hence the small step)
     rng = np.random.default_rng(43)
-    h = 1e-2
+    h = 2e-3
     for p in rng.standard_normal((3, 3)):
         def f(q):
             r = np.linalg.norm(q)
-            Y = O.sh(6, q[None])[0]
+            Y = O.sh(LH, q[None])[0]
             return np.concatenate([r ** l * Y[OFF[l]:OFF[l + 1]] for l in HI])
         lap = -90 * f(p)
         for k in range(3):
@@ -75,7 +77,7 @@ def test_high_degree_harmonic_polynomials():
                                    atol=1e-5 * max(1.0, np.abs(f(p)).max()))
 
 
-@pytest.mark.parametrize("l1,l2", [(l1, l2) for l1, l2 in itertools.product(range(7), repeat=2)
+@pytest.mark.parametrize("l1,l2", [(l1, l2) for l1, l2 in itertools.product(range(LH + 1), repeat=2)
                                    if max(l1, l2) >= 4])
 def test_racah_equals_eigh_construction_high_degree(l1, l2):
     ref = _cg_by_eigh(l1, l2)
@@ -90,8 +92,8 @@ def test_racah_equals_eigh_construction_high_degree(l1, l2):
 
 
 def _triples_hi():
-    for l1, l2 in itertools.product(range(7), repeat=2):
-        for L in range(abs(l1 - l2), min(l1 + l2, 6) + 1):
+    for l1, l2 in itertools.product(range(LH + 1), repeat=2):
+        for L in range(abs(l1 - l2), min(l1 + l2, LH) + 1):
             if max(l1, l2, L) >= 4:
                 yield l1, l2, L
 
@@ -105,7 +107,7 @@ def test_real_blocks_orthonormal_high_degree():
 def test_real_blocks_equivariant_high_degree():
     rng = np.random.default_rng(44)
     R = _rand_rot(rng)
-    D = {l: wigner_d(l, R, rng) for l in range(7)}
+    D = {l: wigner_d(l, R, rng) for l in range(LH + 1)}
     for l1, l2, L in _triples_hi():
         T = O.cg_real(l1, l2, L)
         lhs = np.einsum("Mij,ia,jb->Mab", T, D[l1], D[l2])
@@ -118,7 +120,7 @@ def test_gaunt_identity_high_degree():
     # L: kappa = sqrt((2l1+1)(2l2+1)/(2L+1)) <l1 0 l2 0|L 0>
     rng = np.random.default_rng(45)
     r = rng.standard_normal((5, 3))
-    Y = O.sh(6, r)
+    Y = O.sh(LH, r)
     for l1, l2, L in _triples_hi():
         if (l1 + l2 + L) % 2:
             continue
@@ -131,11 +133,11 @@ def test_gaunt_identity_high_degree():
 
 
 def test_zero_vector_high_degree():
-    Y = O.sh(6, np.zeros((1, 3)))[0]
+    Y = O.sh(LH, np.zeros((1, 3)))[0]
     assert Y[0] == 1.0 and np.all(Y[1:] == 0.0)
 
 
-# ------------------------------------------- harmonics gradient, degrees 4..6
+# ------------------------------------------- harmonics gradient, degrees 4..8
 
 def test_sh_grad_fd_matches_closed_form_partials():
     # the finite-difference gradient reproduces the closed-form one to l = 3
@@ -146,28 +148,30 @@ def test_sh_grad_fd_matches_closed_form_partials():
     assert np.abs(a - b).max() <= 1e-8 * np.abs(b).max()
 
 
-def test_sh_grad_fd_high_degree_properties():
+@pytest.mark.parametrize("L", [6, 8])
+def test_sh_grad_fd_high_degree_properties(L):
     # the harmonics depend on the direction only: the gradient is orthogonal
     # to r and scales as 1/|r|; a single component's gradient matches the
     # derivative of the Legendre form along a tangent direction
     rng = np.random.default_rng(61)
-    v = rng.standard_normal((30, 3))
-    dY = rng.standard_normal((30, 49))
-    g = O.sh_grad_fd(6, v, dY)
+    n, dy = 30, (L + 1) ** 2
+    v = rng.standard_normal((n, 3))
+    dY = rng.standard_normal((n, dy))
+    g = O.sh_grad_fd(L, v, dY)
     assert np.abs((g * v).sum(1)).max() <= 1e-8 * np.abs(g).max()
-    g3 = O.sh_grad_fd(6, 3.0 * v, dY)
+    g3 = O.sh_grad_fd(L, 3.0 * v, dY)
     assert np.abs(3.0 * g3 - g).max() <= 1e-8 * np.abs(g).max()
-    # d/dphi of the m = +6 component: Y_66 ~ sin^6(theta) cos(6 phi), so its
-    # derivative along e_phi is -6 Y_6,-6 / (|r| sin theta)
+    # d/dphi of the m = +L component: Y_LL ~ sin^L(theta) cos(L phi), so its
+    # derivative along e_phi is -L Y_L,-L / (|r| sin theta)
     u = v / np.linalg.norm(v, axis=1, keepdims=True)
-    e_phi = np.stack([-u[:, 1], u[:, 0], np.zeros(30)], 1)
+    e_phi = np.stack([-u[:, 1], u[:, 0], np.zeros(n)], 1)
     e_phi /= np.linalg.norm(e_phi, axis=1, keepdims=True)
-    sel = np.zeros((30, 49))
-    sel[:, 36 + 12] = 1.0  # (l, m) = (6, 6)
-    d = (O.sh_grad_fd(6, u, sel) * e_phi).sum(1)
+    sel = np.zeros((n, dy))
+    sel[:, L * L + 2 * L] = 1.0  # (l, m) = (L, L)
+    d = (O.sh_grad_fd(L, u, sel) * e_phi).sum(1)
     sin_t = np.sqrt(u[:, 0] ** 2 + u[:, 1] ** 2)
-    Y = O.sh(6, u)
-    np.testing.assert_allclose(d, -6 * Y[:, 36] / sin_t, rtol=1e-7, atol=1e-8)
+    Y = O.sh(L, u)
+    np.testing.assert_allclose(d, -L * Y[:, L * L] / sin_t, rtol=1e-7, atol=1e-8)
 
 
 def test_sh_grad_fd_zero_vector():

@@ -108,4 +108,4 @@ def test_zero_vector():
 
 def test_rejects_unsupported_degree():
     with pytest.raises(ValueError):
-        O.sh(7, np.ones((1, 3)))
+        O.sh(9, np.ones((1, 3)))
