@@ -775,7 +775,8 @@ def generic_plan(desc: Desc, device, table=0):
 
 def tp_forward_generic(desc: Desc, x, y, w, out=None, stream=None):
     """z = tensor product of x and y weighted by w (as tp_forward) through the
-    coefficient-table kernel: any signature with degrees up to 6."""
+    coefficient-table kernel: any signature with degrees up to 7 (at most 63
+    components per operand)."""
     import torch
     B = x.shape[0]
     P = num_paths(desc)
@@ -795,7 +796,7 @@ def tp_forward_generic(desc: Desc, x, y, w, out=None, stream=None):
 def tp_forward_gemm(desc: Desc, x, y, w, out=None, stream=None):
     """z = tensor product of x and y weighted by w (as tp_forward_generic) as
     one dense product per output block on the fp32 matrix cores (float32,
-    C % 16 == 0, degrees up to 6)."""
+    C % 16 == 0, degrees up to 7)."""
     import torch
     B = x.shape[0]
     P = num_paths(desc)
@@ -908,7 +909,8 @@ def tp_backward_generic(desc: Desc, x, y, w, dz, stream=None):
 def conv_forward_generic(desc: Desc, rowptr, sender, edge_vec_or_Y, x, w, out=None,
                          workspace=None, stream=None):
     """m = conv(x, Y(edge_vec), w) (as conv_forward) through the
-    coefficient-table kernels: any signature with degrees up to 6."""
+    coefficient-table kernels: any signature with degrees up to 7 (at most 63
+    components per operand; harmonics from edge vectors to degree 6)."""
     import torch
     N, E = rowptr.shape[0] - 1, sender.shape[0]
     P = num_paths(desc)
@@ -966,7 +968,7 @@ def conv_backward_generic(desc: Desc, rowptr, sender, workspace, edge_vec_or_Y, 
 def conv_double_backward_generic(desc: Desc, rowptr, sender, workspace, Y, x, w, dm, ddx, ddY,
                                  ddw, scratch=None, stream=None):
     """(dx2, dY2, dw2, ddm) as conv_double_backward through the coefficient
-    tables (degrees up to 6); desc needs E3_Y_GIVEN."""
+    tables (degrees up to 7); desc needs E3_Y_GIVEN."""
     import torch
     N, E = rowptr.shape[0] - 1, sender.shape[0]
     P = num_paths(desc)

@@ -32,7 +32,8 @@ e3_status ok() {
   return E3_OK;
 }
 
-constexpr int kGenericLmax = 6;  // coefficient tables of the generic tensor product
+constexpr int kGenericLmax = 7;  // coefficient tables of the generic tensor product
+constexpr int kTableHarmonicsLmax = 6;  // harmonics the coefficient-table kernels compute
 
 e3_status check_graph_host(int32_t n_nodes, int32_t n_edges, const int32_t* rp,
                            const int32_t* sn);
@@ -287,7 +288,7 @@ int32_t e3_supported(const e3_desc* desc, e3_dtype dtype) {
 e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out) {
   if (!out) return fail(E3_ERR_INVALID_ARG, "out is null");
   if (l1 < 0 || l2 < 0 || L < 0 || l1 > kGenericLmax || l2 > kGenericLmax || L > kGenericLmax)
-    return fail(E3_ERR_INVALID_ARG, "degrees must be in 0..6");
+    return fail(E3_ERR_INVALID_ARG, "degrees must be in 0..7");
   std::vector<double> T;
   if (!e3::cg_real_block(l1, l2, L, T)) return fail(E3_ERR_INVALID_ARG, "triple does not couple");
   for (size_t k = 0; k < T.size(); ++k) out[k] = T[k];
@@ -296,7 +297,7 @@ e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out) {
 
 e3_status e3_spherical_harmonics(int32_t lmax, int64_t n, const float* vec, float* Y,
                                  void* stream) {
-  if (lmax < 0 || lmax > 6) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..6");
+  if (lmax < 0 || lmax > 7) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..7");
   if (n < 0) return fail(E3_ERR_INVALID_ARG, "n < 0");
   if (n == 0) return ok();
   if (!vec || !Y) return fail(E3_ERR_INVALID_ARG, "null pointer");
@@ -341,7 +342,7 @@ e3_status e3_tp_backward(const e3_desc* desc, int64_t n_rows, const void* x, con
 
 e3_status e3_spherical_harmonics_backward(int32_t lmax, int64_t n, const float* vec,
                                           const float* dY, float* dvec, void* stream) {
-  if (lmax < 0 || lmax > 6) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..6");
+  if (lmax < 0 || lmax > 7) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..7");
   if (n < 0) return fail(E3_ERR_INVALID_ARG, "n < 0");
   if (n == 0) return ok();
   if (!vec || !dY || !dvec) return fail(E3_ERR_INVALID_ARG, "null pointer");
@@ -1099,7 +1100,7 @@ e3_status generic_entries(const e3_desc* desc, Parsed& p, std::vector<GenEntry>&
   if (s != E3_OK) return s;
   for (const auto* v : {&p.x, &p.y, &p.o})
     for (const auto& r : *v)
-      if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 6");
+      if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 7");
   if (p.dy >= 65536) return fail(E3_ERR_UNSUPPORTED, "too many y components");
   if (table_limits && (p.dx * 64 + p.dy > 4096 || p.dout * 64 + p.dy > 4096))
     return fail(E3_ERR_UNSUPPORTED,
@@ -1652,7 +1653,7 @@ e3_status generic_parse(const e3_desc* desc, e3_dtype dtype, Parsed& p) {
   if (dtype != E3_F32 && dtype != E3_BF16) return fail(E3_ERR_INVALID_ARG, "unknown dtype");
   for (const auto* v : {&p.x, &p.y, &p.o})
     for (const auto& r : *v)
-      if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 6");
+      if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 7");
   if (p.dx * 64 + p.dy > 4096 || p.dout * 64 + p.dy > 4096)
     return fail(E3_ERR_UNSUPPORTED, "too many components for the generic kernel (dx, dout <= 63)");
   return ok();
@@ -2092,6 +2093,10 @@ e3_status generic_y_source(const e3_desc* desc, const Parsed& p, int& ly, e3k::Y
     ly = std::max(ly, r.l);
     for (int m = 0; m < 2 * r.l + 1; ++m) ym.idx[i++] = static_cast<signed char>(r.l * r.l + m);
   }
+  if (ly > kTableHarmonicsLmax)
+    return fail(E3_ERR_UNSUPPORTED,
+                "the coefficient-table convolution computes harmonics to degree 6; pass Y "
+                "(E3_Y_GIVEN) or use the dense-product form");
   return ok();
 }
 

@@ -228,7 +228,8 @@ __device__ __forceinline__ void edge_bank(int ly, const float* v, float* s_bank)
     case 3: bank_of<3>(v, s_bank); break;
     case 4: bank_of<4>(v, s_bank); break;
     case 5: bank_of<5>(v, s_bank); break;
-    default: bank_of<6>(v, s_bank); break;
+    case 6: bank_of<6>(v, s_bank); break;
+    default: bank_of<7>(v, s_bank); break;  // 64 values: the bank's size
   }
 }
 
@@ -274,7 +275,7 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
     __builtin_memcpy(&wd, cg.ym.idx + 4 * threadIdx.x, 4);
     s_ym[threadIdx.x] = wd;
   }
-  const int nbank = (min(max(cg.ly, 0), 6) + 1) * (min(max(cg.ly, 0), 6) + 1);
+  const int nbank = (min(max(cg.ly, 0), 7) + 1) * (min(max(cg.ly, 0), 7) + 1);
   // y component i of the edge: given, or the bank entry the map names (clamped)
   auto yval = [&](int i) {
     if constexpr (!VEC) return s_y[i];
@@ -772,7 +773,7 @@ hipError_t launch_conv_gemm_pre(const ConvGemmArgs& a, int per_cu, hipStream_t s
 hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
   if (a.n_nodes <= 0) return hipSuccess;
   if (a.t.lds_bytes > 160 * 1024 || a.t.n_blocks > kConvGemmBlocks || a.t.CS > 128 ||
-      a.ly > 6 || (a.ly >= 0 && a.t.dy > 64))
+      a.ly > 7 || (a.ly >= 0 && a.t.dy > 64))
     return hipErrorInvalidValue;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
   // one 16-channel tile per wavefront (slabs of at most 64 channels).  The

@@ -1,6 +1,6 @@
 // Channel-wise tensor product and message-passing convolution for any irreps
-// signature with degrees up to 6, interpreted from a coefficient table
-// instead of compiled per signature.
+// signature with degrees up to 7 (harmonics from edge vectors to 6),
+// interpreted from a coefficient table instead of compiled per signature.
 //
 // e3j describes its tensor product as a generic bilinear coupling driven by
 // a sparse COO array of coefficients (E.1 Eq.10-11, B.1) and runs it to

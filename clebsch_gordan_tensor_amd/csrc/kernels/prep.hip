@@ -659,6 +659,7 @@ hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hip
     case 4: hipLaunchKernelGGL(k_harmonics<4>, g, b, 0, s, n, vec, Y); break;
     case 5: hipLaunchKernelGGL(k_harmonics<5>, g, b, 0, s, n, vec, Y); break;
     case 6: hipLaunchKernelGGL(k_harmonics<6>, g, b, 0, s, n, vec, Y); break;
+    case 7: hipLaunchKernelGGL(k_harmonics<7>, g, b, 0, s, n, vec, Y); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -676,6 +677,7 @@ hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const fl
     case 4: hipLaunchKernelGGL(k_harmonics_grad<4>, g, b, 0, s, n, vec, dY, dvec); break;
     case 5: hipLaunchKernelGGL(k_harmonics_grad<5>, g, b, 0, s, n, vec, dY, dvec); break;
     case 6: hipLaunchKernelGGL(k_harmonics_grad<6>, g, b, 0, s, n, vec, dY, dvec); break;
+    case 7: hipLaunchKernelGGL(k_harmonics_grad<7>, g, b, 0, s, n, vec, dY, dvec); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -144,13 +144,13 @@ e3_status e3_path_info(const e3_desc* desc, int32_t i, int32_t* ix, int32_t* iy,
  * The tensor-product calls accept the same. */
 int32_t e3_supported(const e3_desc* desc, e3_dtype dtype);
 
-/* Real coupling block T[M][m1][m2] of (l1, l2, L), l <= 6, written to the
+/* Real coupling block T[M][m1][m2] of (l1, l2, L), l <= 7, written to the
  * HOST array out[(2L+1)(2l1+1)(2l2+1)] (the blocks the kernels' tables are
  * built from; e3j G.2 construction). */
 e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out);
 
-/* Harmonics Y[n][(lmax+1)^2] of vec[n][3] (e3j A.3 Eq.4), lmax <= 6: degrees
- * 0..3 from their closed forms, 4..6 by the coupling of Y_1 and Y_{L-1}
+/* Harmonics Y[n][(lmax+1)^2] of vec[n][3] (e3j A.3 Eq.4), lmax <= 7: degrees
+ * 0..3 from their closed forms, 4..7 by the coupling of Y_1 and Y_{L-1}
  * (Gaunt relation; recursion records generated and checked at build time). */
 e3_status e3_spherical_harmonics(int32_t lmax, int64_t n, const float* vec, float* Y,
                                  void* stream);
@@ -176,7 +176,7 @@ e3_status e3_tp_backward(const e3_desc* desc, int64_t n_rows, const void* x, con
  * the harmonic cotangent to the edge vector, toward conservative forces,
  * Tessera 2.2 Eq.3):
  *   dvec[i][k] = sum_j dY[i][j] dY_j(vec[i]) / dvec[i][k],
- * dY [n][(lmax+1)^2], vec and dvec [n][3], float32, lmax <= 6.  Since the
+ * dY [n][(lmax+1)^2], vec and dvec [n][3], float32, lmax <= 7.  Since the
  * harmonics depend on the direction only, dvec is orthogonal to vec; a zero
  * vector gets 0.  Feed it the dY of e3_conv_backward. */
 e3_status e3_spherical_harmonics_backward(int32_t lmax, int64_t n, const float* vec,
@@ -322,10 +322,10 @@ e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t 
 
 /* Tensor product (as e3_tp_forward: e3j E.1 Eq.10-11, any channel-wise
  * signature, collapsed or per-path outputs) and its backward (as
- * e3_tp_backward, Eq.14-16) for irreps of degree up to 6, driven by
+ * e3_tp_backward, Eq.14-16) for irreps of degree up to 7, driven by
  * coefficient tables instead of compiled kernels (e3j treats the product as
  * a bilinear coupling given by a sparse COO array of coefficients, E.1 and
- * B.1; Figs 5-6 run it to L = 6 and beyond).
+ * B.1; Figs 5-6 run it to L = 8).
  *   e3_generic_plan_size / e3_generic_plan_build: host-only; write table
  *     `table` for desc into a HOST buffer; the caller copies it to device
  *     memory it owns (16-byte aligned) and may reuse it for every call with
@@ -338,8 +338,8 @@ e3_status e3_radial_mlp_backward(const e3_radial* mlp, int32_t n_edges, int32_t 
  *     writes dx [n][dx][C], dw [n][P][C] and dy [n][dy] (float32, summed
  *     over the channels in a fixed order).
  * fp32 or bf16 storage, fp32 accumulation; no alignment beyond the element
- * size.  Needs every degree <= 6 and dx*64 + dy, dout*64 + dy <= 4096
- * (dx, dout <= 63).  A table built for another descriptor gives wrong
+ * size.  Needs every degree <= 7 and dx*64 + dy, dout*64 + dy <= 4096
+ * (dx, dout <= 63: all irreps 0..L once fit up to L = 6).  A table built for another descriptor gives wrong
  * values but never an out-of-bounds access (every index read from it is
  * clamped). */
 enum {
@@ -358,7 +358,7 @@ e3_status e3_generic_plan_build(const e3_desc* desc, int32_t table, void* host_p
 e3_status e3_tp_forward_generic(const e3_desc* desc, int64_t n_rows, const void* plan,
                                 size_t plan_bytes, const void* x, const float* y, const void* w,
                                 void* z, e3_dtype dtype, void* stream);
-/* The same tensor product forward on the fp32 matrix cores (degrees up to 6,
+/* The same tensor product forward on the fp32 matrix cores (degrees up to 7,
  * float32 only).  e3j E.1 Eq.10-11 contracted per output block as one dense
  * product: A_L[M][(P,m1)] = sum_{m2} C_P[M][m1][m2] y[m2] (per row, shared by
  * the channels) times xt[(P,m1)][q] = w[P][q] x[l1,m1][q], on
@@ -389,7 +389,7 @@ e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_e
                                size_t plan_bytes, const float* edge_vec_or_Y, const float* x,
                                const float* w, float* m, void* stream);
 /* The backward of e3_tp_forward_gemm (e3j E.1 Eq.14-16) as dense products
- * on the fp32 matrix cores, for the same descriptors (degrees up to 6,
+ * on the fp32 matrix cores, for the same descriptors (degrees up to 7,
  * float32, C % 16 == 0): with A_L[M][(P,m1)] = sum_m2 C_P[M][m1][m2] y[m2]
  * per row,
  *   dx   = the forward's product with the roles of x and the output swapped:
@@ -431,15 +431,16 @@ e3_status e3_tp_backward_generic(const e3_desc* desc, int64_t n_rows, const void
                                  float* dy, e3_dtype dtype, void* stream);
 
 /* Convolution forward and backward (as e3_conv_forward / e3_conv_backward:
- * e3j A.3 Eq.7, E.1 Eq.12-16) for irreps of degree up to 6, from the
- * coefficient tables above (e3j B.1 Fig 7 runs the convolution to L = 6).
+ * e3j A.3 Eq.7, E.1 Eq.12-16) for irreps of degree up to 7, from the
+ * coefficient tables above (e3j B.1 Fig 7 runs the convolution to L = 8).
  * The messages of a receiver accumulate in an on-chip buffer over its edge
  * list, as in the shared-memory accumulation of e3j's CUDA convolution
  * (E.1), so m is written once per node and the sum is reproducible.
  *   m[b]  = sum_{e in row b} sum_P w[e][P] (x[sender e] (x) Y_e)_P
  *   dx[a] = sum over out-edges of a (sender-ordered index), dw[e], dY[e]
  * edge_vec_or_Y: edge vectors [E][3] (the harmonics of every y irrep are
- * computed from them: needs dy <= 64) or, with E3_Y_GIVEN, Y [E][dy].
+ * computed from them: needs dy <= 64 and degrees <= 6) or, with E3_Y_GIVEN,
+ * Y [E][dy].
  * Forward: table E3_GEN_FORWARD; workspace optional (its node order, as
  * e3_conv_forward).  Backward: tables E3_GEN_DX, E3_GEN_DW, E3_GEN_DY;
  * workspace from e3_conv_prepare_transpose on the same graph (required);
@@ -461,7 +462,7 @@ e3_status e3_conv_backward_generic(const e3_desc* desc, int32_t n_nodes, int32_t
                                    void* stream);
 
 /* Double backward (as e3_conv_double_backward, e3j E.1 Eq.17-18, given
- * harmonics: desc needs E3_Y_GIVEN) for degrees up to 6, composed from the
+ * harmonics: desc needs E3_Y_GIVEN) for degrees up to 7, composed from the
  * generic forward and backward with all four tables; scratch as
  * e3_conv_double_backward_scratch_size gives for desc. */
 e3_status e3_conv_double_backward_generic(

@@ -131,7 +131,7 @@ def test_error_codes(lib):
                                None) == -1  # unknown dtype
     assert lib.e3_tp_forward(_desc_c(good), 0, None, None, None, None, 0, None) == 0
     assert lib.e3_tp_forward(_desc_c(good), -2, None, None, None, None, 0, None) == -1
-    assert lib.e3_spherical_harmonics(7, 10, fake, fake, None) == -1
+    assert lib.e3_spherical_harmonics(8, 10, fake, fake, None) == -1
     assert lib.e3_spherical_harmonics(2, 0, None, None, None) == 0
     sz = C.c_size_t()
     assert lib.e3_conv_workspace_size(10, 100, C.byref(sz)) == 0
@@ -156,7 +156,7 @@ def test_error_codes(lib):
                               None) == -4
     assert lib.e3_tp_backward(_desc_c(uns), 5, fake, fake, fake, fake, fake, fake, fake, 0,
                               None) == -3
-    assert lib.e3_spherical_harmonics_backward(7, 10, fake, fake, fake, None) == -1
+    assert lib.e3_spherical_harmonics_backward(8, 10, fake, fake, fake, None) == -1
     assert lib.e3_spherical_harmonics_backward(3, -1, fake, fake, fake, None) == -1
     assert lib.e3_spherical_harmonics_backward(3, 10, fake, None, fake, None) == -1
     assert lib.e3_spherical_harmonics_backward(3, 0, None, None, None, None) == 0
@@ -228,7 +228,7 @@ def test_error_codes(lib):
     assert rb(fake, rneed, None) == -1
     out = np.zeros(10)
     assert lib.e3_cg_block(1, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
-    assert lib.e3_cg_block(7, 1, 6, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
+    assert lib.e3_cg_block(8, 1, 7, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
 
 
 def test_generic_plan_table(lib):
@@ -320,7 +320,12 @@ def test_generic_plan_table(lib):
     wide = api.Desc([(4, 1), (4, 1), (4, 1)], [(l, 1) for l in range(7)] * 2, [(4, 1)], 8)
     assert lib.e3_conv_forward_generic(C.byref(wide.c()), 4, 8, fk, fk, None, 0, fk, 4096, fk,
                                        fk, fk, fk, 0, None) == -3  # dy > 64 from edge vectors
-    big = api.Desc([(7, 1)], [(0, 1)], [(7, 1)], 64)
+    # the coefficient-table convolution forms harmonics to degree 6 only
+    y7 = api.Desc([(0, 1)], [(7, -1)], [(7, -1)], 8)
+    assert lib.e3_conv_forward_generic(C.byref(y7.c()), 4, 8, fk, fk, None, 0, fk, 4096, fk,
+                                       fk, fk, fk, 0, None) == -3
+    assert "degree 6" in lib.e3_last_error().decode()
+    big = api.Desc([(8, 1)], [(0, 1)], [(8, 1)], 64)
     assert lib.e3_generic_plan_size(C.byref(big.c()), 0, C.byref(nb)) == -3
     assert lib.e3_tp_forward_generic(C.byref(d.c()), 0, None, 0, None, None, None, None, 0,
                                      None) == 0

@@ -2,7 +2,7 @@
 (tables E3_GEN_GEMM, E3_GEN_GEMM_DX, E3_GEN_GEMM_DW, E3_GEN_GEMM_DY): a numpy
 reading of each plan, doing what the matrix-core kernels do with it (A built
 per row from y, one product per block over its K list), against the fp64
-oracle's tensor product and its backward, at degrees 1-6 with natural and
+oracle's tensor product and its backward, at degrees 1-7 with natural and
 skew parities, collapsed and per-path outputs, and an output irrep no path
 reaches.  These pin the host logic; the GPU tests pin the kernels."""
 import ctypes as C
@@ -133,7 +133,8 @@ def _case(L, skew=False, per_path=False, out=None, C=4, B=5, seed=0):
 
 
 CASES = [(1, False, False), (2, False, False), (3, True, False), (4, False, False),
-         (5, False, True), (6, False, False), (6, True, False)]
+         (5, False, True), (6, False, False), (6, True, False), (7, False, False),
+         (7, True, False)]
 
 
 @pytest.mark.parametrize("L,skew,pp", CASES)

@@ -48,7 +48,7 @@ def _case(L, C, B, seed, skew=False, per_path=False):
 
 
 @pytest.mark.parametrize("L,skew", [(1, False), (2, False), (3, False), (4, False), (5, False),
-                                    (6, False), (6, True)])
+                                    (6, False), (6, True), (7, False), (7, True)])
 def test_gemm_tp_matches_oracle(gpu, L, skew):
     d, od, x, y, w = _case(L, 128, 97, 500 + L, skew)
     z = host(gpu.tp_forward_gemm(d, dev(x), dev(y), dev(w)))
@@ -118,7 +118,8 @@ def _conv_problem(L, C, n, seed, pad=0, skew=False):
 
 
 @pytest.mark.parametrize("L,C,skew", [(1, 64, False), (3, 128, False), (4, 64, False),
-                                      (6, 128, False), (6, 48, True)])
+                                      (6, 128, False), (6, 48, True), (7, 128, False),
+                                      (7, 32, True)])
 def test_gemm_conv_matches_oracle(gpu, L, C, skew):
     d, od, g, x, w, Y = _conv_problem(L, C, 40 if L >= 5 else 64, 600 + L, skew=skew)
     rowptr, sender = dev(g.rowptr), dev(g.sender)
@@ -150,7 +151,7 @@ def test_gemm_conv_equals_table_kernel(gpu):
     assert_close(host(a), host(b).astype(np.float64), 2 * TOL_F32, "gemm conv vs table kernel")
 
 
-@pytest.mark.parametrize("L", [2, 6])
+@pytest.mark.parametrize("L", [2, 6, 7])
 def test_gemm_conv_from_edge_vectors(gpu, L):
     # the harmonics computed per edge from the vectors, against the oracle
     from clebsch_gordan_tensor_amd import api

@@ -154,25 +154,26 @@ def test_generic_tp_backward_equals_compiled_kernel(gpu):
         assert_close(host(u), host(v).astype(np.float64), 2 * TOL_F32, f"generic vs compiled:{k}")
 
 
-# ---------------------------------------------------- harmonics up to degree 6
+# ---------------------------------------------------- harmonics up to degree 7
 
-def test_harmonics_to_degree_six_match_oracle(gpu):
-    # the library builds degrees 4..6 by coupling Y_1 with Y_{L-1} (Gaunt
+@pytest.mark.parametrize("lmax", [6, 7])
+def test_harmonics_to_high_degree_match_oracle(gpu, lmax):
+    # the library builds degrees 4..7 by coupling Y_1 with Y_{L-1} (Gaunt
     # relation); the oracle by the Legendre construction
     rng = np.random.default_rng(390)
     v = (rng.standard_normal((5001, 3)) * rng.uniform(0.1, 10, (5001, 1))).astype(np.float32)
     v[7] = 0.0
     v[8] = [0.0, 0.0, 3.0]
-    Y = host(gpu.spherical_harmonics(6, dev(v)))
-    ref = O.sh(6, v)
-    for l in range(7):
+    Y = host(gpu.spherical_harmonics(lmax, dev(v)))
+    ref = O.sh(lmax, v)
+    for l in range(lmax + 1):
         sl = slice(l * l, (l + 1) * (l + 1))
         assert_close(Y[:, sl], ref[:, sl], TOL_F32, f"harmonics l={l}")
     assert np.all(Y[7, 1:] == 0.0) and Y[7, 0] == 1.0
 
 
-@pytest.mark.parametrize("lmax", [4, 6])
-def test_harmonics_gradient_to_degree_six(gpu, lmax):
+@pytest.mark.parametrize("lmax", [4, 6, 7])
+def test_harmonics_gradient_to_high_degree(gpu, lmax):
     # the vector gradient through the coupling recursion, against the
     # fourth-order differences of the oracle's harmonics
     rng = np.random.default_rng(391 + lmax)
