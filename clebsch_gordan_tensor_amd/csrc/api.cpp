@@ -32,7 +32,7 @@ e3_status ok() {
   return E3_OK;
 }
 
-constexpr int kGenericLmax = 7;  // coefficient tables of the generic tensor product
+constexpr int kGenericLmax = 8;  // coefficient tables of the generic tensor product
 constexpr int kTableHarmonicsLmax = 6;  // harmonics the coefficient-table kernels compute
 
 e3_status check_graph_host(int32_t n_nodes, int32_t n_edges, const int32_t* rp,
@@ -288,7 +288,7 @@ int32_t e3_supported(const e3_desc* desc, e3_dtype dtype) {
 e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out) {
   if (!out) return fail(E3_ERR_INVALID_ARG, "out is null");
   if (l1 < 0 || l2 < 0 || L < 0 || l1 > kGenericLmax || l2 > kGenericLmax || L > kGenericLmax)
-    return fail(E3_ERR_INVALID_ARG, "degrees must be in 0..7");
+    return fail(E3_ERR_INVALID_ARG, "degrees must be in 0..8");
   std::vector<double> T;
   if (!e3::cg_real_block(l1, l2, L, T)) return fail(E3_ERR_INVALID_ARG, "triple does not couple");
   for (size_t k = 0; k < T.size(); ++k) out[k] = T[k];
@@ -297,7 +297,7 @@ e3_status e3_cg_block(int32_t l1, int32_t l2, int32_t L, double* out) {
 
 e3_status e3_spherical_harmonics(int32_t lmax, int64_t n, const float* vec, float* Y,
                                  void* stream) {
-  if (lmax < 0 || lmax > 7) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..7");
+  if (lmax < 0 || lmax > 8) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..8");
   if (n < 0) return fail(E3_ERR_INVALID_ARG, "n < 0");
   if (n == 0) return ok();
   if (!vec || !Y) return fail(E3_ERR_INVALID_ARG, "null pointer");
@@ -342,7 +342,7 @@ e3_status e3_tp_backward(const e3_desc* desc, int64_t n_rows, const void* x, con
 
 e3_status e3_spherical_harmonics_backward(int32_t lmax, int64_t n, const float* vec,
                                           const float* dY, float* dvec, void* stream) {
-  if (lmax < 0 || lmax > 7) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..7");
+  if (lmax < 0 || lmax > 8) return fail(E3_ERR_INVALID_ARG, "lmax must be in 0..8");
   if (n < 0) return fail(E3_ERR_INVALID_ARG, "n < 0");
   if (n == 0) return ok();
   if (!vec || !dY || !dvec) return fail(E3_ERR_INVALID_ARG, "null pointer");
@@ -1100,7 +1100,7 @@ e3_status generic_entries(const e3_desc* desc, Parsed& p, std::vector<GenEntry>&
   if (s != E3_OK) return s;
   for (const auto* v : {&p.x, &p.y, &p.o})
     for (const auto& r : *v)
-      if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 7");
+      if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 8");
   if (p.dy >= 65536) return fail(E3_ERR_UNSUPPORTED, "too many y components");
   if (table_limits && (p.dx * 64 + p.dy > 4096 || p.dout * 64 + p.dy > 4096))
     return fail(E3_ERR_UNSUPPORTED,
@@ -1267,7 +1267,7 @@ e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& o
   };
   auto out_comp = [&](const GenEntry& e) { return kind == 1 ? e.xi : e.o; };
   auto in_comp = [&](const GenEntry& e) { return kind == 1 ? e.o : e.xi; };
-  std::vector<int> b_oo(nb), b_rows(nb), b_kb(nb), b_K(nb), b_abase(nb);
+  std::vector<int> b_oo(nb), b_rows(nb), b_kb(nb), b_K(nb);
   for (int b = 0; b < nb; ++b) {
     if (per_path_blocks) {
       b_oo[b] = oo_path[b];
@@ -1284,9 +1284,7 @@ e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& o
   std::vector<std::vector<int>> bpaths(nb);
   for (int pi = 0; pi < p.P; ++pi) bpaths[block_of(pi)].push_back(pi);
   std::vector<int32_t> klist;
-  int abase = 0;
   for (int b = 0; b < nb; ++b) {
-    if (b_rows[b] > 16) return fail(E3_ERR_UNSUPPORTED, "output degree above 7");
     b_kb[b] = int(klist.size());
     int k = 0;
     for (int pi : bpaths[b]) {
@@ -1296,8 +1294,24 @@ e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& o
     }
     while (k % 4) klist.push_back(-1), ++k;
     b_K[b] = k;
-    b_abase[b] = abase;
-    abase += b_rows[b] * k;
+  }
+  // The matrix cores' products have 16 rows: a block of more rows (degree
+  // 8: 17) is emitted as blocks of at most 16 rows sharing its K list, each
+  // with its own part of A.
+  struct Sub {
+    int oo, rows, kb, K, abase;
+  };
+  std::vector<Sub> subs;
+  std::vector<int> b_sub0(nb);
+  int abase = 0;
+  for (int b = 0; b < nb; ++b) {
+    if (b_rows[b] > 64) return fail(E3_ERR_UNSUPPORTED, "an irrep of more than 64 components");
+    b_sub0[b] = int(subs.size());
+    for (int r0 = 0; r0 < b_rows[b]; r0 += 16) {
+      const int rows = std::min(16, b_rows[b] - r0);
+      subs.push_back(Sub{b_oo[b] + r0, rows, b_kb[b], b_K[b], abase});
+      abase += rows * b_K[b];
+    }
   }
   std::vector<AGroupTerm> ge;
   ge.reserve(ent.size());
@@ -1305,15 +1319,17 @@ e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& o
     const int b = block_of(e.P);
     const int M = out_comp(e) - b_oo[b];
     const int k = path_koff[e.P] + (in_comp(e) - in_off(e.P));
-    ge.push_back(AGroupTerm{b_abase[b] + k * b_rows[b] + M, e.yi, e.c});  // A[k][M]
+    const Sub& sb = subs[size_t(b_sub0[b] + M / 16)];
+    ge.push_back(AGroupTerm{sb.abase + k * sb.rows + M % 16, e.yi, e.c});  // A[k][M]
   }
+  const int nsub = int(subs.size());
   std::vector<int32_t> groups;
   if ((s = a_groups(ge, groups)) != E3_OK) return s;
   const int n_groups = int(groups.size() / 4);
   // the kernel's view: input components (dx), output components (dout)
   const int in_dim = kind == 1 ? p.dout : p.dx, out_dim = kind == 1 ? p.dx : p.dout;
   d = e3k::TpGemmArgs{};
-  d.n_blocks = nb;
+  d.n_blocks = nsub;
   d.dx = in_dim;
   d.dy = p.dy;
   d.dout = out_dim;
@@ -1322,20 +1338,20 @@ e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& o
   d.n_groups = n_groups;
   d.a_floats = std::max(abase, 1);
   d.off_blocks = e3k::kGemmHeader;
-  d.off_klist = d.off_blocks + 4 * nb;
+  d.off_klist = d.off_blocks + 4 * nsub;
   d.off_groups = (d.off_klist + d.n_klist + 3) / 4 * 4;  // 16-byte entries
   d.plan_words = d.off_groups + int(groups.size());
   out.assign(size_t(d.plan_words), 0);
-  const int32_t head[14] = {e3k::kGemmMagic + kind, nb,      in_dim,       p.dy,
+  const int32_t head[14] = {e3k::kGemmMagic + kind, nsub,    in_dim,       p.dy,
                             out_dim,           p.P,          d.n_klist,    n_groups,
                             0,                 d.a_floats,   d.off_blocks, d.off_klist,
                             d.off_groups,      d.plan_words};
   std::copy(head, head + 14, out.begin());
-  for (int b = 0; b < nb; ++b) {
-    out[d.off_blocks + 4 * b] = b_oo[b];
-    out[d.off_blocks + 4 * b + 1] = b_rows[b];
-    out[d.off_blocks + 4 * b + 2] = b_kb[b];
-    out[d.off_blocks + 4 * b + 3] = b_K[b];
+  for (int b = 0; b < nsub; ++b) {
+    out[d.off_blocks + 4 * b] = subs[size_t(b)].oo;
+    out[d.off_blocks + 4 * b + 1] = subs[size_t(b)].rows;
+    out[d.off_blocks + 4 * b + 2] = subs[size_t(b)].kb;
+    out[d.off_blocks + 4 * b + 3] = subs[size_t(b)].K;
   }
   std::copy(klist.begin(), klist.end(), out.begin() + d.off_klist);
   std::copy(groups.begin(), groups.end(), out.begin() + d.off_groups);
@@ -1385,7 +1401,8 @@ e3_status build_gemm_dw(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpG
   for (int pi = 1; pi < p.P; ++pi)
     if (p.pix[pi] < p.pix[pi - 1]) return fail(E3_ERR_UNSUPPORTED, "paths not grouped by x irrep");
   std::vector<int32_t> blocks, klist, rowtab;
-  std::vector<int> tile_base;
+  std::vector<int> block_base;
+  std::vector<std::vector<int>> tile_blocks;  // per tile: its block for each K chunk
   std::vector<std::vector<std::pair<int, int>>> path_rows(p.P);  // (P, M) -> tile, row
   for (int pi = 0; pi < p.P; ++pi) path_rows[pi].resize(size_t(2 * p.o[p.pio[pi]].l + 1));
   int abase = 0;
@@ -1393,9 +1410,16 @@ e3_status build_gemm_dw(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpG
     int pb = pa;
     while (pb < p.P && p.pix[pb] == p.pix[pa]) ++pb;
     const int l1 = p.x[p.pix[pa]].l, width = 2 * l1 + 1;
-    if (width > 16) return fail(E3_ERR_UNSUPPORTED, "x degree above 7");
-    const int kb = int(klist.size()), K = (width + 3) / 4 * 4;
-    for (int m = 0; m < K; ++m) klist.push_back(m < width ? xoff[p.pix[pa]] + m : -1);
+    if (width > 64) return fail(E3_ERR_UNSUPPORTED, "an x irrep of more than 64 components");
+    // K chunks of at most 16 components (degree 8: 16 + 1), each a K list
+    // of its own: a tile is one block per chunk, consecutive, so the
+    // chunks' partial products join the same path group's sums
+    std::vector<std::pair<int, int>> chunks;  // (K list start, K)
+    for (int c0 = 0; c0 < width; c0 += 16) {
+      const int n = std::min(16, width - c0), K = (n + 3) / 4 * 4;
+      chunks.push_back({int(klist.size()), K});
+      for (int m = 0; m < K; ++m) klist.push_back(m < n ? xoff[p.pix[pa]] + c0 + m : -1);
+    }
     // quads: each path's rows (P, M) in runs of four, the last one padded
     struct Quad {
       int P, M0, n;
@@ -1410,11 +1434,12 @@ e3_status build_gemm_dw(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpG
       const int t = quads[q0].P / 16;
       int n = 0;
       while (n < 4 && q0 + n < quads.size() && quads[q0 + n].P / 16 == t) ++n;
-      const int tile = int(blocks.size() / 4);
+      const int tile = int(tile_blocks.size());
+      std::vector<int32_t> rt;
       for (int j = 0; j < 4; ++j) {
         for (int i = 0; i < 4; ++i) {
           if (j >= n) {
-            rowtab.push_back(16);  // no path, the zero row
+            rt.push_back(16);  // no path, the zero row
             continue;
           }
           const Quad& qd = quads[q0 + j];
@@ -1422,15 +1447,20 @@ e3_status build_gemm_dw(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpG
           if (i < qd.n) {
             const int M = qd.M0 + i;
             path_rows[qd.P][M] = {tile, 4 * j + i};
-            rowtab.push_back(rel | ((oo_path[qd.P] + M + 1) << 10));
+            rt.push_back(rel | ((oo_path[qd.P] + M + 1) << 10));
           } else {
-            rowtab.push_back(rel);
+            rt.push_back(rel);
           }
         }
       }
-      tile_base.push_back(abase);
-      blocks.insert(blocks.end(), {t, 4 * n, kb, K});
-      abase += 16 * K;
+      tile_blocks.emplace_back();
+      for (const auto& [kb, K] : chunks) {
+        tile_blocks.back().push_back(int(blocks.size() / 4));
+        block_base.push_back(abase);
+        blocks.insert(blocks.end(), {t, 4 * n, kb, K});
+        rowtab.insert(rowtab.end(), rt.begin(), rt.end());
+        abase += 16 * K;
+      }
       q0 += size_t(n);
     }
     pa = pb;
@@ -1441,7 +1471,8 @@ e3_status build_gemm_dw(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpG
   for (const GenEntry& e : ent) {
     const auto [tile, r] = path_rows[e.P][size_t(e.o - oo_path[e.P])];
     const int k = e.xi - xoff[p.pix[e.P]];
-    ge.push_back(AGroupTerm{tile_base[tile] + k * 16 + r, e.yi, e.c});
+    const int blk = tile_blocks[size_t(tile)][size_t(k / 16)];
+    ge.push_back(AGroupTerm{block_base[size_t(blk)] + (k % 16) * 16 + r, e.yi, e.c});
   }
   std::vector<int32_t> groups;
   if ((s = a_groups(ge, groups)) != E3_OK) return s;
@@ -1505,20 +1536,25 @@ e3_status build_gemm_dy(const e3_desc* desc, std::vector<int32_t>& out, int* dim
   const int zrow0 = p.dx + p.P;  // slab row of dz component 0
   auto x_keyed = [&](int pi) { return p.per_path || p.x[p.pix[pi]].l >= p.o[p.pio[pi]].l; };
   std::vector<int32_t> blocks, rows;
-  std::vector<int> path_row(p.P);
+  // path_row[c][pi]: first G row of path pi in its block's column chunk c
+  // (16 columns per chunk: a block of more columns, degree 8, repeats its
+  // rows once per chunk)
+  std::vector<std::vector<int>> path_row(4, std::vector<int>(p.P));
   auto add_block = [&](int col_row, int ncols, auto&& member, auto&& own_row, auto&& n_own) {
     bool any = false;
     for (int pi = 0; pi < p.P; ++pi) any = any || member(pi);
     if (!any) return true;
-    if (ncols > 16) return false;
-    const int r0 = int(rows.size());
-    for (int pi = 0; pi < p.P; ++pi) {
-      if (!member(pi)) continue;
-      path_row[pi] = int(rows.size());
-      for (int i = 0; i < n_own(pi); ++i) rows.push_back(pi | own_row(pi, i) << 16);
+    if (ncols > 64) return false;
+    for (int c0 = 0, c = 0; c0 < ncols; c0 += 16, ++c) {
+      const int r0 = int(rows.size());
+      for (int pi = 0; pi < p.P; ++pi) {
+        if (!member(pi)) continue;
+        path_row[size_t(c)][pi] = int(rows.size());
+        for (int i = 0; i < n_own(pi); ++i) rows.push_back(pi | own_row(pi, i) << 16);
+      }
+      while ((rows.size() - r0) % 16) rows.push_back(-1);
+      blocks.insert(blocks.end(), {col_row + c0, std::min(16, ncols - c0), r0, int(rows.size()) - r0});
     }
-    while ((rows.size() - r0) % 16) rows.push_back(-1);
-    blocks.insert(blocks.end(), {col_row, ncols, r0, int(rows.size()) - r0});
     return true;
   };
   for (size_t i = 0; i < p.x.size(); ++i)
@@ -1527,19 +1563,20 @@ e3_status build_gemm_dy(const e3_desc* desc, std::vector<int32_t>& out, int* dim
             [&](int pi) { return p.pix[pi] == int(i) && x_keyed(pi); },
             [&](int pi, int M) { return zrow0 + oo_path[pi] + M; },
             [&](int pi) { return 2 * p.o[p.pio[pi]].l + 1; }))
-      return fail(E3_ERR_UNSUPPORTED, "x degree above 7");
+      return fail(E3_ERR_UNSUPPORTED, "an x irrep of more than 64 components");
   for (size_t k = 0; k < p.o.size(); ++k)
     if (!add_block(
             zrow0 + ooff[k], 2 * p.o[k].l + 1,
             [&](int pi) { return p.pio[pi] == int(k) && !x_keyed(pi); },
             [&](int pi, int m1) { return xoff[p.pix[pi]] + m1; },
             [&](int pi) { return 2 * p.x[p.pix[pi]].l + 1; }))
-      return fail(E3_ERR_UNSUPPORTED, "output degree above 7");
+      return fail(E3_ERR_UNSUPPORTED, "an output irrep of more than 64 components");
   const int nb = int(blocks.size() / 4);
   std::vector<std::vector<std::pair<int, float>>> by_y(p.dy);
   for (const GenEntry& e : ent) {
     const int M = e.o - oo_path[e.P], m1 = e.xi - xoff[p.pix[e.P]];
-    const int gi = x_keyed(e.P) ? (path_row[e.P] + M) * 16 + m1 : (path_row[e.P] + m1) * 16 + M;
+    const int gi = x_keyed(e.P) ? (path_row[size_t(m1 / 16)][e.P] + M) * 16 + m1 % 16
+                                : (path_row[size_t(M / 16)][e.P] + m1) * 16 + M % 16;
     by_y[e.yi].push_back({gi, e.c});
   }
   const int off_blocks = e3k::kGemmHeader, off_rows = off_blocks + 4 * nb;
@@ -1653,7 +1690,7 @@ e3_status generic_parse(const e3_desc* desc, e3_dtype dtype, Parsed& p) {
   if (dtype != E3_F32 && dtype != E3_BF16) return fail(E3_ERR_INVALID_ARG, "unknown dtype");
   for (const auto* v : {&p.x, &p.y, &p.o})
     for (const auto& r : *v)
-      if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 7");
+      if (r.l > kGenericLmax) return fail(E3_ERR_UNSUPPORTED, "generic tables go to degree 8");
   if (p.dx * 64 + p.dy > 4096 || p.dout * 64 + p.dy > 4096)
     return fail(E3_ERR_UNSUPPORTED, "too many components for the generic kernel (dx, dout <= 63)");
   return ok();
@@ -1827,11 +1864,25 @@ e3_status gemm_backward_setup(const e3_desc* desc, const Parsed& p, const void* 
   bdy.off_rows = dd.off_rows;
   bdy.off_yptr = dd.off_yptr;
   bdy.off_yent = dd.off_yent;
+  bdy.g_rows = std::max(16, dd.n_grows);  // all of G at once if it fits
   bdy.t.CS = pick_slab(p.C, [&](int cs) {
     e3k::GemmBwdArgs t = bdy;
     t.t.CS = cs;
     return e3k::gemm_dy_lds_bytes(t);
   });
+  if (!bdy.t.CS && p.C % 16 == 0) {
+    // 16-channel slabs and G in groups of as many rows as fit (degree 8):
+    // the slabs are staged once per group
+    e3k::GemmBwdArgs t = bdy;
+    t.t.CS = 16;
+    t.g_rows = 16;
+    const long fixed = long(e3k::gemm_dy_lds_bytes(t)) - 16 * 16 * 4;
+    const long rows = (long(160) * 1024 - fixed) / (16 * 4) / 16 * 16;
+    if (rows >= 16) {
+      bdy.t.CS = 16;
+      bdy.g_rows = int(std::max<long>(16, std::min<long>(rows, dd.n_grows)));
+    }
+  }
   if (!tdx.CS || !bdw.t.CS || !bdy.t.CS)
     return fail(E3_ERR_UNSUPPORTED, "a dense-product backward plan does not fit in LDS");
   const int XS = e3k::gemm_row_stride(std::max(tdx.CS, bdw.t.CS));
@@ -1912,7 +1963,8 @@ e3_status e3_conv_backward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_
   if ((s = gemm_backward_setup(desc, p, plan_dx, dx_bytes, plan_dw, dw_bytes, plan_dy, dy_bytes,
                                tdx, bdw, bdy)) != E3_OK)
     return s;
-  if (tdx.n_blocks > 8) return fail(E3_ERR_UNSUPPORTED, "more than 8 x irreps");
+  if (tdx.n_blocks > e3k::kConvGemmMaxBlocks)
+    return fail(E3_ERR_UNSUPPORTED, "more than 10 x blocks (x irreps, degree 8 counting twice)");
   if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");
   if (n_nodes == 0) return ok();
   if ((s = maybe_check(desc, n_nodes, n_edges, rowptr, sender, stream)) != E3_OK) return s;
@@ -1982,7 +2034,9 @@ e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_e
   e3k::ConvGemmArgs a{};
   size_t need = 0;
   if ((s = gemm_dims(desc, a.t, need)) != E3_OK) return s;
-  if (a.t.n_blocks > 8) return fail(E3_ERR_UNSUPPORTED, "more than 8 output irreps");
+  if (a.t.n_blocks > e3k::kConvGemmMaxBlocks)
+    return fail(E3_ERR_UNSUPPORTED,
+                "more than 10 output blocks (output irreps, degree 8 counting twice)");
   // the y operand: given rows, or the harmonics of the edge vectors (one bank
   // per y irrep, y component -> harmonic l*l + m)
   a.ly = -1;
@@ -1996,6 +2050,9 @@ e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_e
       a.ly = std::max(a.ly, r.l);
       for (int m = 0; m < 2 * r.l + 1; ++m) a.ym.idx[i++] = static_cast<signed char>(r.l * r.l + m);
     }
+    if (a.ly > 7)  // the per-edge bank holds degrees 0..7 (64 values)
+      return fail(E3_ERR_UNSUPPORTED,
+                  "harmonics from edge vectors go to degree 7 here; use E3_Y_GIVEN");
   }
   if (p.C % 16) return fail(E3_ERR_UNSUPPORTED, "the dense-product kernel needs C % 16 == 0");
   if (n_nodes < 0 || n_edges < 0) return fail(E3_ERR_INVALID_ARG, "negative size");

@@ -79,7 +79,7 @@ int main(int argc, char** argv) {
   // one vector is kappa_L Y_L (the Gaunt relation), with
   // kappa_L = sqrt(3 (2L-1) / (2L+1)) <1 0 L-1 0 | L 0>.  Records of the real
   // (1, L-1, L) blocks and 1/kappa_L; checked below on random directions.
-  constexpr int SL = 7;
+  constexpr int SL = 8;
   std::vector<R> srec;
   int soff[SL + 1] = {0}, scnt[SL + 1] = {0};
   double inv_kappa[SL + 1] = {0};

@@ -238,13 +238,14 @@ __device__ __forceinline__ void edge_bank(int ly, const float* v, float* s_bank)
 // with xt_e[(P,m1)][q] = w[e][P][q] x[sender e][l1,m1][q].  One workgroup per
 // (receiver, channel slab); per edge the slab of x[sender] and w[e] and Y[e]
 // are staged and A_e built as for one tensor-product row, and every output
-// block's tiles accumulate in registers over the edge list (at most 8 blocks:
-// collapsed outputs), so m is written once per receiver in edge order.
-// PRE as above, for the next edge of the same receiver (built with PRE = 0).
-constexpr int kConvGemmBlocks = 8;
-
-template <int PRE, int NU, bool BATCH, bool VEC>
+// block's tiles accumulate in registers over the edge list (at most NB
+// blocks: collapsed outputs), so m is written once per receiver in edge
+// order.  PRE as above, for the next edge of the same receiver (built with
+// PRE = 0).  NB is 8, or kConvGemmMaxBlocks for plans of more blocks (the
+// smaller form keeps the registers of the common case).
+template <int PRE, int NU, bool BATCH, bool VEC, int NB>
 __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
+  constexpr int kConvGemmBlocks = NB;
   extern __shared__ __align__(16) float gsm[];
   const TpGemmArgs& g = cg.t;
   const int* __restrict__ blocks = g.plan + g.off_blocks;
@@ -630,9 +631,12 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
   float* s_x = gsm;
   float* s_w = s_x + g.dx * XS;
   float* s_z = s_w + g.P * XS;
-  float* s_g = s_z + g.dout * XS;                          // G [n_grows][16]
-  int* s_r = reinterpret_cast<int*>(s_g + a.n_grows * 16);  // per G row: w row | own row << 16
+  // G rows in groups of g_rows (all of them at once when they fit)
+  const int GR = min(max(a.g_rows, 16), a.n_grows) & ~15;
+  float* s_g = s_z + g.dout * XS;                     // G [GR][16]: rows [gr0, gr0 + GR)
+  int* s_r = reinterpret_cast<int*>(s_g + GR * 16);   // per G row: w row | own row << 16
   int* s_b = s_r + a.n_grows;  // per G row: its block's first column row | columns << 16
+  float* s_dy = reinterpret_cast<float*>(s_b + a.n_grows);  // dy of the groups so far
   const int n_srows = g.dx + g.P + g.dout;  // slab rows: x, w, dz
   for (int i = threadIdx.x; i < a.n_grows; i += NT) {
     const int ent = grows[i];
@@ -661,7 +665,11 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
       continue;
     }
     const int64_t zr = a.rowptr ? receiver_of(a.rowptr, a.n_zrows, row) : row;
-    for (int i = threadIdx.x; i < a.n_grows * 16; i += NT) s_g[i] = 0.0f;
+    // (one pass when there are no G rows: dy is then written as zeros)
+    for (int gr0 = 0; gr0 == 0 || gr0 < a.n_grows; gr0 += max(GR, 16)) {
+    const int tg0 = gr0 / 16, tg1 = min(n_gt, (gr0 + GR) / 16);  // this group's tiles
+    __syncthreads();  // the previous group's reads of G are done
+    for (int i = threadIdx.x; i < GR * 16; i += NT) s_g[i] = 0.0f;
     for (int sl = 0; sl < n_slabs; ++sl) {
       const int c0 = sl * CS;
       __syncthreads();  // the previous slab's LDS reads are done (and s_g is cleared)
@@ -678,21 +686,21 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
       __syncthreads();
       // two tiles at a time (independent accumulators), four K steps per
       // batch with their LDS reads issued first
-      for (int t0 = 2 * wave; t0 < n_gt; t0 += 2 * NW) {
+      for (int t0 = tg0 + 2 * wave; t0 < tg1; t0 += 2 * NW) {
         const float* wp[2];
         const float* zp[2];
         const float* xp[2];
         bool aok[2], bok[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int t = min(t0 + h, n_gt - 1);
+          const int t = min(t0 + h, tg1 - 1);
           const int ro = s_r[16 * t + li];
           const int bx = s_b[16 * t];  // column block of the tile (uniform)
           const int xo = bx & 0xFFFF, nc = bx >> 16;
           wp[h] = s_w + (ro < 0 ? 0 : ro & 0xFFFF) * XS + kq;
           zp[h] = s_x + (ro < 0 ? 0 : ro >> 16) * XS + kq;
           xp[h] = s_x + min(xo + min(li, max(nc - 1, 0)), n_srows - 1) * XS + kq;
-          aok[h] = ro >= 0 && t0 + h < n_gt;
+          aok[h] = ro >= 0 && t0 + h < tg1;
           bok[h] = li < nc;
         }
         float4v D[2] = {float4v{0.0f, 0.0f, 0.0f, 0.0f}, float4v{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -716,24 +724,34 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
         // D[h][r]: G row 16 t + 4 kq + r, column li
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          if (t0 + h < n_gt)
+          if (t0 + h < tg1)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s_g[(16 * (t0 + h) + 4 * kq + r) * 16 + li] += D[h][r];
+            for (int r = 0; r < 4; ++r)
+              s_g[(16 * (t0 + h) - gr0 + 4 * kq + r) * 16 + li] += D[h][r];
       }
     }
     __syncthreads();
-    // dy[y]: a wavefront per component, its entries strided over the lanes,
-    // then the fixed-order wavefront sum
+    // dy[y]: a wavefront per component, its entries (those in this group's
+    // G rows) strided over the lanes, then the fixed-order wavefront sum,
+    // added to the earlier groups' in group order
+    const bool last = gr0 + GR >= a.n_grows;
     for (int y = wave; y < g.dy; y += NW) {
       float acc = 0.0f;
       const int k0 = max(yptr[y], 0), k1 = min(yptr[y + 1], a.n_ent);
       for (int k = k0 + lane; k < k1; k += 64) {
-        const int gi = min(max(yent[2 * k], 0), a.n_grows * 16 - 1);
-        acc = fmaf(__int_as_float(yent[2 * k + 1]), s_g[gi], acc);
+        const int gi = min(max(yent[2 * k], 0), a.n_grows * 16 - 1) - gr0 * 16;
+        if (gi >= 0 && gi < GR * 16) acc = fmaf(__int_as_float(yent[2 * k + 1]), s_g[gi], acc);
       }
       acc = wave_sum(acc);
-      if (lane == 0) dyr[y] = acc;
+      if (lane == 0) {
+        const float v = gr0 == 0 ? acc : s_dy[y] + acc;
+        if (last)
+          dyr[y] = v;
+        else
+          s_dy[y] = v;
+      }
     }
+    }  // groups of G rows
   }
 }
 
@@ -757,22 +775,28 @@ hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int PRE, int NU, bool BATCH, bool VEC>
-hipError_t launch_conv_gemm_pre(const ConvGemmArgs& a, int per_cu, hipStream_t s) {
+template <int PRE, int NU, bool BATCH, bool VEC, int NB>
+hipError_t launch_conv_gemm_nb(const ConvGemmArgs& a, int per_cu, hipStream_t s) {
   // the attribute is per function: raised once, retried after a failure
   static std::atomic<bool> lds_set{false};
-  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH, VEC>), 160 * 1024);
+  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH, VEC, NB>), 160 * 1024);
       e != hipSuccess)
     return e;
   const int64_t items = int64_t(a.n_nodes) * (a.t.C / a.t.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
-  hipLaunchKernelGGL((k_conv_gemm<PRE, NU, BATCH, VEC>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
+  hipLaunchKernelGGL((k_conv_gemm<PRE, NU, BATCH, VEC, NB>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
   return hipGetLastError();
+}
+
+template <int PRE, int NU, bool BATCH, bool VEC>
+hipError_t launch_conv_gemm_pre(const ConvGemmArgs& a, int per_cu, hipStream_t s) {
+  return a.t.n_blocks <= 8 ? launch_conv_gemm_nb<PRE, NU, BATCH, VEC, 8>(a, per_cu, s)
+                           : launch_conv_gemm_nb<PRE, NU, BATCH, VEC, kConvGemmMaxBlocks>(a, per_cu, s);
 }
 
 hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
   if (a.n_nodes <= 0) return hipSuccess;
-  if (a.t.lds_bytes > 160 * 1024 || a.t.n_blocks > kConvGemmBlocks || a.t.CS > 128 ||
+  if (a.t.lds_bytes > 160 * 1024 || a.t.n_blocks > kConvGemmMaxBlocks || a.t.CS > 128 ||
       a.ly > 7 || (a.ly >= 0 && a.t.dy > 64))
     return hipErrorInvalidValue;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
@@ -800,7 +824,8 @@ size_t gemm_dw_lds_bytes(const TpGemmArgs& a) {
 
 size_t gemm_dy_lds_bytes(const GemmBwdArgs& a) {
   const int XS = gemm_dy_row_stride(a.t.CS);
-  return size_t((a.t.dx + a.t.P + a.t.dout) * XS + a.n_grows * 16 + 2 * a.n_grows) * 4;
+  const int gr = std::min(std::max(a.g_rows, 16), a.n_grows) & ~15;
+  return size_t((a.t.dx + a.t.P + a.t.dout) * XS + gr * 16 + 2 * a.n_grows + a.t.dy) * 4;
 }
 
 template <int NU, int NW>
@@ -834,7 +859,8 @@ hipError_t launch_gemm_dw(const GemmBwdArgs& a, hipStream_t s) {
 hipError_t launch_gemm_dy(const GemmBwdArgs& a, hipStream_t s) {
   constexpr int NW = 8;
   if (a.t.n_rows <= 0) return hipSuccess;
-  if (a.t.lds_bytes > 160 * 1024 || a.n_grows % 16) return hipErrorInvalidValue;
+  if (a.t.lds_bytes > 160 * 1024 || a.n_grows % 16 || a.g_rows < 16 || a.g_rows % 16)
+    return hipErrorInvalidValue;
   static std::atomic<bool> lds_set{false};
   if (const hipError_t e =
           set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_gemm_dy<NW>), 160 * 1024);

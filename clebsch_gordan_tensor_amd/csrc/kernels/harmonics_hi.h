@@ -1,5 +1,5 @@
-// Real harmonics of degree 0..LMAX (LMAX <= 7) of a unit vector, degrees
-// 0..3 from their closed forms and 4..7 by the library's own recursion: the
+// Real harmonics of degree 0..LMAX (LMAX <= 8) of a unit vector, degrees
+// 0..3 from their closed forms and 4..8 by the library's own recursion: the
 // coupled product of Y_1 and Y_{L-1} through the real (1, L-1 -> L) block is
 // kappa_L Y_L (the Gaunt relation for an even path; e3j G.1-G.2 build the
 // harmonics and the coefficients from the same ladder structure), with the

@@ -660,6 +660,7 @@ hipError_t launch_harmonics(int lmax, int64_t n, const float* vec, float* Y, hip
     case 5: hipLaunchKernelGGL(k_harmonics<5>, g, b, 0, s, n, vec, Y); break;
     case 6: hipLaunchKernelGGL(k_harmonics<6>, g, b, 0, s, n, vec, Y); break;
     case 7: hipLaunchKernelGGL(k_harmonics<7>, g, b, 0, s, n, vec, Y); break;
+    case 8: hipLaunchKernelGGL(k_harmonics<8>, g, b, 0, s, n, vec, Y); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -678,6 +679,7 @@ hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const fl
     case 5: hipLaunchKernelGGL(k_harmonics_grad<5>, g, b, 0, s, n, vec, dY, dvec); break;
     case 6: hipLaunchKernelGGL(k_harmonics_grad<6>, g, b, 0, s, n, vec, dY, dvec); break;
     case 7: hipLaunchKernelGGL(k_harmonics_grad<7>, g, b, 0, s, n, vec, dY, dvec); break;
+    case 8: hipLaunchKernelGGL(k_harmonics_grad<8>, g, b, 0, s, n, vec, dY, dvec); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

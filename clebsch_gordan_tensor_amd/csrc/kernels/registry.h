@@ -301,8 +301,9 @@ struct GemmBwdArgs {
   const int* rowptr;     // convolution: receiver CSR (nullptr: dz row = row)
   int n_x;               // rows of x (convolution: nodes)
   int n_zrows;           // rows of dz
-  // dy plan
-  int n_grows, n_ent, off_rows, off_yptr, off_yent;
+  // dy plan; g_rows: G rows held in LDS at once (a multiple of 16; n_grows
+  // when they all fit, else the kernel walks them in groups of g_rows)
+  int n_grows, n_ent, off_rows, off_yptr, off_yent, g_rows;
 };
 // dw plan: its row table [n_blocks][16] follows the K list, 16-byte aligned
 constexpr int gemm_dw_rowtab_offset(const TpGemmArgs& a) { return (a.off_klist + a.n_klist + 3) / 4 * 4; }
@@ -312,6 +313,9 @@ hipError_t launch_gemm_dw(const GemmBwdArgs& a, hipStream_t s);
 hipError_t launch_gemm_dy(const GemmBwdArgs& a, hipStream_t s);
 // LDS words the convolution adds to tp_gemm_lds_bytes: the harmonic bank and the y map
 constexpr int kConvGemmExtraWords = 64 + 16;
+// output blocks of the dense convolution (its per-block accumulators stay in
+// registers): the irreps 0..8 once, the 17 rows of degree 8 as 16 + 1
+constexpr int kConvGemmMaxBlocks = 10;
 hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s);
 hipError_t launch_harmonics_grad(int lmax, int64_t n, const float* vec, const float* dY,
                                  float* dvec, hipStream_t s);

@@ -131,7 +131,7 @@ def test_error_codes(lib):
                                None) == -1  # unknown dtype
     assert lib.e3_tp_forward(_desc_c(good), 0, None, None, None, None, 0, None) == 0
     assert lib.e3_tp_forward(_desc_c(good), -2, None, None, None, None, 0, None) == -1
-    assert lib.e3_spherical_harmonics(8, 10, fake, fake, None) == -1
+    assert lib.e3_spherical_harmonics(9, 10, fake, fake, None) == -1
     assert lib.e3_spherical_harmonics(2, 0, None, None, None) == 0
     sz = C.c_size_t()
     assert lib.e3_conv_workspace_size(10, 100, C.byref(sz)) == 0
@@ -156,7 +156,7 @@ def test_error_codes(lib):
                               None) == -4
     assert lib.e3_tp_backward(_desc_c(uns), 5, fake, fake, fake, fake, fake, fake, fake, 0,
                               None) == -3
-    assert lib.e3_spherical_harmonics_backward(8, 10, fake, fake, fake, None) == -1
+    assert lib.e3_spherical_harmonics_backward(9, 10, fake, fake, fake, None) == -1
     assert lib.e3_spherical_harmonics_backward(3, -1, fake, fake, fake, None) == -1
     assert lib.e3_spherical_harmonics_backward(3, 10, fake, None, fake, None) == -1
     assert lib.e3_spherical_harmonics_backward(3, 0, None, None, None, None) == 0
@@ -228,7 +228,7 @@ def test_error_codes(lib):
     assert rb(fake, rneed, None) == -1
     out = np.zeros(10)
     assert lib.e3_cg_block(1, 1, 3, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
-    assert lib.e3_cg_block(8, 1, 7, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
+    assert lib.e3_cg_block(9, 1, 8, out.ctypes.data_as(C.POINTER(C.c_double))) == -1
 
 
 def test_generic_plan_table(lib):
@@ -325,7 +325,7 @@ def test_generic_plan_table(lib):
     assert lib.e3_conv_forward_generic(C.byref(y7.c()), 4, 8, fk, fk, None, 0, fk, 4096, fk,
                                        fk, fk, fk, 0, None) == -3
     assert "degree 6" in lib.e3_last_error().decode()
-    big = api.Desc([(8, 1)], [(0, 1)], [(8, 1)], 64)
+    big = api.Desc([(9, -1)], [(0, 1)], [(9, -1)], 64)
     assert lib.e3_generic_plan_size(C.byref(big.c()), 0, C.byref(nb)) == -3
     assert lib.e3_tp_forward_generic(C.byref(d.c()), 0, None, 0, None, None, None, None, 0,
                                      None) == 0
@@ -348,13 +348,18 @@ def test_gemm_entry_arg_errors(lib):
     assert lib.e3_tp_forward_gemm(C.byref(d.c()), 4, fk, nb.value, odd, fk, fk, fk, None) == -4
     d24 = api.Desc(nat, nat, nat, 24)
     assert lib.e3_tp_forward_gemm(C.byref(d24.c()), 4, fk, nb.value, fk, fk, fk, fk, None) == -3
-    # the convolution: collapsed outputs of at most 8 irreps only
+    # the convolution: collapsed outputs of at most 10 blocks only
     pp = api.Desc(nat, nat, nat, 64, api.E3_OUT_PER_PATH)
     assert lib.e3_conv_forward_gemm(C.byref(pp.c()), 4, 8, fk, fk, fk, nb.value, fk, fk, fk, fk,
                                     None) == -3
-    nine = api.Desc([(0, 1)], [(0, 1)], [(0, 1)] * 9, 64)
-    assert lib.e3_conv_forward_gemm(C.byref(nine.c()), 4, 8, fk, fk, fk, 1 << 20, fk, fk, fk, fk,
+    eleven = api.Desc([(0, 1)], [(0, 1)], [(0, 1)] * 11, 64)
+    assert lib.e3_conv_forward_gemm(C.byref(eleven.c()), 4, 8, fk, fk, fk, 1 << 20, fk, fk, fk,
+                                    fk, None) == -3
+    # harmonics from edge vectors: the per-edge bank holds degrees 0..7
+    y8 = api.Desc([(0, 1)], [(8, 1)], [(8, 1)], 64)
+    assert lib.e3_conv_forward_gemm(C.byref(y8.c()), 4, 8, fk, fk, fk, 1 << 20, fk, fk, fk, fk,
                                     None) == -3
+    assert "degree 7" in lib.e3_last_error().decode()
     assert lib.e3_conv_forward_gemm(C.byref(d.c()), 0, 0, None, None, None, 0, None, None, None,
                                     None, None) == 0
     assert lib.e3_conv_forward_gemm(C.byref(d.c()), 4, 8, fk, fk, None, 0, fk, fk, fk, fk,

@@ -2,7 +2,7 @@
 (tables E3_GEN_GEMM, E3_GEN_GEMM_DX, E3_GEN_GEMM_DW, E3_GEN_GEMM_DY): a numpy
 reading of each plan, doing what the matrix-core kernels do with it (A built
 per row from y, one product per block over its K list), against the fp64
-oracle's tensor product and its backward, at degrees 1-7 with natural and
+oracle's tensor product and its backward, at degrees 1-8 with natural and
 skew parities, collapsed and per-path outputs, and an output irrep no path
 reaches.  These pin the host logic; the GPU tests pin the kernels."""
 import ctypes as C
@@ -53,6 +53,7 @@ def run_gemm(plan, y, xin, w, dout):
     A = _A(plan, y)
     out = np.zeros((xin.shape[0], dout, xin.shape[2]))
     for oo, rows, kl, base in _blocks(plan):
+        assert 1 <= rows <= 16  # the matrix cores' 16 rows (degree 8 split as 16 + 1)
         for k, ent in enumerate(kl):
             if ent < 0:
                 continue
@@ -134,7 +135,7 @@ def _case(L, skew=False, per_path=False, out=None, C=4, B=5, seed=0):
 
 CASES = [(1, False, False), (2, False, False), (3, True, False), (4, False, False),
          (5, False, True), (6, False, False), (6, True, False), (7, False, False),
-         (7, True, False)]
+         (7, True, False), (8, False, False), (8, True, False)]
 
 
 @pytest.mark.parametrize("L,skew,pp", CASES)

@@ -48,7 +48,8 @@ def _case(L, C, B, seed, skew=False, per_path=False):
 
 
 @pytest.mark.parametrize("L,skew", [(1, False), (2, False), (3, False), (4, False), (5, False),
-                                    (6, False), (6, True), (7, False), (7, True)])
+                                    (6, False), (6, True), (7, False), (7, True), (8, False),
+                                    (8, True)])
 def test_gemm_tp_matches_oracle(gpu, L, skew):
     d, od, x, y, w = _case(L, 128, 97, 500 + L, skew)
     z = host(gpu.tp_forward_gemm(d, dev(x), dev(y), dev(w)))
@@ -119,7 +120,7 @@ def _conv_problem(L, C, n, seed, pad=0, skew=False):
 
 @pytest.mark.parametrize("L,C,skew", [(1, 64, False), (3, 128, False), (4, 64, False),
                                       (6, 128, False), (6, 48, True), (7, 128, False),
-                                      (7, 32, True)])
+                                      (7, 32, True), (8, 128, False), (8, 32, True)])
 def test_gemm_conv_matches_oracle(gpu, L, C, skew):
     d, od, g, x, w, Y = _conv_problem(L, C, 40 if L >= 5 else 64, 600 + L, skew=skew)
     rowptr, sender = dev(g.rowptr), dev(g.sender)

@@ -57,7 +57,8 @@ def _check_tp(gpu, d, od, x, y, w, dz, what):
 
 
 @pytest.mark.parametrize("L,skew", [(1, False), (2, False), (3, False), (4, False), (5, False),
-                                    (6, False), (6, True), (7, False), (7, True)])
+                                    (6, False), (6, True), (7, False), (7, True), (8, False),
+                                    (8, True)])
 def test_gemm_tp_backward_matches_oracle(gpu, L, skew):
     _check_tp(gpu, *_tp_case(L, 128, 61, 700 + L, skew), f"gemm tp bwd L={L} skew={skew}")
 
@@ -132,7 +133,7 @@ def _conv_ref(od, g, x, w, dm, Y):
 
 @pytest.mark.parametrize("L,C,skew", [(1, 64, False), (3, 128, False), (4, 64, False),
                                       (6, 128, False), (6, 48, True), (7, 128, False),
-                                      (7, 32, True)])
+                                      (7, 32, True), (8, 128, False), (8, 32, True)])
 def test_gemm_conv_backward_matches_oracle(gpu, L, C, skew):
     d, od, g, x, w, dm, Y = _conv_case(L, C, 40 if L >= 5 else 64, 800 + L, skew=skew)
     got = _run_conv(gpu, d, g, x, w, dm, Y)

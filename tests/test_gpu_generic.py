@@ -154,11 +154,11 @@ def test_generic_tp_backward_equals_compiled_kernel(gpu):
         assert_close(host(u), host(v).astype(np.float64), 2 * TOL_F32, f"generic vs compiled:{k}")
 
 
-# ---------------------------------------------------- harmonics up to degree 7
+# ---------------------------------------------------- harmonics up to degree 8
 
-@pytest.mark.parametrize("lmax", [6, 7])
+@pytest.mark.parametrize("lmax", [6, 7, 8])
 def test_harmonics_to_high_degree_match_oracle(gpu, lmax):
-    # the library builds degrees 4..7 by coupling Y_1 with Y_{L-1} (Gaunt
+    # the library builds degrees 4..8 by coupling Y_1 with Y_{L-1} (Gaunt
     # relation); the oracle by the Legendre construction
     rng = np.random.default_rng(390)
     v = (rng.standard_normal((5001, 3)) * rng.uniform(0.1, 10, (5001, 1))).astype(np.float32)
@@ -172,7 +172,7 @@ def test_harmonics_to_high_degree_match_oracle(gpu, lmax):
     assert np.all(Y[7, 1:] == 0.0) and Y[7, 0] == 1.0
 
 
-@pytest.mark.parametrize("lmax", [4, 6, 7])
+@pytest.mark.parametrize("lmax", [4, 6, 7, 8])
 def test_harmonics_gradient_to_high_degree(gpu, lmax):
     # the vector gradient through the coupling recursion, against the
     # fourth-order differences of the oracle's harmonics
