@@ -636,7 +636,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
   float* s_g = s_z + g.dout * XS;                     // G [GR][16]: rows [gr0, gr0 + GR)
   int* s_r = reinterpret_cast<int*>(s_g + GR * 16);   // per G row: w row | own row << 16
   int* s_b = s_r + a.n_grows;  // per G row: its block's first column row | columns << 16
-  float* s_dy = reinterpret_cast<float*>(s_b + a.n_grows);  // dy of the groups so far
+  float* s_dy = reinterpret_cast<float*>(s_b + a.n_grows);  // dy of the groups so far (two or more)
   const int n_srows = g.dx + g.P + g.dout;  // slab rows: x, w, dz
   for (int i = threadIdx.x; i < a.n_grows; i += NT) {
     const int ent = grows[i];
@@ -668,7 +668,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
     // (one pass when there are no G rows: dy is then written as zeros)
     for (int gr0 = 0; gr0 == 0 || gr0 < a.n_grows; gr0 += max(GR, 16)) {
     const int tg0 = gr0 / 16, tg1 = min(n_gt, (gr0 + GR) / 16);  // this group's tiles
-    __syncthreads();  // the previous group's reads of G are done
+    if (gr0 > 0) __syncthreads();  // the previous group's reads of G are done
     for (int i = threadIdx.x; i < GR * 16; i += NT) s_g[i] = 0.0f;
     for (int sl = 0; sl < n_slabs; ++sl) {
       const int c0 = sl * CS;
@@ -738,9 +738,16 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
     for (int y = wave; y < g.dy; y += NW) {
       float acc = 0.0f;
       const int k0 = max(yptr[y], 0), k1 = min(yptr[y + 1], a.n_ent);
-      for (int k = k0 + lane; k < k1; k += 64) {
-        const int gi = min(max(yent[2 * k], 0), a.n_grows * 16 - 1) - gr0 * 16;
-        if (gi >= 0 && gi < GR * 16) acc = fmaf(__int_as_float(yent[2 * k + 1]), s_g[gi], acc);
+      if (GR >= a.n_grows) {  // all of G in LDS (uniform)
+        for (int k = k0 + lane; k < k1; k += 64) {
+          const int gi = min(max(yent[2 * k], 0), a.n_grows * 16 - 1);
+          acc = fmaf(__int_as_float(yent[2 * k + 1]), s_g[gi], acc);
+        }
+      } else {
+        for (int k = k0 + lane; k < k1; k += 64) {
+          const int gi = min(max(yent[2 * k], 0), a.n_grows * 16 - 1) - gr0 * 16;
+          if (gi >= 0 && gi < GR * 16) acc = fmaf(__int_as_float(yent[2 * k + 1]), s_g[gi], acc);
+        }
       }
       acc = wave_sum(acc);
       if (lane == 0) {
@@ -825,7 +832,9 @@ size_t gemm_dw_lds_bytes(const TpGemmArgs& a) {
 size_t gemm_dy_lds_bytes(const GemmBwdArgs& a) {
   const int XS = gemm_dy_row_stride(a.t.CS);
   const int gr = std::min(std::max(a.g_rows, 16), a.n_grows) & ~15;
-  return size_t((a.t.dx + a.t.P + a.t.dout) * XS + gr * 16 + 2 * a.n_grows + a.t.dy) * 4;
+  // dy's running sums only when G is walked in more than one group
+  const int sdy = gr < a.n_grows ? a.t.dy : 0;
+  return size_t((a.t.dx + a.t.P + a.t.dout) * XS + gr * 16 + 2 * a.n_grows + sdy) * 4;
 }
 
 template <int NU, int NW>
