@@ -1846,11 +1846,30 @@ e3_status gemm_backward_setup(const e3_desc* desc, const Parsed& p, const void* 
   });
   // dw: the widest slab (A is built once per slab; the workgroup has a
   // wavefront per 16 channels)
+  bdw.a_win = 0;
   bdw.t.CS = pick_slab(p.C, [&](int cs) {
     e3k::TpGemmArgs t = bdw.t;
     t.CS = cs;
     return e3k::gemm_dw_lds_bytes(t);
   }, true);
+  if (bdw.t.CS < std::min(64, p.C)) {
+    // A fits beside the dz slab only with narrow slabs, if at all (degree
+    // 8: a 16-channel slab, one wavefront per CU): the widest slab of 64 or
+    // more channels whose LDS leaves a window of at least a quarter of A,
+    // the tiles walked in windows of whole tiles with A built per window
+    for (int cs : {128, 64}) {
+      if (cs > p.C || p.C % cs) continue;
+      e3k::TpGemmArgs t = bdw.t;
+      t.CS = cs;
+      const long fixed = long(e3k::gemm_dw_lds_bytes(t, 4)) - 4 * 4;
+      const long win = ((long(160) * 1024 - fixed) / 4) & ~3L;
+      if (win >= std::max<long>(256, bdw.t.a_floats / 4)) {
+        bdw.t.CS = cs;
+        bdw.a_win = int(std::min<long>(win, bdw.t.a_floats));
+        break;
+      }
+    }
+  }
   bdy = e3k::GemmBwdArgs{};
   bdy.t.n_blocks = dd.n_blocks;
   bdy.t.dx = p.dx;
@@ -1889,7 +1908,7 @@ e3_status gemm_backward_setup(const e3_desc* desc, const Parsed& p, const void* 
   if ((p.P + 1) * XS > 65535 || std::max(p.dx, p.dout) * XS > 65535)
     return fail(E3_ERR_UNSUPPORTED, "too many components or paths for the dense-product kernels");
   tdx.lds_bytes = e3k::tp_gemm_lds_bytes(tdx);
-  bdw.t.lds_bytes = e3k::gemm_dw_lds_bytes(bdw.t);
+  bdw.t.lds_bytes = e3k::gemm_dw_lds_bytes(bdw.t, bdw.a_win);
   bdy.t.lds_bytes = e3k::gemm_dy_lds_bytes(bdy);
   tdx.plan = static_cast<const int*>(plan_dx);
   bdw.t.plan = static_cast<const int*>(plan_dw);

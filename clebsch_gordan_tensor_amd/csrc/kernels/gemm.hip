@@ -455,7 +455,9 @@ __host__ __device__ constexpr int gemm_dw_a_slack() { return 256; }
 // (the next quad of one path) then fall in the other half of the banks
 __host__ __device__ constexpr int gemm_dw_row_stride(int CS) { return CS + 4; }
 
-template <int NU, int NW>
+// WIN: A held in windows of whole tiles (a.a_win > 0; otherwise all of it,
+// and this form has no window code in its tile loop)
+template <int NU, int NW, bool WIN>
 __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
   constexpr int NT = 64 * NW;
   extern __shared__ __align__(16) float gsm[];
@@ -466,7 +468,10 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
   const int4* __restrict__ groups = reinterpret_cast<const int4*>(g.plan + g.off_groups);
   const int CS = g.CS, C = g.C, XS = gemm_dw_row_stride(CS);
   const int lg4 = __builtin_ctz(CS / 4);
-  const int a4 = ((g.a_floats + 3) & ~3) + gemm_dw_a_slack();
+  // A of every tile at once, or (AW < a_floats) a window of whole tiles
+  const int AW = WIN && a.a_win > 0 ? min(a.a_win, g.a_floats) : g.a_floats;
+  const bool windowed = WIN && AW < g.a_floats;
+  const int a4 = ((AW + 3) & ~3) + gemm_dw_a_slack();
   float* s_a = gsm;                         // A [tiles][K][16], then slack for reads past the last
   float* s_z = s_a + a4;                    // [dout + 1][XS]: a row of zeros, then the dz slab
   int* s_rt = reinterpret_cast<int*>(s_z + (g.dout + 1) * XS);  // rows [n_blocks][16], staged
@@ -518,15 +523,27 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
     }
     for (int i = threadIdx.x; i < g.dy; i += NT) s_y[i] = g.y[row * g.dy + i];
     __syncthreads();
+    // A[at - a0] for the entries with at in [a0, a1)
+    auto build_a = [&](int a0, int a1) {
 #pragma unroll 4
-    for (int q = threadIdx.x; q < g.n_groups; q += NT) {
-      const int4 e = groups[q];
-      const int at = min(max(e.x, 0), g.a_floats - 1);
-      const int y1 = min(e.y & 0xFFFF, g.dy - 1), y2 = min((e.y >> 16) & 0xFFFF, g.dy - 1);
-      s_a[at] = fmaf(__int_as_float(e.w), s_y[y2], __int_as_float(e.z) * s_y[y1]);
+      for (int q = threadIdx.x; q < g.n_groups; q += NT) {
+        const int4 e = groups[q];
+        const int at = min(max(e.x, 0), g.a_floats - 1);
+        const int y1 = min(e.y & 0xFFFF, g.dy - 1), y2 = min((e.y >> 16) & 0xFFFF, g.dy - 1);
+        if (at >= a0 && at < a1)
+          s_a[at - a0] = fmaf(__int_as_float(e.w), s_y[y2], __int_as_float(e.z) * s_y[y1]);
+      }
+    };
+    if (!windowed) {  // all of A, every entry
+#pragma unroll 4
+      for (int q = threadIdx.x; q < g.n_groups; q += NT) {
+        const int4 e = groups[q];
+        const int at = min(max(e.x, 0), g.a_floats - 1);
+        const int y1 = min(e.y & 0xFFFF, g.dy - 1), y2 = min((e.y >> 16) & 0xFFFF, g.dy - 1);
+        s_a[at] = fmaf(__int_as_float(e.w), s_y[y2], __int_as_float(e.z) * s_y[y1]);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (!active) continue;
     // acc: paths 16 cur + [0, 16); register r of lane (li, kq) holds path
     // 16 cur + 4 kq + r at channel 16 (wave + NW u) + li
     float4v acc[NU];
@@ -544,6 +561,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
     const float* zl = s_z + 16 * wave + li;  // this lane's channel in a dz row
     const float* xl = g.x + int64_t(xr) * g.dx * C + c0 + 16 * wave + li;  // and in x
     int cur = 0, cur_kb = -1, cur_K = -1, abase = 0;
+    int w0 = 0, w1 = windowed ? 0 : g.a_floats;  // A offsets [w0, w1) in LDS
     float xb[4][NU];
     // the tiles' descriptors from LDS, the next one read while this one runs
     int4 bd = g.n_blocks > 0 ? *reinterpret_cast<const int4*>(s_bd) : int4{0, 0, 0, 0};
@@ -553,9 +571,22 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
       const int K = __builtin_amdgcn_readfirstlane(bd.w);
       if (b + 1 < g.n_blocks) bd = *reinterpret_cast<const int4*>(s_bd + 4 * (b + 1));
       if (abase + 16 * K > g.a_floats) break;
+      if (WIN && abase + 16 * K > w1) {  // windowed (uniform): the next window starts at this tile
+        w0 = abase;
+        w1 = abase + AW;
+        __syncthreads();  // the previous window's reads are done
+        for (int i = threadIdx.x; i < a4; i += NT) s_a[i] = 0.0f;
+        __syncthreads();
+        build_a(w0, w1);
+        __syncthreads();
+      }
+      if (!active) {  // the same for the whole wavefront (it still joins the barriers)
+        abase += 16 * K;
+        continue;
+      }
       // A of the tile, its four K steps' reads issued together (past the
       // tile's K they read the next tile's A or the slack, unused)
-      const float* ap = s_a + abase + 16 * kq + li;
+      const float* ap = s_a + (abase - w0) + 16 * kq + li;
       float av[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) av[j] = ap[64 * j];
@@ -600,7 +631,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
       }
       abase += 16 * K;
     }
-    flush(cur);
+    if (active) flush(cur);
   }
 }
 
@@ -823,10 +854,11 @@ hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
                      : launch_conv_gemm_pre<0, 1, false, false>(a, std::min(per_cu, 8), s);
 }
 
-size_t gemm_dw_lds_bytes(const TpGemmArgs& a) {
+size_t gemm_dw_lds_bytes(const TpGemmArgs& a, int a_win) {
   const int XS = gemm_dw_row_stride(a.CS);
-  return size_t(((a.a_floats + 3) & ~3) + gemm_dw_a_slack() + (a.dout + 1) * XS +
-                20 * a.n_blocks + a.n_klist + a.dy) * 4;
+  const int aw = a_win > 0 ? std::min(a_win, a.a_floats) : a.a_floats;
+  return size_t(((aw + 3) & ~3) + gemm_dw_a_slack() + (a.dout + 1) * XS + 20 * a.n_blocks +
+                a.n_klist + a.dy) * 4;
 }
 
 size_t gemm_dy_lds_bytes(const GemmBwdArgs& a) {
@@ -837,24 +869,33 @@ size_t gemm_dy_lds_bytes(const GemmBwdArgs& a) {
   return size_t((a.t.dx + a.t.P + a.t.dout) * XS + gr * 16 + 2 * a.n_grows + sdy) * 4;
 }
 
-template <int NU, int NW>
-hipError_t launch_gemm_dw_nu(const GemmBwdArgs& a, hipStream_t s) {
+template <int NU, int NW, bool WIN>
+hipError_t launch_gemm_dw_win(const GemmBwdArgs& a, hipStream_t s) {
   static std::atomic<bool> lds_set{false};
   if (const hipError_t e = set_max_lds_once(
-          lds_set, reinterpret_cast<const void*>(&k_gemm_dw<NU, NW>), 160 * 1024);
+          lds_set, reinterpret_cast<const void*>(&k_gemm_dw<NU, NW, WIN>), 160 * 1024);
       e != hipSuccess)
     return e;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
   const int64_t items = a.t.n_rows * (a.t.C / a.t.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * std::min(per_cu, 8)));
-  hipLaunchKernelGGL((k_gemm_dw<NU, NW>), dim3(grid), dim3(64 * NW), a.t.lds_bytes, s, a);
+  hipLaunchKernelGGL((k_gemm_dw<NU, NW, WIN>), dim3(grid), dim3(64 * NW), a.t.lds_bytes, s, a);
   return hipGetLastError();
+}
+
+template <int NU, int NW>
+hipError_t launch_gemm_dw_nu(const GemmBwdArgs& a, hipStream_t s) {
+  if constexpr (NW >= 4)  // windows only with slabs of 64 or 128 channels
+    if (a.a_win > 0) return launch_gemm_dw_win<NU, NW, true>(a, s);
+  if (a.a_win > 0) return hipErrorInvalidValue;
+  return launch_gemm_dw_win<NU, NW, false>(a, s);
 }
 
 // one 16-channel tile per wavefront
 hipError_t launch_gemm_dw(const GemmBwdArgs& a, hipStream_t s) {
   if (a.t.n_rows <= 0) return hipSuccess;
-  if (a.t.lds_bytes > 160 * 1024) return hipErrorInvalidValue;
+  // a window holds at least one whole tile (16 x 16 floats)
+  if (a.t.lds_bytes > 160 * 1024 || (a.a_win > 0 && a.a_win < 256)) return hipErrorInvalidValue;
   switch (a.t.CS) {
     case 128: return launch_gemm_dw_nu<1, 8>(a, s);
     case 64: return launch_gemm_dw_nu<1, 4>(a, s);

@@ -304,10 +304,13 @@ struct GemmBwdArgs {
   // dy plan; g_rows: G rows held in LDS at once (a multiple of 16; n_grows
   // when they all fit, else the kernel walks them in groups of g_rows)
   int n_grows, n_ent, off_rows, off_yptr, off_yent, g_rows;
+  // dw plan: floats of A held in LDS at once (0: all of it; else the tiles
+  // are walked in windows of whole tiles, A built per window)
+  int a_win;
 };
 // dw plan: its row table [n_blocks][16] follows the K list, 16-byte aligned
 constexpr int gemm_dw_rowtab_offset(const TpGemmArgs& a) { return (a.off_klist + a.n_klist + 3) / 4 * 4; }
-size_t gemm_dw_lds_bytes(const TpGemmArgs& a);
+size_t gemm_dw_lds_bytes(const TpGemmArgs& a, int a_win = 0);
 size_t gemm_dy_lds_bytes(const GemmBwdArgs& a);
 hipError_t launch_gemm_dw(const GemmBwdArgs& a, hipStream_t s);
 hipError_t launch_gemm_dy(const GemmBwdArgs& a, hipStream_t s);
