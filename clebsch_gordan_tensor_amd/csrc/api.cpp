@@ -1329,6 +1329,7 @@ e3_status build_gemm_kind(const e3_desc* desc, int kind, std::vector<int32_t>& o
   // the kernel's view: input components (dx), output components (dout)
   const int in_dim = kind == 1 ? p.dout : p.dx, out_dim = kind == 1 ? p.dx : p.dout;
   d = e3k::TpGemmArgs{};
+  for (const Sub& sb : subs) d.a_block_max = std::max(d.a_block_max, sb.rows * sb.K);
   d.n_blocks = nsub;
   d.dx = in_dim;
   d.dy = p.dy;
@@ -1649,6 +1650,23 @@ e3_status gemm_dims(const e3_desc* desc, e3k::TpGemmArgs& d, size_t& bytes, int 
   return ok();
 }
 
+// A dense tensor-product plan whose A fits beside the staged slabs only with
+// slabs of fewer than 64 channels (degree 8: 16, one busy wavefront of
+// four): 64-channel slabs with A in windows of whole blocks instead, if a
+// window of at least a quarter of A (and the largest block) fits.
+void tp_gemm_window(e3k::TpGemmArgs& t) {
+  if (t.CS >= 64 || t.C % 64) return;
+  e3k::TpGemmArgs w = t;
+  w.CS = 64;
+  w.a_win = 1;
+  const long fixed = long(e3k::tp_gemm_lds_bytes(w)) - 4;
+  const long win = (long(160) * 1024 - fixed) / 4;
+  if (win < std::max<long>(t.a_block_max, t.a_floats / 4) || win >= t.a_floats) return;
+  t.CS = 64;
+  t.a_win = int(win);
+  t.lds_bytes = e3k::tp_gemm_lds_bytes(t);
+}
+
 e3_status build_table(const e3_desc* desc, int table, std::vector<int32_t>& out) {
   if (table == E3_GEN_GEMM || table == E3_GEN_GEMM_DX || table == E3_GEN_GEMM_DW) {
     e3k::TpGemmArgs d;
@@ -1754,6 +1772,7 @@ e3_status e3_tp_forward_gemm(const e3_desc* desc, int64_t n_rows, const void* pl
     }
     if (a.CS) break;
   }
+  tp_gemm_window(a);
   if (!a.CS) return fail(E3_ERR_UNSUPPORTED, "the dense-product plan does not fit in LDS");
   if ((a.P + 1) * e3k::gemm_row_stride(a.CS) > 65535 || a.dx * e3k::gemm_row_stride(a.CS) > 65535)
     return fail(E3_ERR_UNSUPPORTED, "too many x components or paths for the dense-product kernel");
@@ -1941,6 +1960,10 @@ e3_status e3_tp_backward_gemm(const e3_desc* desc, int64_t n_rows, const void* p
     return fail(E3_ERR_ALIGNMENT, "x, w and dz must be 16-byte aligned");
   const hipStream_t st = hipStream_t(stream);
   // dx: the forward's product with the roles of x and the output swapped
+  tp_gemm_window(tdx);
+  if ((tdx.P + 1) * e3k::gemm_row_stride(tdx.CS) > 65535 ||
+      tdx.dx * e3k::gemm_row_stride(tdx.CS) > 65535)
+    return fail(E3_ERR_UNSUPPORTED, "too many components or paths for the dense-product kernels");
   tdx.n_rows = n_rows;
   tdx.x = dz;
   tdx.y = y;

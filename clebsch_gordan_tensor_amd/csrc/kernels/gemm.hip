@@ -95,16 +95,19 @@ __device__ __forceinline__ void gemm_ksteps(float4v (&D)[NU], const float* ap, c
 // PRE: 16-byte units per thread loaded one item ahead (12 for plans whose
 // LDS leaves at most two workgroups per CU; 0 keeps the registers low so that
 // small plans run more workgroups per CU).
-template <int PRE, int NU>
+// WIN: A in windows of whole blocks (g.a_win > 0), built as the block loop
+// reaches them; this form alone carries the window code.
+template <int PRE, int NU, bool WIN>
 __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
   extern __shared__ __align__(16) float gsm[];
+  const int AW = WIN && g.a_win > 0 ? min(g.a_win, g.a_floats) : g.a_floats;
   const int* __restrict__ blocks = g.plan + g.off_blocks;
   const int* __restrict__ klist = g.plan + g.off_klist;
   const int4* __restrict__ groups = reinterpret_cast<const int4*>(g.plan + g.off_groups);
   const int CS = g.CS, C = g.C, XS = gemm_row_stride(CS);
   const int lg4 = __builtin_ctz(CS / 4);  // CS is a power of two
   float* s_a = gsm;
-  float* s_x = s_a + g.a_floats;
+  float* s_x = s_a + AW;
   float* s_w = s_x + g.dx * XS;  // P rows and a zero row (the padding columns' weight)
   float* s_y = s_w + (g.P + 1) * XS;
   int* s_k = reinterpret_cast<int*>(s_y + g.dy);
@@ -117,8 +120,8 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
   }
   for (int i = threadIdx.x; i < XS; i += 256) s_w[g.P * XS + i] = 0.0f;
   // A's entries outside the plan's groups stay zero: every row (edge)
-  // rewrites all the others, so A is cleared once
-  for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
+  // rewrites all the others, so A is cleared once (a window, per window)
+  for (int i = threadIdx.x; i < AW; i += 256) s_a[i] = 0.0f;
   // wave-uniform (a scalar), so the tile tests below are scalar branches
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, kq = lane >> 4;
@@ -167,26 +170,43 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
       s_y[i] = PRE > 0 && i < 256 ? ypre : g.y[row * g.dy + i];
     __syncthreads();
     // A[k][M] = c1 y[y1] + c2 y[y2]: one independent 16-byte load per entry
+    // (in a window: the entries with A index in [a0, a1) at index - a0)
+    auto build_a = [&](int a0, int a1) {
 #pragma unroll 4
-    for (int q = threadIdx.x; q < g.n_groups; q += 256) {
-      const int4 e = groups[q];
-      const int at = min(max(e.x, 0), g.a_floats - 1);
-      const int y1 = min(e.y & 0xFFFF, g.dy - 1), y2 = min((e.y >> 16) & 0xFFFF, g.dy - 1);
-      s_a[at] = fmaf(__int_as_float(e.w), s_y[y2], __int_as_float(e.z) * s_y[y1]);
+      for (int q = threadIdx.x; q < g.n_groups; q += 256) {
+        const int4 e = groups[q];
+        const int at = min(max(e.x, 0), g.a_floats - 1);
+        const int y1 = min(e.y & 0xFFFF, g.dy - 1), y2 = min((e.y >> 16) & 0xFFFF, g.dy - 1);
+        if (!WIN || (at >= a0 && at < a1))
+          s_a[at - a0] = fmaf(__int_as_float(e.w), s_y[y2], __int_as_float(e.z) * s_y[y1]);
+      }
+    };
+    if (!WIN) {
+      build_a(0, g.a_floats);
+      __syncthreads();
     }
-    __syncthreads();
     // the next item's operands load while this item's products run
     if (PRE > 0 && item + gridDim.x < n_items) prefetch(item + gridDim.x);
-    int abase = 0;
+    int abase = 0, w0 = 0, w1 = WIN ? 0 : g.a_floats;  // A offsets [w0, w1) in LDS
     for (int b = 0; b < g.n_blocks; ++b) {
       const int oo = blocks[4 * b], rows = min(max(blocks[4 * b + 1], 1), 16);
       const int kb = min(max(blocks[4 * b + 2], 0), g.n_klist);
       const int K = min(max(blocks[4 * b + 3], 0), g.n_klist - kb) & ~3;
       if (abase + rows * K > g.a_floats) break;
+      if (WIN && abase + rows * K > w1) {  // the next window starts at this block (uniform)
+        if (rows * K > AW) break;          // a block larger than the window: not built
+        w0 = abase;
+        w1 = abase + AW;
+        __syncthreads();  // the previous window's reads are done
+        for (int i = threadIdx.x; i < AW; i += 256) s_a[i] = 0.0f;
+        __syncthreads();
+        build_a(w0, w1);
+        __syncthreads();
+      }
       // A[k = k0 + kq][M = li] at abase + k * rows + M; lanes past the rows read a
       // valid entry and take zero
       const bool aok = li < rows;
-      const float* ap = s_a + abase + kq * rows + min(li, rows - 1);
+      const float* ap = s_a + (abase - w0) + kq * rows + min(li, rows - 1);
       const int* kp = s_k + kb + kq;
       if (active) {
         float4v D[NU];
@@ -797,19 +817,20 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
 
 size_t tp_gemm_lds_bytes(const TpGemmArgs& a) {
   const int XS = gemm_row_stride(a.CS);
-  return size_t(a.a_floats + a.dx * XS + (a.P + 1) * XS + a.dy + a.n_klist) * 4;
+  const int aw = a.a_win > 0 ? std::min(a.a_win, a.a_floats) : a.a_floats;
+  return size_t(aw + a.dx * XS + (a.P + 1) * XS + a.dy + a.n_klist) * 4;
 }
 
-template <int PRE, int NU>
+template <int PRE, int NU, bool WIN = false>
 hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
   // the attribute is per function: raised once, retried after a failure
   static std::atomic<bool> lds_set{false};
-  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_tp_gemm<PRE, NU>), 160 * 1024);
+  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_tp_gemm<PRE, NU, WIN>), 160 * 1024);
       e != hipSuccess)
     return e;
   const int64_t items = a.n_rows * (a.C / a.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
-  hipLaunchKernelGGL((k_tp_gemm<PRE, NU>), dim3(grid), dim3(256), a.lds_bytes, s, a);
+  hipLaunchKernelGGL((k_tp_gemm<PRE, NU, WIN>), dim3(grid), dim3(256), a.lds_bytes, s, a);
   return hipGetLastError();
 }
 
@@ -834,6 +855,7 @@ hipError_t launch_conv_gemm_pre(const ConvGemmArgs& a, int per_cu, hipStream_t s
 
 hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
   if (a.n_nodes <= 0) return hipSuccess;
+  if (a.t.a_win > 0) return hipErrorInvalidValue;  // all of A per edge
   if (a.t.lds_bytes > 160 * 1024 || a.t.n_blocks > kConvGemmMaxBlocks || a.t.CS > 128 ||
       a.ly > 7 || (a.ly >= 0 && a.t.dy > 64))
     return hipErrorInvalidValue;
@@ -926,6 +948,10 @@ hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
   if (a.lds_bytes > 160 * 1024) return hipErrorInvalidValue;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.lds_bytes, 1)));
+  if (a.a_win > 0) {  // A in windows: 64-channel slabs (a tile per wavefront), one form
+    if (a.CS != 64 || a.a_win < a.a_block_max) return hipErrorInvalidValue;
+    return launch_tp_gemm_pre<12, 1, true>(a, per_cu, s);
+  }
   // tiles per wavefront: a 128-channel slab has 8 tiles (2 per wavefront),
   // smaller slabs at most 4 (1 per wavefront, some wavefronts idle below 64)
   if (a.CS > 64)

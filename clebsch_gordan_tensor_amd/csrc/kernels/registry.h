@@ -271,6 +271,9 @@ struct TpGemmArgs {
   const float* w;
   float* z;
   size_t lds_bytes;
+  // the largest block's A (floats); A held in LDS in windows of whole blocks
+  // of a_win floats (0: all of it; the tensor product's kernel only)
+  int a_block_max = 0, a_win = 0;
 };
 // LDS row stride (floats) of a staged slab of CS channels: 16 (mod 32)
 __host__ __device__ constexpr int gemm_row_stride(int CS) { return CS / 32 * 32 + 16 + (CS % 32 ? 32 : 0); }
