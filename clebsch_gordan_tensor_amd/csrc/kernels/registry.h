@@ -280,7 +280,8 @@ __host__ __device__ constexpr int gemm_row_stride(int CS) { return CS / 32 * 32 
 size_t tp_gemm_lds_bytes(const TpGemmArgs& a);
 hipError_t launch_tp_gemm(const TpGemmArgs& a, hipStream_t s);
 // The convolution forward in the same form (t.n_rows unused; t.y = Y [E][dy];
-// t.x = node features, t.w = edge weights; collapsed outputs, <= 8 blocks).
+// t.x = node features, t.w = edge weights; collapsed outputs, at most
+// kConvGemmMaxBlocks blocks).
 struct ConvGemmArgs {
   TpGemmArgs t;
   int n_nodes;

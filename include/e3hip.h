@@ -378,9 +378,10 @@ e3_status e3_tp_forward_gemm(const e3_desc* desc, int64_t n_rows, const void* pl
  * A_{e,L} xt_e (A from Y[e], xt from w[e] and x[sender e]) accumulates in the
  * matrix cores' registers over the edge list in CSR order, so m is written
  * once per node and reproducibly.  edge_vec_or_Y: edge vectors [E][3] (the
- * harmonics of every y irrep are computed per edge: needs dy <= 64) or,
- * with E3_Y_GIVEN, Y [E][dy]; collapsed outputs with at most 8 output
- * irreps, C % 16 == 0, float32.  plan: table E3_GEN_GEMM (as
+ * harmonics of every y irrep are computed per edge: needs dy <= 64 and
+ * degrees <= 7) or, with E3_Y_GIVEN, Y [E][dy]; collapsed outputs with at
+ * most 10 output blocks (an output irrep is one block, a degree-8 irrep
+ * two: the irreps 0..8 once fit), C % 16 == 0, float32.  plan: table E3_GEN_GEMM (as
  * e3_tp_forward_gemm).  x [N][dx][C], w [E][P][C] (16-byte aligned),
  * m [N][dout][C]; padding edges (a sender outside [0, N)) add nothing, and a
  * row range outside [0, E) is clamped to it. */
@@ -412,7 +413,8 @@ e3_status e3_tp_backward_gemm(const e3_desc* desc, int64_t n_rows, const void* p
 /* The backward of e3_conv_forward_gemm (e3j E.1 Eq.16) in the same dense
  * form, given harmonics only (E3_Y_GIVEN; from edge vectors, form Y with
  * e3_spherical_harmonics and chain dY with e3_spherical_harmonics_backward),
- * collapsed outputs, at most 8 x irreps: dx per sender over its out-edges
+ * collapsed outputs, at most 10 x blocks (as the forward's output blocks):
+ * dx per sender over its out-edges
  * (the workspace of e3_conv_prepare_transpose on this graph, required), the
  * products accumulated in registers in the index's order; dw and dY per
  * edge, x gathered by sender and dm by receiver.  Padding edges (a sender
