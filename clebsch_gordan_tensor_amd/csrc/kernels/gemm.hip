@@ -95,6 +95,35 @@ __device__ __forceinline__ void gemm_ksteps(float4v (&D)[NU], const float* ap, c
 // PRE: 16-byte units per thread loaded one item ahead (12 for plans whose
 // LDS leaves at most two workgroups per CU; 0 keeps the registers low so that
 // small plans run more workgroups per CU).
+// Windows of whole blocks over A, each starting at the first block that does
+// not fit in the previous one (the partition the block loops walk), and,
+// the plans' entries being sorted by A index, each window's run of entries:
+// wq[i] = the first entry whose index is at least window i's start, wq[n] =
+// n_groups.  Run by one thread once per workgroup; returns the number of
+// windows found (at most kMaxWindows: later windows scan every entry).
+constexpr int kMaxWindows = 15;
+template <class SizeOf>
+__device__ int window_runs(int n_blocks, SizeOf size_of, int a_floats, int AW,
+                           const int4* __restrict__ groups, int n_groups, int* wq) {
+  int nw = 0, abase = 0, w1 = 0;
+  for (int b = 0; b < n_blocks && nw < kMaxWindows; ++b) {
+    const int sz = size_of(b);
+    if (abase + sz > a_floats) break;
+    if (abase + sz > w1) {
+      w1 = abase + AW;
+      int lo = 0, hi = n_groups;  // first entry with index >= abase
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (groups[mid].x < abase) lo = mid + 1; else hi = mid;
+      }
+      wq[nw++] = lo;
+    }
+    abase += sz;
+  }
+  wq[nw] = n_groups;
+  return nw;
+}
+
 // WIN: A in windows of whole blocks (g.a_win > 0), built as the block loop
 // reaches them; this form alone carries the window code.
 template <int PRE, int NU, bool WIN>
@@ -122,6 +151,15 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
   // A's entries outside the plan's groups stay zero: every row (edge)
   // rewrites all the others, so A is cleared once (a window, per window)
   for (int i = threadIdx.x; i < AW; i += 256) s_a[i] = 0.0f;
+  int* s_wq = s_k + g.n_klist;  // windows: their runs of entries, then their count
+  if (WIN && threadIdx.x == 0) {
+    auto size_of = [&](int b) {
+      const int rows = min(max(blocks[4 * b + 1], 1), 16);
+      const int kb = min(max(blocks[4 * b + 2], 0), g.n_klist);
+      return rows * (min(max(blocks[4 * b + 3], 0), g.n_klist - kb) & ~3);
+    };
+    s_wq[kMaxWindows + 1] = window_runs(g.n_blocks, size_of, g.a_floats, AW, groups, g.n_groups, s_wq);
+  }
   // wave-uniform (a scalar), so the tile tests below are scalar branches
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, kq = lane >> 4;
@@ -171,9 +209,9 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
     __syncthreads();
     // A[k][M] = c1 y[y1] + c2 y[y2]: one independent 16-byte load per entry
     // (in a window: the entries with A index in [a0, a1) at index - a0)
-    auto build_a = [&](int a0, int a1) {
+    auto build_a = [&](int a0, int a1, int q0, int q1) {
 #pragma unroll 4
-      for (int q = threadIdx.x; q < g.n_groups; q += 256) {
+      for (int q = q0 + threadIdx.x; q < q1; q += 256) {
         const int4 e = groups[q];
         const int at = min(max(e.x, 0), g.a_floats - 1);
         const int y1 = min(e.y & 0xFFFF, g.dy - 1), y2 = min((e.y >> 16) & 0xFFFF, g.dy - 1);
@@ -182,12 +220,13 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
       }
     };
     if (!WIN) {
-      build_a(0, g.a_floats);
+      build_a(0, g.a_floats, 0, g.n_groups);
       __syncthreads();
     }
     // the next item's operands load while this item's products run
     if (PRE > 0 && item + gridDim.x < n_items) prefetch(item + gridDim.x);
     int abase = 0, w0 = 0, w1 = WIN ? 0 : g.a_floats;  // A offsets [w0, w1) in LDS
+    int wi = 0;                                          // window number
     for (int b = 0; b < g.n_blocks; ++b) {
       const int oo = blocks[4 * b], rows = min(max(blocks[4 * b + 1], 1), 16);
       const int kb = min(max(blocks[4 * b + 2], 0), g.n_klist);
@@ -200,7 +239,12 @@ __global__ void __launch_bounds__(256) k_tp_gemm(TpGemmArgs g) {
         __syncthreads();  // the previous window's reads are done
         for (int i = threadIdx.x; i < AW; i += 256) s_a[i] = 0.0f;
         __syncthreads();
-        build_a(w0, w1);
+        const int nw = s_wq[kMaxWindows + 1];
+        if (wi < nw)
+          build_a(w0, w1, s_wq[wi], s_wq[wi + 1]);
+        else
+          build_a(w0, w1, 0, g.n_groups);
+        ++wi;
         __syncthreads();
       }
       // A[k = k0 + kq][M = li] at abase + k * rows + M; lanes past the rows read a
@@ -519,6 +563,14 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
   }
   for (int i = threadIdx.x; i < XS; i += NT) s_z[i] = 0.0f;
   for (int i = threadIdx.x; i < a4; i += NT) s_a[i] = 0.0f;
+  int* s_wq = reinterpret_cast<int*>(s_y + g.dy);  // windows: their runs of entries, their count
+  if (windowed && threadIdx.x == 0) {
+    auto size_of = [&](int b) {  // as the s_bd entries above
+      const int kb = min(max(blocks[4 * b + 2], 0), max(g.n_klist - 1, 0));
+      return 16 * (min(min(max(blocks[4 * b + 3], 0), g.n_klist - kb), 16) & ~3);
+    };
+    s_wq[kMaxWindows + 1] = window_runs(g.n_blocks, size_of, g.a_floats, AW, groups, g.n_groups, s_wq);
+  }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, kq = lane >> 4;
   const int n_slabs = C / CS;
@@ -544,9 +596,9 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
     for (int i = threadIdx.x; i < g.dy; i += NT) s_y[i] = g.y[row * g.dy + i];
     __syncthreads();
     // A[at - a0] for the entries with at in [a0, a1)
-    auto build_a = [&](int a0, int a1) {
+    auto build_a = [&](int a0, int a1, int q0, int q1) {
 #pragma unroll 4
-      for (int q = threadIdx.x; q < g.n_groups; q += NT) {
+      for (int q = q0 + threadIdx.x; q < q1; q += NT) {
         const int4 e = groups[q];
         const int at = min(max(e.x, 0), g.a_floats - 1);
         const int y1 = min(e.y & 0xFFFF, g.dy - 1), y2 = min((e.y >> 16) & 0xFFFF, g.dy - 1);
@@ -582,6 +634,7 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
     const float* xl = g.x + int64_t(xr) * g.dx * C + c0 + 16 * wave + li;  // and in x
     int cur = 0, cur_kb = -1, cur_K = -1, abase = 0;
     int w0 = 0, w1 = windowed ? 0 : g.a_floats;  // A offsets [w0, w1) in LDS
+    int wi = 0;                                   // window number
     float xb[4][NU];
     // the tiles' descriptors from LDS, the next one read while this one runs
     int4 bd = g.n_blocks > 0 ? *reinterpret_cast<const int4*>(s_bd) : int4{0, 0, 0, 0};
@@ -597,7 +650,12 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dw(GemmBwdArgs a) {
         __syncthreads();  // the previous window's reads are done
         for (int i = threadIdx.x; i < a4; i += NT) s_a[i] = 0.0f;
         __syncthreads();
-        build_a(w0, w1);
+        const int nw = s_wq[kMaxWindows + 1];
+        if (wi < nw)
+          build_a(w0, w1, s_wq[wi], s_wq[wi + 1]);
+        else
+          build_a(w0, w1, 0, g.n_groups);
+        ++wi;
         __syncthreads();
       }
       if (!active) {  // the same for the whole wavefront (it still joins the barriers)
@@ -818,7 +876,8 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
 size_t tp_gemm_lds_bytes(const TpGemmArgs& a) {
   const int XS = gemm_row_stride(a.CS);
   const int aw = a.a_win > 0 ? std::min(a.a_win, a.a_floats) : a.a_floats;
-  return size_t(aw + a.dx * XS + (a.P + 1) * XS + a.dy + a.n_klist) * 4;
+  const int wq = a.a_win > 0 ? kMaxWindows + 2 : 0;  // the windows' runs of entries
+  return size_t(aw + a.dx * XS + (a.P + 1) * XS + a.dy + a.n_klist + wq) * 4;
 }
 
 template <int PRE, int NU, bool WIN = false>
@@ -879,8 +938,9 @@ hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
 size_t gemm_dw_lds_bytes(const TpGemmArgs& a, int a_win) {
   const int XS = gemm_dw_row_stride(a.CS);
   const int aw = a_win > 0 ? std::min(a_win, a.a_floats) : a.a_floats;
+  const int wq = a_win > 0 ? kMaxWindows + 2 : 0;  // the windows' runs of entries
   return size_t(((aw + 3) & ~3) + gemm_dw_a_slack() + (a.dout + 1) * XS + 20 * a.n_blocks +
-                a.n_klist + a.dy) * 4;
+                a.n_klist + a.dy + wq) * 4;
 }
 
 size_t gemm_dy_lds_bytes(const GemmBwdArgs& a) {
