@@ -30,6 +30,8 @@ def _A(plan, y):
     """A (all blocks) for each row: A[at] = c1 y[y1] + c2 y[y2]."""
     a_floats, off_groups, n_groups = plan[9], plan[12], plan[7]
     g = plan[off_groups:off_groups + 4 * n_groups].reshape(-1, 4)
+    # entries sorted by A index: the kernels' windows of A each take one run
+    assert np.all(np.diff(g[:, 0]) > 0)
     c = g[:, 2:].copy().view(np.float32).astype(np.float64)
     y1, y2 = g[:, 1] & 0xFFFF, (g[:, 1] >> 16) & 0xFFFF
     A = np.zeros((y.shape[0], a_floats))
