@@ -212,3 +212,29 @@ def test_generic_conv_graph_without_edges(gpu):
     torch.cuda.synchronize()
     assert torch.count_nonzero(m) == 0 and torch.count_nonzero(dx) == 0
     assert dw.numel() == 0 and dY.numel() == 0
+
+
+def test_generic_tables_at_degrees_7_and_8(gpu):
+    # the coefficient tables past degree 6, on operands within their 63
+    # components: x 8e, harmonics 0e+2e+8e and 7o given (rows of any values),
+    # out 8e+6e+7o; the convolution forward and backward and the tensor
+    # product forward and backward
+    xi, oi = [(8, 1)], [(8, 1), (6, 1), (7, -1)]
+    yi = [(0, 1), (2, 1), (8, 1), (7, -1)]
+    g, x, w, dm = _problem(xi, yi, oi, 64, 40, 7.0, 3.5, seed=430, pad=1)
+    Y = np.random.default_rng(431).standard_normal((g.n_edges, S.dim(yi))).astype(np.float32)
+    d = gpu.Desc(xi, yi, oi, 64, gpu.E3_Y_GIVEN)
+    od = O.Desc(xi, yi, oi, 64)
+    got = _run(gpu, d, g, x, w, dm, Y=Y)
+    _check(got, _oracle(od, g, x, w, dm, Y=Y), TOL_F32, "generic conv degree 8")
+    rng = np.random.default_rng(432)
+    B = 53
+    xt = rng.standard_normal((B, S.dim(xi), 64)).astype(np.float32)
+    yt = rng.standard_normal((B, S.dim(yi))).astype(np.float32)
+    wt = rng.standard_normal((B, S.num_paths(xi, yi, oi), 64)).astype(np.float32)
+    dz = rng.standard_normal((B, S.dim(oi), 64)).astype(np.float32)
+    z = host(gpu.tp_forward_generic(d, dev(xt), dev(yt), dev(wt)))
+    assert_close(z, O.tp_forward(od, xt, yt, wt), TOL_F32, "generic tp degree 8")
+    dx, dw, dy = gpu.tp_backward_generic(d, dev(xt), dev(yt), dev(wt), dev(dz))
+    for k, a, b in zip(("dx", "dw", "dy"), (dx, dw, dy), O.tp_backward(od, xt, yt, wt, dz)):
+        assert_close(host(a), b, TOL_F32, f"generic tp bwd degree 8:{k}")
