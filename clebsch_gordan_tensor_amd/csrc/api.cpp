@@ -1370,9 +1370,11 @@ e3_status build_gemm(const e3_desc* desc, std::vector<int32_t>& out, e3k::TpGemm
 // that the paths of one x irrep are consecutive, and cut into tiles of at
 // most four quads that never mix x irreps or groups of 16 paths (16 t ..
 // 16 t + 15): a tile is one product A x over its irrep's components (the K
-// list, shared by the irrep's tiles), each quad's four rows are added up
-// in the lane that holds them, and the quads' sums per path are a second
-// product with a 0/1 matrix into the group's 16 paths.
+// list, shared by the irrep's tiles; an irrep of more than 16 components,
+// degree 8, gives each tile one block per K chunk of 16, consecutive, on
+// the same rows), each quad's four rows are added up in the lane that holds
+// them, and the quads' sums per path are a second product with a 0/1 matrix
+// into the group's 16 paths.
 // Layout: header kGemmHeader words (magic + 2, n_blocks, dx, dy, dout, P,
 // n_klist, n_groups, off_rowtab, a_floats, off_blocks, off_klist,
 // off_groups, words); blocks [nb][4]: path group t, rows (4 per quad), K

@@ -17,13 +17,14 @@
 // Plan (host-built, see the GEMM table of the library):
 //   header kGemmHeader words: magic, n_blocks, dx, dy, dout, P, n_klist,
 //     n_groups, 0, a_floats, off_blocks, off_klist, off_groups, plan words
-//   blocks [n_blocks][4]: output offset, rows (2L+1), K-list start, K (x4)
+//   blocks [n_blocks][4]: output offset, rows (2L+1, at most 16: a degree-8
+//     block is two, of 16 and 1 rows, on one K list), K-list start, K (x4)
 //   klist  [n_klist]: (P << 16) | x component, or -1 for a padding column
-//   groups [n_groups][4]: A index (block base + M * K + k), the two y
+//   groups [n_groups][4] in increasing A index: A index (block base + k * rows + M), the two y
 //     components (y1 | y2 << 16), the two coefficients' bits (a real-basis
 //     entry A[M][m1] couples at most two m2; an unused second term has c = 0)
-// A is stored block after block, each transposed (A[k][M], stride rows =
-// 2L+1; the MFMA's rows past them read zero), so a k-step's 64 reads fall in
+// A is stored block after block, each transposed (A[k][M], stride rows;
+// the MFMA's rows past them read zero), so a k-step's 64 reads fall in
 // distinct banks; the staged x and w rows have a stride of 16 (mod 32)
 // floats for the same reason (the four k of a step read four rows).
 #include <hip/hip_runtime.h>
