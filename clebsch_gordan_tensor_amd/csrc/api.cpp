@@ -1669,6 +1669,22 @@ void tp_gemm_window(e3k::TpGemmArgs& t) {
   t.lds_bytes = e3k::tp_gemm_lds_bytes(t);
 }
 
+// The same for the dense convolution with given harmonics (its LDS adds the
+// harmonic bank and the y map): 64-channel slabs with A in windows where
+// all of A allows only narrower slabs.
+void conv_gemm_window(e3k::TpGemmArgs& t) {
+  if (t.CS >= 64 || t.C % 64) return;
+  e3k::TpGemmArgs w = t;
+  w.CS = 64;
+  w.a_win = 1;
+  const long fixed = long(e3k::tp_gemm_lds_bytes(w)) - 4 + 4L * e3k::kConvGemmExtraWords;
+  const long win = (long(160) * 1024 - fixed) / 4;
+  if (win < std::max<long>(t.a_block_max, t.a_floats / 4) || win >= t.a_floats) return;
+  t.CS = 64;
+  t.a_win = int(win);
+  t.lds_bytes = e3k::tp_gemm_lds_bytes(t) + 4 * e3k::kConvGemmExtraWords;
+}
+
 e3_status build_table(const e3_desc* desc, int table, std::vector<int32_t>& out) {
   if (table == E3_GEN_GEMM || table == E3_GEN_GEMM_DX || table == E3_GEN_GEMM_DW) {
     e3k::TpGemmArgs d;
@@ -2027,8 +2043,12 @@ e3_status e3_conv_backward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_
   } else {
     tdx.lds_bytes += 4 * e3k::kConvGemmExtraWords;
   }
+  conv_gemm_window(tdx);
   if (p.C % tdx.CS || tdx.lds_bytes > 160 * 1024)
     return fail(E3_ERR_UNSUPPORTED, "the dense-product plan does not fit in LDS");
+  if ((tdx.P + 1) * e3k::gemm_row_stride(tdx.CS) > 65535 ||
+      tdx.dx * e3k::gemm_row_stride(tdx.CS) > 65535)
+    return fail(E3_ERR_UNSUPPORTED, "too many components or paths for the dense-product kernels");
   const e3k::TransposeLayout L = e3k::transpose_layout(n_nodes, n_edges);
   const int* ws = static_cast<const int*>(workspace);
   const hipStream_t st = hipStream_t(stream);
@@ -2122,6 +2142,7 @@ e3_status e3_conv_forward_gemm(const e3_desc* desc, int32_t n_nodes, int32_t n_e
     }
     if (a.t.CS) break;
   }
+  if (a.ly < 0) conv_gemm_window(a.t);  // given harmonics
   if (!a.t.CS) return fail(E3_ERR_UNSUPPORTED, "the dense-product plan does not fit in LDS");
   const int XS = e3k::gemm_row_stride(a.t.CS);
   if ((a.t.P + 1) * XS > 65535 || a.t.dx * XS > 65535)

@@ -100,12 +100,14 @@ __device__ __forceinline__ void gemm_ksteps(float4v (&D)[NU], const float* ap, c
 // not fit in the previous one (the partition the block loops walk), and,
 // the plans' entries being sorted by A index, each window's run of entries:
 // wq[i] = the first entry whose index is at least window i's start, wq[n] =
-// n_groups.  Run by one thread once per workgroup; returns the number of
-// windows found (at most kMaxWindows: later windows scan every entry).
+// n_groups; starts (if given) receives each window's A offset.  Run by one
+// thread once per workgroup; returns the number of windows found (at most
+// kMaxWindows: later windows scan every entry).
 constexpr int kMaxWindows = 15;
 template <class SizeOf>
 __device__ int window_runs(int n_blocks, SizeOf size_of, int a_floats, int AW,
-                           const int4* __restrict__ groups, int n_groups, int* wq) {
+                           const int4* __restrict__ groups, int n_groups, int* wq,
+                           int* starts = nullptr) {
   int nw = 0, abase = 0, w1 = 0;
   for (int b = 0; b < n_blocks && nw < kMaxWindows; ++b) {
     const int sz = size_of(b);
@@ -117,6 +119,7 @@ __device__ int window_runs(int n_blocks, SizeOf size_of, int a_floats, int AW,
         const int mid = (lo + hi) >> 1;
         if (groups[mid].x < abase) lo = mid + 1; else hi = mid;
       }
+      if (starts) starts[nw] = abase;
       wq[nw++] = lo;
     }
     abase += sz;
@@ -308,7 +311,9 @@ __device__ __forceinline__ void edge_bank(int ly, const float* v, float* s_bank)
 // order.  PRE as above, for the next edge of the same receiver (built with
 // PRE = 0).  NB is 8, or kConvGemmMaxBlocks for plans of more blocks (the
 // smaller form keeps the registers of the common case).
-template <int PRE, int NU, bool BATCH, bool VEC, int NB>
+// WIN: A in windows of whole blocks (g.a_win > 0), each edge's A built and
+// its blocks' products run one window at a time.
+template <int PRE, int NU, bool BATCH, bool VEC, int NB, bool WIN>
 __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
   constexpr int kConvGemmBlocks = NB;
   extern __shared__ __align__(16) float gsm[];
@@ -318,13 +323,16 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
   const int4* __restrict__ groups = reinterpret_cast<const int4*>(g.plan + g.off_groups);
   const int CS = g.CS, C = g.C, XS = gemm_row_stride(CS);
   const int lg4 = __builtin_ctz(CS / 4);
+  const int AW = WIN && g.a_win > 0 ? min(g.a_win, g.a_floats) : g.a_floats;
   float* s_a = gsm;
-  float* s_x = s_a + g.a_floats;
+  float* s_x = s_a + AW;
   float* s_w = s_x + g.dx * XS;
   float* s_y = s_w + (g.P + 1) * XS;
   int* s_k = reinterpret_cast<int*>(s_y + g.dy);
   float* s_bank = reinterpret_cast<float*>(s_k + g.n_klist);  // 64 floats
   int* s_ym = reinterpret_cast<int*>(s_bank + 64);             // y map, 16 words
+  int* s_wq = s_ym + 16;  // windows: their runs of entries, then their count
+  int* s_ws = s_wq + kMaxWindows + 2;  // and their A offsets
   for (int i = threadIdx.x; i < g.n_klist; i += 256) {
     const int ent = klist[i];
     const int p = ent < 0 ? g.P : min(ent >> 16, g.P - 1);
@@ -334,7 +342,7 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
   for (int i = threadIdx.x; i < XS; i += 256) s_w[g.P * XS + i] = 0.0f;
   // A's entries outside the plan's groups stay zero: every row (edge)
   // rewrites all the others, so A is cleared once
-  for (int i = threadIdx.x; i < g.a_floats; i += 256) s_a[i] = 0.0f;
+  for (int i = threadIdx.x; i < AW; i += 256) s_a[i] = 0.0f;
   constexpr bool vec_y = VEC;  // harmonics from the edge vectors (cg.ly >= 0)
   if (threadIdx.x < 16) {
     int wd;
@@ -364,6 +372,39 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
       b_ab[b] = abase;
       abase += b_rows[b] * b_K[b];
     }
+  }
+  // windows of whole blocks (the partition of window_runs): block b in
+  // window b_wi[b] at b_ab[b] - its start; n_win windows
+  static_assert(NB <= kMaxWindows, "every window holds a block");
+  int b_wi[kConvGemmBlocks], n_win = 1;
+  if constexpr (WIN) {
+    int w0 = 0, w1 = 0, wi = -1;
+#pragma unroll
+    for (int b = 0; b < kConvGemmBlocks; ++b) {
+      const int sz = b_rows[b] * b_K[b];
+      if (b < g.n_blocks && sz > 0 && b_ab[b] + sz > w1) {
+        ++wi;
+        w0 = b_ab[b];
+        w1 = w0 + AW;
+      }
+      b_wi[b] = max(wi, 0);
+      b_ab[b] -= w0;
+      if (sz > AW) b_K[b] = 0;  // larger than a window: not computed
+    }
+    n_win = max(wi + 1, 1);
+    if (threadIdx.x == 0) {
+      auto size_of = [&](int b) {
+        const int rows = min(max(blocks[4 * b + 1], 1), 16);
+        const int kb = min(max(blocks[4 * b + 2], 0), g.n_klist);
+        const int K = min(max(blocks[4 * b + 3], 0), g.n_klist - kb) & ~3;
+        return rows * K;
+      };
+      s_wq[kMaxWindows + 1] =
+          window_runs(g.n_blocks, size_of, g.a_floats, AW, groups, g.n_groups, s_wq, s_ws);
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < kConvGemmBlocks; ++b) b_wi[b] = 0;
   }
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, kq = lane >> 4;
@@ -437,16 +478,30 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
           s_y[i] = PRE > 0 && i < 256 ? ypre : g.y[int64_t(e) * g.dy + i];
       }
       __syncthreads();
+      if (PRE > 0 && j + 1 < e_hi) prefetch(j + 1, c0);
+      for (int wi = 0; wi < n_win; ++wi) {  // one pass unless windowed (uniform)
+      // (the window table is read after the edge's first barrier)
+      const int w0 = WIN && wi < s_wq[kMaxWindows + 1] ? s_ws[wi] : 0;
+      if (WIN) {
+        if (wi > 0) __syncthreads();  // the previous window's reads are done
+        for (int i = threadIdx.x; i < AW; i += 256) s_a[i] = 0.0f;
+        __syncthreads();
+      }
+      {
+        const int q0 = !WIN ? 0 : wi < s_wq[kMaxWindows + 1] ? s_wq[wi] : 0;
+        const int q1 = !WIN ? g.n_groups : wi < s_wq[kMaxWindows + 1] ? s_wq[wi + 1] : g.n_groups;
 #pragma unroll 4
-      for (int q = threadIdx.x; q < g.n_groups; q += 256) {
-        const int4 en = groups[q];
-        const int at = min(max(en.x, 0), g.a_floats - 1);
-        const int y1 = min(en.y & 0xFFFF, g.dy - 1), y2 = min((en.y >> 16) & 0xFFFF, g.dy - 1);
-        s_a[at] = fmaf(__int_as_float(en.w), yval(y2), __int_as_float(en.z) * yval(y1));
+        for (int q = q0 + threadIdx.x; q < q1; q += 256) {
+          const int4 en = groups[q];
+          const int at = min(max(en.x, 0), g.a_floats - 1) - w0;
+          const int y1 = min(en.y & 0xFFFF, g.dy - 1), y2 = min((en.y >> 16) & 0xFFFF, g.dy - 1);
+          if (!WIN || (at >= 0 && at < AW))
+            s_a[at] = fmaf(__int_as_float(en.w), yval(y2), __int_as_float(en.z) * yval(y1));
+        }
       }
       __syncthreads();
-      if (PRE > 0 && j + 1 < e_hi) prefetch(j + 1, c0);
-      if (!active) continue;  // the same for the whole wavefront
+      // the same for the whole wavefront; windowed, it still meets the later windows' barriers
+      if (!active) continue;
       const float* sw = s_w + 16 * wave + li;
       const float* sx = s_x + 16 * wave + li;
       // each edge's product starts from zero and joins the node's sum once,
@@ -454,6 +509,7 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
       // once per K step
 #pragma unroll
       for (int b = 0; b < kConvGemmBlocks; ++b) {
+        if (WIN && b_wi[b] != wi) continue;  // another window's block (uniform)
         const int rows = b_rows[b], K = b_K[b];
         const bool aok = li < rows;
         const float* ap = s_a + b_ab[b] + kq * rows + min(li, rows - 1);
@@ -465,6 +521,7 @@ __global__ void __launch_bounds__(256) k_conv_gemm(ConvGemmArgs cg) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) D[b][u] += De[u];
       }
+      }  // windows
     }
     // D[i][j] in register i % 4 of lane j + 16 (i / 4): row 4 kq + r, channel li
 #pragma unroll
@@ -877,7 +934,8 @@ __global__ void __launch_bounds__(64 * NW) k_gemm_dy(GemmBwdArgs a) {
 size_t tp_gemm_lds_bytes(const TpGemmArgs& a) {
   const int XS = gemm_row_stride(a.CS);
   const int aw = a.a_win > 0 ? std::min(a.a_win, a.a_floats) : a.a_floats;
-  const int wq = a.a_win > 0 ? kMaxWindows + 2 : 0;  // the windows' runs of entries
+  // the windows' runs of entries and (the convolution) their A offsets
+  const int wq = a.a_win > 0 ? 2 * kMaxWindows + 3 : 0;
   return size_t(aw + a.dx * XS + (a.P + 1) * XS + a.dy + a.n_klist + wq) * 4;
 }
 
@@ -894,16 +952,16 @@ hipError_t launch_tp_gemm_pre(const TpGemmArgs& a, int per_cu, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int PRE, int NU, bool BATCH, bool VEC, int NB>
+template <int PRE, int NU, bool BATCH, bool VEC, int NB, bool WIN = false>
 hipError_t launch_conv_gemm_nb(const ConvGemmArgs& a, int per_cu, hipStream_t s) {
   // the attribute is per function: raised once, retried after a failure
   static std::atomic<bool> lds_set{false};
-  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH, VEC, NB>), 160 * 1024);
+  if (const hipError_t e = set_max_lds_once(lds_set, reinterpret_cast<const void*>(&k_conv_gemm<PRE, NU, BATCH, VEC, NB, WIN>), 160 * 1024);
       e != hipSuccess)
     return e;
   const int64_t items = int64_t(a.n_nodes) * (a.t.C / a.t.CS);
   const int grid = int(std::min<int64_t>(items, int64_t(256) * per_cu));
-  hipLaunchKernelGGL((k_conv_gemm<PRE, NU, BATCH, VEC, NB>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
+  hipLaunchKernelGGL((k_conv_gemm<PRE, NU, BATCH, VEC, NB, WIN>), dim3(grid), dim3(256), a.t.lds_bytes, s, a);
   return hipGetLastError();
 }
 
@@ -915,11 +973,14 @@ hipError_t launch_conv_gemm_pre(const ConvGemmArgs& a, int per_cu, hipStream_t s
 
 hipError_t launch_conv_gemm(const ConvGemmArgs& a, hipStream_t s) {
   if (a.n_nodes <= 0) return hipSuccess;
-  if (a.t.a_win > 0) return hipErrorInvalidValue;  // all of A per edge
   if (a.t.lds_bytes > 160 * 1024 || a.t.n_blocks > kConvGemmMaxBlocks || a.t.CS > 128 ||
       a.ly > 7 || (a.ly >= 0 && a.t.dy > 64))
     return hipErrorInvalidValue;
   const int per_cu = std::max<int>(1, int((160 * 1024) / std::max<size_t>(a.t.lds_bytes, 1)));
+  if (a.t.a_win > 0) {  // A in windows: given harmonics, 64-channel slabs, one form
+    if (a.ly >= 0 || a.t.CS != 64 || a.t.a_win < a.t.a_block_max) return hipErrorInvalidValue;
+    return launch_conv_gemm_nb<0, 1, true, false, kConvGemmMaxBlocks, true>(a, per_cu, s);
+  }
   // one 16-channel tile per wavefront (slabs of at most 64 channels).  The
   // next edge's operands are not prefetched here: with the per-block
   // accumulators the registers would leave one wavefront per SIMD.
